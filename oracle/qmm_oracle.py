@@ -1,0 +1,294 @@
+"""Float64 CPU oracle for GGUF block-quantized matrix products.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and its
+Python binding) imports or calls this module.  Only the tests, the smoke check
+in ``__graft_entry__.smoke`` and the CPU-baseline leg of ``bench.py`` use it.
+It shares no code with the GPU path: it decodes the raw bytes itself with numpy.
+
+Every function states the passage it follows.  Pages cited:
+
+* "EdgeRunner Core Architecture" (EdgeRunner): section 1.3 TensorStorage &
+  TensorDataType (GGUF type ids, bytes per block), section 3.1 Quantization
+  Format Summary, section 3.2 Q8_0 Layout, section 3.4 Weight Dequantization
+  Strategy (raw blocks used without materialising float weights), section 8
+  SwiGLU FFN.
+* "llama.cpp Metal (MPS) End-to-End Inference Path" (llama.cpp Metal): section
+  3.2 MUL_MAT 3-way kernel selection (ne00 is the contiguous reduction length K,
+  ne11 the number of tokens).
+* "alpaca.swift": Capabilities (F16, Q8_0, Q4_0 weights used in place),
+  Numerical validation (float64 reference, bit-exact dequantisation, the
+  element-wise error bound 2^-10 * sum |x_k w_k| for the half-precision GEMM),
+  Limitations (activations stay in floating point).
+
+Readings of points the pages leave open (each also listed with the design notes):
+
+* Q8_0: the fp16 scale is little-endian IEEE binary16 at byte 0; the 32 codes are
+  two's-complement int8 at bytes 2..33; weight = d * q.
+* Q4_0: the pages give only "4-bit, 32 per block, fp16 scale, 18 bytes".  Adopted:
+  the GGUF arrangement, byte j of the 16 code bytes carries element j in its low
+  nibble and element j + 16 in its high nibble; weight = d * (nibble - 8).
+* Orientation: W is row-major [M][K] (rows of K/32 blocks), y = x W^T with x
+  token-major [N][K].
+* Fp16 scales decode with IEEE semantics, subnormals included; inf and NaN
+  propagate.
+
+Parity pins (tests under tests/test_oracle.py): hand-computed blocks stored in
+tests/golden (decode and nibble order), all 65536 fp16 patterns against a manual
+sign/exponent/mantissa decode, exact rational brute force on tiny shapes,
+pack/unpack round trip, SiLU closed forms, and the soundness of the fused-output
+bound by perturbation.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+FMT_F16 = 1   # GGUF type ids (EdgeRunner, section 1.3)
+FMT_Q4_0 = 2
+FMT_Q8_0 = 8
+
+QK = 32                         # weights per block (EdgeRunner, section 3.1)
+BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4_0: 18}
+
+# Acceptance constants: |y_gpu - y_ref| <= REL * S + ABS, S = sum_k |w_k x_k|.
+# REL = 2e-3 is about 2x the 2^-10 element-wise bound alpaca.swift states for its
+# half-precision GEMM (Numerical validation).
+TOL_REL = 2e-3
+TOL_ABS = 1e-6
+
+
+# ---------------------------------------------------------------- unpacking
+def row_bytes(fmt: int, K: int) -> int:
+    """Bytes per row: K/32 * 34 (Q8_0), K/32 * 18 (Q4_0), 2K (F16).
+
+    EdgeRunner, section 3.1 (bytes per block) and section 3.2 (block count times 34).
+    """
+    if fmt == FMT_F16:
+        return 2 * K
+    if fmt not in BLOCK_BYTES or K % QK:
+        raise ValueError("bad format or K")
+    return K // QK * BLOCK_BYTES[fmt]
+
+
+def _blocks(raw: np.ndarray, fmt: int, M: int, K: int) -> np.ndarray:
+    raw = np.ascontiguousarray(raw, dtype=np.uint8).reshape(-1)
+    if raw.size != M * row_bytes(fmt, K):
+        raise ValueError("byte count does not match M x K")
+    return raw.reshape(M, K // QK, BLOCK_BYTES[fmt])
+
+
+def _scale64(blk: np.ndarray) -> np.ndarray:
+    """fp16 scale from bytes 0..1 (little endian) -> float64, IEEE semantics."""
+    d16 = np.ascontiguousarray(blk[..., 0:2]).view("<f2")[..., 0]
+    return d16.astype(np.float64)
+
+
+def unpack_q8_0(raw, M: int, K: int) -> np.ndarray:
+    """Q8_0 -> float64 [M][K]: w_i = d * q_i, q_i = int8 at byte 2 + i.
+
+    EdgeRunner, section 3.2 Q8_0 Layout (scale first, then 32 one-byte codes).
+    """
+    blk = _blocks(raw, FMT_Q8_0, M, K)
+    d = _scale64(blk)                                         # [M][nb]
+    q = np.ascontiguousarray(blk[..., 2:34]).view(np.int8)    # [M][nb][32]
+    with np.errstate(invalid="ignore"):                       # inf scale * 0 code -> NaN
+        return (d[..., None] * q.astype(np.float64)).reshape(M, K)
+
+
+def unpack_q4_0(raw, M: int, K: int) -> np.ndarray:
+    """Q4_0 -> float64 [M][K]: w_j = d*((b_j & 15) - 8), w_{j+16} = d*((b_j >> 4) - 8).
+
+    EdgeRunner, sections 1.3 and 3.1 (4-bit codes, fp16 scale, 18 bytes); nibble
+    order and the -8 offset are the adopted GGUF reading.
+    """
+    blk = _blocks(raw, FMT_Q4_0, M, K)
+    d = _scale64(blk)
+    b = blk[..., 2:18].astype(np.int64)                       # [M][nb][16]
+    lo = (b & 15) - 8
+    hi = (b >> 4) - 8
+    q = np.concatenate([lo, hi], axis=-1).astype(np.float64)  # element j, then j + 16
+    with np.errstate(invalid="ignore"):
+        return (d[..., None] * q).reshape(M, K)
+
+
+def unpack_f16(raw, M: int, K: int) -> np.ndarray:
+    """F16 -> float64 [M][K] (EdgeRunner, section 1.3: type id 1)."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8).reshape(-1)
+    if raw.size != M * K * 2:
+        raise ValueError("byte count does not match M x K")
+    return raw.view("<f2").astype(np.float64).reshape(M, K)
+
+
+def dequant(fmt: int, raw, M: int, K: int) -> np.ndarray:
+    if fmt == FMT_Q8_0:
+        return unpack_q8_0(raw, M, K)
+    if fmt == FMT_Q4_0:
+        return unpack_q4_0(raw, M, K)
+    if fmt == FMT_F16:
+        return unpack_f16(raw, M, K)
+    raise ValueError(f"unknown format {fmt}")
+
+
+def dequant_rows(fmt: int, raw, K: int, rows) -> np.ndarray:
+    """Decode only the listed rows of a large matrix (for sampled checks)."""
+    rb = row_bytes(fmt, K)
+    raw = np.asarray(raw, dtype=np.uint8).reshape(-1)
+    rows = np.asarray(rows, dtype=np.int64)
+    sel = raw.reshape(-1, rb)[rows]
+    return dequant(fmt, sel, len(rows), K)
+
+
+# ------------------------------------------------------------------ packing
+def pack_q8_0(q: np.ndarray, d16: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_q8_0 for codes q int8 [M][K] and fp16 scales [M][K/32]."""
+    M, K = q.shape
+    out = np.empty((M, K // QK, 34), dtype=np.uint8)
+    out[..., 0:2] = np.ascontiguousarray(d16, dtype="<f2").view(np.uint8).reshape(M, K // QK, 2)
+    out[..., 2:34] = np.asarray(q, dtype=np.int8).view(np.uint8).reshape(M, K // QK, 32)
+    return out.reshape(-1)
+
+
+def pack_q4_0(n: np.ndarray, d16: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_q4_0 for nibbles n in 0..15 [M][K] and fp16 scales [M][K/32]."""
+    M, K = n.shape
+    n = np.asarray(n, dtype=np.uint8).reshape(M, K // QK, 32)
+    if (n > 15).any():
+        raise ValueError("nibbles must be in 0..15")
+    out = np.empty((M, K // QK, 18), dtype=np.uint8)
+    out[..., 0:2] = np.ascontiguousarray(d16, dtype="<f2").view(np.uint8).reshape(M, K // QK, 2)
+    out[..., 2:18] = n[..., :16] | (n[..., 16:] << 4)
+    return out.reshape(-1)
+
+
+# ------------------------------------------------------------ matmul, SwiGLU
+def _w_rows(fmt, raw, M, K, r0, r1):
+    rb = row_bytes(fmt, K)
+    raw = np.asarray(raw, dtype=np.uint8).reshape(-1)
+    return dequant(fmt, raw[r0 * rb:r1 * rb], r1 - r0, K)
+
+
+def matmul_ref(fmt: int, raw, x, M: int, K: int, rows=None, chunk_rows: int = 8192):
+    """y = x W^T in float64 and S = |x| |W|^T (the scale of the error bound).
+
+    x: [N][K] holding exactly the values the GPU consumed (fp32 for decode, fp16
+    for prefill), upcast to float64.  Orientation as in llama.cpp Metal section
+    3.2 (K contiguous, tokens as the second operand).  ``rows`` restricts the
+    output to selected rows (sampled checks of very large matrices).
+    Returns (y, S), each [N][M] (or [N][len(rows)]).
+    """
+    x64 = np.asarray(x).astype(np.float64)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    ax = np.abs(x64)
+    if rows is not None:
+        W = dequant_rows(fmt, raw, K, rows)
+        return x64 @ W.T, ax @ np.abs(W).T
+    N = x64.shape[0]
+    y = np.empty((N, M))
+    S = np.empty((N, M))
+    for r0 in range(0, M, chunk_rows):
+        r1 = min(M, r0 + chunk_rows)
+        W = _w_rows(fmt, raw, M, K, r0, r1)
+        y[:, r0:r1] = x64 @ W.T
+        S[:, r0:r1] = ax @ np.abs(W).T
+    return y, S
+
+
+def silu(z):
+    """silu(z) = z * sigmoid(z) = z / (1 + e^-z) (EdgeRunner, section 8 SwiGLU FFN)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def gate_up_silu_ref(fmt: int, raw_g, raw_u, x, I: int, K: int, rows=None):
+    """h = silu(x Wg^T) * (x Wu^T) with its error scales.
+
+    EdgeRunner, section 8: the SwiGLU output is SiLU of the gate projection times
+    the up projection.  Returns (h, g, u, Sg, Su).
+    """
+    g, Sg = matmul_ref(fmt, raw_g, x, I, K, rows=rows)
+    u, Su = matmul_ref(fmt, raw_u, x, I, K, rows=rows)
+    return silu(g) * u, g, u, Sg, Su
+
+
+# ---------------------------------------------------------------- tolerances
+def tol_linear(S):
+    """Allowed |y_gpu - y_ref| for a linear output: 2e-3 * S + 1e-6."""
+    return TOL_REL * np.asarray(S) + TOL_ABS
+
+
+SILU_SLOPE_MAX = 1.1   # max |silu'(z)| = 1.0998 near z = 2.40
+
+
+def tol_swiglu(g, u, Sg, Su):
+    """Allowed |h_gpu - h_ref| for h = silu(g) * u when g and u each obey tol_linear.
+
+    With |g~ - g| <= Eg and |u~ - u| <= Eu:
+      |silu(g~) u~ - silu(g) u| <= |silu(g~) - silu(g)| |u~| + |silu(g)| |u~ - u|
+                                 <= 1.1 Eg (|u| + Eu) + |silu(g)| Eu,
+    plus a relative 1e-6 |h| + 1e-6 for the fp32 epilogue itself.
+    """
+    Eg = tol_linear(Sg)
+    Eu = tol_linear(Su)
+    h = silu(g) * u
+    return SILU_SLOPE_MAX * Eg * (np.abs(u) + Eu) + np.abs(silu(g)) * Eu + 1e-6 * np.abs(h) + 1e-6
+
+
+def fp16_round(w):
+    """Round float64 values to the nearest fp16 (ties to even), back to float64.
+
+    Used to state what a prefill GEMM tile holds: fp16(d * q).
+    """
+    return np.asarray(w, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+# ----------------------------------------------------------- plain reference
+def brute_force_matmul(fmt: int, raw: bytes, x_rows, M: int, K: int):
+    """Exact rational y = x W^T with pure-Python loops (tiny shapes only).
+
+    Decodes each block byte by byte from the format definition (no numpy) and
+    accumulates with fractions.Fraction, so the result has no rounding at all.
+    """
+    from fractions import Fraction
+
+    def f16(lo, hi):
+        h = lo | (hi << 8)
+        s = -1 if h >> 15 else 1
+        e = (h >> 10) & 31
+        m = h & 1023
+        if e == 0:
+            return s * Fraction(m, 1 << 24)
+        if e == 31:
+            raise ValueError("inf/nan scale")
+        return s * Fraction(1024 + m, 1024) * Fraction(2) ** (e - 15)
+
+    raw = bytes(raw)
+    rb = row_bytes(fmt, K)
+    W = []
+    for m in range(M):
+        row = raw[m * rb:(m + 1) * rb]
+        w = []
+        if fmt == FMT_F16:
+            for k in range(K):
+                w.append(f16(row[2 * k], row[2 * k + 1]))
+        else:
+            bb = BLOCK_BYTES[fmt]
+            for b in range(K // QK):
+                blk = row[b * bb:(b + 1) * bb]
+                d = f16(blk[0], blk[1])
+                if fmt == FMT_Q8_0:
+                    for i in range(32):
+                        q = blk[2 + i]
+                        w.append(d * (q - 256 if q >= 128 else q))
+                else:
+                    lo = [d * ((blk[2 + j] & 15) - 8) for j in range(16)]
+                    hi = [d * ((blk[2 + j] >> 4) - 8) for j in range(16)]
+                    w.extend(lo + hi)
+        W.append(w)
+    out = []
+    for xr in x_rows:
+        xf = [Fraction(float(v)) for v in xr]
+        out.append([sum(W[m][k] * xf[k] for k in range(K)) for m in range(M)])
+    return out

@@ -1,0 +1,124 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module only draws random numbers (numpy ``Generator(PCG64(seed))``) and lays
+them out in the GGUF block byte layouts through numpy structured dtypes.  It holds
+none of the method's arithmetic: nothing here decodes a block, multiplies, or
+accumulates.  Both the float64 oracle and the GPU library consume the bytes it
+returns; each decodes them with its own code.
+
+Block layouts (EdgeRunner Core Architecture, section 3.1 "Quantization Format
+Summary" and section 3.2 "Q8_0 Layout"; GGUF type ids from section 1.3):
+
+* Q8_0, type id 8: 34 bytes per 32 weights = fp16 scale (little endian) followed
+  by 32 signed bytes.
+* Q4_0, type id 2: 18 bytes per 32 weights = fp16 scale followed by 16 bytes
+  holding 32 four-bit codes (two per byte).
+* F16, type id 1: 2 bytes per weight.
+
+Distributions follow the workloads the library is measured on: Q8_0 codes uniform
+in [-127, 127], Q4_0 codes uniform in 0..15 (a uniform byte carries two
+independent uniform nibbles), fp16 scales uniform in [1e-3, 1e-2], F16 weights
+normal with standard deviation 0.02, activations standard normal.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+FMT_F16 = 1
+FMT_Q4_0 = 2
+FMT_Q8_0 = 8
+FORMATS = (FMT_F16, FMT_Q4_0, FMT_Q8_0)
+FMT_NAMES = {FMT_F16: "F16", FMT_Q4_0: "Q4_0", FMT_Q8_0: "Q8_0"}
+
+# Packed (unaligned) structured dtypes: itemsize 34 and 18 exactly.
+Q8_0_BLOCK = np.dtype([("d", "<f2"), ("qs", "i1", (32,))])
+Q4_0_BLOCK = np.dtype([("d", "<f2"), ("qs", "u1", (16,))])
+assert Q8_0_BLOCK.itemsize == 34 and Q4_0_BLOCK.itemsize == 18
+
+# Rows are drawn in fixed-size chunks so that very large matrices (a 128256-row
+# output head) stay within host memory; the chunk size is part of the recipe.
+_CHUNK_ROWS = 4096
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def layout_bytes(fmt: int, K: int) -> int:
+    """Bytes of one row in the block layout (a size statement, used for allocation)."""
+    if fmt == FMT_F16:
+        return 2 * K
+    if K % 32:
+        raise ValueError("block formats need K % 32 == 0")
+    return (K // 32) * (34 if fmt == FMT_Q8_0 else 18)
+
+
+def _scales(g: np.random.Generator, rows: int, nb: int, scale_mode: str) -> np.ndarray:
+    if scale_mode == "uniform":
+        return g.uniform(1e-3, 1e-2, size=(rows, nb)).astype(np.float16)
+    if scale_mode == "wide":
+        # Any finite fp16 bit pattern with a random sign: zeros, subnormals,
+        # negatives and the largest finite values all appear.
+        bits = g.integers(0, 0x7C00, size=(rows, nb), dtype=np.uint16)
+        bits |= (g.integers(0, 2, size=(rows, nb), dtype=np.uint16) << 15).astype(np.uint16)
+        return bits.view(np.float16)
+    if scale_mode == "gemm_wide":
+        # Finite fp16 scales of either sign with magnitude below 2**8, so that
+        # scale * code stays finite in fp16 (|code| <= 128).
+        bits = g.integers(0, 0x5C00, size=(rows, nb), dtype=np.uint16)
+        bits |= (g.integers(0, 2, size=(rows, nb), dtype=np.uint16) << 15).astype(np.uint16)
+        return bits.view(np.float16)
+    raise ValueError(scale_mode)
+
+
+def weights(fmt: int, M: int, K: int, seed: int, *, scale_mode: str = "uniform",
+            q8_low: int = -127) -> np.ndarray:
+    """Raw weight bytes for an M x K matrix, row-major, as a flat uint8 array.
+
+    Per chunk of rows the draw order is: codes, then scales (F16: values only).
+    ``q8_low`` = -128 widens the Q8_0 code range to the full int8 range.
+    """
+    g = rng(seed)
+    row_bytes = layout_bytes(fmt, K)
+    out = np.empty(M * row_bytes, dtype=np.uint8)
+    nb = K // 32
+    for r0 in range(0, M, _CHUNK_ROWS):
+        rows = min(_CHUNK_ROWS, M - r0)
+        dst = out[r0 * row_bytes:(r0 + rows) * row_bytes]
+        if fmt == FMT_Q8_0:
+            blk = dst.view(Q8_0_BLOCK).reshape(rows, nb)
+            blk["qs"] = g.integers(q8_low, 128, size=(rows, nb, 32), dtype=np.int8)
+            blk["d"] = _scales(g, rows, nb, scale_mode)
+        elif fmt == FMT_Q4_0:
+            blk = dst.view(Q4_0_BLOCK).reshape(rows, nb)
+            blk["qs"] = g.integers(0, 256, size=(rows, nb, 16), dtype=np.uint8)
+            blk["d"] = _scales(g, rows, nb, scale_mode)
+        elif fmt == FMT_F16:
+            dst.view(np.float16)[:] = g.normal(0.0, 0.02, size=rows * K).astype(np.float16)
+        else:
+            raise ValueError(f"unknown format {fmt}")
+    return out
+
+
+def activations(N: int, K: int, seed: int, dtype=np.float32) -> np.ndarray:
+    """Standard-normal activations [N][K] (fp32 for decode, fp16 for prefill)."""
+    return rng(seed).standard_normal((N, K)).astype(dtype)
+
+
+def one_hot(N: int, K: int, cols, dtype=np.float32) -> np.ndarray:
+    """Activations whose row n is the unit vector e_{cols[n]}."""
+    x = np.zeros((N, K), dtype=dtype)
+    for n, c in enumerate(cols):
+        x[n, c] = 1
+    return x
+
+
+# Shapes of the workloads (hidden/intermediate sizes and head layouts).
+SMOLLM2_135M = dict(layers=30, hidden=576, heads=9, kv_heads=3, head_dim=64,
+                    intermediate=1536, vocab=49152)
+LLAMA3_8B = dict(layers=32, hidden=4096, heads=32, kv_heads=8, head_dim=128,
+                 intermediate=14336, vocab=128256)
+
+
+def qkv_rows(cfg: dict) -> int:
+    return (cfg["heads"] + 2 * cfg["kv_heads"]) * cfg["head_dim"]

@@ -1,0 +1,379 @@
+"""Pins of the float64 oracle to facts outside itself (CPU only).
+
+Each check is written as a function taking the oracle's pieces as arguments, so
+that the mutation tests at the bottom can hand it a deliberately wrong variant
+(wrong nibble order, missing offset, unsigned codes, swapped scale, transposed
+operand, dropped term) and show that some pin rejects it.
+"""
+import glob
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from oracle import qmm_oracle as Q
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FMT_BY_NAME = {"Q8_0": Q.FMT_Q8_0, "Q4_0": Q.FMT_Q4_0, "F16": Q.FMT_F16}
+
+
+# ----------------------------------------------------------------- fixtures
+def load_golden(path):
+    fx = {"w": {}, "x": {}}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *rest = line.split()
+        if key == "fmt":
+            fx["fmt"] = FMT_BY_NAME[rest[0]]
+        elif key == "bytes":
+            fx["bytes"] = bytes(int(b, 16) for b in rest)
+        elif key == "w":
+            fx["w"][int(rest[0])] = Fraction(rest[1])
+            if rest[1].startswith("-") and Fraction(rest[1]) == 0:
+                fx.setdefault("negzero", []).append(int(rest[0]))
+        elif key == "x":
+            fx["x"][int(rest[0])] = Fraction(rest[1])
+        elif key == "xramp":
+            fx["x"] = {k: Fraction(k) for k in range(32)}
+        elif key == "xones":
+            fx["x"] = {k: Fraction(1) for k in range(32)}
+        elif key == "dot":
+            fx["dot"] = Fraction(rest[0])
+    return fx
+
+
+GOLDEN_FILES = sorted(glob.glob(os.path.join(GOLDEN, "*.txt")))
+
+
+def check_golden(fx, dequant, matmul):
+    K = 32
+    w = dequant(fx["fmt"], np.frombuffer(fx["bytes"], np.uint8), 1, K)[0]
+    want = np.zeros(K)
+    for k, v in fx["w"].items():
+        want[k] = float(v)
+    if not all(Fraction(float(a)) == Fraction(float(b)) for a, b in zip(w, want)):
+        return False
+    for k in fx.get("negzero", []):
+        if math.copysign(1.0, w[k]) != -1.0:
+            return False
+    x = np.zeros((1, K), np.float32)
+    for k, v in fx["x"].items():
+        x[0, k] = float(v)
+    y, _ = matmul(fx["fmt"], np.frombuffer(fx["bytes"], np.uint8), x, 1, K)
+    return Fraction(float(y[0, 0])) == fx["dot"]
+
+
+@pytest.mark.parametrize("path", GOLDEN_FILES, ids=os.path.basename)
+def test_golden_blocks(path):
+    fx = load_golden(path)
+    assert check_golden(fx, Q.dequant, Q.matmul_ref)
+
+
+@pytest.mark.parametrize("path", GOLDEN_FILES, ids=os.path.basename)
+def test_golden_blocks_brute_force(path):
+    """The byte-by-byte rational decoder agrees with the stored hand values too."""
+    fx = load_golden(path)
+    xr = [float(fx["x"].get(k, 0)) for k in range(32)]
+    (row,) = Q.brute_force_matmul(fx["fmt"], fx["bytes"], [xr], 1, 32)
+    assert row[0] == fx["dot"]
+
+
+def test_golden_fixture_count():
+    assert len(GOLDEN_FILES) >= 5
+
+
+# ------------------------------------------------------------ fp16 decoding
+def manual_f16(h):
+    """IEEE binary16 from sign, exponent and mantissa fields with math.ldexp."""
+    s = -1.0 if h >> 15 else 1.0
+    e = (h >> 10) & 0x1F
+    m = h & 0x3FF
+    if e == 0:
+        return s * math.ldexp(m, -24)
+    if e == 31:
+        return s * math.inf if m == 0 else math.nan
+    return s * math.ldexp(1024 + m, e - 25)
+
+
+def test_fp16_all_patterns_q8_0():
+    """Every fp16 scale pattern times codes {-128,-1,0,1,127} decodes as manual IEEE."""
+    codes = np.array([-128, -1, 0, 1, 127] + [0] * 27, dtype=np.int8)
+    hs = np.arange(65536, dtype=np.uint32)
+    raw = np.zeros((65536, 34), np.uint8)
+    raw[:, 0] = hs & 0xFF
+    raw[:, 1] = hs >> 8
+    raw[:, 2:34] = codes.view(np.uint8)
+    W = Q.unpack_q8_0(raw.reshape(-1), 65536, 32)
+    for h in range(65536):
+        d = manual_f16(h)
+        for i, c in enumerate(codes[:5]):
+            want = d * float(c)
+            got = W[h, i]
+            if math.isnan(want):
+                assert math.isnan(got), (h, c)
+            else:
+                assert got == want, (h, c, got, want)
+                if want == 0:
+                    assert math.copysign(1, got) == math.copysign(1, want), (h, c)
+
+
+def test_fp16_subnormal_example():
+    raw = bytes([0x01, 0x00, 0x80] + [0] * 31)
+    assert Q.unpack_q8_0(np.frombuffer(raw, np.uint8), 1, 32)[0, 0] == -7.62939453125e-06
+
+
+# ------------------------------------------------------------ round trips
+def test_roundtrip_q8_0():
+    g = np.random.default_rng(11)
+    M, K = 7, 96
+    q = g.integers(-128, 128, size=(M, K), dtype=np.int8)
+    q[0, 0], q[0, 1] = -128, 127
+    d = g.uniform(-4, 4, size=(M, K // 32)).astype(np.float16)
+    raw = Q.pack_q8_0(q, d)
+    assert raw.size == M * K // 32 * 34
+    W = Q.unpack_q8_0(raw, M, K)
+    assert np.array_equal(W, np.repeat(d.astype(np.float64), 32, axis=1) * q)
+    assert np.array_equal(Q.pack_q8_0(q, d), raw)
+
+
+def test_roundtrip_q4_0():
+    g = np.random.default_rng(12)
+    M, K = 5, 128
+    n = g.integers(0, 16, size=(M, K), dtype=np.uint8)
+    n[0, :2] = (0, 15)
+    d = g.uniform(-4, 4, size=(M, K // 32)).astype(np.float16)
+    raw = Q.pack_q4_0(n, d)
+    assert raw.size == M * K // 32 * 18
+    W = Q.unpack_q4_0(raw, M, K)
+    assert np.array_equal(W, np.repeat(d.astype(np.float64), 32, axis=1) * (n.astype(np.float64) - 8))
+
+
+def test_row_bytes():
+    assert Q.row_bytes(Q.FMT_Q8_0, 576) == 612
+    assert Q.row_bytes(Q.FMT_Q4_0, 576) == 324
+    assert Q.row_bytes(Q.FMT_F16, 576) == 1152
+    assert Q.row_bytes(Q.FMT_Q8_0, 4096) == 4352
+    assert Q.row_bytes(Q.FMT_Q4_0, 14336) == 8064
+    with pytest.raises(ValueError):
+        Q.row_bytes(Q.FMT_Q8_0, 100)
+
+
+# ------------------------------------------------------------ brute force
+def check_brute_force(fmt, M, K, N, seed, matmul, scale_mode="uniform"):
+    raw = si.weights(fmt, M, K, seed, scale_mode=scale_mode, q8_low=-128)
+    x = si.activations(N, K, seed + 1)
+    y, S = matmul(fmt, raw, x, M, K)
+    exact = Q.brute_force_matmul(fmt, raw.tobytes(), x.tolist(), M, K)
+    for n in range(N):
+        for m in range(M):
+            err = abs(Fraction(float(y[n, m])) - exact[n][m])
+            if err > Fraction(1e-12) * Fraction(float(S[n, m])) + Fraction(1, 10**300):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("fmt", [Q.FMT_Q8_0, Q.FMT_Q4_0, Q.FMT_F16])
+@pytest.mark.parametrize("shape", [(1, 32, 1), (3, 64, 2), (4, 64, 3), (2, 96, 1)])
+def test_brute_force(fmt, shape):
+    M, K, N = shape
+    assert check_brute_force(fmt, M, K, N, 100 + M * 7 + K + N, Q.matmul_ref)
+
+
+def test_brute_force_square_catches_transpose():
+    # Square shapes make a transposed operand type-check, so they are included.
+    assert check_brute_force(Q.FMT_Q8_0, 32, 32, 2, 5, Q.matmul_ref)
+
+
+def test_sampled_rows_match_full():
+    fmt, M, K = Q.FMT_Q4_0, 300, 128
+    raw = si.weights(fmt, M, K, 3)
+    x = si.activations(2, K, 4)
+    y, S = Q.matmul_ref(fmt, raw, x, M, K, chunk_rows=64)
+    rows = [0, 7, 63, 64, 299]
+    ys, Ss = Q.matmul_ref(fmt, raw, x, M, K, rows=rows)
+    assert np.array_equal(ys, y[:, rows]) and np.array_equal(Ss, S[:, rows])
+
+
+# --------------------------------------------------------------- SwiGLU
+def test_silu_closed_forms():
+    assert Q.silu(0.0) == 0.0
+    h = 1e-6
+    assert abs((Q.silu(h) - Q.silu(-h)) / (2 * h) - 0.5) < 1e-9      # silu'(0) = 1/2
+    z = np.linspace(-30, 30, 601)
+    assert np.allclose(Q.silu(z) - Q.silu(-z), z, rtol=0, atol=1e-12)  # silu(z) - silu(-z) = z
+    assert Q.silu(50.0) == pytest.approx(50.0, rel=1e-15)
+    assert abs(Q.silu(-800.0)) == 0.0
+    assert Q.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+
+
+def test_silu_slope_bound():
+    z = np.linspace(-20, 20, 400001)
+    s = 1 / (1 + np.exp(-z))
+    slope = s * (1 + z * (1 - s))
+    assert np.abs(slope).max() <= Q.SILU_SLOPE_MAX
+    assert np.abs(slope).max() > 1.09
+
+
+def test_swiglu_tolerance_sound():
+    """Random g~, u~ inside their linear bounds stay inside tol_swiglu."""
+    g0 = np.random.default_rng(7)
+    n = 200000
+    g = g0.normal(0, 3, n)
+    u = g0.normal(0, 3, n)
+    Sg = np.abs(g) * g0.uniform(1, 50, n)
+    Su = np.abs(u) * g0.uniform(1, 50, n)
+    Eg, Eu = Q.tol_linear(Sg), Q.tol_linear(Su)
+    gt = g + Eg * g0.uniform(-1, 1, n)
+    ut = u + Eu * g0.uniform(-1, 1, n)
+    err = np.abs(Q.silu(gt) * ut - Q.silu(g) * u)
+    assert (err <= Q.tol_swiglu(g, u, Sg, Su)).all()
+
+
+def test_gate_up_ref_definition():
+    fmt, I, K = Q.FMT_Q8_0, 16, 64
+    rg, ru = si.weights(fmt, I, K, 1), si.weights(fmt, I, K, 2)
+    x = si.activations(2, K, 3)
+    h, g, u, Sg, Su = Q.gate_up_silu_ref(fmt, rg, ru, x, I, K)
+    Wg, Wu = Q.dequant(fmt, rg, I, K), Q.dequant(fmt, ru, I, K)
+    x64 = x.astype(np.float64)
+    assert np.allclose(g, x64 @ Wg.T, rtol=1e-14, atol=0)
+    assert np.allclose(h, (x64 @ Wg.T) / (1 + np.exp(-(x64 @ Wg.T))) * (x64 @ Wu.T), rtol=1e-13, atol=0)
+
+
+def test_fp16_round_ties_even():
+    assert Q.fp16_round(2049.0) == 2048.0     # tie -> even mantissa
+    assert Q.fp16_round(2051.0) == 2052.0
+    assert Q.fp16_round(1.0 + 2 ** -11) == 1.0
+
+
+# ------------------------------------------------------------ generators
+def test_generator_ranges_and_determinism():
+    M, K = 64, 256
+    a = si.weights(si.FMT_Q8_0, M, K, 9)
+    assert np.array_equal(a, si.weights(si.FMT_Q8_0, M, K, 9))
+    blk = a.view(si.Q8_0_BLOCK)
+    assert blk["qs"].min() >= -127 and blk["qs"].max() <= 127
+    d = blk["d"].astype(np.float64)
+    assert d.min() >= np.float16(1e-3) and d.max() <= np.float16(1e-2)
+    b = si.weights(si.FMT_Q4_0, M, K, 9).view(si.Q4_0_BLOCK)
+    nib = np.concatenate([b["qs"] & 15, b["qs"] >> 4])
+    counts = np.bincount(nib.reshape(-1), minlength=16)
+    assert counts.min() > 0.8 * counts.mean()
+    f = si.weights(si.FMT_F16, 256, 256, 9).view(np.float16).astype(np.float64)
+    assert abs(f.std() - 0.02) < 0.001
+
+
+def test_generator_chunking_is_part_of_recipe():
+    # Rows beyond one chunk continue the same stream deterministically.
+    M, K = si._CHUNK_ROWS + 3, 32
+    a = si.weights(si.FMT_Q4_0, M, K, 1)
+    assert a.size == M * 18
+    assert np.array_equal(a, si.weights(si.FMT_Q4_0, M, K, 1))
+
+
+# ------------------------------------------------------------ mutation tests
+def _mut_q4_interleaved(raw, M, K):
+    blk = Q._blocks(raw, Q.FMT_Q4_0, M, K)
+    d = Q._scale64(blk)
+    b = blk[..., 2:18].astype(np.int64)
+    q = np.stack([(b & 15) - 8, (b >> 4) - 8], axis=-1).reshape(M, K // 32, 32)
+    return (d[..., None] * q).reshape(M, K)
+
+
+def _mut_q4_no_offset(raw, M, K):
+    blk = Q._blocks(raw, Q.FMT_Q4_0, M, K)
+    d = Q._scale64(blk)
+    b = blk[..., 2:18].astype(np.int64)
+    q = np.concatenate([b & 15, b >> 4], axis=-1)
+    return (d[..., None] * q).reshape(M, K)
+
+
+def _mut_q8_unsigned(raw, M, K):
+    blk = Q._blocks(raw, Q.FMT_Q8_0, M, K)
+    d = Q._scale64(blk)
+    return (d[..., None] * blk[..., 2:34].astype(np.float64)).reshape(M, K)
+
+
+def _mut_q8_scale_last(raw, M, K):
+    blk = Q._blocks(raw, Q.FMT_Q8_0, M, K)
+    d = np.ascontiguousarray(blk[..., 32:34]).view("<f2")[..., 0].astype(np.float64)
+    q = np.ascontiguousarray(blk[..., 0:32]).view(np.int8)
+    return (d[..., None] * q).reshape(M, K)
+
+
+def _mut_q8_big_endian_scale(raw, M, K):
+    blk = Q._blocks(raw, Q.FMT_Q8_0, M, K)
+    d = np.ascontiguousarray(blk[..., 0:2]).view(">f2")[..., 0].astype(np.float64)
+    q = np.ascontiguousarray(blk[..., 2:34]).view(np.int8)
+    return (d[..., None] * q).reshape(M, K)
+
+
+def _mut_f16_ftz(raw, M, K):
+    w = Q.unpack_f16(raw, M, K)
+    w[np.abs(w) < 2.0 ** -14] = 0.0
+    return w
+
+
+def _dequant_with(fmt_mut, fn):
+    def dq(fmt, raw, M, K):
+        return fn(raw, M, K) if fmt == fmt_mut else Q.dequant(fmt, raw, M, K)
+    return dq
+
+
+def _matmul_with_dequant(dq):
+    def mm(fmt, raw, x, M, K, rows=None, chunk_rows=8192):
+        W = dq(fmt, raw, M, K)
+        x64 = np.asarray(x).astype(np.float64).reshape(-1, K)
+        return x64 @ W.T, np.abs(x64) @ np.abs(W).T
+    return mm
+
+
+def _mm_transposed(fmt, raw, x, M, K, rows=None, chunk_rows=8192):
+    W = Q.dequant(fmt, raw, M, K)
+    x64 = np.asarray(x).astype(np.float64).reshape(-1, K)
+    return x64 @ W, np.abs(x64) @ np.abs(W)
+
+
+def _mm_dropped_term(fmt, raw, x, M, K, rows=None, chunk_rows=8192):
+    W = Q.dequant(fmt, raw, M, K)
+    x64 = np.asarray(x).astype(np.float64).reshape(-1, K)
+    return x64[:, :-1] @ W[:, :-1].T, np.abs(x64) @ np.abs(W).T
+
+
+def _pins_pass(dq, mm):
+    """True when every pin accepts the given decode/matmul pair (an error counts as a rejection)."""
+    try:
+        ok = all(check_golden(load_golden(p), dq, mm) for p in GOLDEN_FILES)
+        for fmt in (Q.FMT_Q8_0, Q.FMT_Q4_0, Q.FMT_F16):
+            ok = ok and check_brute_force(fmt, 32, 32, 2, 5, mm) and check_brute_force(fmt, 3, 64, 2, 8, mm)
+        return ok
+    except ValueError:
+        return False
+
+
+@pytest.mark.parametrize("name,fmt,fn", [
+    ("q4_interleaved", Q.FMT_Q4_0, _mut_q4_interleaved),
+    ("q4_no_offset", Q.FMT_Q4_0, _mut_q4_no_offset),
+    ("q8_unsigned", Q.FMT_Q8_0, _mut_q8_unsigned),
+    ("q8_scale_last", Q.FMT_Q8_0, _mut_q8_scale_last),
+    ("q8_big_endian_scale", Q.FMT_Q8_0, _mut_q8_big_endian_scale),
+    ("f16_flush_subnormals", Q.FMT_F16, _mut_f16_ftz),
+])
+def test_mutated_unpack_is_caught(name, fmt, fn):
+    dq = _dequant_with(fmt, fn)
+    assert not _pins_pass(dq, _matmul_with_dequant(dq)), name
+
+
+@pytest.mark.parametrize("mm", [_mm_transposed, _mm_dropped_term])
+def test_mutated_matmul_is_caught(mm):
+    assert not _pins_pass(Q.dequant, mm)
+
+
+def test_unmutated_pins_pass():
+    assert _pins_pass(Q.dequant, _matmul_with_dequant(Q.dequant))
