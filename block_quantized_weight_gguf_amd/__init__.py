@@ -1,0 +1,173 @@
+"""Python binding of the qmm C ABI (include/qmm.h): GGUF block-quantized products on MI355X.
+
+Argument marshalling only.  Each ``qmm_*`` function here has the C entry point's
+name and argument order, with torch device tensors in place of pointers; it
+checks nothing beyond what ctypes needs and raises ``QmmError`` on a negative
+status.  Every step of the computation runs in the HIP kernels of libqmm.so;
+PyTorch supplies device memory and the current stream.  There is no fallback:
+importing this package fails loudly if libqmm.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "QMM_F16", "QMM_Q4_0", "QMM_Q8_0", "QMM_VARIANT_AUTO", "QMM_VARIANT_VALU", "QMM_VARIANT_MFMA",
+    "QmmError", "lib_path", "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv",
+    "qmm_gemv_variant", "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gemm", "qmm_gemm_gate_up_silu",
+    "gemv", "gate_up_silu", "gemm", "gemm_gate_up_silu", "dequant",
+]
+
+QMM_F16, QMM_Q4_0, QMM_Q8_0 = 1, 2, 8
+QMM_VARIANT_AUTO, QMM_VARIANT_VALU, QMM_VARIANT_MFMA = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libqmm.so")
+
+if not os.path.exists(lib_path):
+    raise ImportError(
+        f"{lib_path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(or python block_quantized_weight_gguf_amd/build.py); there is no fallback path")
+
+_lib = ctypes.CDLL(lib_path)
+
+_i64, _i32, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+_SIGS = {
+    "qmm_version": (_i32, []),
+    "qmm_strerror": (ctypes.c_char_p, [_i32]),
+    "qmm_row_bytes": (_i64, [_i32, _i64]),
+    "qmm_dequant": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp]),
+    "qmm_gemv": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "qmm_gemv_variant": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
+    "qmm_gemv_choose": (_i32, [_i32, _i64, _i64, _i64]),
+    "qmm_gate_up_silu": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "qmm_gemm": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "qmm_gemm_gate_up_silu": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {qmm_strerror(status)} (status {status})")
+        self.status = status
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status < 0:
+        raise QmmError(status, where)
+
+
+# ------------------------------------------------------ same names as the C ABI
+def qmm_version() -> int:
+    return _lib.qmm_version()
+
+
+def qmm_strerror(status: int) -> str:
+    return _lib.qmm_strerror(status).decode()
+
+
+def qmm_row_bytes(fmt: int, K: int) -> int:
+    r = _lib.qmm_row_bytes(fmt, K)
+    _check(r, "qmm_row_bytes")
+    return r
+
+
+def qmm_dequant(fmt, W, out, M, K, stream=None) -> None:
+    _check(_lib.qmm_dequant(fmt, _ptr(W), _ptr(out), M, K, _stream(stream)), "qmm_dequant")
+
+
+def qmm_gemv(fmt, W, x, y, M, K, N, stream=None) -> None:
+    _check(_lib.qmm_gemv(fmt, _ptr(W), _ptr(x), _ptr(y), M, K, N, _stream(stream)), "qmm_gemv")
+
+
+def qmm_gemv_variant(fmt, W, x, y, M, K, N, variant, stream=None) -> None:
+    _check(_lib.qmm_gemv_variant(fmt, _ptr(W), _ptr(x), _ptr(y), M, K, N, variant, _stream(stream)),
+           "qmm_gemv_variant")
+
+
+def qmm_gemv_choose(fmt, M, K, N) -> int:
+    r = _lib.qmm_gemv_choose(fmt, M, K, N)
+    _check(r, "qmm_gemv_choose")
+    return r
+
+
+def qmm_gate_up_silu(fmt, Wg, Wu, x, h, I, K, N, stream=None) -> None:
+    _check(_lib.qmm_gate_up_silu(fmt, _ptr(Wg), _ptr(Wu), _ptr(x), _ptr(h), I, K, N, _stream(stream)),
+           "qmm_gate_up_silu")
+
+
+def qmm_gemm(fmt, W, X, Y, M, K, T, stream=None) -> None:
+    _check(_lib.qmm_gemm(fmt, _ptr(W), _ptr(X), _ptr(Y), M, K, T, _stream(stream)), "qmm_gemm")
+
+
+def qmm_gemm_gate_up_silu(fmt, Wg, Wu, X, H, I, K, T, stream=None) -> None:
+    _check(_lib.qmm_gemm_gate_up_silu(fmt, _ptr(Wg), _ptr(Wu), _ptr(X), _ptr(H), I, K, T, _stream(stream)),
+           "qmm_gemm_gate_up_silu")
+
+
+# ------------------------------------------- conveniences (allocate the output)
+def _out(shape, like, out):
+    if out is not None:
+        return out
+    return torch.empty(shape, dtype=torch.float32, device=like.device)
+
+
+def dequant(fmt, W, M, K, out=None, stream=None):
+    out = _out((M, K), W, out)
+    qmm_dequant(fmt, W, out, M, K, stream)
+    return out
+
+
+def gemv(fmt, W, x, M, K, out=None, variant=QMM_VARIANT_AUTO, stream=None):
+    """y[N][M] = x[N][K] W^T for fp32 x (N = x.shape[0] or 1 for a vector)."""
+    N = 1 if x.dim() == 1 else x.shape[0]
+    out = _out((N, M), x, out)
+    qmm_gemv_variant(fmt, W, x, out, M, K, N, variant, stream)
+    return out
+
+
+def gate_up_silu(fmt, Wg, Wu, x, I, K, out=None, stream=None):
+    N = 1 if x.dim() == 1 else x.shape[0]
+    out = _out((N, I), x, out)
+    qmm_gate_up_silu(fmt, Wg, Wu, x, out, I, K, N, stream)
+    return out
+
+
+def gemm(fmt, W, X, M, K, out=None, stream=None):
+    """Y[T][M] = X[T][K] W^T for fp16 X."""
+    T = X.shape[0]
+    out = _out((T, M), X, out)
+    qmm_gemm(fmt, W, X, out, M, K, T, stream)
+    return out
+
+
+def gemm_gate_up_silu(fmt, Wg, Wu, X, I, K, out=None, stream=None):
+    T = X.shape[0]
+    out = _out((T, I), X, out)
+    qmm_gemm_gate_up_silu(fmt, Wg, Wu, X, out, I, K, T, stream)
+    return out

@@ -1,0 +1,144 @@
+// C ABI of the qmm library: host-side argument validation and variant dispatch.
+// Every check runs before any HIP call, so an invalid call enqueues nothing.
+// Size arithmetic is overflow-checked ("alpaca.swift", Highlights: untrusted
+// lengths are bounded and all size arithmetic is checked).
+#include <stdint.h>
+
+#include "../../include/qmm.h"
+#include "qmm_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7FFFFFFFLL;
+
+bool fmt_ok(int fmt) { return fmt == QMM_F16 || fmt == QMM_Q4_0 || fmt == QMM_Q8_0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    // a, b >= 0
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t row_bytes_unchecked(int fmt, int64_t K) {
+    if (fmt == QMM_F16) return 2 * K;
+    return (K / 32) * (fmt == QMM_Q8_0 ? 34 : 18);
+}
+
+// Shape checks shared by all entry points: 1 <= M, K, N <= 2^31 - 1, K % 32 == 0,
+// and the weight bytes M * row_bytes, activations N * K * 4 and outputs N * M * 4
+// all fit in int64.
+int check_shape(int fmt, int64_t M, int64_t K, int64_t N) {
+    if (!fmt_ok(fmt)) return QMM_ERR_FMT;
+    if (M < 1 || K < 1 || N < 1 || M > kMaxDim || K > kMaxDim || N > kMaxDim) return QMM_ERR_SHAPE;
+    if (K % 32) return QMM_ERR_SHAPE;
+    int64_t t;
+    if (!mul_ok(M, row_bytes_unchecked(fmt, K), &t)) return QMM_ERR_OVERFLOW;
+    if (!mul_ok(N, K, &t) || !mul_ok(t, 4, &t)) return QMM_ERR_OVERFLOW;
+    if (!mul_ok(N, M, &t) || !mul_ok(t, 4, &t)) return QMM_ERR_OVERFLOW;
+    return QMM_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
+
+// Batched-GEMV token count from which the fp16-MFMA kernel beats the VALU kernel
+// (measured per format on MI355X at the Llama-3-8B projection shapes).
+int64_t mfma_threshold(int fmt) {
+    switch (fmt) {
+        case QMM_Q4_0: return 8;
+        case QMM_Q8_0: return 8;
+        default: return 8;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmm_version(void) { return 100; }
+
+const char* qmm_strerror(int status) {
+    switch (status) {
+        case QMM_OK: return "ok";
+        case QMM_ERR_NULL: return "a required pointer is NULL";
+        case QMM_ERR_FMT: return "unknown weight format (expected 1=F16, 2=Q4_0, 8=Q8_0)";
+        case QMM_ERR_SHAPE: return "bad shape (need 1 <= M, K, N <= 2^31-1 and K % 32 == 0)";
+        case QMM_ERR_ALIGN: return "misaligned pointer (W, x, X need 16 bytes; outputs 4 bytes)";
+        case QMM_ERR_OVERFLOW: return "a byte count overflows int64";
+        case QMM_ERR_HIP: return "HIP runtime error at launch";
+        case QMM_ERR_VARIANT: return "unknown GEMV variant";
+        default: return "unknown qmm status";
+    }
+}
+
+int64_t qmm_row_bytes(int fmt, int64_t K) {
+    if (!fmt_ok(fmt)) return QMM_ERR_FMT;
+    if (K < 1 || K > kMaxDim || K % 32) return QMM_ERR_SHAPE;
+    return row_bytes_unchecked(fmt, K);
+}
+
+int qmm_dequant(int fmt, const void* W, float* out, int64_t M, int64_t K, void* stream) {
+    if (!W || !out) return QMM_ERR_NULL;
+    int st = check_shape(fmt, M, K, 1);
+    if (st) return st;
+    int64_t t;
+    if (!mul_ok(M, K, &t) || !mul_ok(t, 4, &t)) return QMM_ERR_OVERFLOW;
+    if (!aligned(W, 16) || !aligned(out, 16)) return QMM_ERR_ALIGN;
+    return from_hip(qmm::launch_dequant(fmt, W, out, M, K, static_cast<hipStream_t>(stream)));
+}
+
+int qmm_gemv_choose(int fmt, int64_t M, int64_t K, int64_t N) {
+    const int st = check_shape(fmt, M, K, N);
+    if (st) return st;
+    return N >= mfma_threshold(fmt) ? QMM_VARIANT_MFMA : QMM_VARIANT_VALU;
+}
+
+int qmm_gemv_variant(int fmt, const void* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
+                     int variant, void* stream) {
+    if (!W || !x || !y) return QMM_ERR_NULL;
+    int st = check_shape(fmt, M, K, N);
+    if (st) return st;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return QMM_ERR_ALIGN;
+    if (variant == QMM_VARIANT_AUTO) variant = qmm_gemv_choose(fmt, M, K, N);
+    auto s = static_cast<hipStream_t>(stream);
+    if (variant == QMM_VARIANT_VALU) return from_hip(qmm::launch_gemv_valu(fmt, W, nullptr, x, y, M, K, N, s));
+    if (variant == QMM_VARIANT_MFMA)
+        return from_hip(qmm::launch_gemm_mfma(fmt, W, nullptr, x, true, y, M, K, N, s));
+    return QMM_ERR_VARIANT;
+}
+
+int qmm_gemv(int fmt, const void* W, const float* x, float* y, int64_t M, int64_t K, int64_t N, void* stream) {
+    return qmm_gemv_variant(fmt, W, x, y, M, K, N, QMM_VARIANT_AUTO, stream);
+}
+
+int qmm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, float* h, int64_t I, int64_t K,
+                     int64_t N, void* stream) {
+    if (!Wg || !Wu || !x || !h) return QMM_ERR_NULL;
+    int st = check_shape(fmt, I, K, N);
+    if (st) return st;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(x, 16) || !aligned(h, 4)) return QMM_ERR_ALIGN;
+    auto s = static_cast<hipStream_t>(stream);
+    if (N >= mfma_threshold(fmt)) return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, x, true, h, I, K, N, s));
+    return from_hip(qmm::launch_gemv_valu(fmt, Wg, Wu, x, h, I, K, N, s));
+}
+
+int qmm_gemm(int fmt, const void* W, const void* X, float* Y, int64_t M, int64_t K, int64_t T, void* stream) {
+    if (!W || !X || !Y) return QMM_ERR_NULL;
+    int st = check_shape(fmt, M, K, T);
+    if (st) return st;
+    if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
+    return from_hip(qmm::launch_gemm_mfma(fmt, W, nullptr, X, false, Y, M, K, T, static_cast<hipStream_t>(stream)));
+}
+
+int qmm_gemm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const void* X, float* H, int64_t I, int64_t K,
+                          int64_t T, void* stream) {
+    if (!Wg || !Wu || !X || !H) return QMM_ERR_NULL;
+    int st = check_shape(fmt, I, K, T);
+    if (st) return st;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(X, 16) || !aligned(H, 4)) return QMM_ERR_ALIGN;
+    return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, X, false, H, I, K, T, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

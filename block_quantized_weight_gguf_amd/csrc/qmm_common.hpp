@@ -1,0 +1,129 @@
+// Device-side helpers shared by the qmm kernels (gfx950 / CDNA4, wave64).
+//
+// Block formats ("EdgeRunner Core Architecture", sections 1.3, 3.1 and 3.2):
+//   Q8_0: [fp16 d][32 x int8 q]           34 bytes, weight = d * q
+//   Q4_0: [fp16 d][16 bytes of nibbles]   18 bytes, byte j: low nibble -> weight j,
+//                                          high nibble -> weight j + 16; weight = d * (n - 8)
+//   F16 : 32 halfs treated as a 64-byte "block" so every format shares the 32-wide K tiling.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+constexpr int kWave = 64;
+constexpr int kQK = 32;  // weights per block
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<8> {  // Q8_0
+    static constexpr int BB = 34;
+};
+template <>
+struct Fmt<2> {  // Q4_0
+    static constexpr int BB = 18;
+};
+template <>
+struct Fmt<1> {  // F16
+    static constexpr int BB = 64;
+};
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte global load marked non-temporal (streamed weights are read once).
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu)));
+}
+
+// Signed byte j (0..3) of a dword, converted to float.
+__device__ __forceinline__ float sbyte_to_float(uint32_t w, int j) {
+    return static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(w >> (8 * j))));
+}
+
+// Unsigned byte j (0..3) of a dword, converted to float.
+__device__ __forceinline__ float ubyte_to_float(uint32_t w, int j) {
+    return static_cast<float>(static_cast<uint8_t>(w >> (8 * j)));
+}
+
+// ({hi, lo} >> 8*sh)[31:0] for sh in 0..3: realigns a byte stream read as dwords.
+__device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t sh) {
+    return __builtin_amdgcn_alignbyte(hi, lo, sh);
+}
+
+// Copy the global bytes [src, src + n) to LDS such that byte src + i lands at
+// dst + (src & 15) + i.  Whole 16-byte aligned chunks are moved with one 16-byte
+// load each; nothing at or beyond `end` is read (the chunk holding `end`, if any,
+// is copied byte by byte).  Bytes before src inside the first aligned chunk are
+// read as well; callers guarantee they lie at or after the buffer base (the
+// weight buffer is 16-byte aligned).  Work is spread over `nl` lanes.
+__device__ __forceinline__ void stage_bytes(const uint8_t* src, int n, uint8_t* dst,
+                                            const uint8_t* end, int lane, int nl) {
+    const uint8_t* a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(src) & ~uintptr_t(15));
+    const int total = static_cast<int>(src + n - a);
+    const int chunks = (total + 15) >> 4;
+    for (int c = lane; c < chunks; c += nl) {
+        const uint8_t* p = a + 16 * c;
+        if (p + 16 <= end) {
+            *reinterpret_cast<uint4*>(dst + 16 * c) = load16_nt(p);
+        } else {
+            for (int i = 0; i < 16; ++i) dst[16 * c + i] = (p + i < end) ? p[i] : uint8_t(0);
+        }
+    }
+}
+
+// Read `ND` dwords starting at the 2-byte aligned LDS address p, realigned so
+// that out[i] holds bytes p+4i .. p+4i+3.  Reads ND+1 dwords from the enclosing
+// 4-byte aligned address (the caller keeps 4 bytes of slack after the data).
+template <int ND>
+__device__ __forceinline__ void lds_read_dwords(const uint8_t* p, uint32_t (&out)[ND]) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(p);
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(addr & ~uintptr_t(3));
+    const uint32_t sh = static_cast<uint32_t>(addr & 3);
+    uint32_t d[ND + 1];
+#pragma unroll
+    for (int i = 0; i <= ND; ++i) d[i] = base[i];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) out[i] = align_bytes(d[i + 1], d[i], sh);
+}
+
+__device__ __forceinline__ uint32_t lds_read_u16(const uint8_t* p) {
+    return *reinterpret_cast<const uint16_t*>(p);
+}
+
+// silu(z) = z / (1 + e^-z)  ("EdgeRunner Core Architecture", section 8 SwiGLU FFN).
+// expf is the ROCm device-library exponential.
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Transposing butterfly reduction over a wave64.  On entry every lane holds V
+// partial sums v[0..V); on exit lane l holds, in v[0], the wave-wide sum of
+// index l / (64 / V).  Cost: V - 1 + (6 - log2 V) exchanges instead of 6 V.
+template <int V>
+__device__ __forceinline__ void wave_reduce_transpose(float (&v)[V], int lane) {
+    static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
+    int cnt = V;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        if (cnt > 1) {
+            const bool upper = (lane & off) != 0;
+            const int h = cnt >> 1;
+#pragma unroll
+            for (int i = 0; i < h; ++i) {
+                const float send = upper ? v[i] : v[i + h];
+                const float keep = upper ? v[i + h] : v[i];
+                v[i] = keep + __shfl_xor(send, off, 64);
+            }
+            cnt = h;
+        } else {
+            v[0] += __shfl_xor(v[0], off, 64);
+        }
+    }
+}
+
+}  // namespace qmm

@@ -1,0 +1,24 @@
+// Host-side launch entry points of the qmm kernels (internal; the public C ABI
+// in include/qmm.h validates arguments and calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace qmm {
+
+hipError_t launch_dequant(int fmt, const void* W, float* out, int64_t M, int64_t K, hipStream_t s);
+
+// VALU GEMV over N tokens (any N >= 1): y[n][m] = sum_k W[m][k] x[n][k].
+// Wu != nullptr selects the gate/up SwiGLU epilogue (W = gate, Wu = up, y = h).
+hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float* x, float* y,
+                            int64_t M, int64_t K, int64_t N, hipStream_t s);
+
+// fp16-MFMA GEMM: Y[t][m] = sum_k W[m][k] X[t][k]; X is fp16 (x_is_f32 = false) or fp32
+// rounded to fp16 while staging (x_is_f32 = true).  Wu != nullptr selects the SwiGLU epilogue.
+hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32,
+                            float* Y, int64_t M, int64_t K, int64_t T, hipStream_t s);
+
+}  // namespace qmm

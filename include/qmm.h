@@ -1,0 +1,165 @@
+/*
+ * qmm.h -- GGUF block-quantized weight x activation products on AMD MI355X (gfx950).
+ *
+ * The weights stay in their GGUF block bytes in device memory and are decoded in
+ * registers (or into LDS tiles) inside the product kernels; no float copy of a
+ * weight matrix is ever written.  ("EdgeRunner Core Architecture", section 3.4
+ * Weight Dequantization Strategy, Tier 1: raw quantized buffers go straight into
+ * the fused product kernels; section 15, item 2: this cuts the weight bytes read
+ * by about 3.8x against decoding to float32 first.)
+ *
+ * Formats (GGUF type ids, "EdgeRunner Core Architecture" section 1.3; block sizes,
+ * section 3.1; Q8_0 byte order, section 3.2):
+ *   QMM_F16  = 1 : 2 bytes per weight, IEEE binary16, little endian.
+ *   QMM_Q4_0 = 2 : 18 bytes per 32 weights: fp16 scale d, then 16 bytes; byte j holds
+ *                  weight j in its low nibble and weight j+16 in its high nibble;
+ *                  weight = d * (nibble - 8).
+ *   QMM_Q8_0 = 8 : 34 bytes per 32 weights: fp16 scale d, then 32 int8 codes q;
+ *                  weight = d * q.
+ *
+ * Matrix convention (llama.cpp Metal end-to-end path, section 3.2 MUL_MAT: the
+ * reduction length K is the contiguous weight dimension; the token count is the
+ * second operand's row count):
+ *   W : M rows, each row K weights = K/32 consecutive blocks (F16: K halfs),
+ *       rows stored back to back (row stride = qmm_row_bytes(fmt, K)).
+ *   x : N (or T) rows of K activations, row-major.
+ *   y : N (or T) rows of M outputs, row-major, float32:  y[n][m] = sum_k W[m][k] x[n][k].
+ *
+ * Activations are never quantised ("alpaca.swift", Limitations): decode takes fp32
+ * x; prefill takes fp16 X ("alpaca.swift", Design: half-precision prefill
+ * activations).  Products accumulate in fp32.
+ *
+ * Common rules for every entry point:
+ *   - All array arguments are device pointers owned by the caller.  The library
+ *     allocates no memory, keeps no state between calls and is re-entrant.
+ *     (Pre-allocated buffers with no allocation per pass: "EdgeRunner Core
+ *     Architecture", section 10 Scratch Buffers and section 15, item 4.)
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).  All
+ *     work is enqueued asynchronously on it; nothing synchronises.
+ *   - Arguments are validated on the host before any HIP call; a failure returns
+ *     a negative qmm_status and enqueues nothing.  A launch failure reported by
+ *     hipGetLastError returns QMM_ERR_HIP.
+ *   - Size checks follow the practice of bounding every length and checking
+ *     every size product for overflow ("alpaca.swift", Highlights: the GGUF
+ *     parser treats files as untrusted).
+ *   - Outputs must not alias inputs (not checked).
+ *   - Alignment: W, x, X must be 16-byte aligned; y, Y, h, H, out 4-byte aligned.
+ *   - Limits: 1 <= M, K, N, T <= 2^31 - 1 and K % 32 == 0 for every format (F16
+ *     included, so that all formats share the 32-wide tiling).
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QMM_F16 = 1,
+    QMM_Q4_0 = 2,
+    QMM_Q8_0 = 8
+} qmm_fmt;
+
+typedef enum {
+    QMM_OK = 0,
+    QMM_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    QMM_ERR_FMT = -2,         /* format id is not 1, 2 or 8                        */
+    QMM_ERR_SHAPE = -3,       /* M, K, N or T out of range, or K % 32 != 0         */
+    QMM_ERR_ALIGN = -4,       /* a pointer violates the alignment rule above       */
+    QMM_ERR_OVERFLOW = -5,    /* a byte count does not fit in int64                */
+    QMM_ERR_HIP = -6,         /* the HIP runtime reported an error at launch       */
+    QMM_ERR_VARIANT = -7      /* unknown variant id passed to qmm_gemv_variant     */
+} qmm_status;
+
+/* Variant ids for qmm_gemv_variant / qmm_gemv_choose. */
+typedef enum {
+    QMM_VARIANT_AUTO = 0,     /* library picks from (fmt, M, K, N)                          */
+    QMM_VARIANT_VALU = 1,     /* register-decode GEMV: one weight read, N fp32 FMAs          */
+    QMM_VARIANT_MFMA = 2      /* LDS-tile decode + fp16 MFMA (x rounded to fp16 in-kernel)   */
+} qmm_variant;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int qmm_version(void);
+
+/* Human-readable text for a qmm_status value (static storage; never NULL). */
+const char* qmm_strerror(int status);
+
+/*
+ * Bytes per weight row: K/32*34 (Q8_0), K/32*18 (Q4_0), 2*K (F16).
+ * ("EdgeRunner Core Architecture", section 3.1 bytes per block; section 3.2 block
+ * count times 34.)  Returns a negative qmm_status for an unknown format, K < 1,
+ * K % 32 != 0 or K > 2^31 - 1.  Host-only; makes no HIP call.
+ */
+int64_t qmm_row_bytes(int fmt, int64_t K);
+
+/*
+ * Decode a whole matrix to fp32: out[m][k] = W[m][k] (float32, row-major M x K).
+ * Every decoded value d*q (or d*(n-8), or an f16) is exact in fp32, so the result
+ * is bit-exact.  ("EdgeRunner Core Architecture", section 3.4, Tier 2: GPU decode
+ * kernels that write a float buffer; "alpaca.swift", Numerical validation:
+ * dequantisation is bit-exact.)  Not used by the product paths; it is the
+ * check of the decoders and the building block of decode-then-GEMM prefill.
+ */
+int qmm_dequant(int fmt, const void* W, float* out, int64_t M, int64_t K, void* stream);
+
+/*
+ * Decode GEMV: y[n][m] = sum_k W[m][k] * x[n][k] for n < N, fp32 x and y.
+ * N = 1 is single-token decode; small N (a few tokens) reads every weight once
+ * and reuses it N times.  ("EdgeRunner Core Architecture", section 2.1 fused
+ * Q8_0 dequant + GEMV pipelines; "llama.cpp Metal ...", section 3.2 and P9:
+ * per-format mat-vec kernels for one token and a batched mat-vec for 2..8 tokens.)
+ * The variant is chosen from (fmt, M, K, N) as qmm_gemv_choose reports.  The MFMA
+ * variant, used only for larger N, rounds x to fp16 inside the kernel.
+ * Fused QKV is this call on the row-concatenation [Wq; Wk; Wv] (M = q + 2 kv).
+ */
+int qmm_gemv(int fmt, const void* W, const float* x, float* y,
+             int64_t M, int64_t K, int64_t N, void* stream);
+
+/* As qmm_gemv with an explicit variant (QMM_VARIANT_*), for crossover sweeps. */
+int qmm_gemv_variant(int fmt, const void* W, const float* x, float* y,
+                     int64_t M, int64_t K, int64_t N, int variant, void* stream);
+
+/*
+ * The variant qmm_gemv would run for these sizes (a QMM_VARIANT_* value >= 1),
+ * or a negative qmm_status for invalid sizes.  Host-only.  The GEMV/GEMM split
+ * by token count follows "llama.cpp Metal ...", section 3.2 (mat-vec for few
+ * tokens, the tiled matrix-matrix kernel above a threshold); the threshold here
+ * is measured on MI355X.
+ */
+int qmm_gemv_choose(int fmt, int64_t M, int64_t K, int64_t N);
+
+/*
+ * Fused gate+up projection with the SwiGLU epilogue, fp32 x:
+ *   g = x Wg^T, u = x Wu^T, h[n][i] = silu(g[n][i]) * u[n][i],  silu(z) = z / (1 + e^-z).
+ * Wg and Wu are two I x K matrices in the same format (a concatenated [gate; up]
+ * buffer is Wg = base, Wu = base + I * qmm_row_bytes(fmt, K)).  h is N x I fp32.
+ * ("EdgeRunner Core Architecture", section 8 SwiGLU FFN: SiLU of the gate times
+ * up, fused into one dispatch for single-token decode.)
+ */
+int qmm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, float* h,
+                     int64_t I, int64_t K, int64_t N, void* stream);
+
+/*
+ * Prefill GEMM: Y[t][m] = sum_k W[m][k] * X[t][k], X fp16 (T x K), Y fp32 (T x M).
+ * Weight blocks are decoded into fp16 LDS tiles, fp16(d*q) rounded to nearest
+ * even, and fed to fp16 MFMA with fp32 accumulation.  ("alpaca.swift", Design and
+ * Capabilities: prefill on the matrix hardware with half-precision activations;
+ * Numerical validation: element-wise error bound proportional to sum |x w|.)
+ */
+int qmm_gemm(int fmt, const void* W, const void* X, float* Y,
+             int64_t M, int64_t K, int64_t T, void* stream);
+
+/*
+ * Prefill gate+up with the SwiGLU epilogue: H[t][i] = silu((X Wg^T)[t][i]) * (X Wu^T)[t][i].
+ * X fp16 (T x K), H fp32 (T x I).  Same tiles and rounding as qmm_gemm.
+ */
+int qmm_gemm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const void* X, float* H,
+                          int64_t I, int64_t K, int64_t T, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI (CPU only; no kernel is launched).
+
+The library must load, export every function include/qmm.h declares, compute
+row sizes, and reject every invalid argument before any HIP call.  The pointer
+values used here are never dereferenced: each call fails validation first.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_quantized_weight_gguf_amd as qmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR = 0, -1, -2, -3, -4, -5, -6, -7
+A16 = 0x10000  # a 16-byte aligned fake address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_api():
+    assert declared_functions() == sorted([
+        "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv", "qmm_gemv_variant",
+        "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gemm", "qmm_gemm_gate_up_silu"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(qmm.lib_path)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", qmm.lib_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (qmm_[a-z_0-9]+)\b", out))
+    assert set(declared_functions()) <= exported
+    assert set(qmm.EXPORTED) == set(declared_functions())
+
+
+def test_version_and_strerror():
+    assert qmm.qmm_version() >= 100
+    for s in (OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR):
+        assert qmm.qmm_strerror(s) and "unknown qmm status" not in qmm.qmm_strerror(s)
+    assert "unknown" in qmm.qmm_strerror(-99)
+
+
+@pytest.mark.parametrize("fmt,K,want", [
+    (8, 576, 612), (2, 576, 324), (1, 576, 1152), (8, 4096, 4352), (2, 4096, 2304),
+    (8, 14336, 15232), (2, 14336, 8064), (1, 32, 64), (8, 32, 34), (2, 32, 18)])
+def test_row_bytes(fmt, K, want):
+    assert qmm._lib.qmm_row_bytes(fmt, K) == want
+
+
+@pytest.mark.parametrize("fmt,K,want", [(3, 64, E_FMT), (0, 64, E_FMT), (8, 0, E_SHAPE), (8, 100, E_SHAPE),
+                                        (2, -32, E_SHAPE), (1, 48, E_SHAPE), (8, 2**31, E_SHAPE)])
+def test_row_bytes_errors(fmt, K, want):
+    assert qmm._lib.qmm_row_bytes(fmt, K) == want
+
+
+def test_gemv_validation():
+    L = qmm._lib
+    assert L.qmm_gemv(8, None, A16, A16, 4, 64, 1, None) == E_NULL
+    assert L.qmm_gemv(8, A16, None, A16, 4, 64, 1, None) == E_NULL
+    assert L.qmm_gemv(8, A16, A16, None, 4, 64, 1, None) == E_NULL
+    assert L.qmm_gemv(5, A16, A16, A16, 4, 64, 1, None) == E_FMT
+    assert L.qmm_gemv(8, A16, A16, A16, 0, 64, 1, None) == E_SHAPE
+    assert L.qmm_gemv(8, A16, A16, A16, 4, 0, 1, None) == E_SHAPE
+    assert L.qmm_gemv(8, A16, A16, A16, 4, 48, 1, None) == E_SHAPE
+    assert L.qmm_gemv(8, A16, A16, A16, 4, 64, 0, None) == E_SHAPE
+    assert L.qmm_gemv(8, A16, A16, A16, 2**31, 64, 1, None) == E_SHAPE
+    assert L.qmm_gemv(8, A16, A16, A16, 2**31 - 1, 2**31 - 32, 2**31 - 1, None) == E_OVF
+    assert L.qmm_gemv(8, A16 + 8, A16, A16, 4, 64, 1, None) == E_ALIGN
+    assert L.qmm_gemv(8, A16, A16 + 4, A16, 4, 64, 1, None) == E_ALIGN
+    assert L.qmm_gemv(8, A16, A16, A16 + 2, 4, 64, 1, None) == E_ALIGN
+    assert L.qmm_gemv_variant(8, A16, A16, A16 + 2, 4, 64, 1, 1, None) == E_ALIGN
+
+
+def test_gate_up_validation():
+    L = qmm._lib
+    assert L.qmm_gate_up_silu(2, A16, None, A16, A16, 4, 64, 1, None) == E_NULL
+    assert L.qmm_gate_up_silu(4, A16, A16, A16, A16, 4, 64, 1, None) == E_FMT
+    assert L.qmm_gate_up_silu(2, A16, A16, A16, A16, 4, 40, 1, None) == E_SHAPE
+    assert L.qmm_gate_up_silu(2, A16, A16 + 4, A16, A16, 4, 64, 1, None) == E_ALIGN
+
+
+def test_gemm_validation():
+    L = qmm._lib
+    assert L.qmm_gemm(8, A16, None, A16, 4, 64, 8, None) == E_NULL
+    assert L.qmm_gemm(8, A16, A16, A16, 4, 64, 0, None) == E_SHAPE
+    assert L.qmm_gemm(8, A16, A16 + 2, A16, 4, 64, 8, None) == E_ALIGN
+    assert L.qmm_gemm_gate_up_silu(8, A16, A16, A16, None, 4, 64, 8, None) == E_NULL
+    assert L.qmm_gemm_gate_up_silu(9, A16, A16, A16, A16, 4, 64, 8, None) == E_FMT
+    assert L.qmm_gemm_gate_up_silu(8, A16, A16, A16, A16 + 1, 4, 64, 8, None) == E_ALIGN
+
+
+def test_dequant_validation():
+    L = qmm._lib
+    assert L.qmm_dequant(8, None, A16, 4, 64, None) == E_NULL
+    assert L.qmm_dequant(8, A16, A16, 4, 65, None) == E_SHAPE
+    assert L.qmm_dequant(8, A16, A16 + 4, 4, 64, None) == E_ALIGN
+
+
+def test_variant_choice():
+    L = qmm._lib
+    for fmt in (1, 2, 8):
+        assert L.qmm_gemv_choose(fmt, 4096, 4096, 1) == 1
+        assert L.qmm_gemv_choose(fmt, 4096, 4096, 4096) == 2
+        v = [L.qmm_gemv_choose(fmt, 4096, 4096, n) for n in range(1, 65)]
+        assert v == sorted(v), "the choice must switch once, from VALU to MFMA"
+    assert L.qmm_gemv_choose(7, 4096, 4096, 1) == E_FMT
+    assert L.qmm_gemv_choose(8, 4096, 100, 1) == E_SHAPE
+    assert L.qmm_gemv_variant(8, A16, A16, A16 + 1, 4, 64, 1, 9, None) == E_ALIGN
+    assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, 9, None) == E_VAR
+    assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, -1, None) == E_VAR
+
+
+def test_binding_raises():
+    with pytest.raises(qmm.QmmError) as e:
+        qmm.qmm_gemv(8, 0, A16, A16, 4, 64, 1, stream=0)
+    assert e.value.status == E_NULL
