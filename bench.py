@@ -1,0 +1,272 @@
+"""Benchmark of the qmm hot path on one MI355X.
+
+One step = the single-token (N = 1) decode pass over Llama-3-8B-shaped projections
+-- fused QKV 4096->6144, O 4096->4096, gate+up 4096->2x14336 with the SwiGLU
+epilogue, down 14336->4096 (fed with the gate+up output), LM head 4096->128256 --
+once with Q8_0 weights and once with Q4_0 weights.  Inputs are seeded synthetic
+tensors resident in HBM before timing starts.  The step streams 1.21 GB of
+weights, more than the 256 MB Infinity Cache, so every launch reads from HBM.
+
+value = algorithmic bytes of one step (raw weight blocks + x + y) / step time.
+
+The same run also times the prefill GEMM (fp16 activations, fp32 output) at
+4096->14336 and 14336->4096 for T in {128, 2048, 4096}, Q8_0 and Q4_0, and reports
+TFLOP/s = 2 T M K / time; and times the float64 CPU oracle on a bounded sample of
+the decode step (reported baseline only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--suite PATH]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--suite", default=None, help="write per-kernel details as JSON to this path")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP-event timing of individual launches on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, key, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.setdefault(key, []).append((s, e))
+
+    def ms(self, key):
+        return [s.elapsed_time(e) for s, e in self.pairs.get(key, [])]
+
+
+def decode_workload(torch, qmm, si):
+    L = si.LLAMA3_8B
+    H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
+    dev = torch.device("cuda")
+
+    def W(fmt, M, K, seed):
+        return torch.from_numpy(si.weights(fmt, M, K, seed)).to(dev)
+
+    def X(n, K, seed):
+        return torch.from_numpy(si.activations(n, K, seed)).to(dev)
+
+    fmts = {}
+    for fmt, base in ((si.FMT_Q8_0, 5000), (si.FMT_Q4_0, 6000)):
+        f = dict(
+            qkv=W(fmt, Q, H, base + 1), o=W(fmt, H, H, base + 2), g=W(fmt, I, H, base + 3),
+            u=W(fmt, I, H, base + 4), d=W(fmt, H, I, base + 5), lm=W(fmt, V, H, base + 6),
+            x=X(1, H, base + 7), y_qkv=torch.empty(Q, device=dev), y_o=torch.empty(H, device=dev),
+            h=torch.empty(I, device=dev), y_d=torch.empty(H, device=dev), logits=torch.empty(V, device=dev))
+        fmts[fmt] = f
+    rb = {fmt: (lambda K, fmt=fmt: qmm.qmm_row_bytes(fmt, K)) for fmt in fmts}
+    launches = []  # (kernel key, bytes, callable)
+    for fmt, f in fmts.items():
+        name = si.FMT_NAMES[fmt]
+        r = rb[fmt]
+        launches += [
+            (f"gemv_{name}", "qkv", Q * r(H) + 4 * H + 4 * Q,
+             lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["qkv"], f["x"], f["y_qkv"], Q, H, 1)),
+            (f"gemv_{name}", "o", H * r(H) + 4 * H + 4 * H,
+             lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["o"], f["x"], f["y_o"], H, H, 1)),
+            (f"gate_up_{name}", "gate_up", 2 * I * r(H) + 4 * H + 4 * I,
+             lambda f=f, fmt=fmt: qmm.qmm_gate_up_silu(fmt, f["g"], f["u"], f["x"], f["h"], I, H, 1)),
+            (f"gemv_{name}", "down", H * r(I) + 4 * I + 4 * H,
+             lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["d"], f["h"], f["y_d"], H, I, 1)),
+            (f"gemv_{name}", "lm_head", V * r(H) + 4 * H + 4 * V,
+             lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["lm"], f["x"], f["logits"], V, H, 1)),
+        ]
+    return fmts, launches
+
+
+def prefill_cases(torch, qmm, si):
+    dev = torch.device("cuda")
+    cases = []
+    for fmt in (si.FMT_Q8_0, si.FMT_Q4_0):
+        for (M, K) in ((14336, 4096), (4096, 14336)):
+            Wt = torch.from_numpy(si.weights(fmt, M, K, 7000 + M % 101 + fmt)).to(dev)
+            for T in (128, 2048, 4096):
+                Xt = torch.from_numpy(si.activations(T, K, 7100 + T, dtype=np.float16)).to(dev)
+                Yt = torch.empty((T, M), device=dev)
+                cases.append(dict(fmt=fmt, M=M, K=K, T=T, flops=2.0 * T * M * K,
+                                  fn=lambda fmt=fmt, Wt=Wt, Xt=Xt, Yt=Yt, M=M, K=K, T=T:
+                                  qmm.qmm_gemm(fmt, Wt, Xt, Yt, M, K, T)))
+    return cases
+
+
+def cpu_baseline(si, budget_s=15.0):
+    """Float64 oracle on a bounded sample of the decode step: leading rows of each projection."""
+    import oracle
+    L = si.LLAMA3_8B
+    H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
+    shapes = [("qkv", Q, H), ("o", H, H), ("gate", I, H), ("up", I, H), ("down", H, I), ("lm_head", V, H)]
+    rows = 1024
+    total_bytes = 0.0
+    total_t = 0.0
+    t_start = time.perf_counter()
+    samples = []
+    for fmt in (si.FMT_Q8_0, si.FMT_Q4_0):
+        for name, M, K in shapes:
+            raw = si.weights(fmt, rows, K, 9000 + M)       # same shape rows, seeded
+            x = si.activations(1, K, 9001)
+            t0 = time.perf_counter()
+            oracle.matmul_ref(fmt, raw, x, rows, K)
+            dt = time.perf_counter() - t0
+            b = rows * oracle.row_bytes(fmt, K) + 4 * K + 4 * rows
+            total_bytes += b
+            total_t += dt
+            samples.append(f"{si.FMT_NAMES[fmt]}:{name}")
+        if time.perf_counter() - t_start > budget_s:
+            break
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads),
+            "kind": "oracle",
+            "sample": f"first {rows} rows of each decode projection ({', '.join(samples)}); "
+                      f"float64 numpy unpack + matmul; {total_t:.2f} s of CPU work"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part "
+              "of this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_quantized_weight_gguf_amd as qmm
+    import seeded_inputs as si
+
+    torch.cuda.set_device(0)
+    fmts, launches = decode_workload(torch, qmm, si)
+    step_bytes = float(sum(b for _, _, b, _ in launches))
+    torch.cuda.synchronize()
+
+    def step(timer=None):
+        for key, part, _, fn in launches:
+            if timer is None:
+                fn()
+            else:
+                timer.run((key, part), fn)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # Whole-step timing (no per-launch events inside).
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    # Per-launch timing over the same number of steps, for the roofline of each kernel.
+    timer = Timer(torch)
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+
+    per = {}
+    for key, part, b, _ in launches:
+        ts = timer.ms((key, part))
+        per[f"{key}:{part}"] = {"bytes": b, "us_mean": 1e3 * float(np.mean(ts)),
+                                "GBps": b / (np.mean(ts) * 1e-3) / 1e9}
+    kern = {}
+    for key, part, b, _ in launches:
+        ts = timer.ms((key, part))
+        k = kern.setdefault(key, {"bytes": 0.0, "ms": 0.0, "launches": 0})
+        k["bytes"] += b * len(ts)
+        k["ms"] += float(np.sum(ts))
+        k["launches"] += len(ts)
+    dominant = max(kern, key=lambda k: kern[k]["ms"])
+    dk = kern[dominant]
+    achieved = dk["bytes"] / (dk["ms"] * 1e-3) / 1e9
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": "decode GEMV effective HBM GB/s (% of peak) + prefill GEMM TFLOP/s, Q8_0/Q4_0",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3-8B-shaped single-token decode projections (QKV 6144x4096, O 4096x4096, "
+                               "gate+up 2x14336x4096 + SwiGLU, down 4096x14336, LM head 128256x4096), "
+                               "Q8_0 pass + Q4_0 pass, N=1",
+                   "formats": ["Q8_0", "Q4_0"], "tokens": 1, "step_bytes": int(step_bytes),
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launches_per_step": dk["launches"] // args.steps,
+                     "avg_launch_us": round(1e3 * dk["ms"] / dk["launches"], 3),
+                     "bytes_per_launch": int(dk["bytes"] / dk["launches"])},
+    }
+
+    if not args.no_prefill:
+        cases = prefill_cases(torch, qmm, si)
+        for c in cases:
+            for _ in range(3):
+                c["fn"]()
+        torch.cuda.synchronize()
+        reps = max(3, args.steps // 5)
+        tot_f, tot_ms = 0.0, 0.0
+        details = []
+        for c in cases:
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                c["fn"]()
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e) / reps
+            tot_f += c["flops"]
+            tot_ms += ms
+            details.append({"fmt": si.FMT_NAMES[c["fmt"]], "M": c["M"], "K": c["K"], "T": c["T"],
+                            "us": round(ms * 1e3, 2), "TFLOPs": round(c["flops"] / (ms * 1e-3) / 1e12, 1)})
+        tflops = tot_f / (tot_ms * 1e-3) / 1e12
+        line["prefill_gemm"] = {"value": round(tflops, 1), "unit": "TFLOP/s", "peak": FP16_MFMA_PEAK_TFLOPS,
+                                "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+                                "workload": "Q8_0+Q4_0 x {4096->14336, 14336->4096} x T in {128,2048,4096}, "
+                                            "fp16 X, fp32 Y",
+                                "cases": details}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(si)
+    if args.suite:
+        with open(args.suite, "w") as fh:
+            json.dump({"per_launch": per, "per_kernel": kern}, fh, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

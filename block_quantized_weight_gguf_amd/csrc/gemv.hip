@@ -23,9 +23,9 @@
 //     that the lanes' 16-byte reads hit distinct banks.
 //   * Q8_0: every code is converted with one signed-byte-to-float op and enters
 //     one FMA; the block scale multiplies the block's partial sum once.
-//     Q4_0: codes enter as unsigned nibbles; the -8 offset is applied once per
-//     block as -8 * sum(x_block), which keeps the per-weight cost at one
-//     convert plus one FMA.
+//     Q4_0: xor 0x88 turns each nibble n into n ^ 8, which shifted into the high
+//     half of a byte reads as the signed byte 16 * (n - 8); the same one-op
+//     signed-byte convert then gives the exact code and 1/16 joins the scale.
 //   * At the end each lane holds RU * NT partial sums that a transposing
 //     butterfly reduces across the wave with RU*NT - 1 + few exchanges.
 #include "qmm_common.hpp"
@@ -172,13 +172,11 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_valu_kernel(const uint8_t* __
                         for (int i = 0; i < 4; ++i) cw[u][i] = 0;
                     }
                 }
-                float bacc[RU][NT], sx[NT];
+                float bacc[RU][NT];
 #pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    sx[n] = 0.0f;
+                for (int u = 0; u < RU; ++u)
 #pragma unroll
-                    for (int u = 0; u < RU; ++u) bacc[u][n] = 0.0f;
-                }
+                    for (int n = 0; n < NT; ++n) bacc[u][n] = 0.0f;
                 const int xo = lane * XS_STRIDE;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -187,16 +185,17 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_valu_kernel(const uint8_t* __
                     for (int n = 0; n < NT; ++n) {
                         xl[n] = *reinterpret_cast<const float4*>(&xs[n][xo + 4 * i]);
                         xh[n] = *reinterpret_cast<const float4*>(&xs[n][xo + 16 + 4 * i]);
-                        sx[n] += ((xl[n].x + xl[n].y) + (xl[n].z + xl[n].w)) + ((xh[n].x + xh[n].y) + (xh[n].z + xh[n].w));
                     }
 #pragma unroll
                     for (int u = 0; u < RU; ++u) {
-                        const uint32_t lo = cw[u][i] & 0x0F0F0F0Fu;
-                        const uint32_t hi = (cw[u][i] >> 4) & 0x0F0F0F0Fu;
-                        const float l0 = ubyte_to_float(lo, 0), l1 = ubyte_to_float(lo, 1);
-                        const float l2 = ubyte_to_float(lo, 2), l3 = ubyte_to_float(lo, 3);
-                        const float h0 = ubyte_to_float(hi, 0), h1 = ubyte_to_float(hi, 1);
-                        const float h2 = ubyte_to_float(hi, 2), h3 = ubyte_to_float(hi, 3);
+                        // n ^ 8 in the high half of a byte is the signed byte 16 * (n - 8).
+                        const uint32_t t = cw[u][i] ^ 0x88888888u;
+                        const uint32_t lo = (t << 4) & 0xF0F0F0F0u;
+                        const uint32_t hi = t & 0xF0F0F0F0u;
+                        const float l0 = sbyte_to_float(lo, 0), l1 = sbyte_to_float(lo, 1);
+                        const float l2 = sbyte_to_float(lo, 2), l3 = sbyte_to_float(lo, 3);
+                        const float h0 = sbyte_to_float(hi, 0), h1 = sbyte_to_float(hi, 1);
+                        const float h2 = sbyte_to_float(hi, 2), h3 = sbyte_to_float(hi, 3);
 #pragma unroll
                         for (int n = 0; n < NT; ++n) {
                             float a = bacc[u][n];
@@ -212,11 +211,11 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_valu_kernel(const uint8_t* __
                         }
                     }
                 }
+                // The codes entered as 16 * (n - 8); 1/16 is folded into the scale (exact).
 #pragma unroll
                 for (int u = 0; u < RU; ++u)
 #pragma unroll
-                    for (int n = 0; n < NT; ++n)
-                        acc[u][n] = fmaf(d[u], fmaf(-8.0f, sx[n], bacc[u][n]), acc[u][n]);
+                    for (int n = 0; n < NT; ++n) acc[u][n] = fmaf(d[u] * 0.0625f, bacc[u][n], acc[u][n]);
             }
         } else {  // F16: lane l reads 16-byte chunks l, l+64, l+128, l+192 of the row slice
 #pragma unroll
