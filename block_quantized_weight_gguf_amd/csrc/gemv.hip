@@ -28,7 +28,7 @@
 //     signed-byte convert then gives the exact code and 1/16 joins the scale.
 //   * At the end each lane holds RU * NT partial sums that a transposing
 //     butterfly reduces across the wave with RU*NT - 1 + few exchanges.
-#include "qmm_common.hpp"
+#include "gemv_block.hpp"
 #include "qmm_internal.hpp"
 
 namespace qmm {
@@ -36,7 +36,6 @@ namespace qmm {
 constexpr int GV_THREADS = 256;
 constexpr int GV_WAVES = GV_THREADS / kWave;
 constexpr int GV_SLICE = 64;    // blocks per K slice; lane l handles block l
-constexpr int XS_STRIDE = 36;   // floats per block in the LDS copy of x (32 + 4 padding)
 
 template <int FMT, int NT, int R, bool GATED>
 struct GemvCfg {
@@ -53,9 +52,9 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_valu_kernel(const uint8_t* __
                                                                 const uint8_t* __restrict__ Wu,
                                                                 const float* __restrict__ x,
                                                                 float* __restrict__ y, int M, int K,
-                                                                int64_t ldx, int64_t ldy) {
+                                                                int64_t ldx, int64_t ldy, int row_begin) {
     using C = GemvCfg<FMT, NT, R, GATED>;
-    constexpr int BB = C::BB, RU = C::RU, NTP = C::NTP, V = C::V;
+    constexpr int BB = C::BB, RU = C::RU;
     __shared__ __align__(16) float xs[NT][C::XS];
     __shared__ __align__(16) uint8_t ws[(FMT == 1) ? 1 : GV_WAVES][(FMT == 1) ? 1 : RU][C::ROWBUF];
 
@@ -66,7 +65,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_valu_kernel(const uint8_t* __
     const int wave = threadIdx.x / kWave;
     const int nb = K / kQK;
     const int64_t rb = static_cast<int64_t>(nb) * BB;
-    const int row0 = blockIdx.x * (GV_WAVES * R) + wave * R;
+    const int row0 = row_begin + blockIdx.x * (GV_WAVES * R) + wave * R;
 
     float acc[RU][NT];
 #pragma unroll
@@ -95,127 +94,28 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_valu_kernel(const uint8_t* __
                 const int r = row0 + (u % R);
                 if (r < M) {
                     const bool up = GATED && u >= R;
-                    const uint8_t* base = up ? Wu : Wg;
-                    stage_bytes(base + r * rb + static_cast<int64_t>(s0) * BB, sb * BB, ws[wave][u],
-                                base + static_cast<int64_t>(M) * rb, lane, kWave);
+                    stage_bytes(up ? Wu : Wg, r * rb + static_cast<int64_t>(s0) * BB, sb * BB, ws[wave][u],
+                                static_cast<int64_t>(M) * rb, lane, kWave);
                 }
             }
         }
         __syncthreads();
 
-        if constexpr (FMT == 8) {
+        if constexpr (FMT != 1) {
             if (lane < sb) {
-                uint32_t qw[RU][8];
-                float d[RU];
+                // Rows past the end decode stale LDS bytes; their sums are never stored.
+                const uint8_t* buf[RU];
+                int off[RU];
 #pragma unroll
                 for (int u = 0; u < RU; ++u) {
-                    const int r = row0 + (u % R);
-                    if (r < M) {
-                        const int sh = static_cast<int>((r * rb + static_cast<int64_t>(s0) * BB) & 15);
-                        const uint8_t* p = ws[wave][u] + sh + lane * BB;
-                        d[u] = half_bits_to_float(lds_read_u16(p));
-                        lds_read_dwords<8>(p + 2, qw[u]);
-                    } else {
-                        d[u] = 0.0f;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) qw[u][i] = 0;
-                    }
+                    const int r = min(row0 + (u % R), M - 1);
+                    buf[u] = ws[wave][u];
+                    off[u] = static_cast<int>((r * rb + static_cast<int64_t>(s0) * BB) & 15) + lane * BB;
                 }
-                float bacc[RU][NT];
+                const float* xb[NT];
 #pragma unroll
-                for (int u = 0; u < RU; ++u)
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) bacc[u][n] = 0.0f;
-                const int xo = lane * XS_STRIDE;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    float4 xv[NT];
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) xv[n] = *reinterpret_cast<const float4*>(&xs[n][xo + 4 * i]);
-#pragma unroll
-                    for (int u = 0; u < RU; ++u) {
-                        const float w0 = sbyte_to_float(qw[u][i], 0);
-                        const float w1 = sbyte_to_float(qw[u][i], 1);
-                        const float w2 = sbyte_to_float(qw[u][i], 2);
-                        const float w3 = sbyte_to_float(qw[u][i], 3);
-#pragma unroll
-                        for (int n = 0; n < NT; ++n) {
-                            float a = bacc[u][n];
-                            a = fmaf(w0, xv[n].x, a);
-                            a = fmaf(w1, xv[n].y, a);
-                            a = fmaf(w2, xv[n].z, a);
-                            a = fmaf(w3, xv[n].w, a);
-                            bacc[u][n] = a;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < RU; ++u)
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) acc[u][n] = fmaf(d[u], bacc[u][n], acc[u][n]);
-            }
-        } else if constexpr (FMT == 2) {
-            if (lane < sb) {
-                uint32_t cw[RU][4];
-                float d[RU];
-#pragma unroll
-                for (int u = 0; u < RU; ++u) {
-                    const int r = row0 + (u % R);
-                    if (r < M) {
-                        const int sh = static_cast<int>((r * rb + static_cast<int64_t>(s0) * BB) & 15);
-                        const uint8_t* p = ws[wave][u] + sh + lane * BB;
-                        d[u] = half_bits_to_float(lds_read_u16(p));
-                        lds_read_dwords<4>(p + 2, cw[u]);
-                    } else {
-                        d[u] = 0.0f;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) cw[u][i] = 0;
-                    }
-                }
-                float bacc[RU][NT];
-#pragma unroll
-                for (int u = 0; u < RU; ++u)
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) bacc[u][n] = 0.0f;
-                const int xo = lane * XS_STRIDE;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float4 xl[NT], xh[NT];
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) {
-                        xl[n] = *reinterpret_cast<const float4*>(&xs[n][xo + 4 * i]);
-                        xh[n] = *reinterpret_cast<const float4*>(&xs[n][xo + 16 + 4 * i]);
-                    }
-#pragma unroll
-                    for (int u = 0; u < RU; ++u) {
-                        // n ^ 8 in the high half of a byte is the signed byte 16 * (n - 8).
-                        const uint32_t t = cw[u][i] ^ 0x88888888u;
-                        const uint32_t lo = (t << 4) & 0xF0F0F0F0u;
-                        const uint32_t hi = t & 0xF0F0F0F0u;
-                        const float l0 = sbyte_to_float(lo, 0), l1 = sbyte_to_float(lo, 1);
-                        const float l2 = sbyte_to_float(lo, 2), l3 = sbyte_to_float(lo, 3);
-                        const float h0 = sbyte_to_float(hi, 0), h1 = sbyte_to_float(hi, 1);
-                        const float h2 = sbyte_to_float(hi, 2), h3 = sbyte_to_float(hi, 3);
-#pragma unroll
-                        for (int n = 0; n < NT; ++n) {
-                            float a = bacc[u][n];
-                            a = fmaf(l0, xl[n].x, a);
-                            a = fmaf(l1, xl[n].y, a);
-                            a = fmaf(l2, xl[n].z, a);
-                            a = fmaf(l3, xl[n].w, a);
-                            a = fmaf(h0, xh[n].x, a);
-                            a = fmaf(h1, xh[n].y, a);
-                            a = fmaf(h2, xh[n].z, a);
-                            a = fmaf(h3, xh[n].w, a);
-                            bacc[u][n] = a;
-                        }
-                    }
-                }
-                // The codes entered as 16 * (n - 8); 1/16 is folded into the scale (exact).
-#pragma unroll
-                for (int u = 0; u < RU; ++u)
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) acc[u][n] = fmaf(d[u] * 0.0625f, bacc[u][n], acc[u][n]);
+                for (int n = 0; n < NT; ++n) xb[n] = &xs[n][lane * XS_STRIDE];
+                block_fma<FMT, RU, NT>(buf, off, xb, acc);
             }
         } else {  // F16: lane l reads 16-byte chunks l, l+64, l+128, l+192 of the row slice
 #pragma unroll
@@ -260,74 +160,68 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_valu_kernel(const uint8_t* __
         }
     }
 
-    // Reduce the RU x NT partial sums across the wave; lane l ends with index l / (64/V).
-    float v[V];
-#pragma unroll
-    for (int u = 0; u < RU; ++u)
-#pragma unroll
-        for (int n = 0; n < NTP; ++n) v[u * NTP + n] = (n < NT) ? acc[u][n < NT ? n : 0] : 0.0f;
-    wave_reduce_transpose<V>(v, lane);
-    constexpr int LPI = kWave / V;  // lanes per reduced index
-    const int idx = lane / LPI;
-    const bool holder = (lane % LPI) == 0;
-    const int u = idx / NTP;
-    const int n = idx - u * NTP;
-    if constexpr (!GATED) {
-        const int r = row0 + u;
-        if (holder && n < NT && r < M) y[n * ldy + r] = v[0];
-    } else {
-        const float upv = __shfl(v[0], (lane + R * NTP * LPI) & (kWave - 1), kWave);
-        const int r = row0 + u;
-        if (holder && u < R && n < NT && r < M) y[n * ldy + r] = silu(v[0]) * upv;
-    }
+    reduce_store<R, RU, NT, GATED>(acc, lane, row0, M, y, ldy);
 }
 
 template <int FMT, int NT, bool GATED>
 static void launch_fmt_nt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
-                          int64_t chunks, hipStream_t s) {
+                          int64_t chunks, int64_t row_begin, hipStream_t s) {
     constexpr int R = (FMT == 1) ? 2 : 4;
-    const dim3 grid(static_cast<unsigned>((M + GV_WAVES * R - 1) / (GV_WAVES * R)), static_cast<unsigned>(chunks));
+    const int64_t rows = M - row_begin;
+    const dim3 grid(static_cast<unsigned>((rows + GV_WAVES * R - 1) / (GV_WAVES * R)), static_cast<unsigned>(chunks));
     hipLaunchKernelGGL((gemv_valu_kernel<FMT, NT, R, GATED>), grid, dim3(GV_THREADS), 0, s,
                        static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), x, y,
-                       static_cast<int>(M), static_cast<int>(K), K, M);
+                       static_cast<int>(M), static_cast<int>(K), K, M, static_cast<int>(row_begin));
 }
 
 template <int FMT, bool GATED>
 static void launch_fmt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, int NT,
-                       int64_t chunks, hipStream_t s) {
+                       int64_t chunks, int64_t row_begin, hipStream_t s) {
     switch (NT) {
-        case 1: launch_fmt_nt<FMT, 1, GATED>(W, Wu, x, y, M, K, chunks, s); break;
-        case 2: launch_fmt_nt<FMT, 2, GATED>(W, Wu, x, y, M, K, chunks, s); break;
-        case 3: launch_fmt_nt<FMT, 3, GATED>(W, Wu, x, y, M, K, chunks, s); break;
-        default: launch_fmt_nt<FMT, 4, GATED>(W, Wu, x, y, M, K, chunks, s); break;
+        case 1: launch_fmt_nt<FMT, 1, GATED>(W, Wu, x, y, M, K, chunks, row_begin, s); break;
+        case 2: launch_fmt_nt<FMT, 2, GATED>(W, Wu, x, y, M, K, chunks, row_begin, s); break;
+        case 3: launch_fmt_nt<FMT, 3, GATED>(W, Wu, x, y, M, K, chunks, row_begin, s); break;
+        default: launch_fmt_nt<FMT, 4, GATED>(W, Wu, x, y, M, K, chunks, row_begin, s); break;
     }
 }
 
-static void launch_any(int fmt, bool gated, const void* W, const void* Wu, const float* x, float* y, int64_t M,
-                       int64_t K, int NT, int64_t chunks, hipStream_t s) {
+void launch_gemv_sliced(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                        int NT, int64_t chunks, int64_t row_begin, hipStream_t s) {
+    const bool gated = Wu != nullptr;
     if (gated) {
-        if (fmt == 8) launch_fmt<8, true>(W, Wu, x, y, M, K, NT, chunks, s);
-        else if (fmt == 2) launch_fmt<2, true>(W, Wu, x, y, M, K, NT, chunks, s);
-        else launch_fmt<1, true>(W, Wu, x, y, M, K, NT, chunks, s);
+        if (fmt == 8) launch_fmt<8, true>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
+        else if (fmt == 2) launch_fmt<2, true>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
+        else launch_fmt<1, true>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
     } else {
-        if (fmt == 8) launch_fmt<8, false>(W, Wu, x, y, M, K, NT, chunks, s);
-        else if (fmt == 2) launch_fmt<2, false>(W, Wu, x, y, M, K, NT, chunks, s);
-        else launch_fmt<1, false>(W, Wu, x, y, M, K, NT, chunks, s);
+        if (fmt == 8) launch_fmt<8, false>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
+        else if (fmt == 2) launch_fmt<2, false>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
+        else launch_fmt<1, false>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
     }
 }
 
 hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M,
                             int64_t K, int64_t N, hipStream_t s) {
-    const bool gated = Wu != nullptr;
-    // Tokens go 4 per pass (grid.y indexes the pass); a remainder pass takes N % 4.
-    constexpr int64_t kMaxChunks = 65535;
     int64_t done = 0;
+    // Block formats: the streaming kernel, up to 4 tokens per pass, as many tokens per
+    // pass as its LDS copy of x allows; a final row it leaves is done by the sliced kernel.
+    while (done < N) {
+        int nt = static_cast<int>(std::min<int64_t>(4, N - done));
+        int64_t rows = 0;
+        while (nt > 0 && (rows = launch_gemv_stream(fmt, W, Wu, x + done * K, y + done * M, M, K, nt, s)) == 0) --nt;
+        if (nt == 0) break;
+        if (rows < M) launch_gemv_sliced(fmt, W, Wu, x + done * K, y + done * M, M, K, nt, 1, rows, s);
+        done += nt;
+    }
+    // F16, or x too large for LDS: the sliced kernel, 4 tokens per pass (grid.y
+    // indexes the pass) and a remainder pass.
+    constexpr int64_t kMaxChunks = 65535;
     while (N - done >= 4) {
         const int64_t chunks = std::min<int64_t>((N - done) / 4, kMaxChunks);
-        launch_any(fmt, gated, W, Wu, x + done * K, y + done * M, M, K, 4, chunks, s);
+        launch_gemv_sliced(fmt, W, Wu, x + done * K, y + done * M, M, K, 4, chunks, 0, s);
         done += 4 * chunks;
     }
-    if (N - done > 0) launch_any(fmt, gated, W, Wu, x + done * K, y + done * M, M, K, static_cast<int>(N - done), 1, s);
+    if (N - done > 0)
+        launch_gemv_sliced(fmt, W, Wu, x + done * K, y + done * M, M, K, static_cast<int>(N - done), 1, 0, s);
     return hipGetLastError();
 }
 

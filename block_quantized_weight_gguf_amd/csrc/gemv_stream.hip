@@ -1,0 +1,262 @@
+// Streaming decode GEMV for the block formats (Q8_0, Q4_0), a few tokens per pass.
+//
+// Single-token decode is bound by the weight stream ("EdgeRunner Core
+// Architecture", section 3.4 Tier 1 and section 15 item 2: the raw blocks are the
+// only large operand), so this kernel is organised to keep HBM busy with as few
+// instructions per byte as possible:
+//   * One 8-wave workgroup per CU (LDS-limited).  x (all K, NT tokens) is copied
+//     into LDS once, each 32-float block padded to 36 floats so that the lanes'
+//     16-byte reads hit distinct banks; after that single barrier the 8 waves
+//     never synchronise again.
+//   * Each wave walks a list of tasks.  A task is R rows (2R row units when gated:
+//     R gate rows and the same R up rows) x one K slice of 64*BPL blocks (BPL = 1
+//     for Q8_0, 2 for Q4_0, so a row slice is ~2.2 KB either way).  Each row
+//     slice is contiguous in HBM: it is fetched with coalesced, non-temporal
+//     16-byte loads (SGPR base + lane offset), parked in the wave's private LDS
+//     buffer, and re-read by each lane as "its" block at any byte offset (blocks
+//     are only 2-byte aligned).
+//   * All task bookkeeping (row, slice, base addresses, byte counts) is
+//     wave-uniform and lives in scalar registers; the vector units only decode
+//     and multiply.
+//   * Software pipeline: the loads of task t+1 are issued before task t is
+//     decoded, so every wave keeps a task in flight while it computes.
+//   * The host keeps every 16-byte chunk the kernel reads inside the weight
+//     buffer: when the matrix size is not a multiple of 16 bytes, the last row is
+//     left to the sliced kernel, so this one never needs a tail path.
+//   * A row group's partial sums stay in registers across its K slices and are
+//     reduced across the wave once, with a transposing butterfly.
+#include "gemv_block.hpp"
+#include "qmm_internal.hpp"
+
+namespace qmm {
+
+
+template <int FMT>
+struct StreamGeom {
+    static constexpr int BB = Fmt<FMT>::BB;
+    static constexpr int BPL = (FMT == 2) ? 2 : 1;            // blocks per lane per row slice
+    static constexpr int SLICE = kWave * BPL;                  // blocks per K slice
+    static constexpr int CPR = (SLICE * BB + 15) / 16 + 1;     // 16-byte chunks per row slice, incl. shift
+    static constexpr int LPR = (CPR + kWave - 1) / kWave;      // loads per lane per row slice
+    static constexpr int ROWBUF = (SLICE * BB + 32 + 15) / 16 * 16;  // staged bytes per row unit
+    static_assert(16 * CPR <= ROWBUF, "staging geometry");
+};
+
+// Wave-level ordering of LDS writes and reads: the hardware executes one wave's
+// LDS operations in order; these fences stop the compiler from reordering them.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int FMT, int NT, int R, bool GATED, int WAVES, int D>
+__global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* __restrict__ Wg,
+                                                                  const uint8_t* __restrict__ Wu,
+                                                                  const float* __restrict__ x,
+                                                                  float* __restrict__ y, int M, int K,
+                                                                  int64_t ldx, int64_t ldy, int xs_bytes) {
+    using G = StreamGeom<FMT>;
+    constexpr int BB = G::BB, BPL = G::BPL, SLICE = G::SLICE, CPR = G::CPR, LPR = G::LPR, ROWBUF = G::ROWBUF;
+    constexpr int RU = GATED ? 2 * R : R;
+    extern __shared__ __align__(16) uint8_t smem[];
+    float* xs = reinterpret_cast<float*>(smem);
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int nb = K / kQK;
+    const int xstride = nb * XS_STRIDE;  // floats per token in LDS
+    const int64_t rb = static_cast<int64_t>(nb) * BB;
+
+    uint8_t* my = smem + xs_bytes + wave * (RU * ROWBUF);
+    const int ns = (nb + SLICE - 1) / SLICE;
+    const int ngroups = (M + R - 1) / R;
+    const int nw = gridDim.x * WAVES;
+    const int wid = blockIdx.x * WAVES + wave;
+    const int my_groups = wid < ngroups ? (ngroups - 1 - wid) / nw + 1 : 0;
+    const int ntask = my_groups * ns;
+
+    uint4 regs[D][RU][LPR];
+    // Loads of task t: for each row unit, the chunks [0, nch) of its 16-byte aligned
+    // slice.  Every lane loads on every step (chunk index clamped to nch - 1), so no
+    // load is predicated: a predicated load would have to be merged with the
+    // register's old value, which waits for the load and defeats the pipeline.
+    // The last chunk may extend up to 15 bytes past the slice; the host guarantees
+    // those bytes lie inside the weight buffer.
+    auto issue = [&](int t, uint4 (&rg)[RU][LPR]) {
+        const int gi = t / ns;
+        const int s = t - gi * ns;
+        const int g = wid + gi * nw;
+        const int s0 = s * SLICE;
+        const int sb = min(SLICE, nb - s0);
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            // Rows past the end re-read the last row (in bounds); their sums are never stored.
+            const int row = min(g * R + (u % R), M - 1);
+            const uint8_t* wbase = (GATED && u >= R) ? Wu : Wg;
+            const int64_t off = row * rb + static_cast<int64_t>(s0) * BB;
+            const int64_t a = off & ~int64_t(15);
+            const int nch = static_cast<int>((off - a) + static_cast<int64_t>(sb) * BB + 15) >> 4;
+            const uint8_t* src = wbase + a;
+#pragma unroll
+            for (int kk = 0; kk < LPR; ++kk) {
+                const uint32_t j = static_cast<uint32_t>(min(lane + kWave * kk, nch - 1));
+                rg[u][kk] = load16_nt(src + 16u * j);
+            }
+        }
+    };
+
+    float acc[RU][NT];
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[u][n] = 0.0f;
+
+    // The first D tasks' weight loads go out before x is staged: they do not depend on it.
+#pragma unroll
+    for (int q = 0; q < D; ++q)
+        if (q < ntask) issue(q, regs[q]);
+
+    // x -> LDS once: NT tokens x nb blocks, 8 float4 per block.
+    for (int i = threadIdx.x; i < NT * nb * 8; i += WAVES * kWave) {
+        const int n = i / (nb * 8);
+        const int j = i - n * (nb * 8);
+        const float4 v = *reinterpret_cast<const float4*>(x + n * ldx + 4 * static_cast<int64_t>(j));
+        *reinterpret_cast<float4*>(xs + n * xstride + (j >> 3) * XS_STRIDE + 4 * (j & 7)) = v;
+    }
+    __syncthreads();
+
+    for (int t0 = 0; t0 < ntask; t0 += D) {
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+        const int t = t0 + q;
+        if (t >= ntask) break;
+        wave_lds_sync();  // the previous task's LDS reads are complete
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+#pragma unroll
+            for (int kk = 0; kk < LPR; ++kk) {
+                const int j = lane + kWave * kk;
+                if (kk < LPR - 1 || j < CPR)
+                    *reinterpret_cast<uint4*>(my + u * ROWBUF + 16 * j) = regs[q][u][kk];
+            }
+        wave_lds_sync();
+        if (t + D < ntask) issue(t + D, regs[q]);
+
+        const int gi = t / ns;
+        const int s = t - gi * ns;
+        const int g = wid + gi * nw;
+        const int s0 = s * SLICE;
+        const int sb = min(SLICE, nb - s0);
+        const uint8_t* buf[RU];
+        int sh[RU];
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            const int row = min(g * R + (u % R), M - 1);
+            buf[u] = my + u * ROWBUF;
+            sh[u] = static_cast<int>((row * rb + static_cast<int64_t>(s0) * BB) & 15);
+        }
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+            const int blk = lane + kWave * b;
+            if (blk < sb) {
+                int off[RU];
+#pragma unroll
+                for (int u = 0; u < RU; ++u) off[u] = sh[u] + blk * BB;
+                const float* xb[NT];
+#pragma unroll
+                for (int n = 0; n < NT; ++n) xb[n] = xs + n * xstride + (s0 + blk) * XS_STRIDE;
+                block_fma<FMT, RU, NT>(buf, off, xb, acc);
+            }
+        }
+        if (s == ns - 1) {
+            reduce_store<R, RU, NT, GATED>(acc, lane, g * R, M, y, ldy);
+#pragma unroll
+            for (int u = 0; u < RU; ++u)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[u][n] = 0.0f;
+        }
+    }
+    }
+}
+
+// Returns the number of leading rows launched (M, or M - 1 when the matrix size is
+// not a multiple of 16 bytes: the final row's last 16-byte chunk would cross the
+// end of the buffer, so that row is left to the caller), or 0 when this kernel
+// does not apply (LDS too small for x, or a single such row).
+template <int FMT, int NT, int R, bool GATED, int WAVES, int D>
+static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                        hipStream_t s) {
+    const int64_t ldy = M;
+    using G = StreamGeom<FMT>;
+    constexpr int RU = GATED ? 2 * R : R;
+    const int64_t nb = K / 32;
+    const int64_t rb = nb * G::BB;
+    if ((M * rb) % 16 != 0) {
+        if (M < 2) return 0;
+        M -= 1;  // every chunk of the first M - 1 rows ends at most 15 bytes into the last row
+    }
+    const int64_t xs_bytes = ((NT * nb * XS_STRIDE * 4) + 15) / 16 * 16;
+    const int64_t lds = xs_bytes + static_cast<int64_t>(WAVES) * RU * G::ROWBUF;
+    constexpr int64_t kMaxLds = 160 * 1024;
+    if (lds > kMaxLds) return 0;
+    auto kern = gemv_stream_kernel<FMT, NT, R, GATED, WAVES, D>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(kMaxLds));
+        attr_set = true;
+    }
+    const int64_t ngroups = (M + R - 1) / R;
+    const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(16 / WAVES, kMaxLds / lds));
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((ngroups + WAVES - 1) / WAVES, 256 * per_cu));
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(WAVES * kWave), static_cast<size_t>(lds), s,
+                       static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), x, y, static_cast<int>(M),
+                       static_cast<int>(K), K, ldy, static_cast<int>(xs_bytes));
+    return M;
+}
+
+// Variant choice (measured on MI355X at the Llama-3-8B and SmolLM2-135M shapes):
+// the plain GEMV runs 16 waves per workgroup (8 for 3-4 tokens) with 2 rows per
+// task for large outputs and 1 row otherwise; the gated kernel runs 8 waves with
+// 1 gate + 1 up row per task, prefetching two tasks ahead when each wave owns
+// only a few tasks, so that the whole matrix is in flight at once.
+template <int FMT, int NT>
+static int64_t launch_nt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, hipStream_t s) {
+    const int64_t nb = K / 32;
+    const int64_t slices = (nb + StreamGeom<FMT>::SLICE - 1) / StreamGeom<FMT>::SLICE;
+    if (Wu) {
+        const bool deep = (M * slices) / (256 * 8) <= 2;  // tasks per wave
+        return deep ? launch_t<FMT, NT, 1, true, 8, 2>(W, Wu, x, y, M, K, s)
+                    : launch_t<FMT, NT, 1, true, 8, 1>(W, Wu, x, y, M, K, s);
+    }
+    // 16 waves per workgroup cap a wave at 128 VGPRs; 3-4 tokens need more.
+    constexpr int PW = NT <= 2 ? 16 : 8;
+    if (M >= 16384) return launch_t<FMT, NT, 2, false, PW, 1>(W, Wu, x, y, M, K, s);
+    return launch_t<FMT, NT, 1, false, PW, 1>(W, Wu, x, y, M, K, s);
+}
+
+int64_t launch_gemv_stream(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                        int NT, hipStream_t s) {
+    if (fmt == 8) {
+        switch (NT) {
+            case 1: return launch_nt<8, 1>(W, Wu, x, y, M, K, s);
+            case 2: return launch_nt<8, 2>(W, Wu, x, y, M, K, s);
+            case 3: return launch_nt<8, 3>(W, Wu, x, y, M, K, s);
+            default: return launch_nt<8, 4>(W, Wu, x, y, M, K, s);
+        }
+    }
+    if (fmt == 2) {
+        switch (NT) {
+            case 1: return launch_nt<2, 1>(W, Wu, x, y, M, K, s);
+            case 2: return launch_nt<2, 2>(W, Wu, x, y, M, K, s);
+            case 3: return launch_nt<2, 3>(W, Wu, x, y, M, K, s);
+            default: return launch_nt<2, 4>(W, Wu, x, y, M, K, s);
+        }
+    }
+    return 0;
+}
+
+}  // namespace qmm

@@ -57,35 +57,50 @@ __device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32
     return __builtin_amdgcn_alignbyte(hi, lo, sh);
 }
 
-// Copy the global bytes [src, src + n) to LDS such that byte src + i lands at
-// dst + (src & 15) + i.  Whole 16-byte aligned chunks are moved with one 16-byte
-// load each; nothing at or beyond `end` is read (the chunk holding `end`, if any,
-// is copied byte by byte).  Bytes before src inside the first aligned chunk are
-// read as well; callers guarantee they lie at or after the buffer base (the
-// weight buffer is 16-byte aligned).  Work is spread over `nl` lanes.
-__device__ __forceinline__ void stage_bytes(const uint8_t* src, int n, uint8_t* dst,
-                                            const uint8_t* end, int lane, int nl) {
-    const uint8_t* a = reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(src) & ~uintptr_t(15));
-    const int total = static_cast<int>(src + n - a);
+// Address arithmetic in these helpers is done on integer byte offsets from the
+// original (global or LDS) base pointers, never by casting a pointer to an
+// integer: that keeps the loads in their own address space (global_load /
+// ds_read) instead of flat loads, which would also stall every LDS wait.
+
+// Copy the global bytes [base + off, base + off + n) to LDS such that byte
+// base + off + i lands at dst + (off & 15) + i.  Whole 16-byte aligned chunks
+// (base is 16-byte aligned) move with one 16-byte load each; nothing at or
+// beyond base + end is read (a chunk crossing it is fetched in dword and
+// halfword pieces; buffer sizes are multiples of 2).  Bytes before off inside
+// the first chunk are read too and lie at or after base.  Work is spread over
+// `nl` lanes.
+__device__ __forceinline__ void stage_bytes(const uint8_t* base, int64_t off, int n, uint8_t* dst, int64_t end,
+                                            int lane, int nl) {
+    const int64_t a = off & ~int64_t(15);
+    const int total = static_cast<int>(off + n - a);
     const int chunks = (total + 15) >> 4;
     for (int c = lane; c < chunks; c += nl) {
-        const uint8_t* p = a + 16 * c;
+        const int64_t p = a + 16 * c;
+        uint4 v;
         if (p + 16 <= end) {
-            *reinterpret_cast<uint4*>(dst + 16 * c) = load16_nt(p);
+            v = load16_nt(base + p);
         } else {
-            for (int i = 0; i < 16; ++i) dst[16 * c + i] = (p + i < end) ? p[i] : uint8_t(0);
+            uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t q = p + 4 * i;
+                if (q + 4 <= end) w[i] = *reinterpret_cast<const uint32_t*>(base + q);
+                else if (q + 2 <= end) w[i] = *reinterpret_cast<const uint16_t*>(base + q);
+            }
+            v = make_uint4(w[0], w[1], w[2], w[3]);
         }
+        *reinterpret_cast<uint4*>(dst + 16 * c) = v;
     }
 }
 
-// Read `ND` dwords starting at the 2-byte aligned LDS address p, realigned so
-// that out[i] holds bytes p+4i .. p+4i+3.  Reads ND+1 dwords from the enclosing
-// 4-byte aligned address (the caller keeps 4 bytes of slack after the data).
+// Read `ND` dwords starting at LDS byte offset `off` (2-byte aligned) from the
+// 4-byte aligned LDS buffer `buf`, realigned so that out[i] holds bytes
+// off+4i .. off+4i+3.  Reads ND+1 dwords from the enclosing 4-byte aligned
+// offset (the caller keeps 4 bytes of slack after the data).
 template <int ND>
-__device__ __forceinline__ void lds_read_dwords(const uint8_t* p, uint32_t (&out)[ND]) {
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(p);
-    const uint32_t* base = reinterpret_cast<const uint32_t*>(addr & ~uintptr_t(3));
-    const uint32_t sh = static_cast<uint32_t>(addr & 3);
+__device__ __forceinline__ void lds_read_dwords(const uint8_t* buf, int off, uint32_t (&out)[ND]) {
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(buf + (off & ~3));
+    const uint32_t sh = static_cast<uint32_t>(off & 3);
     uint32_t d[ND + 1];
 #pragma unroll
     for (int i = 0; i <= ND; ++i) d[i] = base[i];
@@ -93,8 +108,8 @@ __device__ __forceinline__ void lds_read_dwords(const uint8_t* p, uint32_t (&out
     for (int i = 0; i < ND; ++i) out[i] = align_bytes(d[i + 1], d[i], sh);
 }
 
-__device__ __forceinline__ uint32_t lds_read_u16(const uint8_t* p) {
-    return *reinterpret_cast<const uint16_t*>(p);
+__device__ __forceinline__ uint32_t lds_read_u16(const uint8_t* buf, int off) {
+    return *reinterpret_cast<const uint16_t*>(buf + off);
 }
 
 // silu(z) = z / (1 + e^-z)  ("EdgeRunner Core Architecture", section 8 SwiGLU FFN).

@@ -16,6 +16,17 @@ hipError_t launch_dequant(int fmt, const void* W, float* out, int64_t M, int64_t
 hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float* x, float* y,
                             int64_t M, int64_t K, int64_t N, hipStream_t s);
 
+// Streaming GEMV for Q8_0 / Q4_0 with NT <= 4 tokens in one pass.  Returns the
+// number of leading rows it launched (M or M - 1); 0 means nothing was launched
+// (format or LDS footprint of x does not fit).
+int64_t launch_gemv_stream(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                           int NT, hipStream_t s);
+
+// Sliced GEMV for rows [row_begin, M), NT <= 4 tokens per pass, `chunks` passes
+// of NT tokens (grid.y).  Handles every format and every size.
+void launch_gemv_sliced(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                        int NT, int64_t chunks, int64_t row_begin, hipStream_t s);
+
 // fp16-MFMA GEMM: Y[t][m] = sum_k W[m][k] X[t][k]; X is fp16 (x_is_f32 = false) or fp32
 // rounded to fp16 while staging (x_is_f32 = true).  Wu != nullptr selects the SwiGLU epilogue.
 hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32,
