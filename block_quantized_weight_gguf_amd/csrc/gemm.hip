@@ -318,6 +318,8 @@ static void launch_f(const void* W, const void* Wu, const void* X, bool xf32, fl
 
 hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32, float* Y,
                             int64_t M, int64_t K, int64_t T, hipStream_t s) {
+    // The tiled kernel covers 16-byte aligned rows; this one covers every other shape.
+    if (launch_gemm_tile(fmt, W, Wu, X, x_is_f32, Y, M, K, T, s)) return hipGetLastError();
     // grid.y is limited to 65535 tiles of 256 tokens; larger T is split into passes.
     constexpr int64_t kMaxT = 65535LL * GM_BN;
     const size_t xe = x_is_f32 ? 4 : 2;

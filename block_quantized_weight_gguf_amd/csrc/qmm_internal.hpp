@@ -32,4 +32,10 @@ void launch_gemv_sliced(int fmt, const void* W, const void* Wu, const float* x, 
 hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32,
                             float* Y, int64_t M, int64_t K, int64_t T, hipStream_t s);
 
+// Tiled fp16-MFMA GEMM (256 x 256 tiles, coalesced raw loads, fp16-domain decode).
+// Returns false, launching nothing, for shapes it does not cover (block formats
+// with K % 256 != 0).
+bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32, float* Y, int64_t M,
+                      int64_t K, int64_t T, hipStream_t s);
+
 }  // namespace qmm
