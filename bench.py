@@ -40,7 +40,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-smollm", action="store_true")
     p.add_argument("--suite", default=None, help="write per-kernel details as JSON to this path")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
     return p.parse_args()
 
 
@@ -68,8 +71,12 @@ def decode_workload(torch, qmm, si):
     H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
     dev = torch.device("cuda")
 
+    host = {}
+
     def W(fmt, M, K, seed):
-        return torch.from_numpy(si.weights(fmt, M, K, seed)).to(dev)
+        a = si.weights(fmt, M, K, seed)
+        host[(fmt, seed)] = (a, M, K)
+        return torch.from_numpy(a).to(dev)
 
     def X(n, K, seed):
         return torch.from_numpy(si.activations(n, K, seed)).to(dev)
@@ -79,11 +86,11 @@ def decode_workload(torch, qmm, si):
         f = dict(
             qkv=W(fmt, Q, H, base + 1), o=W(fmt, H, H, base + 2), g=W(fmt, I, H, base + 3),
             u=W(fmt, I, H, base + 4), d=W(fmt, H, I, base + 5), lm=W(fmt, V, H, base + 6),
-            x=X(1, H, base + 7), y_qkv=torch.empty(Q, device=dev), y_o=torch.empty(H, device=dev),
+            x=X(1, H, base + 7), x_host=si.activations(1, H, base + 7), y_qkv=torch.empty(Q, device=dev), y_o=torch.empty(H, device=dev),
             h=torch.empty(I, device=dev), y_d=torch.empty(H, device=dev), logits=torch.empty(V, device=dev))
         fmts[fmt] = f
     rb = {fmt: (lambda K, fmt=fmt: qmm.qmm_row_bytes(fmt, K)) for fmt in fmts}
-    launches = []  # (kernel key, bytes, callable)
+    launches = []  # (kernel key, part, bytes, callable)
     for fmt, f in fmts.items():
         name = si.FMT_NAMES[fmt]
         r = rb[fmt]
@@ -99,7 +106,7 @@ def decode_workload(torch, qmm, si):
             (f"gemv_{name}", "lm_head", V * r(H) + 4 * H + 4 * V,
              lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["lm"], f["x"], f["logits"], V, H, 1)),
         ]
-    return fmts, launches
+    return fmts, launches, host
 
 
 def prefill_cases(torch, qmm, si):
@@ -117,36 +124,101 @@ def prefill_cases(torch, qmm, si):
     return cases
 
 
-def cpu_baseline(si, budget_s=15.0):
-    """Float64 oracle on a bounded sample of the decode step: leading rows of each projection."""
+def cpu_baseline(host, fmts, budget_s=20.0):
+    """The float64 oracle on a bounded sample of the same decode step.
+
+    Walks the step's projections in order (Q8_0 pass, then Q4_0 pass), each on the
+    very weight bytes the GPU streamed, until about budget_s seconds of CPU work;
+    reports weight-stream GB/s like the GPU figure.
+    """
     import oracle
-    L = si.LLAMA3_8B
-    H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
-    shapes = [("qkv", Q, H), ("o", H, H), ("gate", I, H), ("up", I, H), ("down", H, I), ("lm_head", V, H)]
-    rows = 1024
     total_bytes = 0.0
     total_t = 0.0
-    t_start = time.perf_counter()
-    samples = []
-    for fmt in (si.FMT_Q8_0, si.FMT_Q4_0):
-        for name, M, K in shapes:
-            raw = si.weights(fmt, rows, K, 9000 + M)       # same shape rows, seeded
-            x = si.activations(1, K, 9001)
-            t0 = time.perf_counter()
-            oracle.matmul_ref(fmt, raw, x, rows, K)
-            dt = time.perf_counter() - t0
-            b = rows * oracle.row_bytes(fmt, K) + 4 * K + 4 * rows
-            total_bytes += b
-            total_t += dt
-            samples.append(f"{si.FMT_NAMES[fmt]}:{name}")
-        if time.perf_counter() - t_start > budget_s:
+    done = []
+    for (fmt, seed), (raw, M, K) in host.items():
+        if total_t > budget_s:
             break
+        x = fmts[fmt]["x_host"] if K == fmts[fmt]["x_host"].shape[1] else np.ones((1, K), np.float32)
+        t0 = time.perf_counter()
+        oracle.matmul_ref(fmt, raw, x, M, K)
+        total_t += time.perf_counter() - t0
+        total_bytes += raw.size + 4 * K + 4 * M
+        done.append(f"{'Q8_0' if fmt == 8 else 'Q4_0'} {M}x{K}")
     cores = len(os.sched_getaffinity(0))
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads),
             "kind": "oracle",
-            "sample": f"first {rows} rows of each decode projection ({', '.join(samples)}); "
-                      f"float64 numpy unpack + matmul; {total_t:.2f} s of CPU work"}
+            "sample": f"{len(done)} of {len(host)} weight matrices of the step, whole matrices "
+                      f"({', '.join(done)}); float64 numpy unpack + matmul; {total_t:.1f} s of CPU work"}
+
+
+def smollm2_step(torch, qmm, si, steps):
+    """SmolLM2-135M-shaped decode step (30 layers + LM head), Q8_0 and Q4_0, eager and graph-replayed."""
+    S = si.SMOLLM2_135M
+    H, I, V, Q = S["hidden"], S["intermediate"], S["vocab"], si.qkv_rows(S)
+    dev = torch.device("cuda")
+    out = {}
+    for fmt, base in ((si.FMT_Q8_0, 8000), (si.FMT_Q4_0, 8500)):
+        Ws = []
+        for layer in range(S["layers"]):
+            s0 = base + 10 * layer
+            Ws.append([torch.from_numpy(si.weights(fmt, m, k, s0 + i)).to(dev)
+                       for i, (m, k) in enumerate(((Q, H), (H, H), (I, H), (I, H), (H, I)))])
+        lm = torch.from_numpy(si.weights(fmt, V, H, base + 999)).to(dev)
+        x = torch.from_numpy(si.activations(1, H, base + 998)).to(dev)
+        yq, yo, h, yd, logits = (torch.empty(n, device=dev) for n in (Q, H, I, H, V))
+        nbytes = sum(w.numel() for ws in Ws for w in ws) + lm.numel()
+
+        def step():
+            for (wq, wo, wg, wu, wd) in Ws:
+                qmm.qmm_gemv(fmt, wq, x, yq, Q, H, 1)
+                qmm.qmm_gemv(fmt, wo, x, yo, H, H, 1)
+                qmm.qmm_gate_up_silu(fmt, wg, wu, x, h, I, H, 1)
+                qmm.qmm_gemv(fmt, wd, h, yd, H, I, 1)
+            qmm.qmm_gemv(fmt, lm, x, logits, V, H, 1)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / steps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / steps
+        out[si.FMT_NAMES[fmt]] = {"eager_tok_s": round(1e3 / eager_ms, 1), "graph_tok_s": round(1e3 / graph_ms, 1),
+                                  "graph_GBps": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),
+                                  "weight_bytes": int(nbytes)}
+    return out
+
+
+def traffic_for(kernel_file, launch_key):
+    """HBM bytes per launch from the committed counter summary, if the kernel source is unchanged."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "block_quantized_weight_gguf_amd", "csrc", kernel_file)
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        e = rec.get(launch_key)
+        if e and e.get("source_sha256") == digest:
+            return e["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    return None
 
 
 def main():
@@ -161,7 +233,16 @@ def main():
     import seeded_inputs as si
 
     torch.cuda.set_device(0)
-    fmts, launches = decode_workload(torch, qmm, si)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "copies": 5}))
+        return
+    fmts, launches, host = decode_workload(torch, qmm, si)
     step_bytes = float(sum(b for _, _, b, _ in launches))
     torch.cuda.synchronize()
 
@@ -202,9 +283,11 @@ def main():
         k["bytes"] += b * len(ts)
         k["ms"] += float(np.sum(ts))
         k["launches"] += len(ts)
-    dominant = max(kern, key=lambda k: kern[k]["ms"])
-    dk = kern[dominant]
-    achieved = dk["bytes"] / (dk["ms"] * 1e-3) / 1e9
+    # Dominant kernel: the launch with the largest share of the step (one kernel
+    # instance, as rocprofv3 names it): the Q8_0 LM-head GEMV.
+    dom = max(per, key=lambda k: per[k]["us_mean"])
+    dk = per[dom]
+    achieved = dk["bytes"] / (dk["us_mean"] * 1e-6) / 1e9
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     line = {
@@ -225,11 +308,12 @@ def main():
                                "Q8_0 pass + Q4_0 pass, N=1",
                    "formats": ["Q8_0", "Q4_0"], "tokens": 1, "step_bytes": int(step_bytes),
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "launches_per_step": dk["launches"] // args.steps,
-                     "avg_launch_us": round(1e3 * dk["ms"] / dk["launches"], 3),
-                     "bytes_per_launch": int(dk["bytes"] / dk["launches"])},
+        "roofline": {"bound": "hbm",
+                     "kernel": ("gemv_stream_kernel<8, 1, 2, false, 16, 1> (" + dom + ")") if dom == "gemv_Q8_0:lm_head" else dom,
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("gemv_stream.hip", dom),
+                     "avg_launch_us": round(dk["us_mean"], 3), "bytes_per_launch": int(dk["bytes"])},
     }
 
     if not args.no_prefill:
@@ -260,8 +344,10 @@ def main():
                                 "workload": "Q8_0+Q4_0 x {4096->14336, 14336->4096} x T in {128,2048,4096}, "
                                             "fp16 X, fp32 Y",
                                 "cases": details}
+    if not args.no_smollm:
+        line["smollm2_135m_decode_step"] = smollm2_step(torch, qmm, si, max(10, args.steps))
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(si)
+        line["cpu_baseline"] = cpu_baseline(host, fmts)
     if args.suite:
         with open(args.suite, "w") as fh:
             json.dump({"per_launch": per, "per_kernel": kern}, fh, indent=1)
