@@ -2,38 +2,49 @@
 //
 // ("alpaca.swift", Capabilities and Design: prefill GEMMs on the matrix hardware
 // with half-precision activations; "llama.cpp Metal ...", section 3.2 and P9: a
-// tiled matrix-matrix kernel above a token threshold.)  Weights are decoded from
-// their GGUF blocks into fp16 LDS tiles once per (tile, K step) and fed to
-// v_mfma_f32_16x16x32_f16.
+// tiled matrix-matrix kernel above a token threshold.)  Weights stay in their GGUF
+// blocks in HBM and are decoded to fp16 MFMA operands inside the kernel.
 //
 // Work layout (wave64, 160 KB LDS per CU, 8 XCDs):
-//   * A workgroup owns a 256 (weight rows) x 256 (tokens) output tile with 8 waves
-//     (2 per SIMD) in a 2 x 4 arrangement; each wave computes 128 x 64 outputs as
-//     8 x 4 MFMA fragments accumulating in AGPRs.
-//   * Token operands never touch LDS: each wave loads its MFMA B fragments (16
-//     contiguous bytes of one token row per lane) straight from L2 into VGPRs, one
-//     32-wide K sub-step ahead of use.
-//   * Weight operands: per K step of 64 (two blocks) the raw blocks are fetched with
-//     coalesced 16-byte loads (consecutive lanes walk one row's window).  Rows are
-//     16-byte aligned (K % 256 == 0), so a step's two-block segment sits at the same
-//     dword offset s in its window for every row.  The bytes go through a raw LDS
-//     area, then two threads per row decode one block each in the fp16 domain (a
-//     code byte c becomes the half 1024 + c via v_perm with 0x64 bytes,
-//     v_pk_add_f16 removes the offset exactly, v_pk_mul_f16 by the fp16 scale gives
-//     fp16(d*q) with a single rounding) into the fp16 weight tile (rows padded to
-//     144 bytes so each 16-lane fragment read hits distinct banks).
-//   * Pipeline with one barrier per step: during step k the waves store the raw
-//     bytes of step k+2, decode step k+1 into the other weight stage, run the MFMAs
-//     of step k, and have the raw loads of step k+3 in flight (F16 rows skip the
-//     raw area: step k copies step k+1 into the other stage).  The loop is
-//     unrolled by two so that every stage is its own LDS array and the compiler can
-//     overlap the decode with the MFMAs.
+//   * A workgroup owns a 256 (weight rows) x 256 (tokens) output tile with 4 waves,
+//     one per SIMD with the whole 512-entry register file: each wave computes 64
+//     weight rows x 256 tokens as 4 x 16 v_mfma_f32_16x16x32_f16 fragments whose
+//     256 accumulators live in AGPRs.
+//   * Both operands reach LDS by direct global->LDS DMA (global_load_lds_dwordx4):
+//     no VGPRs are spent on staging and every load instruction reads whole 128-byte
+//     lines.  Token tile: 256 rows x 64 halfs per K step, 16-byte chunks stored
+//     XOR-swizzled by row (the swizzle is applied to the source address, since the
+//     DMA writes lane L's 16 bytes at base + 16 L), so fragment reads hit distinct
+//     banks.
+//   * Block formats: a weight stage holds the raw GGUF bytes of two K steps (four
+//     blocks) of all 256 rows.  Rows are 16-byte aligned (K % 256 == 0), so the
+//     four-block segment of every row sits at the same offset (0 or 8) inside a
+//     window of whole 16-byte chunks (Q8_0: 136 bytes in 9 chunks, Q4_0: 72 bytes
+//     in 5).  Each wave then decodes its own MFMA A fragments straight from the raw
+//     bytes (each weight row belongs to one wave, so nothing is decoded twice): lane
+//     l needs 8 consecutive weights of row l % 16, i.e. the block scale and 8 code
+//     bytes (Q4_0: 8 nibbles).  Decoding is done in the fp16 domain: a
+//     code byte c becomes the half 1024 + c via v_perm with 0x64 bytes, v_pk_add_f16
+//     removes the offset exactly and v_pk_mul_f16 by the fp16 scale gives fp16(d*q)
+//     with a single rounding.  F16 weights use the token-tile layout.
+//   * Pipeline: one barrier per K step.  After it, the DMA of the next token stage
+//     (and, every second step, of the next weight stage) is issued into the buffer
+//     that every wave has finished reading, then the step's fragments are read and
+//     multiplied.  Before the next barrier each wave waits for its own DMA of the
+//     stage about to be read; the barrier makes every wave's DMA visible.  The loop
+//     is unrolled so that each stage is its own LDS array, which lets the compiler
+//     see that reads of one stage do not depend on the DMA into another.
 //   * Tile order is XCD-aware: each XCD (workgroup id % 8) takes a contiguous run
 //     of tiles, walked in groups of 4 weight-row tiles so that concurrently
 //     running tiles share both weight and token K slices in that XCD's L2.
-//   * Gated instance: the 256 tile rows are 64 gate rows, the same 64 up rows, and
-//     the next 64 of each, so each thread ends holding g and u for the same
-//     outputs and applies h = silu(g) * u before the store.
+//   * Gated instance: stage rows 0..127 hold 128 gate rows and rows 128..255 the up
+//     rows of the same outputs (so each DMA instruction reads one matrix); each wave
+//     takes 32 gate and the matching 32 up rows, so every lane ends holding g and u
+//     for the same outputs and applies h = silu(g) * u before the store.
+//   * fp32 tokens (batched decode through the MFMA path) are converted while being
+//     staged through VGPRs instead of by DMA.
+#include <type_traits>
+
 #include "qmm_common.hpp"
 #include "qmm_internal.hpp"
 
@@ -47,8 +58,7 @@ constexpr int GT_BM = 256;
 constexpr int GT_BN = 256;
 constexpr int GT_BK = 64;
 constexpr int GT_THREADS = 512;
-constexpr int GT_WLD = GT_BK + 8;          // padded weight-tile row, halfs
-constexpr int GT_RAW = 80;                 // raw staging bytes per row
+constexpr int GT_WAVES = GT_THREADS / 64;
 constexpr int GT_GROUP_M = 4;
 
 __device__ __forceinline__ uint32_t h2_bits(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
@@ -80,15 +90,58 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     return h2_bits(half2_t{static_cast<_Float16>(a), static_cast<_Float16>(b)});
 }
 
+#define QMM_G1 __attribute__((address_space(1)))
+#define QMM_L3 __attribute__((address_space(3)))
+
+// Weight stage geometry: K steps per stage, 16-byte chunks per row window, and
+// the bytes of the per-row segment one stage covers.
 template <int FMT>
-struct TileGeom {
-    // 16-byte loads per thread per step for the weights: F16 rows are 128-byte
-    // slices (8 chunks x 256 rows / 512 threads); the block formats fetch the
-    // window holding the two-block segment (68 + up to 12 bytes for Q8_0 -> 5
-    // chunks, 36 + up to 12 for Q4_0 -> 3 chunks) for every row.
-    static constexpr int CPR = (FMT == 1) ? 8 : (FMT == 8 ? 5 : 3);  // chunks per row
-    static constexpr int NLD = (GT_BM * CPR + GT_THREADS - 1) / GT_THREADS;
+struct WStage;
+template <>
+struct WStage<8> {  // Q8_0: 4 blocks = 136 bytes, in 9 chunks
+    static constexpr int KPS = 2, WCH = 9;
 };
+template <>
+struct WStage<2> {  // Q4_0: 4 blocks = 72 bytes, in 5 chunks
+    static constexpr int KPS = 2, WCH = 5;
+};
+template <>
+struct WStage<1> {  // F16: 64 halfs = 128 bytes
+    static constexpr int KPS = 1, WCH = 8;
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the LDS stages.  A release fence would wait for every
+// outstanding global->LDS DMA (they count as LDS writes), including the prefetches
+// that must stay in flight; instead each wave waits explicitly for the DMA it needs
+// (wait_vm) and for its own LDS stores (lgkmcnt), and the empty asm statements keep
+// the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Buffer resource over [base, base + bytes) (raw addressing, 32-bit data format;
+// reads past `bytes` return zeros instead of faulting).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int n = static_cast<int>(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
+}
+
+// One 16-byte buffer->LDS DMA per lane: lane L's bytes (resource + voff + soff) land
+// at lds + 16 L.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, QMM_L3 uint8_t* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (QMM_L3 void*)lds, 16, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
+}
 
 template <int FMT, bool GATED, bool XF32>
 __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __restrict__ Wg,
@@ -96,21 +149,35 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
                                                                 const void* __restrict__ Xv,
                                                                 float* __restrict__ Y, int M, int K, int T,
                                                                 int vec) {
-    __shared__ __align__(16) _Float16 Wf0[GT_BM * GT_WLD];
-    __shared__ __align__(16) _Float16 Wf1[GT_BM * GT_WLD];
-    __shared__ __align__(16) uint8_t Raw0[(FMT == 1) ? 16 : GT_BM * GT_RAW];
-    __shared__ __align__(16) uint8_t Raw1[(FMT == 1) ? 16 : GT_BM * GT_RAW];
-
-    using G = TileGeom<FMT>;
+    using G = WStage<FMT>;
     constexpr int BB = Fmt<FMT>::BB;
-    constexpr int CPR = G::CPR, NLD = G::NLD;
+    constexpr int WROW = G::WCH * 16;         // bytes per row in a weight stage
+    constexpr int WBYTES = GT_BM * WROW;      // bytes per weight stage
+    constexpr int WINST = WBYTES / 1024;      // wave-wide DMA instructions per weight stage
+    // Weight DMA instructions per wave and stage.  When the stage does not split evenly
+    // over the waves, the surplus instructions repeat the stage's last instruction
+    // (same bytes to the same place), so that every wave issues the same count:
+    // constant wait counts, no branch, and a destination the compiler can tell apart
+    // from the other stage.
+    constexpr int WPER = (WINST + GT_WAVES - 1) / GT_WAVES;
+    constexpr int KPS = G::KPS;
+    constexpr int XBYTES = GT_BN * GT_BK * 2;
+    constexpr int XINST = XBYTES / 1024 / GT_WAVES;          // token DMA instructions per wave and step
+    constexpr int XE = XF32 ? 4 : 2;          // token element bytes
+    static_assert(WINST % 2 == 0, "gate / up halves must split on instruction boundaries");
+
+    __shared__ __align__(16) uint8_t Xs0[XBYTES];
+    __shared__ __align__(16) uint8_t Xs1[XBYTES];
+    __shared__ __align__(16) uint8_t Ws0[WBYTES];
+    __shared__ __align__(16) uint8_t Ws1[WBYTES];
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave >> 1, wn = wave & 1;  // 64 weight rows x 128 tokens per wave
     const int nb = K / kQK;
     const int64_t rb = static_cast<int64_t>(nb) * BB;
-    const int nsteps = nb / 2;  // K % 64 == 0 here
+    const int nsteps = K / GT_BK;
 
     // ---- tile selection: contiguous run per XCD, grouped by GT_GROUP_M weight tiles
     const int rows_per_tile = GATED ? GT_BM / 2 : GT_BM;
@@ -129,234 +196,250 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     const int m0 = mt * rows_per_tile;
     const int t0 = tt * GT_BN;
 
-    // Tile row r -> pointer to the start of its weight row (rows past the end
-    // re-read the last row; their outputs are never stored).
-    auto row_ptr = [&](int r) -> const uint8_t* {
-        int mrow;
-        const uint8_t* base;
-        if constexpr (GATED) {
-            const int grp = r >> 6;  // 64-row groups: gate, up, gate, up
-            mrow = m0 + (grp >> 1) * 64 + (r & 63);
-            base = (grp & 1) ? Wu : Wg;
+    // ---- DMA sources: a buffer resource per operand tile (uniform) plus a 32-bit
+    // lane offset fixed for the whole K loop; the K position goes in the scalar
+    // offset.  A tile spans 256 rows, so offsets stay below 2^31 (the launcher checks).
+    // Swizzled 128-byte-row tiles (tokens, F16 weights): wave instruction n = wave + 8 i
+    // fills rows 8n .. 8n+7; lane L writes slot L & 7 of row 8n + L / 8, which holds
+    // chunk (L & 7) ^ (row & 7) of that row.
+    const int sw_chunk = (lane & 7) ^ ((lane >> 3) & 7);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(static_cast<const uint8_t*>(Xv) + static_cast<int64_t>(t0) * K * XE,
+                                                static_cast<int64_t>(T - t0) * K * XE);
+    uint32_t xoffs[XINST];
+#pragma unroll
+    for (int i = 0; i < XINST; ++i) {
+        const int R = 8 * (wave + GT_WAVES * i) + (lane >> 3);
+        xoffs[i] = static_cast<uint32_t>((min(t0 + R, T - 1) - t0) * K * XE + 8 * XE * sw_chunk);
+    }
+    // Weight stage rows: tile row R is global row m0 + R; gated tiles hold the 128 gate
+    // rows in stage rows 0..127 and the same 128 up rows in 128..255.  Rows past the
+    // end re-read the last row; their outputs are never stored.
+    const int wrows = min(rows_per_tile, M - m0);
+    const __amdgpu_buffer_rsrc_t wgr = make_rsrc(Wg + static_cast<int64_t>(m0) * rb, wrows * rb);
+    const __amdgpu_buffer_rsrc_t wur = GATED ? make_rsrc(Wu + static_cast<int64_t>(m0) * rb, wrows * rb) : wgr;
+    auto row_off = [&](int R) -> uint32_t {
+        const int r = GATED ? (R & 127) : R;
+        return static_cast<uint32_t>(min(r, wrows - 1) * rb);
+    };
+    uint32_t woffs[WPER];
+#pragma unroll
+    for (int i = 0; i < WPER; ++i) {
+        if constexpr (FMT == 1) {
+            const int R = 8 * (wave + GT_WAVES * i) + (lane >> 3);
+            woffs[i] = row_off(R) + 16 * sw_chunk;
         } else {
-            mrow = m0 + r;
-            base = Wg;
-        }
-        return base + min(mrow, M - 1) * rb;
-    };
-
-    // ---- weight loads: chunk c = tid + 512 * i -> tile row c / CPR, chunk c % CPR
-    uint4 wr[NLD];
-    auto load_w = [&](int step) {
-        const int64_t seg = static_cast<int64_t>(2 * step) * BB;
-        const int64_t a = (FMT == 1) ? static_cast<int64_t>(step) * 128 : (seg & ~int64_t(15));
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int c = min(tid + GT_THREADS * i, GT_BM * CPR - 1);
-            const int r = c / CPR, ch = c - CPR * (c / CPR);
-            // A window never passes its row's end: on a row's last step the segment ends
-            // exactly at the 16-byte aligned row end; the clamp only trims the Q4_0 window.
-            const int64_t o = min(a + 16 * ch, rb - 16);
-            wr[i] = load16_nt(row_ptr(r) + o);
-        }
-    };
-    // Park the loaded bytes: block formats into a raw area, F16 directly into a weight stage.
-    auto store_w = [&](uint8_t* raw, _Float16* wf) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int c = tid + GT_THREADS * i;
-            if (c < GT_BM * CPR) {
-                const int r = c / CPR, ch = c - CPR * (c / CPR);
-                if constexpr (FMT == 1) *reinterpret_cast<uint4*>(wf + r * GT_WLD + 8 * ch) = wr[i];
-                else *reinterpret_cast<uint4*>(raw + r * GT_RAW + 16 * ch) = wr[i];
-            }
-        }
-    };
-    // Two threads per row: thread tid decodes block (tid & 1) of tile row tid >> 1.
-    auto decode_w = [&](int step, const uint8_t* raw, _Float16* wf) {
-        if constexpr (FMT != 1) {
-            const int r = tid >> 1, h = tid & 1;
-            const int64_t seg = static_cast<int64_t>(2 * step) * BB;
-            const int sh = static_cast<int>(seg & 15) >> 2;  // dword offset of the segment in the window
-            const uint32_t* src = reinterpret_cast<const uint32_t*>(raw + r * GT_RAW);
-            uint32_t o[16];
-            if constexpr (FMT == 8) {
-                // [d0][q0 x32][d1][q1 x32]: block 0 = dwords 0..8 (codes from byte 2),
-                // block 1 = scale in the high half of dword 8, codes in dwords 9..16.
-                uint32_t w[9];
-#pragma unroll
-                for (int i = 0; i < 9; ++i) w[i] = src[sh + 8 * h + i];
-                const uint32_t d = h ? (w[0] >> 16) : (w[0] & 0xFFFFu);
-                const half2_t d2 = bits_h2(d | (d << 16));
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t codes = h ? w[1 + i] : align_bytes(w[i + 1], w[i], 2);
-                    q8_4(codes, d2, o[2 * i], o[2 * i + 1]);
-                }
-            } else {
-                // [d0][16 code bytes][d1][16 code bytes]: block 0 = dwords 0..4 (codes from
-                // byte 2), block 1 = scale in the high half of dword 4, codes in dwords 5..8.
-                uint32_t w[5];
-#pragma unroll
-                for (int i = 0; i < 5; ++i) w[i] = src[sh + 4 * h + i];
-                const uint32_t d = h ? (w[0] >> 16) : (w[0] & 0xFFFFu);
-                const half2_t d2 = bits_h2(d | (d << 16));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t cw = h ? w[1 + i] : align_bytes(w[i + 1], w[i], 2);
-                    q4_4(cw & 0x0F0F0F0Fu, d2, o[2 * i], o[2 * i + 1]);            // weights 4i..4i+3
-                    q4_4((cw >> 4) & 0x0F0F0F0Fu, d2, o[8 + 2 * i], o[8 + 2 * i + 1]);  // 16+4i..
-                }
-            }
-            uint4* dst = reinterpret_cast<uint4*>(wf + r * GT_WLD + 32 * h);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-        }
-    };
-
-    // ---- token fragments: lane l of fragment j holds X[t][k .. k+7], t = row of the
-    // fragment, k = 8 * (l / 16) within the 32-wide sub-step.
-    const int b_tok0 = t0 + wn * 64 + (lane & 15);
-    const int b_k = 8 * (lane >> 4);
-    auto load_b = [&](int kk, half8_t (&bf)[4]) {  // kk = absolute K offset of the sub-step
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = min(b_tok0 + 16 * j, T - 1);
-            if constexpr (XF32) {
-                const float* xp = static_cast<const float*>(Xv) + static_cast<int64_t>(t) * K + kk + b_k;
-                const float4 a = reinterpret_cast<const float4*>(xp)[0];
-                const float4 b = reinterpret_cast<const float4*>(xp)[1];
-                const uint4 u = make_uint4(pack_h2(a.x, a.y), pack_h2(a.z, a.w), pack_h2(b.x, b.y), pack_h2(b.z, b.w));
-                bf[j] = __builtin_bit_cast(half8_t, u);
-            } else {
-                const _Float16* xp = static_cast<const _Float16*>(Xv) + static_cast<int64_t>(t) * K + kk + b_k;
-                bf[j] = *reinterpret_cast<const half8_t*>(xp);
-            }
-        }
-    };
-
-    float4_t acc[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int a_row = wm * 128 + (lane & 15);
-    const int a_k = 8 * (lane >> 4);
-    half8_t bcur[4], bnxt[4];
-
-    // One K step: MFMAs on weight stage `wc` with token fragments for K offset k0,
-    // prefetching the fragments of the next sub-steps.
-    auto mfma_step = [&](const _Float16* wc, int step) {
-        const int k0 = step * GT_BK;
-        load_b(k0 + 32, bnxt);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const half8_t af = *reinterpret_cast<const half8_t*>(wc + (a_row + 16 * i) * GT_WLD + a_k);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bcur[j], acc[i][j], 0, 0, 0);
-        }
-        if (step + 1 < nsteps) load_b(k0 + GT_BK, bcur);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const half8_t af = *reinterpret_cast<const half8_t*>(wc + (a_row + 16 * i) * GT_WLD + 32 + a_k);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bnxt[j], acc[i][j], 0, 0, 0);
-        }
-    };
-
-    if constexpr (FMT == 1) {
-        // F16: the loaded rows are copied straight into a weight stage.
-        // Step k: copy data(k+1) -> Wf[(k+1)%2], issue loads of data(k+2), MFMAs on Wf[k%2].
-        load_b(0, bcur);
-        load_w(0);
-        store_w(nullptr, Wf0);
-        if (nsteps > 1) load_w(1);
-        __syncthreads();
-        for (int step = 0; step < nsteps; step += 2) {
-            if (step + 1 < nsteps) store_w(nullptr, Wf1);
-            if (step + 2 < nsteps) load_w(step + 2);
-            mfma_step(Wf0, step);
-            __syncthreads();
-            if (step + 1 < nsteps) {
-                if (step + 2 < nsteps) store_w(nullptr, Wf0);
-                if (step + 3 < nsteps) load_w(step + 3);
-                mfma_step(Wf1, step + 1);
-                __syncthreads();
-            }
-        }
-    } else {
-        // Block formats.  Prologue: stage 0 decoded, raw(1) parked in Raw1, raw(2) in flight.
-        load_b(0, bcur);
-        load_w(0);
-        store_w(Raw0, nullptr);
-        if (nsteps > 1) load_w(1);
-        __syncthreads();
-        decode_w(0, Raw0, Wf0);
-        if (nsteps > 1) store_w(Raw1, nullptr);
-        if (nsteps > 2) load_w(2);
-        __syncthreads();
-        // Step k: park raw(k+2) in Raw[k%2], issue loads of raw(k+3), decode raw(k+1)
-        // from Raw[(k+1)%2] into Wf[(k+1)%2], MFMAs on Wf[k%2]; one barrier.
-        for (int step = 0; step < nsteps; step += 2) {
-            if (step + 2 < nsteps) store_w(Raw0, nullptr);
-            if (step + 3 < nsteps) load_w(step + 3);
-            if (step + 1 < nsteps) decode_w(step + 1, Raw1, Wf1);
-            mfma_step(Wf0, step);
-            __syncthreads();
-            if (step + 1 < nsteps) {
-                if (step + 3 < nsteps) store_w(Raw1, nullptr);
-                if (step + 4 < nsteps) load_w(step + 4);
-                if (step + 2 < nsteps) decode_w(step + 2, Raw0, Wf0);
-                mfma_step(Wf1, step + 1);
-                __syncthreads();
-            }
+            // Block formats: wave instruction n covers items 64 n .. 64 n + 63 of the
+            // stage, item q = chunk q % WCH of tile row q / WCH.
+            const int n = min(wave + GT_WAVES * i, WINST - 1);
+            const int q = 64 * n + lane;
+            woffs[i] = row_off(q / G::WCH) + 16 * (q % G::WCH);
         }
     }
+
+    // Issue the DMA of weight stage `st` (K steps st*KPS ..) into buffer Wd.
+    auto issue_w = [&](QMM_L3 uint8_t* Wd, int st) {
+        uint32_t a;
+        if constexpr (FMT == 1) a = static_cast<uint32_t>(st) * 128;
+        else a = (static_cast<uint32_t>(st) * (2 * KPS * BB)) & ~15u;
+#pragma unroll
+        for (int i = 0; i < WPER; ++i) {
+            const int n = min(wave + GT_WAVES * i, WINST - 1);
+            dma16((GATED && n >= WINST / 2) ? wur : wgr, woffs[i], a, Wd + 1024 * n);
+        }
+    };
+
+    // Token step k: DMA for fp16 tokens; fp32 tokens are loaded to VGPRs here and
+    // converted / stored by store_x before the barrier of step k.
+    u32x4_t xreg[XF32 ? 2 * XINST : 1];
+    auto issue_x = [&](QMM_L3 uint8_t* Xd, int k) {
+        if constexpr (XF32) {
+#pragma unroll
+            for (int i = 0; i < XINST; ++i) {
+                xreg[2 * i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoffs[i], k * 256, 0);
+                xreg[2 * i + 1] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoffs[i] + 16, k * 256, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < XINST; ++i)
+                dma16(xr, xoffs[i], static_cast<uint32_t>(k) * 128, Xd + 1024 * (wave + GT_WAVES * i));
+        }
+    };
+    auto store_x = [&](QMM_L3 uint8_t* Xd) {
+        if constexpr (XF32) {
+#pragma unroll
+            for (int i = 0; i < XINST; ++i) {
+                // Elements are copied out before the bit cast: bit-casting an element
+                // access of an ext-vector directly reads element 0 with this compiler.
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t ua = xreg[2 * i][e], ub = xreg[2 * i + 1][e];
+                    f[e] = __builtin_bit_cast(float, ua);
+                    f[4 + e] = __builtin_bit_cast(float, ub);
+                }
+                const u32x4_t h = {pack_h2(f[0], f[1]), pack_h2(f[2], f[3]), pack_h2(f[4], f[5]), pack_h2(f[6], f[7])};
+                *reinterpret_cast<QMM_L3 u32x4_t*>(Xd + 1024 * (wave + GT_WAVES * i) + 16 * lane) = h;
+            }
+        }
+    };
+
+    float4_t acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Fragment addressing.  Token fragment j of sub-step ks: row 128 wn + 16 j + l % 16,
+    // chunk 4 ks + l / 16 (swizzled by row & 7 = l & 7).
+    const int q4 = lane >> 4;
+    int xoff[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) xoff[ks] = (128 * wn + (lane & 15)) * 128 + (((4 * ks + q4) ^ (lane & 7)) << 4);
+    // Weight fragment i: stage row 64 wm + 16 i + l % 16; gated: fragments 0, 1 are the
+    // gate rows 32 wm + 16 i + l % 16 and fragments 2, 3 the up rows of the same outputs.
+    auto arow = [&](int i) -> int {
+        if constexpr (GATED) return (i < 2 ? 32 * wm + 16 * i : 128 + 32 * wm + 16 * (i - 2)) + (lane & 15);
+        else return 64 * wm + 16 * i + (lane & 15);
+    };
+
+    // Decode A fragment i (weights 8 q4 .. 8 q4 + 7 of block b of the stage) from a raw
+    // weight stage.  `sh` is the segment's offset in the row window (8 for odd stages).
+    auto frag_a = [&](const QMM_L3 uint8_t* Wsrc, int i, int b, int sh) -> half8_t {
+        const int rowb = arow(i) * WROW;
+        if constexpr (FMT == 1) {
+            (void)sh;
+            // Swizzled 128-byte rows; the row's swizzle key is l & 7.
+            return *reinterpret_cast<const QMM_L3 half8_t*>(Wsrc + rowb + (((4 * b + q4) ^ (lane & 7)) << 4));
+        } else {
+            const int o = sh + BB * b;  // block start inside the row window
+            const QMM_L3 uint32_t* dw = reinterpret_cast<const QMM_L3 uint32_t*>(Wsrc + rowb);
+            uint32_t d, c0, c1;
+            const int cb = (FMT == 8) ? 8 * q4 : 8 * (q4 & 1);  // code byte offset in the block
+            if ((o & 3) == 0) {
+                d = dw[o >> 2] & 0xFFFFu;
+                const int base = (o + cb) >> 2;  // codes start 2 bytes into dword `base`
+                const uint32_t w0 = dw[base], w1 = dw[base + 1], w2 = dw[base + 2];
+                c0 = align_bytes(w1, w0, 2);
+                c1 = align_bytes(w2, w1, 2);
+            } else {
+                d = dw[(o - 2) >> 2] >> 16;
+                const int base = (o + 2 + cb) >> 2;
+                c0 = dw[base];
+                c1 = dw[base + 1];
+            }
+            const half2_t d2 = bits_h2(d | (d << 16));
+            uint32_t r0, r1, r2, r3;
+            if constexpr (FMT == 8) {
+                q8_4(c0, d2, r0, r1);
+                q8_4(c1, d2, r2, r3);
+            } else {
+                const uint32_t s4 = 4 * (q4 >> 1);  // fragments 2, 3 take the high nibbles
+                q4_4((c0 >> s4) & 0x0F0F0F0Fu, d2, r0, r1);
+                q4_4((c1 >> s4) & 0x0F0F0F0Fu, d2, r2, r3);
+            }
+            return __builtin_bit_cast(half8_t, u32x4_t{r0, r1, r2, r3});
+        }
+    };
+
+    // One K step: A fragments decoded from weight stage Wc (block pair kk, segment
+    // offset sh), token fragments streamed from Xc; 64 MFMAs per wave.
+    auto mfma_step = [&](const QMM_L3 uint8_t* Xc, const QMM_L3 uint8_t* Wc, int kk, int sh) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            // Keep each 32-wide sub-step's fragment reads inside its own region: hoisting
+            // the next sub-step's reads would push the wave past its 256 registers.
+            __builtin_amdgcn_sched_barrier(0);
+            half8_t af[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = frag_a(Wc, i, 2 * kk + ks, sh);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const half8_t bf = *reinterpret_cast<const QMM_L3 half8_t*>(Xc + xoff[ks] + j * 16 * 128);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf, acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+
+    QMM_L3 uint8_t* X0 = (QMM_L3 uint8_t*)Xs0;
+    QMM_L3 uint8_t* X1 = (QMM_L3 uint8_t*)Xs1;
+    QMM_L3 uint8_t* W0 = (QMM_L3 uint8_t*)Ws0;
+    QMM_L3 uint8_t* W1 = (QMM_L3 uint8_t*)Ws1;
+    const int nstages = nsteps / KPS;
+
+    // Step k with token stage XS (= k % 2), weight stage WS, block pair KK.  Order:
+    // finish own DMA / staging of this step's stages, barrier, issue the prefetch of
+    // token step k+1 (and of weight stage k/KPS + 1 on the first step of a stage),
+    // compute.  Prefetches past the end re-load the last step into the free buffer,
+    // which keeps the loop body free of branches (and the wait counts constant): on
+    // the second step of a block-format stage the weight DMA issued on the previous
+    // step, after the token DMA needed now, may stay in flight.
+    auto step = [&](auto XS_, auto WS_, auto KK_, int k) {
+        constexpr int XS = decltype(XS_)::value, WS = decltype(WS_)::value, KK = decltype(KK_)::value;
+        QMM_L3 uint8_t* Xc = XS ? X1 : X0;
+        QMM_L3 uint8_t* Xn = XS ? X0 : X1;
+        QMM_L3 uint8_t* Wc = WS ? W1 : W0;
+        QMM_L3 uint8_t* Wn = WS ? W0 : W1;
+        if constexpr (KPS == 2 && KK == 1) wait_vm<WPER>();
+        else wait_vm<0>();
+        if constexpr (XF32) store_x(Xc);
+        lds_barrier();
+        // fp32 tokens are loaded after the step's MFMAs, so that their staging registers
+        // are live only across the barrier (their latency is exposed; this path serves
+        // small decode batches).
+        if constexpr (!XF32) issue_x(Xn, min(k + 1, nsteps - 1));
+        if constexpr (KK == 0) issue_w(Wn, min(k / KPS + 1, nstages - 1));
+        mfma_step(Xc, Wc, KK, FMT == 1 ? 0 : 8 * WS);
+        if constexpr (XF32) issue_x(Xn, min(k + 1, nsteps - 1));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // ---- prologue: stage 0 of both operands
+    issue_w(W0, 0);
+    issue_x(X0, 0);
+    if constexpr (KPS == 2) {
+        // K % 256 == 0: whole groups of 4 steps (weight stages 0, 0, 1, 1).
+        for (int k = 0; k < nsteps; k += 4) {
+            step(I0{}, I0{}, I0{}, k);
+            step(I1{}, I0{}, I1{}, k + 1);
+            step(I0{}, I1{}, I0{}, k + 2);
+            step(I1{}, I1{}, I1{}, k + 3);
+        }
+    } else {
+        int k = 0;
+        for (; k + 2 <= nsteps; k += 2) {
+            step(I0{}, I0{}, I0{}, k);
+            step(I1{}, I1{}, I0{}, k + 1);
+        }
+        if (k < nsteps) step(I0{}, I0{}, I0{}, k);
+    }
+    // Drain the trailing re-load DMAs before the workgroup can exit.
+    wait_vm<0>();
 
     // ---- epilogue.  D fragment: lane l holds rows 4*(l/16) + e of column l%16.
     const int er = 4 * (lane >> 4);
     const int ec = lane & 15;
-    if constexpr (!GATED) {
+    constexpr int NOUT = GATED ? 2 : 4;  // output fragments per wave
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int m = m0 + wm * 128 + 16 * i + er;
+    for (int i = 0; i < NOUT; ++i) {
+        const int m = m0 + (GATED ? 32 * wm : 64 * wm) + 16 * i + er;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = t0 + wn * 64 + 16 * j + ec;
-                if (t < T && m < M) {
-                    float* yp = Y + static_cast<int64_t>(t) * M + m;
-                    if (vec) {
-                        *reinterpret_cast<float4*>(yp) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-                    } else {
+        for (int j = 0; j < 8; ++j) {
+            const int t = t0 + 128 * wn + 16 * j + ec;
+            if (t < T && m < M) {
+                float h[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (m + e < M) yp[e] = acc[i][j][e];
-                    }
-                }
-            }
-        }
-    } else {
+                for (int e = 0; e < 4; ++e) h[e] = GATED ? silu(acc[i][j][e]) * acc[i + 2][j][e] : acc[i][j][e];
+                float* yp = Y + static_cast<int64_t>(t) * M + m;
+                if (vec) {
+                    *reinterpret_cast<float4*>(yp) = make_float4(h[0], h[1], h[2], h[3]);
+                } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + wm * 64 + 16 * i + er;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = t0 + wn * 64 + 16 * j + ec;
-                if (t < T && m < M) {
-                    float h[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) h[e] = silu(acc[i][j][e]) * acc[i + 4][j][e];
-                    float* yp = Y + static_cast<int64_t>(t) * M + m;
-                    if (vec) {
-                        *reinterpret_cast<float4*>(yp) = make_float4(h[0], h[1], h[2], h[3]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (m + e < M) yp[e] = h[e];
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        if (m + e < M) yp[e] = h[e];
                 }
             }
         }
@@ -380,6 +463,9 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
     // Block formats need 16-byte aligned rows (K % 256 == 0); F16 needs K % 64 == 0.
     if (fmt != 1 && K % 256 != 0) return false;
     if (K % 64 != 0) return false;
+    // 32-bit lane offsets inside a tile: 256 rows of tokens (fp32: 4 K bytes each)
+    // and of weights must span less than 2^31 bytes.
+    if (K > (int64_t{1} << 20)) return false;
     const int64_t rows_per_tile = Wu ? GT_BM / 2 : GT_BM;
     const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + GT_BN - 1) / GT_BN);
     if (ntiles > (int64_t{1} << 30)) return false;
