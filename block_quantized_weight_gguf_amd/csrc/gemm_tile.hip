@@ -43,6 +43,8 @@
 //     for the same outputs and applies h = silu(g) * u before the store.
 //   * fp32 tokens (batched decode through the MFMA path) are converted while being
 //     staged through VGPRs instead of by DMA.
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "qmm_common.hpp"
@@ -143,12 +145,16 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (QMM_L3 void*)lds, 16, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
 }
 
-template <int FMT, bool GATED, bool XF32>
+// SPLIT: the workgroup computes the K steps [split * ksteps, (split + 1) * ksteps) of
+// its tile and stores the raw partial sums to Y[split][T][Mo] (Mo = M, or 2 M for the
+// gated instance: gate sums in columns 0..M-1, up sums in M..2M-1); splitk_reduce
+// adds the splits in order and applies the epilogue.
+template <int FMT, bool GATED, bool XF32, bool SPLIT>
 __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __restrict__ Wg,
                                                                 const uint8_t* __restrict__ Wu,
                                                                 const void* __restrict__ Xv,
                                                                 float* __restrict__ Y, int M, int K, int T,
-                                                                int vec) {
+                                                                int vec, int nsplit, int ksteps) {
     using G = WStage<FMT>;
     constexpr int BB = Fmt<FMT>::BB;
     constexpr int WROW = G::WCH * 16;         // bytes per row in a weight stage
@@ -184,9 +190,16 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     const int nMt = (M + rows_per_tile - 1) / rows_per_tile;
     const int nTt = (T + GT_BN - 1) / GT_BN;
     const int ntiles = nMt * nTt;
-    const int per_xcd = (ntiles + 7) / 8;
-    const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if (tile >= ntiles) return;
+    const int nunits = ntiles * (SPLIT ? nsplit : 1);
+    const int per_xcd = (nunits + 7) / 8;
+    const int unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (unit >= nunits) return;
+    const int tile = SPLIT ? unit / nsplit : unit;
+    const int split = SPLIT ? unit - tile * nsplit : 0;
+    // K steps of this workgroup (a multiple of 4 steps per split, so that block-format
+    // weight stages keep their global parity).
+    const int kbeg = SPLIT ? split * ksteps : 0;
+    const int kend = SPLIT ? min(kbeg + ksteps, nsteps) : nsteps;
     const int group = tile / (GT_GROUP_M * nTt);
     const int first_m = group * GT_GROUP_M;
     const int gm = min(GT_GROUP_M, nMt - first_m);
@@ -341,32 +354,42 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         }
     };
 
-    // One K step: A fragments decoded from weight stage Wc (block pair kk, segment
-    // offset sh), token fragments streamed from Xc; 64 MFMAs per wave.
-    auto mfma_step = [&](const QMM_L3 uint8_t* Xc, const QMM_L3 uint8_t* Wc, int kk, int sh) {
+    // A fragments are software-pipelined: the 4 fragments of a 32-wide sub-step are
+    // decoded while the MFMAs of the previous sub-step run (token fragments are
+    // streamed from LDS one at a time).  Within a weight stage the next step's first
+    // sub-step is decoded during the current step's second one; across stages that
+    // decode has to wait for the barrier that publishes the new stage.
+    half8_t a0[4], a1[4];
+    // Decode fragments i0, i0+1 of block b into a.
+    auto decode2 = [&](half8_t (&a)[4], int i0, const QMM_L3 uint8_t* Wc, int b, int sh) {
+        a[i0] = frag_a(Wc, i0, b, sh);
+        a[i0 + 1] = frag_a(Wc, i0 + 1, b, sh);
+    };
+    // 32 MFMAs of sub-step ks with fragments a, in two scheduling regions of 16; the
+    // decode of the next fragments (nxt, block nb; skipped when nb < 0) is split over
+    // them, so that its temporaries stay small and it overlaps the MFMAs.
+    auto mfma_sub = [&](const half8_t (&a)[4], const QMM_L3 uint8_t* Xc, int ks, half8_t (&nxt)[4], int nb,
+                        const QMM_L3 uint8_t* Wc, int sh) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            // Keep each 32-wide sub-step's fragment reads inside its own region: hoisting
-            // the next sub-step's reads would push the wave past its 256 registers.
+        for (int h = 0; h < 2; ++h) {
             __builtin_amdgcn_sched_barrier(0);
-            half8_t af[4];
+            if (nb >= 0) decode2(nxt, 2 * h, Wc, nb, sh);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = frag_a(Wc, i, 2 * kk + ks, sh);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 4 * h; j < 4 * h + 4; ++j) {
                 const half8_t bf = *reinterpret_cast<const QMM_L3 half8_t*>(Xc + xoff[ks] + j * 16 * 128);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf, acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bf, acc[i][j], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     QMM_L3 uint8_t* X0 = (QMM_L3 uint8_t*)Xs0;
     QMM_L3 uint8_t* X1 = (QMM_L3 uint8_t*)Xs1;
     QMM_L3 uint8_t* W0 = (QMM_L3 uint8_t*)Ws0;
     QMM_L3 uint8_t* W1 = (QMM_L3 uint8_t*)Ws1;
-    const int nstages = nsteps / KPS;
+    const int send = kend / KPS;  // one past the last weight stage
 
     // Step k with token stage XS (= k % 2), weight stage WS, block pair KK.  Order:
     // finish own DMA / staging of this step's stages, barrier, issue the prefetch of
@@ -388,33 +411,44 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         // fp32 tokens are loaded after the step's MFMAs, so that their staging registers
         // are live only across the barrier (their latency is exposed; this path serves
         // small decode batches).
-        if constexpr (!XF32) issue_x(Xn, min(k + 1, nsteps - 1));
-        if constexpr (KK == 0) issue_w(Wn, min(k / KPS + 1, nstages - 1));
-        mfma_step(Xc, Wc, KK, FMT == 1 ? 0 : 8 * WS);
-        if constexpr (XF32) issue_x(Xn, min(k + 1, nsteps - 1));
+        if constexpr (!XF32) issue_x(Xn, min(k + 1, kend - 1));
+        if constexpr (KK == 0) issue_w(Wn, min(k / KPS + 1, send - 1));
+        constexpr int SH = FMT == 1 ? 0 : 8 * WS;
+        // a0 holds this step's first sub-step when it was decoded on the previous step
+        // (second step of a block-format stage); otherwise decode it now.
+        // (fp32 tokens skip the cross-step decode: their staging registers are live
+        // across the barrier.)
+        constexpr bool PRE = KPS == 2 && !XF32;
+        if constexpr (!(PRE && KK == 1)) {
+            decode2(a0, 0, Wc, 2 * KK, SH);
+            decode2(a0, 2, Wc, 2 * KK, SH);
+        }
+        mfma_sub(a0, Xc, 0, a1, 2 * KK + 1, Wc, SH);
+        mfma_sub(a1, Xc, 1, a0, (PRE && KK == 0) ? 2 : -1, Wc, SH);
+        if constexpr (XF32) issue_x(Xn, min(k + 1, kend - 1));
         __builtin_amdgcn_sched_barrier(0);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
     // ---- prologue: stage 0 of both operands
-    issue_w(W0, 0);
-    issue_x(X0, 0);
+    issue_w(W0, kbeg / KPS);
+    issue_x(X0, kbeg);
     if constexpr (KPS == 2) {
         // K % 256 == 0: whole groups of 4 steps (weight stages 0, 0, 1, 1).
-        for (int k = 0; k < nsteps; k += 4) {
+        for (int k = kbeg; k < kend; k += 4) {
             step(I0{}, I0{}, I0{}, k);
             step(I1{}, I0{}, I1{}, k + 1);
             step(I0{}, I1{}, I0{}, k + 2);
             step(I1{}, I1{}, I1{}, k + 3);
         }
     } else {
-        int k = 0;
-        for (; k + 2 <= nsteps; k += 2) {
+        int k = kbeg;
+        for (; k + 2 <= kend; k += 2) {
             step(I0{}, I0{}, I0{}, k);
             step(I1{}, I1{}, I0{}, k + 1);
         }
-        if (k < nsteps) step(I0{}, I0{}, I0{}, k);
+        if (k < kend) step(I0{}, I0{}, I0{}, k);
     }
     // Drain the trailing re-load DMAs before the workgroup can exit.
     wait_vm<0>();
@@ -422,40 +456,124 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     // ---- epilogue.  D fragment: lane l holds rows 4*(l/16) + e of column l%16.
     const int er = 4 * (lane >> 4);
     const int ec = lane & 15;
-    constexpr int NOUT = GATED ? 2 : 4;  // output fragments per wave
+    auto store4 = [&](float* yp, int m, const float (&h)[4]) {
+        if (vec) {
+            *reinterpret_cast<float4*>(yp) = make_float4(h[0], h[1], h[2], h[3]);
+        } else {
 #pragma unroll
-    for (int i = 0; i < NOUT; ++i) {
-        const int m = m0 + (GATED ? 32 * wm : 64 * wm) + 16 * i + er;
+            for (int e = 0; e < 4; ++e)
+                if (m + e < M) yp[e] = h[e];
+        }
+    };
+    if constexpr (SPLIT) {
+        const int Mo = GATED ? 2 * M : M;
+        float* P = Y + static_cast<int64_t>(split) * T * Mo;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = t0 + 128 * wn + 16 * j + ec;
-            if (t < T && m < M) {
-                float h[4];
+        for (int i = 0; i < 4; ++i) {
+            const int m = GATED ? m0 + 32 * wm + 16 * (i & 1) + er : m0 + 64 * wm + 16 * i + er;
+            const int col = (GATED && i >= 2 ? M : 0) + m;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = GATED ? silu(acc[i][j][e]) * acc[i + 2][j][e] : acc[i][j][e];
-                float* yp = Y + static_cast<int64_t>(t) * M + m;
-                if (vec) {
-                    *reinterpret_cast<float4*>(yp) = make_float4(h[0], h[1], h[2], h[3]);
-                } else {
+            for (int j = 0; j < 8; ++j) {
+                const int t = t0 + 128 * wn + 16 * j + ec;
+                if (t < T && m < M) {
+                    const float h[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                    store4(P + static_cast<int64_t>(t) * Mo + col, m, h);
+                }
+            }
+        }
+    } else {
+        constexpr int NOUT = GATED ? 2 : 4;  // output fragments per wave
+#pragma unroll
+        for (int i = 0; i < NOUT; ++i) {
+            const int m = m0 + (GATED ? 32 * wm : 64 * wm) + 16 * i + er;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = t0 + 128 * wn + 16 * j + ec;
+                if (t < T && m < M) {
+                    float h[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (m + e < M) yp[e] = h[e];
+                        h[e] = GATED ? silu(acc[i][j][e]) * acc[i + 2][j][e] : acc[i][j][e];
+                    store4(Y + static_cast<int64_t>(t) * M + m, m, h);
                 }
             }
         }
     }
 }
 
-template <int FMT, bool GATED, bool XF32>
+// Sums the split-K partials P[s][T][Mo] in split order and applies the epilogue
+// (gated: h = silu(sum of gate partials) * (sum of up partials)).  Four outputs per
+// thread when M % 4 == 0 (16-byte aligned rows), else one.
+template <bool GATED>
+__global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P, float* __restrict__ Y,
+                                                     int64_t T, int64_t M, int nsplit, int vec) {
+    const int64_t Mo = GATED ? 2 * M : M;
+    const int64_t plane = T * Mo;
+    const int W = vec ? 4 : 1;
+    const int64_t n = T * M / W;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t t = e * W / M, m = e * W - t * M;
+        const float* p = P + t * Mo + m;
+        if (vec) {
+            float4 g = *reinterpret_cast<const float4*>(p);
+            float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (GATED) u = *reinterpret_cast<const float4*>(p + M);
+            for (int s = 1; s < nsplit; ++s) {
+                const float4 a = *reinterpret_cast<const float4*>(p + s * plane);
+                g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+                if (GATED) {
+                    const float4 b = *reinterpret_cast<const float4*>(p + s * plane + M);
+                    u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+                }
+            }
+            if (GATED) g = make_float4(silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
+            *reinterpret_cast<float4*>(Y + t * M + m) = g;
+        } else {
+            float g = p[0], u = GATED ? p[M] : 0.0f;
+            for (int s = 1; s < nsplit; ++s) {
+                g += p[s * plane];
+                if (GATED) u += p[s * plane + M];
+            }
+            Y[t * M + m] = GATED ? silu(g) * u : g;
+        }
+    }
+}
+
+template <int FMT, bool GATED, bool XF32, bool SPLIT>
 static void launch_tile_t(const void* W, const void* Wu, const void* X, float* Y, int64_t M, int64_t K, int64_t T,
-                          hipStream_t s) {
+                          int nsplit, int ksteps, hipStream_t s) {
     const int64_t rows_per_tile = GATED ? GT_BM / 2 : GT_BM;
     const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + GT_BN - 1) / GT_BN);
-    const int64_t grid = (ntiles + 7) / 8 * 8;  // whole runs per XCD
-    hipLaunchKernelGGL((gemm_tile_kernel<FMT, GATED, XF32>), dim3(static_cast<unsigned>(grid)), dim3(GT_THREADS), 0,
-                       s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), X, Y, static_cast<int>(M),
-                       static_cast<int>(K), static_cast<int>(T),
-                       static_cast<int>(M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0));
+    const int64_t grid = (ntiles * (SPLIT ? nsplit : 1) + 7) / 8 * 8;  // whole runs per XCD
+    hipLaunchKernelGGL((gemm_tile_kernel<FMT, GATED, XF32, SPLIT>), dim3(static_cast<unsigned>(grid)),
+                       dim3(GT_THREADS), 0, s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), X, Y,
+                       static_cast<int>(M), static_cast<int>(K), static_cast<int>(T),
+                       static_cast<int>(M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0), nsplit, ksteps);
+}
+
+// Stream-ordered workspace for split-K partials: a memory pool of this library per
+// device, which keeps freed blocks for reuse (so steady-state calls do not go to the
+// driver) and orders reuse by stream.
+static hipMemPool_t splitk_pool() {
+    static std::mutex mu;
+    static hipMemPool_t pools[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t p = nullptr;
+        if (hipMemPoolCreate(&p, &props) != hipSuccess) return nullptr;
+        uint64_t keep = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+        pools[dev] = p;
+    }
+    return pools[dev];
 }
 
 bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32, float* Y, int64_t M,
@@ -466,20 +584,56 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
     // 32-bit lane offsets inside a tile: 256 rows of tokens (fp32: 4 K bytes each)
     // and of weights must span less than 2^31 bytes.
     if (K > (int64_t{1} << 20)) return false;
-    const int64_t rows_per_tile = Wu ? GT_BM / 2 : GT_BM;
+    const bool gated = Wu != nullptr;
+    const int64_t rows_per_tile = gated ? GT_BM / 2 : GT_BM;
     const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + GT_BN - 1) / GT_BN);
     if (ntiles > (int64_t{1} << 30)) return false;
-#define QMM_TILE_CASE(F)                                                                      \
-    if (Wu) {                                                                                 \
-        if (x_is_f32) launch_tile_t<F, true, true>(W, Wu, X, Y, M, K, T, s);                  \
-        else launch_tile_t<F, true, false>(W, Wu, X, Y, M, K, T, s);                          \
-    } else {                                                                                  \
-        if (x_is_f32) launch_tile_t<F, false, true>(W, Wu, X, Y, M, K, T, s);                 \
-        else launch_tile_t<F, false, false>(W, Wu, X, Y, M, K, T, s);                         \
+
+    // Split K when the tiles cannot fill the 256 CUs: at most one wave of workgroups,
+    // at least 4 K steps (256) per split, split boundaries on multiples of 4 steps.
+    const int64_t nsteps = K / GT_BK;
+    int nsplit = 1, ksteps = static_cast<int>(nsteps);
+    if (ntiles < 192 && nsteps >= 8) {
+        const int64_t want = std::min<int64_t>(256 / ntiles, nsteps / 4);
+        if (want >= 2) {
+            ksteps = static_cast<int>((nsteps + want - 1) / want + 3) / 4 * 4;
+            nsplit = static_cast<int>((nsteps + ksteps - 1) / ksteps);
+        }
     }
-    if (fmt == 8) { QMM_TILE_CASE(8) }
-    else if (fmt == 2) { QMM_TILE_CASE(2) }
-    else { QMM_TILE_CASE(1) }
+    float* P = nullptr;
+    if (nsplit > 1) {
+        const size_t bytes = static_cast<size_t>(nsplit) * T * (gated ? 2 * M : M) * sizeof(float);
+        hipMemPool_t pool = splitk_pool();
+        if (!pool || hipMallocFromPoolAsync(reinterpret_cast<void**>(&P), bytes, pool, s) != hipSuccess) {
+            (void)hipGetLastError();
+            P = nullptr;
+            nsplit = 1;
+            ksteps = static_cast<int>(nsteps);
+        }
+    }
+#define QMM_TILE_CASE(F, SP, OUT)                                                                        \
+    if (gated) {                                                                                        \
+        if (x_is_f32) launch_tile_t<F, true, true, SP>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);       \
+        else launch_tile_t<F, true, false, SP>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);               \
+    } else {                                                                                            \
+        if (x_is_f32) launch_tile_t<F, false, true, SP>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);      \
+        else launch_tile_t<F, false, false, SP>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);              \
+    }
+    if (P) {
+        if (fmt == 8) { QMM_TILE_CASE(8, true, P) }
+        else if (fmt == 2) { QMM_TILE_CASE(2, true, P) }
+        else { QMM_TILE_CASE(1, true, P) }
+        const int vec = M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+        const int64_t n = T * M / (vec ? 4 : 1);
+        const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 256 * 16));
+        if (gated) hipLaunchKernelGGL(splitk_reduce<true>, dim3(grid), dim3(256), 0, s, P, Y, T, M, nsplit, vec);
+        else hipLaunchKernelGGL(splitk_reduce<false>, dim3(grid), dim3(256), 0, s, P, Y, T, M, nsplit, vec);
+        (void)hipFreeAsync(P, s);
+    } else {
+        if (fmt == 8) { QMM_TILE_CASE(8, false, Y) }
+        else if (fmt == 2) { QMM_TILE_CASE(2, false, Y) }
+        else { QMM_TILE_CASE(1, false, Y) }
+    }
 #undef QMM_TILE_CASE
     return true;
 }

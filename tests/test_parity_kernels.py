@@ -244,6 +244,49 @@ def test_gemm_gate_up_silu(fmt, I, K, T):
     check_swiglu(buf[:T * I].cpu().numpy().reshape(T, I), h_ref, g, u, Sg, Su, f"gemm gate_up fmt={fmt}")
 
 
+# Split-K: few tiles and a long K make the tiled GEMM split the K loop over several
+# workgroups and add the partial sums in a second pass.  Shapes cover uneven splits,
+# an F16 K whose step count is odd (last split shorter than the rest), M % 4 != 0
+# (scalar reduce path) and the gated epilogue applied after the reduction.
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("M,K,T", [(300, 2816, 40), (301, 2816, 3), (64, 14336, 130)])
+def test_gemm_split_k(fmt, M, K, T):
+    if fmt == si.FMT_F16:
+        K += 64  # odd number of 64-wide steps
+    seed = 5000 + M + K + T
+    raw = si.weights(fmt, M, K, seed, scale_mode="gemm_wide", q8_low=-128)
+    X = si.activations(T, K, seed + 1, dtype=np.float16)
+    announce(f"qmm_gemm split-K fmt={fmt} M={M} K={K} T={T} seed={seed}")
+    buf = poisoned(T * M)
+    Wd, Xd = dev(raw), dev(X)
+    qmm.qmm_gemm(fmt, Wd, Xd, buf, M, K, T)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, T * M)
+    y_ref, S = oracle.matmul_ref(fmt, raw, X, M, K)
+    got = buf[:T * M].cpu().numpy().reshape(T, M)
+    check_linear(got, y_ref, S, f"gemm split-K fmt={fmt} M={M} K={K} T={T}")
+    # The partials are added in a fixed order: a second call gives the same bits.
+    buf2 = poisoned(T * M)
+    qmm.qmm_gemm(fmt, Wd, Xd, buf2, M, K, T)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf2[:T * M].cpu().numpy().reshape(T, M), got)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("I,K,T", [(200, 2816, 70), (130, 4096, 9)])
+def test_gemm_gate_up_split_k(fmt, I, K, T):
+    seed = 6000 + I + K + T
+    rg, ru = si.weights(fmt, I, K, seed), si.weights(fmt, I, K, seed + 1)
+    X = si.activations(T, K, seed + 2, dtype=np.float16)
+    announce(f"qmm_gemm_gate_up_silu split-K fmt={fmt} I={I} K={K} T={T}")
+    buf = poisoned(T * I)
+    qmm.qmm_gemm_gate_up_silu(fmt, dev(rg), dev(ru), dev(X), buf, I, K, T)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, T * I)
+    h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, X, I, K)
+    check_swiglu(buf[:T * I].cpu().numpy().reshape(T, I), h_ref, g, u, Sg, Su, f"gemm gate_up split-K fmt={fmt}")
+
+
 def test_stream_argument():
     """Work goes to the stream passed in; results match the default-stream run."""
     fmt, M, K, N = si.FMT_Q8_0, 256, 1536, 2
