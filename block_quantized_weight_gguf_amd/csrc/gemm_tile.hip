@@ -63,6 +63,7 @@ constexpr int GT_THREADS = 512;
 constexpr int GT_WAVES = GT_THREADS / 64;
 constexpr int GT_GROUP_M = 4;
 
+
 __device__ __forceinline__ uint32_t h2_bits(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ half2_t bits_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
@@ -171,6 +172,15 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     constexpr int XINST = XBYTES / 1024 / GT_WAVES;          // token DMA instructions per wave and step
     constexpr int XE = XF32 ? 4 : 2;          // token element bytes
     static_assert(WINST % 2 == 0, "gate / up halves must split on instruction boundaries");
+    // Wave layout: 8 / GT_WN waves along the weight rows, GT_WN along the tokens; each
+    // wave holds GT_NI x GT_NJ 16x16 fragments (128 accumulators).  fp16 tokens: 8 x 1
+    // (each weight row is decoded by one wave only); fp32 tokens: 4 x 2, which leaves
+    // room for their staging registers.
+    constexpr int GT_WN = XF32 ? 2 : 1;
+    constexpr int GT_RW = GT_BM / (GT_WAVES / GT_WN);  // weight rows per wave
+    constexpr int GT_TW = GT_BN / GT_WN;               // tokens per wave
+    constexpr int GT_NI = GT_RW / 16;
+    constexpr int GT_NJ = GT_TW / 16;
 
     __shared__ __align__(16) uint8_t Xs0[XBYTES];
     __shared__ __align__(16) uint8_t Xs1[XBYTES];
@@ -180,7 +190,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;  // 64 weight rows x 128 tokens per wave
+    const int wm = wave / GT_WN, wn = wave % GT_WN;  // GT_RW weight rows x GT_TW tokens per wave
     const int nb = K / kQK;
     const int64_t rb = static_cast<int64_t>(nb) * BB;
     const int nsteps = K / GT_BK;
@@ -296,23 +306,26 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         }
     };
 
-    float4_t acc[4][8];
+    float4_t acc[GT_NI][GT_NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < GT_NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < GT_NJ; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Fragment addressing.  Token fragment j of sub-step ks: row 128 wn + 16 j + l % 16,
+    // Fragment addressing.  Token fragment j of sub-step ks: row GT_TW wn + 16 j + l % 16,
     // chunk 4 ks + l / 16 (swizzled by row & 7 = l & 7).
     const int q4 = lane >> 4;
     int xoff[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) xoff[ks] = (128 * wn + (lane & 15)) * 128 + (((4 * ks + q4) ^ (lane & 7)) << 4);
-    // Weight fragment i: stage row 64 wm + 16 i + l % 16; gated: fragments 0, 1 are the
-    // gate rows 32 wm + 16 i + l % 16 and fragments 2, 3 the up rows of the same outputs.
+    for (int ks = 0; ks < 2; ++ks)
+        xoff[ks] = (GT_TW * wn + (lane & 15)) * 128 + (((4 * ks + q4) ^ (lane & 7)) << 4);
+    // Weight fragment i: stage row GT_RW wm + 16 i + l % 16; gated: the first half of the
+    // fragments are gate rows (GT_RW / 2) wm + 16 i + l % 16, the second half the up
+    // rows of the same outputs.
+    constexpr int NH = GT_NI / 2;
     auto arow = [&](int i) -> int {
-        if constexpr (GATED) return (i < 2 ? 32 * wm + 16 * i : 128 + 32 * wm + 16 * (i - 2)) + (lane & 15);
-        else return 64 * wm + 16 * i + (lane & 15);
+        if constexpr (GATED) return (i < NH ? (GT_RW / 2) * wm + 16 * i : 128 + (GT_RW / 2) * wm + 16 * (i - NH)) + (lane & 15);
+        else return GT_RW * wm + 16 * i + (lane & 15);
     };
 
     // Decode A fragment i (weights 8 q4 .. 8 q4 + 7 of block b of the stage) from a raw
@@ -359,26 +372,26 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     // streamed from LDS one at a time).  Within a weight stage the next step's first
     // sub-step is decoded during the current step's second one; across stages that
     // decode has to wait for the barrier that publishes the new stage.
-    half8_t a0[4], a1[4];
-    // Decode fragments i0, i0+1 of block b into a.
-    auto decode2 = [&](half8_t (&a)[4], int i0, const QMM_L3 uint8_t* Wc, int b, int sh) {
-        a[i0] = frag_a(Wc, i0, b, sh);
-        a[i0 + 1] = frag_a(Wc, i0 + 1, b, sh);
+    half8_t a0[GT_NI], a1[GT_NI];
+    // Decode fragments i0 .. i0 + NH - 1 of block b into a.
+    auto decode2 = [&](half8_t (&a)[GT_NI], int i0, const QMM_L3 uint8_t* Wc, int b, int sh) {
+#pragma unroll
+        for (int i = i0; i < i0 + NH; ++i) a[i] = frag_a(Wc, i, b, sh);
     };
     // 32 MFMAs of sub-step ks with fragments a, in two scheduling regions of 16; the
     // decode of the next fragments (nxt, block nb; skipped when nb < 0) is split over
     // them, so that its temporaries stay small and it overlaps the MFMAs.
-    auto mfma_sub = [&](const half8_t (&a)[4], const QMM_L3 uint8_t* Xc, int ks, half8_t (&nxt)[4], int nb,
+    auto mfma_sub = [&](const half8_t (&a)[GT_NI], const QMM_L3 uint8_t* Xc, int ks, half8_t (&nxt)[GT_NI], int nb,
                         const QMM_L3 uint8_t* Wc, int sh) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             __builtin_amdgcn_sched_barrier(0);
-            if (nb >= 0) decode2(nxt, 2 * h, Wc, nb, sh);
+            if (nb >= 0) decode2(nxt, NH * h, Wc, nb, sh);
 #pragma unroll
-            for (int j = 4 * h; j < 4 * h + 4; ++j) {
+            for (int j = (GT_NJ / 2) * h; j < (GT_NJ / 2) * (h + 1); ++j) {
                 const half8_t bf = *reinterpret_cast<const QMM_L3 half8_t*>(Xc + xoff[ks] + j * 16 * 128);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < GT_NI; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bf, acc[i][j], 0, 0, 0);
             }
         }
@@ -421,7 +434,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         constexpr bool PRE = KPS == 2 && !XF32;
         if constexpr (!(PRE && KK == 1)) {
             decode2(a0, 0, Wc, 2 * KK, SH);
-            decode2(a0, 2, Wc, 2 * KK, SH);
+            decode2(a0, NH, Wc, 2 * KK, SH);
         }
         mfma_sub(a0, Xc, 0, a1, 2 * KK + 1, Wc, SH);
         mfma_sub(a1, Xc, 1, a0, (PRE && KK == 0) ? 2 : -1, Wc, SH);
@@ -469,12 +482,12 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         const int Mo = GATED ? 2 * M : M;
         float* P = Y + static_cast<int64_t>(split) * T * Mo;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = GATED ? m0 + 32 * wm + 16 * (i & 1) + er : m0 + 64 * wm + 16 * i + er;
-            const int col = (GATED && i >= 2 ? M : 0) + m;
+        for (int i = 0; i < GT_NI; ++i) {
+            const int m = GATED ? m0 + (GT_RW / 2) * wm + 16 * (i % NH) + er : m0 + GT_RW * wm + 16 * i + er;
+            const int col = (GATED && i >= NH ? M : 0) + m;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = t0 + 128 * wn + 16 * j + ec;
+            for (int j = 0; j < GT_NJ; ++j) {
+                const int t = t0 + GT_TW * wn + 16 * j + ec;
                 if (t < T && m < M) {
                     const float h[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
                     store4(P + static_cast<int64_t>(t) * Mo + col, m, h);
@@ -482,18 +495,18 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
             }
         }
     } else {
-        constexpr int NOUT = GATED ? 2 : 4;  // output fragments per wave
+        constexpr int NOUT = GATED ? NH : GT_NI;  // output fragments per wave
 #pragma unroll
         for (int i = 0; i < NOUT; ++i) {
-            const int m = m0 + (GATED ? 32 * wm : 64 * wm) + 16 * i + er;
+            const int m = m0 + (GATED ? (GT_RW / 2) * wm : GT_RW * wm) + 16 * i + er;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = t0 + 128 * wn + 16 * j + ec;
+            for (int j = 0; j < GT_NJ; ++j) {
+                const int t = t0 + GT_TW * wn + 16 * j + ec;
                 if (t < T && m < M) {
                     float h[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        h[e] = GATED ? silu(acc[i][j][e]) * acc[i + 2][j][e] : acc[i][j][e];
+                        h[e] = GATED ? silu(acc[i][j][e]) * acc[i + NH][j][e] : acc[i][j][e];
                     store4(Y + static_cast<int64_t>(t) * M + m, m, h);
                 }
             }
