@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-smollm", action="store_true")
+    p.add_argument("--no-small-batch", action="store_true")
     p.add_argument("--suite", default=None, help="write per-kernel details as JSON to this path")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
@@ -205,6 +206,96 @@ def smollm2_step(torch, qmm, si, steps):
     return out
 
 
+def small_batch(torch, qmm, si, reps=20):
+    """Decode GEMV at N in {1,2,4,8,16} on the Llama-3-8B shapes, F16 / Q8_0 / Q4_0.
+
+    Each (format, shape) rotates through weight copies totalling >= 512 MB, so every
+    call streams from HBM rather than the 256 MB Infinity Cache (values are random
+    bytes: timing only; parity is covered by the tests).  Reports weight GB/s of the
+    VALU streaming path, of the MFMA path, and of qmm_gemv's own choice, per N, and
+    the smallest N at which the MFMA path is faster (the crossover).
+    """
+    L = si.LLAMA3_8B
+    H, I, Q = L["hidden"], L["intermediate"], si.qkv_rows(L)
+    shapes = [("qkv", Q, H), ("o", H, H), ("gate_up", I, H), ("down", H, I)]
+    dev = torch.device("cuda")
+    Ns = (1, 2, 4, 8, 16)
+    x = torch.randn(16 * I, device=dev)
+    y = torch.empty(16 * I, device=dev)
+    out = {}
+    for fmt in (si.FMT_F16, si.FMT_Q8_0, si.FMT_Q4_0):
+        name = si.FMT_NAMES[fmt]
+        res = {v: {n: [0.0, 0.0] for n in Ns} for v in ("valu", "mfma", "auto")}  # bytes, ms
+        for sname, M, K in shapes:
+            n_mats = 2 if sname == "gate_up" else 1
+            nbytes = n_mats * M * qmm.qmm_row_bytes(fmt, K)
+            copies = max(1, -(-(512 << 20) // nbytes))
+            pool = [[torch.randint(0, 256, (M * qmm.qmm_row_bytes(fmt, K),), dtype=torch.uint8, device=dev)
+                     for _ in range(n_mats)] for _ in range(copies)]
+            for n in Ns:
+                for v, code in (("valu", 1), ("mfma", 2), ("auto", 0)):
+                    def call(i, n=n, code=code):
+                        w = pool[i % copies]
+                        if sname == "gate_up":
+                            if code == 0:
+                                qmm.qmm_gate_up_silu(fmt, w[0], w[1], x, y, M, K, n)
+                            else:
+                                qmm.qmm_gate_up_silu_variant(fmt, w[0], w[1], x, y, M, K, n, code)
+                        else:
+                            qmm.qmm_gemv_variant(fmt, w[0], x, y, M, K, n, code)
+                    for i in range(3):
+                        call(i)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for i in range(reps):
+                        call(i)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    res[v][n][0] += nbytes
+                    res[v][n][1] += e0.elapsed_time(e1) / reps
+            del pool
+        gbs = {v: {n: round(b / (ms * 1e-3) / 1e9, 1) for n, (b, ms) in d.items()} for v, d in res.items()}
+        cross = next((n for n in Ns if gbs["mfma"][n] > gbs["valu"][n]), None)
+        out[name] = {"weight_GBps": gbs, "mfma_faster_from_N": cross}
+    return out
+
+
+def ceilings(torch):
+    """Achievable ceilings measured with vendor code (never linked into qmm): a 2 GiB
+    device-to-device copy (bytes read + bytes written per second) and fp16
+    torch.matmul at the prefill shapes."""
+    dev = torch.device("cuda")
+    a = torch.ones(1 << 29, device=dev)  # 2 GiB fp32
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 31) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del a, b
+    mm = []
+    for (M, K) in ((14336, 4096), (4096, 14336)):
+        B = torch.randn(M, K, device=dev).half()
+        for T in (128, 2048, 4096):
+            A = torch.randn(T, K, device=dev).half()
+            for _ in range(3):
+                torch.matmul(A, B.t())
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                torch.matmul(A, B.t())
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            mm.append({"M": M, "K": K, "T": T, "TFLOPs": round(2.0 * T * M * K / (ms * 1e-3) / 1e12, 1)})
+    return {"copy_read_plus_write_GBps": round(copy_gbs, 1), "torch_fp16_matmul": mm}
+
+
 def traffic_for(kernel_file, launch_key):
     """HBM bytes per launch from the committed counter summary, if the kernel source is unchanged."""
     import hashlib
@@ -346,6 +437,10 @@ def main():
                                 "cases": details}
     if not args.no_smollm:
         line["smollm2_135m_decode_step"] = smollm2_step(torch, qmm, si, max(10, args.steps))
+    if not args.no_small_batch:
+        line["small_batch_decode"] = small_batch(torch, qmm, si)
+    if not (args.no_prefill or args.no_small_batch):
+        line["ceilings"] = ceilings(torch)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(host, fmts)
     if args.suite:

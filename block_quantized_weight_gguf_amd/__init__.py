@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "QMM_F16", "QMM_Q4_0", "QMM_Q8_0", "QMM_VARIANT_AUTO", "QMM_VARIANT_VALU", "QMM_VARIANT_MFMA",
     "QmmError", "lib_path", "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv",
-    "qmm_gemv_variant", "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gemm", "qmm_gemm_gate_up_silu",
+    "qmm_gemv_variant", "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
+    "qmm_gemm_gate_up_silu",
     "gemv", "gate_up_silu", "gemm", "gemm_gate_up_silu", "dequant",
 ]
 
@@ -44,6 +45,7 @@ _SIGS = {
     "qmm_gemv_variant": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
     "qmm_gemv_choose": (_i32, [_i32, _i64, _i64, _i64]),
     "qmm_gate_up_silu": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "qmm_gate_up_silu_variant": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
     "qmm_gemm": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "qmm_gemm_gate_up_silu": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
@@ -121,6 +123,11 @@ def qmm_gate_up_silu(fmt, Wg, Wu, x, h, I, K, N, stream=None) -> None:
            "qmm_gate_up_silu")
 
 
+def qmm_gate_up_silu_variant(fmt, Wg, Wu, x, h, I, K, N, variant, stream=None) -> None:
+    _check(_lib.qmm_gate_up_silu_variant(fmt, _ptr(Wg), _ptr(Wu), _ptr(x), _ptr(h), I, K, N, variant,
+                                         _stream(stream)), "qmm_gate_up_silu_variant")
+
+
 def qmm_gemm(fmt, W, X, Y, M, K, T, stream=None) -> None:
     _check(_lib.qmm_gemm(fmt, _ptr(W), _ptr(X), _ptr(Y), M, K, T, _stream(stream)), "qmm_gemm")
 
@@ -151,10 +158,10 @@ def gemv(fmt, W, x, M, K, out=None, variant=QMM_VARIANT_AUTO, stream=None):
     return out
 
 
-def gate_up_silu(fmt, Wg, Wu, x, I, K, out=None, stream=None):
+def gate_up_silu(fmt, Wg, Wu, x, I, K, out=None, variant=QMM_VARIANT_AUTO, stream=None):
     N = 1 if x.dim() == 1 else x.shape[0]
     out = _out((N, I), x, out)
-    qmm_gate_up_silu(fmt, Wg, Wu, x, out, I, K, N, stream)
+    qmm_gate_up_silu_variant(fmt, Wg, Wu, x, out, I, K, N, variant, stream)
     return out
 
 

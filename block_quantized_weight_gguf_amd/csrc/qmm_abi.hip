@@ -113,15 +113,22 @@ int qmm_gemv(int fmt, const void* W, const float* x, float* y, int64_t M, int64_
     return qmm_gemv_variant(fmt, W, x, y, M, K, N, QMM_VARIANT_AUTO, stream);
 }
 
-int qmm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, float* h, int64_t I, int64_t K,
-                     int64_t N, void* stream) {
+int qmm_gate_up_silu_variant(int fmt, const void* Wg, const void* Wu, const float* x, float* h, int64_t I,
+                             int64_t K, int64_t N, int variant, void* stream) {
     if (!Wg || !Wu || !x || !h) return QMM_ERR_NULL;
     int st = check_shape(fmt, I, K, N);
     if (st) return st;
     if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(x, 16) || !aligned(h, 4)) return QMM_ERR_ALIGN;
+    if (variant == QMM_VARIANT_AUTO) variant = qmm_gemv_choose(fmt, I, K, N);
     auto s = static_cast<hipStream_t>(stream);
-    if (N >= mfma_threshold(fmt)) return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, x, true, h, I, K, N, s));
-    return from_hip(qmm::launch_gemv_valu(fmt, Wg, Wu, x, h, I, K, N, s));
+    if (variant == QMM_VARIANT_VALU) return from_hip(qmm::launch_gemv_valu(fmt, Wg, Wu, x, h, I, K, N, s));
+    if (variant == QMM_VARIANT_MFMA) return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, x, true, h, I, K, N, s));
+    return QMM_ERR_VARIANT;
+}
+
+int qmm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, float* h, int64_t I, int64_t K,
+                     int64_t N, void* stream) {
+    return qmm_gate_up_silu_variant(fmt, Wg, Wu, x, h, I, K, N, QMM_VARIANT_AUTO, stream);
 }
 
 int qmm_gemm(int fmt, const void* W, const void* X, float* Y, int64_t M, int64_t K, int64_t T, void* stream) {

@@ -70,10 +70,10 @@ typedef enum {
     QMM_ERR_ALIGN = -4,       /* a pointer violates the alignment rule above       */
     QMM_ERR_OVERFLOW = -5,    /* a byte count does not fit in int64                */
     QMM_ERR_HIP = -6,         /* the HIP runtime reported an error at launch       */
-    QMM_ERR_VARIANT = -7      /* unknown variant id passed to qmm_gemv_variant     */
+    QMM_ERR_VARIANT = -7      /* unknown variant id passed to a *_variant call     */
 } qmm_status;
 
-/* Variant ids for qmm_gemv_variant / qmm_gemv_choose. */
+/* Variant ids for qmm_gemv_variant, qmm_gate_up_silu_variant and qmm_gemv_choose. */
 typedef enum {
     QMM_VARIANT_AUTO = 0,     /* library picks from (fmt, M, K, N)                          */
     QMM_VARIANT_VALU = 1,     /* register-decode GEMV: one weight read, N fp32 FMAs          */
@@ -140,6 +140,10 @@ int qmm_gemv_choose(int fmt, int64_t M, int64_t K, int64_t N);
  */
 int qmm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, float* h,
                      int64_t I, int64_t K, int64_t N, void* stream);
+
+/* As qmm_gate_up_silu with an explicit variant (QMM_VARIANT_*), for crossover sweeps. */
+int qmm_gate_up_silu_variant(int fmt, const void* Wg, const void* Wu, const float* x, float* h,
+                             int64_t I, int64_t K, int64_t N, int variant, void* stream);
 
 /*
  * Prefill GEMM: Y[t][m] = sum_k W[m][k] * X[t][k], X fp16 (T x K), Y fp32 (T x M).

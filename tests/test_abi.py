@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_expected_api():
     assert declared_functions() == sorted([
         "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv", "qmm_gemv_variant",
-        "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gemm", "qmm_gemm_gate_up_silu"])
+        "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
+        "qmm_gemm_gate_up_silu"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -117,6 +118,11 @@ def test_variant_choice():
     assert L.qmm_gemv_variant(8, A16, A16, A16 + 1, 4, 64, 1, 9, None) == E_ALIGN
     assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, 9, None) == E_VAR
     assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, -1, None) == E_VAR
+    assert L.qmm_gate_up_silu_variant(8, A16, None, A16, A16, 4, 64, 1, 1, None) == E_NULL
+    assert L.qmm_gate_up_silu_variant(3, A16, A16, A16, A16, 4, 64, 1, 1, None) == E_FMT
+    assert L.qmm_gate_up_silu_variant(8, A16, A16, A16, A16, 4, 48, 1, 1, None) == E_SHAPE
+    assert L.qmm_gate_up_silu_variant(8, A16, A16 + 8, A16, A16, 4, 64, 1, 1, None) == E_ALIGN
+    assert L.qmm_gate_up_silu_variant(8, A16, A16, A16, A16, 4, 64, 1, 5, None) == E_VAR
 
 
 def test_binding_raises():

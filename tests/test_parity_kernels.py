@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 FMTS = [si.FMT_Q8_0, si.FMT_Q4_0, si.FMT_F16]
 FID = {si.FMT_Q8_0: "q8_0", si.FMT_Q4_0: "q4_0", si.FMT_F16: "f16"}
-VALU, MFMA = qmm.QMM_VARIANT_VALU, qmm.QMM_VARIANT_MFMA
+AUTO, VALU, MFMA = qmm.QMM_VARIANT_AUTO, qmm.QMM_VARIANT_VALU, qmm.QMM_VARIANT_MFMA
 
 
 def _seed(*parts):
@@ -165,15 +165,16 @@ def test_gemv_auto_matches_choice():
 # -------------------------------------------------------------- gate + up
 @pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
 @pytest.mark.parametrize("I,K,N", [(1, 32, 1), (96, 128, 2), (1536, 576, 1), (300, 4096, 3), (64, 576, 8),
-                                   (50, 4160, 4), (130, 96, 20)])
-def test_gate_up_silu(fmt, I, K, N):
+                                   (50, 4160, 4), (130, 96, 20), (200, 4096, 16)])
+@pytest.mark.parametrize("variant", [AUTO, VALU, MFMA], ids=["auto", "valu", "mfma"])
+def test_gate_up_silu(fmt, I, K, N, variant):
     seed = 2000 + I + K + N
     rg = si.weights(fmt, I, K, seed)
     ru = si.weights(fmt, I, K, seed + 1)
     x = si.activations(N, K, seed + 2) * 2.0
-    announce(f"qmm_gate_up_silu fmt={fmt} I={I} K={K} N={N} seed={seed}")
+    announce(f"qmm_gate_up_silu_variant fmt={fmt} I={I} K={K} N={N} variant={variant} seed={seed}")
     buf = poisoned(N * I)
-    qmm.qmm_gate_up_silu(fmt, dev(rg), dev(ru), dev(x), buf, I, K, N)
+    qmm.qmm_gate_up_silu_variant(fmt, dev(rg), dev(ru), dev(x), buf, I, K, N, variant)
     torch.cuda.synchronize()
     assert guard_intact(buf, N * I)
     h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, x, I, K)
