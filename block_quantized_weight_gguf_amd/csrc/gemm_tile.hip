@@ -47,14 +47,11 @@
 #include <mutex>
 #include <type_traits>
 
+#include "mfma_tile.hpp"
 #include "qmm_common.hpp"
 #include "qmm_internal.hpp"
 
 namespace qmm {
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int GT_BM = 256;
 constexpr int GT_BN = 256;
@@ -63,88 +60,6 @@ constexpr int GT_THREADS = 512;
 constexpr int GT_WAVES = GT_THREADS / 64;
 constexpr int GT_GROUP_M = 4;
 
-
-__device__ __forceinline__ uint32_t h2_bits(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
-__device__ __forceinline__ half2_t bits_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
-
-// Two bytes (selected by `sel`) of `c` as halves 1024 + byte, i.e. bits 0x64bb.
-__device__ __forceinline__ half2_t bytes_to_h2(uint32_t c, uint32_t sel) {
-    return bits_h2(__builtin_amdgcn_perm(0x64646464u, c, sel));
-}
-constexpr uint32_t kSelLo = 0x05010400u;  // bytes 0, 1
-constexpr uint32_t kSelHi = 0x05030402u;  // bytes 2, 3
-
-// 4 Q8_0 codes (one dword) -> 4 fp16 weights fp16(d * q) in 2 dwords.
-__device__ __forceinline__ void q8_4(uint32_t codes, half2_t d2, uint32_t& o0, uint32_t& o1) {
-    const uint32_t c = codes ^ 0x80808080u;  // q + 128 as unsigned bytes
-    const half2_t off = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
-    o0 = h2_bits((bytes_to_h2(c, kSelLo) + off) * d2);
-    o1 = h2_bits((bytes_to_h2(c, kSelHi) + off) * d2);
-}
-
-// 4 Q4_0 nibbles (one per byte, already masked) -> 4 fp16 weights fp16(d * (n - 8)).
-__device__ __forceinline__ void q4_4(uint32_t nib, half2_t d2, uint32_t& o0, uint32_t& o1) {
-    const half2_t off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
-    o0 = h2_bits((bytes_to_h2(nib, kSelLo) + off) * d2);
-    o1 = h2_bits((bytes_to_h2(nib, kSelHi) + off) * d2);
-}
-
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-    return h2_bits(half2_t{static_cast<_Float16>(a), static_cast<_Float16>(b)});
-}
-
-#define QMM_G1 __attribute__((address_space(1)))
-#define QMM_L3 __attribute__((address_space(3)))
-
-// Weight stage geometry: K steps per stage, 16-byte chunks per row window, and
-// the bytes of the per-row segment one stage covers.
-template <int FMT>
-struct WStage;
-template <>
-struct WStage<8> {  // Q8_0: 4 blocks = 136 bytes, in 9 chunks
-    static constexpr int KPS = 2, WCH = 9;
-};
-template <>
-struct WStage<2> {  // Q4_0: 4 blocks = 72 bytes, in 5 chunks
-    static constexpr int KPS = 2, WCH = 5;
-};
-template <>
-struct WStage<1> {  // F16: 64 halfs = 128 bytes
-    static constexpr int KPS = 1, WCH = 8;
-};
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for the LDS stages.  A release fence would wait for every
-// outstanding global->LDS DMA (they count as LDS writes), including the prefetches
-// that must stay in flight; instead each wave waits explicitly for the DMA it needs
-// (wait_vm) and for its own LDS stores (lgkmcnt), and the empty asm statements keep
-// the compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Buffer resource over [base, base + bytes) (raw addressing, 32-bit data format;
-// reads past `bytes` return zeros instead of faulting).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int n = static_cast<int>(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
-}
-
-// One 16-byte buffer->LDS DMA per lane: lane L's bytes (resource + voff + soff) land
-// at lds + 16 L.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, QMM_L3 uint8_t* lds) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (QMM_L3 void*)lds, 16, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
-}
 
 // SPLIT: the workgroup computes the K steps [split * ksteps, (split + 1) * ksteps) of
 // its tile and stores the raw partial sums to Y[split][T][Mo] (Mo = M, or 2 M for the
@@ -337,41 +252,10 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
             // Swizzled 128-byte rows; the row's swizzle key is l & 7.
             return *reinterpret_cast<const QMM_L3 half8_t*>(Wsrc + rowb + (((4 * b + q4) ^ (lane & 7)) << 4));
         } else {
-            const int o = sh + BB * b;  // block start inside the row window
-            const QMM_L3 uint32_t* dw = reinterpret_cast<const QMM_L3 uint32_t*>(Wsrc + rowb);
-            uint32_t d, c0, c1;
-            const int cb = (FMT == 8) ? 8 * q4 : 8 * (q4 & 1);  // code byte offset in the block
-            if ((o & 3) == 0) {
-                d = dw[o >> 2] & 0xFFFFu;
-                const int base = (o + cb) >> 2;  // codes start 2 bytes into dword `base`
-                const uint32_t w0 = dw[base], w1 = dw[base + 1], w2 = dw[base + 2];
-                c0 = align_bytes(w1, w0, 2);
-                c1 = align_bytes(w2, w1, 2);
-            } else {
-                d = dw[(o - 2) >> 2] >> 16;
-                const int base = (o + 2 + cb) >> 2;
-                c0 = dw[base];
-                c1 = dw[base + 1];
-            }
-            const half2_t d2 = bits_h2(d | (d << 16));
-            uint32_t r0, r1, r2, r3;
-            if constexpr (FMT == 8) {
-                q8_4(c0, d2, r0, r1);
-                q8_4(c1, d2, r2, r3);
-            } else {
-                const uint32_t s4 = 4 * (q4 >> 1);  // fragments 2, 3 take the high nibbles
-                q4_4((c0 >> s4) & 0x0F0F0F0Fu, d2, r0, r1);
-                q4_4((c1 >> s4) & 0x0F0F0F0Fu, d2, r2, r3);
-            }
-            return __builtin_bit_cast(half8_t, u32x4_t{r0, r1, r2, r3});
+            return frag_raw<FMT>(Wsrc + rowb, sh + BB * b, q4);  // block start inside the row window
         }
     };
 
-    // A fragments are software-pipelined: the 4 fragments of a 32-wide sub-step are
-    // decoded while the MFMAs of the previous sub-step run (token fragments are
-    // streamed from LDS one at a time).  Within a weight stage the next step's first
-    // sub-step is decoded during the current step's second one; across stages that
-    // decode has to wait for the barrier that publishes the new stage.
     half8_t a0[GT_NI], a1[GT_NI];
     // Decode fragments i0 .. i0 + NH - 1 of block b into a.
     auto decode2 = [&](half8_t (&a)[GT_NI], int i0, const QMM_L3 uint8_t* Wc, int b, int sh) {
@@ -565,10 +449,18 @@ static void launch_tile_t(const void* W, const void* Wu, const void* X, float* Y
                        static_cast<int>(M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0), nsplit, ksteps);
 }
 
+void launch_splitk_reduce(const float* P, float* Y, int64_t T, int64_t M, int nsplit, bool gated, hipStream_t s) {
+    const int vec = M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+    const int64_t n = T * M / (vec ? 4 : 1);
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 256 * 16));
+    if (gated) hipLaunchKernelGGL(splitk_reduce<true>, dim3(grid), dim3(256), 0, s, P, Y, T, M, nsplit, vec);
+    else hipLaunchKernelGGL(splitk_reduce<false>, dim3(grid), dim3(256), 0, s, P, Y, T, M, nsplit, vec);
+}
+
 // Stream-ordered workspace for split-K partials: a memory pool of this library per
 // device, which keeps freed blocks for reuse (so steady-state calls do not go to the
 // driver) and orders reuse by stream.
-static hipMemPool_t splitk_pool() {
+hipMemPool_t workspace_pool() {
     static std::mutex mu;
     static hipMemPool_t pools[64] = {};
     int dev = 0;
@@ -616,7 +508,7 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
     float* P = nullptr;
     if (nsplit > 1) {
         const size_t bytes = static_cast<size_t>(nsplit) * T * (gated ? 2 * M : M) * sizeof(float);
-        hipMemPool_t pool = splitk_pool();
+        hipMemPool_t pool = workspace_pool();
         if (!pool || hipMallocFromPoolAsync(reinterpret_cast<void**>(&P), bytes, pool, s) != hipSuccess) {
             (void)hipGetLastError();
             P = nullptr;
@@ -636,11 +528,7 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
         if (fmt == 8) { QMM_TILE_CASE(8, true, P) }
         else if (fmt == 2) { QMM_TILE_CASE(2, true, P) }
         else { QMM_TILE_CASE(1, true, P) }
-        const int vec = M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
-        const int64_t n = T * M / (vec ? 4 : 1);
-        const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 256 * 16));
-        if (gated) hipLaunchKernelGGL(splitk_reduce<true>, dim3(grid), dim3(256), 0, s, P, Y, T, M, nsplit, vec);
-        else hipLaunchKernelGGL(splitk_reduce<false>, dim3(grid), dim3(256), 0, s, P, Y, T, M, nsplit, vec);
+        launch_splitk_reduce(P, Y, T, M, nsplit, gated, s);
         (void)hipFreeAsync(P, s);
     } else {
         if (fmt == 8) { QMM_TILE_CASE(8, false, Y) }

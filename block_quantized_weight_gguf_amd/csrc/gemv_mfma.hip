@@ -1,0 +1,326 @@
+// Small-batch decode GEMV on the matrix cores: y[n][m] = sum_k W[m][k] x[n][k] for a
+// few tokens (2..32), Q8_0 / Q4_0 weights, fp32 x rounded to fp16, fp32 accumulate.
+//
+// ("llama.cpp Metal ...", section 3.2 and P9: a batched mat-vec for a handful of
+// tokens, each weight read once and reused for every token; "EdgeRunner Core
+// Architecture", section 3.4 Tier 1: the raw blocks are the only large operand.)
+//
+// Like single-token decode this is bound by the weight stream, so the kernel is a
+// weight-streaming loop whose dot products happen to run on v_mfma_f32_16x16x32_f16:
+//   * A workgroup (8 waves, one per CU: LDS-limited) owns 256 weight rows and a
+//     range of K.  Each wave owns 32 rows: 2 MFMA row fragments; the tokens (padded
+//     to 16 or 32) are 1 or 2 column fragments.
+//   * x for the workgroup's K range is converted to fp16 into LDS once (rows padded
+//     by 16 bytes so that the 16 token rows of a fragment read hit distinct banks).
+//   * Weights stream through a ring of 3 LDS stages by buffer->LDS DMA, each stage
+//     the raw GGUF bytes of 4 blocks of all 256 rows (16-byte chunks of the row
+//     windows, whole 128-byte lines per load instruction).  Two stages are always
+//     in flight, ~70 KB per CU, which covers HBM latency at the per-CU share of the
+//     bandwidth.
+//   * Each wave decodes its A fragments straight from the raw bytes in the fp16
+//     domain (shared with the prefill GEMM) and issues 2 x (tokens / 16) MFMAs per
+//     block: the matrix cores do the multiply-adds, the VALU only decodes.
+//   * When the rows alone cannot fill the machine (or K is long), K is split over
+//     several workgroups; their partial sums go to a stream-ordered workspace and a
+//     second kernel adds them in a fixed order and applies the gated epilogue.
+//   * Gated instance: stage rows 0..127 are 128 gate rows and 128..255 the up rows
+//     of the same outputs; each wave takes 16 gate and the matching 16 up rows.
+#include <algorithm>
+#include <type_traits>
+
+#include "mfma_tile.hpp"
+#include "qmm_common.hpp"
+#include "qmm_internal.hpp"
+
+namespace qmm {
+
+constexpr int GM_BM = 256;       // weight rows per workgroup
+constexpr int GM_THREADS = 512;  // 8 waves
+constexpr int GM_WAVES = GM_THREADS / 64;
+constexpr int GM_STAGE_K = 128;  // K per weight stage (4 blocks)
+
+// K range per workgroup that fits x in LDS next to the weight ring.
+template <int NJ>
+struct GmGeom {
+    static constexpr int KRMAX = 1024 / NJ;           // halfs of x per token row
+    static constexpr int XSTR = KRMAX * 2 + 16;       // bytes per token row (+16: banks)
+    static constexpr int XBYTES = 16 * NJ * XSTR;
+    static constexpr int SMAX = KRMAX / GM_STAGE_K;   // stages per workgroup, at most
+};
+
+template <int FMT, bool GATED, int NJ, bool SPLIT>
+__global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __restrict__ Wg,
+                                                                const uint8_t* __restrict__ Wu,
+                                                                const float* __restrict__ x, float* __restrict__ Y,
+                                                                int M, int K, int N, int nsplit, int kst, int vec) {
+    using G = WStage<FMT>;
+    using X = GmGeom<NJ>;
+    constexpr int BB = Fmt<FMT>::BB;
+    constexpr int WROW = G::WCH * 16;     // bytes per row in a weight stage
+    constexpr int WBYTES = GM_BM * WROW;  // bytes per weight stage
+    constexpr int WINST = WBYTES / 1024;  // wave-wide DMA instructions per stage
+    // Every wave issues WPER instructions per stage; surplus ones repeat the stage's
+    // last instruction (same bytes to the same place), keeping the wait counts fixed.
+    constexpr int WPER = (WINST + GM_WAVES - 1) / GM_WAVES;
+    static_assert(WINST % 2 == 0, "gate / up halves must split on instruction boundaries");
+
+    __shared__ __align__(16) uint8_t xs[X::XBYTES];
+    __shared__ __align__(16) uint8_t R0[WBYTES];
+    __shared__ __align__(16) uint8_t R1[WBYTES];
+    __shared__ __align__(16) uint8_t R2[WBYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nb = K / kQK;
+    const int64_t rb = static_cast<int64_t>(nb) * BB;
+    const int nst = K / GM_STAGE_K;
+
+    // ---- work unit: (row tile, K split); the splits of a tile are adjacent.
+    const int rows_per_tile = GATED ? GM_BM / 2 : GM_BM;
+    const int ntiles = (M + rows_per_tile - 1) / rows_per_tile;
+    const int unit = blockIdx.x;
+    if (unit >= ntiles * nsplit) return;
+    const int tile = unit / nsplit;
+    const int split = unit - tile * nsplit;
+    const int m0 = tile * rows_per_tile;
+    const int st0 = split * kst;
+    const int st1 = min(st0 + kst, nst);
+
+    // ---- weight DMA sources (buffer resource per matrix, lane offsets fixed).
+    const int wrows = min(rows_per_tile, M - m0);
+    const __amdgpu_buffer_rsrc_t wgr = make_rsrc(Wg + static_cast<int64_t>(m0) * rb, wrows * rb);
+    const __amdgpu_buffer_rsrc_t wur = GATED ? make_rsrc(Wu + static_cast<int64_t>(m0) * rb, wrows * rb) : wgr;
+    uint32_t woffs[WPER];
+#pragma unroll
+    for (int i = 0; i < WPER; ++i) {
+        // Wave instruction n covers items 64 n .. 64 n + 63: item q = chunk q % WCH of
+        // stage row q / WCH.  Rows past the end re-read the last row (never stored).
+        const int n = min(wave + GM_WAVES * i, WINST - 1);
+        const int q = 64 * n + lane;
+        const int R = q / G::WCH;
+        const int r = GATED ? (R & 127) : R;
+        woffs[i] = static_cast<uint32_t>(min(r, wrows - 1) * rb) + 16 * (q % G::WCH);
+    }
+    // Stage st holds the 16-byte aligned windows around the 4-block segment
+    // [136 st, 136 st + 136) (Q4_0: 72) of every row; the segment starts 0 or 8
+    // bytes into the window.
+    auto issue_w = [&](QMM_L3 uint8_t* Wd, int st) {
+        const uint32_t a = (static_cast<uint32_t>(st) * (4 * BB)) & ~15u;
+#pragma unroll
+        for (int i = 0; i < WPER; ++i) {
+            const int n = min(wave + GM_WAVES * i, WINST - 1);
+            dma16((GATED && n >= WINST / 2) ? wur : wgr, woffs[i], a, Wd + 1024 * n);
+        }
+    };
+
+    QMM_L3 uint8_t* W0 = (QMM_L3 uint8_t*)R0;
+    QMM_L3 uint8_t* W1 = (QMM_L3 uint8_t*)R1;
+    QMM_L3 uint8_t* W2 = (QMM_L3 uint8_t*)R2;
+    QMM_L3 uint8_t* XS = (QMM_L3 uint8_t*)xs;
+
+    // ---- x (fp32, N tokens) -> fp16 LDS rows for this K range; tokens >= N are zero.
+    // Loaded before the weight DMA is issued, so that waiting for x does not also
+    // wait for the weights.
+    const int k0 = st0 * GM_STAGE_K;
+    const int kr = (st1 - st0) * GM_STAGE_K;
+    {
+        constexpr int ITEMS_MAX = 16 * NJ * X::KRMAX / 8;
+        constexpr int PER = ITEMS_MAX / GM_THREADS;
+        float4 v[PER][2];
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int item = tid + GM_THREADS * p;
+            const int n = item / (X::KRMAX / 8), c = item % (X::KRMAX / 8);
+            if (n < N && 8 * c < kr) {
+                const float4* src = reinterpret_cast<const float4*>(x + static_cast<int64_t>(n) * K + k0 + 8 * c);
+                v[p][0] = src[0];
+                v[p][1] = src[1];
+            } else {
+                v[p][0] = v[p][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        issue_w(W0, st0);
+        issue_w(W1, min(st0 + 1, st1 - 1));
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int item = tid + GM_THREADS * p;
+            const int n = item / (X::KRMAX / 8), c = item % (X::KRMAX / 8);
+            const u32x4_t h = {pack_h2(v[p][0].x, v[p][0].y), pack_h2(v[p][0].z, v[p][0].w),
+                               pack_h2(v[p][1].x, v[p][1].y), pack_h2(v[p][1].z, v[p][1].w)};
+            *reinterpret_cast<QMM_L3 u32x4_t*>(XS + n * X::XSTR + 16 * c) = h;
+        }
+    }
+
+    float4_t acc[2][NJ];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int q4 = lane >> 4;
+    // A fragment i: stage row 32 w + 16 i + l % 16; gated: fragment 0 is gate row
+    // 16 w + l % 16, fragment 1 the up row of the same output.
+    auto arow = [&](int i) -> int {
+        if constexpr (GATED) return (i == 0 ? 16 * wave : 128 + 16 * wave) + (lane & 15);
+        else return 32 * wave + 16 * i + (lane & 15);
+    };
+    const int arow0 = arow(0) * WROW, arow1 = arow(1) * WROW;
+    // Token fragment j of block b: token 16 j + l % 16, halfs 8 q4 .. 8 q4 + 7 of the
+    // block's 32, at k_local = 128 (st - st0) + 32 b.
+    const int xoff = (lane & 15) * X::XSTR + 16 * q4;
+
+    // Stage st from ring slot Wc: wait for its DMA (the next stage's may stay in
+    // flight), barrier, refill the slot read on the previous stage with stage st + 2
+    // (past the end: the last stage again, into a slot nobody reads), compute.
+    // PAR_ is the stage's parity (st0 is even), which fixes the segment offset at
+    // compile time; with a run-time offset the compiler cannot tell the ring slots'
+    // reads from the DMA in flight and waits for all of it.
+    auto stage = [&](auto PAR_, QMM_L3 uint8_t* Wc, QMM_L3 uint8_t* Wn2, int st) {
+        constexpr int sh = 8 * decltype(PAR_)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<WPER>();
+        lds_barrier();
+        issue_w(Wn2, min(st + 2, st1 - 1));
+        const int kl = (st - st0) * GM_STAGE_K;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const half8_t a0 = frag_raw<FMT>(Wc + arow0, sh + BB * b, q4);
+            const half8_t a1 = frag_raw<FMT>(Wc + arow1, sh + BB * b, q4);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const half8_t bf =
+                    *reinterpret_cast<const QMM_L3 half8_t*>(XS + xoff + j * 16 * X::XSTR + 2 * (kl + 32 * b));
+                acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bf, acc[0][j], 0, 0, 0);
+                acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bf, acc[1][j], 0, 0, 0);
+            }
+        }
+    };
+    // Two turns of the ring per iteration (static slots and parities, no branches
+    // inside, which keeps the compiler's own wait tracking exact); the remaining
+    // 0-5 stages after it.
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int st = st0;
+    for (; st + 6 <= st1; st += 6) {
+        stage(P0{}, W0, W2, st);
+        stage(P1{}, W1, W0, st + 1);
+        stage(P0{}, W2, W1, st + 2);
+        stage(P1{}, W0, W2, st + 3);
+        stage(P0{}, W1, W0, st + 4);
+        stage(P1{}, W2, W1, st + 5);
+    }
+    if (st < st1) stage(P0{}, W0, W2, st);
+    if (st + 1 < st1) stage(P1{}, W1, W0, st + 1);
+    if (st + 2 < st1) stage(P0{}, W2, W1, st + 2);
+    if (st + 3 < st1) stage(P1{}, W0, W2, st + 3);
+    if (st + 4 < st1) stage(P0{}, W1, W0, st + 4);
+    // Drain the trailing re-load DMAs before the workgroup can exit.
+    wait_vm<0>();
+
+    // ---- epilogue.  D fragment: lane l holds rows 4 (l / 16) + e of token l % 16.
+    const int er = 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int t = 16 * j + (lane & 15);
+        if (t >= N) continue;
+        auto store4 = [&](float* yp, int m, const float (&h)[4]) {
+            if (vec) {
+                *reinterpret_cast<float4*>(yp) = make_float4(h[0], h[1], h[2], h[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (m + e < M) yp[e] = h[e];
+            }
+        };
+        if constexpr (SPLIT) {
+            const int Mo = GATED ? 2 * M : M;
+            float* P = Y + (static_cast<int64_t>(split) * N + t) * Mo;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int m = GATED ? m0 + 16 * wave + er : m0 + 32 * wave + 16 * i + er;
+                const int col = (GATED && i == 1 ? M : 0) + m;
+                if (m < M) {
+                    const float h[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                    store4(P + col, m, h);
+                }
+            }
+        } else if constexpr (GATED) {
+            const int m = m0 + 16 * wave + er;
+            if (m < M) {
+                float h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = silu(acc[0][j][e]) * acc[1][j][e];
+                store4(Y + static_cast<int64_t>(t) * M + m, m, h);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int m = m0 + 32 * wave + 16 * i + er;
+                if (m < M) {
+                    const float h[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                    store4(Y + static_cast<int64_t>(t) * M + m, m, h);
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, bool GATED, int NJ, bool SPLIT>
+static void launch_gm_t(const void* W, const void* Wu, const float* x, float* Y, int64_t M, int64_t K, int64_t N,
+                        int nsplit, int kst, hipStream_t s) {
+    const int64_t rows_per_tile = GATED ? GM_BM / 2 : GM_BM;
+    const int64_t ntiles = (M + rows_per_tile - 1) / rows_per_tile;
+    const int vec = M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+    hipLaunchKernelGGL((gemv_mfma_kernel<FMT, GATED, NJ, SPLIT>), dim3(static_cast<unsigned>(ntiles * nsplit)),
+                       dim3(GM_THREADS), 0, s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), x, Y,
+                       static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), nsplit, kst, vec);
+}
+
+template <int FMT, int NJ>
+static bool launch_gm_nj(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, int64_t N,
+                         hipStream_t s) {
+    const bool gated = Wu != nullptr;
+    const int64_t rows_per_tile = gated ? GM_BM / 2 : GM_BM;
+    const int64_t ntiles = (M + rows_per_tile - 1) / rows_per_tile;
+    const int64_t nst = K / GM_STAGE_K;
+    // Stages per workgroup: enough units to give every CU work (about 256 of them),
+    // no more than x's LDS room allows, at least 2 so the ring has work to overlap.
+    // Even, so that every split starts on an even stage (the kernel's parity
+    // bookkeeping relies on it).
+    int64_t kst = (nst * ntiles + 255) / 256;
+    kst = std::max<int64_t>(2, std::min<int64_t>(kst, GmGeom<NJ>::SMAX));
+    kst = std::min(kst, nst);
+    kst = (kst + 1) / 2 * 2;
+    const int nsplit = static_cast<int>((nst + kst - 1) / kst);
+    if (ntiles * nsplit > (int64_t{1} << 30)) return false;
+    if (nsplit == 1) {
+        if (gated) launch_gm_t<FMT, true, NJ, false>(W, Wu, x, y, M, K, N, 1, static_cast<int>(kst), s);
+        else launch_gm_t<FMT, false, NJ, false>(W, Wu, x, y, M, K, N, 1, static_cast<int>(kst), s);
+        return true;
+    }
+    hipMemPool_t pool = workspace_pool();
+    float* P = nullptr;
+    const size_t bytes = static_cast<size_t>(nsplit) * N * (gated ? 2 * M : M) * sizeof(float);
+    if (!pool || hipMallocFromPoolAsync(reinterpret_cast<void**>(&P), bytes, pool, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    if (gated) launch_gm_t<FMT, true, NJ, true>(W, Wu, x, P, M, K, N, nsplit, static_cast<int>(kst), s);
+    else launch_gm_t<FMT, false, NJ, true>(W, Wu, x, P, M, K, N, nsplit, static_cast<int>(kst), s);
+    launch_splitk_reduce(P, y, N, M, nsplit, gated, s);
+    (void)hipFreeAsync(P, s);
+    return true;
+}
+
+bool launch_gemv_mfma(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                      int64_t N, hipStream_t s) {
+    if (fmt != 8 && fmt != 2) return false;
+    if (K % 256 != 0 || N < 1 || N > 32) return false;
+    // 32-bit lane offsets: 256 weight rows must span less than 2^31 bytes.
+    if (K > (int64_t{1} << 20)) return false;
+    if (N <= 16) return fmt == 8 ? launch_gm_nj<8, 1>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<2, 1>(W, Wu, x, y, M, K, N, s);
+    return fmt == 8 ? launch_gm_nj<8, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<2, 2>(W, Wu, x, y, M, K, N, s);
+}
+
+}  // namespace qmm

@@ -104,8 +104,11 @@ int qmm_gemv_variant(int fmt, const void* W, const float* x, float* y, int64_t M
     if (variant == QMM_VARIANT_AUTO) variant = qmm_gemv_choose(fmt, M, K, N);
     auto s = static_cast<hipStream_t>(stream);
     if (variant == QMM_VARIANT_VALU) return from_hip(qmm::launch_gemv_valu(fmt, W, nullptr, x, y, M, K, N, s));
-    if (variant == QMM_VARIANT_MFMA)
+    if (variant == QMM_VARIANT_MFMA) {
+        // Up to 32 tokens: the weight-streaming MFMA GEMV; otherwise the tiled GEMM.
+        if (qmm::launch_gemv_mfma(fmt, W, nullptr, x, y, M, K, N, s)) return from_hip(hipGetLastError());
         return from_hip(qmm::launch_gemm_mfma(fmt, W, nullptr, x, true, y, M, K, N, s));
+    }
     return QMM_ERR_VARIANT;
 }
 
@@ -122,7 +125,10 @@ int qmm_gate_up_silu_variant(int fmt, const void* Wg, const void* Wu, const floa
     if (variant == QMM_VARIANT_AUTO) variant = qmm_gemv_choose(fmt, I, K, N);
     auto s = static_cast<hipStream_t>(stream);
     if (variant == QMM_VARIANT_VALU) return from_hip(qmm::launch_gemv_valu(fmt, Wg, Wu, x, h, I, K, N, s));
-    if (variant == QMM_VARIANT_MFMA) return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, x, true, h, I, K, N, s));
+    if (variant == QMM_VARIANT_MFMA) {
+        if (qmm::launch_gemv_mfma(fmt, Wg, Wu, x, h, I, K, N, s)) return from_hip(hipGetLastError());
+        return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, x, true, h, I, K, N, s));
+    }
     return QMM_ERR_VARIANT;
 }
 

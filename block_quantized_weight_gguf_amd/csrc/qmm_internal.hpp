@@ -38,4 +38,18 @@ hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* 
 bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32, float* Y, int64_t M,
                       int64_t K, int64_t T, hipStream_t s);
 
+// Weight-streaming fp16-MFMA GEMV for 2..32 tokens (Q8_0 / Q4_0, K % 256 == 0): each
+// weight byte is read once per call.  Returns false, launching nothing, when it does
+// not apply.
+bool launch_gemv_mfma(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                      int64_t N, hipStream_t s);
+
+// Stream-ordered memory pool of this library for the current device (split-K
+// partials); nullptr if pools are unavailable.
+hipMemPool_t workspace_pool();
+
+// Y[t][m] = sum over s < nsplit of P[s][t][m] (gated: P holds gate sums in columns
+// 0..M-1 and up sums in M..2M-1 of each 2M-wide row, and Y = silu(gate) * up).
+void launch_splitk_reduce(const float* P, float* Y, int64_t T, int64_t M, int nsplit, bool gated, hipStream_t s);
+
 }  // namespace qmm

@@ -162,10 +162,31 @@ def test_gemv_auto_matches_choice():
         assert guard_intact(buf, N * M)
 
 
+# The MFMA variant for a handful of tokens (N <= 32, K % 256 == 0) streams the weights
+# once and runs the dot products on the matrix cores; shapes cover one and two token
+# fragments, ragged M, a single weight stage (K = 256), long K (split over workgroups)
+# and the partial last split.
+@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_0], ids=FID.get)
+@pytest.mark.parametrize("M,K,N", [(300, 2048, 5), (1000, 4096, 17), (33, 256, 32), (513, 14336, 9),
+                                   (257, 1280, 2), (4096, 768, 16)])
+def test_gemv_mfma_small_batch(fmt, M, K, N):
+    seed = 2500 + M + K + N
+    raw = si.weights(fmt, M, K, seed, scale_mode="gemm_wide", q8_low=-128)  # fp16(d*q) stays finite
+    x = si.activations(N, K, seed + 1)
+    announce(f"qmm_gemv_variant mfma small-batch fmt={fmt} M={M} K={K} N={N} seed={seed}")
+    buf = poisoned(N * M)
+    qmm.qmm_gemv_variant(fmt, dev(raw), dev(x), buf, M, K, N, MFMA)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, N * M)
+    # The MFMA variant rounds x to fp16: the oracle takes the same fp16 inputs.
+    y_ref, S = oracle.matmul_ref(fmt, raw, x.astype(np.float16), M, K)
+    check_linear(buf[:N * M].cpu().numpy().reshape(N, M), y_ref, S, f"gemv mfma fmt={fmt} M={M} K={K} N={N}")
+
+
 # -------------------------------------------------------------- gate + up
 @pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
 @pytest.mark.parametrize("I,K,N", [(1, 32, 1), (96, 128, 2), (1536, 576, 1), (300, 4096, 3), (64, 576, 8),
-                                   (50, 4160, 4), (130, 96, 20), (200, 4096, 16)])
+                                   (50, 4160, 4), (130, 96, 20), (200, 4096, 16), (130, 256, 3), (200, 2816, 24)])
 @pytest.mark.parametrize("variant", [AUTO, VALU, MFMA], ids=["auto", "valu", "mfma"])
 def test_gate_up_silu(fmt, I, K, N, variant):
     seed = 2000 + I + K + N
