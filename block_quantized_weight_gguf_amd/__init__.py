@@ -71,8 +71,13 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream) -> int | None:
     if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(torch.cuda.current_device())
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
         return stream

@@ -400,10 +400,13 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
 
 // Sums the split-K partials P[s][T][Mo] in split order and applies the epilogue
 // (gated: h = silu(sum of gate partials) * (sum of up partials)).  Four outputs per
-// thread when M % 4 == 0 (16-byte aligned rows), else one.
+// thread when M % 4 == 0 (16-byte aligned rows), else one.  The partials of each
+// output are loaded 8 at a time (independent loads in flight together) and added in
+// split order, so the result does not depend on the launch.
 template <bool GATED>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P, float* __restrict__ Y,
                                                      int64_t T, int64_t M, int nsplit, int vec) {
+    constexpr int B = 8;
     const int64_t Mo = GATED ? 2 * M : M;
     const int64_t plane = T * Mo;
     const int W = vec ? 4 : 1;
@@ -413,22 +416,48 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P
         const int64_t t = e * W / M, m = e * W - t * M;
         const float* p = P + t * Mo + m;
         if (vec) {
-            float4 g = *reinterpret_cast<const float4*>(p);
-            float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (GATED) u = *reinterpret_cast<const float4*>(p + M);
-            for (int s = 1; s < nsplit; ++s) {
+            float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+            int s = 0;
+            for (; s + B <= nsplit; s += B) {
+                float4 a[B], c[B];
+#pragma unroll
+                for (int i = 0; i < B; ++i) {
+                    a[i] = *reinterpret_cast<const float4*>(p + (s + i) * plane);
+                    if (GATED) c[i] = *reinterpret_cast<const float4*>(p + (s + i) * plane + M);
+                }
+#pragma unroll
+                for (int i = 0; i < B; ++i) {
+                    g.x += a[i].x; g.y += a[i].y; g.z += a[i].z; g.w += a[i].w;
+                    if (GATED) { u.x += c[i].x; u.y += c[i].y; u.z += c[i].z; u.w += c[i].w; }
+                }
+            }
+            for (; s < nsplit; ++s) {
                 const float4 a = *reinterpret_cast<const float4*>(p + s * plane);
                 g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
                 if (GATED) {
-                    const float4 b = *reinterpret_cast<const float4*>(p + s * plane + M);
-                    u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+                    const float4 c = *reinterpret_cast<const float4*>(p + s * plane + M);
+                    u.x += c.x; u.y += c.y; u.z += c.z; u.w += c.w;
                 }
             }
             if (GATED) g = make_float4(silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
             *reinterpret_cast<float4*>(Y + t * M + m) = g;
         } else {
-            float g = p[0], u = GATED ? p[M] : 0.0f;
-            for (int s = 1; s < nsplit; ++s) {
+            float g = 0.0f, u = 0.0f;
+            int s = 0;
+            for (; s + B <= nsplit; s += B) {
+                float a[B], c[B];
+#pragma unroll
+                for (int i = 0; i < B; ++i) {
+                    a[i] = p[(s + i) * plane];
+                    if (GATED) c[i] = p[(s + i) * plane + M];
+                }
+#pragma unroll
+                for (int i = 0; i < B; ++i) {
+                    g += a[i];
+                    if (GATED) u += c[i];
+                }
+            }
+            for (; s < nsplit; ++s) {
                 g += p[s * plane];
                 if (GATED) u += p[s * plane + M];
             }
@@ -481,6 +510,22 @@ hipMemPool_t workspace_pool() {
     return pools[dev];
 }
 
+float* workspace_alloc(size_t bytes, hipStream_t s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (cs != hipStreamCaptureStatusNone) return nullptr;
+    hipMemPool_t pool = workspace_pool();
+    float* P = nullptr;
+    if (!pool || hipMallocFromPoolAsync(reinterpret_cast<void**>(&P), bytes, pool, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    return P;
+}
+
 bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32, float* Y, int64_t M,
                       int64_t K, int64_t T, hipStream_t s) {
     // Block formats need 16-byte aligned rows (K % 256 == 0); F16 needs K % 64 == 0.
@@ -507,11 +552,8 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
     }
     float* P = nullptr;
     if (nsplit > 1) {
-        const size_t bytes = static_cast<size_t>(nsplit) * T * (gated ? 2 * M : M) * sizeof(float);
-        hipMemPool_t pool = workspace_pool();
-        if (!pool || hipMallocFromPoolAsync(reinterpret_cast<void**>(&P), bytes, pool, s) != hipSuccess) {
-            (void)hipGetLastError();
-            P = nullptr;
+        P = workspace_alloc(static_cast<size_t>(nsplit) * T * (gated ? 2 * M : M) * sizeof(float), s);
+        if (!P) {  // no workspace (or the stream is being captured): one workgroup per tile
             nsplit = 1;
             ksteps = static_cast<int>(nsteps);
         }

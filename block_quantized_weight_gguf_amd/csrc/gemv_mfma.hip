@@ -10,13 +10,13 @@
 //   * A workgroup (8 waves, one per CU: LDS-limited) owns 256 weight rows and a
 //     range of K.  Each wave owns 32 rows: 2 MFMA row fragments; the tokens (padded
 //     to 16 or 32) are 1 or 2 column fragments.
-//   * x for the workgroup's K range is converted to fp16 into LDS once (rows padded
-//     by 16 bytes so that the 16 token rows of a fragment read hit distinct banks).
-//   * Weights stream through a ring of 3 LDS stages by buffer->LDS DMA, each stage
-//     the raw GGUF bytes of 4 blocks of all 256 rows (16-byte chunks of the row
-//     windows, whole 128-byte lines per load instruction).  Two stages are always
-//     in flight, ~70 KB per CU, which covers HBM latency at the per-CU share of the
-//     bandwidth.
+//   * Weights and x stream through a ring of 3 LDS stages by buffer->LDS DMA.  A
+//     stage holds the raw GGUF bytes of 4 blocks of all 256 rows (16-byte chunks of
+//     the row windows, whole 128-byte lines per load instruction) and the fp32 x of
+//     the same 128-wide K range for every token (16-byte chunks XOR-swizzled by
+//     token, so that the 16 token rows of a fragment read hit distinct banks; x is
+//     rounded to fp16 as the fragments are read).  Two stages are always in flight,
+//     ~80 KB per CU, which covers HBM latency at the per-CU share of the bandwidth.
 //   * Each wave decodes its A fragments straight from the raw bytes in the fp16
 //     domain (shared with the prefill GEMM) and issues 2 x (tokens / 16) MFMAs per
 //     block: the matrix cores do the multiply-adds, the VALU only decodes.
@@ -40,34 +40,32 @@ constexpr int GM_WAVES = GM_THREADS / 64;
 constexpr int GM_STAGE_K = 128;  // K per weight stage (4 blocks)
 
 // K range per workgroup that fits x in LDS next to the weight ring.
-template <int NJ>
-struct GmGeom {
-    static constexpr int KRMAX = 1024 / NJ;           // halfs of x per token row
-    static constexpr int XSTR = KRMAX * 2 + 16;       // bytes per token row (+16: banks)
-    static constexpr int XBYTES = 16 * NJ * XSTR;
-    static constexpr int SMAX = KRMAX / GM_STAGE_K;   // stages per workgroup, at most
-};
-
 template <int FMT, bool GATED, int NJ, bool SPLIT>
 __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __restrict__ Wg,
                                                                 const uint8_t* __restrict__ Wu,
                                                                 const float* __restrict__ x, float* __restrict__ Y,
                                                                 int M, int K, int N, int nsplit, int kst, int vec) {
     using G = WStage<FMT>;
-    using X = GmGeom<NJ>;
     constexpr int BB = Fmt<FMT>::BB;
     constexpr int WROW = G::WCH * 16;     // bytes per row in a weight stage
-    constexpr int WBYTES = GM_BM * WROW;  // bytes per weight stage
-    constexpr int WINST = WBYTES / 1024;  // wave-wide DMA instructions per stage
-    // Every wave issues WPER instructions per stage; surplus ones repeat the stage's
-    // last instruction (same bytes to the same place), keeping the wait counts fixed.
+    constexpr int WBYTES = GM_BM * WROW;  // weight bytes per stage
+    constexpr int WINST = WBYTES / 1024;  // wave-wide DMA instructions per stage (weights)
+    // Every wave issues WPER weight instructions per stage; surplus ones repeat the
+    // stage's last instruction (same bytes to the same place), keeping the wait counts
+    // fixed.
     constexpr int WPER = (WINST + GM_WAVES - 1) / GM_WAVES;
     static_assert(WINST % 2 == 0, "gate / up halves must split on instruction boundaries");
+    constexpr int NTOK = 16 * NJ;                    // token rows of x per stage
+    constexpr int XROW = GM_STAGE_K * 4;             // 512 bytes of fp32 x per token row
+    constexpr int XBYTES = NTOK * XROW;              // x bytes per stage
+    constexpr int XPER = XBYTES / 1024 / GM_WAVES;   // x DMA instructions per wave and stage
+    static_assert(XPER * GM_WAVES * 1024 == XBYTES, "x stage splits evenly over the waves");
+    constexpr int SLOT = WBYTES + XBYTES;            // one ring slot: weights, then x
+    constexpr int NDMA = WPER + XPER;                // DMA instructions per wave and stage
 
-    __shared__ __align__(16) uint8_t xs[X::XBYTES];
-    __shared__ __align__(16) uint8_t R0[WBYTES];
-    __shared__ __align__(16) uint8_t R1[WBYTES];
-    __shared__ __align__(16) uint8_t R2[WBYTES];
+    __shared__ __align__(16) uint8_t R0[SLOT];
+    __shared__ __align__(16) uint8_t R1[SLOT];
+    __shared__ __align__(16) uint8_t R2[SLOT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -87,7 +85,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
     const int st0 = split * kst;
     const int st1 = min(st0 + kst, nst);
 
-    // ---- weight DMA sources (buffer resource per matrix, lane offsets fixed).
+    // ---- DMA sources: a buffer resource per operand, lane offsets fixed, the stage's
+    // position in the scalar offset.
     const int wrows = min(rows_per_tile, M - m0);
     const __amdgpu_buffer_rsrc_t wgr = make_rsrc(Wg + static_cast<int64_t>(m0) * rb, wrows * rb);
     const __amdgpu_buffer_rsrc_t wur = GATED ? make_rsrc(Wu + static_cast<int64_t>(m0) * rb, wrows * rb) : wgr;
@@ -102,55 +101,36 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
         const int r = GATED ? (R & 127) : R;
         woffs[i] = static_cast<uint32_t>(min(r, wrows - 1) * rb) + 16 * (q % G::WCH);
     }
-    // Stage st holds the 16-byte aligned windows around the 4-block segment
-    // [136 st, 136 st + 136) (Q4_0: 72) of every row; the segment starts 0 or 8
-    // bytes into the window.
-    auto issue_w = [&](QMM_L3 uint8_t* Wd, int st) {
+    // x: item q = slot q % 32 of token row q / 32, holding chunk slot ^ (token & 15)
+    // of that token's 128-float range.  Tokens past N re-read token N - 1 (never stored).
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, static_cast<int64_t>(N) * K * 4);
+    uint32_t xoffs[XPER];
+#pragma unroll
+    for (int i = 0; i < XPER; ++i) {
+        const int q = 64 * (wave + GM_WAVES * i) + lane;
+        const int n = q >> 5, sl = q & 31;
+        xoffs[i] = static_cast<uint32_t>(min(n, N - 1) * K * 4) + 16 * (sl ^ (n & 15));
+    }
+    // Stage st: the 16-byte aligned windows around the 4-block segment
+    // [136 st, 136 st + 136) (Q4_0: 72) of every row (the segment starts 0 or 8 bytes
+    // into the window), then x[., 128 st .. 128 st + 127].
+    auto issue = [&](QMM_L3 uint8_t* S, int st) {
         const uint32_t a = (static_cast<uint32_t>(st) * (4 * BB)) & ~15u;
 #pragma unroll
         for (int i = 0; i < WPER; ++i) {
             const int n = min(wave + GM_WAVES * i, WINST - 1);
-            dma16((GATED && n >= WINST / 2) ? wur : wgr, woffs[i], a, Wd + 1024 * n);
+            dma16((GATED && n >= WINST / 2) ? wur : wgr, woffs[i], a, S + 1024 * n);
         }
+#pragma unroll
+        for (int i = 0; i < XPER; ++i)
+            dma16(xr, xoffs[i], static_cast<uint32_t>(st) * XROW, S + WBYTES + 1024 * (wave + GM_WAVES * i));
     };
 
     QMM_L3 uint8_t* W0 = (QMM_L3 uint8_t*)R0;
     QMM_L3 uint8_t* W1 = (QMM_L3 uint8_t*)R1;
     QMM_L3 uint8_t* W2 = (QMM_L3 uint8_t*)R2;
-    QMM_L3 uint8_t* XS = (QMM_L3 uint8_t*)xs;
-
-    // ---- x (fp32, N tokens) -> fp16 LDS rows for this K range; tokens >= N are zero.
-    // Loaded before the weight DMA is issued, so that waiting for x does not also
-    // wait for the weights.
-    const int k0 = st0 * GM_STAGE_K;
-    const int kr = (st1 - st0) * GM_STAGE_K;
-    {
-        constexpr int ITEMS_MAX = 16 * NJ * X::KRMAX / 8;
-        constexpr int PER = ITEMS_MAX / GM_THREADS;
-        float4 v[PER][2];
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int item = tid + GM_THREADS * p;
-            const int n = item / (X::KRMAX / 8), c = item % (X::KRMAX / 8);
-            if (n < N && 8 * c < kr) {
-                const float4* src = reinterpret_cast<const float4*>(x + static_cast<int64_t>(n) * K + k0 + 8 * c);
-                v[p][0] = src[0];
-                v[p][1] = src[1];
-            } else {
-                v[p][0] = v[p][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        }
-        issue_w(W0, st0);
-        issue_w(W1, min(st0 + 1, st1 - 1));
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int item = tid + GM_THREADS * p;
-            const int n = item / (X::KRMAX / 8), c = item % (X::KRMAX / 8);
-            const u32x4_t h = {pack_h2(v[p][0].x, v[p][0].y), pack_h2(v[p][0].z, v[p][0].w),
-                               pack_h2(v[p][1].x, v[p][1].y), pack_h2(v[p][1].z, v[p][1].w)};
-            *reinterpret_cast<QMM_L3 u32x4_t*>(XS + n * X::XSTR + 16 * c) = h;
-        }
-    }
+    issue(W0, st0);
+    issue(W1, min(st0 + 1, st1 - 1));
 
     float4_t acc[2][NJ];
 #pragma unroll
@@ -166,9 +146,19 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
         else return 32 * wave + 16 * i + (lane & 15);
     };
     const int arow0 = arow(0) * WROW, arow1 = arow(1) * WROW;
-    // Token fragment j of block b: token 16 j + l % 16, halfs 8 q4 .. 8 q4 + 7 of the
-    // block's 32, at k_local = 128 (st - st0) + 32 b.
-    const int xoff = (lane & 15) * X::XSTR + 16 * q4;
+    // Token fragment j of block b: token 16 j + l % 16, floats 8 q4 .. 8 q4 + 7 of the
+    // block's 32 = chunks 8 b + 2 q4 and 8 b + 2 q4 + 1 of the token row, stored at
+    // slots chunk ^ (l % 16).
+    const int xrow = WBYTES + (lane & 15) * XROW;
+    const int xsw = lane & 15;
+    auto frag_x = [&](const QMM_L3 uint8_t* S, int j, int b) -> half8_t {
+        const int c = 8 * b + 2 * q4;
+        const QMM_L3 uint8_t* r = S + xrow + j * 16 * XROW;
+        const float4_t lo = *reinterpret_cast<const QMM_L3 float4_t*>(r + 16 * (c ^ xsw));
+        const float4_t hi = *reinterpret_cast<const QMM_L3 float4_t*>(r + 16 * ((c + 1) ^ xsw));
+        const u32x4_t h = {pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3])};
+        return __builtin_bit_cast(half8_t, h);
+    };
 
     // Stage st from ring slot Wc: wait for its DMA (the next stage's may stay in
     // flight), barrier, refill the slot read on the previous stage with stage st + 2
@@ -179,18 +169,16 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
     auto stage = [&](auto PAR_, QMM_L3 uint8_t* Wc, QMM_L3 uint8_t* Wn2, int st) {
         constexpr int sh = 8 * decltype(PAR_)::value;
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<WPER>();
+        wait_vm<NDMA>();
         lds_barrier();
-        issue_w(Wn2, min(st + 2, st1 - 1));
-        const int kl = (st - st0) * GM_STAGE_K;
+        issue(Wn2, min(st + 2, st1 - 1));
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const half8_t a0 = frag_raw<FMT>(Wc + arow0, sh + BB * b, q4);
             const half8_t a1 = frag_raw<FMT>(Wc + arow1, sh + BB * b, q4);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const half8_t bf =
-                    *reinterpret_cast<const QMM_L3 half8_t*>(XS + xoff + j * 16 * X::XSTR + 2 * (kl + 32 * b));
+                const half8_t bf = frag_x(Wc, j, b);
                 acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bf, acc[0][j], 0, 0, 0);
                 acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bf, acc[1][j], 0, 0, 0);
             }
@@ -284,27 +272,23 @@ static bool launch_gm_nj(const void* W, const void* Wu, const float* x, float* y
     const int64_t rows_per_tile = gated ? GM_BM / 2 : GM_BM;
     const int64_t ntiles = (M + rows_per_tile - 1) / rows_per_tile;
     const int64_t nst = K / GM_STAGE_K;
-    // Stages per workgroup: enough units to give every CU work (about 256 of them),
-    // no more than x's LDS room allows, at least 2 so the ring has work to overlap.
-    // Even, so that every split starts on an even stage (the kernel's parity
-    // bookkeeping relies on it).
-    int64_t kst = (nst * ntiles + 255) / 256;
-    kst = std::max<int64_t>(2, std::min<int64_t>(kst, GmGeom<NJ>::SMAX));
-    kst = std::min(kst, nst);
-    kst = (kst + 1) / 2 * 2;
+    // K is split only when the row tiles cannot give every CU a workgroup (and each
+    // split keeps at least 2 stages); kst is even, so that every split starts on an
+    // even stage (the kernel's parity bookkeeping relies on it).
+    int64_t kst = nst;
+    if (ntiles < 256) {
+        const int64_t want = std::max<int64_t>(1, std::min<int64_t>(256 / ntiles, nst / 2));
+        kst = (nst + want - 1) / want;
+    }
+    kst = std::min<int64_t>((kst + 1) / 2 * 2, nst);
     const int nsplit = static_cast<int>((nst + kst - 1) / kst);
     if (ntiles * nsplit > (int64_t{1} << 30)) return false;
-    if (nsplit == 1) {
-        if (gated) launch_gm_t<FMT, true, NJ, false>(W, Wu, x, y, M, K, N, 1, static_cast<int>(kst), s);
-        else launch_gm_t<FMT, false, NJ, false>(W, Wu, x, y, M, K, N, 1, static_cast<int>(kst), s);
-        return true;
-    }
-    hipMemPool_t pool = workspace_pool();
     float* P = nullptr;
-    const size_t bytes = static_cast<size_t>(nsplit) * N * (gated ? 2 * M : M) * sizeof(float);
-    if (!pool || hipMallocFromPoolAsync(reinterpret_cast<void**>(&P), bytes, pool, s) != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
+    if (nsplit > 1) P = workspace_alloc(static_cast<size_t>(nsplit) * N * (gated ? 2 * M : M) * sizeof(float), s);
+    if (!P) {  // one split (or no workspace, e.g. during graph capture): all of K per workgroup
+        if (gated) launch_gm_t<FMT, true, NJ, false>(W, Wu, x, y, M, K, N, 1, static_cast<int>(nst), s);
+        else launch_gm_t<FMT, false, NJ, false>(W, Wu, x, y, M, K, N, 1, static_cast<int>(nst), s);
+        return true;
     }
     if (gated) launch_gm_t<FMT, true, NJ, true>(W, Wu, x, P, M, K, N, nsplit, static_cast<int>(kst), s);
     else launch_gm_t<FMT, false, NJ, true>(W, Wu, x, P, M, K, N, nsplit, static_cast<int>(kst), s);

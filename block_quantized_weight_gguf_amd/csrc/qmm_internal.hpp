@@ -48,6 +48,13 @@ bool launch_gemv_mfma(int fmt, const void* W, const void* Wu, const float* x, fl
 // partials); nullptr if pools are unavailable.
 hipMemPool_t workspace_pool();
 
+// Allocates a split-K workspace of `bytes` on stream s from workspace_pool(), or
+// returns nullptr (launching nothing) when none can be had.  Never allocates while
+// s is being captured into a graph: stream-ordered allocations replayed from a
+// captured graph have given wrong results, so callers then take their paths that
+// need no workspace.
+float* workspace_alloc(size_t bytes, hipStream_t s);
+
 // Y[t][m] = sum over s < nsplit of P[s][t][m] (gated: P holds gate sums in columns
 // 0..M-1 and up sums in M..2M-1 of each 2M-wide row, and Y = silu(gate) * up).
 void launch_splitk_reduce(const float* P, float* Y, int64_t T, int64_t M, int nsplit, bool gated, hipStream_t s);

@@ -1,0 +1,103 @@
+"""Calls captured into a HIP graph and replayed.
+
+Paths that use a split-K workspace outside of capture (small-batch MFMA GEMV, the
+tiled GEMM on few tiles) must run without one while the stream is captured.  Each
+graph is replayed several times with eager work and synchronisations in between,
+and every replay is checked against the oracle and against the first replay.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_gguf_amd as qmm
+import oracle
+import seeded_inputs as si
+from parity_util import announce, check_linear, check_swiglu, dev
+
+pytestmark = pytest.mark.gpu
+
+MFMA = qmm.QMM_VARIANT_MFMA
+
+
+def _replays(g, out, eager_noise):
+    got = []
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        got.append(out.cpu().numpy().copy())
+        eager_noise()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+    for r in range(1, 3):
+        assert np.array_equal(got[r], got[0]), f"replay {r} differs from replay 0"
+    return got[0]
+
+
+@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_0], ids=["q8_0", "q4_0"])
+def test_graph_gemv_small_batch_and_n1(fmt):
+    M, K = 1024, 4096
+    raw = si.weights(fmt, M, K, 7001, scale_mode="gemm_wide", q8_low=-128)
+    x16 = si.activations(16, K, 7002)
+    x1 = si.activations(1, K, 7003)
+    Wd, x16d, x1d = dev(raw), dev(x16), dev(x1)
+    y16 = torch.empty((16, M), device="cuda")
+    y1 = torch.empty((1, M), device="cuda")
+    scratch = torch.empty((16, M), device="cuda")
+    announce(f"graph capture: gemv N=16 (mfma) + N=1, fmt={fmt} M={M} K={K}")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        qmm.qmm_gemv_variant(fmt, Wd, x16d, y16, M, K, 16, MFMA)
+        qmm.qmm_gemv(fmt, Wd, x1d, y1, M, K, 1)
+    torch.cuda.synchronize()
+
+    def noise():
+        qmm.qmm_gemv_variant(fmt, Wd, x16d, scratch, M, K, 16, MFMA)  # eager, may use the workspace
+
+    got16 = _replays(g, y16, noise)
+    y_ref, S = oracle.matmul_ref(fmt, raw, x16.astype(np.float16), M, K)
+    check_linear(got16, y_ref, S, f"graph gemv mfma fmt={fmt}")
+    y_ref1, S1 = oracle.matmul_ref(fmt, raw, x1, M, K)
+    check_linear(y1.cpu().numpy(), y_ref1, S1, f"graph gemv N=1 fmt={fmt}")
+
+
+@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_0, si.FMT_F16], ids=["q8_0", "q4_0", "f16"])
+def test_graph_gemm_few_tiles(fmt):
+    M, K, T = 300, 2816, 40  # 2 tiles: split-K outside of capture
+    raw = si.weights(fmt, M, K, 7101, scale_mode="gemm_wide", q8_low=-128)
+    X = si.activations(T, K, 7102, dtype=np.float16)
+    Wd, Xd = dev(raw), dev(X)
+    Y = torch.empty((T, M), device="cuda")
+    scratch = torch.empty((T, M), device="cuda")
+    announce(f"graph capture: gemm split-K shape fmt={fmt} M={M} K={K} T={T}")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        qmm.qmm_gemm(fmt, Wd, Xd, Y, M, K, T)
+    torch.cuda.synchronize()
+
+    def noise():
+        qmm.qmm_gemm(fmt, Wd, Xd, scratch, M, K, T)
+
+    got = _replays(g, Y, noise)
+    y_ref, S = oracle.matmul_ref(fmt, raw, X, M, K)
+    check_linear(got, y_ref, S, f"graph gemm fmt={fmt}")
+
+
+def test_graph_gemm_gate_up_few_tiles():
+    fmt, I, K, T = si.FMT_Q8_0, 200, 2816, 24
+    rg, ru = si.weights(fmt, I, K, 7201), si.weights(fmt, I, K, 7202)
+    X = si.activations(T, K, 7203, dtype=np.float16)
+    g_d, u_d, Xd = dev(rg), dev(ru), dev(X)
+    H = torch.empty((T, I), device="cuda")
+    announce(f"graph capture: gemm gate_up split-K shape I={I} K={K} T={T}")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        qmm.qmm_gemm_gate_up_silu(fmt, g_d, u_d, Xd, H, I, K, T)
+    torch.cuda.synchronize()
+    got = _replays(g, H, lambda: qmm.qmm_gemm_gate_up_silu(fmt, g_d, u_d, Xd, torch.empty_like(H), I, K, T))
+    h_ref, gg, uu, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, X, I, K)
+    check_swiglu(got, h_ref, gg, uu, Sg, Su, "graph gemm gate_up")
