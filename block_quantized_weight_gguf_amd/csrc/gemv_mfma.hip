@@ -37,7 +37,13 @@ namespace qmm {
 constexpr int GM_BM = 256;       // weight rows per workgroup
 constexpr int GM_THREADS = 512;  // 8 waves
 constexpr int GM_WAVES = GM_THREADS / 64;
-constexpr int GM_STAGE_K = 128;  // K per weight stage (4 blocks)
+
+// Blocks per ring stage.  4 for both formats: 8-block Q4_0 stages (144 bytes, 9
+// aligned chunks) double the work per barrier but halve the stages a K range splits
+// into, and on the 4096-row matrices the lost parallelism costs more than the
+// barriers save (measured).
+template <int FMT, int NJ>
+constexpr int gm_stage_blocks() { return 4; }
 
 // K range per workgroup that fits x in LDS next to the weight ring.
 template <int FMT, bool GATED, int NJ, bool SPLIT>
@@ -45,9 +51,13 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
                                                                 const uint8_t* __restrict__ Wu,
                                                                 const float* __restrict__ x, float* __restrict__ Y,
                                                                 int M, int K, int N, int nsplit, int kst, int vec) {
-    using G = WStage<FMT>;
     constexpr int BB = Fmt<FMT>::BB;
-    constexpr int WROW = G::WCH * 16;     // bytes per row in a weight stage
+    constexpr int SB = gm_stage_blocks<FMT, NJ>();
+    constexpr int STAGE_K = 32 * SB;
+    constexpr int SEG = SB * BB;                       // row segment bytes per stage
+    constexpr bool SHIFT = SEG % 16 != 0;              // odd stages start 8 bytes into their window
+    constexpr int WCH = (SEG + (SHIFT ? 8 : 0) + 15) / 16;  // 16-byte chunks per row window
+    constexpr int WROW = WCH * 16;        // bytes per row in a weight stage
     constexpr int WBYTES = GM_BM * WROW;  // weight bytes per stage
     constexpr int WINST = WBYTES / 1024;  // wave-wide DMA instructions per stage (weights)
     // Every wave issues WPER weight instructions per stage; surplus ones repeat the
@@ -56,7 +66,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
     constexpr int WPER = (WINST + GM_WAVES - 1) / GM_WAVES;
     static_assert(WINST % 2 == 0, "gate / up halves must split on instruction boundaries");
     constexpr int NTOK = 16 * NJ;                    // token rows of x per stage
-    constexpr int XROW = GM_STAGE_K * 4;             // 512 bytes of fp32 x per token row
+    constexpr int XROW = STAGE_K * 4;                // fp32 x bytes per token row and stage
+    constexpr int XC = XROW / 16;                    // 16-byte chunks per token row
     constexpr int XBYTES = NTOK * XROW;              // x bytes per stage
     constexpr int XPER = XBYTES / 1024 / GM_WAVES;   // x DMA instructions per wave and stage
     static_assert(XPER * GM_WAVES * 1024 == XBYTES, "x stage splits evenly over the waves");
@@ -72,7 +83,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nb = K / kQK;
     const int64_t rb = static_cast<int64_t>(nb) * BB;
-    const int nst = K / GM_STAGE_K;
+    const int nst = K / STAGE_K;
 
     // ---- work unit: (row tile, K split); the splits of a tile are adjacent.
     const int rows_per_tile = GATED ? GM_BM / 2 : GM_BM;
@@ -97,25 +108,25 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
         // stage row q / WCH.  Rows past the end re-read the last row (never stored).
         const int n = min(wave + GM_WAVES * i, WINST - 1);
         const int q = 64 * n + lane;
-        const int R = q / G::WCH;
+        const int R = q / WCH;
         const int r = GATED ? (R & 127) : R;
-        woffs[i] = static_cast<uint32_t>(min(r, wrows - 1) * rb) + 16 * (q % G::WCH);
+        woffs[i] = static_cast<uint32_t>(min(r, wrows - 1) * rb) + 16 * (q % WCH);
     }
-    // x: item q = slot q % 32 of token row q / 32, holding chunk slot ^ (token & 15)
-    // of that token's 128-float range.  Tokens past N re-read token N - 1 (never stored).
+    // x: item q = slot q % XC of token row q / XC, holding chunk slot ^ (token & 15)
+    // of that token's STAGE_K floats.  Tokens past N re-read token N - 1 (never stored).
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, static_cast<int64_t>(N) * K * 4);
     uint32_t xoffs[XPER];
 #pragma unroll
     for (int i = 0; i < XPER; ++i) {
         const int q = 64 * (wave + GM_WAVES * i) + lane;
-        const int n = q >> 5, sl = q & 31;
+        const int n = q / XC, sl = q % XC;
         xoffs[i] = static_cast<uint32_t>(min(n, N - 1) * K * 4) + 16 * (sl ^ (n & 15));
     }
-    // Stage st: the 16-byte aligned windows around the 4-block segment
-    // [136 st, 136 st + 136) (Q4_0: 72) of every row (the segment starts 0 or 8 bytes
-    // into the window), then x[., 128 st .. 128 st + 127].
+    // Stage st: the 16-byte aligned windows around the row segment [SEG st, SEG st +
+    // SEG) of every row (with SHIFT the segment starts 0 or 8 bytes into the window),
+    // then x[., STAGE_K st .. STAGE_K st + STAGE_K - 1].
     auto issue = [&](QMM_L3 uint8_t* S, int st) {
-        const uint32_t a = (static_cast<uint32_t>(st) * (4 * BB)) & ~15u;
+        const uint32_t a = (static_cast<uint32_t>(st) * SEG) & ~15u;
 #pragma unroll
         for (int i = 0; i < WPER; ++i) {
             const int n = min(wave + GM_WAVES * i, WINST - 1);
@@ -148,7 +159,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
     const int arow0 = arow(0) * WROW, arow1 = arow(1) * WROW;
     // Token fragment j of block b: token 16 j + l % 16, floats 8 q4 .. 8 q4 + 7 of the
     // block's 32 = chunks 8 b + 2 q4 and 8 b + 2 q4 + 1 of the token row, stored at
-    // slots chunk ^ (l % 16).
+    // slots chunk ^ (l % 16) (the XOR stays inside the row's XC chunks).
     const int xrow = WBYTES + (lane & 15) * XROW;
     const int xsw = lane & 15;
     auto frag_x = [&](const QMM_L3 uint8_t* S, int j, int b) -> half8_t {
@@ -167,13 +178,13 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
     // compile time; with a run-time offset the compiler cannot tell the ring slots'
     // reads from the DMA in flight and waits for all of it.
     auto stage = [&](auto PAR_, QMM_L3 uint8_t* Wc, QMM_L3 uint8_t* Wn2, int st) {
-        constexpr int sh = 8 * decltype(PAR_)::value;
+        constexpr int sh = SHIFT ? 8 * decltype(PAR_)::value : 0;
         __builtin_amdgcn_sched_barrier(0);
         wait_vm<NDMA>();
         lds_barrier();
         issue(Wn2, min(st + 2, st1 - 1));
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < SB; ++b) {
             const half8_t a0 = frag_raw<FMT>(Wc + arow0, sh + BB * b, q4);
             const half8_t a1 = frag_raw<FMT>(Wc + arow1, sh + BB * b, q4);
 #pragma unroll
@@ -271,7 +282,7 @@ static bool launch_gm_nj(const void* W, const void* Wu, const float* x, float* y
     const bool gated = Wu != nullptr;
     const int64_t rows_per_tile = gated ? GM_BM / 2 : GM_BM;
     const int64_t ntiles = (M + rows_per_tile - 1) / rows_per_tile;
-    const int64_t nst = K / GM_STAGE_K;
+    const int64_t nst = K / (32 * gm_stage_blocks<FMT, NJ>());
     // K is split only when the row tiles cannot give every CU a workgroup (and each
     // split keeps at least 2 stages); kst is even, so that every split starts on an
     // even stage (the kernel's parity bookkeeping relies on it).
