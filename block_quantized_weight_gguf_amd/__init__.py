@@ -18,8 +18,8 @@ __all__ = [
     "QMM_F16", "QMM_Q4_0", "QMM_Q8_0", "QMM_VARIANT_AUTO", "QMM_VARIANT_VALU", "QMM_VARIANT_MFMA",
     "QmmError", "lib_path", "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv",
     "qmm_gemv_variant", "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
-    "qmm_gemm_gate_up_silu",
-    "gemv", "gate_up_silu", "gemm", "gemm_gate_up_silu", "dequant",
+    "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16",
+    "gemv", "get_rows", "expand_f16", "gate_up_silu", "gemm", "gemm_gate_up_silu", "dequant",
 ]
 
 QMM_F16, QMM_Q4_0, QMM_Q8_0 = 1, 2, 8
@@ -41,6 +41,8 @@ _SIGS = {
     "qmm_strerror": (ctypes.c_char_p, [_i32]),
     "qmm_row_bytes": (_i64, [_i32, _i64]),
     "qmm_dequant": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp]),
+    "qmm_get_rows": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "qmm_expand_f16": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp]),
     "qmm_gemv": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "qmm_gemv_variant": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
     "qmm_gemv_choose": (_i32, [_i32, _i64, _i64, _i64]),
@@ -108,6 +110,14 @@ def qmm_dequant(fmt, W, out, M, K, stream=None) -> None:
     _check(_lib.qmm_dequant(fmt, _ptr(W), _ptr(out), M, K, _stream(stream)), "qmm_dequant")
 
 
+def qmm_get_rows(fmt, W, ids, out, M, K, n, stream=None) -> None:
+    _check(_lib.qmm_get_rows(fmt, _ptr(W), _ptr(ids), _ptr(out), M, K, n, _stream(stream)), "qmm_get_rows")
+
+
+def qmm_expand_f16(fmt, W, out, M, K, stream=None) -> None:
+    _check(_lib.qmm_expand_f16(fmt, _ptr(W), _ptr(out), M, K, _stream(stream)), "qmm_expand_f16")
+
+
 def qmm_gemv(fmt, W, x, y, M, K, N, stream=None) -> None:
     _check(_lib.qmm_gemv(fmt, _ptr(W), _ptr(x), _ptr(y), M, K, N, _stream(stream)), "qmm_gemv")
 
@@ -152,6 +162,22 @@ def _out(shape, like, out):
 def dequant(fmt, W, M, K, out=None, stream=None):
     out = _out((M, K), W, out)
     qmm_dequant(fmt, W, out, M, K, stream)
+    return out
+
+
+def get_rows(fmt, W, ids, M, K, out=None, stream=None):
+    """out[i] = W[ids[i]] in fp32 (ids: int32 device tensor)."""
+    n = ids.numel()
+    out = _out((n, K), W, out)
+    qmm_get_rows(fmt, W, ids, out, M, K, n, stream)
+    return out
+
+
+def expand_f16(fmt, W, M, K, out=None, stream=None):
+    """fp16 copy of the whole matrix (round to nearest even)."""
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float16, device=W.device)
+    qmm_expand_f16(fmt, W, out, M, K, stream)
     return out
 
 

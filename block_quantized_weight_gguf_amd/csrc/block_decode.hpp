@@ -1,0 +1,60 @@
+// Decode of one chunk of C consecutive weights (C = 4 or 8) of a 32-weight block to
+// fp32, for the element-wise kernels (dequant, row gather, fp16 expansion).  A lane
+// per chunk keeps every output store a whole 16-byte piece with consecutive lanes
+// on consecutive addresses.  ("EdgeRunner Core Architecture", sections 1.3, 3.1 and
+// 3.2: Q8_0 = fp16 d + 32 int8 codes, w = d * q; Q4_0 = fp16 d + 16 bytes, byte j
+// holding weight j in its low nibble and weight j + 16 in its high nibble,
+// w = d * (n - 8).)  Quantised blocks are only 2-byte aligned, so their bytes are
+// read with 2-byte loads; F16 chunks are 8- or 16-byte aligned.  Every decoded value
+// is exact in fp32: an 11-bit scale times a code of at most 8 bits.
+#pragma once
+
+#include "qmm_common.hpp"
+
+namespace qmm {
+
+// Weights [C*c, C*c + C) of block blk.
+template <int FMT, int C>
+__device__ __forceinline__ void decode_chunk_f32(const uint8_t* blk, int c, float (&w)[C]) {
+    static_assert(C == 4 || C == 8, "chunk of 4 or 8 weights");
+    if constexpr (FMT == 1) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(blk + 2 * C * c);
+        uint32_t v[C / 2];
+        if constexpr (C == 8) {
+            const uint4 t = *reinterpret_cast<const uint4*>(p);
+            v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+        } else {
+            const uint2 t = *reinterpret_cast<const uint2*>(p);
+            v[0] = t.x; v[1] = t.y;
+        }
+#pragma unroll
+        for (int j = 0; j < C / 2; ++j) {
+            w[2 * j] = half_bits_to_float(v[j]);
+            w[2 * j + 1] = half_bits_to_float(v[j] >> 16);
+        }
+    } else {
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(blk);
+        const float d = half_bits_to_float(p[0]);
+        if constexpr (FMT == 8) {
+            const uint16_t* q = p + 1 + (C / 2) * c;
+#pragma unroll
+            for (int j = 0; j < C / 2; ++j) {
+                const uint32_t h = q[j];
+                w[2 * j] = d * sbyte_to_float(h, 0);
+                w[2 * j + 1] = d * sbyte_to_float(h, 1);
+            }
+        } else {
+            const int first = C * c;                 // first weight of the chunk
+            const uint16_t* q = p + 1 + (first & 15) / 2;
+            const int sh = first >= 16 ? 4 : 0;      // high nibbles hold weights 16..31
+#pragma unroll
+            for (int j = 0; j < C / 2; ++j) {
+                const uint32_t h = static_cast<uint32_t>(q[j]) >> sh;
+                w[2 * j] = d * static_cast<float>(static_cast<int>(h & 15u) - 8);
+                w[2 * j + 1] = d * static_cast<float>(static_cast<int>((h >> 8) & 15u) - 8);
+            }
+        }
+    }
+}
+
+}  // namespace qmm

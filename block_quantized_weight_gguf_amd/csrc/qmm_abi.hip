@@ -89,6 +89,27 @@ int qmm_dequant(int fmt, const void* W, float* out, int64_t M, int64_t K, void* 
     return from_hip(qmm::launch_dequant(fmt, W, out, M, K, static_cast<hipStream_t>(stream)));
 }
 
+int qmm_get_rows(int fmt, const void* W, const int32_t* ids, float* out, int64_t M, int64_t K, int64_t n,
+                 void* stream) {
+    if (n == 0) return fmt_ok(fmt) ? QMM_OK : QMM_ERR_FMT;
+    if (!W || !ids || !out) return QMM_ERR_NULL;
+    if (n < 0) return QMM_ERR_SHAPE;
+    int st = check_shape(fmt, M, K, n);
+    if (st) return st;
+    if (!aligned(W, 16) || !aligned(ids, 4) || !aligned(out, 16)) return QMM_ERR_ALIGN;
+    return from_hip(qmm::launch_get_rows(fmt, W, ids, out, M, K, n, static_cast<hipStream_t>(stream)));
+}
+
+int qmm_expand_f16(int fmt, const void* W, void* out, int64_t M, int64_t K, void* stream) {
+    if (!W || !out) return QMM_ERR_NULL;
+    int st = check_shape(fmt, M, K, 1);
+    if (st) return st;
+    int64_t t;
+    if (!mul_ok(M, K, &t) || !mul_ok(t, 2, &t)) return QMM_ERR_OVERFLOW;
+    if (!aligned(W, 16) || !aligned(out, 16)) return QMM_ERR_ALIGN;
+    return from_hip(qmm::launch_expand_f16(fmt, W, out, M, K, static_cast<hipStream_t>(stream)));
+}
+
 int qmm_gemv_choose(int fmt, int64_t M, int64_t K, int64_t N) {
     const int st = check_shape(fmt, M, K, N);
     if (st) return st;

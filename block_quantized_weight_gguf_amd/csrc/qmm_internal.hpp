@@ -11,6 +11,13 @@ namespace qmm {
 
 hipError_t launch_dequant(int fmt, const void* W, float* out, int64_t M, int64_t K, hipStream_t s);
 
+// out[i][k] = W[ids[i]][k] (fp32) for i < n; ids outside [0, M) give NaN rows.
+hipError_t launch_get_rows(int fmt, const void* W, const int32_t* ids, float* out, int64_t M, int64_t K, int64_t n,
+                           hipStream_t s);
+
+// out[m][k] = fp16(W[m][k]), rounded to nearest even.
+hipError_t launch_expand_f16(int fmt, const void* W, void* out, int64_t M, int64_t K, hipStream_t s);
+
 // VALU GEMV over N tokens (any N >= 1): y[n][m] = sum_k W[m][k] x[n][k].
 // Wu != nullptr selects the gate/up SwiGLU epilogue (W = gate, Wu = up, y = h).
 hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float* x, float* y,

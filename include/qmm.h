@@ -30,10 +30,15 @@
  * activations).  Products accumulate in fp32.
  *
  * Common rules for every entry point:
- *   - All array arguments are device pointers owned by the caller.  The library
- *     allocates no memory, keeps no state between calls and is re-entrant.
- *     (Pre-allocated buffers with no allocation per pass: "EdgeRunner Core
- *     Architecture", section 10 Scratch Buffers and section 15, item 4.)
+ *   - All array arguments are device pointers owned by the caller.  The only
+ *     memory the library allocates is the split-K workspace of the MFMA products
+ *     on few output tiles: stream-ordered allocations from a per-device pool the
+ *     library keeps for the life of the process (its memory is retained, so a
+ *     steady loop allocates nothing new).  While the stream is being captured
+ *     into a graph no workspace is taken and those calls run unsplit.  Calls are
+ *     re-entrant.  (Pre-allocated buffers with no allocation per pass:
+ *     "EdgeRunner Core Architecture", section 10 Scratch Buffers and section 15,
+ *     item 4.)
  *   - stream is a hipStream_t passed as void* (NULL = the default stream).  All
  *     work is enqueued asynchronously on it; nothing synchronises.
  *   - Arguments are validated on the host before any HIP call; a failure returns
@@ -103,6 +108,34 @@ int64_t qmm_row_bytes(int fmt, int64_t K);
  * check of the decoders and the building block of decode-then-GEMM prefill.
  */
 int qmm_dequant(int fmt, const void* W, float* out, int64_t M, int64_t K, void* stream);
+
+/*
+ * Quantised row gather (embedding lookup): out[i][k] = W[ids[i]][k] as float32,
+ * for i < n; out is n x K row-major.  ids is a device array of n int32 row
+ * indices (4-byte aligned; repeats allowed); only the rows named are read.
+ * Each value is exact in fp32, so the result is bit-exact.  An id outside
+ * [0, M) cannot be checked on the host (ids live on the device): its output row
+ * is filled with NaN and nothing outside W is read.  n == 0 is a no-op that
+ * returns QMM_OK.  out must be 16-byte aligned.
+ * ("llama.cpp Metal ...", section 3.2 Input embd and P8: token ids go through a
+ * per-format get_rows kernel on the token-embedding matrix; "EdgeRunner Core
+ * Architecture", section 3.4, Tier 3: embeddings decode straight into the
+ * destination, with no float copy of the table.)
+ */
+int qmm_get_rows(int fmt, const void* W, const int32_t* ids, float* out,
+                 int64_t M, int64_t K, int64_t n, void* stream);
+
+/*
+ * Expand a whole matrix to half precision: out[m][k] = fp16(W[m][k]), rounded to
+ * nearest even (F16: a copy), M x K row-major, 16-byte aligned.  These are the
+ * same fp16 values the fused qmm_gemm decodes into its LDS tiles, so
+ * qmm_gemm(QMM_F16, out, ...) computes what qmm_gemm(fmt, W, ...) computes.  This
+ * is the expand-then-GEMM prefill variant: the caller owns the M*K*2-byte buffer.
+ * ("alpaca.swift", Design: quantised matrices are expanded one at a time into a
+ * scratch buffer before the matrix-hardware GEMM; "EdgeRunner Core Architecture",
+ * section 3.4, Tier 2: GPU decode kernels writing float16.)
+ */
+int qmm_expand_f16(int fmt, const void* W, void* out, int64_t M, int64_t K, void* stream);
 
 /*
  * Decode GEMV: y[n][m] = sum_k W[m][k] * x[n][k] for n < N, fp32 x and y.

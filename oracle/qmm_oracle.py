@@ -139,6 +139,34 @@ def dequant_rows(fmt: int, raw, K: int, rows) -> np.ndarray:
     return dequant(fmt, sel, len(rows), K)
 
 
+def get_rows_ref(fmt: int, raw, M: int, K: int, ids) -> np.ndarray:
+    """Row gather of a quantised matrix: out[i] = W[ids[i]] decoded, float64 [n][K].
+
+    llama.cpp Metal, section 3.2 Input embd (token ids select rows of the
+    token-embedding matrix through get_rows) and P8 (one get_rows kernel per
+    weight format); EdgeRunner, section 3.4 Tier 3 (embedding rows decoded straight
+    into the destination).  An id outside [0, M) gives a NaN row (the library's
+    stated behaviour for ids it cannot check on the host).
+    """
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    out = np.full((ids.size, K), np.nan)
+    ok = (ids >= 0) & (ids < M)
+    if ok.any():
+        out[ok] = dequant_rows(fmt, raw, K, ids[ok])
+    return out
+
+
+def expand_f16_ref(fmt: int, raw, M: int, K: int) -> np.ndarray:
+    """Whole-matrix expansion to half precision, float16 [M][K].
+
+    alpaca.swift, Design (quantised matrices expanded into a half-precision buffer
+    ahead of the matrix-hardware GEMM); EdgeRunner, section 3.4 Tier 2 (decode
+    kernels writing float16).  Each exact decoded weight is rounded once to the
+    nearest fp16, ties to even.
+    """
+    return fp16_round(dequant(fmt, raw, M, K)).astype(np.float16)
+
+
 # ------------------------------------------------------------------ packing
 def pack_q8_0(q: np.ndarray, d16: np.ndarray) -> np.ndarray:
     """Inverse of unpack_q8_0 for codes q int8 [M][K] and fp16 scales [M][K/32]."""

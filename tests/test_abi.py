@@ -30,7 +30,7 @@ def test_header_declares_expected_api():
     assert declared_functions() == sorted([
         "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv", "qmm_gemv_variant",
         "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
-        "qmm_gemm_gate_up_silu"])
+        "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -104,6 +104,36 @@ def test_dequant_validation():
     assert L.qmm_dequant(8, None, A16, 4, 64, None) == E_NULL
     assert L.qmm_dequant(8, A16, A16, 4, 65, None) == E_SHAPE
     assert L.qmm_dequant(8, A16, A16 + 4, 4, 64, None) == E_ALIGN
+
+
+def test_get_rows_validation():
+    L = qmm._lib
+    A4 = A16 + 4
+    assert L.qmm_get_rows(8, A16, A16, A16, 4, 64, 0, None) == OK  # empty gather: nothing enqueued
+    assert L.qmm_get_rows(8, None, None, None, 4, 64, 0, None) == OK
+    assert L.qmm_get_rows(7, A16, A16, A16, 4, 64, 0, None) == E_FMT
+    assert L.qmm_get_rows(8, None, A16, A16, 4, 64, 3, None) == E_NULL
+    assert L.qmm_get_rows(8, A16, None, A16, 4, 64, 3, None) == E_NULL
+    assert L.qmm_get_rows(8, A16, A16, None, 4, 64, 3, None) == E_NULL
+    assert L.qmm_get_rows(3, A16, A16, A16, 4, 64, 3, None) == E_FMT
+    assert L.qmm_get_rows(8, A16, A16, A16, 4, 64, -1, None) == E_SHAPE
+    assert L.qmm_get_rows(8, A16, A16, A16, 0, 64, 3, None) == E_SHAPE
+    assert L.qmm_get_rows(2, A16, A16, A16, 4, 33, 3, None) == E_SHAPE
+    assert L.qmm_get_rows(8, A16, A16, A16, 4, 2**31 - 32, 2**31 - 1, None) == E_OVF
+    assert L.qmm_get_rows(8, A16 + 2, A16, A16, 4, 64, 3, None) == E_ALIGN
+    assert L.qmm_get_rows(8, A16, A16 + 2, A16, 4, 64, 3, None) == E_ALIGN
+    assert L.qmm_get_rows(8, A16, A4, A16 + 4, 4, 64, 3, None) == E_ALIGN  # out needs 16 bytes
+
+
+def test_expand_f16_validation():
+    L = qmm._lib
+    assert L.qmm_expand_f16(8, None, A16, 4, 64, None) == E_NULL
+    assert L.qmm_expand_f16(8, A16, None, 4, 64, None) == E_NULL
+    assert L.qmm_expand_f16(6, A16, A16, 4, 64, None) == E_FMT
+    assert L.qmm_expand_f16(1, A16, A16, 4, 16, None) == E_SHAPE
+    assert L.qmm_expand_f16(1, A16, A16, 0, 64, None) == E_SHAPE
+    assert L.qmm_expand_f16(2, A16, A16 + 8, 4, 64, None) == E_ALIGN
+    assert L.qmm_expand_f16(2, A16 + 2, A16, 4, 64, None) == E_ALIGN
 
 
 def test_variant_choice():

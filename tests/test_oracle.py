@@ -39,6 +39,8 @@ def load_golden(path):
                 fx.setdefault("negzero", []).append(int(rest[0]))
         elif key == "x":
             fx["x"][int(rest[0])] = Fraction(rest[1])
+        elif key == "h":
+            fx.setdefault("h", {})[int(rest[0])] = Fraction(rest[1])
         elif key == "xramp":
             fx["x"] = {k: Fraction(k) for k in range(32)}
         elif key == "xones":
@@ -86,6 +88,111 @@ def test_golden_blocks_brute_force(path):
 
 def test_golden_fixture_count():
     assert len(GOLDEN_FILES) >= 5
+
+
+# --------------------------------------------- row gather and fp16 expansion
+def _golden_by_fmt():
+    by = {}
+    for p in GOLDEN_FILES:
+        fx = load_golden(p)
+        by.setdefault(fx["fmt"], []).append(fx)
+    return by
+
+
+def _hand_block(fx):
+    want = np.zeros(32)
+    for k, v in fx["w"].items():
+        want[k] = float(v)
+    return want
+
+
+def check_get_rows(get_rows):
+    """A matrix whose rows are strings of golden blocks; gathered rows must show
+    those blocks' hand values in order, repeats included, and NaN for bad ids."""
+    for fmt, fxs in _golden_by_fmt().items():
+        blocks = [(fx["bytes"], _hand_block(fx)) for fx in fxs]
+        if len(blocks) == 1:  # a lone fixture: pair it with an all-zero block
+            blocks.append((bytes(len(blocks[0][0])), np.zeros(32)))
+        nb, M, L = 3, 4, len(blocks)
+        K = 32 * nb
+        # row r spells r + 1 in base L over its blocks: rows differ, none is a palindrome of row 0
+        pick = [[((r + 1) // L ** (nb - 1 - b)) % L for b in range(nb)] for r in range(M)]
+        raw = np.frombuffer(b"".join(blocks[i][0] for r in range(M) for i in pick[r]), np.uint8)
+        hand = [np.concatenate([blocks[i][1] for i in pick[r]]) for r in range(M)]
+        ids = [3, 0, 3, 1, -1, M, 2]
+        got = get_rows(fmt, raw, M, K, ids)
+        if got.shape != (len(ids), K):
+            return False
+        for i, r in enumerate(ids):
+            if 0 <= r < M:
+                if not np.array_equal(got[i], hand[r]):
+                    return False
+            elif not np.isnan(got[i]).all():
+                return False
+        if get_rows(fmt, raw, M, K, []).shape != (0, K):
+            return False
+    return True
+
+
+def test_get_rows_golden():
+    assert check_get_rows(Q.get_rows_ref)
+
+
+def test_get_rows_pin_catches_mistakes():
+    # a wrapped id, an off-by-one row, a zero fill for bad ids, blocks reversed
+    wrap = lambda f, raw, M, K, ids: Q.get_rows_ref(f, raw, M, K, np.mod(np.asarray(ids, np.int64), M))
+    off1 = lambda f, raw, M, K, ids: Q.get_rows_ref(f, raw, M, K, [i + 1 if 0 <= i < M - 1 else i for i in ids])
+    zero = lambda f, raw, M, K, ids: np.nan_to_num(Q.get_rows_ref(f, raw, M, K, ids), nan=0.0)
+    rev = lambda f, raw, M, K, ids: Q.get_rows_ref(f, raw, M, K, ids).reshape(len(ids), K // 32, 32)[:, ::-1].reshape(
+        len(ids), K)
+    for bad in (wrap, off1, zero, rev):
+        assert not check_get_rows(bad)
+
+
+def check_expand(expand):
+    n = 0
+    for p in GOLDEN_FILES:
+        fx = load_golden(p)
+        if "h" not in fx:
+            continue
+        got = expand(fx["fmt"], np.frombuffer(fx["bytes"], np.uint8), 1, 32)
+        if got.dtype != np.float16:
+            return False
+        for k in range(32):
+            want = float(fx["h"].get(k, fx["w"].get(k, 0)))
+            if Fraction(float(got[0, k])) != Fraction(want):
+                return False
+        n += 1
+    return n >= 1
+
+
+def test_expand_f16_golden_ties():
+    assert check_expand(Q.expand_f16_ref)
+
+
+def test_expand_pin_catches_truncation():
+    # truncation toward zero, and rounding ties away from zero, both differ on the fixture
+    def trunc(f, raw, M, K):
+        w = Q.dequant(f, raw, M, K)
+        h = w.astype(np.float16)
+        back = h.astype(np.float64)
+        over = np.abs(back) > np.abs(w)
+        h[over] = np.nextafter(h[over], np.float16(0))
+        return h
+
+    def away(f, raw, M, K):
+        w = Q.dequant(f, raw, M, K)
+        h = w.astype(np.float16)
+        lo = np.nextafter(h, np.float16(0))
+        hi = np.nextafter(h, np.where(h < 0, np.float16(-np.inf), np.float16(np.inf)))
+        for c in (lo, hi):
+            tie = np.abs(c.astype(np.float64) - w) == np.abs(h.astype(np.float64) - w)
+            pick = tie & (np.abs(c) > np.abs(h))
+            h[pick] = c[pick]
+        return h
+
+    assert not check_expand(trunc)
+    assert not check_expand(away)
 
 
 # ------------------------------------------------------------ fp16 decoding
