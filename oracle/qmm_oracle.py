@@ -241,10 +241,58 @@ def gate_up_silu_ref(fmt: int, raw_g, raw_u, x, I: int, K: int, rows=None):
     return silu(g) * u, g, u, Sg, Su
 
 
+def rmsnorm_ref(x, gamma, eps: float):
+    """RMSNorm of each token row: x / sqrt(mean_k x_k^2 + eps) * gamma, float64 [N][K].
+
+    EdgeRunner, section 6 RMSNorm: the input times the inverse of its root mean
+    square, times the norm weight; the epsilon is a parameter of the norm (the
+    model configuration gives 1e-5 as an example).  Reading where the page is
+    silent: eps is added to the mean square inside the square root, and Llama-style
+    norms carry no bias.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    ms = np.mean(x64 * x64, axis=1, keepdims=True)
+    return x64 / np.sqrt(ms + float(eps)) * np.asarray(gamma, dtype=np.float64)[None, :]
+
+
+def rmsnorm_matmul_ref(fmt: int, raw, x, gamma, eps: float, M: int, K: int, rows=None):
+    """RMSNorm prologue fused with a projection: y = rmsnorm(x) W^T, with S of the
+    normalised input (EdgeRunner, section 2.1 and section 9.2: the attention norm
+    folded into the fused QKV GEMV, the final norm into the LM head)."""
+    return matmul_ref(fmt, raw, rmsnorm_ref(x, gamma, eps), M, K, rows=rows)
+
+
+def rmsnorm_gate_up_silu_ref(fmt: int, raw_g, raw_u, x, gamma, eps: float, I: int, K: int, rows=None):
+    """FFN norm folded into gate+up+SwiGLU (EdgeRunner, section 8: one dispatch for
+    RMSNorm, gate, up and SiLU at a single token)."""
+    return gate_up_silu_ref(fmt, raw_g, raw_u, rmsnorm_ref(x, gamma, eps), I, K, rows=rows)
+
+
+def matmul_add_ref(fmt: int, raw, x, r, M: int, K: int, rows=None):
+    """Residual-add epilogue: y = x W^T + r (EdgeRunner, section 9.1 steps 13-14 and
+    section 9.2: the O and down projections add into the residual stream)."""
+    y, S = matmul_ref(fmt, raw, x, M, K, rows=rows)
+    r64 = np.asarray(r, dtype=np.float64)
+    if r64.ndim == 1:
+        r64 = r64[None, :]
+    if rows is not None:
+        r64 = r64[:, rows]
+    return y + r64, S
+
+
 # ---------------------------------------------------------------- tolerances
 def tol_linear(S):
     """Allowed |y_gpu - y_ref| for a linear output: 2e-3 * S + 1e-6."""
     return TOL_REL * np.asarray(S) + TOL_ABS
+
+
+def tol_residual(S, y):
+    """Allowed error of y = x W^T + r: the linear bound for the product plus the
+    fp32 rounding of the final addition (one rounding, at most 2^-24 |y|; 2^-23 |y|
+    is allowed)."""
+    return tol_linear(S) + 2.0 ** -23 * np.abs(np.asarray(y))
 
 
 SILU_SLOPE_MAX = 1.1   # max |silu'(z)| = 1.0998 near z = 2.40

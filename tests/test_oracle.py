@@ -195,6 +195,99 @@ def test_expand_pin_catches_truncation():
     assert not check_expand(away)
 
 
+# ------------------------------------------------------ RMSNorm and residual
+def check_rmsnorm(rmsnorm):
+    """Closed forms of x / sqrt(mean(x^2) + eps) * gamma."""
+    def close(a, b):
+        return np.allclose(np.asarray(a, np.float64), np.asarray(b, np.float64), rtol=1e-15, atol=0)
+
+    # mean of (9, 16, 0, 0) is 25/4: rms 2.5
+    if not close(rmsnorm([[3, 4, 0, 0]], [1, 2, 3, 4], 0.0), [[1.2, 3.2, 0, 0]]):
+        return False
+    # eps inside the root: sqrt(1 + 3) = 2
+    if not close(rmsnorm([[1, 1, 1, 1]], [2, 4, 6, 8], 3.0), [[1, 2, 3, 4]]):
+        return False
+    # the mean is over K, whatever K is: a constant row normalises to gamma
+    for K in (1, 5, 64):
+        if not close(rmsnorm([[2.0] * K], np.arange(K), 0.0), [np.arange(K)]):
+            return False
+    # token rows are normalised independently
+    if not close(rmsnorm([[3, 4, 0, 0], [1, 1, 1, 1]], [1, 1, 1, 1], 0.0), [[1.2, 1.6, 0, 0], [1, 1, 1, 1]]):
+        return False
+    # a zero row stays zero (eps > 0) and odd symmetry holds
+    if not close(rmsnorm([[0.0] * 8], np.ones(8), 1e-5), [[0.0] * 8]):
+        return False
+    x = np.random.default_rng(1).standard_normal((3, 40))
+    g = np.random.default_rng(2).standard_normal(40)
+    if not np.allclose(rmsnorm(-x, g, 1e-5), -rmsnorm(x, g, 1e-5), rtol=1e-15, atol=0):
+        return False
+    return True
+
+
+def test_rmsnorm_closed_forms():
+    assert check_rmsnorm(Q.rmsnorm_ref)
+
+
+def test_rmsnorm_pin_catches_mistakes():
+    def g64(g):
+        return np.asarray(g, np.float64)[None, :]
+
+    def x64(x):
+        return np.atleast_2d(np.asarray(x, np.float64))
+
+    sum_sq = lambda x, g, e: x64(x) / np.sqrt((x64(x) ** 2).sum(1, keepdims=True) + e) * g64(g)
+    eps_out = lambda x, g, e: x64(x) / (np.sqrt((x64(x) ** 2).mean(1, keepdims=True)) + e) * g64(g)
+    tok_axis = lambda x, g, e: x64(x) / np.sqrt((x64(x) ** 2).mean(0, keepdims=True) + e) * g64(g)
+    no_gamma = lambda x, g, e: x64(x) / np.sqrt((x64(x) ** 2).mean(1, keepdims=True) + e)
+    with np.errstate(all="ignore"):
+        for bad in (sum_sq, eps_out, tok_axis, no_gamma):
+            assert not check_rmsnorm(bad)
+
+
+@pytest.mark.parametrize("path", GOLDEN_FILES, ids=os.path.basename)
+def test_rmsnorm_matmul_golden(path):
+    """A constant input row of 2s normalises to exactly gamma; with gamma set to the
+    fixture's x the fused product must give the fixture's hand-computed dot."""
+    fx = load_golden(path)
+    gamma = np.array([float(fx["x"].get(k, 0)) for k in range(32)])
+    y, S = Q.rmsnorm_matmul_ref(fx["fmt"], np.frombuffer(fx["bytes"], np.uint8), np.full((1, 32), 2.0), gamma,
+                                0.0, 1, 32)
+    assert Fraction(float(y[0, 0])) == fx["dot"]
+    # eps = 12 with a row of 2s: sqrt(4 + 12) = 4, so gamma is halved
+    y2, _ = Q.rmsnorm_matmul_ref(fx["fmt"], np.frombuffer(fx["bytes"], np.uint8), np.full((1, 32), 2.0),
+                                 2 * gamma, 12.0, 1, 32)
+    assert Fraction(float(y2[0, 0])) == fx["dot"]
+
+
+@pytest.mark.parametrize("path", GOLDEN_FILES, ids=os.path.basename)
+def test_matmul_add_golden(path):
+    fx = load_golden(path)
+    x = np.array([[float(fx["x"].get(k, 0)) for k in range(32)]])
+    y, _ = Q.matmul_add_ref(fx["fmt"], np.frombuffer(fx["bytes"], np.uint8), x, np.array([[0.25]]), 1, 32)
+    assert Fraction(float(y[0, 0])) == fx["dot"] + Fraction(1, 4)
+
+
+def test_rmsnorm_gate_up_is_gate_up_of_the_norm():
+    """With a constant input row the norm is gamma itself: the fused FFN reference
+    must equal the plain gate+up reference applied to gamma."""
+    fmt, I, K = Q.FMT_Q8_0, 5, 64
+    rg, ru = si.weights(fmt, I, K, 41), si.weights(fmt, I, K, 42)
+    gamma = si.activations(1, K, 43)[0].astype(np.float64)
+    h, g, u, Sg, Su = Q.rmsnorm_gate_up_silu_ref(fmt, rg, ru, np.full((1, K), -3.0), gamma, 0.0, I, K)
+    h2, g2, u2, _, _ = Q.gate_up_silu_ref(fmt, rg, ru, -gamma[None, :], I, K)
+    assert np.array_equal(h, h2) and np.array_equal(g, g2) and np.array_equal(u, u2)
+
+
+def test_tol_residual_covers_fp32_addition():
+    g = np.random.default_rng(5)
+    y = g.standard_normal(10000) * 10.0 ** g.integers(-3, 4, 10000)
+    r = g.standard_normal(10000) * 10.0 ** g.integers(-3, 4, 10000)
+    y32, r32 = y.astype(np.float32), r.astype(np.float32)
+    s32 = (y32 + r32).astype(np.float64)
+    exact = y32.astype(np.float64) + r32.astype(np.float64)
+    assert (np.abs(s32 - exact) <= Q.tol_residual(np.zeros_like(exact), exact)).all()
+
+
 # ------------------------------------------------------------ fp16 decoding
 def manual_f16(h):
     """IEEE binary16 from sign, exponent and mantissa fields with math.ldexp."""
