@@ -18,12 +18,14 @@ __all__ = [
     "QMM_F16", "QMM_Q4_0", "QMM_Q8_0", "QMM_VARIANT_AUTO", "QMM_VARIANT_VALU", "QMM_VARIANT_MFMA",
     "QmmError", "lib_path", "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv",
     "qmm_gemv_variant", "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
-    "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16",
-    "gemv", "get_rows", "expand_f16", "gate_up_silu", "gemm", "gemm_gate_up_silu", "dequant",
+    "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16", "qmm_rmsnorm_gemv", "qmm_rmsnorm_gate_up_silu",
+    "qmm_gemv_add", "QMM_ERR_ARG",
+    "gemv", "get_rows", "expand_f16", "rmsnorm_gemv", "rmsnorm_gate_up_silu", "gemv_add", "gate_up_silu", "gemm", "gemm_gate_up_silu", "dequant",
 ]
 
 QMM_F16, QMM_Q4_0, QMM_Q8_0 = 1, 2, 8
 QMM_VARIANT_AUTO, QMM_VARIANT_VALU, QMM_VARIANT_MFMA = 0, 1, 2
+QMM_ERR_ARG = -8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libqmm.so")
@@ -48,6 +50,9 @@ _SIGS = {
     "qmm_gemv_choose": (_i32, [_i32, _i64, _i64, _i64]),
     "qmm_gate_up_silu": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "qmm_gate_up_silu_variant": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
+    "qmm_rmsnorm_gemv": (_i32, [_i32, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i64, _vp]),
+    "qmm_rmsnorm_gate_up_silu": (_i32, [_i32, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i64, _vp]),
+    "qmm_gemv_add": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "qmm_gemm": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "qmm_gemm_gate_up_silu": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
@@ -143,6 +148,20 @@ def qmm_gate_up_silu_variant(fmt, Wg, Wu, x, h, I, K, N, variant, stream=None) -
                                          _stream(stream)), "qmm_gate_up_silu_variant")
 
 
+def qmm_rmsnorm_gemv(fmt, W, x, gamma, eps, y, M, K, N, stream=None) -> None:
+    _check(_lib.qmm_rmsnorm_gemv(fmt, _ptr(W), _ptr(x), _ptr(gamma), eps, _ptr(y), M, K, N, _stream(stream)),
+           "qmm_rmsnorm_gemv")
+
+
+def qmm_rmsnorm_gate_up_silu(fmt, Wg, Wu, x, gamma, eps, h, I, K, N, stream=None) -> None:
+    _check(_lib.qmm_rmsnorm_gate_up_silu(fmt, _ptr(Wg), _ptr(Wu), _ptr(x), _ptr(gamma), eps, _ptr(h), I, K, N,
+                                         _stream(stream)), "qmm_rmsnorm_gate_up_silu")
+
+
+def qmm_gemv_add(fmt, W, x, r, y, M, K, N, stream=None) -> None:
+    _check(_lib.qmm_gemv_add(fmt, _ptr(W), _ptr(x), _ptr(r), _ptr(y), M, K, N, _stream(stream)), "qmm_gemv_add")
+
+
 def qmm_gemm(fmt, W, X, Y, M, K, T, stream=None) -> None:
     _check(_lib.qmm_gemm(fmt, _ptr(W), _ptr(X), _ptr(Y), M, K, T, _stream(stream)), "qmm_gemm")
 
@@ -193,6 +212,29 @@ def gate_up_silu(fmt, Wg, Wu, x, I, K, out=None, variant=QMM_VARIANT_AUTO, strea
     N = 1 if x.dim() == 1 else x.shape[0]
     out = _out((N, I), x, out)
     qmm_gate_up_silu_variant(fmt, Wg, Wu, x, out, I, K, N, variant, stream)
+    return out
+
+
+def rmsnorm_gemv(fmt, W, x, gamma, eps, M, K, out=None, stream=None):
+    """y = rmsnorm(x; gamma, eps) W^T for fp32 x."""
+    N = 1 if x.dim() == 1 else x.shape[0]
+    out = _out((N, M), x, out)
+    qmm_rmsnorm_gemv(fmt, W, x, gamma, eps, out, M, K, N, stream)
+    return out
+
+
+def rmsnorm_gate_up_silu(fmt, Wg, Wu, x, gamma, eps, I, K, out=None, stream=None):
+    N = 1 if x.dim() == 1 else x.shape[0]
+    out = _out((N, I), x, out)
+    qmm_rmsnorm_gate_up_silu(fmt, Wg, Wu, x, gamma, eps, out, I, K, N, stream)
+    return out
+
+
+def gemv_add(fmt, W, x, r, M, K, out=None, stream=None):
+    """y = x W^T + r; pass out=r to add into r in place."""
+    N = 1 if x.dim() == 1 else x.shape[0]
+    out = _out((N, M), x, out)
+    qmm_gemv_add(fmt, W, x, r, out, M, K, N, stream)
     return out
 
 

@@ -47,19 +47,25 @@ struct GemvCfg {
     static constexpr int XS = (FMT == 1) ? GV_SLICE * 32 : GV_SLICE * XS_STRIDE;  // floats per token
 };
 
-template <int FMT, int NT, int R, bool GATED>
+template <int FMT, int NT, int R, bool GATED, int EP>
 __global__ __launch_bounds__(GV_THREADS) void gemv_valu_kernel(const uint8_t* __restrict__ Wg,
                                                                 const uint8_t* __restrict__ Wu,
                                                                 const float* __restrict__ x,
                                                                 float* __restrict__ y, int M, int K,
-                                                                int64_t ldx, int64_t ldy, int row_begin) {
+                                                                int64_t ldx, int64_t ldy, int row_begin,
+                                                                DecodeEpi epi) {
     using C = GemvCfg<FMT, NT, R, GATED>;
     constexpr int BB = C::BB, RU = C::RU;
     __shared__ __align__(16) float xs[NT][C::XS];
     __shared__ __align__(16) uint8_t ws[(FMT == 1) ? 1 : GV_WAVES][(FMT == 1) ? 1 : RU][C::ROWBUF];
+    __shared__ float red[(EP == EP_NORM) ? GV_WAVES * NT : 1];
 
     x += static_cast<int64_t>(blockIdx.y) * NT * ldx;
     y += static_cast<int64_t>(blockIdx.y) * NT * ldy;
+    const float* res = (EP == EP_RES) ? epi.res + static_cast<int64_t>(blockIdx.y) * NT * ldy : nullptr;
+    float ss[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) ss[n] = 0.0f;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -77,14 +83,31 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_valu_kernel(const uint8_t* __
         const int sb = min(GV_SLICE, nb - s0);
         __syncthreads();  // the previous slice's readers are done with LDS
 
-        // Stage this slice of x (NT tokens x sb*32 floats).
-        const int nx4 = NT * sb * 8;
-        for (int i = threadIdx.x; i < nx4; i += GV_THREADS) {
-            const int n = i / (sb * 8);
-            const int j = i - n * (sb * 8);  // float4 index inside the slice
-            const float4 v = *reinterpret_cast<const float4*>(x + n * ldx + static_cast<int64_t>(s0) * kQK + 4 * j);
-            const int dst = (FMT == 1) ? 4 * j : (j >> 3) * XS_STRIDE + 4 * (j & 7);
-            *reinterpret_cast<float4*>(&xs[n][dst]) = v;
+        // Stage this slice of x (NT tokens x sb*32 floats); EP_NORM: gamma .* x, with
+        // the sum of squares of x gathered on the way.
+        if constexpr (EP == EP_NORM) {
+            for (int j = threadIdx.x; j < sb * 8; j += GV_THREADS) {  // float4 index inside the slice
+                const int64_t k = static_cast<int64_t>(s0) * kQK + 4 * j;
+                const int dst = (FMT == 1) ? 4 * j : (j >> 3) * XS_STRIDE + 4 * (j & 7);
+                const float4 gm = *reinterpret_cast<const float4*>(epi.gamma + k);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    float4 v = *reinterpret_cast<const float4*>(x + n * ldx + k);
+                    ss[n] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss[n]))));
+                    v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
+                    *reinterpret_cast<float4*>(&xs[n][dst]) = v;
+                }
+            }
+        } else {
+            const int nx4 = NT * sb * 8;
+            for (int i = threadIdx.x; i < nx4; i += GV_THREADS) {
+                const int n = i / (sb * 8);
+                const int j = i - n * (sb * 8);  // float4 index inside the slice
+                const float4 v =
+                    *reinterpret_cast<const float4*>(x + n * ldx + static_cast<int64_t>(s0) * kQK + 4 * j);
+                const int dst = (FMT == 1) ? 4 * j : (j >> 3) * XS_STRIDE + 4 * (j & 7);
+                *reinterpret_cast<float4*>(&xs[n][dst]) = v;
+            }
         }
 
         // Stage this wave's weight row slices (block formats only).
@@ -160,56 +183,78 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_valu_kernel(const uint8_t* __
         }
     }
 
-    reduce_store<R, RU, NT, GATED>(acc, lane, row0, M, y, ldy);
+    float scale = 1.0f;
+    if constexpr (EP == EP_NORM) {
+        norm_partials<NT>(ss, red, wave, lane);
+        __syncthreads();
+        scale = norm_scale<NT>(red, GV_WAVES, reduced_token<RU, NT>(lane), K, epi.eps);
+    }
+    reduce_store<R, RU, NT, GATED, EP>(acc, lane, row0, M, y, ldy, scale, res);
 }
 
-template <int FMT, int NT, bool GATED>
+template <int FMT, int NT, bool GATED, int EP>
 static void launch_fmt_nt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
-                          int64_t chunks, int64_t row_begin, hipStream_t s) {
+                          int64_t chunks, int64_t row_begin, const DecodeEpi& epi, hipStream_t s) {
     constexpr int R = (FMT == 1) ? 2 : 4;
     const int64_t rows = M - row_begin;
     const dim3 grid(static_cast<unsigned>((rows + GV_WAVES * R - 1) / (GV_WAVES * R)), static_cast<unsigned>(chunks));
-    hipLaunchKernelGGL((gemv_valu_kernel<FMT, NT, R, GATED>), grid, dim3(GV_THREADS), 0, s,
+    hipLaunchKernelGGL((gemv_valu_kernel<FMT, NT, R, GATED, EP>), grid, dim3(GV_THREADS), 0, s,
                        static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), x, y,
-                       static_cast<int>(M), static_cast<int>(K), K, M, static_cast<int>(row_begin));
+                       static_cast<int>(M), static_cast<int>(K), K, M, static_cast<int>(row_begin), epi);
 }
 
-template <int FMT, bool GATED>
+template <int FMT, bool GATED, int EP>
 static void launch_fmt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, int NT,
-                       int64_t chunks, int64_t row_begin, hipStream_t s) {
+                       int64_t chunks, int64_t row_begin, const DecodeEpi& epi, hipStream_t s) {
     switch (NT) {
-        case 1: launch_fmt_nt<FMT, 1, GATED>(W, Wu, x, y, M, K, chunks, row_begin, s); break;
-        case 2: launch_fmt_nt<FMT, 2, GATED>(W, Wu, x, y, M, K, chunks, row_begin, s); break;
-        case 3: launch_fmt_nt<FMT, 3, GATED>(W, Wu, x, y, M, K, chunks, row_begin, s); break;
-        default: launch_fmt_nt<FMT, 4, GATED>(W, Wu, x, y, M, K, chunks, row_begin, s); break;
+        case 1: launch_fmt_nt<FMT, 1, GATED, EP>(W, Wu, x, y, M, K, chunks, row_begin, epi, s); break;
+        case 2: launch_fmt_nt<FMT, 2, GATED, EP>(W, Wu, x, y, M, K, chunks, row_begin, epi, s); break;
+        case 3: launch_fmt_nt<FMT, 3, GATED, EP>(W, Wu, x, y, M, K, chunks, row_begin, epi, s); break;
+        default: launch_fmt_nt<FMT, 4, GATED, EP>(W, Wu, x, y, M, K, chunks, row_begin, epi, s); break;
+    }
+}
+
+template <int FMT>
+static void launch_fmt_any(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, int NT,
+                           int64_t chunks, int64_t row_begin, int ep, const DecodeEpi& epi, hipStream_t s) {
+    if (Wu) {
+        if (ep == EP_NORM) launch_fmt<FMT, true, EP_NORM>(W, Wu, x, y, M, K, NT, chunks, row_begin, epi, s);
+        else launch_fmt<FMT, true, EP_NONE>(W, Wu, x, y, M, K, NT, chunks, row_begin, epi, s);
+    } else if (ep == EP_NORM) {
+        launch_fmt<FMT, false, EP_NORM>(W, Wu, x, y, M, K, NT, chunks, row_begin, epi, s);
+    } else if (ep == EP_RES) {
+        launch_fmt<FMT, false, EP_RES>(W, Wu, x, y, M, K, NT, chunks, row_begin, epi, s);
+    } else {
+        launch_fmt<FMT, false, EP_NONE>(W, Wu, x, y, M, K, NT, chunks, row_begin, epi, s);
     }
 }
 
 void launch_gemv_sliced(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
-                        int NT, int64_t chunks, int64_t row_begin, hipStream_t s) {
-    const bool gated = Wu != nullptr;
-    if (gated) {
-        if (fmt == 8) launch_fmt<8, true>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
-        else if (fmt == 2) launch_fmt<2, true>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
-        else launch_fmt<1, true>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
-    } else {
-        if (fmt == 8) launch_fmt<8, false>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
-        else if (fmt == 2) launch_fmt<2, false>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
-        else launch_fmt<1, false>(W, Wu, x, y, M, K, NT, chunks, row_begin, s);
-    }
+                        int NT, int64_t chunks, int64_t row_begin, int ep, const DecodeEpi& epi, hipStream_t s) {
+    if (fmt == 8) launch_fmt_any<8>(W, Wu, x, y, M, K, NT, chunks, row_begin, ep, epi, s);
+    else if (fmt == 2) launch_fmt_any<2>(W, Wu, x, y, M, K, NT, chunks, row_begin, ep, epi, s);
+    else launch_fmt_any<1>(W, Wu, x, y, M, K, NT, chunks, row_begin, ep, epi, s);
 }
 
 hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M,
-                            int64_t K, int64_t N, hipStream_t s) {
+                            int64_t K, int64_t N, hipStream_t s, int ep, const DecodeEpi& epi) {
     int64_t done = 0;
+    // The residual of the pass that starts at token `done`.
+    auto at = [&](int64_t d) {
+        DecodeEpi e = epi;
+        if (e.res) e.res += d * M;
+        return e;
+    };
     // Block formats: the streaming kernel, up to 4 tokens per pass, as many tokens per
     // pass as its LDS copy of x allows; a final row it leaves is done by the sliced kernel.
     while (done < N) {
         int nt = static_cast<int>(std::min<int64_t>(4, N - done));
         int64_t rows = 0;
-        while (nt > 0 && (rows = launch_gemv_stream(fmt, W, Wu, x + done * K, y + done * M, M, K, nt, s)) == 0) --nt;
+        const DecodeEpi e = at(done);
+        while (nt > 0 && (rows = launch_gemv_stream(fmt, W, Wu, x + done * K, y + done * M, M, K, nt, ep, e, s)) == 0)
+            --nt;
         if (nt == 0) break;
-        if (rows < M) launch_gemv_sliced(fmt, W, Wu, x + done * K, y + done * M, M, K, nt, 1, rows, s);
+        if (rows < M) launch_gemv_sliced(fmt, W, Wu, x + done * K, y + done * M, M, K, nt, 1, rows, ep, e, s);
         done += nt;
     }
     // F16, or x too large for LDS: the sliced kernel, 4 tokens per pass (grid.y
@@ -217,11 +262,12 @@ hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float*
     constexpr int64_t kMaxChunks = 65535;
     while (N - done >= 4) {
         const int64_t chunks = std::min<int64_t>((N - done) / 4, kMaxChunks);
-        launch_gemv_sliced(fmt, W, Wu, x + done * K, y + done * M, M, K, 4, chunks, 0, s);
+        launch_gemv_sliced(fmt, W, Wu, x + done * K, y + done * M, M, K, 4, chunks, 0, ep, at(done), s);
         done += 4 * chunks;
     }
     if (N - done > 0)
-        launch_gemv_sliced(fmt, W, Wu, x + done * K, y + done * M, M, K, static_cast<int>(N - done), 1, 0, s);
+        launch_gemv_sliced(fmt, W, Wu, x + done * K, y + done * M, M, K, static_cast<int>(N - done), 1, 0, ep,
+                           at(done), s);
     return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@
 #pragma once
 
 #include "qmm_common.hpp"
+#include "qmm_internal.hpp"
 
 namespace qmm {
 
@@ -102,12 +103,43 @@ __device__ __forceinline__ void block_fma(const uint8_t* const (&buf)[RU], const
         for (int n = 0; n < NT; ++n) acc[u][n] = fmaf(d[u], bacc[u][n], acc[u][n]);
 }
 
+// Per-token partial sums of squares of a workgroup -> LDS.  Each wave reduces its
+// lanes' values; lane 0 writes red[wave * NT + n].  A barrier must separate this
+// from norm_scales.
+template <int NT>
+__device__ __forceinline__ void norm_partials(float (&ss)[NT], float* red, int wave, int lane) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        float v = ss[n];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) red[wave * NT + n] = v;
+    }
+}
+
+// The token whose sums lane `lane` holds after reduce_store's transposing reduction.
+template <int RU, int NT>
+__device__ __forceinline__ int reduced_token(int lane) {
+    constexpr int NTP = (NT == 3) ? 4 : NT;
+    constexpr int LPI = kWave / (RU * NTP);
+    return min((lane / LPI) % NTP, NT - 1);
+}
+
+// Inverse RMS of token n from the waves' partials, summed in wave order.
+template <int NT>
+__device__ __forceinline__ float norm_scale(const float* red, int waves, int n, int K, float eps) {
+    float t = 0.0f;
+    for (int w = 0; w < waves; ++w) t += red[w * NT + n];
+    return 1.0f / sqrtf(t / static_cast<float>(K) + eps);
+}
+
 // Reduce the RU x NT per-lane partial sums of a wave and store them:
 // rows row0 + (u % R) for u < R go to y (or, gated, h = silu(gate) * up with the
-// up partials in u >= R).
-template <int R, int RU, int NT, bool GATED>
+// up partials in u >= R), with the EP step applied (scale: the norm scale of the
+// lane's reduced token, reduced_token<RU, NT>(lane)).
+template <int R, int RU, int NT, bool GATED, int EP = EP_NONE>
 __device__ __forceinline__ void reduce_store(float (&acc)[RU][NT], int lane, int row0, int M, float* y,
-                                             int64_t ldy) {
+                                             int64_t ldy, float scale, const float* res) {
     constexpr int NTP = (NT == 3) ? 4 : NT;
     constexpr int V = RU * NTP;
     float v[V];
@@ -123,10 +155,20 @@ __device__ __forceinline__ void reduce_store(float (&acc)[RU][NT], int lane, int
     const int n = idx - u * NTP;
     const int r = row0 + u;
     if constexpr (!GATED) {
-        if (holder && n < NT && r < M) y[n * ldy + r] = v[0];
+        if (holder && n < NT && r < M) {
+            float val = v[0];
+            if constexpr (EP == EP_NORM) val *= scale;
+            if constexpr (EP == EP_RES) val += res[n * ldy + r];
+            y[n * ldy + r] = val;
+        }
     } else {
-        const float upv = __shfl(v[0], (lane + R * NTP * LPI) & (kWave - 1), kWave);
-        if (holder && u < R && n < NT && r < M) y[n * ldy + r] = silu(v[0]) * upv;
+        float upv = __shfl(v[0], (lane + R * NTP * LPI) & (kWave - 1), kWave);
+        float gv = v[0];
+        if constexpr (EP == EP_NORM) {
+            gv *= scale;
+            upv *= scale;
+        }
+        if (holder && u < R && n < NT && r < M) y[n * ldy + r] = silu(gv) * upv;
     }
 }
 

@@ -52,12 +52,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int FMT, int NT, int R, bool GATED, int WAVES, int D>
+template <int FMT, int NT, int R, bool GATED, int WAVES, int D, int EP>
 __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* __restrict__ Wg,
                                                                   const uint8_t* __restrict__ Wu,
                                                                   const float* __restrict__ x,
                                                                   float* __restrict__ y, int M, int K,
-                                                                  int64_t ldx, int64_t ldy, int xs_bytes) {
+                                                                  int64_t ldx, int64_t ldy, int xs_bytes,
+                                                                  DecodeEpi epi) {
     using G = StreamGeom<FMT>;
     constexpr int BB = G::BB, BPL = G::BPL, SLICE = G::SLICE, CPR = G::CPR, LPR = G::LPR, ROWBUF = G::ROWBUF;
     constexpr int RU = GATED ? 2 * R : R;
@@ -119,14 +120,29 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
     for (int q = 0; q < D; ++q)
         if (q < ntask) issue(q, regs[q]);
 
-    // x -> LDS once: NT tokens x nb blocks, 8 float4 per block.
-    for (int i = threadIdx.x; i < NT * nb * 8; i += WAVES * kWave) {
-        const int n = i / (nb * 8);
-        const int j = i - n * (nb * 8);
-        const float4 v = *reinterpret_cast<const float4*>(x + n * ldx + 4 * static_cast<int64_t>(j));
-        *reinterpret_cast<float4*>(xs + n * xstride + (j >> 3) * XS_STRIDE + 4 * (j & 7)) = v;
+    // x -> LDS once: NT tokens x nb blocks, 8 float4 per block (EP_NORM: gamma .* x,
+    // with the sum of squares of x gathered on the way).
+    float ss[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) ss[n] = 0.0f;
+    for (int j = threadIdx.x; j < nb * 8; j += WAVES * kWave) {
+        float4 gm = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        if constexpr (EP == EP_NORM) gm = *reinterpret_cast<const float4*>(epi.gamma + 4 * static_cast<int64_t>(j));
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            float4 v = *reinterpret_cast<const float4*>(x + n * ldx + 4 * static_cast<int64_t>(j));
+            if constexpr (EP == EP_NORM) {
+                ss[n] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss[n]))));
+                v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
+            }
+            *reinterpret_cast<float4*>(xs + n * xstride + (j >> 3) * XS_STRIDE + 4 * (j & 7)) = v;
+        }
     }
+    float* red = reinterpret_cast<float*>(smem + xs_bytes + WAVES * (RU * ROWBUF));
+    if constexpr (EP == EP_NORM) norm_partials<NT>(ss, red, wave, lane);
     __syncthreads();
+    float scale = 1.0f;
+    if constexpr (EP == EP_NORM) scale = norm_scale<NT>(red, WAVES, reduced_token<RU, NT>(lane), K, epi.eps);
 
     for (int t0 = 0; t0 < ntask; t0 += D) {
 #pragma unroll
@@ -172,7 +188,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
             }
         }
         if (s == ns - 1) {
-            reduce_store<R, RU, NT, GATED>(acc, lane, g * R, M, y, ldy);
+            reduce_store<R, RU, NT, GATED, EP>(acc, lane, g * R, M, y, ldy, scale, epi.res);
 #pragma unroll
             for (int u = 0; u < RU; ++u)
 #pragma unroll
@@ -186,9 +202,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
 // not a multiple of 16 bytes: the final row's last 16-byte chunk would cross the
 // end of the buffer, so that row is left to the caller), or 0 when this kernel
 // does not apply (LDS too small for x, or a single such row).
-template <int FMT, int NT, int R, bool GATED, int WAVES, int D>
+template <int FMT, int NT, int R, bool GATED, int WAVES, int D, int EP>
 static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
-                        hipStream_t s) {
+                        const DecodeEpi& epi, hipStream_t s) {
     const int64_t ldy = M;
     using G = StreamGeom<FMT>;
     constexpr int RU = GATED ? 2 * R : R;
@@ -199,10 +215,10 @@ static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y,
         M -= 1;  // every chunk of the first M - 1 rows ends at most 15 bytes into the last row
     }
     const int64_t xs_bytes = ((NT * nb * XS_STRIDE * 4) + 15) / 16 * 16;
-    const int64_t lds = xs_bytes + static_cast<int64_t>(WAVES) * RU * G::ROWBUF;
+    const int64_t lds = xs_bytes + static_cast<int64_t>(WAVES) * RU * G::ROWBUF + (EP == EP_NORM ? WAVES * NT * 4 : 0);
     constexpr int64_t kMaxLds = 160 * 1024;
     if (lds > kMaxLds) return 0;
-    auto kern = gemv_stream_kernel<FMT, NT, R, GATED, WAVES, D>;
+    auto kern = gemv_stream_kernel<FMT, NT, R, GATED, WAVES, D, EP>;
     static bool attr_set = false;
     if (!attr_set) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -214,7 +230,7 @@ static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y,
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((ngroups + WAVES - 1) / WAVES, 256 * per_cu));
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(WAVES * kWave), static_cast<size_t>(lds), s,
                        static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), x, y, static_cast<int>(M),
-                       static_cast<int>(K), K, ldy, static_cast<int>(xs_bytes));
+                       static_cast<int>(K), K, ldy, static_cast<int>(xs_bytes), epi);
     return M;
 }
 
@@ -223,39 +239,51 @@ static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y,
 // task for large outputs and 1 row otherwise; the gated kernel runs 8 waves with
 // 1 gate + 1 up row per task, prefetching two tasks ahead when each wave owns
 // only a few tasks, so that the whole matrix is in flight at once.
-template <int FMT, int NT>
-static int64_t launch_nt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, hipStream_t s) {
+template <int FMT, int NT, int EP>
+static int64_t launch_nt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                         const DecodeEpi& epi, hipStream_t s) {
     const int64_t nb = K / 32;
     const int64_t slices = (nb + StreamGeom<FMT>::SLICE - 1) / StreamGeom<FMT>::SLICE;
     if (Wu) {
-        const bool deep = (M * slices) / (256 * 8) <= 2;  // tasks per wave
-        return deep ? launch_t<FMT, NT, 1, true, 8, 2>(W, Wu, x, y, M, K, s)
-                    : launch_t<FMT, NT, 1, true, 8, 1>(W, Wu, x, y, M, K, s);
+        if constexpr (EP == EP_RES) {
+            return 0;  // no residual on the gated product
+        } else {
+            const bool deep = (M * slices) / (256 * 8) <= 2;  // tasks per wave
+            return deep ? launch_t<FMT, NT, 1, true, 8, 2, EP>(W, Wu, x, y, M, K, epi, s)
+                        : launch_t<FMT, NT, 1, true, 8, 1, EP>(W, Wu, x, y, M, K, epi, s);
+        }
     }
     // 16 waves per workgroup cap a wave at 128 VGPRs; 3-4 tokens need more.
     constexpr int PW = NT <= 2 ? 16 : 8;
-    if (M >= 16384) return launch_t<FMT, NT, 2, false, PW, 1>(W, Wu, x, y, M, K, s);
-    return launch_t<FMT, NT, 1, false, PW, 1>(W, Wu, x, y, M, K, s);
+    if (M >= 16384) return launch_t<FMT, NT, 2, false, PW, 1, EP>(W, Wu, x, y, M, K, epi, s);
+    return launch_t<FMT, NT, 1, false, PW, 1, EP>(W, Wu, x, y, M, K, epi, s);
+}
+
+template <int FMT, int EP>
+static int64_t launch_fmt_ep(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, int NT,
+                             const DecodeEpi& epi, hipStream_t s) {
+    switch (NT) {
+        case 1: return launch_nt<FMT, 1, EP>(W, Wu, x, y, M, K, epi, s);
+        case 2: return launch_nt<FMT, 2, EP>(W, Wu, x, y, M, K, epi, s);
+        case 3: return launch_nt<FMT, 3, EP>(W, Wu, x, y, M, K, epi, s);
+        default: return launch_nt<FMT, 4, EP>(W, Wu, x, y, M, K, epi, s);
+    }
+}
+
+template <int FMT>
+static int64_t launch_fmt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, int NT,
+                          int ep, const DecodeEpi& epi, hipStream_t s) {
+    switch (ep) {
+        case EP_NORM: return launch_fmt_ep<FMT, EP_NORM>(W, Wu, x, y, M, K, NT, epi, s);
+        case EP_RES: return launch_fmt_ep<FMT, EP_RES>(W, Wu, x, y, M, K, NT, epi, s);
+        default: return launch_fmt_ep<FMT, EP_NONE>(W, Wu, x, y, M, K, NT, epi, s);
+    }
 }
 
 int64_t launch_gemv_stream(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
-                        int NT, hipStream_t s) {
-    if (fmt == 8) {
-        switch (NT) {
-            case 1: return launch_nt<8, 1>(W, Wu, x, y, M, K, s);
-            case 2: return launch_nt<8, 2>(W, Wu, x, y, M, K, s);
-            case 3: return launch_nt<8, 3>(W, Wu, x, y, M, K, s);
-            default: return launch_nt<8, 4>(W, Wu, x, y, M, K, s);
-        }
-    }
-    if (fmt == 2) {
-        switch (NT) {
-            case 1: return launch_nt<2, 1>(W, Wu, x, y, M, K, s);
-            case 2: return launch_nt<2, 2>(W, Wu, x, y, M, K, s);
-            case 3: return launch_nt<2, 3>(W, Wu, x, y, M, K, s);
-            default: return launch_nt<2, 4>(W, Wu, x, y, M, K, s);
-        }
-    }
+                           int NT, int ep, const DecodeEpi& epi, hipStream_t s) {
+    if (fmt == 8) return launch_fmt<8>(W, Wu, x, y, M, K, NT, ep, epi, s);
+    if (fmt == 2) return launch_fmt<2>(W, Wu, x, y, M, K, NT, ep, epi, s);
     return 0;
 }
 

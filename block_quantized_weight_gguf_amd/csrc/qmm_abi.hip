@@ -2,6 +2,7 @@
 // Every check runs before any HIP call, so an invalid call enqueues nothing.
 // Size arithmetic is overflow-checked ("alpaca.swift", Highlights: untrusted
 // lengths are bounded and all size arithmetic is checked).
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/qmm.h"
@@ -69,6 +70,7 @@ const char* qmm_strerror(int status) {
         case QMM_ERR_OVERFLOW: return "a byte count overflows int64";
         case QMM_ERR_HIP: return "HIP runtime error at launch";
         case QMM_ERR_VARIANT: return "unknown GEMV variant";
+        case QMM_ERR_ARG: return "a scalar argument is out of range (eps must be finite and >= 0)";
         default: return "unknown qmm status";
     }
 }
@@ -156,6 +158,47 @@ int qmm_gate_up_silu_variant(int fmt, const void* Wg, const void* Wu, const floa
 int qmm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, float* h, int64_t I, int64_t K,
                      int64_t N, void* stream) {
     return qmm_gate_up_silu_variant(fmt, Wg, Wu, x, h, I, K, N, QMM_VARIANT_AUTO, stream);
+}
+
+int qmm_rmsnorm_gemv(int fmt, const void* W, const float* x, const float* gamma, float eps, float* y, int64_t M,
+                     int64_t K, int64_t N, void* stream) {
+    if (!W || !x || !gamma || !y) return QMM_ERR_NULL;
+    int st = check_shape(fmt, M, K, N);
+    if (st) return st;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return QMM_ERR_ARG;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(gamma, 16) || !aligned(y, 4)) return QMM_ERR_ALIGN;
+    qmm::DecodeEpi epi;
+    epi.gamma = gamma;
+    epi.eps = eps;
+    return from_hip(qmm::launch_gemv_valu(fmt, W, nullptr, x, y, M, K, N, static_cast<hipStream_t>(stream),
+                                          qmm::EP_NORM, epi));
+}
+
+int qmm_rmsnorm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, const float* gamma, float eps,
+                             float* h, int64_t I, int64_t K, int64_t N, void* stream) {
+    if (!Wg || !Wu || !x || !gamma || !h) return QMM_ERR_NULL;
+    int st = check_shape(fmt, I, K, N);
+    if (st) return st;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return QMM_ERR_ARG;
+    if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(x, 16) || !aligned(gamma, 16) || !aligned(h, 4))
+        return QMM_ERR_ALIGN;
+    qmm::DecodeEpi epi;
+    epi.gamma = gamma;
+    epi.eps = eps;
+    return from_hip(qmm::launch_gemv_valu(fmt, Wg, Wu, x, h, I, K, N, static_cast<hipStream_t>(stream),
+                                          qmm::EP_NORM, epi));
+}
+
+int qmm_gemv_add(int fmt, const void* W, const float* x, const float* r, float* y, int64_t M, int64_t K, int64_t N,
+                 void* stream) {
+    if (!W || !x || !r || !y) return QMM_ERR_NULL;
+    int st = check_shape(fmt, M, K, N);
+    if (st) return st;
+    if (!aligned(W, 16) || !aligned(x, 16) || !aligned(r, 4) || !aligned(y, 4)) return QMM_ERR_ALIGN;
+    qmm::DecodeEpi epi;
+    epi.res = r;
+    return from_hip(qmm::launch_gemv_valu(fmt, W, nullptr, x, y, M, K, N, static_cast<hipStream_t>(stream),
+                                          qmm::EP_RES, epi));
 }
 
 int qmm_gemm(int fmt, const void* W, const void* X, float* Y, int64_t M, int64_t K, int64_t T, void* stream) {

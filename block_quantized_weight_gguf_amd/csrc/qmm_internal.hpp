@@ -9,6 +9,23 @@
 
 namespace qmm {
 
+// Fused steps around the decode GEMV ("EdgeRunner Core Architecture", section 9.2:
+// the attention and FFN norms are folded into the QKV and gate+up GEMVs, the
+// final norm into the LM head, and the O and down GEMVs add into the residual).
+//   EP_NORM: y = s * (W (gamma .* x)), s = 1 / sqrt(mean_k x_k^2 + eps) per token
+//            (RMSNorm, section 6).  gamma .* x is formed while x is staged in LDS;
+//            the sum of squares is gathered on the same pass and s scales the
+//            reduced dot products.
+//   EP_RES:  y = W x + res, res laid out like y (it may be y itself: each element
+//            is read and then written by the same lane).
+enum : int { EP_NONE = 0, EP_NORM = 1, EP_RES = 2 };
+
+struct DecodeEpi {
+    const float* gamma = nullptr;  // EP_NORM: K norm weights
+    float eps = 0.0f;
+    const float* res = nullptr;    // EP_RES: residual input
+};
+
 hipError_t launch_dequant(int fmt, const void* W, float* out, int64_t M, int64_t K, hipStream_t s);
 
 // out[i][k] = W[ids[i]][k] (fp32) for i < n; ids outside [0, M) give NaN rows.
@@ -20,19 +37,21 @@ hipError_t launch_expand_f16(int fmt, const void* W, void* out, int64_t M, int64
 
 // VALU GEMV over N tokens (any N >= 1): y[n][m] = sum_k W[m][k] x[n][k].
 // Wu != nullptr selects the gate/up SwiGLU epilogue (W = gate, Wu = up, y = h).
+// ep (EP_*) adds the norm prologue or the residual epilogue (not with Wu) from epi.
 hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float* x, float* y,
-                            int64_t M, int64_t K, int64_t N, hipStream_t s);
+                            int64_t M, int64_t K, int64_t N, hipStream_t s, int ep = EP_NONE,
+                            const DecodeEpi& epi = DecodeEpi{});
 
 // Streaming GEMV for Q8_0 / Q4_0 with NT <= 4 tokens in one pass.  Returns the
 // number of leading rows it launched (M or M - 1); 0 means nothing was launched
 // (format or LDS footprint of x does not fit).
 int64_t launch_gemv_stream(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
-                           int NT, hipStream_t s);
+                           int NT, int ep, const DecodeEpi& epi, hipStream_t s);
 
 // Sliced GEMV for rows [row_begin, M), NT <= 4 tokens per pass, `chunks` passes
 // of NT tokens (grid.y).  Handles every format and every size.
 void launch_gemv_sliced(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
-                        int NT, int64_t chunks, int64_t row_begin, hipStream_t s);
+                        int NT, int64_t chunks, int64_t row_begin, int ep, const DecodeEpi& epi, hipStream_t s);
 
 // fp16-MFMA GEMM: Y[t][m] = sum_k W[m][k] X[t][k]; X is fp16 (x_is_f32 = false) or fp32
 // rounded to fp16 while staging (x_is_f32 = true).  Wu != nullptr selects the SwiGLU epilogue.

@@ -47,8 +47,9 @@
  *   - Size checks follow the practice of bounding every length and checking
  *     every size product for overflow ("alpaca.swift", Highlights: the GGUF
  *     parser treats files as untrusted).
- *   - Outputs must not alias inputs (not checked).
- *   - Alignment: W, x, X must be 16-byte aligned; y, Y, h, H, out 4-byte aligned.
+ *   - Outputs must not alias inputs (not checked), except where a call says so.
+ *   - Alignment: W, x, X, gamma must be 16-byte aligned; y, Y, h, H, r 4-byte aligned
+ *     (out of qmm_get_rows / qmm_expand_f16: 16 bytes).
  *   - Limits: 1 <= M, K, N, T <= 2^31 - 1 and K % 32 == 0 for every format (F16
  *     included, so that all formats share the 32-wide tiling).
  */
@@ -75,7 +76,8 @@ typedef enum {
     QMM_ERR_ALIGN = -4,       /* a pointer violates the alignment rule above       */
     QMM_ERR_OVERFLOW = -5,    /* a byte count does not fit in int64                */
     QMM_ERR_HIP = -6,         /* the HIP runtime reported an error at launch       */
-    QMM_ERR_VARIANT = -7      /* unknown variant id passed to a *_variant call     */
+    QMM_ERR_VARIANT = -7,     /* unknown variant id passed to a *_variant call     */
+    QMM_ERR_ARG = -8          /* a scalar argument is out of range (eps)           */
 } qmm_status;
 
 /* Variant ids for qmm_gemv_variant, qmm_gate_up_silu_variant and qmm_gemv_choose. */
@@ -177,6 +179,43 @@ int qmm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, fl
 /* As qmm_gate_up_silu with an explicit variant (QMM_VARIANT_*), for crossover sweeps. */
 int qmm_gate_up_silu_variant(int fmt, const void* Wg, const void* Wu, const float* x, float* h,
                              int64_t I, int64_t K, int64_t N, int variant, void* stream);
+
+/*
+ * Decode GEMV with the RMSNorm prologue fused in:
+ *   x'[n][k] = x[n][k] / sqrt(mean_k x[n][k]^2 + eps) * gamma[k],
+ *   y[n][m]  = sum_k W[m][k] * x'[n][k].
+ * For the attention norm + fused QKV and the final norm + LM head.  gamma is K
+ * fp32 norm weights (16-byte aligned); eps must be finite and >= 0 (else
+ * QMM_ERR_ARG).  Runs the register-decode GEMV kernels (4 tokens per weight pass):
+ * each workgroup forms gamma .* x while staging x and gathers the sum of squares on
+ * the same pass, then scales its reduced dot products, so the norm adds only the
+ * K * 4 bytes of gamma.  ("EdgeRunner Core Architecture", section 6 RMSNorm,
+ * section 2.1 fused QKV with RMSNorm, section 9.2 fused decode pass with the final
+ * norm folded into the LM head.  The page leaves open where eps enters: here it is
+ * added to the mean square inside the root; Llama-style norms have no bias.)
+ */
+int qmm_rmsnorm_gemv(int fmt, const void* W, const float* x, const float* gamma, float eps, float* y,
+                     int64_t M, int64_t K, int64_t N, void* stream);
+
+/*
+ * Gate+up SwiGLU with the FFN RMSNorm prologue: h = silu(x' Wg^T) * (x' Wu^T) with
+ * x' as in qmm_rmsnorm_gemv.  ("EdgeRunner Core Architecture", section 8: RMSNorm,
+ * gate, up and SiLU in one dispatch at a single token.)
+ */
+int qmm_rmsnorm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, const float* gamma,
+                             float eps, float* h, int64_t I, int64_t K, int64_t N, void* stream);
+
+/*
+ * Decode GEMV with the residual-add epilogue: y[n][m] = sum_k W[m][k] x[n][k] + r[n][m].
+ * r has y's layout (N x M fp32, 4-byte aligned) and may be y itself (in-place add
+ * into the residual stream; each element is read, then written, by one lane; any
+ * other overlap is not allowed).  For the O and down projections.  Register-decode
+ * GEMV kernels, 4 tokens per weight pass.  ("EdgeRunner Core Architecture",
+ * section 9.1 steps 13-14 and section 9.2: the O and down GEMVs add into the
+ * residual in the same dispatch.)
+ */
+int qmm_gemv_add(int fmt, const void* W, const float* x, const float* r, float* y,
+                 int64_t M, int64_t K, int64_t N, void* stream);
 
 /*
  * Prefill GEMM: Y[t][m] = sum_k W[m][k] * X[t][k], X fp16 (T x K), Y fp32 (T x M).

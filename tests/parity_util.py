@@ -60,3 +60,16 @@ def sample_rows(M: int, n: int, seed: int) -> np.ndarray:
     g = np.random.default_rng(seed)
     rows = set([0, 1, M - 1, M - 2] + list(g.integers(0, M, size=n)))
     return np.array(sorted(r for r in rows if 0 <= r < M), dtype=np.int64)
+
+
+def check_residual(got, ref, S, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output (unwritten element?)"
+    err = np.abs(got - ref)
+    tol = oracle.tol_residual(S, ref)
+    bad = err > tol
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} elements out of tolerance; first at {tuple(i)}: "
+                             f"got {got[tuple(i)]!r} ref {ref[tuple(i)]!r} tol {tol[tuple(i)]!r}")

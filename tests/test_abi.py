@@ -16,7 +16,7 @@ import block_quantized_weight_gguf_amd as qmm
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qmm.h")
 
-OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR = 0, -1, -2, -3, -4, -5, -6, -7
+OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
 A16 = 0x10000  # a 16-byte aligned fake address (never dereferenced)
 
 
@@ -30,7 +30,8 @@ def test_header_declares_expected_api():
     assert declared_functions() == sorted([
         "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv", "qmm_gemv_variant",
         "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
-        "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16"])
+        "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16", "qmm_rmsnorm_gemv",
+        "qmm_rmsnorm_gate_up_silu", "qmm_gemv_add"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert qmm.qmm_version() >= 100
-    for s in (OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR):
+    for s in (OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR, E_ARG):
         assert qmm.qmm_strerror(s) and "unknown qmm status" not in qmm.qmm_strerror(s)
     assert "unknown" in qmm.qmm_strerror(-99)
 
@@ -134,6 +135,40 @@ def test_expand_f16_validation():
     assert L.qmm_expand_f16(1, A16, A16, 0, 64, None) == E_SHAPE
     assert L.qmm_expand_f16(2, A16, A16 + 8, 4, 64, None) == E_ALIGN
     assert L.qmm_expand_f16(2, A16 + 2, A16, 4, 64, None) == E_ALIGN
+
+
+def test_rmsnorm_gemv_validation():
+    L = qmm._lib
+    f = ctypes.c_float
+    assert L.qmm_rmsnorm_gemv(8, A16, A16, None, f(1e-5), A16, 4, 64, 1, None) == E_NULL
+    assert L.qmm_rmsnorm_gemv(8, None, A16, A16, f(1e-5), A16, 4, 64, 1, None) == E_NULL
+    assert L.qmm_rmsnorm_gemv(8, A16, A16, A16, f(1e-5), None, 4, 64, 1, None) == E_NULL
+    assert L.qmm_rmsnorm_gemv(4, A16, A16, A16, f(1e-5), A16, 4, 64, 1, None) == E_FMT
+    assert L.qmm_rmsnorm_gemv(8, A16, A16, A16, f(1e-5), A16, 4, 50, 1, None) == E_SHAPE
+    assert L.qmm_rmsnorm_gemv(8, A16, A16, A16, f(1e-5), A16, 4, 64, 0, None) == E_SHAPE
+    for bad in (-1e-6, float("nan"), float("inf"), -float("inf")):
+        assert L.qmm_rmsnorm_gemv(8, A16, A16, A16, f(bad), A16, 4, 64, 1, None) == E_ARG
+    assert L.qmm_rmsnorm_gemv(8, A16, A16, A16 + 4, f(1e-5), A16, 4, 64, 1, None) == E_ALIGN
+    assert L.qmm_rmsnorm_gemv(8, A16, A16 + 8, A16, f(1e-5), A16, 4, 64, 1, None) == E_ALIGN
+    assert L.qmm_rmsnorm_gemv(8, A16, A16, A16, f(1e-5), A16 + 2, 4, 64, 1, None) == E_ALIGN
+    assert L.qmm_rmsnorm_gate_up_silu(8, A16, A16, A16, None, f(1e-5), A16, 4, 64, 1, None) == E_NULL
+    assert L.qmm_rmsnorm_gate_up_silu(8, A16, None, A16, A16, f(1e-5), A16, 4, 64, 1, None) == E_NULL
+    assert L.qmm_rmsnorm_gate_up_silu(1, A16, A16, A16, A16, f(1e-5), A16, 4, 48, 1, None) == E_SHAPE
+    assert L.qmm_rmsnorm_gate_up_silu(8, A16, A16, A16, A16, f(-1.0), A16, 4, 64, 1, None) == E_ARG
+    assert L.qmm_rmsnorm_gate_up_silu(8, A16, A16, A16, A16 + 8, f(0.0), A16, 4, 64, 1, None) == E_ALIGN
+    assert L.qmm_rmsnorm_gate_up_silu(8, A16, A16, A16, A16, f(0.0), A16 + 1, 4, 64, 1, None) == E_ALIGN
+
+
+def test_gemv_add_validation():
+    L = qmm._lib
+    assert L.qmm_gemv_add(8, A16, A16, None, A16, 4, 64, 1, None) == E_NULL
+    assert L.qmm_gemv_add(8, A16, None, A16, A16, 4, 64, 1, None) == E_NULL
+    assert L.qmm_gemv_add(2, A16, A16, A16, None, 4, 64, 1, None) == E_NULL
+    assert L.qmm_gemv_add(0, A16, A16, A16, A16, 4, 64, 1, None) == E_FMT
+    assert L.qmm_gemv_add(2, A16, A16, A16, A16, 0, 64, 1, None) == E_SHAPE
+    assert L.qmm_gemv_add(2, A16, A16, A16 + 2, A16, 4, 64, 1, None) == E_ALIGN
+    assert L.qmm_gemv_add(2, A16, A16, A16, A16 + 2, 4, 64, 1, None) == E_ALIGN
+    assert L.qmm_gemv_add(2, A16 + 4, A16, A16, A16, 4, 64, 1, None) == E_ALIGN
 
 
 def test_variant_choice():
