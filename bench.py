@@ -14,6 +14,11 @@ The same run also times the prefill GEMM (fp16 activations, fp32 output) at
 TFLOP/s = 2 T M K / time; and times the float64 CPU oracle on a bounded sample of
 the decode step (reported baseline only).
 
+Further sections (timing only): the decode step with the RMSNorm prologues and
+residual epilogues fused in, expand-then-GEMM prefill against the fused GEMM,
+the quantised embedding row gather, small-batch decode, measured ceilings and a
+SmolLM2-135M-shaped decode step.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--suite PATH]
 """
 from __future__ import annotations
@@ -42,6 +47,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-smollm", action="store_true")
     p.add_argument("--no-small-batch", action="store_true")
+    p.add_argument("--no-next", action="store_true",
+                   help="skip the fused-norm/residual step, expand-then-GEMM and row gather sections")
     p.add_argument("--suite", default=None, help="write per-kernel details as JSON to this path")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
@@ -260,6 +267,129 @@ def small_batch(torch, qmm, si, reps=20):
     return out
 
 
+def fused_decode(torch, qmm, si, fmts, steps):
+    """The decode step with the neighbouring steps fused in: attention norm + QKV,
+    O + residual, FFN norm + gate+up+SwiGLU, down + residual, final norm + LM head,
+    on the same weights as the plain step.  Bytes add gamma (4 K per norm) and the
+    residual read (4 M per add) to the plain step's."""
+    L = si.LLAMA3_8B
+    H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
+    dev = torch.device("cuda")
+    gamma = torch.from_numpy((1.0 + 0.1 * si.activations(1, H, 4242)[0]).astype(np.float32)).to(dev)
+    resid = torch.from_numpy(si.activations(1, H, 4243)).to(dev)
+    eps = 1e-5
+    out = {}
+    for fmt, f in fmts.items():
+        r = lambda K: qmm.qmm_row_bytes(fmt, K)
+        plain_bytes = (Q * r(H) + 4 * H + 4 * Q) + (H * r(H) + 8 * H) + (2 * I * r(H) + 4 * H + 4 * I) + \
+                      (H * r(I) + 4 * I + 4 * H) + (V * r(H) + 4 * H + 4 * V)
+        fused_bytes = plain_bytes + 3 * 4 * H + 2 * 4 * H
+
+        def plain(f=f):
+            qmm.qmm_gemv(fmt, f["qkv"], f["x"], f["y_qkv"], Q, H, 1)
+            qmm.qmm_gemv(fmt, f["o"], f["x"], f["y_o"], H, H, 1)
+            qmm.qmm_gate_up_silu(fmt, f["g"], f["u"], f["x"], f["h"], I, H, 1)
+            qmm.qmm_gemv(fmt, f["d"], f["h"], f["y_d"], H, I, 1)
+            qmm.qmm_gemv(fmt, f["lm"], f["x"], f["logits"], V, H, 1)
+
+        def fused(f=f):
+            qmm.qmm_rmsnorm_gemv(fmt, f["qkv"], f["x"], gamma, eps, f["y_qkv"], Q, H, 1)
+            qmm.qmm_gemv_add(fmt, f["o"], f["x"], resid, resid, H, H, 1)
+            qmm.qmm_rmsnorm_gate_up_silu(fmt, f["g"], f["u"], f["x"], gamma, eps, f["h"], I, H, 1)
+            qmm.qmm_gemv_add(fmt, f["d"], f["h"], resid, resid, H, I, 1)
+            qmm.qmm_rmsnorm_gemv(fmt, f["lm"], f["x"], gamma, eps, f["logits"], V, H, 1)
+
+        res = {}
+        for name, fn, nb in (("plain", plain, plain_bytes), ("fused", fused, fused_bytes)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            res[name] = {"us": round(ms * 1e3, 2), "GBps": round(nb / (ms * 1e-3) / 1e9, 1), "bytes": int(nb)}
+        res["fused_over_plain_time"] = round(res["fused"]["us"] / res["plain"]["us"], 4)
+        out[si.FMT_NAMES[fmt]] = res
+    return out
+
+
+def expand_gemm(torch, qmm, si, reps=10):
+    """Expand-then-GEMM prefill (qmm_expand_f16 into a caller-owned fp16 buffer, then
+    the F16 qmm_gemm) against the fused LDS-decode GEMM, and the expansion's own HBM
+    rate (bytes = raw blocks read + 2 M K written).  Random weight bytes with the
+    scale bytes cleared of inf/NaN patterns: timing only."""
+    dev = torch.device("cuda")
+
+    def timed(fn, n=reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    out = []
+    for fmt in (si.FMT_Q8_0, si.FMT_Q4_0):
+        for (M, K) in ((14336, 4096), (4096, 14336)):
+            rb = qmm.qmm_row_bytes(fmt, K)
+            bb = 34 if fmt == si.FMT_Q8_0 else 18
+            W = torch.randint(0, 256, (M * rb,), dtype=torch.uint8, device=dev)
+            W.view(M * K // 32, bb)[:, 1] &= 0x3B  # scale exponent below the inf/NaN range
+            W16 = torch.empty((M, K), dtype=torch.float16, device=dev)
+            ms_e = timed(lambda: qmm.qmm_expand_f16(fmt, W, W16, M, K), 20)
+            row = {"fmt": si.FMT_NAMES[fmt], "M": M, "K": K, "expand_us": round(ms_e * 1e3, 2),
+                   "expand_GBps": round((M * rb + 2 * M * K) / (ms_e * 1e-3) / 1e9, 1), "T": []}
+            for T in (128, 2048, 4096):
+                X = torch.randn(T, K, device=dev).half()
+                Y = torch.empty((T, M), device=dev)
+                fl = 2.0 * T * M * K
+                ms_f = timed(lambda: qmm.qmm_gemm(fmt, W, X, Y, M, K, T))
+                ms_x = timed(lambda: (qmm.qmm_expand_f16(fmt, W, W16, M, K), qmm.qmm_gemm(1, W16, X, Y, M, K, T)))
+                row["T"].append({"T": T, "fused_TFLOPs": round(fl / (ms_f * 1e-3) / 1e12, 1),
+                                 "expand_then_gemm_TFLOPs": round(fl / (ms_x * 1e-3) / 1e12, 1)})
+            out.append(row)
+            del W, W16
+    return out
+
+
+def get_rows_bench(torch, qmm, si, reps=20):
+    """Quantised embedding gather from the Llama-3-8B token table (128256 x 4096):
+    bytes = n rows of raw blocks read + n x 4096 fp32 written."""
+    L = si.LLAMA3_8B
+    V, H = L["vocab"], L["hidden"]
+    dev = torch.device("cuda")
+    out = {}
+    for fmt in (si.FMT_Q8_0, si.FMT_Q4_0, si.FMT_F16):
+        rb = qmm.qmm_row_bytes(fmt, H)
+        W = torch.randint(0, 256, (V * rb,), dtype=torch.uint8, device=dev)
+        res = {}
+        for n in (1, 4096):
+            ids = torch.randint(0, V, (n,), dtype=torch.int32, device=dev)
+            o = torch.empty((n, H), device=dev)
+            for _ in range(3):
+                qmm.qmm_get_rows(fmt, W, ids, o, V, H, n)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                qmm.qmm_get_rows(fmt, W, ids, o, V, H, n)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            res[f"n{n}"] = {"us": round(ms * 1e3, 2), "GBps": round(n * (rb + 4 * H) / (ms * 1e-3) / 1e9, 1)}
+        out[si.FMT_NAMES[fmt]] = res
+        del W
+    return out
+
+
 def ceilings(torch):
     """Achievable ceilings measured with vendor code (never linked into qmm): a 2 GiB
     device-to-device copy (bytes read + bytes written per second) and fp16
@@ -439,6 +569,10 @@ def main():
         line["smollm2_135m_decode_step"] = smollm2_step(torch, qmm, si, max(10, args.steps))
     if not args.no_small_batch:
         line["small_batch_decode"] = small_batch(torch, qmm, si)
+    if not args.no_next:
+        line["fused_decode_step"] = fused_decode(torch, qmm, si, fmts, max(10, args.steps))
+        line["expand_then_gemm"] = expand_gemm(torch, qmm, si)
+        line["get_rows"] = get_rows_bench(torch, qmm, si)
     if not (args.no_prefill or args.no_small_batch):
         line["ceilings"] = ceilings(torch)
     if not args.no_cpu:
