@@ -10,12 +10,14 @@ Every function states the passage it follows.  Pages cited:
 * "EdgeRunner Core Architecture" (EdgeRunner): section 1.3 TensorStorage &
   TensorDataType (GGUF type ids, bytes per block), section 3.1 Quantization
   Format Summary, section 3.2 Q8_0 Layout, section 3.4 Weight Dequantization
-  Strategy (raw blocks used without materialising float weights), section 8
-  SwiGLU FFN.
+  Strategy (raw blocks used without materialising float weights; Tier 2 decode to
+  float16; Tier 3 embedding rows), section 6 RMSNorm, section 8 SwiGLU FFN,
+  sections 9.1 and 9.2 (norms and residual adds folded into the decode GEMVs).
 * "llama.cpp Metal (MPS) End-to-End Inference Path" (llama.cpp Metal): section
   3.2 MUL_MAT 3-way kernel selection (ne00 is the contiguous reduction length K,
-  ne11 the number of tokens).
+  ne11 the number of tokens) and Input embd; P8 GET_ROWS.
 * "alpaca.swift": Capabilities (F16, Q8_0, Q4_0 weights used in place),
+  Design (weights expanded to half precision for the prefill GEMM),
   Numerical validation (float64 reference, bit-exact dequantisation, the
   element-wise error bound 2^-10 * sum |x_k w_k| for the half-precision GEMM),
   Limitations (activations stay in floating point).
@@ -33,10 +35,12 @@ Readings of points the pages leave open (each also listed with the design notes)
   propagate.
 
 Parity pins (tests under tests/test_oracle.py): hand-computed blocks stored in
-tests/golden (decode and nibble order), all 65536 fp16 patterns against a manual
-sign/exponent/mantissa decode, exact rational brute force on tiny shapes,
-pack/unpack round trip, SiLU closed forms, and the soundness of the fused-output
-bound by perturbation.
+tests/golden (decode and nibble order; one block for the fp16 expansion's
+ties-to-even), all 65536 fp16 patterns against a manual sign/exponent/mantissa
+decode, exact rational brute force on tiny shapes, pack/unpack round trip, SiLU
+and RMSNorm closed forms, row gathers of golden blocks, the golden dots reached
+through the norm and residual references, and the soundness of the fused-output
+bounds by perturbation.
 """
 from __future__ import annotations
 
