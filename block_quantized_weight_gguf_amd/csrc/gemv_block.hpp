@@ -103,6 +103,167 @@ __device__ __forceinline__ void block_fma(const uint8_t* const (&buf)[RU], const
         for (int n = 0; n < NT; ++n) acc[u][n] = fmaf(d[u], bacc[u][n], acc[u][n]);
 }
 
+// ---- fp16-pair activations with packed dot products (streaming kernel) ----
+//
+// The streaming kernel keeps x in LDS as block floating point: each 32-value block
+// of a token is scaled by a power of two 2^s that brings its largest magnitude into
+// [2^14, 2^15), then rounded to fp16 (x~ = fp16(2^s x)).  That cannot overflow or
+// lose a block to underflow, and every element keeps a relative error <= 2^-11.
+// Codes enter v_dot2_f32_f16 as normal fp16 numbers built with one v_perm against a
+// constant byte (the instruction is accurate to about an fp32 ulp for normal
+// operands; it loses precision on subnormal ones):
+//   Q8_0: u = q + 128 (xor 0x80) as the low byte under 0x64: v = 1024 + u, and
+//         w = d (v - 1152);
+//   Q4_0: the nibble n in bits 4..7 under 0x3C: v = 1 + n/64, and
+//         w = 64 d (v - 1.125).
+// Both products v x~ are exact in fp32.  With
+//     p = sum_j v_j x~_j   and   c = sum_j v0 x~_j   (v0 = 1152 or 1.125),
+// accumulated by the same chain of dot2 steps in the same pair order, a block
+// contributes (d F) (p - c) 2^-s with F = 1 or 64.  Codes all equal to the offset
+// (q = 0, n = 8) therefore give exactly zero, and the cancellation costs at most
+// about 2^-24 * 16 * 2 * max(v0 / |v - v0|) ~ 3e-5 of sum |w x| (|v - v0| averages
+// 64 resp. 4/64), so |y - y_exact| <= (2^-11 + 4e-5) sum |w x|, inside the 2e-3 bound.
+// Per block the LDS copy holds 16 dwords of fp16 pairs in the order the codes are
+// unpacked (see stage_x16), then c and 2^-s, padded to XS16 dwords so that the
+// lanes' 16-byte reads at a stride of XS16 dwords hit distinct banks.
+constexpr int XS16 = 20;
+
+typedef _Float16 h2x_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2x_t as_h2x(uint32_t u) { return __builtin_bit_cast(h2x_t, u); }
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(as_h2x(a), as_h2x(b), c, false);
+}
+// Code pairs: bytes 0 and 2 (sel02) or 1 and 3 (sel13) of v as the low bytes of the
+// two 16-bit halves, under the high byte of k (v_perm_b32 of {k, v}).
+__device__ __forceinline__ uint32_t sel02(uint32_t v, uint32_t k) { return __builtin_amdgcn_perm(k, v, 0x07020400u); }
+__device__ __forceinline__ uint32_t sel13(uint32_t v, uint32_t k) { return __builtin_amdgcn_perm(k, v, 0x07030401u); }
+
+template <int FMT>
+struct DotCode {
+    static constexpr uint32_t K = FMT == 8 ? 0x64646464u : 0x3C3C3C3Cu;    // high bytes
+    static constexpr uint32_t V0 = FMT == 8 ? 0x64806480u : 0x3C803C80u;   // offset code pair
+    static constexpr float F = FMT == 8 ? 1.0f : 64.0f;
+};
+
+// v from another lane of the row, as selected by the DPP control CTRL (all lanes of
+// the 8-lane groups using it are active).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(lo))) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(hi))) << 16);
+}
+
+// Stage chunk c (0..7: values 4c..4c+3) of one block of one token.  Called by 8
+// consecutive lanes per block, all active, lane c of the group holding chunk c.
+// They agree on the block's scale with three DPP exchanges; stage_chain fills in
+// c once every block is written.  Pair order matches
+// the unpacking in block_dot:
+//   Q8_0: dword 2c holds (x[4c], x[4c+2]), dword 2c+1 holds (x[4c+1], x[4c+3]) --
+//         the lanes of sel02 / sel13 applied to code dword c;
+//   Q4_0: code dword i holds weights 4i..4i+3 (low nibbles) and 16+4i..16+4i+3
+//         (high nibbles); dwords 4i, 4i+1 pair the low ones, 4i+2, 4i+3 the high.
+template <int FMT>
+__device__ __forceinline__ void stage_x16(float4 v, int c, uint32_t* blk) {
+    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    // Max over the 8 lanes with DPP moves: swap neighbours, swap pairs (quad_perm),
+    // then mirror the two quads of the 8-lane half row.
+    m = fmaxf(m, dpp_f32<0xB1>(m));   // quad_perm [1, 0, 3, 2]
+    m = fmaxf(m, dpp_f32<0x4E>(m));   // quad_perm [2, 3, 0, 1]
+    m = fmaxf(m, dpp_f32<0x141>(m));  // row_half_mirror
+    const int e = static_cast<int>((__float_as_uint(m) >> 23) & 0xFFu) - 127;  // floor(log2 m); -127 for 0
+    const int se = min(126, 14 - e);                                            // >= -114 (m <= inf)
+    const float sc = __uint_as_float(static_cast<uint32_t>(se + 127) << 23);     // 2^se
+    const float inv = __uint_as_float(static_cast<uint32_t>(127 - se) << 23);    // 2^-se
+    const uint32_t w0 = pack_h2(v.x * sc, v.z * sc), w1 = pack_h2(v.y * sc, v.w * sc);
+    const int slot = (FMT == 8) ? 2 * c : 4 * (c & 3) + ((c >> 2) << 1);
+    *reinterpret_cast<uint2*>(blk + slot) = make_uint2(w0, w1);
+    if (c == 0) blk[17] = __float_as_uint(inv);
+}
+
+// After the staged pairs are visible: c of one block, the dot2 chain over its 16
+// dwords in slot order with every code equal to the offset code (block_dot's chain).
+template <int FMT>
+__device__ __forceinline__ void stage_chain(uint32_t* blk) {
+    float chain = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 w = *reinterpret_cast<const uint4*>(blk + 4 * i);
+        chain = dot2(DotCode<FMT>::V0, w.x, chain);
+        chain = dot2(DotCode<FMT>::V0, w.y, chain);
+        chain = dot2(DotCode<FMT>::V0, w.z, chain);
+        chain = dot2(DotCode<FMT>::V0, w.w, chain);
+    }
+    blk[16] = __float_as_uint(chain);
+}
+
+// One lane's block for RU row units and NT tokens with packed fp16 dot products
+// (xb[n]: the token's staged block, XS16 dwords).
+template <int FMT, int RU, int NT>
+__device__ __forceinline__ void block_dot(const uint8_t* const (&buf)[RU], const int (&off)[RU],
+                                          const uint32_t* const (&xb)[NT], float (&acc)[RU][NT]) {
+    constexpr int NDW = FMT == 8 ? 8 : 4;
+    constexpr uint32_t KB = DotCode<FMT>::K;
+    float p[RU][NT];
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) p[u][n] = 0.0f;
+    float d[RU];
+    uint32_t cw[RU][NDW];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        d[u] = half_bits_to_float(lds_read_u16(buf[u], off[u]));
+        lds_read_dwords<NDW>(buf[u], off[u] + 2, cw[u]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint4 xv[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) xv[n] = *reinterpret_cast<const uint4*>(xb[n] + 4 * i);
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            uint32_t a0, a1, a2, a3;
+            if constexpr (FMT == 8) {
+                const uint32_t t0 = cw[u][2 * i] ^ 0x80808080u, t1 = cw[u][2 * i + 1] ^ 0x80808080u;
+                a0 = sel02(t0, KB), a1 = sel13(t0, KB), a2 = sel02(t1, KB), a3 = sel13(t1, KB);
+            } else {
+                const uint32_t lo = (cw[u][i] << 4) & 0xF0F0F0F0u, hi = cw[u][i] & 0xF0F0F0F0u;
+                a0 = sel02(lo, KB), a1 = sel13(lo, KB), a2 = sel02(hi, KB), a3 = sel13(hi, KB);
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                float a = p[u][n];
+                a = dot2(a0, xv[n].x, a);
+                a = dot2(a1, xv[n].y, a);
+                a = dot2(a2, xv[n].z, a);
+                a = dot2(a3, xv[n].w, a);
+                p[u][n] = a;
+            }
+        }
+    }
+    float cs[NT], inv[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const uint2 t = *reinterpret_cast<const uint2*>(xb[n] + 16);
+        cs[n] = __uint_as_float(t.x);
+        inv[n] = __uint_as_float(t.y);
+    }
+    // ((p - c) * d F) * 2^-s: each factor stays within the block's own contribution,
+    // so nothing overflows unless that contribution does.
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        const float dF = d[u] * DotCode<FMT>::F;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[u][n] = fmaf((p[u][n] - cs[n]) * dF, inv[n], acc[u][n]);
+    }
+}
+
+// ---- end of fp16-pair helpers ----
+
 // Per-token partial sums of squares of a workgroup -> LDS.  Each wave reduces its
 // lanes' values; lane 0 writes red[wave * NT + n].  A barrier must separate this
 // from norm_scales.

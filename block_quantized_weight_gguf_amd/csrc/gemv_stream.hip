@@ -4,10 +4,11 @@
 // Architecture", section 3.4 Tier 1 and section 15 item 2: the raw blocks are the
 // only large operand), so this kernel is organised to keep HBM busy with as few
 // instructions per byte as possible:
-//   * One 8-wave workgroup per CU (LDS-limited).  x (all K, NT tokens) is copied
-//     into LDS once, each 32-float block padded to 36 floats so that the lanes'
-//     16-byte reads hit distinct banks; after that single barrier the 8 waves
-//     never synchronise again.
+//   * One workgroup per CU (LDS-limited).  x (all K, NT tokens) is copied into LDS
+//     once, as block-scaled fp16 pairs (stage_x16); after that single barrier the
+//     waves never synchronise again.  Dot products run on v_dot2_f32_f16 with the
+//     codes as fp16 subnormals (block_dot), about half the VALU work of a
+//     convert and an FMA per weight.
 //   * Each wave walks a list of tasks.  A task is R rows (2R row units when gated:
 //     R gate rows and the same R up rows) x one K slice of 64*BPL blocks (BPL = 1
 //     for Q8_0, 2 for Q4_0, so a row slice is ~2.2 KB either way).  Each row
@@ -63,12 +64,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
     constexpr int BB = G::BB, BPL = G::BPL, SLICE = G::SLICE, CPR = G::CPR, LPR = G::LPR, ROWBUF = G::ROWBUF;
     constexpr int RU = GATED ? 2 * R : R;
     extern __shared__ __align__(16) uint8_t smem[];
-    float* xs = reinterpret_cast<float*>(smem);
+    uint32_t* xs = reinterpret_cast<uint32_t*>(smem);
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int nb = K / kQK;
-    const int xstride = nb * XS_STRIDE;  // floats per token in LDS
+    const int xstride = nb * XS16;  // dwords per token in LDS
     const int64_t rb = static_cast<int64_t>(nb) * BB;
 
     uint8_t* my = smem + xs_bytes + wave * (RU * ROWBUF);
@@ -121,25 +122,47 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
         if (q < ntask) issue(q, regs[q]);
 
     // x -> LDS once: NT tokens x nb blocks, 8 float4 per block (EP_NORM: gamma .* x,
-    // with the sum of squares of x gathered on the way).
+    // with the sum of squares of x gathered on the way).  Lanes 8b..8b+7 of a round
+    // hold the 8 chunks of one block (nb * 8 is a multiple of 8).
     float ss[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) ss[n] = 0.0f;
-    for (int j = threadIdx.x; j < nb * 8; j += WAVES * kWave) {
-        float4 gm = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-        if constexpr (EP == EP_NORM) gm = *reinterpret_cast<const float4*>(epi.gamma + 4 * static_cast<int64_t>(j));
+    // SU rounds of the workgroup are loaded before any is converted, so their
+    // latencies overlap (one pass covers K <= 16384 with 16 waves).
+    constexpr int SU = 4;
+    for (int j0 = threadIdx.x; j0 < nb * 8; j0 += SU * WAVES * kWave) {
+        float4 xv[SU][NT], gv[SU];
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            float4 v = *reinterpret_cast<const float4*>(x + n * ldx + 4 * static_cast<int64_t>(j));
-            if constexpr (EP == EP_NORM) {
-                ss[n] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss[n]))));
-                v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
+        for (int r = 0; r < SU; ++r) {
+            const int j = j0 + r * WAVES * kWave;
+            if (j < nb * 8) {
+                if constexpr (EP == EP_NORM) gv[r] = *reinterpret_cast<const float4*>(epi.gamma + 4 * static_cast<int64_t>(j));
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+                    xv[r][n] = *reinterpret_cast<const float4*>(x + n * ldx + 4 * static_cast<int64_t>(j));
             }
-            *reinterpret_cast<float4*>(xs + n * xstride + (j >> 3) * XS_STRIDE + 4 * (j & 7)) = v;
+        }
+#pragma unroll
+        for (int r = 0; r < SU; ++r) {
+            const int j = j0 + r * WAVES * kWave;
+            if (j < nb * 8) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    float4 v = xv[r][n];
+                    if constexpr (EP == EP_NORM) {
+                        const float4 gm = gv[r];
+                        ss[n] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss[n]))));
+                        v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
+                    }
+                    stage_x16<FMT>(v, j & 7, xs + n * xstride + (j >> 3) * XS16);
+                }
+            }
         }
     }
     float* red = reinterpret_cast<float*>(smem + xs_bytes + WAVES * (RU * ROWBUF));
     if constexpr (EP == EP_NORM) norm_partials<NT>(ss, red, wave, lane);
+    __syncthreads();
+    for (int b = threadIdx.x; b < NT * nb; b += WAVES * kWave) stage_chain<FMT>(xs + b * XS16);
     __syncthreads();
     float scale = 1.0f;
     if constexpr (EP == EP_NORM) scale = norm_scale<NT>(red, WAVES, reduced_token<RU, NT>(lane), K, epi.eps);
@@ -181,10 +204,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
                 int off[RU];
 #pragma unroll
                 for (int u = 0; u < RU; ++u) off[u] = sh[u] + blk * BB;
-                const float* xb[NT];
+                const uint32_t* xb[NT];
 #pragma unroll
-                for (int n = 0; n < NT; ++n) xb[n] = xs + n * xstride + (s0 + blk) * XS_STRIDE;
-                block_fma<FMT, RU, NT>(buf, off, xb, acc);
+                for (int n = 0; n < NT; ++n) xb[n] = xs + n * xstride + (s0 + blk) * XS16;
+                block_dot<FMT, RU, NT>(buf, off, xb, acc);
             }
         }
         if (s == ns - 1) {
@@ -214,7 +237,7 @@ static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y,
         if (M < 2) return 0;
         M -= 1;  // every chunk of the first M - 1 rows ends at most 15 bytes into the last row
     }
-    const int64_t xs_bytes = ((NT * nb * XS_STRIDE * 4) + 15) / 16 * 16;
+    const int64_t xs_bytes = ((NT * nb * XS16 * 4) + 15) / 16 * 16;
     const int64_t lds = xs_bytes + static_cast<int64_t>(WAVES) * RU * G::ROWBUF + (EP == EP_NORM ? WAVES * NT * 4 : 0);
     constexpr int64_t kMaxLds = 160 * 1024;
     if (lds > kMaxLds) return 0;

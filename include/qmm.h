@@ -145,8 +145,14 @@ int qmm_expand_f16(int fmt, const void* W, void* out, int64_t M, int64_t K, void
  * and reuses it N times.  ("EdgeRunner Core Architecture", section 2.1 fused
  * Q8_0 dequant + GEMV pipelines; "llama.cpp Metal ...", section 3.2 and P9:
  * per-format mat-vec kernels for one token and a batched mat-vec for 2..8 tokens.)
- * The variant is chosen from (fmt, M, K, N) as qmm_gemv_choose reports.  The MFMA
- * variant, used only for larger N, rounds x to fp16 inside the kernel.
+ * The variant is chosen from (fmt, M, K, N) as qmm_gemv_choose reports.
+ * Precision: accumulation is fp32 everywhere.  For Q8_0 / Q4_0 the register-decode
+ * variant holds x in block floating point (each 32-value block scaled by a power
+ * of two, then rounded to fp16) and forms the products with packed fp16 dot
+ * products; F16 weights and rows it leaves to its fallback use fp32 x.  The MFMA
+ * variant, used for larger N, rounds x to fp16 inside the kernel.  Either way
+ * |y - y_exact| <= about 2^-11 sum_k |W[m][k] x[n][k]|, and x = e_k returns the
+ * column W[:, k] exactly on the register-decode variant.
  * Fused QKV is this call on the row-concatenation [Wq; Wk; Wv] (M = q + 2 kv).
  */
 int qmm_gemv(int fmt, const void* W, const float* x, float* y,
