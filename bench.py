@@ -522,7 +522,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "Llama-3-8B-shaped single-token decode projections (QKV 6144x4096, O 4096x4096, "
                                "gate+up 2x14336x4096 + SwiGLU, down 4096x14336, LM head 128256x4096), "
@@ -530,7 +530,7 @@ def main():
                    "formats": ["Q8_0", "Q4_0"], "tokens": 1, "step_bytes": int(step_bytes),
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm",
-                     "kernel": ("gemv_stream_kernel<8, 1, 2, false, 16, 1> (" + dom + ")") if dom == "gemv_Q8_0:lm_head" else dom,
+                     "kernel": ("gemv_stream_kernel<8, 1, 2, false, 16, 1, 0> (" + dom + ")") if dom == "gemv_Q8_0:lm_head" else dom,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for("gemv_stream.hip", dom),
