@@ -65,7 +65,7 @@ constexpr int GT_GROUP_M = 4;
 // its tile and stores the raw partial sums to Y[split][T][Mo] (Mo = M, or 2 M for the
 // gated instance: gate sums in columns 0..M-1, up sums in M..2M-1); splitk_reduce
 // adds the splits in order and applies the epilogue.
-template <int FMT, bool GATED, bool XF32, bool SPLIT>
+template <int FMT, bool GATED, bool XF32, bool SPLIT, int BN>
 __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __restrict__ Wg,
                                                                 const uint8_t* __restrict__ Wu,
                                                                 const void* __restrict__ Xv,
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     // from the other stage.
     constexpr int WPER = (WINST + GT_WAVES - 1) / GT_WAVES;
     constexpr int KPS = G::KPS;
-    constexpr int XBYTES = GT_BN * GT_BK * 2;
+    constexpr int XBYTES = BN * GT_BK * 2;
     constexpr int XINST = XBYTES / 1024 / GT_WAVES;          // token DMA instructions per wave and step
     constexpr int XE = XF32 ? 4 : 2;          // token element bytes
     static_assert(WINST % 2 == 0, "gate / up halves must split on instruction boundaries");
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     // room for their staging registers.
     constexpr int GT_WN = XF32 ? 2 : 1;
     constexpr int GT_RW = GT_BM / (GT_WAVES / GT_WN);  // weight rows per wave
-    constexpr int GT_TW = GT_BN / GT_WN;               // tokens per wave
+    constexpr int GT_TW = BN / GT_WN;                  // tokens per wave
     constexpr int GT_NI = GT_RW / 16;
     constexpr int GT_NJ = GT_TW / 16;
 
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     // ---- tile selection: contiguous run per XCD, grouped by GT_GROUP_M weight tiles
     const int rows_per_tile = GATED ? GT_BM / 2 : GT_BM;
     const int nMt = (M + rows_per_tile - 1) / rows_per_tile;
-    const int nTt = (T + GT_BN - 1) / GT_BN;
+    const int nTt = (T + BN - 1) / BN;
     const int ntiles = nMt * nTt;
     const int nunits = ntiles * (SPLIT ? nsplit : 1);
     const int per_xcd = (nunits + 7) / 8;
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     const int mt = first_m + in_group % gm;
     const int tt = in_group / gm;
     const int m0 = mt * rows_per_tile;
-    const int t0 = tt * GT_BN;
+    const int t0 = tt * BN;
 
     // ---- DMA sources: a buffer resource per operand tile (uniform) plus a 32-bit
     // lane offset fixed for the whole K loop; the K position goes in the scalar
@@ -466,13 +466,13 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P
     }
 }
 
-template <int FMT, bool GATED, bool XF32, bool SPLIT>
+template <int FMT, bool GATED, bool XF32, bool SPLIT, int BN>
 static void launch_tile_t(const void* W, const void* Wu, const void* X, float* Y, int64_t M, int64_t K, int64_t T,
                           int nsplit, int ksteps, hipStream_t s) {
     const int64_t rows_per_tile = GATED ? GT_BM / 2 : GT_BM;
-    const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + GT_BN - 1) / GT_BN);
+    const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + BN - 1) / BN);
     const int64_t grid = (ntiles * (SPLIT ? nsplit : 1) + 7) / 8 * 8;  // whole runs per XCD
-    hipLaunchKernelGGL((gemm_tile_kernel<FMT, GATED, XF32, SPLIT>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((gemm_tile_kernel<FMT, GATED, XF32, SPLIT, BN>), dim3(static_cast<unsigned>(grid)),
                        dim3(GT_THREADS), 0, s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), X, Y,
                        static_cast<int>(M), static_cast<int>(K), static_cast<int>(T),
                        static_cast<int>(M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0), nsplit, ksteps);
@@ -536,7 +536,12 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
     if (K > (int64_t{1} << 20)) return false;
     const bool gated = Wu != nullptr;
     const int64_t rows_per_tile = gated ? GT_BM / 2 : GT_BM;
-    const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + GT_BN - 1) / GT_BN);
+#ifndef QMM_NARROW_T
+#define QMM_NARROW_T 128
+#endif
+    const bool narrow = T <= QMM_NARROW_T;
+    const int64_t bn = narrow ? 128 : GT_BN;
+    const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + bn - 1) / bn);
     if (ntiles > (int64_t{1} << 30)) return false;
 
     // Split K when the tiles cannot fill the 256 CUs: at most one wave of workgroups,
@@ -558,13 +563,16 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
             ksteps = static_cast<int>(nsteps);
         }
     }
+#define QMM_TILE_BN(F, G, XF, SP, OUT)                                                                   \
+    if (narrow) launch_tile_t<F, G, XF, SP, 128>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);               \
+    else launch_tile_t<F, G, XF, SP, GT_BN>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);
 #define QMM_TILE_CASE(F, SP, OUT)                                                                        \
     if (gated) {                                                                                        \
-        if (x_is_f32) launch_tile_t<F, true, true, SP>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);       \
-        else launch_tile_t<F, true, false, SP>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);               \
+        if (x_is_f32) { QMM_TILE_BN(F, true, true, SP, OUT) }                                          \
+        else { QMM_TILE_BN(F, true, false, SP, OUT) }                                                  \
     } else {                                                                                            \
-        if (x_is_f32) launch_tile_t<F, false, true, SP>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);      \
-        else launch_tile_t<F, false, false, SP>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);              \
+        if (x_is_f32) { QMM_TILE_BN(F, false, true, SP, OUT) }                                         \
+        else { QMM_TILE_BN(F, false, false, SP, OUT) }                                                 \
     }
     if (P) {
         if (fmt == 8) { QMM_TILE_CASE(8, true, P) }
@@ -578,6 +586,7 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
         else { QMM_TILE_CASE(1, false, Y) }
     }
 #undef QMM_TILE_CASE
+#undef QMM_TILE_BN
     return true;
 }
 

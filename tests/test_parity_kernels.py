@@ -220,7 +220,7 @@ def test_gate_up_concatenated_buffer():
 # ------------------------------------------------------------------ GEMM
 @pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
 @pytest.mark.parametrize("M,K,T", [(1, 32, 1), (300, 256, 40), (256, 4096, 256), (513, 96, 300), (64, 4160, 17),
-                                   (1000, 576, 513)])
+                                   (1000, 576, 513), (520, 1024, 128), (520, 1024, 129)])
 def test_gemm(fmt, M, K, T):
     seed = 3000 + M + K + T
     mode = "gemm_wide" if T % 2 else "uniform"
@@ -233,6 +233,21 @@ def test_gemm(fmt, M, K, T):
     assert guard_intact(buf, T * M)
     y_ref, S = oracle.matmul_ref(fmt, raw, X, M, K)
     check_linear(buf[:T * M].cpu().numpy().reshape(T, M), y_ref, S, f"gemm fmt={fmt} M={M} K={K} T={T}")
+
+
+# The MFMA GEMV variant above 32 tokens runs the tiled GEMM on fp32 x (converted to
+# fp16 while staged); up to 128 tokens with 128-token tiles, beyond with 256.
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("M,K,N", [(300, 1024, 40), (257, 2048, 128), (130, 1024, 150)])
+def test_gemv_mfma_tile_fp32_x(fmt, M, K, N):
+    seed = 3300 + M + K + N
+    raw = si.weights(fmt, M, K, seed, scale_mode="gemm_wide", q8_low=-128)
+    x = si.activations(N, K, seed + 1)
+    announce(f"gemv mfma (tile, fp32 x) fmt={fmt} M={M} K={K} N={N}")
+    y = qmm.gemv(fmt, dev(raw), dev(x), M, K, variant=MFMA)
+    torch.cuda.synchronize()
+    y_ref, S = oracle.matmul_ref(fmt, raw, x.astype(np.float16), M, K)
+    check_linear(y.cpu().numpy(), y_ref, S, f"gemv mfma tile fmt={fmt} N={N}")
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
