@@ -27,6 +27,10 @@
 //     code byte c becomes the half 1024 + c via v_perm with 0x64 bytes, v_pk_add_f16
 //     removes the offset exactly and v_pk_mul_f16 by the fp16 scale gives fp16(d*q)
 //     with a single rounding.  F16 weights use the token-tile layout.
+//   * Inside a K step the token fragments are read one group ahead of the MFMAs
+//     that use them, in scheduling regions of their own (the compiler would
+//     otherwise read each just before its MFMA and expose the LDS latency), after
+//     the LDS words of the A fragments decoded in the same group.
 //   * Pipeline: one barrier per K step.  After it, the DMA of the next token stage
 //     (and, every second step, of the next weight stage) is issued into the buffer
 //     that every wave has finished reading, then the step's fragments are read and
@@ -262,21 +266,72 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
 #pragma unroll
         for (int i = i0; i < i0 + NH; ++i) a[i] = frag_a(Wc, i, b, sh);
     };
-    // 32 MFMAs of sub-step ks with fragments a, in two scheduling regions of 16; the
-    // decode of the next fragments (nxt, block nb; skipped when nb < 0) is split over
-    // them, so that its temporaries stay small and it overlaps the MFMAs.
-    auto mfma_sub = [&](const half8_t (&a)[GT_NI], const QMM_L3 uint8_t* Xc, int ks, half8_t (&nxt)[GT_NI], int nb,
-                        const QMM_L3 uint8_t* Wc, int sh) {
+    // The MFMAs of both sub-steps of a K step.  Token fragments are read in groups of
+    // NJG, one group ahead of the MFMAs that use them: each group's reads sit in their
+    // own scheduling region, after the LDS reads of the A fragments decoded in that
+    // group, so that waiting for the decode's words never waits for the token reads
+    // (LDS waits count in issue order) and the LDS latency of a group is covered by the
+    // previous group's MFMAs.  The decode of the next A fragments (sub-step 0: a1 from
+    // block nb0; sub-step 1: a0 of the next step from block nb1; skipped when negative)
+    // is spread over the first two groups of each sub-step.
+    using RawT = std::conditional_t<FMT == 1, half8_t, RawA>;
+    auto load_a = [&](const QMM_L3 uint8_t* Wsrc, int i, int b, int sh) -> RawT {
+        const int rowb = arow(i) * WROW;
+        if constexpr (FMT == 1) {
+            (void)sh;
+            return *reinterpret_cast<const QMM_L3 half8_t*>(Wsrc + rowb + (((4 * b + q4) ^ (lane & 7)) << 4));
+        } else {
+            return frag_load<FMT>(Wsrc + rowb, sh + BB * b, q4);
+        }
+    };
+    auto dec_a = [&](const RawT& r, int b, int sh) -> half8_t {
+        if constexpr (FMT == 1) return r;
+        else return frag_decode<FMT>(r, sh + BB * b, q4);
+    };
+    // Group size: as many fragments read ahead as the registers allow (the 256-token
+    // tile holds 128 accumulators; gated and fp32-token instances need more besides).
+    constexpr int NJG_MAX = BN == 128 ? 4 : (GATED || XF32) ? 1 : 2;
+    constexpr int NJG = (GT_NJ / 2 < NJG_MAX) ? GT_NJ / 2 : NJG_MAX;
+    constexpr int NG = GT_NJ / NJG;
+    static_assert(GT_NJ % NJG == 0 && NG >= 2, "token fragment groups");
+    auto mfma_step = [&](half8_t (&a0r)[GT_NI], half8_t (&a1r)[GT_NI], const QMM_L3 uint8_t* Xc, int nb0, int nb1,
+                         const QMM_L3 uint8_t* Wc, int sh) {
+        half8_t bf[2][NJG];
+        auto readg = [&](half8_t (&b)[NJG], int q) {
+            const int ks = q / NG, g = q % NG;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+            for (int jj = 0; jj < NJG; ++jj)
+                b[jj] = *reinterpret_cast<const QMM_L3 half8_t*>(Xc + xoff[ks] + (NJG * g + jj) * 16 * 128);
+        };
+        readg(bf[0], 0);
+#pragma unroll
+        for (int q = 0; q < 2 * NG; ++q) {
+            const int ks = q / NG, g = q % NG;
+            const int nbq = ks == 0 ? nb0 : nb1;
+            const bool dec = g < 2 && nbq >= 0;
             __builtin_amdgcn_sched_barrier(0);
-            if (nb >= 0) decode2(nxt, NH * h, Wc, nb, sh);
+            RawT raw[NH];
+            if (dec) {
 #pragma unroll
-            for (int j = (GT_NJ / 2) * h; j < (GT_NJ / 2) * (h + 1); ++j) {
-                const half8_t bf = *reinterpret_cast<const QMM_L3 half8_t*>(Xc + xoff[ks] + j * 16 * 128);
+                for (int i = 0; i < NH; ++i) raw[i] = load_a(Wc, NH * g + i, nbq, sh);
+            }
+            if (q + 1 < 2 * NG) readg(bf[(q + 1) & 1], q + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (dec) {
 #pragma unroll
-                for (int i = 0; i < GT_NI; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bf, acc[i][j], 0, 0, 0);
+                for (int i = 0; i < NH; ++i) {
+                    if (ks == 0) a1r[NH * g + i] = dec_a(raw[i], nbq, sh);
+                    else a0r[NH * g + i] = dec_a(raw[i], nbq, sh);
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < NJG; ++jj) {
+#pragma unroll
+                for (int i = 0; i < GT_NI; ++i) {
+                    const half8_t ai = ks == 0 ? a0r[i] : a1r[i];
+                    acc[i][NJG * g + jj] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(ai, bf[q & 1][jj], acc[i][NJG * g + jj], 0, 0, 0);
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -320,8 +375,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
             decode2(a0, 0, Wc, 2 * KK, SH);
             decode2(a0, NH, Wc, 2 * KK, SH);
         }
-        mfma_sub(a0, Xc, 0, a1, 2 * KK + 1, Wc, SH);
-        mfma_sub(a1, Xc, 1, a0, (PRE && KK == 0) ? 2 : -1, Wc, SH);
+        mfma_step(a0, a1, Xc, 2 * KK + 1, (PRE && KK == 0) ? 2 : -1, Wc, SH);
         if constexpr (XF32) issue_x(Xn, min(k + 1, kend - 1));
         __builtin_amdgcn_sched_barrier(0);
     };

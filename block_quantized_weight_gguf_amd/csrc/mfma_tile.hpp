@@ -105,23 +105,44 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 // LDS: the 8 weights 8 q4 .. 8 q4 + 7 (lane l: q4 = l / 16) of the block that starts
 // `o` bytes into the row (o even; blocks are 2-byte aligned).  Q4_0 fragments 0, 1
 // take the low nibbles of code bytes 0..7 / 8..15, fragments 2, 3 the high nibbles.
+// The LDS words frag_decode needs: the scale dword and the (unaligned) code dwords.
+struct RawA {
+    uint32_t d, w0, w1, w2;
+};
+
 template <int FMT>
-__device__ __forceinline__ half8_t frag_raw(const QMM_L3 uint8_t* row, int o, int q4) {
+__device__ __forceinline__ RawA frag_load(const QMM_L3 uint8_t* row, int o, int q4) {
     static_assert(FMT == 8 || FMT == 2, "block formats only");
     const QMM_L3 uint32_t* dw = reinterpret_cast<const QMM_L3 uint32_t*>(row);
-    uint32_t d, c0, c1;
     const int cb = (FMT == 8) ? 8 * q4 : 8 * (q4 & 1);  // code byte offset in the block
+    RawA r;
     if ((o & 3) == 0) {
-        d = dw[o >> 2] & 0xFFFFu;
+        r.d = dw[o >> 2];
         const int base = (o + cb) >> 2;  // codes start 2 bytes into dword `base`
-        const uint32_t w0 = dw[base], w1 = dw[base + 1], w2 = dw[base + 2];
-        c0 = align_bytes(w1, w0, 2);
-        c1 = align_bytes(w2, w1, 2);
+        r.w0 = dw[base];
+        r.w1 = dw[base + 1];
+        r.w2 = dw[base + 2];
     } else {
-        d = dw[(o - 2) >> 2] >> 16;
+        r.d = dw[(o - 2) >> 2];
         const int base = (o + 2 + cb) >> 2;
-        c0 = dw[base];
-        c1 = dw[base + 1];
+        r.w0 = dw[base];
+        r.w1 = dw[base + 1];
+        r.w2 = 0;
+    }
+    return r;
+}
+
+template <int FMT>
+__device__ __forceinline__ half8_t frag_decode(const RawA& r, int o, int q4) {
+    uint32_t d, c0, c1;
+    if ((o & 3) == 0) {
+        d = r.d & 0xFFFFu;
+        c0 = align_bytes(r.w1, r.w0, 2);
+        c1 = align_bytes(r.w2, r.w1, 2);
+    } else {
+        d = r.d >> 16;
+        c0 = r.w0;
+        c1 = r.w1;
     }
     const half2_t d2 = bits_h2(d | (d << 16));
     uint32_t r0, r1, r2, r3;
@@ -134,6 +155,11 @@ __device__ __forceinline__ half8_t frag_raw(const QMM_L3 uint8_t* row, int o, in
         q4_4((c1 >> s4) & 0x0F0F0F0Fu, d2, r2, r3);
     }
     return __builtin_bit_cast(half8_t, u32x4_t{r0, r1, r2, r3});
+}
+
+template <int FMT>
+__device__ __forceinline__ half8_t frag_raw(const QMM_L3 uint8_t* row, int o, int q4) {
+    return frag_decode<FMT>(frag_load<FMT>(row, o, q4), o, q4);
 }
 
 }  // namespace qmm
