@@ -242,6 +242,8 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     // fragments are gate rows (GT_RW / 2) wm + 16 i + l % 16, the second half the up
     // rows of the same outputs.
     constexpr int NH = GT_NI / 2;
+    constexpr int ND = (GT_NI + 1) / 2;   // A fragments decoded per decode group
+    constexpr int NDG = GT_NI / ND;       // decode groups per sub-step (1 or 2)
     auto arow = [&](int i) -> int {
         if constexpr (GATED) return (i < NH ? (GT_RW / 2) * wm + 16 * i : 128 + (GT_RW / 2) * wm + 16 * (i - NH)) + (lane & 15);
         else return GT_RW * wm + 16 * i + (lane & 15);
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     // Decode fragments i0 .. i0 + NH - 1 of block b into a.
     auto decode2 = [&](half8_t (&a)[GT_NI], int i0, const QMM_L3 uint8_t* Wc, int b, int sh) {
 #pragma unroll
-        for (int i = i0; i < i0 + NH; ++i) a[i] = frag_a(Wc, i, b, sh);
+        for (int i = i0; i < i0 + ND; ++i) a[i] = frag_a(Wc, i, b, sh);
     };
     // The MFMAs of both sub-steps of a K step.  Token fragments are read in groups of
     // NJG, one group ahead of the MFMAs that use them: each group's reads sit in their
@@ -308,20 +310,20 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         for (int q = 0; q < 2 * NG; ++q) {
             const int ks = q / NG, g = q % NG;
             const int nbq = ks == 0 ? nb0 : nb1;
-            const bool dec = g < 2 && nbq >= 0;
+            const bool dec = g < NDG && nbq >= 0;
             __builtin_amdgcn_sched_barrier(0);
-            RawT raw[NH];
+            RawT raw[ND];
             if (dec) {
 #pragma unroll
-                for (int i = 0; i < NH; ++i) raw[i] = load_a(Wc, NH * g + i, nbq, sh);
+                for (int i = 0; i < ND; ++i) raw[i] = load_a(Wc, ND * g + i, nbq, sh);
             }
             if (q + 1 < 2 * NG) readg(bf[(q + 1) & 1], q + 1);
             __builtin_amdgcn_sched_barrier(0);
             if (dec) {
 #pragma unroll
-                for (int i = 0; i < NH; ++i) {
-                    if (ks == 0) a1r[NH * g + i] = dec_a(raw[i], nbq, sh);
-                    else a0r[NH * g + i] = dec_a(raw[i], nbq, sh);
+                for (int i = 0; i < ND; ++i) {
+                    if (ks == 0) a1r[ND * g + i] = dec_a(raw[i], nbq, sh);
+                    else a0r[ND * g + i] = dec_a(raw[i], nbq, sh);
                 }
             }
 #pragma unroll
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         constexpr bool PRE = KPS == 2 && !XF32;
         if constexpr (!(PRE && KK == 1)) {
             decode2(a0, 0, Wc, 2 * KK, SH);
-            decode2(a0, NH, Wc, 2 * KK, SH);
+            if constexpr (NDG > 1) decode2(a0, ND, Wc, 2 * KK, SH);
         }
         mfma_step(a0, a1, Xc, 2 * KK + 1, (PRE && KK == 0) ? 2 : -1, Wc, SH);
         if constexpr (XF32) issue_x(Xn, min(k + 1, kend - 1));
