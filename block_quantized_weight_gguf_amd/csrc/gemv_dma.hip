@@ -1,0 +1,388 @@
+// DMA-fed streaming decode GEMV for the block formats (Q8_0, Q4_0) with 16-byte
+// aligned rows (K % 256 == 0), a few tokens per pass.
+//
+// Single-token decode is bound by the weight stream ("EdgeRunner Core
+// Architecture", section 3.4 Tier 1 and section 15 item 2: the raw blocks are the
+// only large operand).  Keeping HBM busy takes tens of KB of reads in flight per
+// CU.  Here the weights never pass through VGPRs: each wave owns a private ring of
+// S LDS slots, and every task's raw bytes go straight from HBM into a slot by
+// buffer->LDS DMA, S - 1 tasks ahead of the one being computed.
+//   * One workgroup per CU (LDS-limited).  x (all K, NT tokens) is staged into LDS
+//     once as block-scaled fp16 pairs, as in the register-staged streaming kernel;
+//     after that the waves never synchronise again.
+//   * A task is R rows (2R row units when gated: R gate rows and the same R up
+//     rows) x one K slice of 64 * BPL blocks (BPL = 1 for Q8_0, 2 for Q4_0: 2176
+//     and 2304 bytes, both whole 16-byte chunks because rows are 16-byte aligned).
+//     A row unit's slice moves with three wave-wide DMA instructions (two of
+//     16 bytes per lane, one of 4 bytes per lane: 2304 bytes).  Each uses a
+//     buffer resource that covers exactly that slice, so lanes past its end (and
+//     tasks past the end of the list, and rows past M) read zeros without touching
+//     memory; every task therefore issues the same number of DMA instructions and
+//     the waits are compile-time constants.
+//   * The ring slots are separate LDS arrays and the loop is unrolled over them,
+//     so the compiler can tell the slot being read from the DMA still in flight
+//     into the others.
+//   * Lane l decodes block l (and l + 64) of the slice for every row unit with the
+//     packed fp16 dot products of block_dot; partial sums stay in registers across
+//     a row group's slices and are reduced across the wave once.
+#include "gemv_block.hpp"
+#include "dma.hpp"
+#include "qmm_internal.hpp"
+
+namespace qmm {
+
+constexpr int DG_SLOT = 2304;  // bytes per row unit and slot: 2 x 1024 (16-byte DMA) + 256 (4-byte DMA)
+constexpr int DG_NI = 3;       // DMA instructions per row unit and task
+constexpr int DG_PAD = 16;     // slack after each slot array (block reads may touch 4 bytes past a slice)
+constexpr int DG_GMAX = 4;     // EP_RES: row groups per wave whose residuals are read before the loop
+
+template <int FMT>
+struct DmaGeom {
+    static constexpr int BB = Fmt<FMT>::BB;
+    static constexpr int BPL = (FMT == 2) ? 2 : 1;  // blocks per lane per row slice
+    static constexpr int SLICE = kWave * BPL;       // blocks per K slice
+    static_assert(SLICE * BB <= DG_SLOT, "slice must fit a slot");
+    static_assert((8 * BB) % 16 == 0, "8-block multiples are whole 16-byte chunks");
+};
+
+// LDS of one instance: S ring stages of WAVES * RU slots, the norm partials, and
+// XCAP bytes left for x (NT tokens x K / 32 blocks x XS16 dwords).
+template <int NT, int RU, int WAVES, int S>
+struct DmaLds {
+    static constexpr int kMax = 160 * 1024;
+    static constexpr int STAGE = WAVES * RU * DG_SLOT + DG_PAD;
+    static constexpr int RING = 2 * STAGE + (S > 2 ? STAGE : 16) + (S > 3 ? STAGE : 16);
+    static constexpr int XCAP = (kMax - RING - WAVES * NT * 4) / 16 * 16;
+    static_assert(XCAP >= 16 * XS16 * 4, "room for x");
+};
+
+// Cursor over a wave's task list: task (gi, s) is slice s of the wave's gi-th row group.
+struct TaskCursor {
+    int gi, s;
+    __device__ __forceinline__ void next(int ns) {
+        if (++s == ns) {
+            s = 0;
+            ++gi;
+        }
+    }
+};
+
+// Reduce the RU x NT per-lane sums of a wave and store them (reduce_store's
+// transposing reduction); `resv` is the residual of the element this lane stores
+// (EP_RES), read before the loop.
+template <int R, int RU, int NT, bool GATED, int EP>
+__device__ __forceinline__ void dma_reduce_store(float (&acc)[RU][NT], int lane, int row0, int M, float* y,
+                                                 int64_t ldy, float scale, float resv) {
+    constexpr int NTP = (NT == 3) ? 4 : NT;
+    constexpr int V = RU * NTP;
+    float v[V];
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int n = 0; n < NTP; ++n) v[u * NTP + n] = (n < NT) ? acc[u][n < NT ? n : 0] : 0.0f;
+    wave_reduce_transpose<V>(v, lane);
+    constexpr int LPI = kWave / V;
+    const int idx = lane / LPI;
+    const bool holder = (lane % LPI) == 0;
+    const int u = idx / NTP;
+    const int n = idx - u * NTP;
+    const int r = row0 + u;
+    if constexpr (!GATED) {
+        if (holder && n < NT && r < M) {
+            float val = v[0];
+            if constexpr (EP == EP_NORM) val *= scale;
+            if constexpr (EP == EP_RES) val += resv;
+            y[n * ldy + r] = val;
+        }
+    } else {
+        float upv = __shfl(v[0], (lane + R * NTP * LPI) & (kWave - 1), kWave);
+        float gv = v[0];
+        if constexpr (EP == EP_NORM) {
+            gv *= scale;
+            upv *= scale;
+        }
+        if (holder && u < R && n < NT && r < M) y[n * ldy + r] = silu(gv) * upv;
+    }
+}
+
+template <int FMT, int NT, int R, bool GATED, int WAVES, int S, int EP>
+__global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __restrict__ Wg,
+                                                               const uint8_t* __restrict__ Wu,
+                                                               const float* __restrict__ x, float* __restrict__ y,
+                                                               int M, int K, int64_t ldx, int64_t ldy, DecodeEpi epi) {
+    static_assert(S >= 2 && S <= 4, "ring depth");
+    using G = DmaGeom<FMT>;
+    constexpr int BB = G::BB, BPL = G::BPL, SLICE = G::SLICE;
+    constexpr int RU = GATED ? 2 * R : R;
+    constexpr int NI = RU * DG_NI;         // DMA instructions per task
+    constexpr int WS = WAVES * RU * DG_SLOT;  // bytes of one ring stage (all waves)
+    __shared__ __align__(16) uint8_t RS0[WS + DG_PAD];
+    __shared__ __align__(16) uint8_t RS1[WS + DG_PAD];
+    __shared__ __align__(16) uint8_t RS2[S > 2 ? WS + DG_PAD : 16];
+    __shared__ __align__(16) uint8_t RS3[S > 3 ? WS + DG_PAD : 16];
+    // x and the norm partials take the rest of the CU's LDS, also as static arrays:
+    // the compiler treats dynamic LDS as possibly written by any DMA in flight and
+    // would wait for all of them before every read of x.
+    using L = DmaLds<NT, RU, WAVES, S>;
+    __shared__ __align__(16) uint32_t xs[L::XCAP / 4];
+    __shared__ float red[WAVES * NT];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nb = K / kQK;
+    const int xstride = nb * XS16;
+    const int64_t rb = static_cast<int64_t>(nb) * BB;
+    const int ns = (nb + SLICE - 1) / SLICE;
+    const int ngroups = (M + R - 1) / R;
+    const int nw = gridDim.x * WAVES;
+    const int wid = blockIdx.x * WAVES + wave;
+    const int my_groups = wid < ngroups ? (ngroups - 1 - wid) / nw + 1 : 0;
+    const int ntask = my_groups * ns;
+    const int wslot = wave * RU * DG_SLOT;  // this wave's part of a stage
+
+    // DMA of the task at cursor c into stage array `stage`; tasks past the list read zeros.
+    const uint32_t v16 = 16u * static_cast<uint32_t>(lane);
+    const uint32_t v4 = 4u * static_cast<uint32_t>(lane) + 2048u;
+    auto issue = [&](uint8_t* stage, const TaskCursor& c) {
+        const bool real = c.gi < my_groups;
+        const int g = wid + c.gi * nw;
+        const int s0 = c.s * SLICE;
+        const int sbytes = real ? min(SLICE, nb - s0) * BB : 0;
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            const int row = g * R + (u % R);
+            const bool ok = real && row < M;
+            const uint8_t* wb = (GATED && u >= R) ? Wu : Wg;
+            const __amdgpu_buffer_rsrc_t r =
+                make_rsrc(wb + (ok ? row * rb + static_cast<int64_t>(s0) * BB : 0), ok ? sbytes : 0);
+            QMM_L3 uint8_t* d = (QMM_L3 uint8_t*)(stage + wslot + u * DG_SLOT);
+            dma16<kCacheNT>(r, v16, 0, d);
+            dma16<kCacheNT>(r, v16 + 1024u, 0, d + 1024);
+            dma4<kCacheNT>(r, v4, d + 2048);
+        }
+    };
+
+    float acc[RU][NT];
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[u][n] = 0.0f;
+
+    // x (with gamma, and the residuals) is requested first and the first S tasks'
+    // weights right after it: converting x then waits only for its own loads, and the
+    // weight DMAs stay in flight while x is staged.  x -> LDS once (EP_NORM:
+    // gamma .* x, with the sum of squares of x gathered on the way); lanes 8b..8b+7 of
+    // a round hold the 8 chunks of block b.
+    constexpr int SU = WAVES >= 16 ? 4 : 64 / WAVES;  // one round covers K <= 16384
+    constexpr int XR = SU * WAVES * kWave;             // float4s of one token per round
+    float4 xv[SU][NT], gv[SU];
+    float ss[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) ss[n] = 0.0f;
+    // Loads are unconditional (index clamped; surplus lanes re-read the last chunk
+    // and stage nothing): loads under a branch make the compiler wait for every
+    // outstanding load, the weight DMAs included, before their use.
+    auto load_round = [&](int j0) {
+#pragma unroll
+        for (int r = 0; r < SU; ++r) {
+            const int64_t j = min(j0 + r * WAVES * kWave, nb * 8 - 1);
+            if constexpr (EP == EP_NORM) gv[r] = *reinterpret_cast<const float4*>(epi.gamma + 4 * j);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) xv[r][n] = *reinterpret_cast<const float4*>(x + n * ldx + 4 * j);
+        }
+    };
+    auto stage_round = [&](int j0) {
+#pragma unroll
+        for (int r = 0; r < SU; ++r) {
+            const int j = j0 + r * WAVES * kWave;
+            if (j < nb * 8) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    float4 v = xv[r][n];
+                    if constexpr (EP == EP_NORM) {
+                        const float4 gm = gv[r];
+                        ss[n] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss[n]))));
+                        v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
+                    }
+                    stage_x16<FMT>(v, j & 7, xs + n * xstride + (j >> 3) * XS16);
+                }
+            }
+        }
+    };
+    load_round(threadIdx.x);
+
+    // EP_RES: the residuals of this lane's output in the wave's first row groups.
+    constexpr int NTP = (NT == 3) ? 4 : NT;
+    constexpr int LPI = kWave / (RU * NTP);
+    // res0 belongs to the current row group; the values move down one place per
+    // group (registers only: a value selected by the group number is turned into an
+    // indexed table in scratch memory, whose reads would wait for the weight DMAs).
+    float res0 = 0.0f, res1 = 0.0f, res2 = 0.0f, res3 = 0.0f;
+    static_assert(DG_GMAX == 4, "four read-ahead residuals");
+    if constexpr (EP == EP_RES) {
+        const int idx = lane / LPI;
+        const int u = idx / NTP, n = idx - (idx / NTP) * NTP;
+        auto res_at = [&](int gi) -> float {
+            const int r = (wid + gi * nw) * R + u;
+            const bool ok = gi < my_groups && lane % LPI == 0 && n < NT && r < M;
+            const float v = epi.res[ok ? n * ldy + r : 0];  // unconditional load (see load_round)
+            return ok ? v : 0.0f;
+        };
+        res0 = res_at(0);
+        res1 = res_at(1);
+        res2 = res_at(2);
+        res3 = res_at(3);
+    }
+
+    TaskCursor ic{0, 0};
+    issue(RS0, ic);
+    ic.next(ns);
+    issue(RS1, ic);
+    ic.next(ns);
+    if constexpr (S > 2) {
+        issue(RS2, ic);
+        ic.next(ns);
+    }
+    if constexpr (S > 3) {
+        issue(RS3, ic);
+        ic.next(ns);
+    }
+
+    stage_round(threadIdx.x);
+    for (int j0 = threadIdx.x + XR; j0 < nb * 8; j0 += XR) {  // K > 4 XR floats per token only
+        load_round(j0);
+        stage_round(j0);
+    }
+    if constexpr (EP == EP_NORM) norm_partials<NT>(ss, red, wave, lane);
+    // LDS-only barriers: a full __syncthreads would also wait for the weight DMAs.
+    lds_barrier();
+    for (int b = threadIdx.x; b < NT * nb; b += WAVES * kWave) stage_chain<FMT>(xs + b * XS16);
+    lds_barrier();
+    float scale = 1.0f;
+    if constexpr (EP == EP_NORM) scale = norm_scale<NT>(red, WAVES, reduced_token<RU, NT>(lane), K, epi.eps);
+
+    // One task from stage array `stage`, then its refill with the task S ahead.
+    TaskCursor cc{0, 0};
+    auto step = [&](uint8_t* stage) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<(S - 1) * NI>();  // this task's DMA has landed; the next S - 1 stay in flight
+        __builtin_amdgcn_sched_barrier(0);
+        if (cc.gi < my_groups) {
+            const int s0 = cc.s * SLICE;
+            const int sb = min(SLICE, nb - s0);
+            const uint8_t* buf[RU];
+#pragma unroll
+            for (int u = 0; u < RU; ++u) buf[u] = stage + wslot + u * DG_SLOT;
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) {
+                const int blk = lane + kWave * b;
+                if (blk < sb) {
+                    int off[RU];
+#pragma unroll
+                    for (int u = 0; u < RU; ++u) off[u] = blk * BB;
+                    const uint32_t* xb[NT];
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) xb[n] = xs + n * xstride + (s0 + blk) * XS16;
+                    block_dot<FMT, RU, NT>(buf, off, xb, acc);
+                }
+            }
+            if (cc.s == ns - 1) {
+                dma_reduce_store<R, RU, NT, GATED, EP>(acc, lane, (wid + cc.gi * nw) * R, M, y, ldy, scale, res0);
+                if constexpr (EP == EP_RES) {
+                    res0 = res1;
+                    res1 = res2;
+                    res2 = res3;
+                }
+#pragma unroll
+                for (int u = 0; u < RU; ++u)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) acc[u][n] = 0.0f;
+            }
+        }
+        // The slot's LDS reads are complete before the DMA that overwrites it goes out.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        issue(stage, ic);
+        ic.next(ns);
+        cc.next(ns);
+    };
+    for (int t0 = 0; t0 < ntask; t0 += S) {
+        step(RS0);
+        step(RS1);
+        if constexpr (S > 2) step(RS2);
+        if constexpr (S > 3) step(RS3);
+    }
+    // Drain the trailing DMAs (zero-length reads) before the workgroup can exit.
+    wait_vm<0>();
+}
+
+template <int FMT, int NT, int R, bool GATED, int WAVES, int S, int EP>
+static int64_t dma_launch(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                          const DecodeEpi& epi, hipStream_t s) {
+    constexpr int RU = GATED ? 2 * R : R;
+    const int64_t nb = K / 32;
+    if (NT * nb * XS16 * 4 > DmaLds<NT, RU, WAVES, S>::XCAP) return 0;
+    const int64_t ngroups = (M + R - 1) / R;
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((ngroups + WAVES - 1) / WAVES, 256));
+    if (EP == EP_RES) {
+        const int64_t nw = grid * WAVES;
+        if ((ngroups + nw - 1) / nw > DG_GMAX) return 0;
+    }
+    hipLaunchKernelGGL((gemv_dma_kernel<FMT, NT, R, GATED, WAVES, S, EP>), dim3(static_cast<unsigned>(grid)),
+                       dim3(WAVES * kWave), 0, s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), x,
+                       y, static_cast<int>(M), static_cast<int>(K), K, M, epi);
+    return M;
+}
+
+// Variant choice (measured on MI355X at the Llama-3-8B decode shapes, weights
+// streamed from HBM): about 70 KB of weights in flight per CU is best; deeper rings
+// are slower.
+//   * >= 16384 rows (LM head): 2 rows per task (x is read from LDS once per two
+//     rows), 16 waves, 2 slots;
+//   * fewer rows: 1 row per task, 8 waves, 2 slots (more waves or slots in flight
+//     were slower on the 4096- and 6144-row matrices);
+//   * gated: one gate and one up row per task, 8 waves, 3 slots.
+template <int FMT, int NT, int EP>
+static int64_t dma_nt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                      const DecodeEpi& epi, hipStream_t s) {
+    if (Wu) {
+        if constexpr (EP == EP_RES) return 0;
+        else return dma_launch<FMT, NT, 1, true, 8, 3, EP>(W, Wu, x, y, M, K, epi, s);
+    }
+    int64_t r = 0;
+    if constexpr (NT <= 2)  // (4 tokens x 2 rows exceed the 128 registers of 16 waves)
+        if (M >= 16384) r = dma_launch<FMT, NT, 2, false, 16, 2, EP>(W, Wu, x, y, M, K, epi, s);
+    if (!r) r = dma_launch<FMT, NT, 1, false, 8, 2, EP>(W, Wu, x, y, M, K, epi, s);
+    return r;
+}
+
+template <int FMT, int EP>
+static int64_t dma_fmt_ep(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, int NT,
+                          const DecodeEpi& epi, hipStream_t s) {
+    switch (NT) {
+        case 1: return dma_nt<FMT, 1, EP>(W, Wu, x, y, M, K, epi, s);
+        case 2: return dma_nt<FMT, 2, EP>(W, Wu, x, y, M, K, epi, s);
+        case 3: return dma_nt<FMT, 3, EP>(W, Wu, x, y, M, K, epi, s);
+        default: return dma_nt<FMT, 4, EP>(W, Wu, x, y, M, K, epi, s);
+    }
+}
+
+template <int FMT>
+static int64_t dma_fmt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, int NT, int ep,
+                       const DecodeEpi& epi, hipStream_t s) {
+    switch (ep) {
+        case EP_NORM: return dma_fmt_ep<FMT, EP_NORM>(W, Wu, x, y, M, K, NT, epi, s);
+        case EP_RES: return dma_fmt_ep<FMT, EP_RES>(W, Wu, x, y, M, K, NT, epi, s);
+        default: return dma_fmt_ep<FMT, EP_NONE>(W, Wu, x, y, M, K, NT, epi, s);
+    }
+}
+
+int64_t launch_gemv_dma(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                        int NT, int ep, const DecodeEpi& epi, hipStream_t s) {
+    if (K % 256 != 0 || NT < 1 || NT > 4) return 0;
+    if (fmt == 8) return dma_fmt<8>(W, Wu, x, y, M, K, NT, ep, epi, s);
+    if (fmt == 2) return dma_fmt<2>(W, Wu, x, y, M, K, NT, ep, epi, s);
+    return 0;
+}
+
+}  // namespace qmm

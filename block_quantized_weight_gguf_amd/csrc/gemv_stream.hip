@@ -26,6 +26,7 @@
 //     left to the sliced kernel, so this one never needs a tail path.
 //   * A row group's partial sums stay in registers across its K slices and are
 //     reduced across the wave once, with a transposing butterfly.
+#include "dma.hpp"
 #include "gemv_block.hpp"
 #include "qmm_internal.hpp"
 
@@ -116,32 +117,32 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[u][n] = 0.0f;
 
-    // The first D tasks' weight loads go out before x is staged: they do not depend on it.
-#pragma unroll
-    for (int q = 0; q < D; ++q)
-        if (q < ntask) issue(q, regs[q]);
-
-    // x -> LDS once: NT tokens x nb blocks, 8 float4 per block (EP_NORM: gamma .* x,
-    // with the sum of squares of x gathered on the way).  Lanes 8b..8b+7 of a round
-    // hold the 8 chunks of one block (nb * 8 is a multiple of 8).
+    // x (with gamma) is requested first and the first D tasks' weights right after
+    // it: converting x then waits only for its own loads, and the weight loads stay
+    // in flight while x is staged.  x -> LDS once: NT tokens x nb blocks, 8 float4
+    // per block (EP_NORM: gamma .* x, with the sum of squares of x gathered on the
+    // way).  Lanes 8b..8b+7 of a round hold the 8 chunks of one block (nb * 8 is a
+    // multiple of 8).  SU rounds of the workgroup are loaded before any is
+    // converted, so their latencies overlap (one pass covers K <= 16384 with 16 waves).
+    constexpr int SU = 4;
+    constexpr int XR = SU * WAVES * kWave;
+    float4 xv[SU][NT], gv[SU];
     float ss[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) ss[n] = 0.0f;
-    // SU rounds of the workgroup are loaded before any is converted, so their
-    // latencies overlap (one pass covers K <= 16384 with 16 waves).
-    constexpr int SU = 4;
-    for (int j0 = threadIdx.x; j0 < nb * 8; j0 += SU * WAVES * kWave) {
-        float4 xv[SU][NT], gv[SU];
+    // Loads are unconditional (index clamped; surplus lanes re-read the last chunk
+    // and stage nothing): loads under a branch make the compiler wait for every
+    // outstanding load, the weight DMAs included, before their use.
+    auto load_round = [&](int j0) {
 #pragma unroll
         for (int r = 0; r < SU; ++r) {
-            const int j = j0 + r * WAVES * kWave;
-            if (j < nb * 8) {
-                if constexpr (EP == EP_NORM) gv[r] = *reinterpret_cast<const float4*>(epi.gamma + 4 * static_cast<int64_t>(j));
+            const int64_t j = min(j0 + r * WAVES * kWave, nb * 8 - 1);
+            if constexpr (EP == EP_NORM) gv[r] = *reinterpret_cast<const float4*>(epi.gamma + 4 * j);
 #pragma unroll
-                for (int n = 0; n < NT; ++n)
-                    xv[r][n] = *reinterpret_cast<const float4*>(x + n * ldx + 4 * static_cast<int64_t>(j));
-            }
+            for (int n = 0; n < NT; ++n) xv[r][n] = *reinterpret_cast<const float4*>(x + n * ldx + 4 * j);
         }
+    };
+    auto stage_round = [&](int j0) {
 #pragma unroll
         for (int r = 0; r < SU; ++r) {
             const int j = j0 + r * WAVES * kWave;
@@ -158,12 +159,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
                 }
             }
         }
+    };
+    load_round(threadIdx.x);
+#pragma unroll
+    for (int q = 0; q < D; ++q)
+        if (q < ntask) issue(q, regs[q]);
+    stage_round(threadIdx.x);
+    for (int j0 = threadIdx.x + XR; j0 < nb * 8; j0 += XR) {
+        load_round(j0);
+        stage_round(j0);
     }
     float* red = reinterpret_cast<float*>(smem + xs_bytes + WAVES * (RU * ROWBUF));
     if constexpr (EP == EP_NORM) norm_partials<NT>(ss, red, wave, lane);
-    __syncthreads();
+    // LDS-only barriers: a full __syncthreads would also wait for the weight loads.
+    lds_barrier();
     for (int b = threadIdx.x; b < NT * nb; b += WAVES * kWave) stage_chain<FMT>(xs + b * XS16);
-    __syncthreads();
+    lds_barrier();
     float scale = 1.0f;
     if constexpr (EP == EP_NORM) scale = norm_scale<NT>(red, WAVES, reduced_token<RU, NT>(lane), K, epi.eps);
 

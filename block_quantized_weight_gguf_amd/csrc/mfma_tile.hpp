@@ -1,6 +1,6 @@
 // Shared pieces of the MFMA kernels (prefill GEMM and small-batch GEMV) for gfx950:
-// fp16-domain decode of GGUF blocks into MFMA operands, buffer->LDS DMA, and the
-// wait/barrier helpers that keep DMA prefetches in flight across barriers.
+// fp16-domain decode of GGUF blocks into MFMA operands (the buffer->LDS DMA and
+// wait helpers are in dma.hpp).
 //
 // Decode ("EdgeRunner Core Architecture", sections 3.1 and 3.2: w = d * q for Q8_0,
 // d * (n - 8) for Q4_0, byte j of a Q4_0 block holding weights j and j + 16): a code
@@ -9,6 +9,7 @@
 // single rounding.
 #pragma once
 
+#include "dma.hpp"
 #include "qmm_common.hpp"
 
 namespace qmm {
@@ -16,8 +17,6 @@ namespace qmm {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-
-
 
 __device__ __forceinline__ uint32_t h2_bits(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ half2_t bits_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
@@ -48,9 +47,6 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     return h2_bits(half2_t{static_cast<_Float16>(a), static_cast<_Float16>(b)});
 }
 
-#define QMM_G1 __attribute__((address_space(1)))
-#define QMM_L3 __attribute__((address_space(3)))
-
 // Weight stage geometry: K steps per stage, 16-byte chunks per row window, and
 // the bytes of the per-row segment one stage covers.
 template <int FMT>
@@ -67,39 +63,6 @@ template <>
 struct WStage<1> {  // F16: 64 halfs = 128 bytes
     static constexpr int KPS = 1, WCH = 8;
 };
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier for the LDS stages.  A release fence would wait for every
-// outstanding global->LDS DMA (they count as LDS writes), including the prefetches
-// that must stay in flight; instead each wave waits explicitly for the DMA it needs
-// (wait_vm) and for its own LDS stores (lgkmcnt), and the empty asm statements keep
-// the compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Buffer resource over [base, base + bytes) (raw addressing, 32-bit data format;
-// reads past `bytes` return zeros instead of faulting).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int n = static_cast<int>(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
-}
-
-// One 16-byte buffer->LDS DMA per lane: lane L's bytes (resource + voff + soff) land
-// at lds + 16 L.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, QMM_L3 uint8_t* lds) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (QMM_L3 void*)lds, 16, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
-}
 
 // A fragment of v_mfma_f32_16x16x32_f16 decoded from a raw Q8_0 / Q4_0 row window in
 // LDS: the 8 weights 8 q4 .. 8 q4 + 7 (lane l: q4 = l / 16) of the block that starts

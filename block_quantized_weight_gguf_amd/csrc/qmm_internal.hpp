@@ -48,6 +48,12 @@ hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float*
 int64_t launch_gemv_stream(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
                            int NT, int ep, const DecodeEpi& epi, hipStream_t s);
 
+// DMA-fed streaming GEMV for Q8_0 / Q4_0 with K % 256 == 0 and NT <= 4 tokens in
+// one pass.  Returns M when it launched, 0 when it does not apply (format, K, LDS
+// footprint of x, or EP_RES with more row groups per wave than it reads ahead).
+int64_t launch_gemv_dma(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                        int NT, int ep, const DecodeEpi& epi, hipStream_t s);
+
 // Sliced GEMV for rows [row_begin, M), NT <= 4 tokens per pass, `chunks` passes
 // of NT tokens (grid.y).  Handles every format and every size.
 void launch_gemv_sliced(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
