@@ -184,6 +184,37 @@ __device__ __forceinline__ void stage_x16(float4 v, int c, uint32_t* blk) {
     if (c == 0) blk[17] = __float_as_uint(inv);
 }
 
+// One whole block of one token staged by one lane: v holds its 32 values (chunk c =
+// values 4c..4c+3).  The same block floating point and pair order as stage_x16,
+// and the offset chain c (stage_chain's dot2 steps in block_dot's order, so c is
+// bit-identical) formed from the lane's own registers; the block's 20 dwords go
+// out as five 16-byte LDS writes.
+template <int FMT>
+__device__ __forceinline__ void stage_block(const float4 (&v)[8], uint32_t* blk) {
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[c].x), fabsf(v[c].y)), fmaxf(fabsf(v[c].z), fabsf(v[c].w))));
+    const int e = static_cast<int>((__float_as_uint(m) >> 23) & 0xFFu) - 127;  // floor(log2 m); -127 for 0
+    const int se = min(126, 14 - e);
+    const float sc = __uint_as_float(static_cast<uint32_t>(se + 127) << 23);   // 2^se
+    const float inv = __uint_as_float(static_cast<uint32_t>(127 - se) << 23);  // 2^-se
+    uint32_t w[16];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int slot = (FMT == 8) ? 2 * c : 4 * (c & 3) + ((c >> 2) << 1);
+        w[slot] = pack_h2(v[c].x * sc, v[c].z * sc);
+        w[slot + 1] = pack_h2(v[c].y * sc, v[c].w * sc);
+    }
+    float chain = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) chain = dot2(DotCode<FMT>::V0, w[i], chain);
+    uint4* o = reinterpret_cast<uint4*>(blk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    o[4] = make_uint4(__float_as_uint(chain), __float_as_uint(inv), 0u, 0u);
+}
+
 // After the staged pairs are visible: c of one block, the dot2 chain over its 16
 // dwords in slot order with every code equal to the offset code (block_dot's chain).
 template <int FMT>
@@ -323,7 +354,9 @@ __device__ __forceinline__ void reduce_store(float (&acc)[RU][NT], int lane, int
             y[n * ldy + r] = val;
         }
     } else {
-        float upv = __shfl(v[0], (lane + R * NTP * LPI) & (kWave - 1), kWave);
+        // The up sums sit 32 lanes above the gate sums (R * NTP * LPI == 32).
+        static_assert(R * NTP * LPI == 32, "up rows reduce into the upper half");
+        float upv = wave_partner<32>(v[0]);
         float gv = v[0];
         if constexpr (EP == EP_NORM) {
             gv *= scale;

@@ -95,7 +95,9 @@ __device__ __forceinline__ void dma_reduce_store(float (&acc)[RU][NT], int lane,
             y[n * ldy + r] = val;
         }
     } else {
-        float upv = __shfl(v[0], (lane + R * NTP * LPI) & (kWave - 1), kWave);
+        // The up sums sit 32 lanes above the gate sums (R * NTP * LPI == 32).
+        static_assert(R * NTP * LPI == 32, "up rows reduce into the upper half");
+        float upv = wave_partner<32>(v[0]);
         float gv = v[0];
         if constexpr (EP == EP_NORM) {
             gv *= scale;
@@ -170,43 +172,46 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
 
     // x (with gamma, and the residuals) is requested first and the first S tasks'
     // weights right after it: converting x then waits only for its own loads, and the
-    // weight DMAs stay in flight while x is staged.  x -> LDS once (EP_NORM:
-    // gamma .* x, with the sum of squares of x gathered on the way); lanes 8b..8b+7 of
-    // a round hold the 8 chunks of block b.
-    constexpr int SU = WAVES >= 16 ? 4 : 64 / WAVES;  // one round covers K <= 16384
-    constexpr int XR = SU * WAVES * kWave;             // float4s of one token per round
-    float4 xv[SU][NT], gv[SU];
+    // weight DMAs stay in flight while x is staged.  x -> LDS once, one lane per
+    // (token, 32-value block): the lane loads the block's 8 float4 (EP_NORM: times
+    // gamma, with the sum of squares of x gathered on the way) and stages it with its
+    // offset chain (stage_block).  Only the first round's loads precede the DMAs.
+    constexpr int XT = WAVES * kWave;  // blocks per round
+    const int nxb = NT * nb;           // blocks to stage
+    float4 xv[8], gv[8];
     float ss[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) ss[n] = 0.0f;
-    // Loads are unconditional (index clamped; surplus lanes re-read the last chunk
+    // Loads are unconditional (index clamped; surplus lanes re-read the last block
     // and stage nothing): loads under a branch make the compiler wait for every
     // outstanding load, the weight DMAs included, before their use.
     auto load_round = [&](int j0) {
+        const int j = min(j0, nxb - 1);
+        const int n = j / nb, b = j - (j / nb) * nb;
+        const float4* src = reinterpret_cast<const float4*>(x + n * ldx + 32 * static_cast<int64_t>(b));
 #pragma unroll
-        for (int r = 0; r < SU; ++r) {
-            const int64_t j = min(j0 + r * WAVES * kWave, nb * 8 - 1);
-            if constexpr (EP == EP_NORM) gv[r] = *reinterpret_cast<const float4*>(epi.gamma + 4 * j);
+        for (int c = 0; c < 8; ++c) xv[c] = src[c];
+        if constexpr (EP == EP_NORM) {
+            const float4* gsrc = reinterpret_cast<const float4*>(epi.gamma + 32 * static_cast<int64_t>(b));
 #pragma unroll
-            for (int n = 0; n < NT; ++n) xv[r][n] = *reinterpret_cast<const float4*>(x + n * ldx + 4 * j);
+            for (int c = 0; c < 8; ++c) gv[c] = gsrc[c];
         }
     };
     auto stage_round = [&](int j0) {
+        if (j0 < nxb) {
+            const int n = j0 / nb, b = j0 - (j0 / nb) * nb;
+            if constexpr (EP == EP_NORM) {
+                float q = 0.0f;
 #pragma unroll
-        for (int r = 0; r < SU; ++r) {
-            const int j = j0 + r * WAVES * kWave;
-            if (j < nb * 8) {
-#pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    float4 v = xv[r][n];
-                    if constexpr (EP == EP_NORM) {
-                        const float4 gm = gv[r];
-                        ss[n] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss[n]))));
-                        v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
-                    }
-                    stage_x16<FMT>(v, j & 7, xs + n * xstride + (j >> 3) * XS16);
+                for (int c = 0; c < 8; ++c) {
+                    float4& t = xv[c];
+                    q = fmaf(t.x, t.x, fmaf(t.y, t.y, fmaf(t.z, t.z, fmaf(t.w, t.w, q))));
+                    t.x *= gv[c].x, t.y *= gv[c].y, t.z *= gv[c].z, t.w *= gv[c].w;
                 }
+#pragma unroll
+                for (int k = 0; k < NT; ++k) ss[k] += (k == n) ? q : 0.0f;
             }
+            stage_block<FMT>(xv, xs + n * xstride + b * XS16);
         }
     };
     load_round(threadIdx.x);
@@ -249,14 +254,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
     }
 
     stage_round(threadIdx.x);
-    for (int j0 = threadIdx.x + XR; j0 < nb * 8; j0 += XR) {  // K > 4 XR floats per token only
+    for (int j0 = threadIdx.x + XT; j0 < nxb; j0 += XT) {  // more blocks than lanes only
         load_round(j0);
         stage_round(j0);
     }
     if constexpr (EP == EP_NORM) norm_partials<NT>(ss, red, wave, lane);
-    // LDS-only barriers: a full __syncthreads would also wait for the weight DMAs.
-    lds_barrier();
-    for (int b = threadIdx.x; b < NT * nb; b += WAVES * kWave) stage_chain<FMT>(xs + b * XS16);
+    // LDS-only barrier: a full __syncthreads would also wait for the weight DMAs.
     lds_barrier();
     float scale = 1.0f;
     if constexpr (EP == EP_NORM) scale = norm_scale<NT>(red, WAVES, reduced_token<RU, NT>(lane), K, epi.eps);

@@ -116,29 +116,55 @@ __device__ __forceinline__ uint32_t lds_read_u16(const uint8_t* buf, int off) {
 // expf is the ROCm device-library exponential.
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Transposing butterfly reduction over a wave64.  On entry every lane holds V
-// partial sums v[0..V); on exit lane l holds, in v[0], the wave-wide sum of
-// index l / (64 / V).  Cost: V - 1 + (6 - log2 V) exchanges instead of 6 V.
+// The value `send` of this lane's partner at butterfly distance OFF, in VALU
+// instructions only (a ds_bpermute per step would make the reduction a chain of
+// LDS round trips).  OFF = 32, 16: v_permlane32_swap / v_permlane16_swap exchange
+// the two halves / the odd and even 16-lane rows; of the two registers they return,
+// one keeps this lane's value and the other holds the partner's, so their xor with
+// the lane's own value is the partner's, bit for bit.  OFF = 8, 4, 2, 1: DPP moves
+// within a row, whose partners (row_mirror 15 - i, row_half_mirror 7 - i,
+// quad_perm i ^ 2, i ^ 1) differ from the lane exactly in bit OFF and pair up
+// disjoint sets of lanes at every step, like the xor partners.
+template <int OFF>
+__device__ __forceinline__ float wave_partner(float send) {
+    if constexpr (OFF == 32 || OFF == 16) {
+        const uint32_t s = __float_as_uint(send);
+        const auto r = (OFF == 32) ? __builtin_amdgcn_permlane32_swap(s, s, false, false)
+                                   : __builtin_amdgcn_permlane16_swap(s, s, false, false);
+        return __uint_as_float(r[0] ^ r[1] ^ s);
+    } else {
+        constexpr int CTRL = OFF == 8 ? 0x140 : OFF == 4 ? 0x141 : OFF == 2 ? 0x4E : 0xB1;
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xF, 0xF, false));
+    }
+}
+
+template <int CNT, int OFF, int V>
+__device__ __forceinline__ void wave_reduce_step(float (&v)[V], int lane) {
+    if constexpr (OFF >= 1) {
+        if constexpr (CNT > 1) {
+            const bool upper = (lane & OFF) != 0;
+            constexpr int H = CNT / 2;
+#pragma unroll
+            for (int i = 0; i < H; ++i) {
+                const float send = upper ? v[i] : v[i + H];
+                const float keep = upper ? v[i + H] : v[i];
+                v[i] = keep + wave_partner<OFF>(send);
+            }
+            wave_reduce_step<H, OFF / 2>(v, lane);
+        } else {
+            v[0] += wave_partner<OFF>(v[0]);
+            wave_reduce_step<1, OFF / 2>(v, lane);
+        }
+    }
+}
+
+// Transposing butterfly reduction over a wave64 (all lanes active).  On entry every
+// lane holds V partial sums v[0..V); on exit lane l holds, in v[0], the wave-wide sum
+// of index l / (64 / V).  Cost: V - 1 + (6 - log2 V) exchanges instead of 6 V.
 template <int V>
 __device__ __forceinline__ void wave_reduce_transpose(float (&v)[V], int lane) {
     static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
-    int cnt = V;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        if (cnt > 1) {
-            const bool upper = (lane & off) != 0;
-            const int h = cnt >> 1;
-#pragma unroll
-            for (int i = 0; i < h; ++i) {
-                const float send = upper ? v[i] : v[i + h];
-                const float keep = upper ? v[i + h] : v[i];
-                v[i] = keep + __shfl_xor(send, off, 64);
-            }
-            cnt = h;
-        } else {
-            v[0] += __shfl_xor(v[0], off, 64);
-        }
-    }
+    wave_reduce_step<V, 32>(v, lane);
 }
 
 }  // namespace qmm

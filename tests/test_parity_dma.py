@@ -7,7 +7,7 @@ The shapes walk the kernel's geometry:
 * fewer tasks per wave than ring slots, and many more (the ring wraps);
 * row counts that are not multiples of the rows per task (the 2-row variant for
   >= 16384 rows), and more row groups than waves;
-* x sizes that select the 16-, 12-, 8- and 6-wave instances;
+* x sizes up to 35 KB per token (K = 14336) and 4 tokens of K = 4096;
 * the gated (SwiGLU), RMSNorm and residual modes, including the residual with more
   row groups per wave than the kernel reads ahead (another kernel takes those).
 Each output is poisoned with NaNs and followed by a guard band.
@@ -34,8 +34,8 @@ GEMV_CASES = [
     (4100, 4352, 1),   # more row groups than waves; Q8_0 3 slices, Q4_0 128 + 8
     (16385, 2304, 1),  # 2-row tasks with a lone last row
     (20000, 4352, 3),  # 2-row tasks, ring wraps many times, 3 tokens
-    (513, 14336, 1),   # x 35 KB: 12-wave instance
-    (300, 4096, 4),    # 4 tokens, x 40 KB: 12-wave instance
+    (513, 14336, 1),   # x 35 KB per token
+    (300, 4096, 4),    # 4 tokens, x 40 KB
     (9, 4096, 6),      # two passes (4 + 2 tokens)
 ]
 
@@ -116,3 +116,21 @@ def test_dma_gemv_add(fmt, M, K, N, inplace):
     check_residual(y.cpu().numpy(), y_ref, S, "dma gemv_add")
     if not inplace:
         assert np.array_equal(rd.cpu().numpy(), r), "the residual input must not change"
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("N", [1, 3])
+def test_dma_zero_codes_give_zero(fmt, N):
+    """Codes equal to the offset (q = 0, nibble 8) give exactly zero: the staged
+    offset chain of every x block equals the decode's dot product chain bit for bit."""
+    M, K = 300, 4352
+    d = np.full((M, K // 32), 0.75, dtype=np.float16)
+    if fmt == si.FMT_Q8_0:
+        raw = oracle.pack_q8_0(np.zeros((M, K), dtype=np.int8), d)
+    else:
+        raw = oracle.pack_q4_0(np.full((M, K), 8, dtype=np.uint8), d)
+    x = (si.activations(N, K, 17) * np.float32(1e3)).astype(np.float32)
+    announce(f"dma zero codes fmt={fmt} N={N}")
+    y = qmm.gemv(fmt, dev(raw), dev(x), M, K, variant=VALU)
+    torch.cuda.synchronize()
+    assert (y.cpu().numpy() == 0).all()
