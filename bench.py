@@ -428,7 +428,7 @@ def ceilings(torch):
 
 # Sources the dominant decode kernel is built from; its counter-derived traffic is
 # reported only while their combined hash matches the one recorded with the counters.
-DOMINANT_KERNEL = "gemv_dma_kernel<8, 1, 2, false, 16, 2, 0>"
+DOMINANT_KERNEL = "gemv_dma_kernel<8, 1, 1, false, 8, 3, 0>"
 DOMINANT_SOURCES = ("gemv_dma.hip", "gemv_block.hpp", "dma.hpp", "qmm_common.hpp", "qmm_internal.hpp")
 
 

@@ -337,14 +337,13 @@ static int64_t dma_launch(const void* W, const void* Wu, const float* x, float* 
     return M;
 }
 
-// Variant choice (measured on MI355X at the Llama-3-8B decode shapes, weights
-// streamed from HBM): about 70 KB of weights in flight per CU is best; deeper rings
-// are slower.
-//   * >= 16384 rows (LM head): 2 rows per task (x is read from LDS once per two
-//     rows), 16 waves, 2 slots;
-//   * fewer rows: 1 row per task, 8 waves, 2 slots (more waves or slots in flight
-//     were slower on the 4096- and 6144-row matrices);
-//   * gated: one gate and one up row per task, 8 waves, 3 slots.
+// Variant choice (kernel-trace durations on MI355X, K = 4096, 256 to 131072 rows,
+// weights streamed from HBM): 8 waves with a 3-slot ring and 1-row tasks is best or
+// within noise at every size for Q8_0 (at 570 MB it is within 1% of the same kernel
+// with the decode removed, i.e. of the stream itself) and for Q4_0 up to 32768 rows;
+// the Q4_0 LM head (>= 65536 rows), whose decode is twice the work per byte, runs
+// best with 16 waves and 2-row tasks (x read from LDS once per two rows) on 2 slots.
+// Gated: one gate and one up row per task, 8 waves, 3 slots.
 template <int FMT, int NT, int EP>
 static int64_t dma_nt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
                       const DecodeEpi& epi, hipStream_t s) {
@@ -353,9 +352,9 @@ static int64_t dma_nt(const void* W, const void* Wu, const float* x, float* y, i
         else return dma_launch<FMT, NT, 1, true, 8, 3, EP>(W, Wu, x, y, M, K, epi, s);
     }
     int64_t r = 0;
-    if constexpr (NT <= 2)  // (4 tokens x 2 rows exceed the 128 registers of 16 waves)
-        if (M >= 16384) r = dma_launch<FMT, NT, 2, false, 16, 2, EP>(W, Wu, x, y, M, K, epi, s);
-    if (!r) r = dma_launch<FMT, NT, 1, false, 8, 2, EP>(W, Wu, x, y, M, K, epi, s);
+    if constexpr (FMT == 2 && NT <= 2)  // (4 tokens x 2 rows exceed the 128 registers of 16 waves)
+        if (M >= 65536) r = dma_launch<FMT, NT, 2, false, 16, 2, EP>(W, Wu, x, y, M, K, epi, s);
+    if (!r) r = dma_launch<FMT, NT, 1, false, 8, 3, EP>(W, Wu, x, y, M, K, epi, s);
     return r;
 }
 
