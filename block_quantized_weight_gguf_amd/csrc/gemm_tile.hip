@@ -48,6 +48,7 @@
 //   * fp32 tokens (batched decode through the MFMA path) are converted while being
 //     staged through VGPRs instead of by DMA.
 #include <algorithm>
+#include <map>
 #include <mutex>
 #include <type_traits>
 
@@ -566,20 +567,52 @@ hipMemPool_t workspace_pool() {
     return pools[dev];
 }
 
-float* workspace_alloc(size_t bytes, hipStream_t s) {
+// Split-K workspace kept per (device, stream) and reused by every call on that
+// stream: a stream-ordered allocation and free per call cost about 20 us of host time,
+// more than the kernels of a small call.  Growth allocates the larger buffer from the
+// pool and frees the old one on the same stream, after its last use there.  The lock
+// is held until the lease ends, so host threads that share a stream cannot interleave
+// one call's partial sums with another's reduction.  While the stream is being captured
+// into a graph no workspace is handed out.
+namespace {
+std::mutex g_ws_mu;
+struct WsEntry {
+    float* p = nullptr;
+    size_t bytes = 0;
+};
+std::map<std::pair<int, uintptr_t>, WsEntry> g_ws;
+}  // namespace
+
+WorkspaceLease::WorkspaceLease(size_t bytes, hipStream_t s) {
+    if (bytes == 0) return;
+    lock_ = std::unique_lock<std::mutex>(g_ws_mu);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
         (void)hipGetLastError();
-        return nullptr;
+        return;
     }
-    if (cs != hipStreamCaptureStatusNone) return nullptr;
-    hipMemPool_t pool = workspace_pool();
-    float* P = nullptr;
-    if (!pool || hipMallocFromPoolAsync(reinterpret_cast<void**>(&P), bytes, pool, s) != hipSuccess) {
+    if (cs != hipStreamCaptureStatusNone) return;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
-        return nullptr;
+        return;
     }
-    return P;
+    hipMemPool_t pool = workspace_pool();
+    if (!pool) return;
+    WsEntry& e = g_ws[{dev, reinterpret_cast<uintptr_t>(s)}];
+    if (e.bytes < bytes) {
+        constexpr size_t kGrain = size_t{1} << 20;
+        const size_t want = (std::max(bytes, 2 * e.bytes) + kGrain - 1) / kGrain * kGrain;
+        float* np = nullptr;
+        if (hipMallocFromPoolAsync(reinterpret_cast<void**>(&np), want, pool, s) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        if (e.p) (void)hipFreeAsync(e.p, s);
+        e.p = np;
+        e.bytes = want;
+    }
+    p_ = e.p;
 }
 
 bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32, float* Y, int64_t M,
@@ -611,9 +644,10 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
             nsplit = static_cast<int>((nsteps + ksteps - 1) / ksteps);
         }
     }
+    WorkspaceLease ws(nsplit > 1 ? static_cast<size_t>(nsplit) * T * (gated ? 2 * M : M) * sizeof(float) : 0, s);
     float* P = nullptr;
     if (nsplit > 1) {
-        P = workspace_alloc(static_cast<size_t>(nsplit) * T * (gated ? 2 * M : M) * sizeof(float), s);
+        P = ws.get();
         if (!P) {  // no workspace (or the stream is being captured): one workgroup per tile
             nsplit = 1;
             ksteps = static_cast<int>(nsteps);
@@ -635,7 +669,6 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
         else if (fmt == 2) { QMM_TILE_CASE(2, true, P) }
         else { QMM_TILE_CASE(1, true, P) }
         launch_splitk_reduce(P, Y, T, M, nsplit, gated, s);
-        (void)hipFreeAsync(P, s);
     } else {
         if (fmt == 8) { QMM_TILE_CASE(8, false, Y) }
         else if (fmt == 2) { QMM_TILE_CASE(2, false, Y) }

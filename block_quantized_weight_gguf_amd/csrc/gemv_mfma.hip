@@ -294,8 +294,8 @@ static bool launch_gm_nj(const void* W, const void* Wu, const float* x, float* y
     kst = std::min<int64_t>((kst + 1) / 2 * 2, nst);
     const int nsplit = static_cast<int>((nst + kst - 1) / kst);
     if (ntiles * nsplit > (int64_t{1} << 30)) return false;
-    float* P = nullptr;
-    if (nsplit > 1) P = workspace_alloc(static_cast<size_t>(nsplit) * N * (gated ? 2 * M : M) * sizeof(float), s);
+    WorkspaceLease ws(nsplit > 1 ? static_cast<size_t>(nsplit) * N * (gated ? 2 * M : M) * sizeof(float) : 0, s);
+    float* P = nsplit > 1 ? ws.get() : nullptr;
     if (!P) {  // one split (or no workspace, e.g. during graph capture): all of K per workgroup
         if (gated) launch_gm_t<FMT, true, NJ, false>(W, Wu, x, y, M, K, N, 1, static_cast<int>(nst), s);
         else launch_gm_t<FMT, false, NJ, false>(W, Wu, x, y, M, K, N, 1, static_cast<int>(nst), s);
@@ -304,7 +304,6 @@ static bool launch_gm_nj(const void* W, const void* Wu, const float* x, float* y
     if (gated) launch_gm_t<FMT, true, NJ, true>(W, Wu, x, P, M, K, N, nsplit, static_cast<int>(kst), s);
     else launch_gm_t<FMT, false, NJ, true>(W, Wu, x, P, M, K, N, nsplit, static_cast<int>(kst), s);
     launch_splitk_reduce(P, y, N, M, nsplit, gated, s);
-    (void)hipFreeAsync(P, s);
     return true;
 }
 

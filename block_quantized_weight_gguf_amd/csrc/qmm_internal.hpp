@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace qmm {
 
@@ -80,12 +81,25 @@ bool launch_gemv_mfma(int fmt, const void* W, const void* Wu, const float* x, fl
 // partials); nullptr if pools are unavailable.
 hipMemPool_t workspace_pool();
 
-// Allocates a split-K workspace of `bytes` on stream s from workspace_pool(), or
-// returns nullptr (launching nothing) when none can be had.  Never allocates while
-// s is being captured into a graph: stream-ordered allocations replayed from a
-// captured graph have given wrong results, so callers then take their paths that
-// need no workspace.
-float* workspace_alloc(size_t bytes, hipStream_t s);
+// Split-K workspace of at least `bytes` for calls on stream s, kept per (device,
+// stream) and reused by later calls on that stream (it grows with a stream-ordered
+// allocation from workspace_pool() and a stream-ordered free of the old buffer).  get()
+// is nullptr when none can be had, and always while s is being captured into a graph
+// (stream-ordered allocations replayed from a captured graph have given wrong results),
+// so callers then take their paths that need no workspace; bytes == 0 asks for none.
+// A lease that asked for a workspace holds a lock
+// until it ends: one call's launches that use the workspace are enqueued together.
+// A stream destroyed while its work is pending must not be followed by a new stream
+// that the runtime hands the same handle before that work ends.
+class WorkspaceLease {
+   public:
+    WorkspaceLease(size_t bytes, hipStream_t s);
+    float* get() const { return p_; }
+
+   private:
+    std::unique_lock<std::mutex> lock_;
+    float* p_ = nullptr;
+};
 
 // Y[t][m] = sum over s < nsplit of P[s][t][m] (gated: P holds gate sums in columns
 // 0..M-1 and up sums in M..2M-1 of each 2M-wide row, and Y = silu(gate) * up).
