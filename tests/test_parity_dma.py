@@ -5,11 +5,13 @@ The shapes walk the kernel's geometry:
 * a partial last K slice (64 blocks per Q8_0 slice, 128 per Q4_0 slice) and a
   single partial slice;
 * fewer tasks per wave than ring slots, and many more (the ring wraps);
-* row counts that are not multiples of the rows per task (the 2-row variant for
-  >= 16384 rows), and more row groups than waves;
+* row counts that are not multiples of the rows per task (Q4_0 with >= 65536 rows
+  runs 2-row tasks), and more row groups than waves;
 * x sizes up to 35 KB per token (K = 14336) and 4 tokens of K = 4096;
-* the gated (SwiGLU), RMSNorm and residual modes, including the residual with more
-  row groups per wave than the kernel reads ahead (another kernel takes those).
+* the RMSNorm and residual modes, including the residual with more row groups per
+  wave than the kernel reads ahead (another kernel takes those);
+* the gated (SwiGLU) product at the same shapes (served by the register-staged
+  kernel, which measured faster for it).
 Each output is poisoned with NaNs and followed by a guard band.
 """
 import numpy as np
@@ -32,8 +34,10 @@ GEMV_CASES = [
     (257, 768, 4),     # 4 tokens per pass
     (1000, 2304, 2),   # Q8_0: 64 + 8 blocks; Q4_0: one 72-block slice
     (4100, 4352, 1),   # more row groups than waves; Q8_0 3 slices, Q4_0 128 + 8
-    (16385, 2304, 1),  # 2-row tasks with a lone last row
-    (20000, 4352, 3),  # 2-row tasks, ring wraps many times, 3 tokens
+    (16385, 2304, 1),  # many row groups per wave
+    (20000, 4352, 3),  # ring wraps many times, 3 tokens
+    (65537, 512, 1),   # Q4_0: 2-row tasks with a lone last row
+    (65600, 256, 4),   # Q4_0: 2-row tasks, 4 tokens
     (513, 14336, 1),   # x 35 KB per token
     (300, 4096, 4),    # 4 tokens, x 40 KB
     (9, 4096, 6),      # two passes (4 + 2 tokens)
