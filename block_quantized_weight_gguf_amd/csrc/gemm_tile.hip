@@ -102,8 +102,15 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     constexpr int GT_NI = GT_RW / 16;
     constexpr int GT_NJ = GT_TW / 16;
 
-    __shared__ __align__(16) uint8_t Xs0[XBYTES];
-    __shared__ __align__(16) uint8_t Xs1[XBYTES];
+    // 128-token tiles (T <= 128, block formats, fp16 tokens) do half the MFMA work per
+    // K step of a 256-token tile, too little to cover HBM latency with the token DMA one
+    // step ahead.  Their token stages span two K steps like the weight stages, so both
+    // operands are fetched a whole stage (two steps) ahead, and only the first step of
+    // a stage needs a wait and a barrier.
+    constexpr bool X2 = BN == 128 && KPS == 2 && !XF32;
+    constexpr int XSTAGE = X2 ? 2 * XBYTES : XBYTES;  // bytes per token stage
+    __shared__ __align__(16) uint8_t Xs0[XSTAGE];
+    __shared__ __align__(16) uint8_t Xs1[XSTAGE];
     __shared__ __align__(16) uint8_t Ws0[WBYTES];
     __shared__ __align__(16) uint8_t Ws1[WBYTES];
 
@@ -353,21 +360,37 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     // which keeps the loop body free of branches (and the wait counts constant): on
     // the second step of a block-format stage the weight DMA issued on the previous
     // step, after the token DMA needed now, may stay in flight.
+    //
+    // Two-step token stages (X2): the stage's token and weight DMAs were issued on the
+    // first step of the previous stage and nothing after them, so that step waits for
+    // all DMA and then issues the next stage of both; the second step needs neither a
+    // wait nor a barrier (its data arrived with the first step's).
     auto step = [&](auto XS_, auto WS_, auto KK_, int k) {
         constexpr int XS = decltype(XS_)::value, WS = decltype(WS_)::value, KK = decltype(KK_)::value;
-        QMM_L3 uint8_t* Xc = XS ? X1 : X0;
+        QMM_L3 uint8_t* Xc = X2 ? (WS ? X1 : X0) + KK * XBYTES : (XS ? X1 : X0);
         QMM_L3 uint8_t* Xn = XS ? X0 : X1;
         QMM_L3 uint8_t* Wc = WS ? W1 : W0;
         QMM_L3 uint8_t* Wn = WS ? W0 : W1;
-        if constexpr (KPS == 2 && KK == 1) wait_vm<WPER>();
-        else wait_vm<0>();
-        if constexpr (XF32) store_x(Xc);
-        lds_barrier();
-        // fp32 tokens are loaded after the step's MFMAs, so that their staging registers
-        // are live only across the barrier (their latency is exposed; this path serves
-        // small decode batches).
-        if constexpr (!XF32) issue_x(Xn, min(k + 1, kend - 1));
-        if constexpr (KK == 0) issue_w(Wn, min(k / KPS + 1, send - 1));
+        if constexpr (X2) {
+            if constexpr (KK == 0) {
+                wait_vm<0>();
+                lds_barrier();
+                QMM_L3 uint8_t* Xs = WS ? X0 : X1;  // the other token stage
+                issue_x(Xs, min(k + 2, kend - 1));
+                issue_x(Xs + XBYTES, min(k + 3, kend - 1));
+                issue_w(Wn, min(k / KPS + 1, send - 1));
+            }
+        } else {
+            if constexpr (KPS == 2 && KK == 1) wait_vm<WPER>();
+            else wait_vm<0>();
+            if constexpr (XF32) store_x(Xc);
+            lds_barrier();
+            // fp32 tokens are loaded after the step's MFMAs, so that their staging
+            // registers are live only across the barrier (their latency is exposed; this
+            // path serves small decode batches).
+            if constexpr (!XF32) issue_x(Xn, min(k + 1, kend - 1));
+            if constexpr (KK == 0) issue_w(Wn, min(k / KPS + 1, send - 1));
+        }
         constexpr int SH = FMT == 1 ? 0 : 8 * WS;
         // a0 holds this step's first sub-step when it was decoded on the previous step
         // (second step of a block-format stage); otherwise decode it now.
@@ -388,6 +411,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     // ---- prologue: stage 0 of both operands
     issue_w(W0, kbeg / KPS);
     issue_x(X0, kbeg);
+    if constexpr (X2) issue_x(X0 + XBYTES, min(kbeg + 1, kend - 1));
     if constexpr (KPS == 2) {
         // K % 256 == 0: whole groups of 4 steps (weight stages 0, 0, 1, 1).
         for (int k = kbeg; k < kend; k += 4) {

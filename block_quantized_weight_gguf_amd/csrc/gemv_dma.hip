@@ -135,11 +135,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
     const int xstride = nb * XS16;
     const int64_t rb = static_cast<int64_t>(nb) * BB;
     const int ns = (nb + SLICE - 1) / SLICE;
-    const int ngroups = (M + R - 1) / R;
+    const int ngroups = (M - 1) / R + 1;  // (no overflow for M up to 2^31 - 1)
     const int nw = gridDim.x * WAVES;
     const int wid = blockIdx.x * WAVES + wave;
     const int my_groups = wid < ngroups ? (ngroups - 1 - wid) / nw + 1 : 0;
-    const int ntask = my_groups * ns;
+    const int ntask = my_groups * ns;  // the host keeps this below 2^31
     const int wslot = wave * RU * DG_SLOT;  // this wave's part of a stage
 
     // DMA of the task at cursor c into stage array `stage`; tasks past the list read zeros.
@@ -147,12 +147,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
     const uint32_t v4 = 4u * static_cast<uint32_t>(lane) + 2048u;
     auto issue = [&](uint8_t* stage, const TaskCursor& c) {
         const bool real = c.gi < my_groups;
-        const int g = wid + c.gi * nw;
+        const int64_t g = wid + static_cast<int64_t>(c.gi) * nw;  // past the list for the trailing dummies
         const int s0 = c.s * SLICE;
         const int sbytes = real ? min(SLICE, nb - s0) * BB : 0;
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
-            const int row = g * R + (u % R);
+            const int64_t row = g * R + (u % R);
             const bool ok = real && row < M;
             const uint8_t* wb = (GATED && u >= R) ? Wu : Wg;
             const __amdgpu_buffer_rsrc_t r =
@@ -327,6 +327,8 @@ static int64_t dma_launch(const void* W, const void* Wu, const float* x, float* 
     if (NT * nb * XS16 * 4 > DmaLds<NT, RU, WAVES, S>::XCAP) return 0;
     const int64_t ngroups = (M + R - 1) / R;
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((ngroups + WAVES - 1) / WAVES, 256));
+    const int64_t ns = (nb + DmaGeom<FMT>::SLICE - 1) / DmaGeom<FMT>::SLICE;
+    if (((ngroups + grid * WAVES - 1) / (grid * WAVES) + S) * ns >= (int64_t{1} << 31)) return 0;  // int task counts
     if (EP == EP_RES) {
         const int64_t nw = grid * WAVES;
         if ((ngroups + nw - 1) / nw > DG_GMAX) return 0;

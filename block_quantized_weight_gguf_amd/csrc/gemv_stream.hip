@@ -75,7 +75,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
 
     uint8_t* my = smem + xs_bytes + wave * (RU * ROWBUF);
     const int ns = (nb + SLICE - 1) / SLICE;
-    const int ngroups = (M + R - 1) / R;
+    const int ngroups = (M - 1) / R + 1;  // (no overflow for M up to 2^31 - 1)
     const int nw = gridDim.x * WAVES;
     const int wid = blockIdx.x * WAVES + wave;
     const int my_groups = wid < ngroups ? (ngroups - 1 - wid) / nw + 1 : 0;
@@ -262,6 +262,8 @@ static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y,
     const int64_t ngroups = (M + R - 1) / R;
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(16 / WAVES, kMaxLds / lds));
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((ngroups + WAVES - 1) / WAVES, 256 * per_cu));
+    const int64_t ns = (nb + G::SLICE - 1) / G::SLICE;
+    if (((ngroups + grid * WAVES - 1) / (grid * WAVES) + D) * ns >= (int64_t{1} << 31)) return 0;  // int task counts
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(WAVES * kWave), static_cast<size_t>(lds), s,
                        static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), x, y, static_cast<int>(M),
                        static_cast<int>(K), K, ldy, static_cast<int>(xs_bytes), epi);
