@@ -166,8 +166,10 @@ int qmm_gemv_variant(int fmt, const void* W, const float* x, float* y,
  * The variant qmm_gemv would run for these sizes (a QMM_VARIANT_* value >= 1),
  * or a negative qmm_status for invalid sizes.  Host-only.  The GEMV/GEMM split
  * by token count follows "llama.cpp Metal ...", section 3.2 (mat-vec for few
- * tokens, the tiled matrix-matrix kernel above a threshold); the threshold here
- * is measured on MI355X.
+ * tokens, the tiled matrix-matrix kernel above a threshold); the thresholds here
+ * are measured on MI355X: Q8_0 / Q4_0 switch to MFMA from 5 tokens, and at 4
+ * tokens when the weights reach 32 MB; F16 from 4 tokens.  (qmm_gate_up_silu
+ * applies the same rule to the combined gate and up weights.)
  */
 int qmm_gemv_choose(int fmt, int64_t M, int64_t K, int64_t N);
 

@@ -178,6 +178,14 @@ def test_variant_choice():
         assert L.qmm_gemv_choose(fmt, 4096, 4096, 4096) == 2
         v = [L.qmm_gemv_choose(fmt, 4096, 4096, n) for n in range(1, 65)]
         assert v == sorted(v), "the choice must switch once, from VALU to MFMA"
+    # Measured thresholds: Q8_0 / Q4_0 from 5 tokens, or 4 tokens over >= 32 MB of weights.
+    for fmt in (2, 8):
+        assert L.qmm_gemv_choose(fmt, 4096, 4096, 4) == 1       # 17.8 / 9.4 MB
+        assert L.qmm_gemv_choose(fmt, 4096, 4096, 5) == 2
+        assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == 2     # LM head
+        assert L.qmm_gemv_choose(fmt, 128256, 4096, 3) == 1
+    assert L.qmm_gemv_choose(1, 4096, 4096, 4) == 2
+    assert L.qmm_gemv_choose(1, 4096, 4096, 3) == 1
     assert L.qmm_gemv_choose(7, 4096, 4096, 1) == E_FMT
     assert L.qmm_gemv_choose(8, 4096, 100, 1) == E_SHAPE
     assert L.qmm_gemv_variant(8, A16, A16, A16 + 1, 4, 64, 1, 9, None) == E_ALIGN
