@@ -29,6 +29,17 @@ Readings of points the pages leave open (each also listed with the design notes)
 * Q4_0: the pages give only "4-bit, 32 per block, fp16 scale, 18 bytes".  Adopted:
   the GGUF arrangement, byte j of the 16 code bytes carries element j in its low
   nibble and element j + 16 in its high nibble; weight = d * (nibble - 8).
+* Q4_1, Q5_0, Q5_1: the pages give the type ids (3, 6, 7), the bytes per block
+  (20, 22, 24) and one phrase each (4-bit codes with an fp16 bias; 5-bit codes
+  with an fp16 scale; 5-bit codes with an fp16 bias).  Adopted, the GGUF
+  arrangement: fp16 scale d at byte 0; for the biased formats the fp16 bias m
+  follows at byte 2; the 5-bit formats then hold a 32-bit little-endian word qh
+  whose bit e is the fifth (high) bit of element e; the last 16 bytes hold the
+  low four bits in Q4_0's nibble order.  With u the element's 4- or 5-bit code:
+  Q4_1 w = d*u + m, Q5_0 w = d*(u - 16), Q5_1 w = d*u + m.  d*u + m is exact in
+  float64 (every fp16 is a multiple of 2^-24 below 2^16, so the sum spans fewer
+  than 53 bits).  These layouts are not printed on the pages: the pins below fix
+  the oracle to this reading, not the reading to an outside specification.
 * Orientation: W is row-major [M][K] (rows of K/32 blocks), y = x W^T with x
   token-major [N][K].
 * Fp16 scales decode with IEEE semantics, subnormals included; inf and NaN
@@ -40,7 +51,11 @@ ties-to-even), all 65536 fp16 patterns against a manual sign/exponent/mantissa
 decode, exact rational brute force on tiny shapes, pack/unpack round trip, SiLU
 and RMSNorm closed forms, row gathers of golden blocks, the golden dots reached
 through the norm and residual references, and the soundness of the fused-output
-bounds by perturbation.
+bounds by perturbation.  Q4_1 / Q5_0 / Q5_1: hand-computed blocks (field order,
+fifth-bit order, offset and bias sign; one block whose fp16 expansion needs a
+single rounding of the exact value), identities that reduce each to the pinned
+Q4_0 decoder or to one another, the per-bit placement of the fifth bits, round
+trips, the pages' byte counts, and exact rational brute force.
 """
 from __future__ import annotations
 
@@ -50,10 +65,13 @@ import numpy as np
 
 FMT_F16 = 1   # GGUF type ids (EdgeRunner, section 1.3)
 FMT_Q4_0 = 2
+FMT_Q4_1 = 3
+FMT_Q5_0 = 6
+FMT_Q5_1 = 7
 FMT_Q8_0 = 8
 
 QK = 32                         # weights per block (EdgeRunner, section 3.1)
-BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4_0: 18}
+BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4_0: 18, FMT_Q4_1: 20, FMT_Q5_0: 22, FMT_Q5_1: 24}
 
 # Acceptance constants: |y_gpu - y_ref| <= REL * S + ABS, S = sum_k |w_k x_k|.
 # REL = 2e-3 is about 2x the 2^-10 element-wise bound alpaca.swift states for its
@@ -64,7 +82,8 @@ TOL_ABS = 1e-6
 
 # ---------------------------------------------------------------- unpacking
 def row_bytes(fmt: int, K: int) -> int:
-    """Bytes per row: K/32 * 34 (Q8_0), K/32 * 18 (Q4_0), 2K (F16).
+    """Bytes per row: K/32 blocks of 34 (Q8_0), 18 (Q4_0), 20 (Q4_1), 22 (Q5_0) or
+    24 (Q5_1) bytes; 2K (F16).
 
     EdgeRunner, section 3.1 (bytes per block) and section 3.2 (block count times 34).
     """
@@ -82,10 +101,23 @@ def _blocks(raw: np.ndarray, fmt: int, M: int, K: int) -> np.ndarray:
     return raw.reshape(M, K // QK, BLOCK_BYTES[fmt])
 
 
-def _scale64(blk: np.ndarray) -> np.ndarray:
-    """fp16 scale from bytes 0..1 (little endian) -> float64, IEEE semantics."""
-    d16 = np.ascontiguousarray(blk[..., 0:2]).view("<f2")[..., 0]
+def _scale64(blk: np.ndarray, at: int = 0) -> np.ndarray:
+    """fp16 at bytes at..at+1 (little endian) -> float64, IEEE semantics."""
+    d16 = np.ascontiguousarray(blk[..., at:at + 2]).view("<f2")[..., 0]
     return d16.astype(np.float64)
+
+
+def _nibbles(qs: np.ndarray) -> np.ndarray:
+    """16 code bytes -> 32 four-bit codes: low nibbles are elements 0..15, high
+    nibbles elements 16..31 (the adopted GGUF order, shared by Q4_0/Q4_1/Q5_x)."""
+    b = qs.astype(np.int64)
+    return np.concatenate([b & 15, b >> 4], axis=-1)
+
+
+def _high_bits(qh: np.ndarray) -> np.ndarray:
+    """4 bytes of a little-endian 32-bit word -> its 32 bits, bit e at index e."""
+    word = np.ascontiguousarray(qh).view("<u4")[..., 0].astype(np.int64)
+    return (word[..., None] >> np.arange(32)) & 1
 
 
 def unpack_q8_0(raw, M: int, K: int) -> np.ndarray:
@@ -116,6 +148,47 @@ def unpack_q4_0(raw, M: int, K: int) -> np.ndarray:
         return (d[..., None] * q).reshape(M, K)
 
 
+def unpack_q4_1(raw, M: int, K: int) -> np.ndarray:
+    """Q4_1 -> float64 [M][K]: w_e = d * u_e + m, u_e the 4-bit code of element e.
+
+    EdgeRunner, sections 1.3 and 3.1 (type id 3, 20 bytes: 4-bit codes with an fp16
+    bias).  Byte positions (d at 0, m at 2, codes at 4..19) and nibble order are the
+    adopted GGUF reading.
+    """
+    blk = _blocks(raw, FMT_Q4_1, M, K)
+    d, m = _scale64(blk, 0), _scale64(blk, 2)
+    u = _nibbles(blk[..., 4:20]).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return (d[..., None] * u + m[..., None]).reshape(M, K)
+
+
+def unpack_q5_0(raw, M: int, K: int) -> np.ndarray:
+    """Q5_0 -> float64 [M][K]: w_e = d * (u_e - 16), u_e = nibble_e + 16 * bit e of qh.
+
+    EdgeRunner, sections 1.3 and 3.1 (type id 6, 22 bytes: 5-bit codes with an fp16
+    scale).  d at 0, qh at 2..5, low nibbles at 6..21, and the offset 16 (the
+    middle of the 5-bit range, as 8 is for Q4_0) are the adopted GGUF reading.
+    """
+    blk = _blocks(raw, FMT_Q5_0, M, K)
+    d = _scale64(blk, 0)
+    u = _nibbles(blk[..., 6:22]) + 16 * _high_bits(blk[..., 2:6])
+    with np.errstate(invalid="ignore"):
+        return (d[..., None] * (u - 16).astype(np.float64)).reshape(M, K)
+
+
+def unpack_q5_1(raw, M: int, K: int) -> np.ndarray:
+    """Q5_1 -> float64 [M][K]: w_e = d * u_e + m, u_e = nibble_e + 16 * bit e of qh.
+
+    EdgeRunner, sections 1.3 and 3.1 (type id 7, 24 bytes: 5-bit codes with an fp16
+    bias).  d at 0, m at 2, qh at 4..7, low nibbles at 8..23: adopted GGUF reading.
+    """
+    blk = _blocks(raw, FMT_Q5_1, M, K)
+    d, m = _scale64(blk, 0), _scale64(blk, 2)
+    u = (_nibbles(blk[..., 8:24]) + 16 * _high_bits(blk[..., 4:8])).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return (d[..., None] * u + m[..., None]).reshape(M, K)
+
+
 def unpack_f16(raw, M: int, K: int) -> np.ndarray:
     """F16 -> float64 [M][K] (EdgeRunner, section 1.3: type id 1)."""
     raw = np.ascontiguousarray(raw, dtype=np.uint8).reshape(-1)
@@ -129,6 +202,12 @@ def dequant(fmt: int, raw, M: int, K: int) -> np.ndarray:
         return unpack_q8_0(raw, M, K)
     if fmt == FMT_Q4_0:
         return unpack_q4_0(raw, M, K)
+    if fmt == FMT_Q4_1:
+        return unpack_q4_1(raw, M, K)
+    if fmt == FMT_Q5_0:
+        return unpack_q5_0(raw, M, K)
+    if fmt == FMT_Q5_1:
+        return unpack_q5_1(raw, M, K)
     if fmt == FMT_F16:
         return unpack_f16(raw, M, K)
     raise ValueError(f"unknown format {fmt}")
@@ -191,6 +270,42 @@ def pack_q4_0(n: np.ndarray, d16: np.ndarray) -> np.ndarray:
     out[..., 0:2] = np.ascontiguousarray(d16, dtype="<f2").view(np.uint8).reshape(M, K // QK, 2)
     out[..., 2:18] = n[..., :16] | (n[..., 16:] << 4)
     return out.reshape(-1)
+
+
+def _pack_common(fmt, codes, d16, m16, nbits):
+    M, K = codes.shape
+    u = np.asarray(codes, dtype=np.int64).reshape(M, K // QK, 32)
+    if (u < 0).any() or (u >= (1 << nbits)).any():
+        raise ValueError(f"codes must be in 0..{(1 << nbits) - 1}")
+    bb = BLOCK_BYTES[fmt]
+    out = np.zeros((M, K // QK, bb), dtype=np.uint8)
+    out[..., 0:2] = np.ascontiguousarray(d16, dtype="<f2").view(np.uint8).reshape(M, K // QK, 2)
+    at = 2
+    if m16 is not None:
+        out[..., 2:4] = np.ascontiguousarray(m16, dtype="<f2").view(np.uint8).reshape(M, K // QK, 2)
+        at = 4
+    if nbits == 5:
+        word = ((u >> 4) << np.arange(32)).sum(axis=-1).astype("<u4")
+        out[..., at:at + 4] = word[..., None].view(np.uint8).reshape(M, K // QK, 4)
+        at += 4
+    lo = u & 15
+    out[..., at:at + 16] = (lo[..., :16] | (lo[..., 16:] << 4)).astype(np.uint8)
+    return out.reshape(-1)
+
+
+def pack_q4_1(n: np.ndarray, d16: np.ndarray, m16: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_q4_1 for codes n in 0..15 [M][K], fp16 scales and biases [M][K/32]."""
+    return _pack_common(FMT_Q4_1, n, d16, m16, 4)
+
+
+def pack_q5_0(u: np.ndarray, d16: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_q5_0 for codes u in 0..31 [M][K] and fp16 scales [M][K/32]."""
+    return _pack_common(FMT_Q5_0, u, d16, None, 5)
+
+
+def pack_q5_1(u: np.ndarray, d16: np.ndarray, m16: np.ndarray) -> np.ndarray:
+    """Inverse of unpack_q5_1 for codes u in 0..31 [M][K], fp16 scales and biases [M][K/32]."""
+    return _pack_common(FMT_Q5_1, u, d16, m16, 5)
 
 
 # ------------------------------------------------------------ matmul, SwiGLU
@@ -362,10 +477,28 @@ def brute_force_matmul(fmt: int, raw: bytes, x_rows, M: int, K: int):
                     for i in range(32):
                         q = blk[2 + i]
                         w.append(d * (q - 256 if q >= 128 else q))
-                else:
-                    lo = [d * ((blk[2 + j] & 15) - 8) for j in range(16)]
-                    hi = [d * ((blk[2 + j] >> 4) - 8) for j in range(16)]
-                    w.extend(lo + hi)
+                    continue
+                # Every other block format: [d][m if biased][qh if 5-bit][16 nibble bytes].
+                biased = fmt in (FMT_Q4_1, FMT_Q5_1)
+                five = fmt in (FMT_Q5_0, FMT_Q5_1)
+                m = f16(blk[2], blk[3]) if biased else 0
+                pos = 4 if biased else 2
+                qh = 0
+                if five:
+                    qh = blk[pos] + 256 * blk[pos + 1] + 65536 * blk[pos + 2] + 16777216 * blk[pos + 3]
+                    pos += 4
+                codes = [0] * 32
+                for j in range(16):
+                    codes[j] = blk[pos + j] % 16
+                    codes[j + 16] = blk[pos + j] // 16
+                for e in range(32):
+                    u = codes[e] + (16 if five and (qh // 2 ** e) % 2 else 0)
+                    if fmt == FMT_Q4_0:
+                        w.append(d * (u - 8))
+                    elif fmt == FMT_Q5_0:
+                        w.append(d * (u - 16))
+                    else:
+                        w.append(d * u + m)
         W.append(w)
     out = []
     for xr in x_rows:

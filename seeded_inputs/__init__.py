@@ -2,9 +2,10 @@
 
 This module only draws random numbers (numpy ``Generator(PCG64(seed))``) and lays
 them out in the GGUF block byte layouts through numpy structured dtypes.  It holds
-none of the method's arithmetic: nothing here decodes a block, multiplies, or
-accumulates.  Both the float64 oracle and the GPU library consume the bytes it
-returns; each decodes them with its own code.
+none of the method's arithmetic: nothing here decodes a block or forms a product
+with the activations (the one product, a bias drawn relative to its block's scale,
+shapes a distribution).  Both the float64 oracle and the GPU library consume the
+bytes it returns; each decodes them with its own code.
 
 Block layouts (EdgeRunner Core Architecture, section 3.1 "Quantization Format
 Summary" and section 3.2 "Q8_0 Layout"; GGUF type ids from section 1.3):
@@ -13,12 +14,20 @@ Summary" and section 3.2 "Q8_0 Layout"; GGUF type ids from section 1.3):
   by 32 signed bytes.
 * Q4_0, type id 2: 18 bytes per 32 weights = fp16 scale followed by 16 bytes
   holding 32 four-bit codes (two per byte).
+* Q4_1, type id 3: 20 bytes = fp16 scale, fp16 bias, 16 code bytes.
+* Q5_0, type id 6: 22 bytes = fp16 scale, 4 bytes of fifth bits, 16 code bytes.
+* Q5_1, type id 7: 24 bytes = fp16 scale, fp16 bias, 4 bytes of fifth bits, 16 code
+  bytes.  (The pages give these byte counts; the field order is the GGUF one.)
 * F16, type id 1: 2 bytes per weight.
 
 Distributions follow the workloads the library is measured on: Q8_0 codes uniform
 in [-127, 127], Q4_0 codes uniform in 0..15 (a uniform byte carries two
 independent uniform nibbles), fp16 scales uniform in [1e-3, 1e-2], F16 weights
-normal with standard deviation 0.02, activations standard normal.
+normal with standard deviation 0.02, activations standard normal.  Q4_1 / Q5_0 /
+Q5_1 code bytes and fifth-bit words are uniform bytes (uniform 4- and 5-bit codes);
+the biases of Q4_1 and Q5_1 are drawn as -(6..9) scales per block and -(12..18) scales
+per block respectively, where a min/max quantiser puts the block minimum of normal
+weights.
 """
 from __future__ import annotations
 
@@ -26,14 +35,24 @@ import numpy as np
 
 FMT_F16 = 1
 FMT_Q4_0 = 2
+FMT_Q4_1 = 3
+FMT_Q5_0 = 6
+FMT_Q5_1 = 7
 FMT_Q8_0 = 8
 FORMATS = (FMT_F16, FMT_Q4_0, FMT_Q8_0)
-FMT_NAMES = {FMT_F16: "F16", FMT_Q4_0: "Q4_0", FMT_Q8_0: "Q8_0"}
+BIAS_FORMATS = (FMT_Q4_1, FMT_Q5_0, FMT_Q5_1)
+FMT_NAMES = {FMT_F16: "F16", FMT_Q4_0: "Q4_0", FMT_Q8_0: "Q8_0", FMT_Q4_1: "Q4_1", FMT_Q5_0: "Q5_0",
+             FMT_Q5_1: "Q5_1"}
 
-# Packed (unaligned) structured dtypes: itemsize 34 and 18 exactly.
+# Packed (unaligned) structured dtypes: itemsize 34, 18, 20, 22, 24 exactly.
 Q8_0_BLOCK = np.dtype([("d", "<f2"), ("qs", "i1", (32,))])
 Q4_0_BLOCK = np.dtype([("d", "<f2"), ("qs", "u1", (16,))])
-assert Q8_0_BLOCK.itemsize == 34 and Q4_0_BLOCK.itemsize == 18
+Q4_1_BLOCK = np.dtype([("d", "<f2"), ("m", "<f2"), ("qs", "u1", (16,))])
+Q5_0_BLOCK = np.dtype([("d", "<f2"), ("qh", "u1", (4,)), ("qs", "u1", (16,))])
+Q5_1_BLOCK = np.dtype([("d", "<f2"), ("m", "<f2"), ("qh", "u1", (4,)), ("qs", "u1", (16,))])
+BLOCK_DTYPES = {FMT_Q8_0: Q8_0_BLOCK, FMT_Q4_0: Q4_0_BLOCK, FMT_Q4_1: Q4_1_BLOCK, FMT_Q5_0: Q5_0_BLOCK,
+                FMT_Q5_1: Q5_1_BLOCK}
+assert [BLOCK_DTYPES[f].itemsize for f in (8, 2, 3, 6, 7)] == [34, 18, 20, 22, 24]
 
 # Rows are drawn in fixed-size chunks so that very large matrices (a 128256-row
 # output head) stay within host memory; the chunk size is part of the recipe.
@@ -50,7 +69,7 @@ def layout_bytes(fmt: int, K: int) -> int:
         return 2 * K
     if K % 32:
         raise ValueError("block formats need K % 32 == 0")
-    return (K // 32) * (34 if fmt == FMT_Q8_0 else 18)
+    return (K // 32) * BLOCK_DTYPES[fmt].itemsize
 
 
 def _scales(g: np.random.Generator, rows: int, nb: int, scale_mode: str) -> np.ndarray:
@@ -93,6 +112,19 @@ def weights(fmt: int, M: int, K: int, seed: int, *, scale_mode: str = "uniform",
             blk = dst.view(Q4_0_BLOCK).reshape(rows, nb)
             blk["qs"] = g.integers(0, 256, size=(rows, nb, 16), dtype=np.uint8)
             blk["d"] = _scales(g, rows, nb, scale_mode)
+        elif fmt in BIAS_FORMATS:
+            blk = dst.view(BLOCK_DTYPES[fmt]).reshape(rows, nb)
+            blk["qs"] = g.integers(0, 256, size=(rows, nb, 16), dtype=np.uint8)
+            if fmt != FMT_Q4_1:
+                blk["qh"] = g.integers(0, 256, size=(rows, nb, 4), dtype=np.uint8)
+            d = _scales(g, rows, nb, scale_mode)
+            blk["d"] = d
+            if fmt != FMT_Q5_0:
+                if scale_mode == "uniform":
+                    lo, hi = (6.0, 9.0) if fmt == FMT_Q4_1 else (12.0, 18.0)
+                    blk["m"] = (-g.uniform(lo, hi, size=(rows, nb)) * d.astype(np.float64)).astype(np.float16)
+                else:
+                    blk["m"] = _scales(g, rows, nb, scale_mode)
         elif fmt == FMT_F16:
             dst.view(np.float16)[:] = g.normal(0.0, 0.02, size=rows * K).astype(np.float16)
         else:

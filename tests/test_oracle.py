@@ -18,7 +18,9 @@ import seeded_inputs as si
 from oracle import qmm_oracle as Q
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-FMT_BY_NAME = {"Q8_0": Q.FMT_Q8_0, "Q4_0": Q.FMT_Q4_0, "F16": Q.FMT_F16}
+FMT_BY_NAME = {"Q8_0": Q.FMT_Q8_0, "Q4_0": Q.FMT_Q4_0, "F16": Q.FMT_F16, "Q4_1": Q.FMT_Q4_1,
+               "Q5_0": Q.FMT_Q5_0, "Q5_1": Q.FMT_Q5_1}
+BIAS_FMTS = [Q.FMT_Q4_1, Q.FMT_Q5_0, Q.FMT_Q5_1]
 
 
 # ----------------------------------------------------------------- fixtures
@@ -87,7 +89,9 @@ def test_golden_blocks_brute_force(path):
 
 
 def test_golden_fixture_count():
-    assert len(GOLDEN_FILES) >= 5
+    assert len(GOLDEN_FILES) >= 10
+    fmts = {load_golden(p)["fmt"] for p in GOLDEN_FILES}
+    assert set(FMT_BY_NAME.values()) <= fmts
 
 
 # --------------------------------------------- row gather and fp16 expansion
@@ -191,8 +195,12 @@ def test_expand_pin_catches_truncation():
             h[pick] = c[pick]
         return h
 
+    def via_fp32(f, raw, M, K):  # two roundings: exact -> fp32 -> fp16
+        return Q.dequant(f, raw, M, K).astype(np.float32).astype(np.float16)
+
     assert not check_expand(trunc)
     assert not check_expand(away)
+    assert not check_expand(via_fp32)
 
 
 # ------------------------------------------------------ RMSNorm and residual
@@ -354,7 +362,84 @@ def test_roundtrip_q4_0():
     assert np.array_equal(W, np.repeat(d.astype(np.float64), 32, axis=1) * (n.astype(np.float64) - 8))
 
 
+def _codes_and_scales(g, M, K, bits):
+    u = g.integers(0, 1 << bits, size=(M, K), dtype=np.int64)
+    u[0, :4] = (0, (1 << bits) - 1, 1 << (bits - 1), 1)
+    d = g.uniform(-4, 4, size=(M, K // 32)).astype(np.float16)
+    m = g.uniform(-30, 30, size=(M, K // 32)).astype(np.float16)
+    return u, d, m
+
+
+def test_roundtrip_bias_formats():
+    """pack -> unpack gives d*u + m (or d*(u-16)) element for element, and the byte
+    counts are the pages' 20 / 22 / 24 per block."""
+    g = np.random.default_rng(13)
+    M, K = 6, 96
+    for fmt, bits, bb in ((Q.FMT_Q4_1, 4, 20), (Q.FMT_Q5_0, 5, 22), (Q.FMT_Q5_1, 5, 24)):
+        u, d, m = _codes_and_scales(g, M, K, bits)
+        if fmt == Q.FMT_Q4_1:
+            raw = Q.pack_q4_1(u, d, m)
+        elif fmt == Q.FMT_Q5_0:
+            raw = Q.pack_q5_0(u, d)
+        else:
+            raw = Q.pack_q5_1(u, d, m)
+        assert raw.size == M * K // 32 * bb
+        d64 = np.repeat(d.astype(np.float64), 32, axis=1)
+        m64 = np.repeat(m.astype(np.float64), 32, axis=1)
+        want = d64 * (u - 16) if fmt == Q.FMT_Q5_0 else d64 * u + m64
+        assert np.array_equal(Q.dequant(fmt, raw, M, K), want), fmt
+
+
+def test_bias_formats_reduce_to_q4_0():
+    """Identities between the formats under the adopted layouts, each tying a new
+    decoder to the pinned Q4_0 decoder or to another new one:
+    Q4_1 with m = -8d is Q4_0; Q5_0 with every fifth bit clear is Q4_0 shifted by
+    -8d; Q5_1 with every fifth bit clear is Q4_1; Q5_1 with m = -16d is Q5_0."""
+    g = np.random.default_rng(14)
+    M, K = 5, 128
+    n = g.integers(0, 16, size=(M, K), dtype=np.int64)
+    d = g.uniform(-4, 4, size=(M, K // 32)).astype(np.float16)
+    m8 = (np.float16(-8) * d).astype(np.float16)       # exact: a power-of-two multiple
+    m16 = (np.float16(-16) * d).astype(np.float16)
+    q40 = Q.unpack_q4_0(Q.pack_q4_0(n.astype(np.uint8), d), M, K)
+    assert np.array_equal(Q.unpack_q4_1(Q.pack_q4_1(n, d, m8), M, K), q40)
+    d64 = np.repeat(d.astype(np.float64), 32, axis=1)
+    assert np.array_equal(Q.unpack_q5_0(Q.pack_q5_0(n, d), M, K), q40 - 8 * d64)
+    m = g.uniform(-9, 9, size=(M, K // 32)).astype(np.float16)
+    assert np.array_equal(Q.unpack_q5_1(Q.pack_q5_1(n, d, m), M, K), Q.unpack_q4_1(Q.pack_q4_1(n, d, m), M, K))
+    u = g.integers(0, 32, size=(M, K), dtype=np.int64)
+    assert np.array_equal(Q.unpack_q5_1(Q.pack_q5_1(u, d, m16), M, K), Q.unpack_q5_0(Q.pack_q5_0(u, d), M, K))
+
+
+def test_fifth_bits_are_one_word():
+    """Setting only bit e of the 32-bit word moves exactly element e up by 16 scales."""
+    M, K = 1, 32
+    d = np.full((1, 1), 0.5, np.float16)
+    base = Q.unpack_q5_0(Q.pack_q5_0(np.zeros((M, K), np.int64), d), M, K)[0]
+    for e in (0, 7, 8, 15, 16, 23, 24, 31):
+        u = np.zeros((M, K), np.int64)
+        u[0, e] = 16
+        raw = Q.pack_q5_0(u, d)
+        word = int.from_bytes(bytes(raw[2:6]), "little")
+        assert word == 1 << e
+        diff = Q.unpack_q5_0(raw, M, K)[0] - base
+        assert np.flatnonzero(diff).tolist() == [e] and diff[e] == 8.0
+
+
+def test_bias_exact_in_float64():
+    """d*u + m with the extreme fp16 exponents is still exact in float64 (the
+    reading's claim): largest d with u = 31 plus the smallest subnormal bias."""
+    d = np.full((1, 1), 65504.0, np.float16)
+    m = np.full((1, 1), 2.0 ** -24, np.float16)
+    u = np.full((1, 32), 31, np.int64)
+    w = Q.unpack_q5_1(Q.pack_q5_1(u, d, m), 1, 32)[0, 0]
+    assert Fraction(float(w)) == Fraction(65504 * 31) + Fraction(1, 2 ** 24)
+
+
 def test_row_bytes():
+    assert Q.row_bytes(Q.FMT_Q4_1, 4096) == 128 * 20
+    assert Q.row_bytes(Q.FMT_Q5_0, 4096) == 128 * 22
+    assert Q.row_bytes(Q.FMT_Q5_1, 4096) == 128 * 24
     assert Q.row_bytes(Q.FMT_Q8_0, 576) == 612
     assert Q.row_bytes(Q.FMT_Q4_0, 576) == 324
     assert Q.row_bytes(Q.FMT_F16, 576) == 1152
@@ -378,7 +463,7 @@ def check_brute_force(fmt, M, K, N, seed, matmul, scale_mode="uniform"):
     return True
 
 
-@pytest.mark.parametrize("fmt", [Q.FMT_Q8_0, Q.FMT_Q4_0, Q.FMT_F16])
+@pytest.mark.parametrize("fmt", [Q.FMT_Q8_0, Q.FMT_Q4_0, Q.FMT_F16] + BIAS_FMTS)
 @pytest.mark.parametrize("shape", [(1, 32, 1), (3, 64, 2), (4, 64, 3), (2, 96, 1)])
 def test_brute_force(fmt, shape):
     M, K, N = shape
@@ -514,6 +599,67 @@ def _mut_q8_big_endian_scale(raw, M, K):
     return (d[..., None] * q).reshape(M, K)
 
 
+def _bias_fields(raw, fmt, M, K):
+    """Fields of a biased/5-bit block as the adopted reading places them."""
+    blk = Q._blocks(raw, fmt, M, K)
+    biased = fmt in (Q.FMT_Q4_1, Q.FMT_Q5_1)
+    at = 4 if biased else 2
+    qh = blk[..., at:at + 4] if fmt != Q.FMT_Q4_1 else None
+    qs = blk[..., (at + 4 if qh is not None else at):][..., :16]
+    return blk, qh, qs
+
+
+def _mut_q4_1_swapped(raw, M, K):
+    blk, _, qs = _bias_fields(raw, Q.FMT_Q4_1, M, K)
+    d, m = Q._scale64(blk, 2), Q._scale64(blk, 0)
+    return (d[..., None] * Q._nibbles(qs) + m[..., None]).reshape(M, K)
+
+
+def _mut_q4_1_minus_bias(raw, M, K):
+    blk, _, qs = _bias_fields(raw, Q.FMT_Q4_1, M, K)
+    d, m = Q._scale64(blk, 0), Q._scale64(blk, 2)
+    return (d[..., None] * Q._nibbles(qs) - m[..., None]).reshape(M, K)
+
+
+def _mut_q5_0_no_offset(raw, M, K):
+    blk, qh, qs = _bias_fields(raw, Q.FMT_Q5_0, M, K)
+    u = Q._nibbles(qs) + 16 * Q._high_bits(qh)
+    return (Q._scale64(blk)[..., None] * u).reshape(M, K)
+
+
+def _mut_q5_0_reversed_bits(raw, M, K):
+    blk, qh, qs = _bias_fields(raw, Q.FMT_Q5_0, M, K)
+    u = Q._nibbles(qs) + 16 * Q._high_bits(qh)[..., ::-1]
+    return (Q._scale64(blk)[..., None] * (u - 16)).reshape(M, K)
+
+
+def _mut_q5_0_big_endian_word(raw, M, K):
+    blk, qh, qs = _bias_fields(raw, Q.FMT_Q5_0, M, K)
+    u = Q._nibbles(qs) + 16 * Q._high_bits(np.ascontiguousarray(qh[..., ::-1]))
+    return (Q._scale64(blk)[..., None] * (u - 16)).reshape(M, K)
+
+
+def _mut_q5_0_interleaved_bits(raw, M, K):
+    # bit 2j -> element j, bit 2j+1 -> element j + 16
+    blk, qh, qs = _bias_fields(raw, Q.FMT_Q5_0, M, K)
+    bits = Q._high_bits(qh)
+    u = Q._nibbles(qs) + 16 * np.concatenate([bits[..., 0::2], bits[..., 1::2]], axis=-1)
+    return (Q._scale64(blk)[..., None] * (u - 16)).reshape(M, K)
+
+
+def _mut_q5_1_codes_first(raw, M, K):
+    # codes before the fifth-bit word
+    blk = Q._blocks(raw, Q.FMT_Q5_1, M, K)
+    u = Q._nibbles(blk[..., 4:20]) + 16 * Q._high_bits(blk[..., 20:24])
+    return (Q._scale64(blk, 0)[..., None] * u + Q._scale64(blk, 2)[..., None]).reshape(M, K)
+
+
+def _mut_q5_1_no_bias(raw, M, K):
+    blk, qh, qs = _bias_fields(raw, Q.FMT_Q5_1, M, K)
+    u = Q._nibbles(qs) + 16 * Q._high_bits(qh)
+    return (Q._scale64(blk, 0)[..., None] * u).reshape(M, K)
+
+
 def _mut_f16_ftz(raw, M, K):
     w = Q.unpack_f16(raw, M, K)
     w[np.abs(w) < 2.0 ** -14] = 0.0
@@ -550,7 +696,7 @@ def _pins_pass(dq, mm):
     """True when every pin accepts the given decode/matmul pair (an error counts as a rejection)."""
     try:
         ok = all(check_golden(load_golden(p), dq, mm) for p in GOLDEN_FILES)
-        for fmt in (Q.FMT_Q8_0, Q.FMT_Q4_0, Q.FMT_F16):
+        for fmt in (Q.FMT_Q8_0, Q.FMT_Q4_0, Q.FMT_F16, *BIAS_FMTS):
             ok = ok and check_brute_force(fmt, 32, 32, 2, 5, mm) and check_brute_force(fmt, 3, 64, 2, 8, mm)
         return ok
     except ValueError:
@@ -564,6 +710,14 @@ def _pins_pass(dq, mm):
     ("q8_scale_last", Q.FMT_Q8_0, _mut_q8_scale_last),
     ("q8_big_endian_scale", Q.FMT_Q8_0, _mut_q8_big_endian_scale),
     ("f16_flush_subnormals", Q.FMT_F16, _mut_f16_ftz),
+    ("q4_1_scale_bias_swapped", Q.FMT_Q4_1, _mut_q4_1_swapped),
+    ("q4_1_bias_subtracted", Q.FMT_Q4_1, _mut_q4_1_minus_bias),
+    ("q5_0_no_offset", Q.FMT_Q5_0, _mut_q5_0_no_offset),
+    ("q5_0_reversed_bits", Q.FMT_Q5_0, _mut_q5_0_reversed_bits),
+    ("q5_0_big_endian_word", Q.FMT_Q5_0, _mut_q5_0_big_endian_word),
+    ("q5_0_interleaved_bits", Q.FMT_Q5_0, _mut_q5_0_interleaved_bits),
+    ("q5_1_codes_first", Q.FMT_Q5_1, _mut_q5_1_codes_first),
+    ("q5_1_no_bias", Q.FMT_Q5_1, _mut_q5_1_no_bias),
 ])
 def test_mutated_unpack_is_caught(name, fmt, fn):
     dq = _dequant_with(fmt, fn)
