@@ -15,7 +15,7 @@ import os
 import torch
 
 __all__ = [
-    "QMM_F16", "QMM_Q4_0", "QMM_Q8_0", "QMM_VARIANT_AUTO", "QMM_VARIANT_VALU", "QMM_VARIANT_MFMA",
+    "QMM_F16", "QMM_Q4_0", "QMM_Q4_1", "QMM_Q5_0", "QMM_Q5_1", "QMM_Q8_0", "QMM_VARIANT_AUTO", "QMM_VARIANT_VALU", "QMM_VARIANT_MFMA",
     "QmmError", "lib_path", "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv",
     "qmm_gemv_variant", "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
     "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16", "qmm_rmsnorm_gemv", "qmm_rmsnorm_gate_up_silu",
@@ -23,7 +23,7 @@ __all__ = [
     "gemv", "get_rows", "expand_f16", "rmsnorm_gemv", "rmsnorm_gate_up_silu", "gemv_add", "gate_up_silu", "gemm", "gemm_gate_up_silu", "dequant",
 ]
 
-QMM_F16, QMM_Q4_0, QMM_Q8_0 = 1, 2, 8
+QMM_F16, QMM_Q4_0, QMM_Q4_1, QMM_Q5_0, QMM_Q5_1, QMM_Q8_0 = 1, 2, 3, 6, 7, 8
 QMM_VARIANT_AUTO, QMM_VARIANT_VALU, QMM_VARIANT_MFMA = 0, 1, 2
 QMM_ERR_ARG = -8
 

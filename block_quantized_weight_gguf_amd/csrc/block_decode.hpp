@@ -4,9 +4,11 @@
 // on consecutive addresses.  ("EdgeRunner Core Architecture", sections 1.3, 3.1 and
 // 3.2: Q8_0 = fp16 d + 32 int8 codes, w = d * q; Q4_0 = fp16 d + 16 bytes, byte j
 // holding weight j in its low nibble and weight j + 16 in its high nibble,
-// w = d * (n - 8).)  Quantised blocks are only 2-byte aligned, so their bytes are
-// read with 2-byte loads; F16 chunks are 8- or 16-byte aligned.  Every decoded value
-// is exact in fp32: an 11-bit scale times a code of at most 8 bits.
+// w = d * (n - 8); Q4_1, Q5_0, Q5_1 as laid out in qmm_common.hpp.)  Quantised blocks
+// are only 2-byte aligned, so their bytes are read with 2-byte loads; F16 chunks are
+// 8- or 16-byte aligned.  The unbiased formats decode exactly in fp32 (an 11-bit
+// scale times a code of at most 8 bits); the biased ones as fma(d, u, m), the exact
+// d * u + m rounded once.
 #pragma once
 
 #include "qmm_common.hpp"
@@ -44,16 +46,52 @@ __device__ __forceinline__ void decode_chunk_f32(const uint8_t* blk, int c, floa
                 w[2 * j + 1] = d * sbyte_to_float(h, 1);
             }
         } else {
+            using T = Nib<FMT>;
             const int first = C * c;                 // first weight of the chunk
-            const uint16_t* q = p + 1 + (first & 15) / 2;
+            const uint16_t* q = p + T::QS / 2 + (first & 15) / 2;
             const int sh = first >= 16 ? 4 : 0;      // high nibbles hold weights 16..31
+            uint32_t hb = 0;                         // fifth bits of the chunk, from bit 0
+            if constexpr (T::FIVE) hb = (p[T::QH / 2] | (static_cast<uint32_t>(p[T::QH / 2 + 1]) << 16)) >> first;
+            const float m = T::BIAS ? half_bits_to_float(p[1]) : 0.0f;
 #pragma unroll
             for (int j = 0; j < C / 2; ++j) {
                 const uint32_t h = static_cast<uint32_t>(q[j]) >> sh;
-                w[2 * j] = d * static_cast<float>(static_cast<int>(h & 15u) - 8);
-                w[2 * j + 1] = d * static_cast<float>(static_cast<int>((h >> 8) & 15u) - 8);
+                const int u0 = static_cast<int>((h & 15u) | (((hb >> (2 * j)) & 1u) << 4));
+                const int u1 = static_cast<int>(((h >> 8) & 15u) | (((hb >> (2 * j + 1)) & 1u) << 4));
+                if constexpr (T::BIAS) {
+                    w[2 * j] = fmaf(d, static_cast<float>(u0), m);
+                    w[2 * j + 1] = fmaf(d, static_cast<float>(u1), m);
+                } else {
+                    w[2 * j] = d * static_cast<float>(u0 - T::OFF);
+                    w[2 * j + 1] = d * static_cast<float>(u1 - T::OFF);
+                }
             }
         }
+    }
+}
+
+// The biased formats (Q4_1, Q5_1) to fp16: fp16 fma(d, u, m) rounds the exact
+// d * u + m once (u <= 31 is exact in fp16), which a round to fp32 and then to fp16
+// would not always do.
+template <int FMT, int C>
+__device__ __forceinline__ void decode_chunk_f16_biased(const uint8_t* blk, int c, _Float16 (&w)[C]) {
+    using T = Nib<FMT>;
+    static_assert(T::BIAS, "biased formats only");
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(blk);
+    const _Float16 d = __builtin_bit_cast(_Float16, p[0]);
+    const _Float16 m = __builtin_bit_cast(_Float16, p[1]);
+    const int first = C * c;
+    const uint16_t* q = p + T::QS / 2 + (first & 15) / 2;
+    const int sh = first >= 16 ? 4 : 0;
+    uint32_t hb = 0;
+    if constexpr (T::FIVE) hb = (p[T::QH / 2] | (static_cast<uint32_t>(p[T::QH / 2 + 1]) << 16)) >> first;
+#pragma unroll
+    for (int j = 0; j < C / 2; ++j) {
+        const uint32_t h = static_cast<uint32_t>(q[j]) >> sh;
+        const uint32_t u0 = (h & 15u) | (((hb >> (2 * j)) & 1u) << 4);
+        const uint32_t u1 = ((h >> 8) & 15u) | (((hb >> (2 * j + 1)) & 1u) << 4);
+        w[2 * j] = __builtin_fmaf16(d, static_cast<_Float16>(static_cast<int>(u0)), m);
+        w[2 * j + 1] = __builtin_fmaf16(d, static_cast<_Float16>(static_cast<int>(u1)), m);
     }
 }
 

@@ -3,8 +3,9 @@
 //
 // One thread per 32-weight block: the block's bytes are read with 2-byte loads
 // (blocks are only 2-byte aligned), decoded in registers, and written as eight
-// 16-byte stores.  Each decoded value is exact in fp32 (an 11-bit scale times a
-// code of at most 8 bits), so the output equals the float64 definition.
+// 16-byte stores.  Each decoded value is the float64 definition rounded once to
+// fp32 (exact for the unbiased formats: an 11-bit scale times a code of at most 8
+// bits; fma(d, u, m) for the biased ones).
 #include "block_decode.hpp"
 #include "qmm_internal.hpp"
 
@@ -29,6 +30,9 @@ hipError_t launch_dequant(int fmt, const void* W, float* out, int64_t M, int64_t
     switch (fmt) {
         case 8: hipLaunchKernelGGL(dequant_kernel<8>, dim3(grid), dim3(256), 0, s, w, out, nchunks); break;
         case 2: hipLaunchKernelGGL(dequant_kernel<2>, dim3(grid), dim3(256), 0, s, w, out, nchunks); break;
+        case 3: hipLaunchKernelGGL(dequant_kernel<3>, dim3(grid), dim3(256), 0, s, w, out, nchunks); break;
+        case 6: hipLaunchKernelGGL(dequant_kernel<6>, dim3(grid), dim3(256), 0, s, w, out, nchunks); break;
+        case 7: hipLaunchKernelGGL(dequant_kernel<7>, dim3(grid), dim3(256), 0, s, w, out, nchunks); break;
         default: hipLaunchKernelGGL(dequant_kernel<1>, dim3(grid), dim3(256), 0, s, w, out, nchunks); break;
     }
     return hipGetLastError();

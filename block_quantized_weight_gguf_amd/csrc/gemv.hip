@@ -13,7 +13,8 @@
 //   * K is walked in slices of 64 blocks (2048 weights).  Lane l always handles
 //     block l of the slice, for every row the wave owns: the activations of that
 //     block are read once from LDS and reused for all row units.
-//   * Q8_0 / Q4_0 blocks are 34 / 18 bytes, so a block is only 2-byte aligned.
+//   * Q8_0 / Q4_0 / Q5_0 blocks are 34 / 18 / 22 bytes, so a block is only 2-byte
+//     aligned (Q4_1 / Q5_1: 20 / 24 bytes).
 //     Each row slice is therefore copied to LDS with whole, coalesced 16-byte
 //     loads, and each lane then re-reads its own block from LDS at any byte
 //     offset (dword reads realigned with v_alignbyte).  F16 rows are 16-byte
@@ -233,6 +234,9 @@ void launch_gemv_sliced(int fmt, const void* W, const void* Wu, const float* x, 
                         int NT, int64_t chunks, int64_t row_begin, int ep, const DecodeEpi& epi, hipStream_t s) {
     if (fmt == 8) launch_fmt_any<8>(W, Wu, x, y, M, K, NT, chunks, row_begin, ep, epi, s);
     else if (fmt == 2) launch_fmt_any<2>(W, Wu, x, y, M, K, NT, chunks, row_begin, ep, epi, s);
+    else if (fmt == 3) launch_fmt_any<3>(W, Wu, x, y, M, K, NT, chunks, row_begin, ep, epi, s);
+    else if (fmt == 6) launch_fmt_any<6>(W, Wu, x, y, M, K, NT, chunks, row_begin, ep, epi, s);
+    else if (fmt == 7) launch_fmt_any<7>(W, Wu, x, y, M, K, NT, chunks, row_begin, ep, epi, s);
     else launch_fmt_any<1>(W, Wu, x, y, M, K, NT, chunks, row_begin, ep, epi, s);
 }
 

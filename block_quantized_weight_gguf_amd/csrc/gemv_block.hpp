@@ -9,6 +9,10 @@
 //   Q4_0: xor 0x88 maps each nibble n to n ^ 8; moved into the high half of a byte
 //         it reads as the signed byte 16 * (n - 8), so the same one-op convert gives
 //         the exact code; the scale is d / 16 (exact).
+//   Q5_0: the same with the fifth bit: (u ^ 16) << 3 reads as the signed byte
+//         8 * (u - 16); the scale is d / 8.
+//   Q4_1, Q5_1: the unsigned code u as an unsigned byte; per block and token the
+//         lane sums u x and x, and adds d * sum(u x) + m * sum(x).
 #pragma once
 
 #include "qmm_common.hpp"
@@ -17,6 +21,107 @@
 namespace qmm {
 
 constexpr int XS_STRIDE = 36;  // floats per block in the LDS copy of x (32 + 4 padding)
+
+// The fields of a Q4_1 / Q5_0 / Q5_1 block from LDS: scale, bias (biased formats),
+// the fifth-bit word (5-bit formats) and the four dwords of nibbles.
+template <int FMT>
+__device__ __forceinline__ void read_nib_block(const uint8_t* buf, int off, float& d, float& m, uint32_t& qh,
+                                               uint32_t (&cw)[4]) {
+    using T = Nib<FMT>;
+    d = half_bits_to_float(lds_read_u16(buf, off));
+    m = T::BIAS ? half_bits_to_float(lds_read_u16(buf, off + 2)) : 0.0f;
+    if constexpr (T::FIVE) {
+        uint32_t w[5];  // qh is followed directly by the nibbles
+        lds_read_dwords<5>(buf, off + T::QH, w);
+        qh = w[0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cw[i] = w[i + 1];
+    } else {
+        qh = 0;
+        lds_read_dwords<4>(buf, off + T::QS, cw);
+    }
+}
+
+// Code bytes of weights 4i..4i+3 (lo) and 16+4i..16+4i+3 (hi) of a nibble-format
+// block, from nibble dword cw = dword i and the fifth-bit word qh:
+//   Q5_0: signed bytes 8 (u - 16); Q4_1 / Q5_1: unsigned bytes u.
+template <int FMT>
+__device__ __forceinline__ void nib_code_bytes(uint32_t cw, uint32_t qh, int i, uint32_t& lo, uint32_t& hi) {
+    using T = Nib<FMT>;
+    lo = cw & 0x0F0F0F0Fu;
+    hi = (cw >> 4) & 0x0F0F0F0Fu;
+    if constexpr (T::FIVE) {
+        lo |= spread4(qh >> (4 * i)) << 4;
+        hi |= spread4(qh >> (16 + 4 * i)) << 4;
+    }
+    if constexpr (FMT == 6) {
+        lo = (lo ^ 0x10101010u) << 3;
+        hi = (hi ^ 0x10101010u) << 3;
+    }
+}
+
+// block_fma for Q4_1, Q5_0, Q5_1 (see the header comment for the code bytes).
+template <int FMT, int RU, int NT>
+__device__ __forceinline__ void block_fma_nib(const uint8_t* const (&buf)[RU], const int (&off)[RU],
+                                              const float* const (&xb)[NT], float (&acc)[RU][NT]) {
+    constexpr bool BIAS = Nib<FMT>::BIAS;
+    float bacc[RU][NT], sx[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) sx[n] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) bacc[u][n] = 0.0f;
+    float d[RU], m[RU];
+    uint32_t qh[RU], cw[RU][4];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        read_nib_block<FMT>(buf[u], off[u], d[u], m[u], qh[u], cw[u]);
+        if constexpr (FMT == 6) d[u] *= 0.125f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float4 xl[NT], xh[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            xl[n] = *reinterpret_cast<const float4*>(xb[n] + 4 * i);
+            xh[n] = *reinterpret_cast<const float4*>(xb[n] + 16 + 4 * i);
+            if constexpr (BIAS) sx[n] += ((xl[n].x + xl[n].y) + (xl[n].z + xl[n].w)) +
+                                         ((xh[n].x + xh[n].y) + (xh[n].z + xh[n].w));
+        }
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            uint32_t lo, hi;
+            nib_code_bytes<FMT>(cw[u][i], qh[u], i, lo, hi);
+            float c[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c[j] = (FMT == 6) ? sbyte_to_float(lo, j) : ubyte_to_float(lo, j);
+                c[4 + j] = (FMT == 6) ? sbyte_to_float(hi, j) : ubyte_to_float(hi, j);
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                float a = bacc[u][n];
+                a = fmaf(c[0], xl[n].x, a);
+                a = fmaf(c[1], xl[n].y, a);
+                a = fmaf(c[2], xl[n].z, a);
+                a = fmaf(c[3], xl[n].w, a);
+                a = fmaf(c[4], xh[n].x, a);
+                a = fmaf(c[5], xh[n].y, a);
+                a = fmaf(c[6], xh[n].z, a);
+                a = fmaf(c[7], xh[n].w, a);
+                bacc[u][n] = a;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            if constexpr (BIAS) acc[u][n] = fmaf(d[u], bacc[u][n], fmaf(m[u], sx[n], acc[u][n]));
+            else acc[u][n] = fmaf(d[u], bacc[u][n], acc[u][n]);
+        }
+}
 
 // buf[u]: 16-byte aligned LDS buffer of row unit u; off[u]: byte offset of the block in it.
 template <int FMT, int RU, int NT>
@@ -57,6 +162,9 @@ __device__ __forceinline__ void block_fma(const uint8_t* const (&buf)[RU], const
                 }
             }
         }
+    } else if constexpr (FMT != 2) {
+        block_fma_nib<FMT, RU, NT>(buf, off, xb, acc);
+        return;
     } else {
         uint32_t cw[RU][4];
 #pragma unroll
@@ -115,14 +223,19 @@ __device__ __forceinline__ void block_fma(const uint8_t* const (&buf)[RU], const
 //   Q8_0: u = q + 128 (xor 0x80) as the low byte under 0x64: v = 1024 + u, and
 //         w = d (v - 1152);
 //   Q4_0: the nibble n in bits 4..7 under 0x3C: v = 1 + n/64, and
-//         w = 64 d (v - 1.125).
+//         w = 64 d (v - 1.125);
+//   Q5_0: the 5-bit code u in bits 3..7 under 0x3C: v = 1 + u/128, and
+//         w = 128 d (v - 1.125);
+//   Q4_1, Q5_1: v as for Q4_0 / Q5_0 with offset 1: w = 64 d (v - 1) + m and
+//         128 d (v - 1) + m.
 // Both products v x~ are exact in fp32.  With
-//     p = sum_j v_j x~_j   and   c = sum_j v0 x~_j   (v0 = 1152 or 1.125),
+//     p = sum_j v_j x~_j   and   c = sum_j v0 x~_j   (v0 = 1152, 1.125 or 1),
 // accumulated by the same chain of dot2 steps in the same pair order, a block
 // contributes (d F) (p - c) 2^-s with F = 1 or 64.  Codes all equal to the offset
 // (q = 0, n = 8) therefore give exactly zero, and the cancellation costs at most
 // about 2^-24 * 16 * 2 * max(v0 / |v - v0|) ~ 3e-5 of sum |w x| (|v - v0| averages
 // 64 resp. 4/64), so |y - y_exact| <= (2^-11 + 4e-5) sum |w x|, inside the 2e-3 bound.
+// The biased formats add m c 2^-s (c = sum x~ there): the block's sum of x~ w.
 // Per block the LDS copy holds 16 dwords of fp16 pairs in the order the codes are
 // unpacked (see stage_x16), then c and 2^-s, padded to XS16 dwords so that the
 // lanes' 16-byte reads at a stride of XS16 dwords hit distinct banks.
@@ -141,8 +254,10 @@ __device__ __forceinline__ uint32_t sel13(uint32_t v, uint32_t k) { return __bui
 template <int FMT>
 struct DotCode {
     static constexpr uint32_t K = FMT == 8 ? 0x64646464u : 0x3C3C3C3Cu;    // high bytes
-    static constexpr uint32_t V0 = FMT == 8 ? 0x64806480u : 0x3C803C80u;   // offset code pair
-    static constexpr float F = FMT == 8 ? 1.0f : 64.0f;
+    static constexpr uint32_t V0 = FMT == 8                 ? 0x64806480u   // offset code pair
+                                   : (FMT == 2 || FMT == 6) ? 0x3C803C80u
+                                                            : 0x3C003C00u;
+    static constexpr float F = FMT == 8 ? 1.0f : (FMT == 2 || FMT == 3) ? 64.0f : 128.0f;
 };
 
 // v from another lane of the row, as selected by the DPP control CTRL (all lanes of
@@ -238,17 +353,25 @@ __device__ __forceinline__ void block_dot(const uint8_t* const (&buf)[RU], const
                                           const uint32_t* const (&xb)[NT], float (&acc)[RU][NT]) {
     constexpr int NDW = FMT == 8 ? 8 : 4;
     constexpr uint32_t KB = DotCode<FMT>::K;
+    constexpr bool BIAS = FMT != 8 && Nib<FMT>::BIAS;
+    constexpr bool FIVE = FMT != 8 && Nib<FMT>::FIVE;
     float p[RU][NT];
 #pragma unroll
     for (int u = 0; u < RU; ++u)
 #pragma unroll
         for (int n = 0; n < NT; ++n) p[u][n] = 0.0f;
-    float d[RU];
-    uint32_t cw[RU][NDW];
+    float d[RU], mb[RU];
+    uint32_t cw[RU][NDW], qh[RU];
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
-        d[u] = half_bits_to_float(lds_read_u16(buf[u], off[u]));
-        lds_read_dwords<NDW>(buf[u], off[u] + 2, cw[u]);
+        if constexpr (FMT == 8 || FMT == 2) {
+            d[u] = half_bits_to_float(lds_read_u16(buf[u], off[u]));
+            lds_read_dwords<NDW>(buf[u], off[u] + 2, cw[u]);
+            mb[u] = 0.0f;
+            qh[u] = 0;
+        } else {
+            read_nib_block<FMT>(buf[u], off[u], d[u], mb[u], qh[u], cw[u]);
+        }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -261,6 +384,10 @@ __device__ __forceinline__ void block_dot(const uint8_t* const (&buf)[RU], const
             if constexpr (FMT == 8) {
                 const uint32_t t0 = cw[u][2 * i] ^ 0x80808080u, t1 = cw[u][2 * i + 1] ^ 0x80808080u;
                 a0 = sel02(t0, KB), a1 = sel13(t0, KB), a2 = sel02(t1, KB), a3 = sel13(t1, KB);
+            } else if constexpr (FIVE) {  // 5-bit code in bits 3..7 of each byte
+                const uint32_t lo = ((cw[u][i] << 3) & 0x78787878u) | (spread4(qh[u] >> (4 * i)) << 7);
+                const uint32_t hi = ((cw[u][i] >> 1) & 0x78787878u) | (spread4(qh[u] >> (16 + 4 * i)) << 7);
+                a0 = sel02(lo, KB), a1 = sel13(lo, KB), a2 = sel02(hi, KB), a3 = sel13(hi, KB);
             } else {
                 const uint32_t lo = (cw[u][i] << 4) & 0xF0F0F0F0u, hi = cw[u][i] & 0xF0F0F0F0u;
                 a0 = sel02(lo, KB), a1 = sel13(lo, KB), a2 = sel02(hi, KB), a3 = sel13(hi, KB);
@@ -289,7 +416,10 @@ __device__ __forceinline__ void block_dot(const uint8_t* const (&buf)[RU], const
     for (int u = 0; u < RU; ++u) {
         const float dF = d[u] * DotCode<FMT>::F;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc[u][n] = fmaf((p[u][n] - cs[n]) * dF, inv[n], acc[u][n]);
+        for (int n = 0; n < NT; ++n) {
+            if constexpr (BIAS) acc[u][n] = fmaf(fmaf(mb[u], cs[n], (p[u][n] - cs[n]) * dF), inv[n], acc[u][n]);
+            else acc[u][n] = fmaf((p[u][n] - cs[n]) * dF, inv[n], acc[u][n]);
+        }
     }
 }
 

@@ -1,4 +1,5 @@
-// Streaming decode GEMV for the block formats (Q8_0, Q4_0), a few tokens per pass.
+// Streaming decode GEMV for the block formats (Q8_0, Q4_0, Q4_1, Q5_0, Q5_1), a few
+// tokens per pass.
 //
 // Single-token decode is bound by the weight stream ("EdgeRunner Core
 // Architecture", section 3.4 Tier 1 and section 15 item 2: the raw blocks are the
@@ -36,7 +37,7 @@ namespace qmm {
 template <int FMT>
 struct StreamGeom {
     static constexpr int BB = Fmt<FMT>::BB;
-    static constexpr int BPL = (FMT == 2) ? 2 : 1;            // blocks per lane per row slice
+    static constexpr int BPL = (FMT == 8) ? 1 : 2;            // blocks per lane per row slice
     static constexpr int SLICE = kWave * BPL;                  // blocks per K slice
     static constexpr int CPR = (SLICE * BB + 15) / 16 + 1;     // 16-byte chunks per row slice, incl. shift
     static constexpr int LPR = (CPR + kWave - 1) / kWave;      // loads per lane per row slice
@@ -320,6 +321,9 @@ int64_t launch_gemv_stream(int fmt, const void* W, const void* Wu, const float* 
                            int NT, int ep, const DecodeEpi& epi, hipStream_t s) {
     if (fmt == 8) return launch_fmt<8>(W, Wu, x, y, M, K, NT, ep, epi, s);
     if (fmt == 2) return launch_fmt<2>(W, Wu, x, y, M, K, NT, ep, epi, s);
+    if (fmt == 3) return launch_fmt<3>(W, Wu, x, y, M, K, NT, ep, epi, s);
+    if (fmt == 6) return launch_fmt<6>(W, Wu, x, y, M, K, NT, ep, epi, s);
+    if (fmt == 7) return launch_fmt<7>(W, Wu, x, y, M, K, NT, ep, epi, s);
     return 0;
 }
 

@@ -4,6 +4,12 @@
 //   Q8_0: [fp16 d][32 x int8 q]           34 bytes, weight = d * q
 //   Q4_0: [fp16 d][16 bytes of nibbles]   18 bytes, byte j: low nibble -> weight j,
 //                                          high nibble -> weight j + 16; weight = d * (n - 8)
+//   Q4_1: [fp16 d][fp16 m][16 bytes of nibbles]              20 bytes, weight = d * n + m
+//   Q5_0: [fp16 d][u32 qh][16 bytes of nibbles]              22 bytes, weight = d * (u - 16)
+//   Q5_1: [fp16 d][fp16 m][u32 qh][16 bytes of nibbles]      24 bytes, weight = d * u + m
+//         (the pages give the type ids, byte counts and the bias / 5-bit nature; the
+//         field order is GGUF's: nibbles in Q4_0's order, bit e of the little-endian
+//         word qh is the fifth bit of element e, u = n + 16 * bit)
 //   F16 : 32 halfs treated as a 64-byte "block" so every format shares the 32-wide K tiling.
 #pragma once
 
@@ -26,9 +32,35 @@ struct Fmt<2> {  // Q4_0
     static constexpr int BB = 18;
 };
 template <>
+struct Fmt<3> {  // Q4_1
+    static constexpr int BB = 20;
+};
+template <>
+struct Fmt<6> {  // Q5_0
+    static constexpr int BB = 22;
+};
+template <>
+struct Fmt<7> {  // Q5_1
+    static constexpr int BB = 24;
+};
+template <>
 struct Fmt<1> {  // F16
     static constexpr int BB = 64;
 };
+
+// Fields of the formats whose codes are (at least) nibbles in Q4_0's order.
+template <int FMT>
+struct Nib {
+    static constexpr bool BIAS = FMT == 3 || FMT == 7;        // weight = d * u + m
+    static constexpr bool FIVE = FMT == 6 || FMT == 7;        // fifth bits in qh
+    static constexpr int QH = BIAS ? 4 : 2;                   // byte offset of qh
+    static constexpr int QS = 2 + (BIAS ? 2 : 0) + (FIVE ? 4 : 0);  // byte offset of the nibbles
+    static constexpr int OFF = FMT == 2 ? 8 : FMT == 6 ? 16 : 0;    // code offset of the unbiased ones
+};
+
+// Bits 0..3 of x moved to bit 0 of bytes 0..3: the four copies of x made by the
+// multiply sit at bits 0, 7, 14 and 21 and do not overlap, so no carry crosses them.
+__device__ __forceinline__ uint32_t spread4(uint32_t x) { return ((x & 15u) * 0x00204081u) & 0x01010101u; }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 

@@ -8,9 +8,9 @@
 //     expand-then-GEMM prefill variant ("alpaca.swift", Design: quantised weights are
 //     expanded one matrix at a time into a scratch buffer for the tensor-op GEMMs;
 //     "EdgeRunner Core Architecture", section 3.4 Tier 2: GPU decode to float16).
-// A thread per chunk of 4 (fp32) or 8 (fp16) weights; decoded values are exact in fp32, and the fp16
-// expansion rounds each of them once, which is the value the fused GEMM feeds its
-// MFMAs.
+// A thread per chunk of 4 (fp32) or 8 (fp16) weights.  The fp16 expansion rounds
+// each exact weight once (which is the value the fused GEMM feeds its MFMAs): the
+// unbiased formats decode exactly in fp32 first, the biased ones use an fp16 fma.
 #include "block_decode.hpp"
 #include "qmm_internal.hpp"
 
@@ -46,6 +46,15 @@ __global__ __launch_bounds__(256) void expand_f16_kernel(const uint8_t* __restri
         uint4* dst = reinterpret_cast<uint4*>(out + e * 8);
         if constexpr (FMT == 1) {  // already half precision: a copy, bit for bit
             *dst = *reinterpret_cast<const uint4*>(W + e * 16);
+        } else if constexpr (Nib<FMT>::BIAS) {
+            _Float16 w[8];
+            decode_chunk_f16_biased<FMT, 8>(W + (e >> 2) * Fmt<FMT>::BB, static_cast<int>(e & 3), w);
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                h[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, w[2 * j])) |
+                       (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, w[2 * j + 1])) << 16);
+            *dst = make_uint4(h[0], h[1], h[2], h[3]);
         } else {
             float w[8];
             decode_chunk_f32<FMT, 8>(W + (e >> 2) * Fmt<FMT>::BB, static_cast<int>(e & 3), w);
@@ -74,6 +83,9 @@ hipError_t launch_get_rows(int fmt, const void* W, const int32_t* ids, float* ou
     switch (fmt) {
         case 8: hipLaunchKernelGGL(get_rows_kernel<8>, grid, dim3(256), 0, s, w, ids, out, M, nb, n); break;
         case 2: hipLaunchKernelGGL(get_rows_kernel<2>, grid, dim3(256), 0, s, w, ids, out, M, nb, n); break;
+        case 3: hipLaunchKernelGGL(get_rows_kernel<3>, grid, dim3(256), 0, s, w, ids, out, M, nb, n); break;
+        case 6: hipLaunchKernelGGL(get_rows_kernel<6>, grid, dim3(256), 0, s, w, ids, out, M, nb, n); break;
+        case 7: hipLaunchKernelGGL(get_rows_kernel<7>, grid, dim3(256), 0, s, w, ids, out, M, nb, n); break;
         default: hipLaunchKernelGGL(get_rows_kernel<1>, grid, dim3(256), 0, s, w, ids, out, M, nb, n); break;
     }
     return hipGetLastError();
@@ -87,6 +99,9 @@ hipError_t launch_expand_f16(int fmt, const void* W, void* out, int64_t M, int64
     switch (fmt) {
         case 8: hipLaunchKernelGGL(expand_f16_kernel<8>, dim3(grid), dim3(256), 0, s, w, o, nchunks); break;
         case 2: hipLaunchKernelGGL(expand_f16_kernel<2>, dim3(grid), dim3(256), 0, s, w, o, nchunks); break;
+        case 3: hipLaunchKernelGGL(expand_f16_kernel<3>, dim3(grid), dim3(256), 0, s, w, o, nchunks); break;
+        case 6: hipLaunchKernelGGL(expand_f16_kernel<6>, dim3(grid), dim3(256), 0, s, w, o, nchunks); break;
+        case 7: hipLaunchKernelGGL(expand_f16_kernel<7>, dim3(grid), dim3(256), 0, s, w, o, nchunks); break;
         default: hipLaunchKernelGGL(expand_f16_kernel<1>, dim3(grid), dim3(256), 0, s, w, o, nchunks); break;
     }
     return hipGetLastError();

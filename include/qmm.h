@@ -16,6 +16,18 @@
  *                  weight = d * (nibble - 8).
  *   QMM_Q8_0 = 8 : 34 bytes per 32 weights: fp16 scale d, then 32 int8 codes q;
  *                  weight = d * q.
+ *   QMM_Q4_1 = 3 : 20 bytes per 32 weights: fp16 scale d, fp16 bias m, then 16 bytes
+ *                  of nibbles in Q4_0's order; weight = d * n + m.
+ *   QMM_Q5_0 = 6 : 22 bytes per 32 weights: fp16 scale d, a 32-bit little-endian word
+ *                  qh whose bit e is the fifth bit of weight e, then 16 bytes of low
+ *                  nibbles in Q4_0's order; u = n + 16 * bit, weight = d * (u - 16).
+ *   QMM_Q5_1 = 7 : 24 bytes per 32 weights: fp16 d, fp16 m, qh, 16 bytes of nibbles;
+ *                  weight = d * u + m.
+ *   (Section 1.3 gives the ids 3, 6, 7 and section 3.1 the byte counts and the
+ *   scale/bias/5-bit nature; the field order within the block is GGUF's.)
+ *   The MFMA products (qmm_gemm, qmm_gemm_gate_up_silu and QMM_VARIANT_MFMA) take F16,
+ *   Q4_0 and Q8_0; the others return QMM_ERR_FMT for Q4_1 / Q5_0 / Q5_1, whose
+ *   prefill path is qmm_expand_f16 followed by qmm_gemm(QMM_F16, ...).
  *
  * Matrix convention (llama.cpp Metal end-to-end path, section 3.2 MUL_MAT: the
  * reduction length K is the contiguous weight dimension; the token count is the
@@ -65,13 +77,16 @@ extern "C" {
 typedef enum {
     QMM_F16 = 1,
     QMM_Q4_0 = 2,
+    QMM_Q4_1 = 3,
+    QMM_Q5_0 = 6,
+    QMM_Q5_1 = 7,
     QMM_Q8_0 = 8
 } qmm_fmt;
 
 typedef enum {
     QMM_OK = 0,
     QMM_ERR_NULL = -1,        /* a required pointer is NULL                        */
-    QMM_ERR_FMT = -2,         /* format id is not 1, 2 or 8                        */
+    QMM_ERR_FMT = -2,         /* format id not 1, 2, 3, 6, 7, 8 (or not taken here) */
     QMM_ERR_SHAPE = -3,       /* M, K, N or T out of range, or K % 32 != 0         */
     QMM_ERR_ALIGN = -4,       /* a pointer violates the alignment rule above       */
     QMM_ERR_OVERFLOW = -5,    /* a byte count does not fit in int64                */
@@ -94,7 +109,8 @@ int qmm_version(void);
 const char* qmm_strerror(int status);
 
 /*
- * Bytes per weight row: K/32*34 (Q8_0), K/32*18 (Q4_0), 2*K (F16).
+ * Bytes per weight row: K/32 blocks of 34 (Q8_0), 18 (Q4_0), 20 (Q4_1), 22 (Q5_0) or
+ * 24 (Q5_1) bytes; 2*K (F16).
  * ("EdgeRunner Core Architecture", section 3.1 bytes per block; section 3.2 block
  * count times 34.)  Returns a negative qmm_status for an unknown format, K < 1,
  * K % 32 != 0 or K > 2^31 - 1.  Host-only; makes no HIP call.
@@ -103,8 +119,8 @@ int64_t qmm_row_bytes(int fmt, int64_t K);
 
 /*
  * Decode a whole matrix to fp32: out[m][k] = W[m][k] (float32, row-major M x K).
- * Every decoded value d*q (or d*(n-8), or an f16) is exact in fp32, so the result
- * is bit-exact.  ("EdgeRunner Core Architecture", section 3.4, Tier 2: GPU decode
+ * Every decoded value d*q (or d*(n-8), d*(u-16), or an f16) is exact in fp32, so the
+ * result is bit-exact; the biased formats give d*u + m rounded once to fp32.  ("EdgeRunner Core Architecture", section 3.4, Tier 2: GPU decode
  * kernels that write a float buffer; "alpaca.swift", Numerical validation:
  * dequantisation is bit-exact.)  Not used by the product paths; it is the
  * check of the decoders and the building block of decode-then-GEMM prefill.
@@ -115,7 +131,7 @@ int qmm_dequant(int fmt, const void* W, float* out, int64_t M, int64_t K, void* 
  * Quantised row gather (embedding lookup): out[i][k] = W[ids[i]][k] as float32,
  * for i < n; out is n x K row-major.  ids is a device array of n int32 row
  * indices (4-byte aligned; repeats allowed); only the rows named are read.
- * Each value is exact in fp32, so the result is bit-exact.  An id outside
+ * Values as in qmm_dequant (bit-exact against the same rounding).  An id outside
  * [0, M) cannot be checked on the host (ids live on the device): its output row
  * is filled with NaN and nothing outside W is read.  n == 0 is a no-op that
  * returns QMM_OK.  out must be 16-byte aligned.

@@ -53,12 +53,14 @@ def test_version_and_strerror():
 
 @pytest.mark.parametrize("fmt,K,want", [
     (8, 576, 612), (2, 576, 324), (1, 576, 1152), (8, 4096, 4352), (2, 4096, 2304),
-    (8, 14336, 15232), (2, 14336, 8064), (1, 32, 64), (8, 32, 34), (2, 32, 18)])
+    (8, 14336, 15232), (2, 14336, 8064), (1, 32, 64), (8, 32, 34), (2, 32, 18),
+    (3, 32, 20), (6, 32, 22), (7, 32, 24), (3, 4096, 2560), (6, 4096, 2816), (7, 14336, 10752)])
 def test_row_bytes(fmt, K, want):
     assert qmm._lib.qmm_row_bytes(fmt, K) == want
 
 
-@pytest.mark.parametrize("fmt,K,want", [(3, 64, E_FMT), (0, 64, E_FMT), (8, 0, E_SHAPE), (8, 100, E_SHAPE),
+@pytest.mark.parametrize("fmt,K,want", [(4, 64, E_FMT), (5, 64, E_FMT), (9, 64, E_FMT), (0, 64, E_FMT),
+                                        (8, 0, E_SHAPE), (8, 100, E_SHAPE), (6, 48, E_SHAPE),
                                         (2, -32, E_SHAPE), (1, 48, E_SHAPE), (8, 2**31, E_SHAPE)])
 def test_row_bytes_errors(fmt, K, want):
     assert qmm._lib.qmm_row_bytes(fmt, K) == want
@@ -112,11 +114,11 @@ def test_get_rows_validation():
     A4 = A16 + 4
     assert L.qmm_get_rows(8, A16, A16, A16, 4, 64, 0, None) == OK  # empty gather: nothing enqueued
     assert L.qmm_get_rows(8, None, None, None, 4, 64, 0, None) == OK
-    assert L.qmm_get_rows(7, A16, A16, A16, 4, 64, 0, None) == E_FMT
+    assert L.qmm_get_rows(5, A16, A16, A16, 4, 64, 0, None) == E_FMT
     assert L.qmm_get_rows(8, None, A16, A16, 4, 64, 3, None) == E_NULL
     assert L.qmm_get_rows(8, A16, None, A16, 4, 64, 3, None) == E_NULL
     assert L.qmm_get_rows(8, A16, A16, None, 4, 64, 3, None) == E_NULL
-    assert L.qmm_get_rows(3, A16, A16, A16, 4, 64, 3, None) == E_FMT
+    assert L.qmm_get_rows(4, A16, A16, A16, 4, 64, 3, None) == E_FMT
     assert L.qmm_get_rows(8, A16, A16, A16, 4, 64, -1, None) == E_SHAPE
     assert L.qmm_get_rows(8, A16, A16, A16, 0, 64, 3, None) == E_SHAPE
     assert L.qmm_get_rows(2, A16, A16, A16, 4, 33, 3, None) == E_SHAPE
@@ -130,7 +132,7 @@ def test_expand_f16_validation():
     L = qmm._lib
     assert L.qmm_expand_f16(8, None, A16, 4, 64, None) == E_NULL
     assert L.qmm_expand_f16(8, A16, None, 4, 64, None) == E_NULL
-    assert L.qmm_expand_f16(6, A16, A16, 4, 64, None) == E_FMT
+    assert L.qmm_expand_f16(5, A16, A16, 4, 64, None) == E_FMT
     assert L.qmm_expand_f16(1, A16, A16, 4, 16, None) == E_SHAPE
     assert L.qmm_expand_f16(1, A16, A16, 0, 64, None) == E_SHAPE
     assert L.qmm_expand_f16(2, A16, A16 + 8, 4, 64, None) == E_ALIGN
@@ -186,13 +188,16 @@ def test_variant_choice():
         assert L.qmm_gemv_choose(fmt, 128256, 4096, 3) == 1
     assert L.qmm_gemv_choose(1, 4096, 4096, 4) == 2
     assert L.qmm_gemv_choose(1, 4096, 4096, 3) == 1
-    assert L.qmm_gemv_choose(7, 4096, 4096, 1) == E_FMT
+    assert L.qmm_gemv_choose(5, 4096, 4096, 1) == E_FMT
+    # Q4_1 / Q5_0 / Q5_1: the register-decode kernels at every token count.
+    for fmt in (3, 6, 7):
+        assert all(L.qmm_gemv_choose(fmt, 4096, 4096, n) == 1 for n in (1, 4, 5, 64, 4096))
     assert L.qmm_gemv_choose(8, 4096, 100, 1) == E_SHAPE
     assert L.qmm_gemv_variant(8, A16, A16, A16 + 1, 4, 64, 1, 9, None) == E_ALIGN
     assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, 9, None) == E_VAR
     assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, -1, None) == E_VAR
     assert L.qmm_gate_up_silu_variant(8, A16, None, A16, A16, 4, 64, 1, 1, None) == E_NULL
-    assert L.qmm_gate_up_silu_variant(3, A16, A16, A16, A16, 4, 64, 1, 1, None) == E_FMT
+    assert L.qmm_gate_up_silu_variant(5, A16, A16, A16, A16, 4, 64, 1, 1, None) == E_FMT
     assert L.qmm_gate_up_silu_variant(8, A16, A16, A16, A16, 4, 48, 1, 1, None) == E_SHAPE
     assert L.qmm_gate_up_silu_variant(8, A16, A16 + 8, A16, A16, 4, 64, 1, 1, None) == E_ALIGN
     assert L.qmm_gate_up_silu_variant(8, A16, A16, A16, A16, 4, 64, 1, 5, None) == E_VAR
@@ -202,3 +207,16 @@ def test_binding_raises():
     with pytest.raises(qmm.QmmError) as e:
         qmm.qmm_gemv(8, 0, A16, A16, 4, 64, 1, stream=0)
     assert e.value.status == E_NULL
+
+
+def test_mfma_products_reject_the_other_block_formats():
+    """qmm_gemm, qmm_gemm_gate_up_silu and the MFMA variant take F16 / Q4_0 / Q8_0;
+    Q4_1 / Q5_0 / Q5_1 are refused before any HIP call."""
+    L = qmm._lib
+    for fmt in (3, 6, 7):
+        assert L.qmm_gemm(fmt, A16, A16, A16, 256, 256, 256, None) == E_FMT
+        assert L.qmm_gemm_gate_up_silu(fmt, A16, A16, A16, A16, 256, 256, 256, None) == E_FMT
+        assert L.qmm_gemv_variant(fmt, A16, A16, A16, 256, 256, 8, 2, None) == E_FMT
+        assert L.qmm_gate_up_silu_variant(fmt, A16, A16, A16, A16, 256, 256, 8, 2, None) == E_FMT
+        # shape errors still come first
+        assert L.qmm_gemm(fmt, A16, A16, A16, 256, 100, 256, None) == E_SHAPE
