@@ -16,8 +16,9 @@ the decode step (reported baseline only).
 
 Further sections (timing only): the decode step with the RMSNorm prologues and
 residual epilogues fused in, expand-then-GEMM prefill against the fused GEMM,
-the quantised embedding row gather, small-batch decode, measured ceilings and a
-SmolLM2-135M-shaped decode step.
+the quantised embedding row gather, small-batch decode, measured ceilings, a
+SmolLM2-135M-shaped decode step, and the decode step and prefill route of the
+Q4_1 / Q5_0 / Q5_1 formats.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--suite PATH]
 """
@@ -48,7 +49,8 @@ def parse():
     p.add_argument("--no-smollm", action="store_true")
     p.add_argument("--no-small-batch", action="store_true")
     p.add_argument("--no-next", action="store_true",
-                   help="skip the fused-norm/residual step, expand-then-GEMM and row gather sections")
+                   help="skip the fused-norm/residual step, expand-then-GEMM, row gather and "
+                        "Q4_1/Q5_0/Q5_1 sections")
     p.add_argument("--suite", default=None, help="write per-kernel details as JSON to this path")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
@@ -75,8 +77,6 @@ class Timer:
 
 
 def decode_workload(torch, qmm, si):
-    L = si.LLAMA3_8B
-    H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
     dev = torch.device("cuda")
 
     host = {}
@@ -91,30 +91,121 @@ def decode_workload(torch, qmm, si):
 
     fmts = {}
     for fmt, base in ((si.FMT_Q8_0, 5000), (si.FMT_Q4_0, 6000)):
-        f = dict(
-            qkv=W(fmt, Q, H, base + 1), o=W(fmt, H, H, base + 2), g=W(fmt, I, H, base + 3),
-            u=W(fmt, I, H, base + 4), d=W(fmt, H, I, base + 5), lm=W(fmt, V, H, base + 6),
-            x=X(1, H, base + 7), x_host=si.activations(1, H, base + 7), y_qkv=torch.empty(Q, device=dev), y_o=torch.empty(H, device=dev),
-            h=torch.empty(I, device=dev), y_d=torch.empty(H, device=dev), logits=torch.empty(V, device=dev))
-        fmts[fmt] = f
-    rb = {fmt: (lambda K, fmt=fmt: qmm.qmm_row_bytes(fmt, K)) for fmt in fmts}
+        fmts[fmt] = decode_tensors(torch, si, fmt, base, W, X)
     launches = []  # (kernel key, part, bytes, callable)
     for fmt, f in fmts.items():
-        name = si.FMT_NAMES[fmt]
-        r = rb[fmt]
-        launches += [
-            (f"gemv_{name}", "qkv", Q * r(H) + 4 * H + 4 * Q,
-             lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["qkv"], f["x"], f["y_qkv"], Q, H, 1)),
-            (f"gemv_{name}", "o", H * r(H) + 4 * H + 4 * H,
-             lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["o"], f["x"], f["y_o"], H, H, 1)),
-            (f"gate_up_{name}", "gate_up", 2 * I * r(H) + 4 * H + 4 * I,
-             lambda f=f, fmt=fmt: qmm.qmm_gate_up_silu(fmt, f["g"], f["u"], f["x"], f["h"], I, H, 1)),
-            (f"gemv_{name}", "down", H * r(I) + 4 * I + 4 * H,
-             lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["d"], f["h"], f["y_d"], H, I, 1)),
-            (f"gemv_{name}", "lm_head", V * r(H) + 4 * H + 4 * V,
-             lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["lm"], f["x"], f["logits"], V, H, 1)),
-        ]
+        launches += decode_launches(qmm, si, fmt, f)
     return fmts, launches, host
+
+
+def decode_tensors(torch, si, fmt, base, W, X):
+    """Weights, input and outputs of the five 8B decode projections in one format."""
+    L = si.LLAMA3_8B
+    H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
+    dev = torch.device("cuda")
+    return dict(
+        qkv=W(fmt, Q, H, base + 1), o=W(fmt, H, H, base + 2), g=W(fmt, I, H, base + 3),
+        u=W(fmt, I, H, base + 4), d=W(fmt, H, I, base + 5), lm=W(fmt, V, H, base + 6),
+        x=X(1, H, base + 7), x_host=si.activations(1, H, base + 7), y_qkv=torch.empty(Q, device=dev),
+        y_o=torch.empty(H, device=dev), h=torch.empty(I, device=dev), y_d=torch.empty(H, device=dev),
+        logits=torch.empty(V, device=dev))
+
+
+def decode_launches(qmm, si, fmt, f):
+    """(kernel key, part, algorithmic bytes, callable) for each launch of the step."""
+    L = si.LLAMA3_8B
+    H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
+    name = si.FMT_NAMES[fmt]
+
+    def r(K):
+        return qmm.qmm_row_bytes(fmt, K)
+    launches = [
+        (f"gemv_{name}", "qkv", Q * r(H) + 4 * H + 4 * Q,
+         lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["qkv"], f["x"], f["y_qkv"], Q, H, 1)),
+        (f"gemv_{name}", "o", H * r(H) + 4 * H + 4 * H,
+         lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["o"], f["x"], f["y_o"], H, H, 1)),
+        (f"gate_up_{name}", "gate_up", 2 * I * r(H) + 4 * H + 4 * I,
+         lambda f=f, fmt=fmt: qmm.qmm_gate_up_silu(fmt, f["g"], f["u"], f["x"], f["h"], I, H, 1)),
+        (f"gemv_{name}", "down", H * r(I) + 4 * I + 4 * H,
+         lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["d"], f["h"], f["y_d"], H, I, 1)),
+        (f"gemv_{name}", "lm_head", V * r(H) + 4 * H + 4 * V,
+         lambda f=f, fmt=fmt: qmm.qmm_gemv(fmt, f["lm"], f["x"], f["logits"], V, H, 1)),
+    ]
+    return launches
+
+
+def more_formats(torch, qmm, si, steps, reps=10):
+    """Q4_1, Q5_0 and Q5_1 (the block formats beside Q8_0 / Q4_0): the same 8B decode
+    step (per-launch and whole-step HBM rate of the raw blocks + x + y), and their
+    prefill route, fp16 expansion followed by the F16 GEMM, at 14336 x 4096 with
+    T = 2048 (TFLOP/s = 2 T M K / time of both launches)."""
+    dev = torch.device("cuda")
+
+    def W(fmt, M, K, seed):
+        return torch.from_numpy(si.weights(fmt, M, K, seed)).to(dev)
+
+    def X(n, K, seed):
+        return torch.from_numpy(si.activations(n, K, seed)).to(dev)
+
+    out = {}
+    for fmt, base in ((si.FMT_Q4_1, 7000), (si.FMT_Q5_0, 8000), (si.FMT_Q5_1, 9000)):
+        f = decode_tensors(torch, si, fmt, base, W, X)
+        launches = decode_launches(qmm, si, fmt, f)
+        nbytes = float(sum(b for _, _, b, _ in launches))
+        for _ in range(3):
+            for _, _, _, fn in launches:
+                fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            for _, _, _, fn in launches:
+                fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        timer = Timer(torch)
+        for _ in range(steps):
+            for key, part, _, fn in launches:
+                timer.run(part, fn)
+        torch.cuda.synchronize()
+        per = {}
+        for _, part, b, _ in launches:
+            us = 1e3 * float(np.mean(timer.ms(part)))
+            per[part] = {"us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1), "bytes": int(b)}
+        res = {"step_us": round(ms * 1e3, 2), "step_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "step_bytes": int(nbytes), "launches": per}
+        M, K, T = 14336, 4096, 2048
+        W16 = torch.empty((M, K), dtype=torch.float16, device=dev)
+        Xh = torch.randn(T, K, device=dev).half()
+        Y = torch.empty((T, M), device=dev)
+        for _ in range(3):
+            qmm.qmm_expand_f16(fmt, f["g"], W16, M, K)
+            qmm.qmm_gemm(1, W16, Xh, Y, M, K, T)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            qmm.qmm_expand_f16(fmt, f["g"], W16, M, K)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_e = e0.elapsed_time(e1) / reps
+        e0.record()
+        for _ in range(reps):
+            qmm.qmm_expand_f16(fmt, f["g"], W16, M, K)
+            qmm.qmm_gemm(1, W16, Xh, Y, M, K, T)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_x = e0.elapsed_time(e1) / reps
+        rb = qmm.qmm_row_bytes(fmt, K)
+        res["prefill_expand_then_gemm"] = {
+            "M": M, "K": K, "T": T, "expand_us": round(ms_e * 1e3, 2),
+            "expand_GBps": round((M * rb + 2 * M * K) / (ms_e * 1e-3) / 1e9, 1),
+            "TFLOPs": round(2.0 * T * M * K / (ms_x * 1e-3) / 1e12, 1)}
+        out[si.FMT_NAMES[fmt]] = res
+        del f, launches, W16, Xh, Y
+        torch.cuda.empty_cache()
+    return out
 
 
 def prefill_cases(torch, qmm, si):
@@ -585,6 +676,7 @@ def main():
         line["fused_decode_step"] = fused_decode(torch, qmm, si, fmts, max(10, args.steps))
         line["expand_then_gemm"] = expand_gemm(torch, qmm, si)
         line["get_rows"] = get_rows_bench(torch, qmm, si)
+        line["more_formats"] = more_formats(torch, qmm, si, max(10, args.steps))
     if not (args.no_prefill or args.no_small_batch):
         line["ceilings"] = ceilings(torch)
     if not args.no_cpu:
