@@ -57,6 +57,18 @@ struct RawRow<2> {
     uint32_t w[9];  // two Q4_0 blocks: 36 bytes
 };
 template <>
+struct RawRow<3> {
+    uint32_t w[10];  // two Q4_1 blocks: 40 bytes
+};
+template <>
+struct RawRow<6> {
+    uint32_t w[11];  // two Q5_0 blocks: 44 bytes
+};
+template <>
+struct RawRow<7> {
+    uint32_t w[12];  // two Q5_1 blocks: 48 bytes
+};
+template <>
 struct RawRow<1> {
     uint4 w[8];  // 64 halfs
 };
@@ -93,11 +105,54 @@ __device__ __forceinline__ void load_raw(RawRow<FMT>& rr, const uint8_t* rowp, i
     }
 }
 
+// Byte i (a constant after unrolling) of the raw bytes held as dwords.
+template <int N>
+__device__ __forceinline__ uint32_t raw_byte(const uint32_t (&w)[N], int i) {
+    return (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+}
+
 // Decode one row's two blocks into 64 fp16 values fp16(w) and store them to LDS.
 template <int FMT>
 __device__ __forceinline__ void decode_store(const RawRow<FMT>& rr, _Float16* dst) {
     uint32_t o[32];
-    if constexpr (FMT == 1) {
+    if constexpr (FMT == 3 || FMT == 6 || FMT == 7) {
+        // Q4_1 / Q5_0 / Q5_1 (fields as in qmm_common.hpp), block b at byte b * BB.  The
+        // biased weights round once through an fp16 fma; Q5_0's d * (u - 16) is exact
+        // in fp32 and rounds once on the conversion.
+        using T = Nib<FMT>;
+        constexpr int BB = Fmt<FMT>::BB;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int base = b * BB;
+            const uint16_t dbits = static_cast<uint16_t>(raw_byte(rr.w, base) | (raw_byte(rr.w, base + 1) << 8));
+            const uint16_t mbits = static_cast<uint16_t>(raw_byte(rr.w, base + 2) | (raw_byte(rr.w, base + 3) << 8));
+            uint32_t qh = 0;
+            if constexpr (T::FIVE)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) qh |= raw_byte(rr.w, base + T::QH + i) << (8 * i);
+#pragma unroll
+            for (int e = 0; e < 32; e += 2) {
+                uint32_t u[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int el = e + t;
+                    const uint32_t byte = raw_byte(rr.w, base + T::QS + (el & 15));
+                    u[t] = ((el < 16 ? byte : byte >> 4) & 15u) | (((qh >> el) & 1u) << 4);
+                }
+                if constexpr (T::BIAS) {
+                    const _Float16 d = __builtin_bit_cast(_Float16, dbits), m = __builtin_bit_cast(_Float16, mbits);
+                    const _Float16 w0 = __builtin_fmaf16(d, static_cast<_Float16>(static_cast<int>(u[0])), m);
+                    const _Float16 w1 = __builtin_fmaf16(d, static_cast<_Float16>(static_cast<int>(u[1])), m);
+                    o[16 * b + e / 2] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, w0)) |
+                                        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, w1)) << 16);
+                } else {
+                    const float d = half_bits_to_float(dbits);
+                    o[16 * b + e / 2] = pack_half2(d * static_cast<float>(static_cast<int>(u[0]) - 16),
+                                                   d * static_cast<float>(static_cast<int>(u[1]) - 16));
+                }
+            }
+        }
+    } else if constexpr (FMT == 1) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             o[4 * i] = rr.w[i].x;
@@ -327,9 +382,14 @@ hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* 
         const int64_t tt = std::min(kMaxT, T - t);
         const void* Xp = static_cast<const char*>(X) + t * K * xe;
         float* Yp = Y + t * M;
-        if (fmt == 8) launch_f<8>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s);
-        else if (fmt == 2) launch_f<2>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s);
-        else launch_f<1>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s);
+        switch (fmt) {
+            case 8: launch_f<8>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
+            case 2: launch_f<2>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
+            case 3: launch_f<3>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
+            case 6: launch_f<6>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
+            case 7: launch_f<7>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
+            default: launch_f<1>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
+        }
     }
     return hipGetLastError();
 }

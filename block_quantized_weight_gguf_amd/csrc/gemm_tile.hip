@@ -391,7 +391,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
             if constexpr (!XF32) issue_x(Xn, min(k + 1, kend - 1));
             if constexpr (KK == 0) issue_w(Wn, min(k / KPS + 1, send - 1));
         }
-        constexpr int SH = FMT == 1 ? 0 : 8 * WS;
+        constexpr int SH = stage_shift<FMT>(WS);
         // a0 holds this step's first sub-step when it was decoded on the previous step
         // (second step of a block-format stage); otherwise decode it now.
         // (fp32 tokens skip the cross-step decode: their staging registers are live
@@ -691,11 +691,17 @@ bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, boo
     if (P) {
         if (fmt == 8) { QMM_TILE_CASE(8, true, P) }
         else if (fmt == 2) { QMM_TILE_CASE(2, true, P) }
+        else if (fmt == 3) { QMM_TILE_CASE(3, true, P) }
+        else if (fmt == 6) { QMM_TILE_CASE(6, true, P) }
+        else if (fmt == 7) { QMM_TILE_CASE(7, true, P) }
         else { QMM_TILE_CASE(1, true, P) }
         launch_splitk_reduce(P, Y, T, M, nsplit, gated, s);
     } else {
         if (fmt == 8) { QMM_TILE_CASE(8, false, Y) }
         else if (fmt == 2) { QMM_TILE_CASE(2, false, Y) }
+        else if (fmt == 3) { QMM_TILE_CASE(3, false, Y) }
+        else if (fmt == 6) { QMM_TILE_CASE(6, false, Y) }
+        else if (fmt == 7) { QMM_TILE_CASE(7, false, Y) }
         else { QMM_TILE_CASE(1, false, Y) }
     }
 #undef QMM_TILE_CASE

@@ -1,5 +1,5 @@
 // Small-batch decode GEMV on the matrix cores: y[n][m] = sum_k W[m][k] x[n][k] for a
-// few tokens (2..32), Q8_0 / Q4_0 weights, fp32 x rounded to fp16, fp32 accumulate.
+// few tokens (2..32), block-format weights, fp32 x rounded to fp16, fp32 accumulate.
 //
 // ("llama.cpp Metal ...", section 3.2 and P9: a batched mat-vec for a handful of
 // tokens, each weight read once and reused for every token; "EdgeRunner Core
@@ -309,12 +309,19 @@ static bool launch_gm_nj(const void* W, const void* Wu, const float* x, float* y
 
 bool launch_gemv_mfma(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
                       int64_t N, hipStream_t s) {
-    if (fmt != 8 && fmt != 2) return false;
+    if (fmt == 1) return false;
     if (K % 256 != 0 || N < 1 || N > 32) return false;
     // 32-bit lane offsets: 256 weight rows must span less than 2^31 bytes.
     if (K > (int64_t{1} << 20)) return false;
-    if (N <= 16) return fmt == 8 ? launch_gm_nj<8, 1>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<2, 1>(W, Wu, x, y, M, K, N, s);
-    return fmt == 8 ? launch_gm_nj<8, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<2, 2>(W, Wu, x, y, M, K, N, s);
+    const bool two = N > 16;
+    switch (fmt) {
+        case 8: return two ? launch_gm_nj<8, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<8, 1>(W, Wu, x, y, M, K, N, s);
+        case 2: return two ? launch_gm_nj<2, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<2, 1>(W, Wu, x, y, M, K, N, s);
+        case 3: return two ? launch_gm_nj<3, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<3, 1>(W, Wu, x, y, M, K, N, s);
+        case 6: return two ? launch_gm_nj<6, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<6, 1>(W, Wu, x, y, M, K, N, s);
+        case 7: return two ? launch_gm_nj<7, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<7, 1>(W, Wu, x, y, M, K, N, s);
+        default: return false;
+    }
 }
 
 }  // namespace qmm

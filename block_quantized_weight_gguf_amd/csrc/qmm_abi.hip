@@ -17,8 +17,6 @@ bool fmt_ok(int fmt) {
            fmt == QMM_Q8_0;
 }
 
-// Formats the MFMA kernels (small-batch GEMV and prefill GEMM) decode.
-bool mfma_fmt_ok(int fmt) { return fmt == QMM_F16 || fmt == QMM_Q4_0 || fmt == QMM_Q8_0; }
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
     // a, b >= 0
@@ -63,9 +61,9 @@ int from_hip(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 // at 4 tokens the MFMA kernel wins or ties from about 32 MB of weights (e.g. the Q4_0
 // LM head 82 vs 87 us) and loses on smaller matrices, whose two launches and
 // split-K cost more than the pass; at 2-3 tokens the VALU kernel wins everywhere.
-// F16 (sliced VALU kernel against the tiled GEMM): MFMA from 4 tokens.
+// F16 (sliced VALU kernel against the tiled GEMM): MFMA from 4 tokens.  Q4_1 / Q5_0 /
+// Q5_1 follow the Q8_0 / Q4_0 rule.
 int choose_variant(int fmt, int64_t wbytes, int64_t N) {
-    if (!mfma_fmt_ok(fmt)) return QMM_VARIANT_VALU;
     if (fmt == QMM_F16) return N >= 4 ? QMM_VARIANT_MFMA : QMM_VARIANT_VALU;
     if (N >= 5) return QMM_VARIANT_MFMA;
     if (N == 4 && wbytes >= (int64_t{32} << 20)) return QMM_VARIANT_MFMA;
@@ -82,9 +80,7 @@ const char* qmm_strerror(int status) {
     switch (status) {
         case QMM_OK: return "ok";
         case QMM_ERR_NULL: return "a required pointer is NULL";
-        case QMM_ERR_FMT:
-            return "unknown weight format (expected 1=F16, 2=Q4_0, 3=Q4_1, 6=Q5_0, 7=Q5_1, 8=Q8_0), or a format "
-                   "this product does not take";
+        case QMM_ERR_FMT: return "unknown weight format (expected 1=F16, 2=Q4_0, 3=Q4_1, 6=Q5_0, 7=Q5_1, 8=Q8_0)";
         case QMM_ERR_SHAPE: return "bad shape (need 1 <= M, K, N <= 2^31-1 and K % 32 == 0)";
         case QMM_ERR_ALIGN: return "misaligned pointer (W, x, X need 16 bytes; outputs 4 bytes)";
         case QMM_ERR_OVERFLOW: return "a byte count overflows int64";
@@ -148,7 +144,6 @@ int qmm_gemv_variant(int fmt, const void* W, const float* x, float* y, int64_t M
     auto s = static_cast<hipStream_t>(stream);
     if (variant == QMM_VARIANT_VALU) return from_hip(qmm::launch_gemv_valu(fmt, W, nullptr, x, y, M, K, N, s));
     if (variant == QMM_VARIANT_MFMA) {
-        if (!mfma_fmt_ok(fmt)) return QMM_ERR_FMT;
         // Up to 32 tokens: the weight-streaming MFMA GEMV; otherwise the tiled GEMM.
         if (qmm::launch_gemv_mfma(fmt, W, nullptr, x, y, M, K, N, s)) return from_hip(hipGetLastError());
         return from_hip(qmm::launch_gemm_mfma(fmt, W, nullptr, x, true, y, M, K, N, s));
@@ -170,7 +165,6 @@ int qmm_gate_up_silu_variant(int fmt, const void* Wg, const void* Wu, const floa
     auto s = static_cast<hipStream_t>(stream);
     if (variant == QMM_VARIANT_VALU) return from_hip(qmm::launch_gemv_valu(fmt, Wg, Wu, x, h, I, K, N, s));
     if (variant == QMM_VARIANT_MFMA) {
-        if (!mfma_fmt_ok(fmt)) return QMM_ERR_FMT;
         if (qmm::launch_gemv_mfma(fmt, Wg, Wu, x, h, I, K, N, s)) return from_hip(hipGetLastError());
         return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, x, true, h, I, K, N, s));
     }
@@ -227,7 +221,6 @@ int qmm_gemm(int fmt, const void* W, const void* X, float* Y, int64_t M, int64_t
     if (!W || !X || !Y) return QMM_ERR_NULL;
     int st = check_shape(fmt, M, K, T);
     if (st) return st;
-    if (!mfma_fmt_ok(fmt)) return QMM_ERR_FMT;
     if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
     return from_hip(qmm::launch_gemm_mfma(fmt, W, nullptr, X, false, Y, M, K, T, static_cast<hipStream_t>(stream)));
 }
@@ -237,7 +230,6 @@ int qmm_gemm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const void* X
     if (!Wg || !Wu || !X || !H) return QMM_ERR_NULL;
     int st = check_shape(fmt, I, K, T);
     if (st) return st;
-    if (!mfma_fmt_ok(fmt)) return QMM_ERR_FMT;
     if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(X, 16) || !aligned(H, 4)) return QMM_ERR_ALIGN;
     return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, X, false, H, I, K, T, static_cast<hipStream_t>(stream)));
 }

@@ -25,9 +25,7 @@
  *                  weight = d * u + m.
  *   (Section 1.3 gives the ids 3, 6, 7 and section 3.1 the byte counts and the
  *   scale/bias/5-bit nature; the field order within the block is GGUF's.)
- *   The MFMA products (qmm_gemm, qmm_gemm_gate_up_silu and QMM_VARIANT_MFMA) take F16,
- *   Q4_0 and Q8_0; the others return QMM_ERR_FMT for Q4_1 / Q5_0 / Q5_1, whose
- *   prefill path is qmm_expand_f16 followed by qmm_gemm(QMM_F16, ...).
+ *   Every entry point takes every format.
  *
  * Matrix convention (llama.cpp Metal end-to-end path, section 3.2 MUL_MAT: the
  * reduction length K is the contiguous weight dimension; the token count is the
@@ -86,7 +84,7 @@ typedef enum {
 typedef enum {
     QMM_OK = 0,
     QMM_ERR_NULL = -1,        /* a required pointer is NULL                        */
-    QMM_ERR_FMT = -2,         /* format id not 1, 2, 3, 6, 7, 8 (or not taken here) */
+    QMM_ERR_FMT = -2,         /* format id is not 1, 2, 3, 6, 7 or 8               */
     QMM_ERR_SHAPE = -3,       /* M, K, N or T out of range, or K % 32 != 0         */
     QMM_ERR_ALIGN = -4,       /* a pointer violates the alignment rule above       */
     QMM_ERR_OVERFLOW = -5,    /* a byte count does not fit in int64                */
@@ -243,8 +241,9 @@ int qmm_gemv_add(int fmt, const void* W, const float* x, const float* r, float* 
 
 /*
  * Prefill GEMM: Y[t][m] = sum_k W[m][k] * X[t][k], X fp16 (T x K), Y fp32 (T x M).
- * Weight blocks are decoded into fp16 LDS tiles, fp16(d*q) rounded to nearest
- * even, and fed to fp16 MFMA with fp32 accumulation.  ("alpaca.swift", Design and
+ * Weight blocks are decoded into fp16 MFMA operands, each exact weight (d*q, or
+ * d*u + m) rounded once to nearest even -- the values qmm_expand_f16 writes -- and
+ * fed to fp16 MFMA with fp32 accumulation.  ("alpaca.swift", Design and
  * Capabilities: prefill on the matrix hardware with half-precision activations;
  * Numerical validation: element-wise error bound proportional to sum |x w|.)
  */

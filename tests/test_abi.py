@@ -189,9 +189,10 @@ def test_variant_choice():
     assert L.qmm_gemv_choose(1, 4096, 4096, 4) == 2
     assert L.qmm_gemv_choose(1, 4096, 4096, 3) == 1
     assert L.qmm_gemv_choose(5, 4096, 4096, 1) == E_FMT
-    # Q4_1 / Q5_0 / Q5_1: the register-decode kernels at every token count.
+    # Q4_1 / Q5_0 / Q5_1 follow the Q8_0 / Q4_0 rule.
     for fmt in (3, 6, 7):
-        assert all(L.qmm_gemv_choose(fmt, 4096, 4096, n) == 1 for n in (1, 4, 5, 64, 4096))
+        assert [L.qmm_gemv_choose(fmt, 4096, 4096, n) for n in (1, 3, 4, 5, 64)] == [1, 1, 1, 2, 2]
+        assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == 2
     assert L.qmm_gemv_choose(8, 4096, 100, 1) == E_SHAPE
     assert L.qmm_gemv_variant(8, A16, A16, A16 + 1, 4, 64, 1, 9, None) == E_ALIGN
     assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, 9, None) == E_VAR
@@ -208,15 +209,3 @@ def test_binding_raises():
         qmm.qmm_gemv(8, 0, A16, A16, 4, 64, 1, stream=0)
     assert e.value.status == E_NULL
 
-
-def test_mfma_products_reject_the_other_block_formats():
-    """qmm_gemm, qmm_gemm_gate_up_silu and the MFMA variant take F16 / Q4_0 / Q8_0;
-    Q4_1 / Q5_0 / Q5_1 are refused before any HIP call."""
-    L = qmm._lib
-    for fmt in (3, 6, 7):
-        assert L.qmm_gemm(fmt, A16, A16, A16, 256, 256, 256, None) == E_FMT
-        assert L.qmm_gemm_gate_up_silu(fmt, A16, A16, A16, A16, 256, 256, 256, None) == E_FMT
-        assert L.qmm_gemv_variant(fmt, A16, A16, A16, 256, 256, 8, 2, None) == E_FMT
-        assert L.qmm_gate_up_silu_variant(fmt, A16, A16, A16, A16, 256, 256, 8, 2, None) == E_FMT
-        # shape errors still come first
-        assert L.qmm_gemm(fmt, A16, A16, A16, 256, 100, 256, None) == E_SHAPE

@@ -5,12 +5,16 @@
   than 24 bits, so this pins a single rounding); qmm_expand_f16 must equal the exact
   weights rounded once to fp16 (the tiny-bias golden block would round differently
   through fp32).  Hand-computed golden blocks go through both.
-* Decode products (register-decode kernels, the only ones these formats take):
+* Decode products on the register-decode kernels:
   plain GEMV at shapes that cover the streaming kernel (a K slice of 128 blocks, a
   partial slice, many row groups, 1..4 tokens per pass and a second pass), its
   fallback for the final row when the matrix size is not a multiple of 16 bytes, and
   the sliced kernel when x does not fit in LDS (K = 65536); the gated, RMSNorm and
   residual products; x = e_k returning the decoded column exactly.
+* MFMA products: the prefill GEMM on its tiled kernel (K % 256 == 0: 128- and
+  256-token tiles, split K, the gated epilogue) and on the generic one (other K),
+  with X = e_k returning fp16 of the exact weight bit for bit; the small-batch MFMA
+  GEMV (2..32 tokens, split K) and its tiled hand-off above 32 tokens.
 Outputs are poisoned with NaNs and followed by a guard band.
 """
 import os
@@ -29,7 +33,7 @@ from test_oracle import GOLDEN_FILES, load_golden
 pytestmark = pytest.mark.gpu
 FMTS = [si.FMT_Q4_1, si.FMT_Q5_0, si.FMT_Q5_1]
 FID = {si.FMT_Q4_1: "q4_1", si.FMT_Q5_0: "q5_0", si.FMT_Q5_1: "q5_1"}
-VALU = qmm.QMM_VARIANT_VALU
+VALU, MFMA = qmm.QMM_VARIANT_VALU, qmm.QMM_VARIANT_MFMA
 
 
 def _bits32(a):
@@ -212,3 +216,89 @@ def test_gemv_llama3_8b_down_sampled(fmt):
     rows = sample_rows(M, 64, 7902 + fmt)
     y_ref, S = oracle.matmul_ref(fmt, raw, x, M, K, rows=rows)
     check_linear(y[:, rows], y_ref, S, f"gemv 8B down fmt={fmt}")
+
+
+# ------------------------------------------------------------ MFMA products
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("M,K,T", [(1, 32, 1), (300, 256, 40), (256, 4096, 256), (513, 96, 300), (64, 4160, 17),
+                                   (130, 4096, 129), (300, 2816, 40), (64, 14336, 130)])
+def test_gemm(fmt, M, K, T):
+    """K % 256 == 0: the tiled kernel (2816 and 14336 split K over workgroups); other K:
+    the generic kernel."""
+    seed = 8000 + fmt * 1000 + M + K + T
+    mode = "gemm_wide" if T % 2 else "uniform"
+    raw = si.weights(fmt, M, K, seed, scale_mode=mode)
+    X = si.activations(T, K, seed + 1, dtype=np.float16)
+    announce(f"qmm_gemm fmt={fmt} M={M} K={K} T={T} seed={seed} mode={mode}")
+    buf = poisoned(T * M)
+    qmm.qmm_gemm(fmt, dev(raw), dev(X), buf, M, K, T)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, T * M)
+    y_ref, S = oracle.matmul_ref(fmt, raw, X, M, K)
+    check_linear(buf[:T * M].cpu().numpy().reshape(T, M), y_ref, S, f"gemm fmt={fmt} M={M} K={K} T={T}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("K", [4096, 4160])
+def test_gemm_one_hot_fp16(fmt, K):
+    """X = e_k gives the exact weight rounded once to fp16 (what qmm_expand_f16 writes),
+    on the tiled kernel (K = 4096) and the generic one (K = 4160)."""
+    M = 300
+    raw = si.weights(fmt, M, K, 8100 + fmt, scale_mode="gemm_wide")
+    cols = list(range(0, K, 97)) + [K - 1]
+    X = si.one_hot(len(cols), K, cols, dtype=np.float16)
+    announce(f"gemm one-hot fmt={fmt} K={K}")
+    Y = qmm.gemm(fmt, dev(raw), dev(X), M, K)
+    torch.cuda.synchronize()
+    H = oracle.expand_f16_ref(fmt, raw, M, K).astype(np.float64)
+    Yc = Y.cpu().numpy().astype(np.float64)
+    for t, c in enumerate(cols):
+        assert np.array_equal(Yc[t], H[:, c]), (t, c)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("I,K,T", [(128, 256, 64), (200, 4096, 300), (64, 96, 7), (130, 4096, 9)])
+def test_gemm_gate_up_silu(fmt, I, K, T):
+    seed = 8200 + fmt * 100 + I + K + T
+    rg, ru = si.weights(fmt, I, K, seed), si.weights(fmt, I, K, seed + 1)
+    X = si.activations(T, K, seed + 2, dtype=np.float16)
+    announce(f"qmm_gemm_gate_up_silu fmt={fmt} I={I} K={K} T={T}")
+    buf = poisoned(T * I)
+    qmm.qmm_gemm_gate_up_silu(fmt, dev(rg), dev(ru), dev(X), buf, I, K, T)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, T * I)
+    h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, X, I, K)
+    check_swiglu(buf[:T * I].cpu().numpy().reshape(T, I), h_ref, g, u, Sg, Su, f"gemm gate_up fmt={fmt}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("M,K,N", [(300, 2048, 5), (1000, 4096, 17), (33, 256, 32), (513, 14336, 9),
+                                   (257, 2048, 128)])
+def test_gemv_mfma(fmt, M, K, N):
+    """2..32 tokens: the weight-streaming MFMA GEMV; 128: the tiled GEMM on fp32 x."""
+    seed = 8300 + fmt * 100 + M + K + N
+    raw = si.weights(fmt, M, K, seed, scale_mode="gemm_wide")
+    x = si.activations(N, K, seed + 1)
+    announce(f"gemv mfma fmt={fmt} M={M} K={K} N={N} seed={seed}")
+    buf = poisoned(N * M)
+    qmm.qmm_gemv_variant(fmt, dev(raw), dev(x), buf, M, K, N, MFMA)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, N * M)
+    # x is rounded to fp16 inside the MFMA kernels: the oracle takes the same inputs.
+    y_ref, S = oracle.matmul_ref(fmt, raw, x.astype(np.float16), M, K)
+    check_linear(buf[:N * M].cpu().numpy().reshape(N, M), y_ref, S, f"gemv mfma fmt={fmt} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("I,K,N", [(300, 4096, 3), (1000, 4096, 8)])
+def test_gate_up_silu_mfma(fmt, I, K, N):
+    seed = 8400 + fmt * 100 + I + K + N
+    rg, ru = si.weights(fmt, I, K, seed), si.weights(fmt, I, K, seed + 1)
+    x = si.activations(N, K, seed + 2)
+    announce(f"gate_up_silu mfma fmt={fmt} I={I} K={K} N={N}")
+    buf = poisoned(N * I)
+    qmm.qmm_gate_up_silu_variant(fmt, dev(rg), dev(ru), dev(x), buf, I, K, N, MFMA)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, N * I)
+    h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, x.astype(np.float16), I, K)
+    check_swiglu(buf[:N * I].cpu().numpy().reshape(N, I), h_ref, g, u, Sg, Su, "gate_up_silu mfma")
