@@ -136,9 +136,9 @@ def decode_launches(qmm, si, fmt, f):
 
 def more_formats(torch, qmm, si, steps, reps=10):
     """Q4_1, Q5_0 and Q5_1 (the block formats beside Q8_0 / Q4_0): the same 8B decode
-    step (per-launch and whole-step HBM rate of the raw blocks + x + y), and their
-    prefill route, fp16 expansion followed by the F16 GEMM, at 14336 x 4096 with
-    T = 2048 (TFLOP/s = 2 T M K / time of both launches)."""
+    step (per-launch and whole-step HBM rate of the raw blocks + x + y), and prefill
+    at 14336 x 4096 with T = 128 and 2048: the fused GEMM, and fp16 expansion followed
+    by the F16 GEMM (TFLOP/s = 2 T M K / time)."""
     dev = torch.device("cuda")
 
     def W(fmt, M, K, seed):
@@ -176,34 +176,36 @@ def more_formats(torch, qmm, si, steps, reps=10):
         res = {"step_us": round(ms * 1e3, 2), "step_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                "step_bytes": int(nbytes), "launches": per}
-        M, K, T = 14336, 4096, 2048
+        M, K = 14336, 4096
         W16 = torch.empty((M, K), dtype=torch.float16, device=dev)
-        Xh = torch.randn(T, K, device=dev).half()
-        Y = torch.empty((T, M), device=dev)
-        for _ in range(3):
-            qmm.qmm_expand_f16(fmt, f["g"], W16, M, K)
-            qmm.qmm_gemm(1, W16, Xh, Y, M, K, T)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            qmm.qmm_expand_f16(fmt, f["g"], W16, M, K)
-        e1.record()
-        torch.cuda.synchronize()
-        ms_e = e0.elapsed_time(e1) / reps
-        e0.record()
-        for _ in range(reps):
-            qmm.qmm_expand_f16(fmt, f["g"], W16, M, K)
-            qmm.qmm_gemm(1, W16, Xh, Y, M, K, T)
-        e1.record()
-        torch.cuda.synchronize()
-        ms_x = e0.elapsed_time(e1) / reps
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ms_e = timed(lambda: qmm.qmm_expand_f16(fmt, f["g"], W16, M, K))
         rb = qmm.qmm_row_bytes(fmt, K)
-        res["prefill_expand_then_gemm"] = {
-            "M": M, "K": K, "T": T, "expand_us": round(ms_e * 1e3, 2),
-            "expand_GBps": round((M * rb + 2 * M * K) / (ms_e * 1e-3) / 1e9, 1),
-            "TFLOPs": round(2.0 * T * M * K / (ms_x * 1e-3) / 1e12, 1)}
+        pf = {"M": M, "K": K, "expand_us": round(ms_e * 1e3, 2),
+              "expand_GBps": round((M * rb + 2 * M * K) / (ms_e * 1e-3) / 1e9, 1), "T": []}
+        for T in (128, 2048):
+            Xh = torch.randn(T, K, device=dev).half()
+            Y = torch.empty((T, M), device=dev)
+            fl = 2.0 * T * M * K
+            ms_f = timed(lambda: qmm.qmm_gemm(fmt, f["g"], Xh, Y, M, K, T))
+            ms_x = timed(lambda: (qmm.qmm_expand_f16(fmt, f["g"], W16, M, K), qmm.qmm_gemm(1, W16, Xh, Y, M, K, T)))
+            pf["T"].append({"T": T, "fused_TFLOPs": round(fl / (ms_f * 1e-3) / 1e12, 1),
+                            "expand_then_gemm_TFLOPs": round(fl / (ms_x * 1e-3) / 1e12, 1)})
+            del Xh, Y
+        res["prefill"] = pf
         out[si.FMT_NAMES[fmt]] = res
-        del f, launches, W16, Xh, Y
+        del f, launches, W16
         torch.cuda.empty_cache()
     return out
 

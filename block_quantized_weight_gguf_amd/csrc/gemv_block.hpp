@@ -224,15 +224,14 @@ __device__ __forceinline__ void block_fma(const uint8_t* const (&buf)[RU], const
 //         w = d (v - 1152);
 //   Q4_0: the nibble n in bits 4..7 under 0x3C: v = 1 + n/64, and
 //         w = 64 d (v - 1.125);
-//   Q5_0: the 5-bit code u in bits 3..7 under 0x3C: v = 1 + u/128, and
-//         w = 128 d (v - 1.125);
-//   Q4_1, Q5_1: v as for Q4_0 / Q5_0 with offset 1: w = 64 d (v - 1) + m and
-//         128 d (v - 1) + m.
+//   Q5_0: the nibble as for Q4_0 and the fifth bit h in bit 0 of the high byte,
+//         0x3C | h: v = 1 + h/4 + n/64 = 1 + u/64, and w = 64 d (v - 1.25);
+//   Q4_1, Q5_1: v as for Q4_0 / Q5_0, with offset 1: w = 64 d (v - 1) + m.
 // Both products v x~ are exact in fp32.  With
-//     p = sum_j v_j x~_j   and   c = sum_j v0 x~_j   (v0 = 1152, 1.125 or 1),
+//     p = sum_j v_j x~_j   and   c = sum_j v0 x~_j   (v0 = 1152, 1.125, 1.25 or 1),
 // accumulated by the same chain of dot2 steps in the same pair order, a block
 // contributes (d F) (p - c) 2^-s with F = 1 or 64.  Codes all equal to the offset
-// (q = 0, n = 8) therefore give exactly zero, and the cancellation costs at most
+// (q = 0, n = 8, u = 16) therefore give exactly zero, and the cancellation costs at most
 // about 2^-24 * 16 * 2 * max(v0 / |v - v0|) ~ 3e-5 of sum |w x| (|v - v0| averages
 // 64 resp. 4/64), so |y - y_exact| <= (2^-11 + 4e-5) sum |w x|, inside the 2e-3 bound.
 // The biased formats add m c 2^-s (c = sum x~ there): the block's sum of x~ w.
@@ -254,10 +253,11 @@ __device__ __forceinline__ uint32_t sel13(uint32_t v, uint32_t k) { return __bui
 template <int FMT>
 struct DotCode {
     static constexpr uint32_t K = FMT == 8 ? 0x64646464u : 0x3C3C3C3Cu;    // high bytes
-    static constexpr uint32_t V0 = FMT == 8                 ? 0x64806480u   // offset code pair
-                                   : (FMT == 2 || FMT == 6) ? 0x3C803C80u
-                                                            : 0x3C003C00u;
-    static constexpr float F = FMT == 8 ? 1.0f : (FMT == 2 || FMT == 3) ? 64.0f : 128.0f;
+    static constexpr uint32_t V0 = FMT == 8   ? 0x64806480u   // offset code pair
+                                   : FMT == 2 ? 0x3C803C80u
+                                   : FMT == 6 ? 0x3D003D00u
+                                              : 0x3C003C00u;
+    static constexpr float F = FMT == 8 ? 1.0f : 64.0f;
 };
 
 // v from another lane of the row, as selected by the DPP control CTRL (all lanes of
@@ -384,10 +384,13 @@ __device__ __forceinline__ void block_dot(const uint8_t* const (&buf)[RU], const
             if constexpr (FMT == 8) {
                 const uint32_t t0 = cw[u][2 * i] ^ 0x80808080u, t1 = cw[u][2 * i + 1] ^ 0x80808080u;
                 a0 = sel02(t0, KB), a1 = sel13(t0, KB), a2 = sel02(t1, KB), a3 = sel13(t1, KB);
-            } else if constexpr (FIVE) {  // 5-bit code in bits 3..7 of each byte
-                const uint32_t lo = ((cw[u][i] << 3) & 0x78787878u) | (spread4(qh[u] >> (4 * i)) << 7);
-                const uint32_t hi = ((cw[u][i] >> 1) & 0x78787878u) | (spread4(qh[u] >> (16 + 4 * i)) << 7);
-                a0 = sel02(lo, KB), a1 = sel13(lo, KB), a2 = sel02(hi, KB), a3 = sel13(hi, KB);
+            } else if constexpr (FIVE) {
+                // Nibbles as for Q4_0; the high byte of weight j's half is 0x3C | h_j, one
+                // word per four weights, and the byte selectors pair byte j with byte j.
+                const uint32_t lo = (cw[u][i] << 4) & 0xF0F0F0F0u, hi = cw[u][i] & 0xF0F0F0F0u;
+                const uint32_t hl = spread4(qh[u] >> (4 * i)) | KB, hh = spread4(qh[u] >> (16 + 4 * i)) | KB;
+                a0 = __builtin_amdgcn_perm(hl, lo, 0x06020400u), a1 = __builtin_amdgcn_perm(hl, lo, 0x07030501u);
+                a2 = __builtin_amdgcn_perm(hh, hi, 0x06020400u), a3 = __builtin_amdgcn_perm(hh, hi, 0x07030501u);
             } else {
                 const uint32_t lo = (cw[u][i] << 4) & 0xF0F0F0F0u, hi = cw[u][i] & 0xF0F0F0F0u;
                 a0 = sel02(lo, KB), a1 = sel13(lo, KB), a2 = sel02(hi, KB), a3 = sel13(hi, KB);

@@ -1,5 +1,5 @@
-// DMA-fed streaming decode GEMV for the block formats (Q8_0, Q4_0) with 16-byte
-// aligned rows (K % 256 == 0), a few tokens per pass.
+// DMA-fed streaming decode GEMV for the block formats (Q8_0, Q4_0, Q4_1, Q5_0, Q5_1)
+// with 16-byte aligned rows (K % 256 == 0), a few tokens per pass.
 //
 // Single-token decode is bound by the weight stream ("EdgeRunner Core
 // Architecture", section 3.4 Tier 1 and section 15 item 2: the raw blocks are the
@@ -11,10 +11,12 @@
 //     once as block-scaled fp16 pairs, as in the register-staged streaming kernel;
 //     after that the waves never synchronise again.
 //   * A task is R rows (2R row units when gated: R gate rows and the same R up
-//     rows) x one K slice of 64 * BPL blocks (BPL = 1 for Q8_0, 2 for Q4_0: 2176
-//     and 2304 bytes, both whole 16-byte chunks because rows are 16-byte aligned).
-//     A row unit's slice moves with three wave-wide DMA instructions (two of
-//     16 bytes per lane, one of 4 bytes per lane: 2304 bytes).  Each uses a
+//     rows) x one K slice of 64 * BPL blocks (BPL = 1 for Q8_0, 2 for the nibble
+//     formats: Q8_0 2176, Q4_0 2304, Q4_1 2560, Q5_0 2816, Q5_1 3072 bytes, all
+//     whole 16-byte chunks because rows are 16-byte aligned).  A row unit's slice
+//     moves with three wave-wide DMA instructions (Q8_0, Q4_0: two of 16 bytes per
+//     lane and one of 4 bytes per lane, 2304 bytes; the others: three of 16 bytes
+//     per lane, 3072 bytes).  Each uses a
 //     buffer resource that covers exactly that slice, so lanes past its end (and
 //     tasks past the end of the list, and rows past M) read zeros without touching
 //     memory; every task therefore issues the same number of DMA instructions and
@@ -31,7 +33,6 @@
 
 namespace qmm {
 
-constexpr int DG_SLOT = 2304;  // bytes per row unit and slot: 2 x 1024 (16-byte DMA) + 256 (4-byte DMA)
 constexpr int DG_NI = 3;       // DMA instructions per row unit and task
 constexpr int DG_PAD = 16;     // slack after each slot array (block reads may touch 4 bytes past a slice)
 constexpr int DG_GMAX = 4;     // EP_RES: row groups per wave whose residuals are read before the loop
@@ -39,18 +40,22 @@ constexpr int DG_GMAX = 4;     // EP_RES: row groups per wave whose residuals ar
 template <int FMT>
 struct DmaGeom {
     static constexpr int BB = Fmt<FMT>::BB;
-    static constexpr int BPL = (FMT == 2) ? 2 : 1;  // blocks per lane per row slice
+    static constexpr int BPL = (FMT == 8) ? 1 : 2;  // blocks per lane per row slice
     static constexpr int SLICE = kWave * BPL;       // blocks per K slice
-    static_assert(SLICE * BB <= DG_SLOT, "slice must fit a slot");
+    // Bytes per row unit and slot; the third DMA instruction moves 4 bytes per lane
+    // (Q8_0, Q4_0: 2 x 1024 + 256) or 16 (the others: 3 x 1024).
+    static constexpr bool WIDE = SLICE * BB > 2304;
+    static constexpr int SLOT = WIDE ? 3072 : 2304;
+    static_assert(SLICE * BB <= SLOT, "slice must fit a slot");
     static_assert((8 * BB) % 16 == 0, "8-block multiples are whole 16-byte chunks");
 };
 
 // LDS of one instance: S ring stages of WAVES * RU slots, the norm partials, and
 // XCAP bytes left for x (NT tokens x K / 32 blocks x XS16 dwords).
-template <int NT, int RU, int WAVES, int S>
+template <int FMT, int NT, int RU, int WAVES, int S>
 struct DmaLds {
     static constexpr int kMax = 160 * 1024;
-    static constexpr int STAGE = WAVES * RU * DG_SLOT + DG_PAD;
+    static constexpr int STAGE = WAVES * RU * DmaGeom<FMT>::SLOT + DG_PAD;
     static constexpr int RING = 2 * STAGE + (S > 2 ? STAGE : 16) + (S > 3 ? STAGE : 16);
     static constexpr int XCAP = (kMax - RING - WAVES * NT * 4) / 16 * 16;
     static_assert(XCAP >= 16 * XS16 * 4, "room for x");
@@ -114,10 +119,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
                                                                int M, int K, int64_t ldx, int64_t ldy, DecodeEpi epi) {
     static_assert(S >= 2 && S <= 4, "ring depth");
     using G = DmaGeom<FMT>;
-    constexpr int BB = G::BB, BPL = G::BPL, SLICE = G::SLICE;
+    constexpr int BB = G::BB, BPL = G::BPL, SLICE = G::SLICE, SLOT = G::SLOT;
     constexpr int RU = GATED ? 2 * R : R;
     constexpr int NI = RU * DG_NI;         // DMA instructions per task
-    constexpr int WS = WAVES * RU * DG_SLOT;  // bytes of one ring stage (all waves)
+    constexpr int WS = WAVES * RU * SLOT;  // bytes of one ring stage (all waves)
     __shared__ __align__(16) uint8_t RS0[WS + DG_PAD];
     __shared__ __align__(16) uint8_t RS1[WS + DG_PAD];
     __shared__ __align__(16) uint8_t RS2[S > 2 ? WS + DG_PAD : 16];
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
     // x and the norm partials take the rest of the CU's LDS, also as static arrays:
     // the compiler treats dynamic LDS as possibly written by any DMA in flight and
     // would wait for all of them before every read of x.
-    using L = DmaLds<NT, RU, WAVES, S>;
+    using L = DmaLds<FMT, NT, RU, WAVES, S>;
     __shared__ __align__(16) uint32_t xs[L::XCAP / 4];
     __shared__ float red[WAVES * NT];
 
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
     const int wid = blockIdx.x * WAVES + wave;
     const int my_groups = wid < ngroups ? (ngroups - 1 - wid) / nw + 1 : 0;
     const int ntask = my_groups * ns;  // the host keeps this below 2^31
-    const int wslot = wave * RU * DG_SLOT;  // this wave's part of a stage
+    const int wslot = wave * RU * SLOT;  // this wave's part of a stage
 
     // DMA of the task at cursor c into stage array `stage`; tasks past the list read zeros.
     const uint32_t v16 = 16u * static_cast<uint32_t>(lane);
@@ -157,10 +162,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
             const uint8_t* wb = (GATED && u >= R) ? Wu : Wg;
             const __amdgpu_buffer_rsrc_t r =
                 make_rsrc(wb + (ok ? row * rb + static_cast<int64_t>(s0) * BB : 0), ok ? sbytes : 0);
-            QMM_L3 uint8_t* d = (QMM_L3 uint8_t*)(stage + wslot + u * DG_SLOT);
+            QMM_L3 uint8_t* d = (QMM_L3 uint8_t*)(stage + wslot + u * SLOT);
             dma16<kCacheNT>(r, v16, 0, d);
             dma16<kCacheNT>(r, v16 + 1024u, 0, d + 1024);
-            dma4<kCacheNT>(r, v4, d + 2048);
+            if constexpr (G::WIDE) dma16<kCacheNT>(r, v16 + 2048u, 0, d + 2048);
+            else dma4<kCacheNT>(r, v4, d + 2048);
         }
     };
 
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
             const int sb = min(SLICE, nb - s0);
             const uint8_t* buf[RU];
 #pragma unroll
-            for (int u = 0; u < RU; ++u) buf[u] = stage + wslot + u * DG_SLOT;
+            for (int u = 0; u < RU; ++u) buf[u] = stage + wslot + u * SLOT;
 #pragma unroll
             for (int b = 0; b < BPL; ++b) {
                 const int blk = lane + kWave * b;
@@ -324,7 +330,7 @@ static int64_t dma_launch(const void* W, const void* Wu, const float* x, float* 
                           const DecodeEpi& epi, hipStream_t s) {
     constexpr int RU = GATED ? 2 * R : R;
     const int64_t nb = K / 32;
-    if (NT * nb * XS16 * 4 > DmaLds<NT, RU, WAVES, S>::XCAP) return 0;
+    if (NT * nb * XS16 * 4 > DmaLds<FMT, NT, RU, WAVES, S>::XCAP) return 0;
     const int64_t ngroups = (M + R - 1) / R;
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((ngroups + WAVES - 1) / WAVES, 256));
     const int64_t ns = (nb + DmaGeom<FMT>::SLICE - 1) / DmaGeom<FMT>::SLICE;
@@ -339,22 +345,30 @@ static int64_t dma_launch(const void* W, const void* Wu, const float* x, float* 
     return M;
 }
 
-// Variant choice (kernel-trace durations on MI355X, K = 4096, 256 to 131072 rows,
-// weights streamed from HBM): 8 waves with a 3-slot ring and 1-row tasks is best or
-// within noise at every size for Q8_0 (at 570 MB it is within 1% of the same kernel
-// with the decode removed, i.e. of the stream itself) and for Q4_0 up to 32768 rows;
-// the Q4_0 LM head (>= 65536 rows), whose decode is twice the work per byte, runs best
-// with 2-row tasks (x read from LDS once per two rows).  The gated product (gate and
-// up rows in every task) measured faster on the register-staged kernel for both
-// formats (Q4_0 15.3 vs 16.9 us, Q8_0 21.8 vs 22.4 us at 14336 x 4096), so it is
-// left to that kernel.
+// Variant choice (durations on MI355X, weights streamed from HBM, the 8B shapes).
+// Q8_0: 8 waves with a 3-slot ring and 1-row tasks is best or within noise at every
+// size at K = 4096 (at 570 MB within 1% of the same kernel with the decode removed,
+// i.e. of the stream itself).  The nibble formats decode more per byte (Q5_x about
+// twice Q4_0), and there 2-row tasks (x read from LDS once per two rows) with a
+// 2-slot ring win whenever they spread the rows as evenly over the 2048 waves of a
+// full grid as 1-row tasks do: e.g. Q4_1 / Q5_0 / Q5_1 / Q4_0 at 4096 x 14336 10.3 /
+// 12.4 / 12.8 / 10.2 us against 11.3 / 13.1 / 13.5 / 11.2 us, and the 128256-row LM
+// head 52.8 / 63.9 / 66.2 / 50.2 against 58.3 / 68.8 / 70.6 / 57.0 us; at 6144 rows
+// (3 rows per wave against 4) 1-row tasks stay ahead (Q4_1 6.5 against 6.9 us).
+// The gated product (gate and up rows in every task) measured faster on the
+// register-staged kernel (Q4_0 15.3 vs 16.9 us, Q8_0 21.8 vs 22.4 us at
+// 14336 x 4096), so it is left to that kernel.
 template <int FMT, int NT, int EP>
 static int64_t dma_nt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
                       const DecodeEpi& epi, hipStream_t s) {
     if (Wu) return 0;
     int64_t r = 0;
-    if constexpr (FMT == 2)
-        if (M >= 65536) r = dma_launch<FMT, NT, 2, false, 8, 3, EP>(W, Wu, x, y, M, K, epi, s);
+    if constexpr (FMT != 8) {
+        constexpr int64_t kWaves = 256 * 8;
+        const int64_t rows1 = (M + kWaves - 1) / kWaves;              // rows per wave, 1-row tasks
+        const int64_t rows2 = 2 * ((M + 2 * kWaves - 1) / (2 * kWaves));  // and 2-row tasks
+        if (20 * rows2 <= 21 * rows1) r = dma_launch<FMT, NT, 2, false, 8, 2, EP>(W, Wu, x, y, M, K, epi, s);
+    }
     if (!r) r = dma_launch<FMT, NT, 1, false, 8, 3, EP>(W, Wu, x, y, M, K, epi, s);
     return r;
 }
@@ -383,9 +397,14 @@ static int64_t dma_fmt(const void* W, const void* Wu, const float* x, float* y, 
 int64_t launch_gemv_dma(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
                         int NT, int ep, const DecodeEpi& epi, hipStream_t s) {
     if (K % 256 != 0 || NT < 1 || NT > 4) return 0;
-    if (fmt == 8) return dma_fmt<8>(W, Wu, x, y, M, K, NT, ep, epi, s);
-    if (fmt == 2) return dma_fmt<2>(W, Wu, x, y, M, K, NT, ep, epi, s);
-    return 0;
+    switch (fmt) {
+        case 8: return dma_fmt<8>(W, Wu, x, y, M, K, NT, ep, epi, s);
+        case 2: return dma_fmt<2>(W, Wu, x, y, M, K, NT, ep, epi, s);
+        case 3: return dma_fmt<3>(W, Wu, x, y, M, K, NT, ep, epi, s);
+        case 6: return dma_fmt<6>(W, Wu, x, y, M, K, NT, ep, epi, s);
+        case 7: return dma_fmt<7>(W, Wu, x, y, M, K, NT, ep, epi, s);
+        default: return 0;
+    }
 }
 
 }  // namespace qmm

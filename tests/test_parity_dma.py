@@ -1,12 +1,14 @@
-"""GPU parity of the DMA-fed decode GEMV (Q8_0 / Q4_0 rows that are 16-byte aligned,
+"""GPU parity of the DMA-fed decode GEMV (block-format rows that are 16-byte aligned,
 K % 256 == 0, 1..4 tokens per weight pass) against the float64 oracle.
 
 The shapes walk the kernel's geometry:
-* a partial last K slice (64 blocks per Q8_0 slice, 128 per Q4_0 slice) and a
-  single partial slice;
+* a partial last K slice (64 blocks per Q8_0 slice, 128 per slice of the nibble
+  formats) and a single partial slice;
 * fewer tasks per wave than ring slots, and many more (the ring wraps);
-* row counts that are not multiples of the rows per task (Q4_0 with >= 65536 rows
-  runs 2-row tasks), and more row groups than waves;
+* row counts that are not multiples of the rows per task (the nibble formats run
+  2-row tasks when those spread the rows as evenly over the waves as 1-row tasks:
+  here at 20000, 65537 and 65600 rows, and 8192 rows in the residual mode), and
+  more row groups than waves;
 * x sizes up to 35 KB per token (K = 14336) and 4 tokens of K = 4096;
 * the RMSNorm and residual modes, including the residual with more row groups per
   wave than the kernel reads ahead (another kernel takes those);
@@ -25,7 +27,8 @@ from parity_util import (announce, check_linear, check_residual, check_swiglu, d
 
 pytestmark = pytest.mark.gpu
 FMTS = [si.FMT_Q8_0, si.FMT_Q4_0]
-FID = {si.FMT_Q8_0: "q8_0", si.FMT_Q4_0: "q4_0"}
+ALL_FMTS = FMTS + [si.FMT_Q4_1, si.FMT_Q5_0, si.FMT_Q5_1]  # 3072-byte slots for the last three
+FID = {si.FMT_Q8_0: "q8_0", si.FMT_Q4_0: "q4_0", si.FMT_Q4_1: "q4_1", si.FMT_Q5_0: "q5_0", si.FMT_Q5_1: "q5_1"}
 VALU = qmm.QMM_VARIANT_VALU
 
 GEMV_CASES = [
@@ -35,16 +38,17 @@ GEMV_CASES = [
     (1000, 2304, 2),   # Q8_0: 64 + 8 blocks; Q4_0: one 72-block slice
     (4100, 4352, 1),   # more row groups than waves; Q8_0 3 slices, Q4_0 128 + 8
     (16385, 2304, 1),  # many row groups per wave
-    (20000, 4352, 3),  # ring wraps many times, 3 tokens
-    (65537, 512, 1),   # Q4_0: 2-row tasks with a lone last row
-    (65600, 256, 4),   # Q4_0: 2-row tasks, 4 tokens
+    (20000, 4352, 3),  # ring wraps many times, 3 tokens (nibble formats: 2-row tasks)
+    (65537, 512, 1),   # nibble formats: 2-row tasks with a lone last row
+    (65600, 256, 4),   # nibble formats: 2-row tasks, 4 tokens
+    (4096, 14336, 1),  # nibble formats: 2-row tasks, x 35 KB
     (513, 14336, 1),   # x 35 KB per token
     (300, 4096, 4),    # 4 tokens, x 40 KB
     (9, 4096, 6),      # two passes (4 + 2 tokens)
 ]
 
 
-@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
 @pytest.mark.parametrize("M,K,N", GEMV_CASES)
 def test_dma_gemv(fmt, M, K, N):
     seed = 5000 + M + K + N
@@ -60,16 +64,18 @@ def test_dma_gemv(fmt, M, K, N):
     check_linear(got, y_ref, S, f"dma gemv fmt={fmt} M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
 def test_dma_gemv_one_hot_exact(fmt):
-    """x = e_k returns the decoded column exactly, across slices and ring slots."""
+    """x = e_k returns the decoded column rounded once to fp32 (exact for Q8_0 / Q4_0 /
+    Q5_0; d * u + m of the biased formats may need more bits), across slices and ring
+    slots."""
     M, K = 4100, 4352
     raw = si.weights(fmt, M, K, 61, scale_mode="gemm_wide", q8_low=-128)
     cols = [0, 31, 2047, 4351]
     x = si.one_hot(len(cols), K, cols)
     announce(f"dma gemv one-hot fmt={fmt} M={M} K={K}")
     y = qmm.gemv(fmt, dev(raw), dev(x), M, K, variant=VALU).cpu().numpy().astype(np.float64)
-    W = oracle.dequant(fmt, raw, M, K)
+    W = oracle.dequant(fmt, raw, M, K).astype(np.float32).astype(np.float64)
     for n, c in enumerate(cols):
         assert np.array_equal(y[n], W[:, c]), (n, c)
 
@@ -89,7 +95,7 @@ def test_dma_gate_up_silu(fmt, I, K, N):
     check_swiglu(buf[:N * I].cpu().numpy().reshape(N, I), h_ref, g, u, Sg, Su, "dma gate_up_silu")
 
 
-@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
 @pytest.mark.parametrize("M,K,N", [(257, 768, 1), (4100, 4352, 2), (20000, 2304, 1), (513, 14336, 1)])
 def test_dma_rmsnorm_gemv(fmt, M, K, N):
     seed = 5200 + M + K + N
@@ -103,7 +109,7 @@ def test_dma_rmsnorm_gemv(fmt, M, K, N):
     check_linear(y.cpu().numpy(), y_ref, S, "dma rmsnorm_gemv")
 
 
-@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
 @pytest.mark.parametrize("M,K,N", [(257, 768, 1), (4100, 4352, 1), (8192, 2304, 2), (20000, 2304, 1)])
 @pytest.mark.parametrize("inplace", [False, True], ids=["out", "inplace"])
 def test_dma_gemv_add(fmt, M, K, N, inplace):
@@ -122,15 +128,18 @@ def test_dma_gemv_add(fmt, M, K, N, inplace):
         assert np.array_equal(rd.cpu().numpy(), r), "the residual input must not change"
 
 
-@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("fmt", FMTS + [si.FMT_Q5_0], ids=FID.get)
 @pytest.mark.parametrize("N", [1, 3])
 def test_dma_zero_codes_give_zero(fmt, N):
-    """Codes equal to the offset (q = 0, nibble 8) give exactly zero: the staged
-    offset chain of every x block equals the decode's dot product chain bit for bit."""
+    """Codes equal to the offset (q = 0, nibble 8, 5-bit code 16) give exactly zero: the
+    staged offset chain of every x block equals the decode's dot product chain bit for
+    bit."""
     M, K = 300, 4352
     d = np.full((M, K // 32), 0.75, dtype=np.float16)
     if fmt == si.FMT_Q8_0:
         raw = oracle.pack_q8_0(np.zeros((M, K), dtype=np.int8), d)
+    elif fmt == si.FMT_Q5_0:
+        raw = oracle.pack_q5_0(np.full((M, K), 16, dtype=np.int64), d)
     else:
         raw = oracle.pack_q4_0(np.full((M, K), 8, dtype=np.uint8), d)
     x = (si.activations(N, K, 17) * np.float32(1e3)).astype(np.float32)
