@@ -32,7 +32,8 @@ def _replays(g, out, eager_noise):
     return got[0]
 
 
-@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_0], ids=["q8_0", "q4_0"])
+@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_0, si.FMT_Q4_1, si.FMT_Q5_0, si.FMT_Q5_1],
+                         ids=["q8_0", "q4_0", "q4_1", "q5_0", "q5_1"])
 def test_graph_gemv_small_batch_and_n1(fmt):
     M, K = 1024, 4096
     raw = si.weights(fmt, M, K, 7001, scale_mode="gemm_wide", q8_low=-128)
@@ -61,7 +62,8 @@ def test_graph_gemv_small_batch_and_n1(fmt):
     check_linear(y1.cpu().numpy(), y_ref1, S1, f"graph gemv N=1 fmt={fmt}")
 
 
-@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_0, si.FMT_F16], ids=["q8_0", "q4_0", "f16"])
+@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_0, si.FMT_F16, si.FMT_Q5_0, si.FMT_Q5_1],
+                         ids=["q8_0", "q4_0", "f16", "q5_0", "q5_1"])
 def test_graph_gemm_few_tiles(fmt):
     M, K, T = 300, 2816, 40  # 2 tiles: split-K outside of capture
     raw = si.weights(fmt, M, K, 7101, scale_mode="gemm_wide", q8_low=-128)
