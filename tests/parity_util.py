@@ -16,7 +16,7 @@ def announce(msg: str) -> None:
 
 
 def dev(a: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    return torch.from_numpy(np.require(a, requirements=["C", "W"])).to("cuda")  # writable copy if needed
 
 
 def poisoned(n_elems: int, guard: int = 64):

@@ -86,6 +86,43 @@ def test_golden_count():
     assert {load_golden(p)["fmt"] for p in NEW_GOLDEN} == set(FMTS)
 
 
+def _special_blocks(fmt):
+    """Blocks whose scale or bias is inf, -inf, NaN or zero, or whose d * u + m overflows
+    fp16: codes 0..15 (4-bit) or 0..31 (5-bit) repeated."""
+    M, K = 3, 64
+    d = np.array([[np.inf, -np.inf], [np.nan, 0.0], [1.0, 65504.0]], dtype=np.float16)
+    m = np.array([[0.0, 1.0], [0.0, np.inf], [-np.inf, -65504.0]], dtype=np.float16)
+    bits = 4 if fmt == si.FMT_Q4_1 else 5
+    u = np.tile(np.arange(64, dtype=np.int64) % (1 << bits), (M, 1))
+    if fmt == si.FMT_Q4_1:
+        raw = oracle.pack_q4_1(u, d, m)
+    elif fmt == si.FMT_Q5_0:
+        raw = oracle.pack_q5_0(u, d)
+    else:
+        raw = oracle.pack_q5_1(u, d, m)
+    return raw, M, K
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+def test_special_scales_and_biases(fmt):
+    """IEEE propagation through dequant, gather and fp16 expansion: inf * 0 and
+    inf - inf give NaN, overflow gives inf, the rest are values rounded once."""
+    raw, M, K = _special_blocks(fmt)
+    announce(f"special scales fmt={fmt}")
+    W = dev(raw)
+    ref = oracle.dequant(fmt, raw, M, K)
+    nan = np.isnan(ref)
+    for got in (qmm.dequant(fmt, W, M, K).cpu().numpy(),
+                qmm.get_rows(fmt, W, dev(np.arange(M, dtype=np.int32)), M, K).cpu().numpy()):
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(_bits32(got[~nan]), _bits32(ref[~nan].astype(np.float32)))
+    h = qmm.expand_f16(fmt, W, M, K).cpu().numpy()
+    href = oracle.expand_f16_ref(fmt, raw, M, K)
+    hnan = np.isnan(href)
+    assert np.array_equal(np.isnan(h), hnan)
+    assert np.array_equal(h[~hnan].view(np.uint16), href[~hnan].view(np.uint16))
+
+
 @pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
 def test_get_rows_bit_exact(fmt):
     M, K = 1000, 576
