@@ -339,3 +339,32 @@ def test_gate_up_silu_mfma(fmt, I, K, N):
     assert guard_intact(buf, N * I)
     h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, x.astype(np.float16), I, K)
     check_swiglu(buf[:N * I].cpu().numpy().reshape(N, I), h_ref, g, u, Sg, Su, "gate_up_silu mfma")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+def test_gemv_llama3_8b_lm_head_sampled(fmt):
+    """The 128256 x 4096 LM head (2-row DMA tasks) at its full size, one token; sampled
+    rows against the oracle, and every output finite."""
+    M, K = 128256, 4096
+    raw = si.weights(fmt, M, K, 7950 + fmt)
+    x = si.activations(1, K, 7951 + fmt)
+    announce(f"gemv 8B LM head fmt={fmt}")
+    y = qmm.gemv(fmt, dev(raw), dev(x), M, K).cpu().numpy()
+    assert np.isfinite(y).all()
+    rows = sample_rows(M, 96, 7952 + fmt)
+    y_ref, S = oracle.matmul_ref(fmt, raw, x, M, K, rows=rows)
+    check_linear(y[:, rows], y_ref, S, f"gemv 8B LM head fmt={fmt}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+def test_gate_up_llama3_8b_sampled(fmt):
+    """Gate+up + SwiGLU at 2 x 14336 x 4096, one token; sampled outputs."""
+    I, K = 14336, 4096
+    rg, ru = si.weights(fmt, I, K, 7960 + fmt), si.weights(fmt, I, K, 7961 + fmt)
+    x = si.activations(1, K, 7962 + fmt)
+    announce(f"gate_up 8B fmt={fmt}")
+    h = qmm.gate_up_silu(fmt, dev(rg), dev(ru), dev(x), I, K).cpu().numpy()
+    assert np.isfinite(h).all()
+    rows = sample_rows(I, 96, 7963 + fmt)
+    h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, x, I, K, rows=rows)
+    check_swiglu(h[:, rows], h_ref, g, u, Sg, Su, f"gate_up 8B fmt={fmt}")
