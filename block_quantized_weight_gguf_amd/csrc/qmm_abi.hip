@@ -54,19 +54,26 @@ int check_shape(int fmt, int64_t M, int64_t K, int64_t N) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 
-// VALU or MFMA variant for N tokens over `wbytes` of weights (measured on MI355X at
-// the Llama-3-8B projection shapes, weights streamed from HBM).  Q8_0 / Q4_0: the
-// VALU kernel takes up to 4 tokens per weight pass, so from 5 tokens it reads the
-// weights twice and the single-pass MFMA kernel wins on every shape (by 1.3-1.9x);
-// at 4 tokens the MFMA kernel wins or ties from about 32 MB of weights (e.g. the Q4_0
-// LM head 82 vs 87 us) and loses on smaller matrices, whose two launches and
-// split-K cost more than the pass; at 2-3 tokens the VALU kernel wins everywhere.
-// F16 (sliced VALU kernel against the tiled GEMM): MFMA from 4 tokens.  Q4_1 / Q5_0 /
-// Q5_1 follow the Q8_0 / Q4_0 rule.
-int choose_variant(int fmt, int64_t wbytes, int64_t N) {
+// VALU or MFMA variant for N tokens over `wbytes` of weights (`gated`: the gate+up
+// product), measured on MI355X at the Llama-3-8B projection shapes with the weights
+// streamed from HBM.  The block formats' VALU kernels take up to 4 tokens per weight
+// pass, so from 5 tokens they read the weights twice and the single-pass MFMA kernel
+// wins on every shape (by 1.3-1.9x).  At 4 tokens the MFMA kernel wins or ties from
+// about 32 MB of weights (e.g. the Q4_0 LM head 82 vs 87 us, the Q5_1 down projection
+// 20 vs 30 us) and loses on smaller matrices, whose two launches and split-K cost
+// more than the pass -- except the gate+up product of Q4_1 / Q5_0 / Q5_1, whose VALU
+// kernel stays ahead (26-29 vs 28-31 us at 2 x 14336 x 4096).  At 2-3 tokens the VALU
+// kernel wins, but for the Q8_0 LM head at 3 tokens (MFMA 113 vs 120 us; from 256 MB).
+// F16 (sliced VALU kernel against the tiled GEMM): MFMA from 4 tokens.
+int choose_variant(int fmt, int64_t wbytes, int64_t N, bool gated) {
     if (fmt == QMM_F16) return N >= 4 ? QMM_VARIANT_MFMA : QMM_VARIANT_VALU;
     if (N >= 5) return QMM_VARIANT_MFMA;
-    if (N == 4 && wbytes >= (int64_t{32} << 20)) return QMM_VARIANT_MFMA;
+    if (N == 4) {
+        const bool extra = fmt == QMM_Q4_1 || fmt == QMM_Q5_0 || fmt == QMM_Q5_1;
+        if (gated && extra) return QMM_VARIANT_VALU;
+        return wbytes >= (int64_t{32} << 20) ? QMM_VARIANT_MFMA : QMM_VARIANT_VALU;
+    }
+    if (N == 3 && fmt == QMM_Q8_0 && wbytes >= (int64_t{256} << 20)) return QMM_VARIANT_MFMA;
     return QMM_VARIANT_VALU;
 }
 
@@ -131,7 +138,7 @@ int qmm_expand_f16(int fmt, const void* W, void* out, int64_t M, int64_t K, void
 int qmm_gemv_choose(int fmt, int64_t M, int64_t K, int64_t N) {
     const int st = check_shape(fmt, M, K, N);
     if (st) return st;
-    return choose_variant(fmt, M * row_bytes_unchecked(fmt, K), N);
+    return choose_variant(fmt, M * row_bytes_unchecked(fmt, K), N, false);
 }
 
 int qmm_gemv_variant(int fmt, const void* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
@@ -161,7 +168,7 @@ int qmm_gate_up_silu_variant(int fmt, const void* Wg, const void* Wu, const floa
     int st = check_shape(fmt, I, K, N);
     if (st) return st;
     if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(x, 16) || !aligned(h, 4)) return QMM_ERR_ALIGN;
-    if (variant == QMM_VARIANT_AUTO) variant = choose_variant(fmt, 2 * I * row_bytes_unchecked(fmt, K), N);
+    if (variant == QMM_VARIANT_AUTO) variant = choose_variant(fmt, 2 * I * row_bytes_unchecked(fmt, K), N, true);
     auto s = static_cast<hipStream_t>(stream);
     if (variant == QMM_VARIANT_VALU) return from_hip(qmm::launch_gemv_valu(fmt, Wg, Wu, x, h, I, K, N, s));
     if (variant == QMM_VARIANT_MFMA) {

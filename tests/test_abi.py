@@ -185,14 +185,20 @@ def test_variant_choice():
         assert L.qmm_gemv_choose(fmt, 4096, 4096, 4) == 1       # 17.8 / 9.4 MB
         assert L.qmm_gemv_choose(fmt, 4096, 4096, 5) == 2
         assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == 2     # LM head
-        assert L.qmm_gemv_choose(fmt, 128256, 4096, 3) == 1
+        assert L.qmm_gemv_choose(fmt, 128256, 4096, 2) == 1
     assert L.qmm_gemv_choose(1, 4096, 4096, 4) == 2
     assert L.qmm_gemv_choose(1, 4096, 4096, 3) == 1
     assert L.qmm_gemv_choose(5, 4096, 4096, 1) == E_FMT
-    # Q4_1 / Q5_0 / Q5_1 follow the Q8_0 / Q4_0 rule.
+    # Q4_1 / Q5_0 / Q5_1 follow the same rule for the plain product.
     for fmt in (3, 6, 7):
         assert [L.qmm_gemv_choose(fmt, 4096, 4096, n) for n in (1, 3, 4, 5, 64)] == [1, 1, 1, 2, 2]
         assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == 2
+        assert L.qmm_gemv_choose(fmt, 4096, 14336, 4) == 2
+        assert L.qmm_gemv_choose(fmt, 128256, 4096, 3) == 1
+    # Q8_0 at 3 tokens from 256 MB (the LM head), not below.
+    assert L.qmm_gemv_choose(8, 128256, 4096, 3) == 2
+    assert L.qmm_gemv_choose(8, 14336, 4096, 3) == 1
+    assert L.qmm_gemv_choose(2, 128256, 4096, 3) == 1
     assert L.qmm_gemv_choose(8, 4096, 100, 1) == E_SHAPE
     assert L.qmm_gemv_variant(8, A16, A16, A16 + 1, 4, 64, 1, 9, None) == E_ALIGN
     assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, 9, None) == E_VAR
