@@ -132,6 +132,35 @@ def weights(fmt: int, M: int, K: int, seed: int, *, scale_mode: str = "uniform",
     return out
 
 
+# fp16 bit patterns written into every block of device_weights: scale 2^-8 (0x1C00);
+# the biased formats' bias -2^-4 (0xAC00), about -16 scales.
+_DEV_SCALE = (0x00, 0x1C)
+_DEV_BIAS = (0x00, 0xAC)
+
+
+def device_weights(fmt: int, M: int, K: int, seed: int, device):
+    """Raw weight bytes drawn on the device (torch's seeded generator), for matrices too
+    large to draw on the host: uniform code bytes, and every block's scale (and bias)
+    set to the fixed fp16 patterns above so that every weight is finite.  Returns a
+    flat uint8 device tensor; tests read back the bytes of the rows they check."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    rb = layout_bytes(fmt, K)
+    w = torch.randint(0, 256, (M * rb,), dtype=torch.uint8, device=device, generator=g)
+    if fmt != FMT_F16:
+        blk = w.view(-1, BLOCK_DTYPES[fmt].itemsize)
+        blk[:, 0] = _DEV_SCALE[0]
+        blk[:, 1] = _DEV_SCALE[1]
+        if fmt in (FMT_Q4_1, FMT_Q5_1):
+            blk[:, 2] = _DEV_BIAS[0]
+            blk[:, 3] = _DEV_BIAS[1]
+    else:
+        # keep F16 weights finite: clear the top exponent bit of every half
+        w.view(-1, 2)[:, 1] &= 0xBF
+    return w
+
+
 def activations(N: int, K: int, seed: int, dtype=np.float32) -> np.ndarray:
     """Standard-normal activations [N][K] (fp32 for decode, fp16 for prefill)."""
     return rng(seed).standard_normal((N, K)).astype(dtype)
