@@ -20,13 +20,15 @@
 //     blocks) of all 256 rows.  Rows are 16-byte aligned (K % 256 == 0), so the
 //     four-block segment of every row sits at the same offset (0 or 8) inside a
 //     window of whole 16-byte chunks (Q8_0: 136 bytes in 9 chunks, Q4_0: 72 bytes
-//     in 5).  Each wave then decodes its own MFMA A fragments straight from the raw
-//     bytes (each weight row belongs to one wave, so nothing is decoded twice): lane
-//     l needs 8 consecutive weights of row l % 16, i.e. the block scale and 8 code
-//     bytes (Q4_0: 8 nibbles).  Decoding is done in the fp16 domain: a
-//     code byte c becomes the half 1024 + c via v_perm with 0x64 bytes, v_pk_add_f16
-//     removes the offset exactly and v_pk_mul_f16 by the fp16 scale gives fp16(d*q)
-//     with a single rounding.  F16 weights use the token-tile layout.
+//     in 5, Q4_1 80 in 5, Q5_0 88 in 6, Q5_1 96 in 6).  Each wave then decodes its
+//     own MFMA A fragments straight from the raw bytes (each weight row belongs to
+//     one wave, so nothing is decoded twice): lane l needs 8 consecutive weights of
+//     row l % 16, i.e. the block scale (and bias) and 8 code bytes (nibble formats:
+//     8 nibbles, plus one byte of fifth bits).  Decoding is done in the fp16 domain:
+//     a code byte c becomes the half 1024 + c via v_perm with 0x64 bytes,
+//     v_pk_add_f16 removes the offset exactly and v_pk_mul_f16 by the fp16 scale (the
+//     biased formats: v_pk_fma_f16 with the bias) gives the weight with a single
+//     rounding.  F16 weights use the token-tile layout.
 //   * Inside a K step the token fragments are read one group ahead of the MFMAs
 //     that use them, in scheduling regions of their own (the compiler would
 //     otherwise read each just before its MFMA and expose the LDS latency), after

@@ -38,7 +38,7 @@ constexpr int GM_BM = 256;       // weight rows per workgroup
 constexpr int GM_THREADS = 512;  // 8 waves
 constexpr int GM_WAVES = GM_THREADS / 64;
 
-// Blocks per ring stage.  4 for both formats: 8-block Q4_0 stages (144 bytes, 9
+// Blocks per ring stage.  4 for every format: 8-block Q4_0 stages (144 bytes, 9
 // aligned chunks) double the work per barrier but halve the stages a K range splits
 // into, and on the 4096-row matrices the lost parallelism costs more than the
 // barriers save (measured).

@@ -87,7 +87,7 @@ constexpr int stage_shift(int parity) {
     return (FMT == 1 || (4 * Fmt<FMT>::BB) % 16 == 0) ? 0 : 8 * parity;
 }
 
-// A fragment of v_mfma_f32_16x16x32_f16 decoded from a raw Q8_0 / Q4_0 row window in
+// A fragment of v_mfma_f32_16x16x32_f16 decoded from a raw block-format row window in
 // LDS: the 8 weights 8 q4 .. 8 q4 + 7 (lane l: q4 = l / 16) of the block that starts
 // `o` bytes into the row (o even; blocks are 2-byte aligned).  Q4_0 fragments 0, 1
 // take the low nibbles of code bytes 0..7 / 8..15, fragments 2, 3 the high nibbles.

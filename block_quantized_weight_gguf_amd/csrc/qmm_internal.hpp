@@ -43,13 +43,13 @@ hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float*
                             int64_t M, int64_t K, int64_t N, hipStream_t s, int ep = EP_NONE,
                             const DecodeEpi& epi = DecodeEpi{});
 
-// Streaming GEMV for Q8_0 / Q4_0 with NT <= 4 tokens in one pass.  Returns the
+// Streaming GEMV for the block formats with NT <= 4 tokens in one pass.  Returns the
 // number of leading rows it launched (M or M - 1); 0 means nothing was launched
 // (format or LDS footprint of x does not fit).
 int64_t launch_gemv_stream(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
                            int NT, int ep, const DecodeEpi& epi, hipStream_t s);
 
-// DMA-fed streaming GEMV for Q8_0 / Q4_0 with K % 256 == 0 and NT <= 4 tokens in
+// DMA-fed streaming GEMV for the block formats with K % 256 == 0 and NT <= 4 tokens in
 // one pass.  Returns M when it launched, 0 when it does not apply (format, K, LDS
 // footprint of x, or EP_RES with more row groups per wave than it reads ahead).
 int64_t launch_gemv_dma(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
@@ -71,7 +71,7 @@ hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* 
 bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32, float* Y, int64_t M,
                       int64_t K, int64_t T, hipStream_t s);
 
-// Weight-streaming fp16-MFMA GEMV for 2..32 tokens (Q8_0 / Q4_0, K % 256 == 0): each
+// Weight-streaming fp16-MFMA GEMV for 2..32 tokens (block formats, K % 256 == 0): each
 // weight byte is read once per call.  Returns false, launching nothing, when it does
 // not apply.
 bool launch_gemv_mfma(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,

@@ -160,7 +160,7 @@ int qmm_expand_f16(int fmt, const void* W, void* out, int64_t M, int64_t K, void
  * Q8_0 dequant + GEMV pipelines; "llama.cpp Metal ...", section 3.2 and P9:
  * per-format mat-vec kernels for one token and a batched mat-vec for 2..8 tokens.)
  * The variant is chosen from (fmt, M, K, N) as qmm_gemv_choose reports.
- * Precision: accumulation is fp32 everywhere.  For Q8_0 / Q4_0 the register-decode
+ * Precision: accumulation is fp32 everywhere.  For the block formats the register-decode
  * variant holds x in block floating point (each 32-value block scaled by a power
  * of two, then rounded to fp16) and forms the products with packed fp16 dot
  * products; F16 weights and rows it leaves to its fallback use fp32 x.  The MFMA
