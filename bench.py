@@ -525,11 +525,37 @@ DOMINANT_KERNEL = "gemv_dma_kernel<8, 1, 1, false, 8, 3, 0>"
 DOMINANT_SOURCES = ("gemv_dma.hip", "gemv_block.hpp", "dma.hpp", "qmm_common.hpp", "qmm_internal.hpp")
 
 
+def _code_only(text):
+    """C++ source with comments removed and whitespace runs collapsed: edits to comments
+    or layout leave the kernel, and so this text, unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":  # string or character literal
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def sources_digest(files=DOMINANT_SOURCES):
+    """sha256 of the dominant kernel's sources, code only (comments and layout removed)."""
     import hashlib
     h = hashlib.sha256()
     for f in files:
-        h.update(open(os.path.join(ROOT, "block_quantized_weight_gguf_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "block_quantized_weight_gguf_amd", "csrc", f)).read()
+        h.update(_code_only(text).encode())
     return h.hexdigest()
 
 
