@@ -27,6 +27,10 @@
 //     left to the sliced kernel, so this one never needs a tail path.
 //   * A row group's partial sums stay in registers across its K slices and are
 //     reduced across the wave once, with a transposing butterfly.
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "dma.hpp"
 #include "gemv_block.hpp"
 #include "qmm_internal.hpp"
@@ -233,6 +237,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
     }
 }
 
+// Raise a kernel's dynamic LDS limit once per (kernel, device): the attribute belongs
+// to the current device, and launches may come from several host threads.
+static void allow_dynamic_lds(const void* kern, int bytes) {
+    static std::mutex mu;
+    static std::set<std::pair<const void*, int>> done;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.emplace(kern, dev).second) {
+        if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+            (void)hipGetLastError();  // the launch below then reports the failure
+    }
+}
+
 // Returns the number of leading rows launched (M, or M - 1 when the matrix size is
 // not a multiple of 16 bytes: the final row's last 16-byte chunk would cross the
 // end of the buffer, so that row is left to the caller), or 0 when this kernel
@@ -254,12 +275,7 @@ static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y,
     constexpr int64_t kMaxLds = 160 * 1024;
     if (lds > kMaxLds) return 0;
     auto kern = gemv_stream_kernel<FMT, NT, R, GATED, WAVES, D, EP>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(kMaxLds));
-        attr_set = true;
-    }
+    allow_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kMaxLds));
     const int64_t ngroups = (M + R - 1) / R;
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(16 / WAVES, kMaxLds / lds));
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((ngroups + WAVES - 1) / WAVES, 256 * per_cu));
