@@ -249,15 +249,16 @@ hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float*
         if (e.res) e.res += d * M;
         return e;
     };
-    // Block formats: the DMA-fed streaming kernel (16-byte aligned rows), else the
-    // register-staged one; up to 4 tokens per pass, as many tokens per
-    // pass as its LDS copy of x allows; a final row it leaves is done by the sliced kernel.
+    // Block formats: the DMA-fed streaming kernel (16-byte aligned rows, more than
+    // 2 kSmallRows rows), else the register-staged one; up to 4 tokens per pass, as
+    // many tokens per pass as its LDS copy of x allows; a final row it leaves is done
+    // by the sliced kernel.
     while (done < N) {
         int nt = static_cast<int>(std::min<int64_t>(4, N - done));
         int64_t rows = 0;
         const DecodeEpi e = at(done);
         while (nt > 0) {
-            rows = launch_gemv_dma(fmt, W, Wu, x + done * K, y + done * M, M, K, nt, ep, e, s);
+            rows = M <= 2 * kSmallRows ? 0 : launch_gemv_dma(fmt, W, Wu, x + done * K, y + done * M, M, K, nt, ep, e, s);
             if (rows == 0) rows = launch_gemv_stream(fmt, W, Wu, x + done * K, y + done * M, M, K, nt, ep, e, s);
             if (rows != 0) break;
             --nt;

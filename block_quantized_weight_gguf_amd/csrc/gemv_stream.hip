@@ -287,11 +287,18 @@ static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y,
     return M;
 }
 
-// Variant choice (measured on MI355X at the Llama-3-8B and SmolLM2-135M shapes):
-// the plain GEMV runs 16 waves per workgroup (8 for 3-4 tokens) with 2 rows per
-// task for large outputs and 1 row otherwise; the gated kernel runs 8 waves with
-// 1 gate + 1 up row per task, prefetching two tasks ahead when each wave owns
-// only a few tasks, so that the whole matrix is in flight at once.
+// Variant choice (measured on MI355X at the Llama-3-8B and SmolLM2-135M shapes).
+// Large matrices: the plain GEMV runs 16 waves per workgroup (8 for 3-4 tokens) with 2
+// rows per task from 16384 rows and 1 row otherwise; the gated kernel runs 8 waves
+// with 1 gate + 1 up row per task, prefetching two tasks ahead when each wave owns
+// only a few tasks, so that the whole matrix is in flight at once.  Small matrices
+// are bound by the kernel's own latency chain (x staged, one workgroup barrier, the
+// first weight bytes, the reduction), which shrinks with the workgroup: in HIP-graph
+// replay a 576 x 576 (or 960 x 576, 576 x 1536) GEMV takes 2.4 us on 4-wave
+// workgroups against 3.2-3.4 us on 16 waves (or the DMA-fed kernel), 1024 x 4096 3.2
+// against 3.9 us with two tasks in flight; at 2048 rows 8 waves are best (2.75 against
+// 3.4 us at K = 576, 3.7 against 3.9 us at K = 4096).  The gated product likewise runs
+// 4 waves up to 1024 rows (Q8_0 1024 x 4096: 4.0 against 4.9 us).
 template <int FMT, int NT, int EP>
 static int64_t launch_nt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
                          const DecodeEpi& epi, hipStream_t s) {
@@ -302,10 +309,15 @@ static int64_t launch_nt(const void* W, const void* Wu, const float* x, float* y
             return 0;  // no residual on the gated product
         } else {
             const bool deep = (M * slices) / (256 * 8) <= 2;  // tasks per wave
+            if (M <= kSmallRows)
+                return deep ? launch_t<FMT, NT, 1, true, 4, 2, EP>(W, Wu, x, y, M, K, epi, s)
+                            : launch_t<FMT, NT, 1, true, 4, 1, EP>(W, Wu, x, y, M, K, epi, s);
             return deep ? launch_t<FMT, NT, 1, true, 8, 2, EP>(W, Wu, x, y, M, K, epi, s)
                         : launch_t<FMT, NT, 1, true, 8, 1, EP>(W, Wu, x, y, M, K, epi, s);
         }
     }
+    if (M <= kSmallRows) return launch_t<FMT, NT, 1, false, 4, 2, EP>(W, Wu, x, y, M, K, epi, s);
+    if (M <= 2 * kSmallRows) return launch_t<FMT, NT, 1, false, 8, 1, EP>(W, Wu, x, y, M, K, epi, s);
     // 16 waves per workgroup cap a wave at 128 VGPRs; 3-4 tokens need more.
     constexpr int PW = NT <= 2 ? 16 : 8;
     if (M >= 16384) return launch_t<FMT, NT, 2, false, PW, 1, EP>(W, Wu, x, y, M, K, epi, s);

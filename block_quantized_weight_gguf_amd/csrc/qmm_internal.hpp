@@ -43,6 +43,11 @@ hipError_t launch_gemv_valu(int fmt, const void* W, const void* Wu, const float*
                             int64_t M, int64_t K, int64_t N, hipStream_t s, int ep = EP_NONE,
                             const DecodeEpi& epi = DecodeEpi{});
 
+// Row counts up to which a GEMV counts as small: its time is the kernel's latency chain,
+// and it runs on the register-staged streaming kernel with small workgroups (up to 2 x
+// this many rows) instead of the DMA-fed one.
+constexpr int64_t kSmallRows = 1024;
+
 // Streaming GEMV for the block formats with NT <= 4 tokens in one pass.  Returns the
 // number of leading rows it launched (M or M - 1); 0 means nothing was launched
 // (format or LDS footprint of x does not fit).

@@ -14,7 +14,9 @@ The shapes walk the kernel's geometry:
   wave than the kernel reads ahead (another kernel takes those);
 * the gated (SwiGLU) product at the same shapes (served by the register-staged
   kernel, which measured faster for it).
-Each output is poisoned with NaNs and followed by a guard band.
+Matrices of up to 2048 rows run on the register-staged kernel (its small workgroups
+win there), so every case here has more rows.  Each output is poisoned with NaNs and
+followed by a guard band.
 """
 import numpy as np
 import pytest
@@ -32,19 +34,19 @@ FID = {si.FMT_Q8_0: "q8_0", si.FMT_Q4_0: "q4_0", si.FMT_Q4_1: "q4_1", si.FMT_Q5_
 VALU = qmm.QMM_VARIANT_VALU
 
 GEMV_CASES = [
-    (3, 256, 1),       # one partial slice, fewer tasks than slots
-    (257, 768, 1),     # partial slice, ragged M
-    (257, 768, 4),     # 4 tokens per pass
-    (1000, 2304, 2),   # Q8_0: 64 + 8 blocks; Q4_0: one 72-block slice
+    (2051, 256, 1),    # one partial slice, fewer tasks than slots
+    (2305, 768, 1),    # partial slice, ragged M
+    (2305, 768, 4),    # 4 tokens per pass
+    (3048, 2304, 2),   # Q8_0: 64 + 8 blocks; Q4_0: one 72-block slice
     (4100, 4352, 1),   # more row groups than waves; Q8_0 3 slices, Q4_0 128 + 8
     (16385, 2304, 1),  # many row groups per wave
     (20000, 4352, 3),  # ring wraps many times, 3 tokens (nibble formats: 2-row tasks)
     (65537, 512, 1),   # nibble formats: 2-row tasks with a lone last row
     (65600, 256, 4),   # nibble formats: 2-row tasks, 4 tokens
     (4096, 14336, 1),  # nibble formats: 2-row tasks, x 35 KB
-    (513, 14336, 1),   # x 35 KB per token
-    (300, 4096, 4),    # 4 tokens, x 40 KB
-    (9, 4096, 6),      # two passes (4 + 2 tokens)
+    (2561, 14336, 1),  # x 35 KB per token
+    (2348, 4096, 4),   # 4 tokens, x 40 KB
+    (2057, 4096, 6),   # two passes (4 + 2 tokens)
 ]
 
 
@@ -96,7 +98,7 @@ def test_dma_gate_up_silu(fmt, I, K, N):
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
-@pytest.mark.parametrize("M,K,N", [(257, 768, 1), (4100, 4352, 2), (20000, 2304, 1), (513, 14336, 1)])
+@pytest.mark.parametrize("M,K,N", [(2305, 768, 1), (4100, 4352, 2), (20000, 2304, 1), (2561, 14336, 1)])
 def test_dma_rmsnorm_gemv(fmt, M, K, N):
     seed = 5200 + M + K + N
     raw = si.weights(fmt, M, K, seed)
@@ -110,7 +112,7 @@ def test_dma_rmsnorm_gemv(fmt, M, K, N):
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
-@pytest.mark.parametrize("M,K,N", [(257, 768, 1), (4100, 4352, 1), (8192, 2304, 2), (20000, 2304, 1)])
+@pytest.mark.parametrize("M,K,N", [(2305, 768, 1), (4100, 4352, 1), (8192, 2304, 2), (20000, 2304, 1)])
 @pytest.mark.parametrize("inplace", [False, True], ids=["out", "inplace"])
 def test_dma_gemv_add(fmt, M, K, N, inplace):
     """8192 rows: two row groups per wave (read ahead); 20000: five (another kernel)."""
@@ -134,7 +136,7 @@ def test_dma_zero_codes_give_zero(fmt, N):
     """Codes equal to the offset (q = 0, nibble 8, 5-bit code 16) give exactly zero: the
     staged offset chain of every x block equals the decode's dot product chain bit for
     bit."""
-    M, K = 300, 4352
+    M, K = 2348, 4352
     d = np.full((M, K // 32), 0.75, dtype=np.float16)
     if fmt == si.FMT_Q8_0:
         raw = oracle.pack_q8_0(np.zeros((M, K), dtype=np.int8), d)
