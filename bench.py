@@ -576,8 +576,8 @@ def traffic_for(launch_key):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part "
-              "of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
+              "multi-GPU path; each GPU would run its own share of the rows", file=sys.stderr)
         sys.exit(2)
     import torch
 
