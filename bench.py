@@ -617,6 +617,21 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
+    # The same step captured once as a HIP graph and replayed (the launch path of a
+    # serving loop); reported beside the eager figure.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    graph_ms_per_step = t0.elapsed_time(t1) / args.steps
+    del graph
     # Per-launch timing over the same number of steps, for the roofline of each kernel.
     timer = Timer(torch)
     for _ in range(args.steps):
@@ -659,7 +674,9 @@ def main():
                                "gate+up 2x14336x4096 + SwiGLU, down 4096x14336, LM head 128256x4096), "
                                "Q8_0 pass + Q4_0 pass, N=1",
                    "formats": ["Q8_0", "Q4_0"], "tokens": 1, "step_bytes": int(step_bytes),
-                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "graph_replay": {"ms_per_step": round(graph_ms_per_step, 5),
+                                    "GBps": round(step_bytes / (graph_ms_per_step * 1e-3) / 1e9, 2)}},
         "roofline": {"bound": "hbm",
                      "kernel": (DOMINANT_KERNEL + " (" + dom + ")") if dom == "gemv_Q8_0:lm_head" else dom,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
