@@ -12,7 +12,7 @@ import torch
 import block_quantized_weight_gguf_amd as qmm
 import oracle
 import seeded_inputs as si
-from parity_util import announce, check_linear, check_swiglu, dev
+from parity_util import announce, check_linear, check_residual, check_swiglu, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +103,64 @@ def test_graph_gemm_gate_up_few_tiles():
     got = _replays(g, H, lambda: qmm.qmm_gemm_gate_up_silu(fmt, g_d, u_d, Xd, torch.empty_like(H), I, K, T))
     h_ref, gg, uu, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, X, I, K)
     check_swiglu(got, h_ref, gg, uu, Sg, Su, "graph gemm gate_up")
+
+
+@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_0, si.FMT_Q5_1], ids=["q8_0", "q4_0", "q5_1"])
+def test_graph_decode_chain(fmt):
+    """One decode layer's projections as a replayed graph, on the kernels the 8B step uses:
+    RMSNorm + GEMV on the DMA-fed kernel (3072 rows), RMSNorm + gate/up on the gated
+    kernel, and the down projection with the residual added, fed by the gate/up output of
+    the same graph (DMA-fed, 4096 rows).  Every replay equals the eager calls bit for bit,
+    and the chain matches the oracle."""
+    H, Q, I = 4096, 3072, 3072
+    eps = 1e-5
+    rq = si.weights(fmt, Q, H, 7201)
+    rg = si.weights(fmt, I, H, 7202)
+    ru = si.weights(fmt, I, H, 7203)
+    rd = si.weights(fmt, H, I, 7204)
+    x = si.activations(1, H, 7205)
+    gamma = (1.0 + 0.1 * si.activations(1, H, 7206)[0]).astype(np.float32)
+    Wq, Wg, Wu, Wd, xd, gd = dev(rq), dev(rg), dev(ru), dev(rd), dev(x), dev(gamma)
+    a = torch.empty((1, Q), device="cuda")
+    h = torch.empty((1, I), device="cuda")
+    y = torch.empty((1, H), device="cuda")
+
+    def chain():
+        qmm.qmm_rmsnorm_gemv(fmt, Wq, xd, gd, eps, a, Q, H, 1)
+        qmm.qmm_rmsnorm_gate_up_silu(fmt, Wg, Wu, xd, gd, eps, h, I, H, 1)
+        qmm.qmm_gemv_add(fmt, Wd, h, xd, y, H, I, 1)
+
+    announce(f"graph capture: decode chain fmt={fmt} H={H} Q={Q} I={I}")
+    chain()
+    torch.cuda.synchronize()
+    eager = [t.cpu().numpy().copy() for t in (a, h, y)]
+    for t in (a, h, y):
+        t.fill_(float("nan"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        chain()
+    torch.cuda.synchronize()
+    scratch = torch.empty((1, Q), device="cuda")
+
+    def noise():
+        qmm.qmm_gemv(fmt, Wq, xd, scratch, Q, H, 1)
+
+    for r in range(3):
+        for t in (a, h, y):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, e in zip("ahy", (a, h, y), eager):
+            assert np.array_equal(t.cpu().numpy(), e), f"replay {r}: {name} differs from the eager call"
+        noise()
+        torch.cuda.synchronize()
+
+    a_ref, S = oracle.rmsnorm_matmul_ref(fmt, rq, x, gamma, eps, Q, H)
+    check_linear(eager[0], a_ref, S, f"graph chain rmsnorm gemv fmt={fmt}")
+    h_ref, gg, uu, Sg, Su = oracle.rmsnorm_gate_up_silu_ref(fmt, rg, ru, x, gamma, eps, I, H)
+    check_swiglu(eager[1], h_ref, gg, uu, Sg, Su, f"graph chain gate_up fmt={fmt}")
+    yd, Sd = oracle.matmul_ref(fmt, rd, eager[1], H, I)  # on the h the GPU produced
+    check_residual(eager[2], yd + x.astype(np.float64), Sd, f"graph chain down + residual fmt={fmt}")
