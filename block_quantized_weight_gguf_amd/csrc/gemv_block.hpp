@@ -11,10 +11,11 @@
 //         the exact code; the scale is d / 16 (exact).
 //   Q5_0: the same with the fifth bit: (u ^ 16) << 3 reads as the signed byte
 //         8 * (u - 16); the scale is d / 8.
-//   Q4_1, Q5_1: the unsigned code u as an unsigned byte; per block and token the
-//         lane sums u x and x, and adds d * sum(u x) + m * sum(x).
+//   Q4_1, Q5_1: the unsigned code u as an unsigned byte, each weight formed as
+//         fma(d, u, m) (the exact d * u + m rounded once) before its product with x.
 #pragma once
 
+#include "block_decode.hpp"
 #include "qmm_common.hpp"
 #include "qmm_internal.hpp"
 
@@ -60,14 +61,15 @@ __device__ __forceinline__ void nib_code_bytes(uint32_t cw, uint32_t qh, int i, 
     }
 }
 
-// block_fma for Q4_1, Q5_0, Q5_1 (see the header comment for the code bytes).
+// block_fma for Q4_1, Q5_0, Q5_1 (see the header comment for the code bytes).  The
+// biased formats form each weight w = fma(d, u, m), the exact d u + m rounded once,
+// before its product with x: factoring the bias out (d sum u x + m sum x) would round
+// two sums that can cancel far below sum |w x|.
 template <int FMT, int RU, int NT>
 __device__ __forceinline__ void block_fma_nib(const uint8_t* const (&buf)[RU], const int (&off)[RU],
                                               const float* const (&xb)[NT], float (&acc)[RU][NT]) {
     constexpr bool BIAS = Nib<FMT>::BIAS;
-    float bacc[RU][NT], sx[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) sx[n] = 0.0f;
+    float bacc[RU][NT];
 #pragma unroll
     for (int u = 0; u < RU; ++u)
 #pragma unroll
@@ -86,8 +88,6 @@ __device__ __forceinline__ void block_fma_nib(const uint8_t* const (&buf)[RU], c
         for (int n = 0; n < NT; ++n) {
             xl[n] = *reinterpret_cast<const float4*>(xb[n] + 4 * i);
             xh[n] = *reinterpret_cast<const float4*>(xb[n] + 16 + 4 * i);
-            if constexpr (BIAS) sx[n] += ((xl[n].x + xl[n].y) + (xl[n].z + xl[n].w)) +
-                                         ((xh[n].x + xh[n].y) + (xh[n].z + xh[n].w));
         }
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
@@ -98,6 +98,10 @@ __device__ __forceinline__ void block_fma_nib(const uint8_t* const (&buf)[RU], c
             for (int j = 0; j < 4; ++j) {
                 c[j] = (FMT == 6) ? sbyte_to_float(lo, j) : ubyte_to_float(lo, j);
                 c[4 + j] = (FMT == 6) ? sbyte_to_float(hi, j) : ubyte_to_float(hi, j);
+            }
+            if constexpr (BIAS) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) c[j] = fmaf(d[u], c[j], m[u]);
             }
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
@@ -118,7 +122,7 @@ __device__ __forceinline__ void block_fma_nib(const uint8_t* const (&buf)[RU], c
     for (int u = 0; u < RU; ++u)
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            if constexpr (BIAS) acc[u][n] = fmaf(d[u], bacc[u][n], fmaf(m[u], sx[n], acc[u][n]));
+            if constexpr (BIAS) acc[u][n] += bacc[u][n];
             else acc[u][n] = fmaf(d[u], bacc[u][n], acc[u][n]);
         }
 }
@@ -211,39 +215,69 @@ __device__ __forceinline__ void block_fma(const uint8_t* const (&buf)[RU], const
         for (int n = 0; n < NT; ++n) acc[u][n] = fmaf(d[u], bacc[u][n], acc[u][n]);
 }
 
-// ---- fp16-pair activations with packed dot products (streaming kernel) ----
+// ---- fp16-pair activations with packed dot products (streaming kernels) ----
 //
-// The streaming kernel keeps x in LDS as block floating point: each 32-value block
-// of a token is scaled by a power of two 2^s that brings its largest magnitude into
-// [2^14, 2^15), then rounded to fp16 (x~ = fp16(2^s x)).  That cannot overflow or
-// lose a block to underflow, and every element keeps a relative error <= 2^-11.
-// Codes enter v_dot2_f32_f16 as normal fp16 numbers built with one v_perm against a
-// constant byte (the instruction is accurate to about an fp32 ulp for normal
-// operands; it loses precision on subnormal ones):
-//   Q8_0: u = q + 128 (xor 0x80) as the low byte under 0x64: v = 1024 + u, and
-//         w = d (v - 1152);
-//   Q4_0: the nibble n in bits 4..7 under 0x3C: v = 1 + n/64, and
-//         w = 64 d (v - 1.125);
-//   Q5_0: the nibble as for Q4_0 and the fifth bit h in bit 0 of the high byte,
-//         0x3C | h: v = 1 + h/4 + n/64 = 1 + u/64, and w = 64 d (v - 1.25);
-//   Q4_1, Q5_1: v as for Q4_0 / Q5_0, with offset 1: w = 64 d (v - 1) + m.
-// Both products v x~ are exact in fp32.  With
-//     p = sum_j v_j x~_j   and   c = sum_j v0 x~_j   (v0 = 1152, 1.125, 1.25 or 1),
-// accumulated by the same chain of dot2 steps in the same pair order, a block
-// contributes (d F) (p - c) 2^-s with F = 1 or 64.  Codes all equal to the offset
-// (q = 0, n = 8, u = 16) therefore give exactly zero, and the cancellation costs at most
-// about 2^-24 * 16 * 2 * max(v0 / |v - v0|) ~ 3e-5 of sum |w x| (|v - v0| averages
-// 64 resp. 4/64), so |y - y_exact| <= (2^-11 + 4e-5) sum |w x|, inside the 2e-3 bound.
-// The biased formats add m c 2^-s (c = sum x~ there): the block's sum of x~ w.
+// The streaming kernels keep x in LDS as block floating point: each 32-value block of
+// a token is scaled by a power of two 2^s that brings its largest magnitude into
+// [2^14, 2^15), then rounded to fp16 (x~ = fp16(2^s x)).  Nothing overflows, and every
+// element keeps a relative error <= 2^-11 as long as it is zero or 2^s |x| is a normal
+// fp16 (>= 2^-14).  A block holding a nonzero element below that range (more than
+// about 2^28 under the block's largest) is "wide": staging reports it, and a workgroup
+// that sees one takes the exact fp32 path (gemv_rows_exact) for all its rows instead.
+//
+// Codes enter v_dot2_f32_f16 as exact fp16 numbers.  One v_perm or v_and_or against a
+// constant high byte builds a normal half v = v0 + code * unit, and one packed fp16 add
+// (or fma) removes the offset v0; the difference is representable, so it is exact:
+//   Q8_0: q: the code byte xor 0x80 under 0x64 is v = 1024 + (q + 128); v - 1152;
+//   Q4_0: n - 8: low nibbles under 0x6400 are v = 1024 + n, high ones (in place, bits
+//         4..7) v = 1024 + 16 n; v - 1032, resp. fma(v, 1/16, -72);
+//   Q4_1: n - c, the same with the block's centre c (below) in place of 8;
+//   Q5_0: (u - 16) / 64: the nibble in mantissa bits 4..7 under 0x3C, the fifth bit h
+//         in bit 0 of the high byte 0x3C | h, v = 1 + u/64; v - 1.25;
+//   Q5_1: (u - c) / 64.
+// Every product code * x~ is exact in fp32 (at most 8 + 11 significant bits, and no
+// underflow: |x~| >= 2^-14 and |code| >= 2^-6), so the 16 dot2 steps of a block, each
+// within an fp32 ulp of its exact value (measured), round only terms of sum |w x|: a
+// code equal to the offset contributes exactly zero, and there is no large offset sum
+// to cancel.  A block adds (d F p) 2^-s to the lane's sum, p = sum code * x~ (F = 64
+// for the 5-bit formats, else 1).
+// Biased formats: w = d u + m = d (u - c) + r with r = m + c d (exact) and the integer
+// centre c of block_centre.  Then |r| <= |d| / 2 when -m / d lies in [-1/2, 31 + 1/2];
+// for -m / d in (31 + 1/2, 62] (c = 31) and below -1/2 (c = 0) r has the sign of
+// d (u - c) for every code; above 62 (c = 0, r = m) |w| >= |m| - 31 |d| > (|m| +
+// 31 |d|) / 3.  So |d| |u - c| + |r| <= 3 |d (u - c) + r| = 3 |w| always.  The block adds
+// (d F p + r X) 2^-s with X = sum x~ (a dot2 chain formed at staging), whose rounding
+// is therefore within 3 times that of sum |w x~|.  (Factoring out m alone,
+// d sum u x + m sum x, cancels without bound when d u + m is small against m.)
+// Bound: a term passes through at most 16 dot2 steps, 2 roundings into the lane's sum,
+// K / 2048 later block additions of that lane, 6 butterfly levels and 1 epilogue
+// product, so with u = 2^-23 per step
+//     |y - y_exact| <= (2^-11 + 3 (25 + K / 2048) 2^-23) (1 + 2^-11) sum_k |w_k x_k|,
+// i.e. below 1.3e-3 sum |w x| for every K up to 2^22 (5.0e-4 at K = 14336).
 // Per block the LDS copy holds 16 dwords of fp16 pairs in the order the codes are
-// unpacked (see stage_x16), then c and 2^-s, padded to XS16 dwords so that the
-// lanes' 16-byte reads at a stride of XS16 dwords hit distinct banks.
+// unpacked (see stage_x16), then X (biased formats) and 2^-s, padded to XS16 dwords so
+// that the lanes' 16-byte reads at a stride of XS16 dwords hit distinct banks.
 constexpr int XS16 = 20;
 
 typedef _Float16 h2x_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ h2x_t as_h2x(uint32_t u) { return __builtin_bit_cast(h2x_t, u); }
+__device__ __forceinline__ uint32_t h2x_bits(h2x_t h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(as_h2x(a), as_h2x(b), c, false);
+}
+// Packed fp16 a + b and a * b + c on bit patterns (exact wherever used here).
+__device__ __forceinline__ uint32_t add_h2(uint32_t a, uint32_t b) { return h2x_bits(as_h2x(a) + as_h2x(b)); }
+__device__ __forceinline__ uint32_t fma_h2(uint32_t a, uint32_t b, uint32_t c) {
+    return h2x_bits(__builtin_elementwise_fma(as_h2x(a), as_h2x(b), as_h2x(c)));
+}
+// A constant held in a vector register, opaque to the optimiser: (a & m) | vconst(k)
+// then selects one v_and_or_b32 (a gfx9 VOP3 instruction reads at most one scalar
+// or literal operand; with both constants as literals the compiler emits v_and plus
+// v_or).  Pure (a register move, no side effects), so it is hoisted out of loops.
+__device__ __forceinline__ uint32_t vconst(uint32_t k) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(k));
+    return r;
 }
 // Code pairs: bytes 0 and 2 (sel02) or 1 and 3 (sel13) of v as the low bytes of the
 // two 16-bit halves, under the high byte of k (v_perm_b32 of {k, v}).
@@ -252,13 +286,25 @@ __device__ __forceinline__ uint32_t sel13(uint32_t v, uint32_t k) { return __bui
 
 template <int FMT>
 struct DotCode {
-    static constexpr uint32_t K = FMT == 8 ? 0x64646464u : 0x3C3C3C3Cu;    // high bytes
-    static constexpr uint32_t V0 = FMT == 8   ? 0x64806480u   // offset code pair
-                                   : FMT == 2 ? 0x3C803C80u
-                                   : FMT == 6 ? 0x3D003D00u
-                                              : 0x3C003C00u;
-    static constexpr float F = FMT == 8 ? 1.0f : 64.0f;
+    static constexpr bool NIB4 = FMT == 2 || FMT == 3;                  // v_and_or construction
+    static constexpr bool BIAS = FMT == 3 || FMT == 7;
+    static constexpr uint32_t K = FMT == 8 ? 0x64646464u : 0x3C3C3C3Cu;  // v_perm high bytes
+    // -v0 as an fp16 pair: -1152 (Q8_0), -1032 (Q4_0 low nibbles), -1.25 (Q5_0).
+    static constexpr uint32_t NEG = FMT == 8 ? 0xE480E480u : FMT == 2 ? 0xE408E408u : 0xBD00BD00u;
+    static constexpr uint32_t NEG_HI = 0xD480D480u;                     // -72 (Q4_0 high nibbles)
+    static constexpr uint32_t SIXTEENTH = 0x2C002C00u;                 // 1/16
+    static constexpr float F = (FMT == 6 || FMT == 7) ? 64.0f : 1.0f;
 };
+
+// The integer centre c of a biased block: round(-m / d) clamped to [0, 31] while
+// -m / d <= 62, else 0 (also for a NaN quotient: d = m = 0, or both infinite).  With
+// this choice r = m + c d is exact in fp32 (c = 0: r = m; otherwise |m| <= 62 |d| and
+// m is no finer than half d's last place, so r spans at most 19 bits).
+__device__ __forceinline__ int block_centre(float d, float m) {
+    const float t = -m * __builtin_amdgcn_rcpf(d);
+    const float c = fminf(fmaxf(t + 0.5f, 0.0f), 31.0f);
+    return t <= 62.0f ? static_cast<int>(c) : 0;
+}
 
 // v from another lane of the row, as selected by the DPP control CTRL (all lanes of
 // the 8-lane groups using it are active).
@@ -272,76 +318,101 @@ __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(hi))) << 16);
 }
 
+// Unsigned key of |v| that orders nonzero magnitudes and sends +-0 above them all:
+// 2 * bits(|v|) - 2 (the sign bit shifted out).
+__device__ __forceinline__ uint32_t mag_key(float v) { return (__float_as_uint(v) << 1) - 2u; }
+
+// The scale exponent se of a block with largest magnitude m (2^se m in [2^14, 2^15)),
+// 2^se, 2^-se, and the key of 2^(-14 - se): a nonzero element whose key lies below it
+// would not be a normal fp16 once scaled.
+struct BlockScale {
+    float sc, inv;
+    uint32_t wide_key;
+};
+__device__ __forceinline__ BlockScale block_scale(float m) {
+    const int e = static_cast<int>((__float_as_uint(m) >> 23) & 0xFFu) - 127;  // floor(log2 m); -127 for 0
+    const int se = min(126, 14 - e);                                            // >= -114 (m <= inf)
+    BlockScale b;
+    b.sc = __uint_as_float(static_cast<uint32_t>(se + 127) << 23);   // 2^se
+    b.inv = __uint_as_float(static_cast<uint32_t>(127 - se) << 23);  // 2^-se
+    b.wide_key = mag_key(ldexpf(1.0f, -14 - se));                    // 2^-140 .. 2^100, exact
+    return b;
+}
+
 // Stage chunk c (0..7: values 4c..4c+3) of one block of one token.  Called by 8
 // consecutive lanes per block, all active, lane c of the group holding chunk c.
-// They agree on the block's scale with three DPP exchanges; stage_chain fills in
-// c once every block is written.  Pair order matches
-// the unpacking in block_dot:
+// They agree on the block's scale with three DPP exchanges; stage_chain fills in X
+// (biased formats) once every block is written.  Pair order matches the unpacking in
+// block_dot:
 //   Q8_0: dword 2c holds (x[4c], x[4c+2]), dword 2c+1 holds (x[4c+1], x[4c+3]) --
 //         the lanes of sel02 / sel13 applied to code dword c;
-//   Q4_0: code dword i holds weights 4i..4i+3 (low nibbles) and 16+4i..16+4i+3
-//         (high nibbles); dwords 4i, 4i+1 pair the low ones, 4i+2, 4i+3 the high.
+//   nibble formats: code dword i holds weights 4i..4i+3 (low nibbles) and
+//         16+4i..16+4i+3 (high nibbles); dwords 4i, 4i+1 pair the low ones, 4i+2,
+//         4i+3 the high.
+// Returns true when one of the lane's four values makes the block wide.
 template <int FMT>
-__device__ __forceinline__ void stage_x16(float4 v, int c, uint32_t* blk) {
+__device__ __forceinline__ bool stage_x16(float4 v, int c, uint32_t* blk) {
     float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     // Max over the 8 lanes with DPP moves: swap neighbours, swap pairs (quad_perm),
     // then mirror the two quads of the 8-lane half row.
     m = fmaxf(m, dpp_f32<0xB1>(m));   // quad_perm [1, 0, 3, 2]
     m = fmaxf(m, dpp_f32<0x4E>(m));   // quad_perm [2, 3, 0, 1]
     m = fmaxf(m, dpp_f32<0x141>(m));  // row_half_mirror
-    const int e = static_cast<int>((__float_as_uint(m) >> 23) & 0xFFu) - 127;  // floor(log2 m); -127 for 0
-    const int se = min(126, 14 - e);                                            // >= -114 (m <= inf)
-    const float sc = __uint_as_float(static_cast<uint32_t>(se + 127) << 23);     // 2^se
-    const float inv = __uint_as_float(static_cast<uint32_t>(127 - se) << 23);    // 2^-se
-    const uint32_t w0 = pack_h2(v.x * sc, v.z * sc), w1 = pack_h2(v.y * sc, v.w * sc);
+    const BlockScale s = block_scale(m);
+    const uint32_t w0 = pack_h2(v.x * s.sc, v.z * s.sc), w1 = pack_h2(v.y * s.sc, v.w * s.sc);
     const int slot = (FMT == 8) ? 2 * c : 4 * (c & 3) + ((c >> 2) << 1);
     *reinterpret_cast<uint2*>(blk + slot) = make_uint2(w0, w1);
-    if (c == 0) blk[17] = __float_as_uint(inv);
+    if (c == 0) blk[17] = __float_as_uint(s.inv);
+    const uint32_t k = min(min(mag_key(v.x), mag_key(v.y)), min(mag_key(v.z), mag_key(v.w)));
+    return k < s.wide_key;
 }
 
 // One whole block of one token staged by one lane: v holds its 32 values (chunk c =
-// values 4c..4c+3).  The same block floating point and pair order as stage_x16,
-// and the offset chain c (stage_chain's dot2 steps in block_dot's order, so c is
-// bit-identical) formed from the lane's own registers; the block's 20 dwords go
-// out as five 16-byte LDS writes.
+// values 4c..4c+3).  The same block floating point and pair order as stage_x16, and
+// X (biased formats: stage_chain's dot2 steps, so it is bit-identical) formed from
+// the lane's own registers; the block's 20 dwords go out as five 16-byte LDS writes.
+// Returns true when the block is wide.
 template <int FMT>
-__device__ __forceinline__ void stage_block(const float4 (&v)[8], uint32_t* blk) {
+__device__ __forceinline__ bool stage_block(const float4 (&v)[8], uint32_t* blk) {
     float m = 0.0f;
+    uint32_t k = 0xFFFFFFFFu;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < 8; ++c) {
         m = fmaxf(m, fmaxf(fmaxf(fabsf(v[c].x), fabsf(v[c].y)), fmaxf(fabsf(v[c].z), fabsf(v[c].w))));
-    const int e = static_cast<int>((__float_as_uint(m) >> 23) & 0xFFu) - 127;  // floor(log2 m); -127 for 0
-    const int se = min(126, 14 - e);
-    const float sc = __uint_as_float(static_cast<uint32_t>(se + 127) << 23);   // 2^se
-    const float inv = __uint_as_float(static_cast<uint32_t>(127 - se) << 23);  // 2^-se
+        k = min(k, min(min(mag_key(v[c].x), mag_key(v[c].y)), min(mag_key(v[c].z), mag_key(v[c].w))));
+    }
+    const BlockScale s = block_scale(m);
     uint32_t w[16];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int slot = (FMT == 8) ? 2 * c : 4 * (c & 3) + ((c >> 2) << 1);
-        w[slot] = pack_h2(v[c].x * sc, v[c].z * sc);
-        w[slot + 1] = pack_h2(v[c].y * sc, v[c].w * sc);
+        w[slot] = pack_h2(v[c].x * s.sc, v[c].z * s.sc);
+        w[slot + 1] = pack_h2(v[c].y * s.sc, v[c].w * s.sc);
     }
     float chain = 0.0f;
+    if constexpr (DotCode<FMT>::BIAS) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) chain = dot2(DotCode<FMT>::V0, w[i], chain);
+        for (int i = 0; i < 16; ++i) chain = dot2(0x3C003C00u, w[i], chain);
+    }
     uint4* o = reinterpret_cast<uint4*>(blk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
-    o[4] = make_uint4(__float_as_uint(chain), __float_as_uint(inv), 0u, 0u);
+    o[4] = make_uint4(__float_as_uint(chain), __float_as_uint(s.inv), 0u, 0u);
+    return k < s.wide_key;
 }
 
-// After the staged pairs are visible: c of one block, the dot2 chain over its 16
-// dwords in slot order with every code equal to the offset code (block_dot's chain).
+// Biased formats, after the staged pairs are visible: X of one block, the dot2 chain
+// of its 16 dwords against (1, 1) in slot order.
 template <int FMT>
 __device__ __forceinline__ void stage_chain(uint32_t* blk) {
     float chain = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint4 w = *reinterpret_cast<const uint4*>(blk + 4 * i);
-        chain = dot2(DotCode<FMT>::V0, w.x, chain);
-        chain = dot2(DotCode<FMT>::V0, w.y, chain);
-        chain = dot2(DotCode<FMT>::V0, w.z, chain);
-        chain = dot2(DotCode<FMT>::V0, w.w, chain);
+        chain = dot2(0x3C003C00u, w.x, chain);
+        chain = dot2(0x3C003C00u, w.y, chain);
+        chain = dot2(0x3C003C00u, w.z, chain);
+        chain = dot2(0x3C003C00u, w.w, chain);
     }
     blk[16] = __float_as_uint(chain);
 }
@@ -351,26 +422,41 @@ __device__ __forceinline__ void stage_chain(uint32_t* blk) {
 template <int FMT, int RU, int NT>
 __device__ __forceinline__ void block_dot(const uint8_t* const (&buf)[RU], const int (&off)[RU],
                                           const uint32_t* const (&xb)[NT], float (&acc)[RU][NT]) {
+    using DC = DotCode<FMT>;
     constexpr int NDW = FMT == 8 ? 8 : 4;
-    constexpr uint32_t KB = DotCode<FMT>::K;
-    constexpr bool BIAS = FMT != 8 && Nib<FMT>::BIAS;
-    constexpr bool FIVE = FMT != 8 && Nib<FMT>::FIVE;
+    constexpr uint32_t KB = DC::K;
+    constexpr bool BIAS = DC::BIAS;
+    constexpr bool FIVE = FMT == 6 || FMT == 7;
     float p[RU][NT];
 #pragma unroll
     for (int u = 0; u < RU; ++u)
 #pragma unroll
         for (int n = 0; n < NT; ++n) p[u][n] = 0.0f;
-    float d[RU], mb[RU];
-    uint32_t cw[RU][NDW], qh[RU];
+    float d[RU], r[RU];
+    uint32_t cw[RU][NDW], qh[RU], nlo[RU], nhi[RU];
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
+        nlo[u] = DC::NEG;
+        nhi[u] = DC::NEG_HI;
+        r[u] = 0.0f;
         if constexpr (FMT == 8 || FMT == 2) {
             d[u] = half_bits_to_float(lds_read_u16(buf[u], off[u]));
             lds_read_dwords<NDW>(buf[u], off[u] + 2, cw[u]);
-            mb[u] = 0.0f;
             qh[u] = 0;
         } else {
-            read_nib_block<FMT>(buf[u], off[u], d[u], mb[u], qh[u], cw[u]);
+            float m;
+            read_nib_block<FMT>(buf[u], off[u], d[u], m, qh[u], cw[u]);
+            if constexpr (BIAS) {
+                const int c = block_centre(d[u], m);
+                const uint32_t cu = static_cast<uint32_t>(c);
+                r[u] = fmaf(static_cast<float>(c), d[u], m);
+                if constexpr (FMT == 3) {
+                    nlo[u] = (0xE400u | cu) * 0x10001u;         // -(1024 + c)
+                    nhi[u] = (0xD400u | (cu << 4)) * 0x10001u;  // -(64 + c)
+                } else {
+                    nlo[u] = (0xBC00u | (cu << 4)) * 0x10001u;  // -(1 + c / 64)
+                }
+            }
         }
     }
 #pragma unroll
@@ -383,17 +469,29 @@ __device__ __forceinline__ void block_dot(const uint8_t* const (&buf)[RU], const
             uint32_t a0, a1, a2, a3;
             if constexpr (FMT == 8) {
                 const uint32_t t0 = cw[u][2 * i] ^ 0x80808080u, t1 = cw[u][2 * i + 1] ^ 0x80808080u;
-                a0 = sel02(t0, KB), a1 = sel13(t0, KB), a2 = sel02(t1, KB), a3 = sel13(t1, KB);
-            } else if constexpr (FIVE) {
-                // Nibbles as for Q4_0; the high byte of weight j's half is 0x3C | h_j, one
-                // word per four weights, and the byte selectors pair byte j with byte j.
+                a0 = add_h2(sel02(t0, KB), nlo[u]);
+                a1 = add_h2(sel13(t0, KB), nlo[u]);
+                a2 = add_h2(sel02(t1, KB), nlo[u]);
+                a3 = add_h2(sel13(t1, KB), nlo[u]);
+            } else if constexpr (DC::NIB4) {
+                // (w4i, w4i+2), (w4i+1, w4i+3) from the low nibbles of bytes 0, 2 and 1, 3;
+                // (w16+4i, w16+4i+2), (w16+4i+1, w16+4i+3) from the high nibbles.
+                const uint32_t w = cw[u][i], t = w >> 8, hb = vconst(0x64006400u);
+                a0 = add_h2((w & 0x000F000Fu) | hb, nlo[u]);
+                a1 = add_h2((t & 0x000F000Fu) | hb, nlo[u]);
+                a2 = fma_h2((w & 0x00F000F0u) | hb, DC::SIXTEENTH, nhi[u]);
+                a3 = fma_h2((t & 0x00F000F0u) | hb, DC::SIXTEENTH, nhi[u]);
+            } else {
+                static_assert(FIVE, "5-bit formats");
+                // Nibbles in bits 4..7 of the low byte; the high byte of weight j's half is
+                // 0x3C | h_j, one word per four weights, and the byte selectors pair byte j
+                // with byte j.
                 const uint32_t lo = (cw[u][i] << 4) & 0xF0F0F0F0u, hi = cw[u][i] & 0xF0F0F0F0u;
                 const uint32_t hl = spread4(qh[u] >> (4 * i)) | KB, hh = spread4(qh[u] >> (16 + 4 * i)) | KB;
-                a0 = __builtin_amdgcn_perm(hl, lo, 0x06020400u), a1 = __builtin_amdgcn_perm(hl, lo, 0x07030501u);
-                a2 = __builtin_amdgcn_perm(hh, hi, 0x06020400u), a3 = __builtin_amdgcn_perm(hh, hi, 0x07030501u);
-            } else {
-                const uint32_t lo = (cw[u][i] << 4) & 0xF0F0F0F0u, hi = cw[u][i] & 0xF0F0F0F0u;
-                a0 = sel02(lo, KB), a1 = sel13(lo, KB), a2 = sel02(hi, KB), a3 = sel13(hi, KB);
+                a0 = add_h2(__builtin_amdgcn_perm(hl, lo, 0x06020400u), nlo[u]);
+                a1 = add_h2(__builtin_amdgcn_perm(hl, lo, 0x07030501u), nlo[u]);
+                a2 = add_h2(__builtin_amdgcn_perm(hh, hi, 0x06020400u), nlo[u]);
+                a3 = add_h2(__builtin_amdgcn_perm(hh, hi, 0x07030501u), nlo[u]);
             }
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
@@ -406,22 +504,22 @@ __device__ __forceinline__ void block_dot(const uint8_t* const (&buf)[RU], const
             }
         }
     }
-    float cs[NT], inv[NT];
+    float xs[NT], inv[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const uint2 t = *reinterpret_cast<const uint2*>(xb[n] + 16);
-        cs[n] = __uint_as_float(t.x);
+        xs[n] = __uint_as_float(t.x);
         inv[n] = __uint_as_float(t.y);
     }
-    // ((p - c) * d F) * 2^-s: each factor stays within the block's own contribution,
-    // so nothing overflows unless that contribution does.
+    // (p d F) * 2^-s: each factor stays within the block's own contribution, so
+    // nothing overflows unless that contribution does.
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
-        const float dF = d[u] * DotCode<FMT>::F;
+        const float dF = d[u] * DC::F;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            if constexpr (BIAS) acc[u][n] = fmaf(fmaf(mb[u], cs[n], (p[u][n] - cs[n]) * dF), inv[n], acc[u][n]);
-            else acc[u][n] = fmaf((p[u][n] - cs[n]) * dF, inv[n], acc[u][n]);
+            if constexpr (BIAS) acc[u][n] = fmaf(fmaf(r[u], xs[n], p[u][n] * dF), inv[n], acc[u][n]);
+            else acc[u][n] = fmaf(p[u][n] * dF, inv[n], acc[u][n]);
         }
     }
 }
@@ -497,6 +595,85 @@ __device__ __forceinline__ void reduce_store(float (&acc)[RU][NT], int lane, int
         }
         if (holder && u < R && n < NT && r < M) y[n * ldy + r] = silu(gv) * upv;
     }
+}
+
+// The exact fp32 form of the streaming kernels' product for one wave's row groups
+// (groups first_group + gi * group_stride, gi < my_groups), taken by a whole workgroup
+// when a block of x is wide: weights decoded exactly (the biased ones rounded once, as
+// by qmm_dequant) straight from the weight buffer, fp32 x (EP_NORM: times gamma) from
+// global memory, fp32 FMAs (each block's 32 products summed first, then added to the
+// lane's total).  It keeps the error bound for inputs whose block floating point would
+// not; no workload of interest takes it.
+template <int FMT, int NT, int R, bool GATED, int EP>
+__device__ inline void gemv_rows_exact(const uint8_t* Wg, const uint8_t* Wu, const float* x, float* y, int M,
+                                             int K, int64_t ldx, int64_t ldy, DecodeEpi epi, float scale,
+                                             int first_group, int group_stride, int my_groups, int lane) {
+    constexpr int RU = GATED ? 2 * R : R;
+    constexpr int BB = Fmt<FMT>::BB;
+    const int nb = K / kQK;
+    const int64_t rb = static_cast<int64_t>(nb) * BB;
+    for (int gi = 0; gi < my_groups; ++gi) {
+        const int g = first_group + gi * group_stride;
+        float acc[RU][NT];
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[u][n] = 0.0f;
+        for (int b = lane; b < nb; b += kWave) {
+            float bacc[RU][NT];
+#pragma unroll
+            for (int u = 0; u < RU; ++u)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) bacc[u][n] = 0.0f;
+            for (int c = 0; c < 4; ++c) {
+                float xv[NT][8];
+                const int64_t k0 = 32 * static_cast<int64_t>(b) + 8 * c;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const float4 lo = *reinterpret_cast<const float4*>(x + n * ldx + k0);
+                    const float4 hi = *reinterpret_cast<const float4*>(x + n * ldx + k0 + 4);
+                    xv[n][0] = lo.x, xv[n][1] = lo.y, xv[n][2] = lo.z, xv[n][3] = lo.w;
+                    xv[n][4] = hi.x, xv[n][5] = hi.y, xv[n][6] = hi.z, xv[n][7] = hi.w;
+                    if constexpr (EP == EP_NORM) {
+                        const float4 gl = *reinterpret_cast<const float4*>(epi.gamma + k0);
+                        const float4 gh = *reinterpret_cast<const float4*>(epi.gamma + k0 + 4);
+                        xv[n][0] *= gl.x, xv[n][1] *= gl.y, xv[n][2] *= gl.z, xv[n][3] *= gl.w;
+                        xv[n][4] *= gh.x, xv[n][5] *= gh.y, xv[n][6] *= gh.z, xv[n][7] *= gh.w;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < RU; ++u) {
+                    const int64_t row = min(g * R + (u % R), M - 1);  // rows past M are never stored
+                    const uint8_t* wb = (GATED && u >= R) ? Wu : Wg;
+                    float w[8];
+                    decode_chunk_f32<FMT, 8>(wb + row * rb + static_cast<int64_t>(b) * BB, c, w);
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) bacc[u][n] = fmaf(w[j], xv[n][j], bacc[u][n]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < RU; ++u)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[u][n] += bacc[u][n];
+        }
+        reduce_store<R, RU, NT, GATED, EP>(acc, lane, g * R, M, y, ldy, scale, epi.res);
+    }
+}
+
+// Whether any wave of the workgroup staged a wide block: each wave's lane 0 writes its
+// ballot to flags[wave] before a workgroup barrier; read after it.  Uniform.
+__device__ __forceinline__ void publish_wide(bool wide, uint32_t* flags, int wave, int lane) {
+    const unsigned long long b = __ballot(wide);
+    if (lane == 0) flags[wave] = b != 0ull ? 1u : 0u;
+}
+template <int WAVES>
+__device__ __forceinline__ bool any_wide(const uint32_t* flags) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) a |= flags[w];
+    return __builtin_amdgcn_readfirstlane(a) != 0;
 }
 
 }  // namespace qmm

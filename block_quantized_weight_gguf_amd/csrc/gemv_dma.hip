@@ -50,14 +50,15 @@ struct DmaGeom {
     static_assert((8 * BB) % 16 == 0, "8-block multiples are whole 16-byte chunks");
 };
 
-// LDS of one instance: S ring stages of WAVES * RU slots, the norm partials, and
-// XCAP bytes left for x (NT tokens x K / 32 blocks x XS16 dwords).
+// LDS of one instance: S ring stages of WAVES * RU slots, the norm partials, the
+// per-wave wide-block flags, and XCAP bytes left for x (NT tokens x K / 32 blocks x
+// XS16 dwords).
 template <int FMT, int NT, int RU, int WAVES, int S>
 struct DmaLds {
     static constexpr int kMax = 160 * 1024;
     static constexpr int STAGE = WAVES * RU * DmaGeom<FMT>::SLOT + DG_PAD;
     static constexpr int RING = 2 * STAGE + (S > 2 ? STAGE : 16) + (S > 3 ? STAGE : 16);
-    static constexpr int XCAP = (kMax - RING - WAVES * NT * 4) / 16 * 16;
+    static constexpr int XCAP = (kMax - RING - WAVES * NT * 4 - WAVES * 4) / 16 * 16;
     static_assert(XCAP >= 16 * XS16 * 4, "room for x");
 };
 
@@ -133,6 +134,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
     using L = DmaLds<FMT, NT, RU, WAVES, S>;
     __shared__ __align__(16) uint32_t xs[L::XCAP / 4];
     __shared__ float red[WAVES * NT];
+    __shared__ uint32_t wflag[WAVES];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -180,14 +182,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
     // weights right after it: converting x then waits only for its own loads, and the
     // weight DMAs stay in flight while x is staged.  x -> LDS once, one lane per
     // (token, 32-value block): the lane loads the block's 8 float4 (EP_NORM: times
-    // gamma, with the sum of squares of x gathered on the way) and stages it with its
-    // offset chain (stage_block).  Only the first round's loads precede the DMAs.
+    // gamma, with the sum of squares of x gathered on the way) and stages it
+    // (stage_block), noting whether the block is wide.  Only the first round's loads
+    // precede the DMAs.
     constexpr int XT = WAVES * kWave;  // blocks per round
     const int nxb = NT * nb;           // blocks to stage
     float4 xv[8], gv[8];
     float ss[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) ss[n] = 0.0f;
+    bool wide = false;
     // Loads are unconditional (index clamped; surplus lanes re-read the last block
     // and stage nothing): loads under a branch make the compiler wait for every
     // outstanding load, the weight DMAs included, before their use.
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
 #pragma unroll
                 for (int k = 0; k < NT; ++k) ss[k] += (k == n) ? q : 0.0f;
             }
-            stage_block<FMT>(xv, xs + n * xstride + b * XS16);
+            wide |= stage_block<FMT>(xv, xs + n * xstride + b * XS16);
         }
     };
     load_round(threadIdx.x);
@@ -265,10 +269,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
         stage_round(j0);
     }
     if constexpr (EP == EP_NORM) norm_partials<NT>(ss, red, wave, lane);
+    publish_wide(wide, wflag, wave, lane);
     // LDS-only barrier: a full __syncthreads would also wait for the weight DMAs.
     lds_barrier();
     float scale = 1.0f;
     if constexpr (EP == EP_NORM) scale = norm_scale<NT>(red, WAVES, reduced_token<RU, NT>(lane), K, epi.eps);
+    if (any_wide<WAVES>(wflag)) {
+        // A wide block of x: the exact fp32 path for this workgroup's rows (every
+        // workgroup stages all of x, so all of them take it).  The ring's DMAs land first.
+        wait_vm<0>();
+        gemv_rows_exact<FMT, NT, R, GATED, EP>(Wg, Wu, x, y, M, K, ldx, ldy, epi, scale, wid, nw, my_groups, lane);
+        return;
+    }
 
     // One task from stage array `stage`, then its refill with the task S ahead.
     TaskCursor cc{0, 0};

@@ -6,10 +6,11 @@
 // only large operand), so this kernel is organised to keep HBM busy with as few
 // instructions per byte as possible:
 //   * One workgroup per CU (LDS-limited).  x (all K, NT tokens) is copied into LDS
-//     once, as block-scaled fp16 pairs (stage_x16); after that single barrier the
-//     waves never synchronise again.  Dot products run on v_dot2_f32_f16 with the
-//     codes as fp16 subnormals (block_dot), about half the VALU work of a
-//     convert and an FMA per weight.
+//     once, as block-scaled fp16 pairs (stage_x16); after that barrier (and, for the
+//     biased formats, a second one for the blocks' sums of x) the waves never
+//     synchronise again.  Dot products run on v_dot2_f32_f16 with the codes as exact
+//     small fp16 numbers (block_dot), fewer VALU instructions than a convert and an
+//     FMA per weight.
 //   * Each wave walks a list of tasks.  A task is R rows (2R row units when gated:
 //     R gate rows and the same R up rows) x one K slice of 64*BPL blocks (BPL = 1
 //     for Q8_0, 2 for Q4_0, so a row slice is ~2.2 KB either way).  Each row
@@ -133,6 +134,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
     float ss[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) ss[n] = 0.0f;
+    bool wide = false;
     // Loads are unconditional (index clamped; surplus lanes re-read the last chunk
     // and stage nothing): loads under a branch make the compiler wait for every
     // outstanding load, the weight DMAs included, before their use.
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
                         ss[n] = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss[n]))));
                         v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
                     }
-                    stage_x16<FMT>(v, j & 7, xs + n * xstride + (j >> 3) * XS16);
+                    wide |= stage_x16<FMT>(v, j & 7, xs + n * xstride + (j >> 3) * XS16);
                 }
             }
         }
@@ -173,13 +175,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
         stage_round(j0);
     }
     float* red = reinterpret_cast<float*>(smem + xs_bytes + WAVES * (RU * ROWBUF));
+    uint32_t* wflag = reinterpret_cast<uint32_t*>(red + WAVES * NT);
     if constexpr (EP == EP_NORM) norm_partials<NT>(ss, red, wave, lane);
+    publish_wide(wide, wflag, wave, lane);
     // LDS-only barriers: a full __syncthreads would also wait for the weight loads.
     lds_barrier();
-    for (int b = threadIdx.x; b < NT * nb; b += WAVES * kWave) stage_chain<FMT>(xs + b * XS16);
-    lds_barrier();
+    if constexpr (DotCode<FMT>::BIAS) {
+        for (int b = threadIdx.x; b < NT * nb; b += WAVES * kWave) stage_chain<FMT>(xs + b * XS16);
+        lds_barrier();
+    }
     float scale = 1.0f;
     if constexpr (EP == EP_NORM) scale = norm_scale<NT>(red, WAVES, reduced_token<RU, NT>(lane), K, epi.eps);
+    if (any_wide<WAVES>(wflag)) {
+        // A wide block of x: the exact fp32 path for this workgroup's rows (every
+        // workgroup stages all of x, so all of them take it).
+        gemv_rows_exact<FMT, NT, R, GATED, EP>(Wg, Wu, x, y, M, K, ldx, ldy, epi, scale, wid, nw, my_groups, lane);
+        return;
+    }
 
     for (int t0 = 0; t0 < ntask; t0 += D) {
 #pragma unroll
@@ -255,7 +267,7 @@ static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y,
         M -= 1;  // every chunk of the first M - 1 rows ends at most 15 bytes into the last row
     }
     const int64_t xs_bytes = ((NT * nb * XS16 * 4) + 15) / 16 * 16;
-    const int64_t lds = xs_bytes + static_cast<int64_t>(WAVES) * RU * G::ROWBUF + (EP == EP_NORM ? WAVES * NT * 4 : 0);
+    const int64_t lds = xs_bytes + static_cast<int64_t>(WAVES) * RU * G::ROWBUF + WAVES * NT * 4 + WAVES * 4;
     constexpr int64_t kMaxLds = 160 * 1024;
     if (lds > kMaxLds) return 0;
     auto kern = gemv_stream_kernel<FMT, NT, R, GATED, WAVES, D, EP>;

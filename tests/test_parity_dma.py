@@ -133,9 +133,9 @@ def test_dma_gemv_add(fmt, M, K, N, inplace):
 @pytest.mark.parametrize("fmt", FMTS + [si.FMT_Q5_0], ids=FID.get)
 @pytest.mark.parametrize("N", [1, 3])
 def test_dma_zero_codes_give_zero(fmt, N):
-    """Codes equal to the offset (q = 0, nibble 8, 5-bit code 16) give exactly zero: the
-    staged offset chain of every x block equals the decode's dot product chain bit for
-    bit."""
+    """Codes equal to the zero code (q = 0, nibble 8, 5-bit code 16) give exactly zero:
+    the offset is removed in fp16 before the dot products, so such codes enter them as
+    exact zeros."""
     M, K = 2348, 4352
     d = np.full((M, K // 32), 0.75, dtype=np.float16)
     if fmt == si.FMT_Q8_0:
