@@ -15,7 +15,8 @@
 //     weight tile.  The decode therefore happens once per (tile, block), not once
 //     per MFMA.
 //   * The activation tile (256 tokens x 64 halfs) is copied with coalesced 16-byte
-//     loads; fp32 activations (the batched-GEMV hand-off) are rounded to fp16 here.
+//     loads.  Tokens are fp16; fp32 ones (the batched-GEMV hand-off) arrive scaled
+//     per token (scale_tokens_f16) and the epilogue multiplies by tscale[t].
 //   * Global loads for step k+1 are issued before the MFMAs of step k, so HBM
 //     latency hides behind the matrix work; LDS holds one stage.
 //   * LDS rows are padded from 128 to 144 bytes so the 16-lane groups of each
@@ -203,10 +204,11 @@ __device__ __forceinline__ void decode_store(const RawRow<FMT>& rr, _Float16* ds
     for (int i = 0; i < 8; ++i) d4[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
 }
 
-template <int FMT, bool GATED, bool XF32>
+template <int FMT, bool GATED>
 __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(const uint8_t* __restrict__ Wg,
                                                                 const uint8_t* __restrict__ Wu,
-                                                                const void* __restrict__ Xv, float* __restrict__ Y,
+                                                                const void* __restrict__ Xv,
+                                                                const float* __restrict__ tscale, float* __restrict__ Y,
                                                                 int M, int K, int T, int align4) {
     __shared__ __align__(16) _Float16 Ws[GM_BM * GM_LDK];
     __shared__ __align__(16) _Float16 Xs[GM_BN * GM_LDK];
@@ -246,20 +248,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(const uint8_t* __
             const int tr = c >> 3, kc = (c & 7) * 8;
             const int t = t0 + tr;
             const bool ok = t < T && k0 + kc < K;
-            if constexpr (XF32) {
-                const float* xp = static_cast<const float*>(Xv) + static_cast<int64_t>(t) * K + k0 + kc;
-                if (ok) {
-                    const float4 a = reinterpret_cast<const float4*>(xp)[0];
-                    const float4 b = reinterpret_cast<const float4*>(xp)[1];
-                    xr[i] = make_uint4(pack_half2(a.x, a.y), pack_half2(a.z, a.w), pack_half2(b.x, b.y),
-                                       pack_half2(b.z, b.w));
-                } else {
-                    xr[i] = make_uint4(0, 0, 0, 0);
-                }
-            } else {
-                const _Float16* xp = static_cast<const _Float16*>(Xv) + static_cast<int64_t>(t) * K + k0 + kc;
-                xr[i] = ok ? *reinterpret_cast<const uint4*>(xp) : make_uint4(0, 0, 0, 0);
-            }
+            const _Float16* xp = static_cast<const _Float16*>(Xv) + static_cast<int64_t>(t) * K + k0 + kc;
+            xr[i] = ok ? *reinterpret_cast<const uint4*>(xp) : make_uint4(0, 0, 0, 0);
         }
     };
     auto store_x = [&]() {
@@ -321,10 +311,11 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(const uint8_t* __
             for (int j = 0; j < 8; ++j) {
                 const int t = t0 + wn * 128 + 16 * j + ec;
                 if (t < T) {
+                    const float sc = tscale != nullptr ? tscale[t] : 1.0f;
                     float* yp = Y + static_cast<int64_t>(t) * M + m;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (m + e < M) yp[e] = acc[i][j][e];
+                        if (m + e < M) yp[e] = acc[i][j][e] * sc;
                 }
             }
         }
@@ -337,58 +328,63 @@ __global__ __launch_bounds__(GM_THREADS) void gemm_mfma_kernel(const uint8_t* __
             for (int j = 0; j < 8; ++j) {
                 const int t = t0 + wn * 128 + 16 * j + ec;
                 if (t < T) {
+                    const float sc = tscale != nullptr ? tscale[t] : 1.0f;
                     float* yp = Y + static_cast<int64_t>(t) * M + m;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (m + e < M) yp[e] = silu(acc[i][j][e]) * acc[i + 4][j][e];
+                        if (m + e < M) yp[e] = silu(acc[i][j][e] * sc) * (acc[i + 4][j][e] * sc);
                 }
             }
         }
     }
 }
 
-template <int FMT, bool GATED, bool XF32>
-static void launch_t(const void* W, const void* Wu, const void* X, float* Y, int64_t M, int64_t K, int64_t T,
-                     hipStream_t s) {
+template <int FMT, bool GATED>
+static void launch_t(const void* W, const void* Wu, const void* X, const float* tscale, float* Y, int64_t M, int64_t K,
+                     int64_t T, hipStream_t s) {
     const int rows_per_tile = GATED ? GM_BM / 2 : GM_BM;
     const dim3 grid(static_cast<unsigned>((M + rows_per_tile - 1) / rows_per_tile),
                     static_cast<unsigned>((T + GM_BN - 1) / GM_BN));
     const int64_t rb = (K / 32) * static_cast<int64_t>(Fmt<FMT>::BB);
-    hipLaunchKernelGGL((gemm_mfma_kernel<FMT, GATED, XF32>), grid, dim3(GM_THREADS), 0, s,
-                       static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), X, Y, static_cast<int>(M),
-                       static_cast<int>(K), static_cast<int>(T), static_cast<int>(rb % 4 == 0));
+    hipLaunchKernelGGL((gemm_mfma_kernel<FMT, GATED>), grid, dim3(GM_THREADS), 0, s, static_cast<const uint8_t*>(W),
+                       static_cast<const uint8_t*>(Wu), X, tscale, Y, static_cast<int>(M), static_cast<int>(K),
+                       static_cast<int>(T), static_cast<int>(rb % 4 == 0));
 }
 
 template <int FMT>
-static void launch_f(const void* W, const void* Wu, const void* X, bool xf32, float* Y, int64_t M, int64_t K,
+static void launch_f(const void* W, const void* Wu, const void* X, const float* tscale, float* Y, int64_t M, int64_t K,
                      int64_t T, hipStream_t s) {
-    if (Wu) {
-        if (xf32) launch_t<FMT, true, true>(W, Wu, X, Y, M, K, T, s);
-        else launch_t<FMT, true, false>(W, Wu, X, Y, M, K, T, s);
-    } else {
-        if (xf32) launch_t<FMT, false, true>(W, Wu, X, Y, M, K, T, s);
-        else launch_t<FMT, false, false>(W, Wu, X, Y, M, K, T, s);
-    }
+    if (Wu) launch_t<FMT, true>(W, Wu, X, tscale, Y, M, K, T, s);
+    else launch_t<FMT, false>(W, Wu, X, tscale, Y, M, K, T, s);
 }
 
-hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32, float* Y,
-                            int64_t M, int64_t K, int64_t T, hipStream_t s) {
+size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t T, bool gated) {
+    const TilePlan p = plan_gemm_tile(fmt, M, K, T, gated);
+    return p.ok ? p.ws_bytes : 0;
+}
+
+hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* X, const float* tscale, float* Y,
+                            int64_t M, int64_t K, int64_t T, float* ws, hipStream_t s) {
     // The tiled kernel covers 16-byte aligned rows; this one covers every other shape.
-    if (launch_gemm_tile(fmt, W, Wu, X, x_is_f32, Y, M, K, T, s)) return hipGetLastError();
+    const TilePlan p = plan_gemm_tile(fmt, M, K, T, Wu != nullptr);
+    if (p.ok) {
+        launch_gemm_tile(p, fmt, W, Wu, X, tscale, Y, M, K, T, ws, s);
+        return hipGetLastError();
+    }
     // grid.y is limited to 65535 tiles of 256 tokens; larger T is split into passes.
     constexpr int64_t kMaxT = 65535LL * GM_BN;
-    const size_t xe = x_is_f32 ? 4 : 2;
     for (int64_t t = 0; t < T; t += kMaxT) {
         const int64_t tt = std::min(kMaxT, T - t);
-        const void* Xp = static_cast<const char*>(X) + t * K * xe;
+        const void* Xp = static_cast<const char*>(X) + t * K * 2;
+        const float* tsp = tscale != nullptr ? tscale + t : nullptr;
         float* Yp = Y + t * M;
         switch (fmt) {
-            case 8: launch_f<8>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
-            case 2: launch_f<2>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
-            case 3: launch_f<3>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
-            case 6: launch_f<6>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
-            case 7: launch_f<7>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
-            default: launch_f<1>(W, Wu, Xp, x_is_f32, Yp, M, K, tt, s); break;
+            case 8: launch_f<8>(W, Wu, Xp, tsp, Yp, M, K, tt, s); break;
+            case 2: launch_f<2>(W, Wu, Xp, tsp, Yp, M, K, tt, s); break;
+            case 3: launch_f<3>(W, Wu, Xp, tsp, Yp, M, K, tt, s); break;
+            case 6: launch_f<6>(W, Wu, Xp, tsp, Yp, M, K, tt, s); break;
+            case 7: launch_f<7>(W, Wu, Xp, tsp, Yp, M, K, tt, s); break;
+            default: launch_f<1>(W, Wu, Xp, tsp, Yp, M, K, tt, s); break;
         }
     }
     return hipGetLastError();

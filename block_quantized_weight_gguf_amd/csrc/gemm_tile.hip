@@ -6,12 +6,12 @@
 // blocks in HBM and are decoded to fp16 MFMA operands inside the kernel.
 //
 // Work layout (wave64, 160 KB LDS per CU, 8 XCDs):
-//   * A workgroup owns a 256 (weight rows) x 256 (tokens) output tile with 4 waves,
-//     one per SIMD with the whole 512-entry register file: each wave computes 64
-//     weight rows x 256 tokens as 4 x 16 v_mfma_f32_16x16x32_f16 fragments whose
-//     256 accumulators live in AGPRs.
-//   * Both operands reach LDS by direct global->LDS DMA (global_load_lds_dwordx4):
-//     no VGPRs are spent on staging and every load instruction reads whole 128-byte
+//   * A workgroup owns a 256 (weight rows) x 256 (tokens) output tile (256 x 128 up
+//     to 128 tokens) with 8 waves, two per SIMD: each wave computes 32 weight rows
+//     x all the tile's tokens as 2 x 16 (2 x 8) v_mfma_f32_16x16x32_f16 fragments,
+//     128 (64) fp32 accumulators.
+//   * Both operands reach LDS by buffer->LDS DMA (buffer_load_dwordx4 ... lds): no
+//     VGPRs are spent on staging and every load instruction reads whole 128-byte
 //     lines.  Token tile: 256 rows x 64 halfs per K step, 16-byte chunks stored
 //     XOR-swizzled by row (the swizzle is applied to the source address, since the
 //     DMA writes lane L's 16 bytes at base + 16 L), so fragment reads hit distinct
@@ -47,11 +47,11 @@
 //     rows of the same outputs (so each DMA instruction reads one matrix); each wave
 //     takes 32 gate and the matching 32 up rows, so every lane ends holding g and u
 //     for the same outputs and applies h = silu(g) * u before the store.
-//   * fp32 tokens (batched decode through the MFMA path) are converted while being
-//     staged through VGPRs instead of by DMA.
+//   * Tokens are always fp16.  fp32 tokens (batched decode through the MFMA path)
+//     arrive pre-scaled: scale_tokens_f16 wrote fp16(2^s_t x_t) per token t, and the
+//     epilogue (or the split-K reduce) multiplies token t's outputs by tscale[t] =
+//     2^-s_t.
 #include <algorithm>
-#include <map>
-#include <mutex>
 #include <type_traits>
 
 #include "mfma_tile.hpp"
@@ -72,10 +72,11 @@ constexpr int GT_GROUP_M = 4;
 // its tile and stores the raw partial sums to Y[split][T][Mo] (Mo = M, or 2 M for the
 // gated instance: gate sums in columns 0..M-1, up sums in M..2M-1); splitk_reduce
 // adds the splits in order and applies the epilogue.
-template <int FMT, bool GATED, bool XF32, bool SPLIT, int BN>
+template <int FMT, bool GATED, bool SPLIT, int BN>
 __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __restrict__ Wg,
                                                                 const uint8_t* __restrict__ Wu,
                                                                 const void* __restrict__ Xv,
+                                                                const float* __restrict__ tscale,
                                                                 float* __restrict__ Y, int M, int K, int T,
                                                                 int vec, int nsplit, int ksteps) {
     using G = WStage<FMT>;
@@ -92,13 +93,11 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     constexpr int KPS = G::KPS;
     constexpr int XBYTES = BN * GT_BK * 2;
     constexpr int XINST = XBYTES / 1024 / GT_WAVES;          // token DMA instructions per wave and step
-    constexpr int XE = XF32 ? 4 : 2;          // token element bytes
+    constexpr int XE = 2;                     // token element bytes
     static_assert(WINST % 2 == 0, "gate / up halves must split on instruction boundaries");
-    // Wave layout: 8 / GT_WN waves along the weight rows, GT_WN along the tokens; each
-    // wave holds GT_NI x GT_NJ 16x16 fragments (128 accumulators).  fp16 tokens: 8 x 1
-    // (each weight row is decoded by one wave only); fp32 tokens: 4 x 2, which leaves
-    // room for their staging registers.
-    constexpr int GT_WN = XF32 ? 2 : 1;
+    // Wave layout: 8 waves along the weight rows (each weight row is decoded by one
+    // wave only), each holding GT_NI x GT_NJ 16x16 fragments (128 accumulators).
+    constexpr int GT_WN = 1;
     constexpr int GT_RW = GT_BM / (GT_WAVES / GT_WN);  // weight rows per wave
     constexpr int GT_TW = BN / GT_WN;                  // tokens per wave
     constexpr int GT_NI = GT_RW / 16;
@@ -109,7 +108,7 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     // step ahead.  Their token stages span two K steps like the weight stages, so both
     // operands are fetched a whole stage (two steps) ahead, and only the first step of
     // a stage needs a wait and a barrier.
-    constexpr bool X2 = BN == 128 && KPS == 2 && !XF32;
+    constexpr bool X2 = BN == 128 && KPS == 2;
     constexpr int XSTAGE = X2 ? 2 * XBYTES : XBYTES;  // bytes per token stage
     __shared__ __align__(16) uint8_t Xs0[XSTAGE];
     __shared__ __align__(16) uint8_t Xs1[XSTAGE];
@@ -200,39 +199,11 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         }
     };
 
-    // Token step k: DMA for fp16 tokens; fp32 tokens are loaded to VGPRs here and
-    // converted / stored by store_x before the barrier of step k.
-    u32x4_t xreg[XF32 ? 2 * XINST : 1];
+    // Token step k: DMA into Xd.
     auto issue_x = [&](QMM_L3 uint8_t* Xd, int k) {
-        if constexpr (XF32) {
 #pragma unroll
-            for (int i = 0; i < XINST; ++i) {
-                xreg[2 * i] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoffs[i], k * 256, 0);
-                xreg[2 * i + 1] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoffs[i] + 16, k * 256, 0);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < XINST; ++i)
-                dma16(xr, xoffs[i], static_cast<uint32_t>(k) * 128, Xd + 1024 * (wave + GT_WAVES * i));
-        }
-    };
-    auto store_x = [&](QMM_L3 uint8_t* Xd) {
-        if constexpr (XF32) {
-#pragma unroll
-            for (int i = 0; i < XINST; ++i) {
-                // Elements are copied out before the bit cast: bit-casting an element
-                // access of an ext-vector directly reads element 0 with this compiler.
-                float f[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t ua = xreg[2 * i][e], ub = xreg[2 * i + 1][e];
-                    f[e] = __builtin_bit_cast(float, ua);
-                    f[4 + e] = __builtin_bit_cast(float, ub);
-                }
-                const u32x4_t h = {pack_h2(f[0], f[1]), pack_h2(f[2], f[3]), pack_h2(f[4], f[5]), pack_h2(f[6], f[7])};
-                *reinterpret_cast<QMM_L3 u32x4_t*>(Xd + 1024 * (wave + GT_WAVES * i) + 16 * lane) = h;
-            }
-        }
+        for (int i = 0; i < XINST; ++i)
+            dma16(xr, xoffs[i], static_cast<uint32_t>(k) * 128, Xd + 1024 * (wave + GT_WAVES * i));
     };
 
     float4_t acc[GT_NI][GT_NJ];
@@ -301,8 +272,8 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         else return frag_decode<FMT>(r, sh + BB * b, q4);
     };
     // Group size: as many fragments read ahead as the registers allow (the 256-token
-    // tile holds 128 accumulators; gated and fp32-token instances need more besides).
-    constexpr int NJG_MAX = BN == 128 ? 4 : (GATED || XF32) ? 1 : 2;
+    // tile holds 128 accumulators; the gated instance needs more besides).
+    constexpr int NJG_MAX = BN == 128 ? 4 : GATED ? 1 : 2;
     constexpr int NJG = (GT_NJ / 2 < NJG_MAX) ? GT_NJ / 2 : NJG_MAX;
     constexpr int NG = GT_NJ / NJG;
     static_assert(GT_NJ % NJG == 0 && NG >= 2, "token fragment groups");
@@ -385,26 +356,19 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         } else {
             if constexpr (KPS == 2 && KK == 1) wait_vm<WPER>();
             else wait_vm<0>();
-            if constexpr (XF32) store_x(Xc);
             lds_barrier();
-            // fp32 tokens are loaded after the step's MFMAs, so that their staging
-            // registers are live only across the barrier (their latency is exposed; this
-            // path serves small decode batches).
-            if constexpr (!XF32) issue_x(Xn, min(k + 1, kend - 1));
+            issue_x(Xn, min(k + 1, kend - 1));
             if constexpr (KK == 0) issue_w(Wn, min(k / KPS + 1, send - 1));
         }
         constexpr int SH = stage_shift<FMT>(WS);
         // a0 holds this step's first sub-step when it was decoded on the previous step
         // (second step of a block-format stage); otherwise decode it now.
-        // (fp32 tokens skip the cross-step decode: their staging registers are live
-        // across the barrier.)
-        constexpr bool PRE = KPS == 2 && !XF32;
+        constexpr bool PRE = KPS == 2;
         if constexpr (!(PRE && KK == 1)) {
             decode2(a0, 0, Wc, 2 * KK, SH);
             if constexpr (NDG > 1) decode2(a0, ND, Wc, 2 * KK, SH);
         }
         mfma_step(a0, a1, Xc, 2 * KK + 1, (PRE && KK == 0) ? 2 : -1, Wc, SH);
-        if constexpr (XF32) issue_x(Xn, min(k + 1, kend - 1));
         __builtin_amdgcn_sched_barrier(0);
     };
     using I0 = std::integral_constant<int, 0>;
@@ -464,16 +428,17 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     } else {
         constexpr int NOUT = GATED ? NH : GT_NI;  // output fragments per wave
 #pragma unroll
-        for (int i = 0; i < NOUT; ++i) {
-            const int m = m0 + (GATED ? (GT_RW / 2) * wm : GT_RW * wm) + 16 * i + er;
+        for (int j = 0; j < GT_NJ; ++j) {
+            const int t = t0 + GT_TW * wn + 16 * j + ec;
+            const float sc = (tscale != nullptr && t < T) ? tscale[t] : 1.0f;
 #pragma unroll
-            for (int j = 0; j < GT_NJ; ++j) {
-                const int t = t0 + GT_TW * wn + 16 * j + ec;
+            for (int i = 0; i < NOUT; ++i) {
+                const int m = m0 + (GATED ? (GT_RW / 2) * wm : GT_RW * wm) + 16 * i + er;
                 if (t < T && m < M) {
                     float h[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        h[e] = GATED ? silu(acc[i][j][e]) * acc[i + NH][j][e] : acc[i][j][e];
+                        h[e] = GATED ? silu(acc[i][j][e] * sc) * (acc[i + NH][j][e] * sc) : acc[i][j][e] * sc;
                     store4(Y + static_cast<int64_t>(t) * M + m, m, h);
                 }
             }
@@ -481,14 +446,16 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
     }
 }
 
-// Sums the split-K partials P[s][T][Mo] in split order and applies the epilogue
-// (gated: h = silu(sum of gate partials) * (sum of up partials)).  Four outputs per
-// thread when M % 4 == 0 (16-byte aligned rows), else one.  The partials of each
-// output are loaded 8 at a time (independent loads in flight together) and added in
-// split order, so the result does not depend on the launch.
+// Sums the split-K partials P[s][T][Mo] in split order, scales token t's sums by
+// tscale[t] (when given) and applies the epilogue (gated: h = silu(sum of gate
+// partials) * (sum of up partials)).  Four outputs per thread when M % 4 == 0 (16-byte
+// aligned rows), else one.  The partials of each output are loaded 8 at a time
+// (independent loads in flight together) and added in split order, so the result
+// does not depend on the launch.
 template <bool GATED>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P, float* __restrict__ Y,
-                                                     int64_t T, int64_t M, int nsplit, int vec) {
+                                                     const float* __restrict__ tscale, int64_t T, int64_t M,
+                                                     int nsplit, int vec) {
     constexpr int B = 8;
     const int64_t Mo = GATED ? 2 * M : M;
     const int64_t plane = T * Mo;
@@ -498,6 +465,7 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P
          e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const int64_t t = e * W / M, m = e * W - t * M;
         const float* p = P + t * Mo + m;
+        const float sc = tscale != nullptr ? tscale[t] : 1.0f;
         if (vec) {
             float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
             int s = 0;
@@ -522,7 +490,11 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P
                     u.x += c.x; u.y += c.y; u.z += c.z; u.w += c.w;
                 }
             }
-            if (GATED) g = make_float4(silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
+            g.x *= sc, g.y *= sc, g.z *= sc, g.w *= sc;
+            if (GATED) {
+                u.x *= sc, u.y *= sc, u.z *= sc, u.w *= sc;
+                g = make_float4(silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w);
+            }
             *reinterpret_cast<float4*>(Y + t * M + m) = g;
         } else {
             float g = 0.0f, u = 0.0f;
@@ -544,171 +516,91 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P
                 g += p[s * plane];
                 if (GATED) u += p[s * plane + M];
             }
-            Y[t * M + m] = GATED ? silu(g) * u : g;
+            Y[t * M + m] = GATED ? silu(g * sc) * (u * sc) : g * sc;
         }
     }
 }
 
-template <int FMT, bool GATED, bool XF32, bool SPLIT, int BN>
-static void launch_tile_t(const void* W, const void* Wu, const void* X, float* Y, int64_t M, int64_t K, int64_t T,
-                          int nsplit, int ksteps, hipStream_t s) {
+template <int FMT, bool GATED, bool SPLIT, int BN>
+static void launch_tile_t(const void* W, const void* Wu, const void* X, const float* tscale, float* Y, int64_t M,
+                          int64_t K, int64_t T, int nsplit, int ksteps, hipStream_t s) {
     const int64_t rows_per_tile = GATED ? GT_BM / 2 : GT_BM;
     const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + BN - 1) / BN);
     const int64_t grid = (ntiles * (SPLIT ? nsplit : 1) + 7) / 8 * 8;  // whole runs per XCD
-    hipLaunchKernelGGL((gemm_tile_kernel<FMT, GATED, XF32, SPLIT, BN>), dim3(static_cast<unsigned>(grid)),
-                       dim3(GT_THREADS), 0, s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), X, Y,
-                       static_cast<int>(M), static_cast<int>(K), static_cast<int>(T),
+    hipLaunchKernelGGL((gemm_tile_kernel<FMT, GATED, SPLIT, BN>), dim3(static_cast<unsigned>(grid)),
+                       dim3(GT_THREADS), 0, s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), X,
+                       tscale, Y, static_cast<int>(M), static_cast<int>(K), static_cast<int>(T),
                        static_cast<int>(M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0), nsplit, ksteps);
 }
 
-void launch_splitk_reduce(const float* P, float* Y, int64_t T, int64_t M, int nsplit, bool gated, hipStream_t s) {
+void launch_splitk_reduce(const float* P, float* Y, const float* tscale, int64_t T, int64_t M, int nsplit, bool gated,
+                          hipStream_t s) {
     const int vec = M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
     const int64_t n = T * M / (vec ? 4 : 1);
     const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 256 * 16));
-    if (gated) hipLaunchKernelGGL(splitk_reduce<true>, dim3(grid), dim3(256), 0, s, P, Y, T, M, nsplit, vec);
-    else hipLaunchKernelGGL(splitk_reduce<false>, dim3(grid), dim3(256), 0, s, P, Y, T, M, nsplit, vec);
+    if (gated) hipLaunchKernelGGL(splitk_reduce<true>, dim3(grid), dim3(256), 0, s, P, Y, tscale, T, M, nsplit, vec);
+    else hipLaunchKernelGGL(splitk_reduce<false>, dim3(grid), dim3(256), 0, s, P, Y, tscale, T, M, nsplit, vec);
 }
 
-// Stream-ordered workspace for split-K partials: a memory pool of this library per
-// device, which keeps freed blocks for reuse (so steady-state calls do not go to the
-// driver) and orders reuse by stream.
-hipMemPool_t workspace_pool() {
-    static std::mutex mu;
-    static hipMemPool_t pools[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!pools[dev]) {
-        hipMemPoolProps props = {};
-        props.allocType = hipMemAllocationTypePinned;
-        props.handleTypes = hipMemHandleTypeNone;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t p = nullptr;
-        if (hipMemPoolCreate(&p, &props) != hipSuccess) return nullptr;
-        uint64_t keep = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
-        pools[dev] = p;
-    }
-    return pools[dev];
-}
-
-// Split-K workspace kept per (device, stream) and reused by every call on that
-// stream: a stream-ordered allocation and free per call cost about 20 us of host time,
-// more than the kernels of a small call.  Growth allocates the larger buffer from the
-// pool and frees the old one on the same stream, after its last use there.  The lock
-// is held until the lease ends, so host threads that share a stream cannot interleave
-// one call's partial sums with another's reduction.  While the stream is being captured
-// into a graph no workspace is handed out.
-namespace {
-std::mutex g_ws_mu;
-struct WsEntry {
-    float* p = nullptr;
-    size_t bytes = 0;
-};
-std::map<std::pair<int, uintptr_t>, WsEntry> g_ws;
-}  // namespace
-
-WorkspaceLease::WorkspaceLease(size_t bytes, hipStream_t s) {
-    if (bytes == 0) return;
-    lock_ = std::unique_lock<std::mutex>(g_ws_mu);
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
-        (void)hipGetLastError();
-        return;
-    }
-    if (cs != hipStreamCaptureStatusNone) return;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        (void)hipGetLastError();
-        return;
-    }
-    hipMemPool_t pool = workspace_pool();
-    if (!pool) return;
-    WsEntry& e = g_ws[{dev, reinterpret_cast<uintptr_t>(s)}];
-    if (e.bytes < bytes) {
-        constexpr size_t kGrain = size_t{1} << 20;
-        const size_t want = (std::max(bytes, 2 * e.bytes) + kGrain - 1) / kGrain * kGrain;
-        float* np = nullptr;
-        if (hipMallocFromPoolAsync(reinterpret_cast<void**>(&np), want, pool, s) != hipSuccess) {
-            (void)hipGetLastError();
-            return;
-        }
-        if (e.p) (void)hipFreeAsync(e.p, s);
-        e.p = np;
-        e.bytes = want;
-    }
-    p_ = e.p;
-}
-
-bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32, float* Y, int64_t M,
-                      int64_t K, int64_t T, hipStream_t s) {
-    // Block formats need 16-byte aligned rows (K % 256 == 0); F16 needs K % 64 == 0.
-    if (fmt != 1 && K % 256 != 0) return false;
-    if (K % 64 != 0) return false;
-    // 32-bit lane offsets inside a tile: 256 rows of tokens (fp32: 4 K bytes each)
-    // and of weights must span less than 2^31 bytes.
-    if (K > (int64_t{1} << 20)) return false;
-    const bool gated = Wu != nullptr;
+// The tiled kernel's plan for a shape: whether it applies (block formats need 16-byte
+// aligned rows, K % 256 == 0; F16 K % 64 == 0; 32-bit lane offsets inside a tile need
+// K <= 2^20), the tile width, and the K split.  K is split when the tiles cannot fill
+// the 256 CUs: at most one wave of workgroups, at least 4 K steps (256) per split,
+// split boundaries on multiples of 4 steps.  The partials take nsplit x T x Mo fp32
+// (Mo = 2 M gated) of the caller's workspace.
+TilePlan plan_gemm_tile(int fmt, int64_t M, int64_t K, int64_t T, bool gated) {
+    TilePlan p;
+    if (fmt != 1 && K % 256 != 0) return p;
+    if (K % 64 != 0 || K > (int64_t{1} << 20)) return p;
     const int64_t rows_per_tile = gated ? GT_BM / 2 : GT_BM;
-#ifndef QMM_NARROW_T
-#define QMM_NARROW_T 128
-#endif
-    const bool narrow = T <= QMM_NARROW_T;
-    const int64_t bn = narrow ? 128 : GT_BN;
+    p.narrow = T <= 128;
+    const int64_t bn = p.narrow ? 128 : GT_BN;
     const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + bn - 1) / bn);
-    if (ntiles > (int64_t{1} << 30)) return false;
-
-    // Split K when the tiles cannot fill the 256 CUs: at most one wave of workgroups,
-    // at least 4 K steps (256) per split, split boundaries on multiples of 4 steps.
+    if (ntiles > (int64_t{1} << 30)) return p;
     const int64_t nsteps = K / GT_BK;
-    int nsplit = 1, ksteps = static_cast<int>(nsteps);
+    p.nsplit = 1;
+    p.ksteps = static_cast<int>(nsteps);
     if (ntiles < 192 && nsteps >= 8) {
         const int64_t want = std::min<int64_t>(256 / ntiles, nsteps / 4);
         if (want >= 2) {
-            ksteps = static_cast<int>((nsteps + want - 1) / want + 3) / 4 * 4;
-            nsplit = static_cast<int>((nsteps + ksteps - 1) / ksteps);
+            p.ksteps = static_cast<int>((nsteps + want - 1) / want + 3) / 4 * 4;
+            p.nsplit = static_cast<int>((nsteps + p.ksteps - 1) / p.ksteps);
         }
     }
-    WorkspaceLease ws(nsplit > 1 ? static_cast<size_t>(nsplit) * T * (gated ? 2 * M : M) * sizeof(float) : 0, s);
-    float* P = nullptr;
-    if (nsplit > 1) {
-        P = ws.get();
-        if (!P) {  // no workspace (or the stream is being captured): one workgroup per tile
-            nsplit = 1;
-            ksteps = static_cast<int>(nsteps);
-        }
-    }
-#define QMM_TILE_BN(F, G, XF, SP, OUT)                                                                   \
-    if (narrow) launch_tile_t<F, G, XF, SP, 128>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);               \
-    else launch_tile_t<F, G, XF, SP, GT_BN>(W, Wu, X, OUT, M, K, T, nsplit, ksteps, s);
-#define QMM_TILE_CASE(F, SP, OUT)                                                                        \
-    if (gated) {                                                                                        \
-        if (x_is_f32) { QMM_TILE_BN(F, true, true, SP, OUT) }                                          \
-        else { QMM_TILE_BN(F, true, false, SP, OUT) }                                                  \
-    } else {                                                                                            \
-        if (x_is_f32) { QMM_TILE_BN(F, false, true, SP, OUT) }                                         \
-        else { QMM_TILE_BN(F, false, false, SP, OUT) }                                                 \
-    }
-    if (P) {
-        if (fmt == 8) { QMM_TILE_CASE(8, true, P) }
-        else if (fmt == 2) { QMM_TILE_CASE(2, true, P) }
-        else if (fmt == 3) { QMM_TILE_CASE(3, true, P) }
-        else if (fmt == 6) { QMM_TILE_CASE(6, true, P) }
-        else if (fmt == 7) { QMM_TILE_CASE(7, true, P) }
-        else { QMM_TILE_CASE(1, true, P) }
-        launch_splitk_reduce(P, Y, T, M, nsplit, gated, s);
+    p.ws_bytes = p.nsplit > 1 ? static_cast<size_t>(p.nsplit) * T * (gated ? 2 * M : M) * sizeof(float) : 0;
+    p.ok = true;
+    return p;
+}
+
+void launch_gemm_tile(const TilePlan& p, int fmt, const void* W, const void* Wu, const void* X, const float* tscale,
+                      float* Y, int64_t M, int64_t K, int64_t T, float* ws, hipStream_t s) {
+    const bool gated = Wu != nullptr;
+    const bool split = p.nsplit > 1;
+    float* out = split ? ws : Y;
+#define QMM_TILE_BN(F, G, SP)                                                                           \
+    if (p.narrow) launch_tile_t<F, G, SP, 128>(W, Wu, X, tscale, out, M, K, T, p.nsplit, p.ksteps, s);  \
+    else launch_tile_t<F, G, SP, GT_BN>(W, Wu, X, tscale, out, M, K, T, p.nsplit, p.ksteps, s);
+#define QMM_TILE_CASE(F, SP)                                                                            \
+    if (gated) { QMM_TILE_BN(F, true, SP) }                                                             \
+    else { QMM_TILE_BN(F, false, SP) }
+    if (split) {
+        if (fmt == 8) { QMM_TILE_CASE(8, true) }
+        else if (fmt == 2) { QMM_TILE_CASE(2, true) }
+        else if (fmt == 3) { QMM_TILE_CASE(3, true) }
+        else if (fmt == 6) { QMM_TILE_CASE(6, true) }
+        else if (fmt == 7) { QMM_TILE_CASE(7, true) }
+        else { QMM_TILE_CASE(1, true) }
+        launch_splitk_reduce(ws, Y, tscale, T, M, p.nsplit, gated, s);
     } else {
-        if (fmt == 8) { QMM_TILE_CASE(8, false, Y) }
-        else if (fmt == 2) { QMM_TILE_CASE(2, false, Y) }
-        else if (fmt == 3) { QMM_TILE_CASE(3, false, Y) }
-        else if (fmt == 6) { QMM_TILE_CASE(6, false, Y) }
-        else if (fmt == 7) { QMM_TILE_CASE(7, false, Y) }
-        else { QMM_TILE_CASE(1, false, Y) }
+        if (fmt == 8) { QMM_TILE_CASE(8, false) }
+        else if (fmt == 2) { QMM_TILE_CASE(2, false) }
+        else if (fmt == 3) { QMM_TILE_CASE(3, false) }
+        else if (fmt == 6) { QMM_TILE_CASE(6, false) }
+        else if (fmt == 7) { QMM_TILE_CASE(7, false) }
+        else { QMM_TILE_CASE(1, false) }
     }
 #undef QMM_TILE_CASE
 #undef QMM_TILE_BN
-    return true;
 }
 
 }  // namespace qmm

@@ -1,5 +1,7 @@
 // Small-batch decode GEMV on the matrix cores: y[n][m] = sum_k W[m][k] x[n][k] for a
-// few tokens (2..32), block-format weights, fp32 x rounded to fp16, fp32 accumulate.
+// few tokens (2..32), block-format weights, fp32 accumulate.  x enters as fp16 scaled
+// per token (scale_tokens_f16: x16 = fp16(2^s_n x_n)); the epilogue multiplies token
+// n's outputs by tscale[n] = 2^-s_n.
 //
 // ("llama.cpp Metal ...", section 3.2 and P9: a batched mat-vec for a handful of
 // tokens, each weight read once and reused for every token; "EdgeRunner Core
@@ -12,16 +14,16 @@
 //     to 16 or 32) are 1 or 2 column fragments.
 //   * Weights and x stream through a ring of 3 LDS stages by buffer->LDS DMA.  A
 //     stage holds the raw GGUF bytes of 4 blocks of all 256 rows (16-byte chunks of
-//     the row windows, whole 128-byte lines per load instruction) and the fp32 x of
+//     the row windows, whole 128-byte lines per load instruction) and the fp16 x of
 //     the same 128-wide K range for every token (16-byte chunks XOR-swizzled by
-//     token, so that the 16 token rows of a fragment read hit distinct banks; x is
-//     rounded to fp16 as the fragments are read).  Two stages are always in flight,
-//     ~80 KB per CU, which covers HBM latency at the per-CU share of the bandwidth.
+//     token, so that the 16 token rows of a fragment read hit distinct banks).  Two
+//     stages are always in flight, ~80 KB per CU, which covers HBM latency at the
+//     per-CU share of the bandwidth.
 //   * Each wave decodes its A fragments straight from the raw bytes in the fp16
 //     domain (shared with the prefill GEMM) and issues 2 x (tokens / 16) MFMAs per
 //     block: the matrix cores do the multiply-adds, the VALU only decodes.
 //   * When the rows alone cannot fill the machine (or K is long), K is split over
-//     several workgroups; their partial sums go to a stream-ordered workspace and a
+//     several workgroups; their partial sums go to the caller's workspace and a
 //     second kernel adds them in a fixed order and applies the gated epilogue.
 //   * Gated instance: stage rows 0..127 are 128 gate rows and 128..255 the up rows
 //     of the same outputs; each wave takes 16 gate and the matching 16 up rows.
@@ -45,11 +47,11 @@ constexpr int GM_WAVES = GM_THREADS / 64;
 template <int FMT, int NJ>
 constexpr int gm_stage_blocks() { return 4; }
 
-// K range per workgroup that fits x in LDS next to the weight ring.
 template <int FMT, bool GATED, int NJ, bool SPLIT>
 __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __restrict__ Wg,
                                                                 const uint8_t* __restrict__ Wu,
-                                                                const float* __restrict__ x, float* __restrict__ Y,
+                                                                const _Float16* __restrict__ x,
+                                                                const float* __restrict__ tscale, float* __restrict__ Y,
                                                                 int M, int K, int N, int nsplit, int kst, int vec) {
     constexpr int BB = Fmt<FMT>::BB;
     constexpr int SB = gm_stage_blocks<FMT, NJ>();
@@ -66,11 +68,13 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
     constexpr int WPER = (WINST + GM_WAVES - 1) / GM_WAVES;
     static_assert(WINST % 2 == 0, "gate / up halves must split on instruction boundaries");
     constexpr int NTOK = 16 * NJ;                    // token rows of x per stage
-    constexpr int XROW = STAGE_K * 4;                // fp32 x bytes per token row and stage
+    constexpr int XROW = STAGE_K * 2;                // fp16 x bytes per token row and stage
     constexpr int XC = XROW / 16;                    // 16-byte chunks per token row
+    static_assert(XC == 16, "the swizzle key (token & 15) stays inside a row");
     constexpr int XBYTES = NTOK * XROW;              // x bytes per stage
-    constexpr int XPER = XBYTES / 1024 / GM_WAVES;   // x DMA instructions per wave and stage
-    static_assert(XPER * GM_WAVES * 1024 == XBYTES, "x stage splits evenly over the waves");
+    constexpr int XINST = XBYTES / 1024;             // wave-wide DMA instructions per stage (x)
+    // As for the weights, surplus instructions repeat the stage's last x instruction.
+    constexpr int XPER = (XINST + GM_WAVES - 1) / GM_WAVES;
     constexpr int SLOT = WBYTES + XBYTES;            // one ring slot: weights, then x
     constexpr int NDMA = WPER + XPER;                // DMA instructions per wave and stage
 
@@ -113,14 +117,14 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
         woffs[i] = static_cast<uint32_t>(min(r, wrows - 1) * rb) + 16 * (q % WCH);
     }
     // x: item q = slot q % XC of token row q / XC, holding chunk slot ^ (token & 15)
-    // of that token's STAGE_K floats.  Tokens past N re-read token N - 1 (never stored).
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, static_cast<int64_t>(N) * K * 4);
+    // of that token's STAGE_K halfs.  Tokens past N re-read token N - 1 (never stored).
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, static_cast<int64_t>(N) * K * 2);
     uint32_t xoffs[XPER];
 #pragma unroll
     for (int i = 0; i < XPER; ++i) {
-        const int q = 64 * (wave + GM_WAVES * i) + lane;
+        const int q = 64 * min(wave + GM_WAVES * i, XINST - 1) + lane;
         const int n = q / XC, sl = q % XC;
-        xoffs[i] = static_cast<uint32_t>(min(n, N - 1) * K * 4) + 16 * (sl ^ (n & 15));
+        xoffs[i] = static_cast<uint32_t>(min(n, N - 1) * K * 2) + 16 * (sl ^ (n & 15));
     }
     // Stage st: the 16-byte aligned windows around the row segment [SEG st, SEG st +
     // SEG) of every row (with SHIFT the segment starts 0 or 8 bytes into the window),
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
         }
 #pragma unroll
         for (int i = 0; i < XPER; ++i)
-            dma16(xr, xoffs[i], static_cast<uint32_t>(st) * XROW, S + WBYTES + 1024 * (wave + GM_WAVES * i));
+            dma16(xr, xoffs[i], static_cast<uint32_t>(st) * XROW, S + WBYTES + 1024 * min(wave + GM_WAVES * i, XINST - 1));
     };
 
     QMM_L3 uint8_t* W0 = (QMM_L3 uint8_t*)R0;
@@ -157,18 +161,13 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
         else return 32 * wave + 16 * i + (lane & 15);
     };
     const int arow0 = arow(0) * WROW, arow1 = arow(1) * WROW;
-    // Token fragment j of block b: token 16 j + l % 16, floats 8 q4 .. 8 q4 + 7 of the
-    // block's 32 = chunks 8 b + 2 q4 and 8 b + 2 q4 + 1 of the token row, stored at
-    // slots chunk ^ (l % 16) (the XOR stays inside the row's XC chunks).
+    // Token fragment j of block b: token 16 j + l % 16, halfs 8 q4 .. 8 q4 + 7 of the
+    // block's 32 = chunk 4 b + q4 of the token row, stored at slot chunk ^ (l % 16).
     const int xrow = WBYTES + (lane & 15) * XROW;
     const int xsw = lane & 15;
     auto frag_x = [&](const QMM_L3 uint8_t* S, int j, int b) -> half8_t {
-        const int c = 8 * b + 2 * q4;
-        const QMM_L3 uint8_t* r = S + xrow + j * 16 * XROW;
-        const float4_t lo = *reinterpret_cast<const QMM_L3 float4_t*>(r + 16 * (c ^ xsw));
-        const float4_t hi = *reinterpret_cast<const QMM_L3 float4_t*>(r + 16 * ((c + 1) ^ xsw));
-        const u32x4_t h = {pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3])};
-        return __builtin_bit_cast(half8_t, h);
+        const int c = 4 * b + q4;
+        return *reinterpret_cast<const QMM_L3 half8_t*>(S + xrow + j * 16 * XROW + 16 * (c ^ xsw));
     };
 
     // Stage st from ring slot Wc: wait for its DMA (the next stage's may stay in
@@ -223,6 +222,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
     for (int j = 0; j < NJ; ++j) {
         const int t = 16 * j + (lane & 15);
         if (t >= N) continue;
+        const float sc = tscale[t];
         auto store4 = [&](float* yp, int m, const float (&h)[4]) {
             if (vec) {
                 *reinterpret_cast<float4*>(yp) = make_float4(h[0], h[1], h[2], h[3]);
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
             if (m < M) {
                 float h[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = silu(acc[0][j][e]) * acc[1][j][e];
+                for (int e = 0; e < 4; ++e) h[e] = silu(acc[0][j][e] * sc) * (acc[1][j][e] * sc);
                 store4(Y + static_cast<int64_t>(t) * M + m, m, h);
             }
         } else {
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
             for (int i = 0; i < 2; ++i) {
                 const int m = m0 + 32 * wave + 16 * i + er;
                 if (m < M) {
-                    const float h[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                    const float h[4] = {acc[i][j][0] * sc, acc[i][j][1] * sc, acc[i][j][2] * sc, acc[i][j][3] * sc};
                     store4(Y + static_cast<int64_t>(t) * M + m, m, h);
                 }
             }
@@ -266,62 +266,70 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
 }
 
 template <int FMT, bool GATED, int NJ, bool SPLIT>
-static void launch_gm_t(const void* W, const void* Wu, const float* x, float* Y, int64_t M, int64_t K, int64_t N,
-                        int nsplit, int kst, hipStream_t s) {
+static void launch_gm_t(const void* W, const void* Wu, const void* x16, const float* tscale, float* Y, int64_t M,
+                        int64_t K, int64_t N, int nsplit, int kst, hipStream_t s) {
     const int64_t rows_per_tile = GATED ? GM_BM / 2 : GM_BM;
     const int64_t ntiles = (M + rows_per_tile - 1) / rows_per_tile;
     const int vec = M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
     hipLaunchKernelGGL((gemv_mfma_kernel<FMT, GATED, NJ, SPLIT>), dim3(static_cast<unsigned>(ntiles * nsplit)),
-                       dim3(GM_THREADS), 0, s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), x, Y,
-                       static_cast<int>(M), static_cast<int>(K), static_cast<int>(N), nsplit, kst, vec);
+                       dim3(GM_THREADS), 0, s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu),
+                       static_cast<const _Float16*>(x16), tscale, Y, static_cast<int>(M), static_cast<int>(K),
+                       static_cast<int>(N), nsplit, kst, vec);
 }
 
-template <int FMT, int NJ>
-static bool launch_gm_nj(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K, int64_t N,
-                         hipStream_t s) {
-    const bool gated = Wu != nullptr;
+// K is split only when the row tiles cannot give every CU a workgroup (and each split
+// keeps at least 2 stages); kst is even, so that every split starts on an even stage
+// (the kernel's parity bookkeeping relies on it).  32-bit lane offsets: 256 weight rows
+// must span less than 2^31 bytes (K <= 2^20).
+GemvMfmaPlan plan_gemv_mfma(int fmt, int64_t M, int64_t K, int64_t N, bool gated) {
+    GemvMfmaPlan p;
+    if (fmt == 1 || K % 256 != 0 || N < 1 || N > 32 || K > (int64_t{1} << 20)) return p;
+    p.nj = N > 16 ? 2 : 1;
     const int64_t rows_per_tile = gated ? GM_BM / 2 : GM_BM;
     const int64_t ntiles = (M + rows_per_tile - 1) / rows_per_tile;
-    const int64_t nst = K / (32 * gm_stage_blocks<FMT, NJ>());
-    // K is split only when the row tiles cannot give every CU a workgroup (and each
-    // split keeps at least 2 stages); kst is even, so that every split starts on an
-    // even stage (the kernel's parity bookkeeping relies on it).
+    const int64_t nst = K / (32 * 4);
     int64_t kst = nst;
     if (ntiles < 256) {
         const int64_t want = std::max<int64_t>(1, std::min<int64_t>(256 / ntiles, nst / 2));
         kst = (nst + want - 1) / want;
     }
     kst = std::min<int64_t>((kst + 1) / 2 * 2, nst);
-    const int nsplit = static_cast<int>((nst + kst - 1) / kst);
-    if (ntiles * nsplit > (int64_t{1} << 30)) return false;
-    WorkspaceLease ws(nsplit > 1 ? static_cast<size_t>(nsplit) * N * (gated ? 2 * M : M) * sizeof(float) : 0, s);
-    float* P = nsplit > 1 ? ws.get() : nullptr;
-    if (!P) {  // one split (or no workspace, e.g. during graph capture): all of K per workgroup
-        if (gated) launch_gm_t<FMT, true, NJ, false>(W, Wu, x, y, M, K, N, 1, static_cast<int>(nst), s);
-        else launch_gm_t<FMT, false, NJ, false>(W, Wu, x, y, M, K, N, 1, static_cast<int>(nst), s);
-        return true;
-    }
-    if (gated) launch_gm_t<FMT, true, NJ, true>(W, Wu, x, P, M, K, N, nsplit, static_cast<int>(kst), s);
-    else launch_gm_t<FMT, false, NJ, true>(W, Wu, x, P, M, K, N, nsplit, static_cast<int>(kst), s);
-    launch_splitk_reduce(P, y, N, M, nsplit, gated, s);
-    return true;
+    p.kst = static_cast<int>(kst);
+    p.nsplit = static_cast<int>((nst + kst - 1) / kst);
+    if (ntiles * p.nsplit > (int64_t{1} << 30)) return p;
+    p.ws_bytes = p.nsplit > 1 ? static_cast<size_t>(p.nsplit) * N * (gated ? 2 * M : M) * sizeof(float) : 0;
+    p.ok = true;
+    return p;
 }
 
-bool launch_gemv_mfma(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
-                      int64_t N, hipStream_t s) {
-    if (fmt == 1) return false;
-    if (K % 256 != 0 || N < 1 || N > 32) return false;
-    // 32-bit lane offsets: 256 weight rows must span less than 2^31 bytes.
-    if (K > (int64_t{1} << 20)) return false;
-    const bool two = N > 16;
-    switch (fmt) {
-        case 8: return two ? launch_gm_nj<8, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<8, 1>(W, Wu, x, y, M, K, N, s);
-        case 2: return two ? launch_gm_nj<2, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<2, 1>(W, Wu, x, y, M, K, N, s);
-        case 3: return two ? launch_gm_nj<3, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<3, 1>(W, Wu, x, y, M, K, N, s);
-        case 6: return two ? launch_gm_nj<6, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<6, 1>(W, Wu, x, y, M, K, N, s);
-        case 7: return two ? launch_gm_nj<7, 2>(W, Wu, x, y, M, K, N, s) : launch_gm_nj<7, 1>(W, Wu, x, y, M, K, N, s);
-        default: return false;
+template <int FMT, int NJ>
+static void launch_gm_nj(const GemvMfmaPlan& p, const void* W, const void* Wu, const void* x16, const float* tscale,
+                         float* y, int64_t M, int64_t K, int64_t N, float* ws, hipStream_t s) {
+    const bool gated = Wu != nullptr;
+    if (p.nsplit == 1) {
+        if (gated) launch_gm_t<FMT, true, NJ, false>(W, Wu, x16, tscale, y, M, K, N, 1, p.kst, s);
+        else launch_gm_t<FMT, false, NJ, false>(W, Wu, x16, tscale, y, M, K, N, 1, p.kst, s);
+        return;
     }
+    if (gated) launch_gm_t<FMT, true, NJ, true>(W, Wu, x16, tscale, ws, M, K, N, p.nsplit, p.kst, s);
+    else launch_gm_t<FMT, false, NJ, true>(W, Wu, x16, tscale, ws, M, K, N, p.nsplit, p.kst, s);
+    launch_splitk_reduce(ws, y, tscale, N, M, p.nsplit, gated, s);
+}
+
+void launch_gemv_mfma(const GemvMfmaPlan& p, int fmt, const void* W, const void* Wu, const void* x16,
+                      const float* tscale, float* y, int64_t M, int64_t K, int64_t N, float* ws, hipStream_t s) {
+    const bool two = p.nj == 2;
+#define QMM_GM(F)                                                              \
+    if (two) launch_gm_nj<F, 2>(p, W, Wu, x16, tscale, y, M, K, N, ws, s);   \
+    else launch_gm_nj<F, 1>(p, W, Wu, x16, tscale, y, M, K, N, ws, s);
+    switch (fmt) {
+        case 8: QMM_GM(8) break;
+        case 2: QMM_GM(2) break;
+        case 3: QMM_GM(3) break;
+        case 6: QMM_GM(6) break;
+        default: QMM_GM(7) break;
+    }
+#undef QMM_GM
 }
 
 }  // namespace qmm

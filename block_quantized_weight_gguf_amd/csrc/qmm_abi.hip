@@ -54,6 +54,49 @@ int check_shape(int fmt, int64_t M, int64_t K, int64_t N) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 
+int64_t round_ws(int64_t v) { return (v + QMM_WORKSPACE_ALIGN - 1) / QMM_WORKSPACE_ALIGN * QMM_WORKSPACE_ALIGN; }
+
+// Weight bytes of a product (both matrices for the gated one), overflow-checked.
+bool weight_bytes(int fmt, int64_t M, int64_t K, bool gated, int64_t* out) {
+    int64_t t;
+    if (!mul_ok(M, row_bytes_unchecked(fmt, K), &t)) return false;
+    return mul_ok(gated ? 2 : 1, t, out);
+}
+
+// Workspace of an fp32-token MFMA product (qmm_gemv / qmm_gate_up_silu on the MFMA
+// variant): the tokens as scaled fp16 (N x K halfs), their scales (N floats), then
+// the product's split-K partials; each part starts on a QMM_WORKSPACE_ALIGN boundary.
+// The weight-streaming MFMA GEMV serves 2..32 tokens (block formats, K % 256 == 0);
+// the GEMM every other case.
+struct MfmaWs {
+    qmm::GemvMfmaPlan gp;
+    int64_t x16 = 0, inv = 0, part = 0, total = 0;  // byte offsets of the parts, total size
+    bool ok = false;
+};
+MfmaWs mfma_ws(int fmt, int64_t M, int64_t K, int64_t N, bool gated) {
+    MfmaWs w;
+    w.gp = qmm::plan_gemv_mfma(fmt, M, K, N, gated);
+    const int64_t part = w.gp.ok ? static_cast<int64_t>(w.gp.ws_bytes)
+                                 : static_cast<int64_t>(qmm::gemm_workspace_bytes(fmt, M, K, N, gated));
+    int64_t xb, ib;
+    if (!mul_ok(N, K, &xb) || !mul_ok(xb, 2, &xb) || !mul_ok(N, 4, &ib)) return w;
+    w.x16 = 0;
+    w.inv = round_ws(xb);
+    w.part = w.inv + round_ws(ib);
+    if (part > INT64_MAX - w.part - QMM_WORKSPACE_ALIGN) return w;
+    w.total = w.part + round_ws(part);
+    w.ok = true;
+    return w;
+}
+
+// Checks a caller's workspace against the bytes a call needs.
+int check_ws(const void* ws, int64_t ws_bytes, int64_t need) {
+    if (need == 0) return QMM_OK;
+    if (!ws || ws_bytes < need) return QMM_ERR_WORKSPACE;
+    if (!aligned(ws, QMM_WORKSPACE_ALIGN)) return QMM_ERR_ALIGN;
+    return QMM_OK;
+}
+
 // VALU or MFMA variant for N tokens over `wbytes` of weights (`gated`: the gate+up
 // product), measured on MI355X at the Llama-3-8B projection shapes with the weights
 // streamed from HBM.  The block formats' VALU kernels take up to 4 tokens per weight
@@ -77,11 +120,31 @@ int choose_variant(int fmt, int64_t wbytes, int64_t N, bool gated) {
     return QMM_VARIANT_VALU;
 }
 
+// The fp32-token MFMA product: tokens to scaled fp16, then the MFMA GEMV or GEMM.
+int run_mfma_tokens(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
+                    int64_t N, void* ws, int64_t ws_bytes, hipStream_t s) {
+    const MfmaWs w = mfma_ws(fmt, M, K, N, Wu != nullptr);
+    if (!w.ok) return QMM_ERR_OVERFLOW;
+    const int st = check_ws(ws, ws_bytes, w.total);
+    if (st) return st;
+    char* base = static_cast<char*>(ws);
+    void* x16 = base + w.x16;
+    float* inv = reinterpret_cast<float*>(base + w.inv);
+    float* part = reinterpret_cast<float*>(base + w.part);
+    hipError_t e = qmm::launch_scale_tokens(x, x16, inv, N, K, s);
+    if (e != hipSuccess) return QMM_ERR_HIP;
+    if (w.gp.ok) {
+        qmm::launch_gemv_mfma(w.gp, fmt, W, Wu, x16, inv, y, M, K, N, part, s);
+        return from_hip(hipGetLastError());
+    }
+    return from_hip(qmm::launch_gemm_mfma(fmt, W, Wu, x16, inv, y, M, K, N, part, s));
+}
+
 }  // namespace
 
 extern "C" {
 
-int qmm_version(void) { return 100; }
+int qmm_version(void) { return 200; }
 
 const char* qmm_strerror(int status) {
     switch (status) {
@@ -89,11 +152,12 @@ const char* qmm_strerror(int status) {
         case QMM_ERR_NULL: return "a required pointer is NULL";
         case QMM_ERR_FMT: return "unknown weight format (expected 1=F16, 2=Q4_0, 3=Q4_1, 6=Q5_0, 7=Q5_1, 8=Q8_0)";
         case QMM_ERR_SHAPE: return "bad shape (need 1 <= M, K, N <= 2^31-1 and K % 32 == 0)";
-        case QMM_ERR_ALIGN: return "misaligned pointer (W, x, X need 16 bytes; outputs 4 bytes)";
+        case QMM_ERR_ALIGN: return "misaligned pointer (W, x, X need 16 bytes; outputs 4 bytes; workspace 256 bytes)";
         case QMM_ERR_OVERFLOW: return "a byte count overflows int64";
         case QMM_ERR_HIP: return "HIP runtime error at launch";
         case QMM_ERR_VARIANT: return "unknown GEMV variant";
-        case QMM_ERR_ARG: return "a scalar argument is out of range (eps must be finite and >= 0)";
+        case QMM_ERR_ARG: return "a scalar argument is out of range (eps must be finite and >= 0; op id)";
+        case QMM_ERR_WORKSPACE: return "workspace missing or smaller than qmm_workspace_size reports";
         default: return "unknown qmm status";
     }
 }
@@ -138,49 +202,78 @@ int qmm_expand_f16(int fmt, const void* W, void* out, int64_t M, int64_t K, void
 int qmm_gemv_choose(int fmt, int64_t M, int64_t K, int64_t N) {
     const int st = check_shape(fmt, M, K, N);
     if (st) return st;
-    return choose_variant(fmt, M * row_bytes_unchecked(fmt, K), N, false);
+    int64_t wb;
+    if (!weight_bytes(fmt, M, K, false, &wb)) return QMM_ERR_OVERFLOW;
+    return choose_variant(fmt, wb, N, false);
+}
+
+int64_t qmm_workspace_size(int op, int fmt, int64_t M, int64_t K, int64_t N, int variant) {
+    const int st = check_shape(fmt, M, K, N);
+    if (st) return st;
+    const bool gated = op == QMM_OP_GATE_UP_SILU || op == QMM_OP_GEMM_GATE_UP_SILU;
+    switch (op) {
+        case QMM_OP_GEMV:
+        case QMM_OP_GATE_UP_SILU: {
+            if (variant == QMM_VARIANT_AUTO) {
+                int64_t wb;
+                if (!weight_bytes(fmt, M, K, gated, &wb)) return QMM_ERR_OVERFLOW;
+                variant = choose_variant(fmt, wb, N, gated);
+            }
+            if (variant == QMM_VARIANT_VALU) return 0;
+            if (variant != QMM_VARIANT_MFMA) return QMM_ERR_VARIANT;
+            const MfmaWs w = mfma_ws(fmt, M, K, N, gated);
+            return w.ok ? w.total : QMM_ERR_OVERFLOW;
+        }
+        case QMM_OP_GEMM:
+        case QMM_OP_GEMM_GATE_UP_SILU:
+            return round_ws(static_cast<int64_t>(qmm::gemm_workspace_bytes(fmt, M, K, N, gated)));
+        default:
+            return QMM_ERR_ARG;
+    }
 }
 
 int qmm_gemv_variant(int fmt, const void* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
-                     int variant, void* stream) {
+                     int variant, void* workspace, int64_t workspace_bytes, void* stream) {
     if (!W || !x || !y) return QMM_ERR_NULL;
     int st = check_shape(fmt, M, K, N);
     if (st) return st;
     if (!aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return QMM_ERR_ALIGN;
-    if (variant == QMM_VARIANT_AUTO) variant = qmm_gemv_choose(fmt, M, K, N);
+    if (variant == QMM_VARIANT_AUTO) {
+        variant = qmm_gemv_choose(fmt, M, K, N);
+        if (variant < 0) return variant;
+    }
     auto s = static_cast<hipStream_t>(stream);
     if (variant == QMM_VARIANT_VALU) return from_hip(qmm::launch_gemv_valu(fmt, W, nullptr, x, y, M, K, N, s));
-    if (variant == QMM_VARIANT_MFMA) {
-        // Up to 32 tokens: the weight-streaming MFMA GEMV; otherwise the tiled GEMM.
-        if (qmm::launch_gemv_mfma(fmt, W, nullptr, x, y, M, K, N, s)) return from_hip(hipGetLastError());
-        return from_hip(qmm::launch_gemm_mfma(fmt, W, nullptr, x, true, y, M, K, N, s));
-    }
+    if (variant == QMM_VARIANT_MFMA) return run_mfma_tokens(fmt, W, nullptr, x, y, M, K, N, workspace, workspace_bytes, s);
     return QMM_ERR_VARIANT;
 }
 
-int qmm_gemv(int fmt, const void* W, const float* x, float* y, int64_t M, int64_t K, int64_t N, void* stream) {
-    return qmm_gemv_variant(fmt, W, x, y, M, K, N, QMM_VARIANT_AUTO, stream);
+int qmm_gemv(int fmt, const void* W, const float* x, float* y, int64_t M, int64_t K, int64_t N, void* workspace,
+             int64_t workspace_bytes, void* stream) {
+    return qmm_gemv_variant(fmt, W, x, y, M, K, N, QMM_VARIANT_AUTO, workspace, workspace_bytes, stream);
 }
 
 int qmm_gate_up_silu_variant(int fmt, const void* Wg, const void* Wu, const float* x, float* h, int64_t I,
-                             int64_t K, int64_t N, int variant, void* stream) {
+                             int64_t K, int64_t N, int variant, void* workspace, int64_t workspace_bytes,
+                             void* stream) {
     if (!Wg || !Wu || !x || !h) return QMM_ERR_NULL;
     int st = check_shape(fmt, I, K, N);
     if (st) return st;
     if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(x, 16) || !aligned(h, 4)) return QMM_ERR_ALIGN;
-    if (variant == QMM_VARIANT_AUTO) variant = choose_variant(fmt, 2 * I * row_bytes_unchecked(fmt, K), N, true);
+    if (variant == QMM_VARIANT_AUTO) {
+        int64_t wb;
+        if (!weight_bytes(fmt, I, K, true, &wb)) return QMM_ERR_OVERFLOW;
+        variant = choose_variant(fmt, wb, N, true);
+    }
     auto s = static_cast<hipStream_t>(stream);
     if (variant == QMM_VARIANT_VALU) return from_hip(qmm::launch_gemv_valu(fmt, Wg, Wu, x, h, I, K, N, s));
-    if (variant == QMM_VARIANT_MFMA) {
-        if (qmm::launch_gemv_mfma(fmt, Wg, Wu, x, h, I, K, N, s)) return from_hip(hipGetLastError());
-        return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, x, true, h, I, K, N, s));
-    }
+    if (variant == QMM_VARIANT_MFMA) return run_mfma_tokens(fmt, Wg, Wu, x, h, I, K, N, workspace, workspace_bytes, s);
     return QMM_ERR_VARIANT;
 }
 
 int qmm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, float* h, int64_t I, int64_t K,
-                     int64_t N, void* stream) {
-    return qmm_gate_up_silu_variant(fmt, Wg, Wu, x, h, I, K, N, QMM_VARIANT_AUTO, stream);
+                     int64_t N, void* workspace, int64_t workspace_bytes, void* stream) {
+    return qmm_gate_up_silu_variant(fmt, Wg, Wu, x, h, I, K, N, QMM_VARIANT_AUTO, workspace, workspace_bytes, stream);
 }
 
 int qmm_rmsnorm_gemv(int fmt, const void* W, const float* x, const float* gamma, float eps, float* y, int64_t M,
@@ -224,21 +317,28 @@ int qmm_gemv_add(int fmt, const void* W, const float* x, const float* r, float* 
                                           qmm::EP_RES, epi));
 }
 
-int qmm_gemm(int fmt, const void* W, const void* X, float* Y, int64_t M, int64_t K, int64_t T, void* stream) {
+int qmm_gemm(int fmt, const void* W, const void* X, float* Y, int64_t M, int64_t K, int64_t T, void* workspace,
+             int64_t workspace_bytes, void* stream) {
     if (!W || !X || !Y) return QMM_ERR_NULL;
     int st = check_shape(fmt, M, K, T);
     if (st) return st;
     if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
-    return from_hip(qmm::launch_gemm_mfma(fmt, W, nullptr, X, false, Y, M, K, T, static_cast<hipStream_t>(stream)));
+    st = check_ws(workspace, workspace_bytes, static_cast<int64_t>(qmm::gemm_workspace_bytes(fmt, M, K, T, false)));
+    if (st) return st;
+    return from_hip(qmm::launch_gemm_mfma(fmt, W, nullptr, X, nullptr, Y, M, K, T, static_cast<float*>(workspace),
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int qmm_gemm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const void* X, float* H, int64_t I, int64_t K,
-                          int64_t T, void* stream) {
+                          int64_t T, void* workspace, int64_t workspace_bytes, void* stream) {
     if (!Wg || !Wu || !X || !H) return QMM_ERR_NULL;
     int st = check_shape(fmt, I, K, T);
     if (st) return st;
     if (!aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(X, 16) || !aligned(H, 4)) return QMM_ERR_ALIGN;
-    return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, X, false, H, I, K, T, static_cast<hipStream_t>(stream)));
+    st = check_ws(workspace, workspace_bytes, static_cast<int64_t>(qmm::gemm_workspace_bytes(fmt, I, K, T, true)));
+    if (st) return st;
+    return from_hip(qmm::launch_gemm_mfma(fmt, Wg, Wu, X, nullptr, H, I, K, T, static_cast<float*>(workspace),
+                                          static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

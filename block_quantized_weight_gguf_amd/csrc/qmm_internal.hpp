@@ -5,8 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <stddef.h>
+
 #include <algorithm>
-#include <mutex>
 
 namespace qmm {
 
@@ -65,49 +66,49 @@ int64_t launch_gemv_dma(int fmt, const void* W, const void* Wu, const float* x, 
 void launch_gemv_sliced(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
                         int NT, int64_t chunks, int64_t row_begin, int ep, const DecodeEpi& epi, hipStream_t s);
 
-// fp16-MFMA GEMM: Y[t][m] = sum_k W[m][k] X[t][k]; X is fp16 (x_is_f32 = false) or fp32
-// rounded to fp16 while staging (x_is_f32 = true).  Wu != nullptr selects the SwiGLU epilogue.
-hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32,
-                            float* Y, int64_t M, int64_t K, int64_t T, hipStream_t s);
+// fp32 tokens -> fp16 for the MFMA products: per token t the power of two 2^s_t that
+// brings max_k |x[t][k]| into [2^14, 2^15) (2^126 for an all-zero token),
+// x16[t][k] = fp16(2^s_t x[t][k]) (round to nearest even) and inv[t] = 2^-s_t, which
+// the products' epilogues multiply back.  x, x16 16-byte aligned; K % 32 == 0.
+hipError_t launch_scale_tokens(const float* x, void* x16, float* inv, int64_t N, int64_t K, hipStream_t s);
 
-// Tiled fp16-MFMA GEMM (256 x 256 tiles, coalesced raw loads, fp16-domain decode).
-// Returns false, launching nothing, for shapes it does not cover (block formats
-// with K % 256 != 0).
-bool launch_gemm_tile(int fmt, const void* W, const void* Wu, const void* X, bool x_is_f32, float* Y, int64_t M,
-                      int64_t K, int64_t T, hipStream_t s);
+// fp16-MFMA GEMM: Y[t][m] = tscale[t] * sum_k W[m][k] X[t][k] with X fp16 (tscale ==
+// nullptr: no scale).  Wu != nullptr selects the SwiGLU epilogue.  ws: the split-K
+// partials of the tiled kernel's plan (gemm_workspace_bytes), nullptr when it needs none.
+hipError_t launch_gemm_mfma(int fmt, const void* W, const void* Wu, const void* X, const float* tscale, float* Y,
+                            int64_t M, int64_t K, int64_t T, float* ws, hipStream_t s);
 
-// Weight-streaming fp16-MFMA GEMV for 2..32 tokens (block formats, K % 256 == 0): each
-// weight byte is read once per call.  Returns false, launching nothing, when it does
-// not apply.
-bool launch_gemv_mfma(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
-                      int64_t N, hipStream_t s);
+// Workspace bytes launch_gemm_mfma needs for a shape (0: none).
+size_t gemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t T, bool gated);
 
-// Stream-ordered memory pool of this library for the current device (split-K
-// partials); nullptr if pools are unavailable.
-hipMemPool_t workspace_pool();
-
-// Split-K workspace of at least `bytes` for calls on stream s, kept per (device,
-// stream) and reused by later calls on that stream (it grows with a stream-ordered
-// allocation from workspace_pool() and a stream-ordered free of the old buffer).  get()
-// is nullptr when none can be had, and always while s is being captured into a graph
-// (stream-ordered allocations replayed from a captured graph have given wrong results),
-// so callers then take their paths that need no workspace; bytes == 0 asks for none.
-// A lease that asked for a workspace holds a lock
-// until it ends: one call's launches that use the workspace are enqueued together.
-// A stream destroyed while its work is pending must not be followed by a new stream
-// that the runtime hands the same handle before that work ends.
-class WorkspaceLease {
-   public:
-    WorkspaceLease(size_t bytes, hipStream_t s);
-    float* get() const { return p_; }
-
-   private:
-    std::unique_lock<std::mutex> lock_;
-    float* p_ = nullptr;
+// Plan of the tiled fp16-MFMA GEMM (256 x 256 tiles, coalesced raw loads, fp16-domain
+// decode): ok is false for shapes it does not cover (block formats with K % 256 != 0).
+struct TilePlan {
+    bool ok = false;
+    bool narrow = false;    // 128-token tiles (T <= 128)
+    int nsplit = 1, ksteps = 0;
+    size_t ws_bytes = 0;    // split-K partials
 };
+TilePlan plan_gemm_tile(int fmt, int64_t M, int64_t K, int64_t T, bool gated);
+void launch_gemm_tile(const TilePlan& p, int fmt, const void* W, const void* Wu, const void* X, const float* tscale,
+                      float* Y, int64_t M, int64_t K, int64_t T, float* ws, hipStream_t s);
 
-// Y[t][m] = sum over s < nsplit of P[s][t][m] (gated: P holds gate sums in columns
-// 0..M-1 and up sums in M..2M-1 of each 2M-wide row, and Y = silu(gate) * up).
-void launch_splitk_reduce(const float* P, float* Y, int64_t T, int64_t M, int nsplit, bool gated, hipStream_t s);
+// Plan of the weight-streaming fp16-MFMA GEMV for 2..32 tokens (block formats,
+// K % 256 == 0, K <= 2^20): each weight byte is read once per call.
+struct GemvMfmaPlan {
+    bool ok = false;
+    int nj = 1;             // 16-token column fragments
+    int nsplit = 1, kst = 0;
+    size_t ws_bytes = 0;    // split-K partials
+};
+GemvMfmaPlan plan_gemv_mfma(int fmt, int64_t M, int64_t K, int64_t N, bool gated);
+// y[n][m] = tscale[n] * sum_k W[m][k] x16[n][k] (x16 fp16, tscale never nullptr here).
+void launch_gemv_mfma(const GemvMfmaPlan& p, int fmt, const void* W, const void* Wu, const void* x16,
+                      const float* tscale, float* y, int64_t M, int64_t K, int64_t N, float* ws, hipStream_t s);
+
+// Y[t][m] = tscale[t] * sum over s < nsplit of P[s][t][m] (gated: P holds gate sums in
+// columns 0..M-1 and up sums in M..2M-1 of each 2M-wide row, and Y = silu(gate) * up).
+void launch_splitk_reduce(const float* P, float* Y, const float* tscale, int64_t T, int64_t M, int nsplit, bool gated,
+                          hipStream_t s);
 
 }  // namespace qmm

@@ -40,13 +40,14 @@
  * activations).  Products accumulate in fp32.
  *
  * Common rules for every entry point:
- *   - All array arguments are device pointers owned by the caller.  The only
- *     memory the library allocates is the split-K workspace of the MFMA products
- *     on few output tiles: stream-ordered allocations from a per-device pool the
- *     library keeps for the life of the process (its memory is retained, so a
- *     steady loop allocates nothing new).  While the stream is being captured
- *     into a graph no workspace is taken and those calls run unsplit.  Calls are
- *     re-entrant.  (Pre-allocated buffers with no allocation per pass:
+ *   - All array arguments are device pointers owned by the caller.  The library
+ *     allocates no memory and keeps no state: the MFMA products that need scratch
+ *     memory (split-K partials; fp32 tokens converted to scaled fp16) take it from a
+ *     caller-owned workspace whose size qmm_workspace_size reports for the same
+ *     arguments; calls that need none accept NULL, 0.  The same arguments always
+ *     run the same kernels, eagerly or while the stream is captured into a graph.
+ *     Calls are re-entrant; two calls that run concurrently need separate
+ *     workspaces.  (Pre-allocated scratch buffers and no allocation per pass:
  *     "EdgeRunner Core Architecture", section 10 Scratch Buffers and section 15,
  *     item 4.)
  *   - stream is a hipStream_t passed as void* (NULL = the default stream).  All
@@ -59,7 +60,8 @@
  *     parser treats files as untrusted).
  *   - Outputs must not alias inputs (not checked), except where a call says so.
  *   - Alignment: W, x, X, gamma must be 16-byte aligned; y, Y, h, H, r 4-byte aligned
- *     (out of qmm_get_rows / qmm_expand_f16: 16 bytes).
+ *     (out of qmm_get_rows / qmm_expand_f16: 16 bytes); a workspace
+ *     QMM_WORKSPACE_ALIGN (256) bytes.
  *   - Limits: 1 <= M, K, N, T <= 2^31 - 1 and K % 32 == 0 for every format (F16
  *     included, so that all formats share the 32-wide tiling).
  */
@@ -90,14 +92,26 @@ typedef enum {
     QMM_ERR_OVERFLOW = -5,    /* a byte count does not fit in int64                */
     QMM_ERR_HIP = -6,         /* the HIP runtime reported an error at launch       */
     QMM_ERR_VARIANT = -7,     /* unknown variant id passed to a *_variant call     */
-    QMM_ERR_ARG = -8          /* a scalar argument is out of range (eps)           */
+    QMM_ERR_ARG = -8,         /* a scalar argument is out of range (eps, op id)    */
+    QMM_ERR_WORKSPACE = -9    /* workspace NULL or smaller than the call needs     */
 } qmm_status;
+
+/* Alignment every workspace pointer must have. */
+#define QMM_WORKSPACE_ALIGN 256
+
+/* Operation ids for qmm_workspace_size. */
+typedef enum {
+    QMM_OP_GEMV = 1,              /* qmm_gemv, qmm_gemv_variant                   */
+    QMM_OP_GATE_UP_SILU = 2,      /* qmm_gate_up_silu, qmm_gate_up_silu_variant   */
+    QMM_OP_GEMM = 3,              /* qmm_gemm                                     */
+    QMM_OP_GEMM_GATE_UP_SILU = 4  /* qmm_gemm_gate_up_silu                        */
+} qmm_op;
 
 /* Variant ids for qmm_gemv_variant, qmm_gate_up_silu_variant and qmm_gemv_choose. */
 typedef enum {
     QMM_VARIANT_AUTO = 0,     /* library picks from (fmt, M, K, N)                          */
     QMM_VARIANT_VALU = 1,     /* register-decode GEMV: one weight read, N fp32 FMAs          */
-    QMM_VARIANT_MFMA = 2      /* LDS-tile decode + fp16 MFMA (x rounded to fp16 in-kernel)   */
+    QMM_VARIANT_MFMA = 2      /* LDS-tile decode + fp16 MFMA (x scaled per token, then fp16) */
 } qmm_variant;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -105,6 +119,23 @@ int qmm_version(void);
 
 /* Human-readable text for a qmm_status value (static storage; never NULL). */
 const char* qmm_strerror(int status);
+
+/*
+ * Bytes of caller-owned device workspace that the call of operation `op`
+ * (QMM_OP_*) with these arguments needs, 0 when it needs none; a negative
+ * qmm_status for invalid arguments.  M is the output rows (I for the gated
+ * products), N the token count (T for the GEMMs); `variant` is the variant passed
+ * to qmm_gemv_variant / qmm_gate_up_silu_variant (QMM_VARIANT_AUTO for qmm_gemv,
+ * qmm_gate_up_silu and the GEMMs, where it is ignored).  Host-only; makes no HIP
+ * call.  The workspace holds a call's split-K partial sums (when the output tiles
+ * cannot fill the GPU, K is split over several workgroups and a second kernel adds
+ * their sums in a fixed order) and, for the fp32-token MFMA variant, the tokens
+ * converted to scaled fp16 and their scales.  Its contents need no initialisation
+ * and are dead after the call's kernels finish.  ("EdgeRunner Core Architecture",
+ * section 10 Scratch Buffers: scratch memory is allocated once and reused by every
+ * pass.)
+ */
+int64_t qmm_workspace_size(int op, int fmt, int64_t M, int64_t K, int64_t N, int variant);
 
 /*
  * Bytes per weight row: K/32 blocks of 34 (Q8_0), 18 (Q4_0), 20 (Q4_1), 22 (Q5_0) or
@@ -159,22 +190,34 @@ int qmm_expand_f16(int fmt, const void* W, void* out, int64_t M, int64_t K, void
  * and reuses it N times.  ("EdgeRunner Core Architecture", section 2.1 fused
  * Q8_0 dequant + GEMV pipelines; "llama.cpp Metal ...", section 3.2 and P9:
  * per-format mat-vec kernels for one token and a batched mat-vec for 2..8 tokens.)
- * The variant is chosen from (fmt, M, K, N) as qmm_gemv_choose reports.
- * Precision: accumulation is fp32 everywhere.  For the block formats the register-decode
- * variant holds x in block floating point (each 32-value block scaled by a power
- * of two, then rounded to fp16) and forms the products with packed fp16 dot
- * products; F16 weights and rows it leaves to its fallback use fp32 x.  The MFMA
- * variant, used for larger N, rounds x to fp16 inside the kernel.  Either way
- * |y - y_exact| <= about 2^-11 sum_k |W[m][k] x[n][k]|, and x = e_k returns the
- * column W[:, k] exactly on the register-decode variant.
+ * The variant is chosen from (fmt, M, K, N) as qmm_gemv_choose reports; workspace
+ * (workspace_bytes of it) must hold qmm_workspace_size(QMM_OP_GEMV, ...) bytes
+ * (NULL, 0 when that is 0, as it is for the register-decode variant), else
+ * QMM_ERR_WORKSPACE.
+ * Precision ("alpaca.swift", Numerical validation: each reduced-precision path has
+ * a derived element-wise bound): accumulation is fp32 everywhere.
+ *   Register-decode variant, block formats: x is held in block floating point
+ *   (each 32-value block scaled by a power of two, then rounded to fp16) and every
+ *   weight code enters packed fp16 dot products exactly, so
+ *   |y - y_exact| <= (2^-11 + 3 (25 + K/2048) 2^-23)(1 + 2^-11) sum_k |W[m][k] x[n][k]|
+ *   for every finite x (blocks whose dynamic range fp16 cannot hold take an exact
+ *   fp32 path); x = e_k returns W[:, k] exactly (biased formats: d u + m rounded
+ *   once).  F16 weights and rows left to its fallback use fp32 x and fp32 FMAs.
+ *   MFMA variant: each token is scaled by a power of two (its largest |x| into
+ *   [2^14, 2^15)) and rounded to fp16; weights enter as fp16(w), one rounding;
+ *   |y - y_exact| <= about 2^-10 sum_k |W[m][k] x[n][k]| while every decoded |w|
+ *   is below 65520 (larger ones overflow fp16) and no nonzero x lies more than
+ *   2^28 below its token's largest (such elements keep an absolute error of at
+ *   most 2^-39 times that largest).
  * Fused QKV is this call on the row-concatenation [Wq; Wk; Wv] (M = q + 2 kv).
  */
 int qmm_gemv(int fmt, const void* W, const float* x, float* y,
-             int64_t M, int64_t K, int64_t N, void* stream);
+             int64_t M, int64_t K, int64_t N, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* As qmm_gemv with an explicit variant (QMM_VARIANT_*), for crossover sweeps. */
 int qmm_gemv_variant(int fmt, const void* W, const float* x, float* y,
-                     int64_t M, int64_t K, int64_t N, int variant, void* stream);
+                     int64_t M, int64_t K, int64_t N, int variant,
+                     void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * The variant qmm_gemv would run for these sizes (a QMM_VARIANT_* value >= 1),
@@ -194,15 +237,17 @@ int qmm_gemv_choose(int fmt, int64_t M, int64_t K, int64_t N);
  *   g = x Wg^T, u = x Wu^T, h[n][i] = silu(g[n][i]) * u[n][i],  silu(z) = z / (1 + e^-z).
  * Wg and Wu are two I x K matrices in the same format (a concatenated [gate; up]
  * buffer is Wg = base, Wu = base + I * qmm_row_bytes(fmt, K)).  h is N x I fp32.
+ * Workspace and precision of g and u as for qmm_gemv (QMM_OP_GATE_UP_SILU).
  * ("EdgeRunner Core Architecture", section 8 SwiGLU FFN: SiLU of the gate times
  * up, fused into one dispatch for single-token decode.)
  */
 int qmm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const float* x, float* h,
-                     int64_t I, int64_t K, int64_t N, void* stream);
+                     int64_t I, int64_t K, int64_t N, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* As qmm_gate_up_silu with an explicit variant (QMM_VARIANT_*), for crossover sweeps. */
 int qmm_gate_up_silu_variant(int fmt, const void* Wg, const void* Wu, const float* x, float* h,
-                             int64_t I, int64_t K, int64_t N, int variant, void* stream);
+                             int64_t I, int64_t K, int64_t N, int variant,
+                             void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * Decode GEMV with the RMSNorm prologue fused in:
@@ -245,19 +290,27 @@ int qmm_gemv_add(int fmt, const void* W, const float* x, const float* r, float* 
  * Prefill GEMM: Y[t][m] = sum_k W[m][k] * X[t][k], X fp16 (T x K), Y fp32 (T x M).
  * Weight blocks are decoded into fp16 MFMA operands, each exact weight (d*q, or
  * d*u + m) rounded once to nearest even -- the values qmm_expand_f16 writes -- and
- * fed to fp16 MFMA with fp32 accumulation.  ("alpaca.swift", Design and
- * Capabilities: prefill on the matrix hardware with half-precision activations;
- * Numerical validation: element-wise error bound proportional to sum |x w|.)
+ * fed to fp16 MFMA with fp32 accumulation.  Range: a decoded weight must satisfy
+ * |w| < 65520 (fp16(w) is infinite beyond), i.e. |d q| < 65520 for the block
+ * formats; within it |Y - Y_exact| <= about 2^-11 sum_k |W[m][k] X[t][k]| plus the
+ * fp32 accumulation.  workspace (workspace_bytes of it) must hold
+ * qmm_workspace_size(QMM_OP_GEMM, fmt, M, K, T, 0) bytes (the split-K partials when
+ * the tiles alone cannot fill the GPU; NULL, 0 when that is 0), else
+ * QMM_ERR_WORKSPACE.  ("alpaca.swift", Design and Capabilities: prefill on the
+ * matrix hardware with half-precision activations; Numerical validation:
+ * element-wise error bound proportional to sum |x w|.)
  */
 int qmm_gemm(int fmt, const void* W, const void* X, float* Y,
-             int64_t M, int64_t K, int64_t T, void* stream);
+             int64_t M, int64_t K, int64_t T, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * Prefill gate+up with the SwiGLU epilogue: H[t][i] = silu((X Wg^T)[t][i]) * (X Wu^T)[t][i].
- * X fp16 (T x K), H fp32 (T x I).  Same tiles and rounding as qmm_gemm.
+ * X fp16 (T x K), H fp32 (T x I).  Same tiles, rounding, range and workspace rule
+ * as qmm_gemm (QMM_OP_GEMM_GATE_UP_SILU).
  */
 int qmm_gemm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const void* X, float* H,
-                          int64_t I, int64_t K, int64_t T, void* stream);
+                          int64_t I, int64_t K, int64_t T, void* workspace, int64_t workspace_bytes,
+                          void* stream);
 
 #ifdef __cplusplus
 }

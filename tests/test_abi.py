@@ -16,7 +16,7 @@ import block_quantized_weight_gguf_amd as qmm
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qmm.h")
 
-OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR, E_ARG, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 A16 = 0x10000  # a 16-byte aligned fake address (never dereferenced)
 
 
@@ -31,7 +31,7 @@ def test_header_declares_expected_api():
         "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv", "qmm_gemv_variant",
         "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
         "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16", "qmm_rmsnorm_gemv",
-        "qmm_rmsnorm_gate_up_silu", "qmm_gemv_add"])
+        "qmm_rmsnorm_gate_up_silu", "qmm_gemv_add", "qmm_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert qmm.qmm_version() >= 100
-    for s in (OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR, E_ARG):
+    for s in (OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR, E_ARG, E_WS):
         assert qmm.qmm_strerror(s) and "unknown qmm status" not in qmm.qmm_strerror(s)
     assert "unknown" in qmm.qmm_strerror(-99)
 
@@ -68,38 +68,38 @@ def test_row_bytes_errors(fmt, K, want):
 
 def test_gemv_validation():
     L = qmm._lib
-    assert L.qmm_gemv(8, None, A16, A16, 4, 64, 1, None) == E_NULL
-    assert L.qmm_gemv(8, A16, None, A16, 4, 64, 1, None) == E_NULL
-    assert L.qmm_gemv(8, A16, A16, None, 4, 64, 1, None) == E_NULL
-    assert L.qmm_gemv(5, A16, A16, A16, 4, 64, 1, None) == E_FMT
-    assert L.qmm_gemv(8, A16, A16, A16, 0, 64, 1, None) == E_SHAPE
-    assert L.qmm_gemv(8, A16, A16, A16, 4, 0, 1, None) == E_SHAPE
-    assert L.qmm_gemv(8, A16, A16, A16, 4, 48, 1, None) == E_SHAPE
-    assert L.qmm_gemv(8, A16, A16, A16, 4, 64, 0, None) == E_SHAPE
-    assert L.qmm_gemv(8, A16, A16, A16, 2**31, 64, 1, None) == E_SHAPE
-    assert L.qmm_gemv(8, A16, A16, A16, 2**31 - 1, 2**31 - 32, 2**31 - 1, None) == E_OVF
-    assert L.qmm_gemv(8, A16 + 8, A16, A16, 4, 64, 1, None) == E_ALIGN
-    assert L.qmm_gemv(8, A16, A16 + 4, A16, 4, 64, 1, None) == E_ALIGN
-    assert L.qmm_gemv(8, A16, A16, A16 + 2, 4, 64, 1, None) == E_ALIGN
-    assert L.qmm_gemv_variant(8, A16, A16, A16 + 2, 4, 64, 1, 1, None) == E_ALIGN
+    assert L.qmm_gemv(8, None, A16, A16, 4, 64, 1, None, 0, None) == E_NULL
+    assert L.qmm_gemv(8, A16, None, A16, 4, 64, 1, None, 0, None) == E_NULL
+    assert L.qmm_gemv(8, A16, A16, None, 4, 64, 1, None, 0, None) == E_NULL
+    assert L.qmm_gemv(5, A16, A16, A16, 4, 64, 1, None, 0, None) == E_FMT
+    assert L.qmm_gemv(8, A16, A16, A16, 0, 64, 1, None, 0, None) == E_SHAPE
+    assert L.qmm_gemv(8, A16, A16, A16, 4, 0, 1, None, 0, None) == E_SHAPE
+    assert L.qmm_gemv(8, A16, A16, A16, 4, 48, 1, None, 0, None) == E_SHAPE
+    assert L.qmm_gemv(8, A16, A16, A16, 4, 64, 0, None, 0, None) == E_SHAPE
+    assert L.qmm_gemv(8, A16, A16, A16, 2**31, 64, 1, None, 0, None) == E_SHAPE
+    assert L.qmm_gemv(8, A16, A16, A16, 2**31 - 1, 2**31 - 32, 2**31 - 1, None, 0, None) == E_OVF
+    assert L.qmm_gemv(8, A16 + 8, A16, A16, 4, 64, 1, None, 0, None) == E_ALIGN
+    assert L.qmm_gemv(8, A16, A16 + 4, A16, 4, 64, 1, None, 0, None) == E_ALIGN
+    assert L.qmm_gemv(8, A16, A16, A16 + 2, 4, 64, 1, None, 0, None) == E_ALIGN
+    assert L.qmm_gemv_variant(8, A16, A16, A16 + 2, 4, 64, 1, 1, None, 0, None) == E_ALIGN
 
 
 def test_gate_up_validation():
     L = qmm._lib
-    assert L.qmm_gate_up_silu(2, A16, None, A16, A16, 4, 64, 1, None) == E_NULL
-    assert L.qmm_gate_up_silu(4, A16, A16, A16, A16, 4, 64, 1, None) == E_FMT
-    assert L.qmm_gate_up_silu(2, A16, A16, A16, A16, 4, 40, 1, None) == E_SHAPE
-    assert L.qmm_gate_up_silu(2, A16, A16 + 4, A16, A16, 4, 64, 1, None) == E_ALIGN
+    assert L.qmm_gate_up_silu(2, A16, None, A16, A16, 4, 64, 1, None, 0, None) == E_NULL
+    assert L.qmm_gate_up_silu(4, A16, A16, A16, A16, 4, 64, 1, None, 0, None) == E_FMT
+    assert L.qmm_gate_up_silu(2, A16, A16, A16, A16, 4, 40, 1, None, 0, None) == E_SHAPE
+    assert L.qmm_gate_up_silu(2, A16, A16 + 4, A16, A16, 4, 64, 1, None, 0, None) == E_ALIGN
 
 
 def test_gemm_validation():
     L = qmm._lib
-    assert L.qmm_gemm(8, A16, None, A16, 4, 64, 8, None) == E_NULL
-    assert L.qmm_gemm(8, A16, A16, A16, 4, 64, 0, None) == E_SHAPE
-    assert L.qmm_gemm(8, A16, A16 + 2, A16, 4, 64, 8, None) == E_ALIGN
-    assert L.qmm_gemm_gate_up_silu(8, A16, A16, A16, None, 4, 64, 8, None) == E_NULL
-    assert L.qmm_gemm_gate_up_silu(9, A16, A16, A16, A16, 4, 64, 8, None) == E_FMT
-    assert L.qmm_gemm_gate_up_silu(8, A16, A16, A16, A16 + 1, 4, 64, 8, None) == E_ALIGN
+    assert L.qmm_gemm(8, A16, None, A16, 4, 64, 8, None, 0, None) == E_NULL
+    assert L.qmm_gemm(8, A16, A16, A16, 4, 64, 0, None, 0, None) == E_SHAPE
+    assert L.qmm_gemm(8, A16, A16 + 2, A16, 4, 64, 8, None, 0, None) == E_ALIGN
+    assert L.qmm_gemm_gate_up_silu(8, A16, A16, A16, None, 4, 64, 8, None, 0, None) == E_NULL
+    assert L.qmm_gemm_gate_up_silu(9, A16, A16, A16, A16, 4, 64, 8, None, 0, None) == E_FMT
+    assert L.qmm_gemm_gate_up_silu(8, A16, A16, A16, A16 + 1, 4, 64, 8, None, 0, None) == E_ALIGN
 
 
 def test_dequant_validation():
@@ -200,14 +200,14 @@ def test_variant_choice():
     assert L.qmm_gemv_choose(8, 14336, 4096, 3) == 1
     assert L.qmm_gemv_choose(2, 128256, 4096, 3) == 1
     assert L.qmm_gemv_choose(8, 4096, 100, 1) == E_SHAPE
-    assert L.qmm_gemv_variant(8, A16, A16, A16 + 1, 4, 64, 1, 9, None) == E_ALIGN
-    assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, 9, None) == E_VAR
-    assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, -1, None) == E_VAR
-    assert L.qmm_gate_up_silu_variant(8, A16, None, A16, A16, 4, 64, 1, 1, None) == E_NULL
-    assert L.qmm_gate_up_silu_variant(5, A16, A16, A16, A16, 4, 64, 1, 1, None) == E_FMT
-    assert L.qmm_gate_up_silu_variant(8, A16, A16, A16, A16, 4, 48, 1, 1, None) == E_SHAPE
-    assert L.qmm_gate_up_silu_variant(8, A16, A16 + 8, A16, A16, 4, 64, 1, 1, None) == E_ALIGN
-    assert L.qmm_gate_up_silu_variant(8, A16, A16, A16, A16, 4, 64, 1, 5, None) == E_VAR
+    assert L.qmm_gemv_variant(8, A16, A16, A16 + 1, 4, 64, 1, 9, None, 0, None) == E_ALIGN
+    assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, 9, None, 0, None) == E_VAR
+    assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, -1, None, 0, None) == E_VAR
+    assert L.qmm_gate_up_silu_variant(8, A16, None, A16, A16, 4, 64, 1, 1, None, 0, None) == E_NULL
+    assert L.qmm_gate_up_silu_variant(5, A16, A16, A16, A16, 4, 64, 1, 1, None, 0, None) == E_FMT
+    assert L.qmm_gate_up_silu_variant(8, A16, A16, A16, A16, 4, 48, 1, 1, None, 0, None) == E_SHAPE
+    assert L.qmm_gate_up_silu_variant(8, A16, A16 + 8, A16, A16, 4, 64, 1, 1, None, 0, None) == E_ALIGN
+    assert L.qmm_gate_up_silu_variant(8, A16, A16, A16, A16, 4, 64, 1, 5, None, 0, None) == E_VAR
 
 
 def test_binding_raises():
@@ -215,3 +215,51 @@ def test_binding_raises():
         qmm.qmm_gemv(8, 0, A16, A16, 4, 64, 1, stream=0)
     assert e.value.status == E_NULL
 
+
+
+OP_GEMV, OP_GATE, OP_GEMM, OP_GEMM_GATE = 1, 2, 3, 4
+AUTO, VALU, MFMA = 0, 1, 2
+
+
+def test_workspace_size():
+    """The size query: nothing for the register-decode products and for GEMMs whose
+    tiles fill the GPU; split-K partials otherwise; the fp32-token MFMA products add
+    the scaled fp16 tokens and their scales.  Sizes are whole multiples of 256."""
+    W = qmm._lib.qmm_workspace_size
+    assert W(OP_GEMV, 8, 4096, 4096, 1, AUTO) == 0
+    assert W(OP_GEMV, 8, 4096, 4096, 4, VALU) == 0
+    assert W(OP_GATE, 2, 14336, 4096, 2, AUTO) == 0
+    assert W(OP_GEMM, 8, 14336, 4096, 4096, AUTO) == 0             # 56 x 16 tiles: no split
+    part = W(OP_GEMM, 8, 14336, 4096, 128, AUTO)                   # 56 tiles: K split
+    assert part > 0 and part % 256 == 0
+    assert part % (128 * 14336 * 4) == 0
+    assert W(OP_GEMM_GATE, 8, 14336, 4096, 128, AUTO) >= 2 * part // 2
+    # MFMA GEMV at 8 tokens: fp16 tokens (8 x 4096 x 2), scales, partials (16 row tiles: split).
+    v = W(OP_GEMV, 8, 4096, 4096, 8, AUTO)
+    assert v >= 8 * 4096 * 2 + 256 + 8 * 4096 * 4 and v % 256 == 0
+    assert W(OP_GEMV, 8, 4096, 4096, 8, MFMA) == v
+    assert W(OP_GEMV, 1, 4096, 4096, 64, AUTO) >= 64 * 4096 * 2    # F16 through the GEMM
+    # Errors: op, variant, shape.
+    assert W(9, 8, 64, 64, 1, AUTO) == E_ARG
+    assert W(OP_GEMV, 8, 64, 64, 1, 7) == E_VAR
+    assert W(OP_GEMV, 8, 64, 48, 1, AUTO) == E_SHAPE
+    assert W(OP_GEMM, 5, 64, 64, 1, AUTO) == E_FMT
+    assert W(OP_GEMV, 8, 2**31 - 1, 2**31 - 32, 2**31 - 1, AUTO) == E_OVF
+
+
+def test_workspace_is_checked_before_any_launch():
+    """A call that needs a workspace refuses a missing, short or misaligned one (the
+    fake addresses are never touched: validation fails first)."""
+    L = qmm._lib
+    need = L.qmm_workspace_size(OP_GEMM, 8, 14336, 4096, 128, AUTO)
+    assert L.qmm_gemm(8, A16, A16, A16, 14336, 4096, 128, None, 0, None) == E_WS
+    assert L.qmm_gemm(8, A16, A16, A16, 14336, 4096, 128, A16, need - 1, None) == E_WS
+    assert L.qmm_gemm(8, A16, A16, A16, 14336, 4096, 128, A16 + 16, need, None) == E_ALIGN
+    need = L.qmm_workspace_size(OP_GEMM_GATE, 2, 14336, 4096, 128, AUTO)
+    assert L.qmm_gemm_gate_up_silu(2, A16, A16, A16, A16, 14336, 4096, 128, A16, need - 256, None) == E_WS
+    need = L.qmm_workspace_size(OP_GEMV, 2, 4096, 4096, 8, MFMA)
+    assert L.qmm_gemv_variant(2, A16, A16, A16, 4096, 4096, 8, MFMA, None, 0, None) == E_WS
+    assert L.qmm_gemv(2, A16, A16, A16, 4096, 4096, 8, A16, need - 1, None) == E_WS
+    need = L.qmm_workspace_size(OP_GATE, 8, 14336, 4096, 16, AUTO)
+    assert L.qmm_gate_up_silu(8, A16, A16, A16, A16, 14336, 4096, 16, A16, need // 2, None) == E_WS
+    assert L.qmm_gate_up_silu_variant(8, A16, A16, A16, A16, 14336, 4096, 16, MFMA, A16 + 128, need, None) == E_ALIGN

@@ -322,7 +322,7 @@ def test_gemv_mfma(fmt, M, K, N):
     torch.cuda.synchronize()
     assert guard_intact(buf, N * M)
     # x is rounded to fp16 inside the MFMA kernels: the oracle takes the same inputs.
-    y_ref, S = oracle.matmul_ref(fmt, raw, x.astype(np.float16), M, K)
+    y_ref, S = oracle.matmul_ref(fmt, raw, x, M, K)
     check_linear(buf[:N * M].cpu().numpy().reshape(N, M), y_ref, S, f"gemv mfma fmt={fmt} M={M} K={K} N={N}")
 
 
@@ -337,7 +337,7 @@ def test_gate_up_silu_mfma(fmt, I, K, N):
     qmm.qmm_gate_up_silu_variant(fmt, dev(rg), dev(ru), dev(x), buf, I, K, N, MFMA)
     torch.cuda.synchronize()
     assert guard_intact(buf, N * I)
-    h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, x.astype(np.float16), I, K)
+    h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, x, I, K)
     check_swiglu(buf[:N * I].cpu().numpy().reshape(N, I), h_ref, g, u, Sg, Su, "gate_up_silu mfma")
 
 

@@ -1,9 +1,11 @@
 """Calls captured into a HIP graph and replayed.
 
-Paths that use a split-K workspace outside of capture (small-batch MFMA GEMV, the
-tiled GEMM on few tiles) must run without one while the stream is captured.  Each
-graph is replayed several times with eager work and synchronisations in between,
-and every replay is checked against the oracle and against the first replay.
+The calls run the same kernels eagerly and under capture.  Those captured here use a
+caller workspace (allocated before the capture): the small-batch MFMA GEMV (tokens
+scaled to fp16 there, split-K partials) and the tiled GEMM on few tiles (split-K
+partials); the test asserts that each shape does split K.  Each graph is replayed
+several times with eager work (on a workspace of its own) and synchronisations in
+between, and every replay is checked against the oracle and against the first replay.
 """
 import numpy as np
 import pytest
@@ -43,20 +45,24 @@ def test_graph_gemv_small_batch_and_n1(fmt):
     y16 = torch.empty((16, M), device="cuda")
     y1 = torch.empty((1, M), device="cuda")
     scratch = torch.empty((16, M), device="cuda")
+    need = qmm.qmm_workspace_size(qmm.QMM_OP_GEMV, fmt, M, K, 16, MFMA)
+    assert need > 16 * K * 2 + 256, "this shape splits K (partials in the workspace)"
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws_noise = torch.empty(need, dtype=torch.uint8, device="cuda")
     announce(f"graph capture: gemv N=16 (mfma) + N=1, fmt={fmt} M={M} K={K}")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        qmm.qmm_gemv_variant(fmt, Wd, x16d, y16, M, K, 16, MFMA)
+        qmm.qmm_gemv_variant(fmt, Wd, x16d, y16, M, K, 16, MFMA, ws)
         qmm.qmm_gemv(fmt, Wd, x1d, y1, M, K, 1)
     torch.cuda.synchronize()
 
     def noise():
-        qmm.qmm_gemv_variant(fmt, Wd, x16d, scratch, M, K, 16, MFMA)  # eager, may use the workspace
+        qmm.qmm_gemv_variant(fmt, Wd, x16d, scratch, M, K, 16, MFMA, ws_noise)
 
     got16 = _replays(g, y16, noise)
-    y_ref, S = oracle.matmul_ref(fmt, raw, x16.astype(np.float16), M, K)
+    y_ref, S = oracle.matmul_ref(fmt, raw, x16, M, K)
     check_linear(got16, y_ref, S, f"graph gemv mfma fmt={fmt}")
     y_ref1, S1 = oracle.matmul_ref(fmt, raw, x1, M, K)
     check_linear(y1.cpu().numpy(), y_ref1, S1, f"graph gemv N=1 fmt={fmt}")
@@ -71,16 +77,20 @@ def test_graph_gemm_few_tiles(fmt):
     Wd, Xd = dev(raw), dev(X)
     Y = torch.empty((T, M), device="cuda")
     scratch = torch.empty((T, M), device="cuda")
+    need = qmm.qmm_workspace_size(qmm.QMM_OP_GEMM, fmt, M, K, T)
+    assert need >= 2 * T * M * 4, "this shape splits K"
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws_noise = torch.empty(need, dtype=torch.uint8, device="cuda")
     announce(f"graph capture: gemm split-K shape fmt={fmt} M={M} K={K} T={T}")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        qmm.qmm_gemm(fmt, Wd, Xd, Y, M, K, T)
+        qmm.qmm_gemm(fmt, Wd, Xd, Y, M, K, T, ws)
     torch.cuda.synchronize()
 
     def noise():
-        qmm.qmm_gemm(fmt, Wd, Xd, scratch, M, K, T)
+        qmm.qmm_gemm(fmt, Wd, Xd, scratch, M, K, T, ws_noise)
 
     got = _replays(g, Y, noise)
     y_ref, S = oracle.matmul_ref(fmt, raw, X, M, K)
@@ -93,14 +103,19 @@ def test_graph_gemm_gate_up_few_tiles():
     X = si.activations(T, K, 7203, dtype=np.float16)
     g_d, u_d, Xd = dev(rg), dev(ru), dev(X)
     H = torch.empty((T, I), device="cuda")
+    need = qmm.qmm_workspace_size(qmm.QMM_OP_GEMM_GATE_UP_SILU, fmt, I, K, T)
+    assert need >= 2 * T * 2 * I * 4, "this shape splits K"
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws_noise = torch.empty(need, dtype=torch.uint8, device="cuda")
     announce(f"graph capture: gemm gate_up split-K shape I={I} K={K} T={T}")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        qmm.qmm_gemm_gate_up_silu(fmt, g_d, u_d, Xd, H, I, K, T)
+        qmm.qmm_gemm_gate_up_silu(fmt, g_d, u_d, Xd, H, I, K, T, ws)
     torch.cuda.synchronize()
-    got = _replays(g, H, lambda: qmm.qmm_gemm_gate_up_silu(fmt, g_d, u_d, Xd, torch.empty_like(H), I, K, T))
+    got = _replays(g, H, lambda: qmm.qmm_gemm_gate_up_silu(fmt, g_d, u_d, Xd, torch.empty_like(H), I, K, T,
+                                                            ws_noise))
     h_ref, gg, uu, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, X, I, K)
     check_swiglu(got, h_ref, gg, uu, Sg, Su, "graph gemm gate_up")
 

@@ -179,7 +179,7 @@ def test_gemv_mfma_small_batch(fmt, M, K, N):
     torch.cuda.synchronize()
     assert guard_intact(buf, N * M)
     # The MFMA variant rounds x to fp16: the oracle takes the same fp16 inputs.
-    y_ref, S = oracle.matmul_ref(fmt, raw, x.astype(np.float16), M, K)
+    y_ref, S = oracle.matmul_ref(fmt, raw, x, M, K)
     check_linear(buf[:N * M].cpu().numpy().reshape(N, M), y_ref, S, f"gemv mfma fmt={fmt} M={M} K={K} N={N}")
 
 
@@ -246,7 +246,7 @@ def test_gemv_mfma_tile_fp32_x(fmt, M, K, N):
     announce(f"gemv mfma (tile, fp32 x) fmt={fmt} M={M} K={K} N={N}")
     y = qmm.gemv(fmt, dev(raw), dev(x), M, K, variant=MFMA)
     torch.cuda.synchronize()
-    y_ref, S = oracle.matmul_ref(fmt, raw, x.astype(np.float16), M, K)
+    y_ref, S = oracle.matmul_ref(fmt, raw, x, M, K)
     check_linear(y.cpu().numpy(), y_ref, S, f"gemv mfma tile fmt={fmt} N={N}")
 
 
@@ -339,3 +339,29 @@ def test_stream_argument():
     y0 = qmm.gemv(fmt, Wd, xd, M, K)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FID.get)
+@pytest.mark.parametrize("scale", [1e6, 1e30, 1e-35, 1e-42], ids=["1e6", "1e30", "1e-35", "fp32-subnormal"])
+@pytest.mark.parametrize("M,K,N", [(300, 1024, 8), (257, 2048, 48)])
+def test_mfma_x_beyond_fp16_range(fmt, scale, M, K, N):
+    """The MFMA variant scales each token by a power of two before rounding it to fp16,
+    so x far outside fp16's range (or inside its subnormals) keeps the bound; every
+    token here also has its own magnitude (tokens spread over 1e-6 .. 1 of the scale,
+    so that the exact outputs stay inside fp32's range).  8 tokens: the
+    weight-streaming MFMA GEMV; 48: the tiled GEMM."""
+    seed = 3400 + M + K + N
+    raw = si.weights(fmt, M, K, seed, scale_mode="gemm_wide", q8_low=-128)
+    spread = np.logspace(-6, 0, N).astype(np.float64)[:, None]
+    x = (si.activations(N, K, seed + 1).astype(np.float64) * scale * spread).astype(np.float32)
+    announce(f"mfma x range fmt={fmt} scale={scale} M={M} K={K} N={N}")
+    y = qmm.gemv(fmt, dev(raw), dev(x), M, K, variant=MFMA)
+    torch.cuda.synchronize()
+    y_ref, S = oracle.matmul_ref(fmt, raw, x, M, K)
+    check_linear(y.cpu().numpy(), y_ref, S, f"mfma x range fmt={fmt} scale={scale} N={N}")
+    rg, ru = raw, si.weights(fmt, M, K, seed + 2, scale_mode="gemm_wide", q8_low=-128)
+    xs = (x.astype(np.float64) / max(scale, 1.0)).astype(np.float32)  # keep silu's argument finite
+    h = qmm.gate_up_silu(fmt, dev(rg), dev(ru), dev(xs), M, K, variant=MFMA)
+    torch.cuda.synchronize()
+    h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, xs, M, K)
+    check_swiglu(h.cpu().numpy(), h_ref, g, u, Sg, Su, f"mfma gate_up x range fmt={fmt} scale={scale}")
