@@ -25,7 +25,8 @@ __all__ = [
     "qmm_gemv_variant", "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
     "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16", "qmm_rmsnorm_gemv", "qmm_rmsnorm_gate_up_silu",
     "qmm_gemv_add", "QMM_ERR_ARG", "QMM_ERR_WORKSPACE", "QMM_WORKSPACE_ALIGN", "qmm_workspace_size",
-    "QMM_OP_GEMV", "QMM_OP_GATE_UP_SILU", "QMM_OP_GEMM", "QMM_OP_GEMM_GATE_UP_SILU",
+    "QMM_OP_GEMV", "QMM_OP_GATE_UP_SILU", "QMM_OP_GEMM", "QMM_OP_GEMM_GATE_UP_SILU", "qmm_gemm_noalloc",
+    "QMM_ERR_SCRATCH", "QMM_NOALLOC_SCRATCH_BYTES",
     "gemv", "get_rows", "expand_f16", "rmsnorm_gemv", "rmsnorm_gate_up_silu", "gemv_add", "gate_up_silu", "gemm", "gemm_gate_up_silu", "dequant",
 ]
 
@@ -33,6 +34,8 @@ QMM_F16, QMM_Q4_0, QMM_Q4_1, QMM_Q5_0, QMM_Q5_1, QMM_Q8_0 = 1, 2, 3, 6, 7, 8
 QMM_VARIANT_AUTO, QMM_VARIANT_VALU, QMM_VARIANT_MFMA = 0, 1, 2
 QMM_ERR_ARG = -8
 QMM_ERR_WORKSPACE = -9
+QMM_ERR_SCRATCH = -10
+QMM_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 QMM_WORKSPACE_ALIGN = 256
 QMM_OP_GEMV, QMM_OP_GATE_UP_SILU, QMM_OP_GEMM, QMM_OP_GEMM_GATE_UP_SILU = 1, 2, 3, 4
 
@@ -65,6 +68,7 @@ _SIGS = {
     "qmm_gemv_add": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "qmm_gemm": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]),
     "qmm_gemm_gate_up_silu": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]),
+    "qmm_gemm_noalloc": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -209,6 +213,10 @@ def qmm_gemv_add(fmt, W, x, r, y, M, K, N, stream=None) -> None:
 def qmm_gemm(fmt, W, X, Y, M, K, T, workspace=None, workspace_bytes=None, stream=None) -> None:
     wp, wb, _keep = _workspace(QMM_OP_GEMM, fmt, M, K, T, QMM_VARIANT_AUTO, (Y, X), workspace, workspace_bytes)
     _check(_lib.qmm_gemm(fmt, _ptr(W), _ptr(X), _ptr(Y), M, K, T, wp, wb, _stream(stream)), "qmm_gemm")
+
+
+def qmm_gemm_noalloc(fmt, W, X, Y, M, K, T, stream=None) -> None:
+    _check(_lib.qmm_gemm_noalloc(fmt, _ptr(W), _ptr(X), _ptr(Y), M, K, T, _stream(stream)), "qmm_gemm_noalloc")
 
 
 def qmm_gemm_gate_up_silu(fmt, Wg, Wu, X, H, I, K, T, workspace=None, workspace_bytes=None, stream=None) -> None:

@@ -158,6 +158,7 @@ const char* qmm_strerror(int status) {
         case QMM_ERR_VARIANT: return "unknown GEMV variant";
         case QMM_ERR_ARG: return "a scalar argument is out of range (eps must be finite and >= 0; op id)";
         case QMM_ERR_WORKSPACE: return "workspace missing or smaller than qmm_workspace_size reports";
+        case QMM_ERR_SCRATCH: return "the call needs more scratch than qmm_gemm_noalloc's fixed array holds";
         default: return "unknown qmm status";
     }
 }

@@ -93,11 +93,15 @@ typedef enum {
     QMM_ERR_HIP = -6,         /* the HIP runtime reported an error at launch       */
     QMM_ERR_VARIANT = -7,     /* unknown variant id passed to a *_variant call     */
     QMM_ERR_ARG = -8,         /* a scalar argument is out of range (eps, op id)    */
-    QMM_ERR_WORKSPACE = -9    /* workspace NULL or smaller than the call needs     */
+    QMM_ERR_WORKSPACE = -9,   /* workspace NULL or smaller than the call needs     */
+    QMM_ERR_SCRATCH = -10     /* qmm_gemm_noalloc: the call needs more than its fixed scratch */
 } qmm_status;
 
 /* Alignment every workspace pointer must have. */
 #define QMM_WORKSPACE_ALIGN 256
+
+/* Bytes of the fixed device scratch array qmm_gemm_noalloc uses on each GPU. */
+#define QMM_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
 
 /* Operation ids for qmm_workspace_size. */
 typedef enum {
@@ -302,6 +306,21 @@ int qmm_gemv_add(int fmt, const void* W, const float* x, const float* r, float* 
  */
 int qmm_gemm(int fmt, const void* W, const void* X, float* Y,
              int64_t M, int64_t K, int64_t T, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * qmm_gemm for callers that cannot allocate: code under graph capture that owns no
+ * buffers, tight serving loops, harnesses that forbid hipMalloc.  The same kernels
+ * and results as qmm_gemm with a workspace, but the split-K partials live in a fixed
+ * device array of QMM_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends; the call allocates nothing of any kind.  Every call
+ * on a GPU shares that GPU's array, so calls that overlap on one GPU race (serialise
+ * them: one stream, or events).  A call whose partials would not fit returns
+ * QMM_ERR_SCRATCH (qmm_gemm's plan needs at most 64 MiB).  The device address of the
+ * array is looked up once per device, on the first call made with that device
+ * current.  Other arguments and errors as qmm_gemm.
+ */
+int qmm_gemm_noalloc(int fmt, const void* W, const void* X, float* Y,
+                     int64_t M, int64_t K, int64_t T, void* stream);
 
 /*
  * Prefill gate+up with the SwiGLU epilogue: H[t][i] = silu((X Wg^T)[t][i]) * (X Wu^T)[t][i].

@@ -16,7 +16,7 @@ import block_quantized_weight_gguf_amd as qmm
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qmm.h")
 
-OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR, E_ARG, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR, E_ARG, E_WS, E_SCR = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
 A16 = 0x10000  # a 16-byte aligned fake address (never dereferenced)
 
 
@@ -31,7 +31,7 @@ def test_header_declares_expected_api():
         "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv", "qmm_gemv_variant",
         "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
         "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16", "qmm_rmsnorm_gemv",
-        "qmm_rmsnorm_gate_up_silu", "qmm_gemv_add", "qmm_workspace_size"])
+        "qmm_rmsnorm_gate_up_silu", "qmm_gemv_add", "qmm_workspace_size", "qmm_gemm_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert qmm.qmm_version() >= 100
-    for s in (OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR, E_ARG, E_WS):
+    for s in (OK, E_NULL, E_FMT, E_SHAPE, E_ALIGN, E_OVF, E_HIP, E_VAR, E_ARG, E_WS, E_SCR):
         assert qmm.qmm_strerror(s) and "unknown qmm status" not in qmm.qmm_strerror(s)
     assert "unknown" in qmm.qmm_strerror(-99)
 
@@ -263,3 +263,29 @@ def test_workspace_is_checked_before_any_launch():
     need = L.qmm_workspace_size(OP_GATE, 8, 14336, 4096, 16, AUTO)
     assert L.qmm_gate_up_silu(8, A16, A16, A16, A16, 14336, 4096, 16, A16, need // 2, None) == E_WS
     assert L.qmm_gate_up_silu_variant(8, A16, A16, A16, A16, 14336, 4096, 16, MFMA, A16 + 128, need, None) == E_ALIGN
+
+
+def test_gemm_noalloc_validation():
+    """The allocation-free GEMM checks its arguments as qmm_gemm does, before any HIP
+    call (the fake addresses are never touched)."""
+    L = qmm._lib
+    assert L.qmm_gemm_noalloc(8, None, A16, A16, 4, 64, 8, None) == E_NULL
+    assert L.qmm_gemm_noalloc(8, A16, A16, None, 4, 64, 8, None) == E_NULL
+    assert L.qmm_gemm_noalloc(5, A16, A16, A16, 4, 64, 8, None) == E_FMT
+    assert L.qmm_gemm_noalloc(8, A16, A16, A16, 4, 48, 8, None) == E_SHAPE
+    assert L.qmm_gemm_noalloc(8, A16, A16, A16, 4, 64, 0, None) == E_SHAPE
+    assert L.qmm_gemm_noalloc(8, A16, A16 + 2, A16, 4, 64, 8, None) == E_ALIGN
+    assert L.qmm_gemm_noalloc(8, A16, A16, A16 + 1, 4, 64, 8, None) == E_ALIGN
+
+
+def test_gemm_workspace_fits_the_noalloc_scratch():
+    """qmm_gemm's plan never needs more than the fixed 64 MiB of qmm_gemm_noalloc, over
+    token counts and row counts around the split thresholds."""
+    W = qmm._lib.qmm_workspace_size
+    worst = 0
+    for fmt in (1, 2, 8):
+        for M in (1, 255, 256, 257, 4096, 12288, 14336, 49151, 49152):
+            for T in (1, 100, 128, 129, 256, 1000, 2048, 2304, 4096):
+                for K in (4096, 14336):
+                    worst = max(worst, W(OP_GEMM, fmt, M, K, T, AUTO))
+    assert 0 < worst <= qmm.QMM_NOALLOC_SCRATCH_BYTES
