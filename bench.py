@@ -7,20 +7,29 @@ once with Q8_0 weights and once with Q4_0 weights.  Inputs are seeded synthetic
 tensors resident in HBM before timing starts.  The step streams 1.21 GB of
 weights, more than the 256 MB Infinity Cache, so every launch reads from HBM.
 
-value = algorithmic bytes of one step (raw weight blocks + x + y) / step time.
+value = algorithmic bytes of one step (raw weight blocks + x + y) / step time, the
+median of 7 trials of K steps each (the pages' own protocol: "alpaca.swift",
+Results, median of 7 runs).
 
-The same run also times the prefill GEMM (fp16 activations, fp32 output) at
-4096->14336 and 14336->4096 for T in {128, 2048, 4096}, Q8_0 and Q4_0, and reports
-TFLOP/s = 2 T M K / time; and times the float64 CPU oracle on a bounded sample of
-the decode step (reported baseline only).
-
+The same run also times, each as the median of 7 trials:
+  * the single 576 x 576 Q8_0 GEMV with seed 0 (latency-bound; its 352 KB stay in
+    the caches);
+  * the prefill GEMM (fp16 activations, fp32 output) at 4096->14336 and
+    14336->4096 for T in {128, 2048, 4096}, Q8_0 and Q4_0, with the weights rotated
+    through copies totalling >= 512 MB so that every call streams them from HBM;
+    TFLOP/s = 2 T M K / time;
+  * a SmolLM2-135M-shaped decode step (30 layers + LM head), with its weights
+    rotated through >= 512 MB of copies, and on one resident set (labelled);
+  * small-batch decode (N in {1, 2, 4, 8, 16}), replayed as HIP graphs of rotated
+    calls so that host launch overhead stays out;
+  * the float64 CPU oracle per workload on bounded samples (unpack and matmul
+    timed apart; reported baseline only).
 Further sections (timing only): the decode step with the RMSNorm prologues and
 residual epilogues fused in, expand-then-GEMM prefill against the fused GEMM,
-the quantised embedding row gather, small-batch decode, measured ceilings, a
-SmolLM2-135M-shaped decode step, and the decode step and prefill route of the
-Q4_1 / Q5_0 / Q5_1 formats.
+the quantised embedding row gather, measured ceilings, and the decode step and
+prefill route of the Q4_1 / Q5_0 / Q5_1 formats.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--suite PATH]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--trials 7] [--no-cpu] [--suite PATH]
 """
 from __future__ import annotations
 
@@ -44,6 +53,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--trials", type=int, default=7, help="timed trials per figure; the median is reported")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-smollm", action="store_true")
@@ -55,6 +65,33 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
     return p.parse_args()
+
+
+POOL_BYTES = 512 << 20          # rotation pool: 2 x the 256 MB Infinity Cache
+
+
+def median_trials(torch, body, trials, per):
+    """Median over `trials` of (event time of one call of body()) / per, in ms; the
+    device is synchronised before and after every trial."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(trials):
+        torch.cuda.synchronize()
+        e0.record()
+        body()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / per)
+    return float(np.median(ts)), ts
+
+
+def graph_of(torch, body):
+    """body() captured once into a HIP graph (on a side stream, as torch requires)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    torch.cuda.synchronize()
+    return g
 
 
 class Timer:
@@ -210,108 +247,279 @@ def more_formats(torch, qmm, si, steps, reps=10):
     return out
 
 
-def prefill_cases(torch, qmm, si):
+def config1(torch, qmm, si, trials, calls=400):
+    """The single Q8_0 GEMV 576 x 576 (W seed 0, x seed 1), N = 1: time per call as
+    back-to-back launches and as a replayed graph of `calls` launches.  Its 352 KB
+    of weights stay in the caches between calls: the figure is the launch-and-latency
+    time of one small GEMV, not an HBM rate."""
     dev = torch.device("cuda")
-    cases = []
+    M = K = 576
+    W = torch.from_numpy(si.weights(si.FMT_Q8_0, M, K, 0)).to(dev)
+    x = torch.from_numpy(si.activations(1, K, 1)).to(dev)
+    y = torch.empty(M, device=dev)
+    nbytes = M * qmm.qmm_row_bytes(si.FMT_Q8_0, K) + 4 * K + 4 * M
+
+    def body():
+        for _ in range(calls):
+            qmm.qmm_gemv(si.FMT_Q8_0, W, x, y, M, K, 1)
+
+    body()
+    eager_ms, _ = median_trials(torch, body, trials, calls)
+    g = graph_of(torch, body)
+    g.replay()
+    graph_ms, _ = median_trials(torch, g.replay, trials, calls)
+    del g
+    return {"workload": "Q8_0 GEMV 576x576, N=1, W seed 0, x seed 1 (cache-resident, latency-bound)",
+            "us_per_call_eager": round(eager_ms * 1e3, 3), "us_per_call_graph": round(graph_ms * 1e3, 3),
+            "tok_s_graph": round(1e3 / graph_ms, 1), "GBps_graph": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),
+            "bytes": int(nbytes), "calls_per_trial": calls, "trials": trials}
+
+
+def rotation_pool(torch, make, nbytes):
+    """Enough copies (from make(i)) that together they exceed POOL_BYTES."""
+    copies = max(1, -(-POOL_BYTES // nbytes))
+    return [make(i) for i in range(copies)]
+
+
+def prefill(torch, qmm, si, trials):
+    """Prefill GEMM cases, weights rotated through >= 512 MB of copies (one call per
+    copy in turn), >= 200 calls and >= 2 ms per trial; median of the trials."""
+    dev = torch.device("cuda")
+    details = []
+    tot_f, tot_ms = 0.0, 0.0
     for fmt in (si.FMT_Q8_0, si.FMT_Q4_0):
         for (M, K) in ((14336, 4096), (4096, 14336)):
-            Wt = torch.from_numpy(si.weights(fmt, M, K, 7000 + M % 101 + fmt)).to(dev)
+            base = torch.from_numpy(si.weights(fmt, M, K, 7000 + M % 101 + fmt)).to(dev)
+            pool = rotation_pool(torch, lambda i: base.clone(), base.numel())
             for T in (128, 2048, 4096):
                 Xt = torch.from_numpy(si.activations(T, K, 7100 + T, dtype=np.float16)).to(dev)
                 Yt = torch.empty((T, M), device=dev)
-                cases.append(dict(fmt=fmt, M=M, K=K, T=T, flops=2.0 * T * M * K,
-                                  fn=lambda fmt=fmt, Wt=Wt, Xt=Xt, Yt=Yt, M=M, K=K, T=T:
-                                  qmm.qmm_gemm(fmt, Wt, Xt, Yt, M, K, T)))
-    return cases
+                ws = torch.empty(max(1, qmm.qmm_workspace_size(qmm.QMM_OP_GEMM, fmt, M, K, T)), dtype=torch.uint8,
+                                 device=dev)
+
+                def call(i):
+                    qmm.qmm_gemm(fmt, pool[i % len(pool)], Xt, Yt, M, K, T, ws)
+                for i in range(3):
+                    call(i)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call(0)
+                e1.record()
+                torch.cuda.synchronize()
+                calls = max(200, int(2.0 / max(e0.elapsed_time(e1), 1e-3)) + 1)
+
+                def body():
+                    for i in range(calls):
+                        call(i)
+                ms, _ = median_trials(torch, body, trials, calls)
+                fl = 2.0 * T * M * K
+                tot_f += fl
+                tot_ms += ms
+                details.append({"fmt": si.FMT_NAMES[fmt], "M": M, "K": K, "T": T, "us": round(ms * 1e3, 2),
+                                "TFLOPs": round(fl / (ms * 1e-3) / 1e12, 1),
+                                "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
+                                "copies": len(pool), "calls_per_trial": calls})
+                del Xt, Yt, ws
+            del pool, base
+            torch.cuda.empty_cache()
+    tflops = tot_f / (tot_ms * 1e-3) / 1e12
+    return {"value": round(tflops, 1), "unit": "TFLOP/s", "peak": FP16_MFMA_PEAK_TFLOPS,
+            "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+            "workload": "Q8_0+Q4_0 x {4096->14336, 14336->4096} x T in {128,2048,4096}, fp16 X, fp32 Y; "
+                        "weights rotated through >= 512 MB of copies; median of trials",
+            "cases": details}
 
 
-def cpu_baseline(host, fmts, budget_s=20.0):
-    """The float64 oracle on a bounded sample of the same decode step.
-
-    Walks the step's projections in order (Q8_0 pass, then Q4_0 pass), each on the
-    very weight bytes the GPU streamed, until about budget_s seconds of CPU work;
-    reports weight-stream GB/s like the GPU figure.
+def cpu_baseline(host, si, trials, rows=512):
+    """The float64 oracle on the host cores, per workload, on bounded samples (about
+    20-30 s of CPU work); each figure is the median of `trials` runs, with the unpack
+    (raw blocks -> float64 weights) and the matmul (numpy BLAS on all threads) timed
+    apart.  A reported baseline, never a target.
+      * single 576 x 576 Q8_0 GEMV (seed 0): whole;
+      * Llama-3-8B decode GEMVs, Q8_0 and Q4_0: the first `rows` rows of each of the
+        step's matrices (the very bytes the GPU streamed), scaled to whole matrices;
+      * SmolLM2-135M decode step: one layer and 1024 LM-head rows, scaled to 30 layers
+        and 49152 rows;
+      * small-batch GEMV, 16 tokens, on the sampled O rows (F16, Q8_0, Q4_0);
+      * prefill GEMM, T in {128, 2048, 4096}, on the sampled rows of 14336 x 4096.
     """
     import oracle
-    total_bytes = 0.0
-    total_t = 0.0
-    done = []
-    for (fmt, seed), (raw, M, K) in host.items():
-        if total_t > budget_s:
-            break
-        x = fmts[fmt]["x_host"] if K == fmts[fmt]["x_host"].shape[1] else np.ones((1, K), np.float32)
-        t0 = time.perf_counter()
-        oracle.matmul_ref(fmt, raw, x, M, K)
-        total_t += time.perf_counter() - t0
-        total_bytes += raw.size + 4 * K + 4 * M
-        done.append(f"{'Q8_0' if fmt == 8 else 'Q4_0'} {M}x{K}")
+
+    def timed(fn):
+        ts, r = [], None
+        for _ in range(trials):
+            t0 = time.perf_counter()
+            r = fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)), r
+
+    L, S = si.LLAMA3_8B, si.SMOLLM2_135M
+    out = {}
+    # single GEMV
+    raw = si.weights(si.FMT_Q8_0, 576, 576, 0)
+    x = si.activations(1, 576, 1).astype(np.float64)
+    tu, W = timed(lambda: oracle.dequant(si.FMT_Q8_0, raw, 576, 576))
+    tm, _ = timed(lambda: x @ W.T)
+    out["single_q8_0_gemv_576"] = {"unpack_ms": round(tu * 1e3, 3), "matmul_ms": round(tm * 1e3, 4),
+                                   "tok_s": round(1.0 / (tu + tm), 1),
+                                   "GBps": round(raw.size / (tu + tm) / 1e9, 4)}
+    # 8B decode GEMVs (sampled rows)
+    step_bytes, step_t, samp_bytes, samp_t = 0.0, 0.0, 0.0, 0.0
+    per_fmt = {}
+    o_rows = {}
+    for (fmt, seed), (a, M, K) in host.items():
+        rb = oracle.row_bytes(fmt, K)
+        part = a[:rows * rb]
+        xs = si.activations(1, K, 4321).astype(np.float64)
+        tu, W = timed(lambda: oracle.dequant(fmt, part, rows, K))
+        tm, _ = timed(lambda: xs @ W.T)
+        pf = per_fmt.setdefault(si.FMT_NAMES[fmt], {"unpack_s": 0.0, "matmul_s": 0.0, "bytes": 0})
+        pf["unpack_s"] += tu * M / rows
+        pf["matmul_s"] += tm * M / rows
+        pf["bytes"] += M * rb
+        samp_bytes += part.size
+        samp_t += tu + tm
+        step_bytes += M * rb
+        step_t += (tu + tm) * M / rows
+        if M == L["hidden"] and K == L["hidden"]:
+            o_rows[fmt] = (part, W)
+        if M == L["intermediate"] and K == L["hidden"] and "prefill" not in out:
+            out["prefill"] = {"fmt": si.FMT_NAMES[fmt], "rows": rows, "K": K, "cases": []}
+            for T in (128, 2048, 4096):
+                X = si.activations(T, K, 7100 + T, dtype=np.float16).astype(np.float64)
+                tp, _ = timed(lambda: X @ W.T)
+                out["prefill"]["cases"].append({"T": T, "matmul_s": round(tp, 4),
+                                                "TFLOPs": round(2.0 * T * rows * K / tp / 1e12, 5)})
+            out["prefill"]["unpack_s_per_row"] = round(tu / rows, 6)
+    for v in per_fmt.values():
+        v["GBps"] = round(v["bytes"] / (v["unpack_s"] + v["matmul_s"]) / 1e9, 4)
+        v["tok_s"] = round(1.0 / (v["unpack_s"] + v["matmul_s"]), 4)
+        v["unpack_s"], v["matmul_s"] = round(v["unpack_s"], 2), round(v["matmul_s"], 3)
+    out["llama3_8b_decode_step"] = {"per_format": per_fmt, "step_s_extrapolated": round(step_t, 1),
+                                    "GBps": round(step_bytes / step_t / 1e9, 4), "rows_sampled": rows}
+    # small batch, 16 tokens, on the sampled O rows
+    sb = {}
+    X16 = si.activations(16, L["hidden"], 4322).astype(np.float64)
+    for fmt, (part, W) in o_rows.items():
+        tm, _ = timed(lambda: X16 @ W.T)
+        sb[si.FMT_NAMES[fmt]] = {"matmul_ms_16_tokens": round(tm * 1e3, 3), "rows": rows}
+    f16 = si.weights(si.FMT_F16, rows, L["hidden"], 4323)
+    tu, W = timed(lambda: oracle.dequant(si.FMT_F16, f16, rows, L["hidden"]))
+    tm, _ = timed(lambda: X16 @ W.T)
+    sb["F16"] = {"unpack_ms": round(tu * 1e3, 3), "matmul_ms_16_tokens": round(tm * 1e3, 3), "rows": rows}
+    out["small_batch_16"] = sb
+    # SmolLM2-135M step: one layer + 1024 LM-head rows, scaled
+    H, I, V, Q = S["hidden"], S["intermediate"], S["vocab"], si.qkv_rows(S)
+    sm = {}
+    for fmt in (si.FMT_Q8_0, si.FMT_Q4_0):
+        mats = [(si.weights(fmt, m, k, 8000 + i), m, k) for i, (m, k) in
+                enumerate(((Q, H), (H, H), (I, H), (I, H), (H, I), (1024, H)))]
+        lay_t, lm_t = 0.0, 0.0
+        for j, (a, m, k) in enumerate(mats):
+            xs = si.activations(1, k, 77).astype(np.float64)
+            tu, W = timed(lambda: oracle.dequant(fmt, a, m, k))
+            tm, _ = timed(lambda: xs @ W.T)
+            if j < 5:
+                lay_t += tu + tm
+            else:
+                lm_t += (tu + tm) * V / 1024
+        step = S["layers"] * lay_t + lm_t
+        sm[si.FMT_NAMES[fmt]] = {"step_s_extrapolated": round(step, 3), "tok_s": round(1.0 / step, 3)}
+    out["smollm2_135m_decode_step"] = sm
     cores = len(os.sched_getaffinity(0))
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads),
-            "kind": "oracle",
-            "sample": f"{len(done)} of {len(host)} weight matrices of the step, whole matrices "
-                      f"({', '.join(done)}); float64 numpy unpack + matmul; {total_t:.1f} s of CPU work"}
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(samp_bytes / samp_t / 1e9, 5), "unit": "GB/s", "cores": min(cores, threads),
+            "kind": "oracle", "cpu_model": model, "trials": trials,
+            "sample": f"first {rows} rows of each of the 12 weight matrices of the Llama-3-8B decode step "
+                      f"(Q8_0 and Q4_0), float64 numpy unpack + BLAS matmul, median of {trials} runs; "
+                      f"per-workload figures in configs",
+            "configs": out}
 
 
-def smollm2_step(torch, qmm, si, steps):
-    """SmolLM2-135M-shaped decode step (30 layers + LM head), Q8_0 and Q4_0, eager and graph-replayed."""
+def smollm2_step(torch, qmm, si, steps, trials):
+    """SmolLM2-135M-shaped decode step (30 layers + LM head), Q8_0 and Q4_0: one step
+    per weight set, the sets rotated through >= 512 MB (4 sets of Q8_0, 8 of Q4_0) so
+    that each step streams its weights from HBM, eager and as replayed graphs (one per
+    set); and on a single resident set (its 76-143 MB stay in the Infinity Cache
+    between steps, as in a serving loop of this model alone).  tok/s = 1 / step time."""
     S = si.SMOLLM2_135M
     H, I, V, Q = S["hidden"], S["intermediate"], S["vocab"], si.qkv_rows(S)
     dev = torch.device("cuda")
     out = {}
     for fmt, base in ((si.FMT_Q8_0, 8000), (si.FMT_Q4_0, 8500)):
-        Ws = []
+        layers = []
         for layer in range(S["layers"]):
             s0 = base + 10 * layer
-            Ws.append([torch.from_numpy(si.weights(fmt, m, k, s0 + i)).to(dev)
-                       for i, (m, k) in enumerate(((Q, H), (H, H), (I, H), (I, H), (H, I)))])
+            layers.append([torch.from_numpy(si.weights(fmt, m, k, s0 + i)).to(dev)
+                           for i, (m, k) in enumerate(((Q, H), (H, H), (I, H), (I, H), (H, I)))])
         lm = torch.from_numpy(si.weights(fmt, V, H, base + 999)).to(dev)
+        nbytes = sum(w.numel() for ws in layers for w in ws) + lm.numel()
+        sets = [(layers, lm)] + [([[w.clone() for w in ws] for ws in layers], lm.clone())
+                                 for _ in range(max(1, -(-POOL_BYTES // nbytes)) - 1)]
         x = torch.from_numpy(si.activations(1, H, base + 998)).to(dev)
         yq, yo, h, yd, logits = (torch.empty(n, device=dev) for n in (Q, H, I, H, V))
-        nbytes = sum(w.numel() for ws in Ws for w in ws) + lm.numel()
 
-        def step():
-            for (wq, wo, wg, wu, wd) in Ws:
+        def step(ws):
+            lys, head = ws
+            for (wq, wo, wg, wu, wd) in lys:
                 qmm.qmm_gemv(fmt, wq, x, yq, Q, H, 1)
                 qmm.qmm_gemv(fmt, wo, x, yo, H, H, 1)
                 qmm.qmm_gate_up_silu(fmt, wg, wu, x, h, I, H, 1)
                 qmm.qmm_gemv(fmt, wd, h, yd, H, I, 1)
-            qmm.qmm_gemv(fmt, lm, x, logits, V, H, 1)
+            qmm.qmm_gemv(fmt, head, x, logits, V, H, 1)
 
-        for _ in range(3):
-            step()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            step()
-        e1.record()
-        torch.cuda.synchronize()
-        eager_ms = e0.elapsed_time(e1) / steps
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(steps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        graph_ms = e0.elapsed_time(e1) / steps
-        out[si.FMT_NAMES[fmt]] = {"eager_tok_s": round(1e3 / eager_ms, 1), "graph_tok_s": round(1e3 / graph_ms, 1),
-                                  "graph_GBps": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),
-                                  "weight_bytes": int(nbytes)}
+        n = len(sets) * max(1, steps // len(sets))
+        for ws in sets:
+            step(ws)
+
+        def rotated():
+            for i in range(n):
+                step(sets[i % len(sets)])
+
+        def resident():
+            for _ in range(n):
+                step(sets[0])
+        eager_ms, _ = median_trials(torch, rotated, trials, n)
+        eager_res_ms, _ = median_trials(torch, resident, trials, n)
+        graphs = [graph_of(torch, lambda ws=ws: step(ws)) for ws in sets]
+
+        def g_rotated():
+            for i in range(n):
+                graphs[i % len(graphs)].replay()
+
+        def g_resident():
+            for _ in range(n):
+                graphs[0].replay()
+        graph_ms, _ = median_trials(torch, g_rotated, trials, n)
+        graph_res_ms, _ = median_trials(torch, g_resident, trials, n)
+        del graphs, sets
+        torch.cuda.empty_cache()
+        out[si.FMT_NAMES[fmt]] = {
+            "weight_bytes": int(nbytes), "sets_rotated": max(1, -(-POOL_BYTES // nbytes)),
+            "hbm": {"eager_tok_s": round(1e3 / eager_ms, 1), "graph_tok_s": round(1e3 / graph_ms, 1),
+                    "graph_GBps": round(nbytes / (graph_ms * 1e-3) / 1e9, 1)},
+            "cache_resident": {"eager_tok_s": round(1e3 / eager_res_ms, 1),
+                               "graph_tok_s": round(1e3 / graph_res_ms, 1)}}
     return out
 
 
-def small_batch(torch, qmm, si, reps=20):
+def small_batch(torch, qmm, si, trials, reps=20):
     """Decode GEMV at N in {1,2,4,8,16} on the Llama-3-8B shapes, F16 / Q8_0 / Q4_0.
 
     Each (format, shape) rotates through weight copies totalling >= 512 MB, so every
     call streams from HBM rather than the 256 MB Infinity Cache (values are random
-    bytes: timing only; parity is covered by the tests).  Reports weight GB/s of the
+    bytes: timing only; parity is covered by the tests).  `reps` rotated calls are
+    captured as one HIP graph with a preallocated workspace and replayed (the median
+    of the trials), so host launch overhead stays out.  Reports weight GB/s of the
     VALU streaming path, of the MFMA path, and of qmm_gemv's own choice, per N, and
     the smallest N at which the MFMA path is faster (the crossover).
     """
@@ -328,32 +536,42 @@ def small_batch(torch, qmm, si, reps=20):
         res = {v: {n: [0.0, 0.0] for n in Ns} for v in ("valu", "mfma", "auto")}  # bytes, ms
         for sname, M, K in shapes:
             n_mats = 2 if sname == "gate_up" else 1
+            op = qmm.QMM_OP_GATE_UP_SILU if sname == "gate_up" else qmm.QMM_OP_GEMV
             nbytes = n_mats * M * qmm.qmm_row_bytes(fmt, K)
-            copies = max(1, -(-(512 << 20) // nbytes))
+            copies = max(1, -(-POOL_BYTES // nbytes))
             pool = [[torch.randint(0, 256, (M * qmm.qmm_row_bytes(fmt, K),), dtype=torch.uint8, device=dev)
                      for _ in range(n_mats)] for _ in range(copies)]
+            for w in pool:  # random bytes: clear the scales' top exponent bit (no inf / NaN)
+                for m in w:
+                    if fmt != si.FMT_F16:
+                        bb = qmm.qmm_row_bytes(fmt, 32)
+                        m.view(-1, bb)[:, 1] &= 0x3B
+                    else:
+                        m.view(-1, 2)[:, 1] &= 0x3B
+            wsb = max(qmm.qmm_workspace_size(op, fmt, M, K, n, v) for n in Ns for v in (0, 1, 2))
+            ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
             for n in Ns:
                 for v, code in (("valu", 1), ("mfma", 2), ("auto", 0)):
                     def call(i, n=n, code=code):
                         w = pool[i % copies]
                         if sname == "gate_up":
-                            if code == 0:
-                                qmm.qmm_gate_up_silu(fmt, w[0], w[1], x, y, M, K, n)
-                            else:
-                                qmm.qmm_gate_up_silu_variant(fmt, w[0], w[1], x, y, M, K, n, code)
+                            qmm.qmm_gate_up_silu_variant(fmt, w[0], w[1], x, y, M, K, n, code, ws)
                         else:
-                            qmm.qmm_gemv_variant(fmt, w[0], x, y, M, K, n, code)
+                            qmm.qmm_gemv_variant(fmt, w[0], x, y, M, K, n, code, ws)
                     for i in range(3):
                         call(i)
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                    for i in range(reps):
-                        call(i)
-                    e1.record()
-                    torch.cuda.synchronize()
+
+                    def body():
+                        for i in range(reps):
+                            call(i)
+                    g = graph_of(torch, body)
+                    g.replay()
+                    ms, _ = median_trials(torch, g.replay, trials, reps)
+                    del g
                     res[v][n][0] += nbytes
-                    res[v][n][1] += e0.elapsed_time(e1) / reps
-            del pool
+                    res[v][n][1] += ms
+            del pool, ws
+            torch.cuda.empty_cache()
         gbs = {v: {n: round(b / (ms * 1e-3) / 1e9, 1) for n, (b, ms) in d.items()} for v, d in res.items()}
         cross = next((n for n in Ns if gbs["mfma"][n] > gbs["valu"][n]), None)
         out[name] = {"weight_GBps": gbs, "mfma_faster_from_N": cross}
@@ -608,29 +826,23 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # Whole-step timing (no per-launch events inside).
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(args.steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    def k_steps():
+        for _ in range(args.steps):
+            step()
+    # Whole-step timing (no per-launch events inside): the median of the trials, each of
+    # K steps between synchronisations.
+    ms_per_step, trial_ms = median_trials(torch, k_steps, args.trials, args.steps)
     # The same step captured once as a HIP graph and replayed (the launch path of a
     # serving loop); reported beside the eager figure.
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
+    graph = graph_of(torch, step)
     for _ in range(args.warmup):
         graph.replay()
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    graph_ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    def k_replays():
+        for _ in range(args.steps):
+            graph.replay()
+    graph_ms_per_step, _ = median_trials(torch, k_replays, args.trials, args.steps)
     del graph
     # Per-launch timing over the same number of steps, for the roofline of each kernel.
     timer = Timer(torch)
@@ -664,6 +876,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "trials": args.trials,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -675,6 +888,7 @@ def main():
                                "Q8_0 pass + Q4_0 pass, N=1",
                    "formats": ["Q8_0", "Q4_0"], "tokens": 1, "step_bytes": int(step_bytes),
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "trial_ms_per_step": [round(t, 5) for t in trial_ms],
                    "graph_replay": {"ms_per_step": round(graph_ms_per_step, 5),
                                     "GBps": round(step_bytes / (graph_ms_per_step * 1e-3) / 1e9, 2)}},
         "roofline": {"bound": "hbm",
@@ -685,38 +899,13 @@ def main():
                      "avg_launch_us": round(dk["us_mean"], 3), "bytes_per_launch": int(dk["bytes"])},
     }
 
+    line["single_gemv_576"] = config1(torch, qmm, si, args.trials)
     if not args.no_prefill:
-        cases = prefill_cases(torch, qmm, si)
-        for c in cases:
-            for _ in range(3):
-                c["fn"]()
-        torch.cuda.synchronize()
-        reps = max(3, args.steps // 5)
-        tot_f, tot_ms = 0.0, 0.0
-        details = []
-        for c in cases:
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
-            s.record()
-            for _ in range(reps):
-                c["fn"]()
-            e.record()
-            torch.cuda.synchronize()
-            ms = s.elapsed_time(e) / reps
-            tot_f += c["flops"]
-            tot_ms += ms
-            details.append({"fmt": si.FMT_NAMES[c["fmt"]], "M": c["M"], "K": c["K"], "T": c["T"],
-                            "us": round(ms * 1e3, 2), "TFLOPs": round(c["flops"] / (ms * 1e-3) / 1e12, 1)})
-        tflops = tot_f / (tot_ms * 1e-3) / 1e12
-        line["prefill_gemm"] = {"value": round(tflops, 1), "unit": "TFLOP/s", "peak": FP16_MFMA_PEAK_TFLOPS,
-                                "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),
-                                "workload": "Q8_0+Q4_0 x {4096->14336, 14336->4096} x T in {128,2048,4096}, "
-                                            "fp16 X, fp32 Y",
-                                "cases": details}
+        line["prefill_gemm"] = prefill(torch, qmm, si, args.trials)
     if not args.no_smollm:
-        line["smollm2_135m_decode_step"] = smollm2_step(torch, qmm, si, max(10, args.steps))
+        line["smollm2_135m_decode_step"] = smollm2_step(torch, qmm, si, max(10, args.steps), args.trials)
     if not args.no_small_batch:
-        line["small_batch_decode"] = small_batch(torch, qmm, si)
+        line["small_batch_decode"] = small_batch(torch, qmm, si, args.trials)
     if not args.no_next:
         line["fused_decode_step"] = fused_decode(torch, qmm, si, fmts, max(10, args.steps))
         line["expand_then_gemm"] = expand_gemm(torch, qmm, si)
@@ -725,7 +914,7 @@ def main():
     if not (args.no_prefill or args.no_small_batch):
         line["ceilings"] = ceilings(torch)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(host, fmts)
+        line["cpu_baseline"] = cpu_baseline(host, si, args.trials)
     if args.suite:
         with open(args.suite, "w") as fh:
             json.dump({"per_launch": per, "per_kernel": kern}, fh, indent=1)
