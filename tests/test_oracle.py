@@ -731,3 +731,44 @@ def test_mutated_matmul_is_caught(mm):
 
 def test_unmutated_pins_pass():
     assert _pins_pass(Q.dequant, _matmul_with_dequant(Q.dequant))
+
+
+# ------------------------------------------------------------- SwiGLU golden
+SWIGLU_GOLDEN = os.path.join(GOLDEN, "swiglu", "q8_0_pair.txt")
+
+
+def _load_swiglu_golden():
+    fx = {"gate": [], "up": [], "x": {}, "g": {}, "u": {}, "h": {}}
+    for line in open(SWIGLU_GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *rest = line.split()
+        if key in ("gate", "up"):
+            fx[key].append(bytes(int(b, 16) for b in rest))
+        elif key in ("x", "g", "u"):
+            fx[key][int(rest[0])] = Fraction(rest[1])
+        elif key == "h":
+            fx["h"][int(rest[0])] = (float(rest[1]), float(rest[2]))
+    return fx
+
+
+def test_swiglu_golden_pair():
+    """gate_up_silu_ref on hand-computed Q8_0 rows: g and u exactly, and h = a / (1 + e^b)
+    from the fixture, so the SiLU sits on the gate and multiplies the up projection."""
+    fx = _load_swiglu_golden()
+    I, K = len(fx["gate"]), 32
+    rg = np.frombuffer(b"".join(fx["gate"]), np.uint8)
+    ru = np.frombuffer(b"".join(fx["up"]), np.uint8)
+    x = np.zeros((1, K), np.float32)
+    for k, v in fx["x"].items():
+        x[0, k] = float(v)
+    h, g, u, Sg, Su = Q.gate_up_silu_ref(Q.FMT_Q8_0, rg, ru, x, I, K)
+    assert [Fraction(float(v)) for v in g[0]] == [fx["g"][i] for i in range(I)]
+    assert [Fraction(float(v)) for v in u[0]] == [fx["u"][i] for i in range(I)]
+    want = np.array([a / (1.0 + math.exp(b)) for a, b in (fx["h"][i] for i in range(I))])
+    assert np.allclose(h[0], want, rtol=1e-15, atol=0)
+    # The pair tells the readings apart: SiLU on the up projection, or no SiLU.
+    gg, uu = g[0], u[0]
+    assert not np.allclose(Q.silu(uu) * gg, want, rtol=1e-3)
+    assert not np.allclose(gg * uu, want, rtol=1e-3)
