@@ -27,6 +27,8 @@
 //   * Lane l decodes block l (and l + 64) of the slice for every row unit with the
 //     packed fp16 dot products of block_dot; partial sums stay in registers across
 //     a row group's slices and are reduced across the wave once.
+#include <type_traits>
+
 #include "gemv_block.hpp"
 #include "dma.hpp"
 #include "qmm_internal.hpp"
@@ -274,17 +276,37 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
     lds_barrier();
     float scale = 1.0f;
     if constexpr (EP == EP_NORM) scale = norm_scale<NT>(red, WAVES, reduced_token<RU, NT>(lane), K, epi.eps);
-    if (any_wide<WAVES>(wflag)) {
-        // A wide block of x: the exact fp32 path for this workgroup's rows (every
-        // workgroup stages all of x, so all of them take it).  The ring's DMAs land first.
-        wait_vm<0>();
-        gemv_rows_exact<FMT, NT, R, GATED, EP>(Wg, Wu, x, y, M, K, ldx, ldy, epi, scale, wid, nw, my_groups, lane);
-        return;
+    // A wide block of x (every workgroup stages all of x, so all of them see it): x
+    // again, as fp32 in the same LDS (XS_STRIDE floats per block), and the same loop
+    // on fp32 products (block_fma); when fp32 x does not fit, the exact path that reads
+    // everything from global memory.
+    const bool wide_x = any_wide<WAVES>(wflag);
+    if (wide_x) {
+        if (NT * nb * XS_STRIDE * 4 > L::XCAP) {
+            wait_vm<0>();  // the ring's DMAs land before the workgroup can exit
+            gemv_rows_exact<FMT, NT, R, GATED, EP>(Wg, Wu, x, y, M, K, ldx, ldy, epi, scale, wid, nw, my_groups,
+                                                   lane);
+            return;
+        }
+        float* xf = reinterpret_cast<float*>(xs);
+        for (int j = threadIdx.x; j < NT * nb * 8; j += XT) {
+            const int n = j / (nb * 8), r = j - n * (nb * 8);
+            const int64_t k = 4 * static_cast<int64_t>(r);
+            float4 v = *reinterpret_cast<const float4*>(x + n * ldx + k);
+            if constexpr (EP == EP_NORM) {
+                const float4 gm = *reinterpret_cast<const float4*>(epi.gamma + k);
+                v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
+            }
+            *reinterpret_cast<float4*>(xf + n * nb * XS_STRIDE + (r >> 3) * XS_STRIDE + 4 * (r & 7)) = v;
+        }
+        lds_barrier();
     }
 
-    // One task from stage array `stage`, then its refill with the task S ahead.
+    // One task from stage array `stage`, then its refill with the task S ahead; XF_
+    // selects the x form (fp32 for wide x, block floating point otherwise).
     TaskCursor cc{0, 0};
-    auto step = [&](uint8_t* stage) {
+    auto step = [&](uint8_t* stage, auto XF_) __attribute__((always_inline)) {
+        constexpr bool XF = decltype(XF_)::value;
         __builtin_amdgcn_sched_barrier(0);
         wait_vm<(S - 1) * NI>();  // this task's DMA has landed; the next S - 1 stay in flight
         __builtin_amdgcn_sched_barrier(0);
@@ -301,10 +323,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
                     int off[RU];
 #pragma unroll
                     for (int u = 0; u < RU; ++u) off[u] = blk * BB;
-                    const uint32_t* xb[NT];
+                    if constexpr (XF) {
+                        const float* xb[NT];
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) xb[n] = xs + n * xstride + (s0 + blk) * XS16;
-                    block_dot<FMT, RU, NT>(buf, off, xb, acc);
+                        for (int n = 0; n < NT; ++n)
+                            xb[n] = reinterpret_cast<const float*>(xs) + (n * nb + s0 + blk) * XS_STRIDE;
+                        block_fma<FMT, RU, NT>(buf, off, xb, acc);
+                    } else {
+                        const uint32_t* xb[NT];
+#pragma unroll
+                        for (int n = 0; n < NT; ++n) xb[n] = xs + n * xstride + (s0 + blk) * XS16;
+                        block_dot<FMT, RU, NT>(buf, off, xb, acc);
+                    }
                 }
             }
             if (cc.s == ns - 1) {
@@ -327,12 +357,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
         ic.next(ns);
         cc.next(ns);
     };
-    for (int t0 = 0; t0 < ntask; t0 += S) {
-        step(RS0);
-        step(RS1);
-        if constexpr (S > 2) step(RS2);
-        if constexpr (S > 3) step(RS3);
-    }
+    auto run = [&](auto XF_) __attribute__((always_inline)) {
+        for (int t0 = 0; t0 < ntask; t0 += S) {
+            step(RS0, XF_);
+            step(RS1, XF_);
+            if constexpr (S > 2) step(RS2, XF_);
+            if constexpr (S > 3) step(RS3, XF_);
+        }
+    };
+    if (wide_x) run(std::true_type{});
+    else run(std::false_type{});
     // Drain the trailing DMAs (zero-length reads) before the workgroup can exit.
     wait_vm<0>();
 }

@@ -30,6 +30,8 @@
 //     reduced across the wave once, with a transposing butterfly.
 #pragma once
 
+#include <type_traits>
+
 #include "dma.hpp"
 #include "gemv_block.hpp"
 #include "qmm_internal.hpp"
@@ -186,13 +188,35 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
     }
     float scale = 1.0f;
     if constexpr (EP == EP_NORM) scale = norm_scale<NT>(red, WAVES, reduced_token<RU, NT>(lane), K, epi.eps);
-    if (any_wide<WAVES>(wflag)) {
-        // A wide block of x: the exact fp32 path for this workgroup's rows (every
-        // workgroup stages all of x, so all of them take it).
-        gemv_rows_exact<FMT, NT, R, GATED, EP>(Wg, Wu, x, y, M, K, ldx, ldy, epi, scale, wid, nw, my_groups, lane);
-        return;
+    // A wide block of x (every workgroup stages all of x, so all of them see it): x
+    // again, as fp32 in the same LDS (XS_STRIDE floats per block; the host sizes x's
+    // region for it whenever that costs no occupancy), and the same loop on fp32
+    // products (block_fma); when fp32 x does not fit, the exact path that reads
+    // everything from global memory.
+    const bool wide_x = any_wide<WAVES>(wflag);
+    if (wide_x) {
+        if (NT * nb * XS_STRIDE * 4 > xs_bytes) {
+            gemv_rows_exact<FMT, NT, R, GATED, EP>(Wg, Wu, x, y, M, K, ldx, ldy, epi, scale, wid, nw, my_groups,
+                                                   lane);
+            return;
+        }
+        float* xf = reinterpret_cast<float*>(smem);
+        for (int j = threadIdx.x; j < NT * nb * 8; j += WAVES * kWave) {
+            const int n = j / (nb * 8), r = j - n * (nb * 8);
+            const int64_t k = 4 * static_cast<int64_t>(r);
+            float4 v = *reinterpret_cast<const float4*>(x + n * ldx + k);
+            if constexpr (EP == EP_NORM) {
+                const float4 gm = *reinterpret_cast<const float4*>(epi.gamma + k);
+                v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
+            }
+            *reinterpret_cast<float4*>(xf + n * nb * XS_STRIDE + (r >> 3) * XS_STRIDE + 4 * (r & 7)) = v;
+        }
+        lds_barrier();
     }
 
+    // XF_ selects the x form (fp32 for wide x, block floating point otherwise).
+    auto run = [&](auto XF_) __attribute__((always_inline)) {
+    constexpr bool XF = decltype(XF_)::value;
     for (int t0 = 0; t0 < ntask; t0 += D) {
 #pragma unroll
     for (int q = 0; q < D; ++q) {
@@ -230,10 +254,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
                 int off[RU];
 #pragma unroll
                 for (int u = 0; u < RU; ++u) off[u] = sh[u] + blk * BB;
-                const uint32_t* xb[NT];
+                if constexpr (XF) {
+                    const float* xb[NT];
 #pragma unroll
-                for (int n = 0; n < NT; ++n) xb[n] = xs + n * xstride + (s0 + blk) * XS16;
-                block_dot<FMT, RU, NT>(buf, off, xb, acc);
+                    for (int n = 0; n < NT; ++n)
+                        xb[n] = reinterpret_cast<const float*>(smem) + (n * nb + s0 + blk) * XS_STRIDE;
+                    block_fma<FMT, RU, NT>(buf, off, xb, acc);
+                } else {
+                    const uint32_t* xb[NT];
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) xb[n] = xs + n * xstride + (s0 + blk) * XS16;
+                    block_dot<FMT, RU, NT>(buf, off, xb, acc);
+                }
             }
         }
         if (s == ns - 1) {
@@ -245,6 +277,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_stream_kernel(const uint8_t* 
         }
     }
     }
+    };
+    if (wide_x) run(std::true_type{});
+    else run(std::false_type{});
 }
 
 // Raise a kernel's dynamic LDS limit once per (kernel, device) (gemv_stream.hip).
@@ -266,14 +301,22 @@ static int64_t launch_t(const void* W, const void* Wu, const float* x, float* y,
         if (M < 2) return 0;
         M -= 1;  // every chunk of the first M - 1 rows ends at most 15 bytes into the last row
     }
-    const int64_t xs_bytes = ((NT * nb * XS16 * 4) + 15) / 16 * 16;
-    const int64_t lds = xs_bytes + static_cast<int64_t>(WAVES) * RU * G::ROWBUF + WAVES * NT * 4 + WAVES * 4;
+    int64_t xs_bytes = ((NT * nb * XS16 * 4) + 15) / 16 * 16;
+    const int64_t rest = static_cast<int64_t>(WAVES) * RU * G::ROWBUF + WAVES * NT * 4 + WAVES * 4;
+    int64_t lds = xs_bytes + rest;
     constexpr int64_t kMaxLds = 160 * 1024;
     if (lds > kMaxLds) return 0;
     auto kern = gemv_stream_kernel<FMT, NT, R, GATED, WAVES, D, EP>;
     allow_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(kMaxLds));
     const int64_t ngroups = (M + R - 1) / R;
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(16 / WAVES, kMaxLds / lds));
+    // Room for x as fp32 (the kernel's path for wide blocks of x) when it leaves as
+    // many workgroups per CU.
+    const int64_t xs32 = NT * nb * XS_STRIDE * 4;
+    if (xs32 > xs_bytes && (xs32 + rest) * per_cu <= kMaxLds) {
+        xs_bytes = xs32;
+        lds = xs32 + rest;
+    }
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((ngroups + WAVES - 1) / WAVES, 256 * per_cu));
     const int64_t ns = (nb + G::SLICE - 1) / G::SLICE;
     if (((ngroups + grid * WAVES - 1) / (grid * WAVES) + D) * ns >= (int64_t{1} << 31)) return 0;  // int task counts
