@@ -62,6 +62,8 @@ def parse():
                    help="skip the fused-norm/residual step, expand-then-GEMM, row gather and "
                         "Q4_1/Q5_0/Q5_1 sections")
     p.add_argument("--suite", default=None, help="write per-kernel details as JSON to this path")
+    p.add_argument("--min-calls", type=int, default=200,
+                   help="prefill: at least this many calls per trial (profiling runs pass a few)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
     return p.parse_args()
@@ -281,9 +283,9 @@ def rotation_pool(torch, make, nbytes):
     return [make(i) for i in range(copies)]
 
 
-def prefill(torch, qmm, si, trials):
+def prefill(torch, qmm, si, trials, min_calls=200):
     """Prefill GEMM cases, weights rotated through >= 512 MB of copies (one call per
-    copy in turn), >= 200 calls and >= 2 ms per trial; median of the trials."""
+    copy in turn), >= min_calls calls and >= 2 ms per trial; median of the trials."""
     dev = torch.device("cuda")
     details = []
     tot_f, tot_ms = 0.0, 0.0
@@ -307,7 +309,9 @@ def prefill(torch, qmm, si, trials):
                 call(0)
                 e1.record()
                 torch.cuda.synchronize()
-                calls = max(200, int(2.0 / max(e0.elapsed_time(e1), 1e-3)) + 1)
+                calls = min_calls
+                if min_calls >= 200:  # timing runs: also >= 2 ms per trial
+                    calls = max(calls, int(2.0 / max(e0.elapsed_time(e1), 1e-3)) + 1)
 
                 def body():
                     for i in range(calls):
@@ -740,7 +744,8 @@ def ceilings(torch):
 # Sources the dominant decode kernel is built from; its counter-derived traffic is
 # reported only while their combined hash matches the one recorded with the counters.
 DOMINANT_KERNEL = "gemv_dma_kernel<8, 1, 1, false, 8, 3, 0>"
-DOMINANT_SOURCES = ("gemv_dma.hip", "gemv_block.hpp", "dma.hpp", "qmm_common.hpp", "qmm_internal.hpp")
+DOMINANT_SOURCES = ("gemv_dma.hip", "gemv_block.hpp", "block_decode.hpp", "dma.hpp", "qmm_common.hpp",
+                    "qmm_internal.hpp")
 
 
 def _code_only(text):
@@ -901,7 +906,7 @@ def main():
 
     line["single_gemv_576"] = config1(torch, qmm, si, args.trials)
     if not args.no_prefill:
-        line["prefill_gemm"] = prefill(torch, qmm, si, args.trials)
+        line["prefill_gemm"] = prefill(torch, qmm, si, args.trials, args.min_calls)
     if not args.no_smollm:
         line["smollm2_135m_decode_step"] = smollm2_step(torch, qmm, si, max(10, args.steps), args.trials)
     if not args.no_small_batch:
