@@ -11,8 +11,9 @@
   qmm_rmsnorm_gate_up_silu and qmm_gemv_add.
 * Wide blocks: x blocks whose dynamic range exceeds what block floating point in
   fp16 keeps (a 1e20 beside ones, a single 1e15 outlier), which switch the kernels
-  to their exact fp32 path; and x far outside the fp16 range in either direction
-  (1e30, 1e-35, fp32 subnormals), which block scaling alone handles.
+  to fp32 x: re-staged in LDS where it fits, else read from global memory (two
+  tokens at K = 14336); and x far outside the fp16 range in either direction (1e30,
+  1e-35, fp32 subnormals), which block scaling alone handles.
 Checked against the float64 oracle with |y - y_ref| <= 2e-3 sum |w x| + 1e-6
 (the fused outputs with their propagated bounds); outputs start as NaN.
 """
@@ -24,7 +25,8 @@ import block_quantized_weight_gguf_amd as qmm
 import near_offset
 import oracle
 import seeded_inputs as si
-from parity_util import (announce, check_linear, check_residual, check_swiglu, dev, guard_intact, poisoned)
+from parity_util import (announce, check_linear, check_residual, check_swiglu, dev, guard_intact, poisoned,
+                         sample_rows)
 
 pytestmark = pytest.mark.gpu
 ALL_FMTS = [si.FMT_Q8_0, si.FMT_Q4_0, si.FMT_Q4_1, si.FMT_Q5_0, si.FMT_Q5_1]
@@ -193,3 +195,43 @@ def test_x_range_gemv(fmt, scale, M, K):
     announce(f"x range gemv fmt={fmt} scale={scale} M={M} K={K}")
     y_ref, S = oracle.matmul_ref(fmt, raw, x, M, K)
     check_linear(_gemv(fmt, raw, x, M, K, VALU), y_ref, S, f"x range gemv scale={scale}")
+
+
+# Two tokens of wide x at K = 14336, whose fp32 copy takes 2 x 448 blocks x 144 bytes.
+# 4096 rows run on the DMA-fed kernel, where it does not fit beside the weight ring: every
+# workgroup takes the exact path that reads x and the weights from global memory.  1000
+# rows run on the register-staged kernel with 4-wave workgroups, whose small ring leaves
+# room for fp32 x in LDS.  The gated product (register-staged, 8 waves, gate and up rows
+# in every task) does not have that room and takes the global path.
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
+@pytest.mark.parametrize("M", [4096, 1000])
+def test_wide_blocks_k14336(fmt, M):
+    K, N = 14336, 2
+    rows = sample_rows(M, 40, 90 + fmt)
+    raw = near_offset.weights(fmt, M, K)
+    x = _wide_near(N, K)
+    announce(f"wide near-offset gemv fmt={fmt} M={M} K={K} N={N}")
+    y_ref, S = oracle.matmul_ref(fmt, raw, x, M, K, rows=rows)
+    check_linear(_gemv(fmt, raw, x, M, K, VALU)[:, rows], y_ref, S, "wide gemv at K = 14336")
+    raw2 = si.weights(fmt, M, K, 91)
+    x2 = _outlier(N, K, 92)
+    announce(f"one-outlier gemv fmt={fmt} M={M} K={K} N={N}")
+    y_ref, S = oracle.matmul_ref(fmt, raw2, x2, M, K, rows=rows)
+    check_linear(_gemv(fmt, raw2, x2, M, K, VALU)[:, rows], y_ref, S, "one-outlier gemv at K = 14336")
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
+def test_wide_blocks_k14336_gated(fmt):
+    I, K, N = 1536, 14336, 2
+    rows = sample_rows(I, 40, 95 + fmt)
+    rg = near_offset.weights(fmt, I, K)
+    ru = np.roll(rg.reshape(I, -1), 1, axis=0).reshape(-1)
+    x = _wide_tiny(N, K)
+    announce(f"wide gate_up_silu (global exact path) fmt={fmt} I={I} K={K} N={N}")
+    buf = poisoned(N * I)
+    qmm.qmm_gate_up_silu_variant(fmt, dev(rg), dev(ru), dev(x), buf, I, K, N, VALU)
+    torch.cuda.synchronize()
+    assert guard_intact(buf, N * I)
+    h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, x, I, K, rows=rows)
+    check_swiglu(buf[:N * I].cpu().numpy().reshape(N, I)[:, rows], h_ref, g, u, Sg, Su,
+                 "wide gate_up_silu, global exact path")
