@@ -401,6 +401,11 @@ static int64_t dma_launch(const void* W, const void* Wu, const float* x, float* 
 // 12.4 / 12.8 / 10.2 us against 11.3 / 13.1 / 13.5 / 11.2 us, and the 128256-row LM
 // head 52.8 / 63.9 / 66.2 / 50.2 against 58.3 / 68.8 / 70.6 / 57.0 us; at 6144 rows
 // (3 rows per wave against 4) 1-row tasks stay ahead (Q4_1 6.5 against 6.9 us).
+// With the exact-code decode the nibble formats' single-token LM heads (128256 rows,
+// 21 two-row groups per wave) gain from a third wave per SIMD: 12-wave workgroups take
+// Q4_0 / Q4_1 / Q5_0 / Q5_1 58.6 / 63.0 / 75.4 / 82.4 us against 62.7 / 65.9 / 79.2 /
+// 86.4 us with 8 (same process), while at 4096 rows (fewer groups than waves) they
+// lose 10-20%; so 12 waves from 49152 rows.
 // The gated product (gate and up rows in every task) measured faster on the
 // register-staged kernel (Q4_0 15.3 vs 16.9 us, Q8_0 21.8 vs 22.4 us at
 // 14336 x 4096), so it is left to that kernel.
@@ -413,7 +418,11 @@ static int64_t dma_nt(const void* W, const void* Wu, const float* x, float* y, i
         constexpr int64_t kWaves = 256 * 8;
         const int64_t rows1 = (M + kWaves - 1) / kWaves;              // rows per wave, 1-row tasks
         const int64_t rows2 = 2 * ((M + 2 * kWaves - 1) / (2 * kWaves));  // and 2-row tasks
-        if (20 * rows2 <= 21 * rows1) r = dma_launch<FMT, NT, 2, false, 8, 2, EP>(W, Wu, x, y, M, K, epi, s);
+        if (20 * rows2 <= 21 * rows1) {
+            if constexpr (NT == 1)
+                if (M >= 49152) r = dma_launch<FMT, NT, 2, false, 12, 2, EP>(W, Wu, x, y, M, K, epi, s);
+            if (!r) r = dma_launch<FMT, NT, 2, false, 8, 2, EP>(W, Wu, x, y, M, K, epi, s);
+        }
     }
     if (!r) r = dma_launch<FMT, NT, 1, false, 8, 3, EP>(W, Wu, x, y, M, K, epi, s);
     return r;
