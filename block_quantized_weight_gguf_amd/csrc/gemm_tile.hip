@@ -69,9 +69,12 @@ constexpr int GT_GROUP_M = 4;
 
 
 // SPLIT: the workgroup computes the K steps [split * ksteps, (split + 1) * ksteps) of
-// its tile and stores the raw partial sums to Y[split][T][Mo] (Mo = M, or 2 M for the
-// gated instance: gate sums in columns 0..M-1, up sums in M..2M-1); splitk_reduce
-// adds the splits in order and applies the epilogue.
+// its tile and stores its raw accumulators, as the lanes hold them, to the partial
+// block of (split, tile) in Y: per wave, per fragment (i, j), 64 lanes x 16 bytes in
+// lane order, so every store instruction writes 1 KB of contiguous memory (stored in
+// output order, a wave's float4s land in 16 token rows, 64 bytes each: the partials,
+// nsplit times the output, went out several times slower).  splitk_reduce_tiles adds
+// the splits in order, maps the lanes back to outputs and applies the epilogue.
 template <int FMT, bool GATED, bool SPLIT, int BN>
 __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __restrict__ Wg,
                                                                 const uint8_t* __restrict__ Wu,
@@ -410,21 +413,14 @@ __global__ __launch_bounds__(GT_THREADS) void gemm_tile_kernel(const uint8_t* __
         }
     };
     if constexpr (SPLIT) {
-        const int Mo = GATED ? 2 * M : M;
-        float* P = Y + static_cast<int64_t>(split) * T * Mo;
+        // Partial block (split, tile): GT_WAVES x GT_NI x GT_NJ x 64 float4, lane fastest.
+        float4* P = reinterpret_cast<float4*>(Y) +
+                    ((static_cast<int64_t>(split) * ntiles + tile) * GT_WAVES + wave) * (GT_NI * GT_NJ * 64) + lane;
 #pragma unroll
-        for (int i = 0; i < GT_NI; ++i) {
-            const int m = GATED ? m0 + (GT_RW / 2) * wm + 16 * (i % NH) + er : m0 + GT_RW * wm + 16 * i + er;
-            const int col = (GATED && i >= NH ? M : 0) + m;
+        for (int i = 0; i < GT_NI; ++i)
 #pragma unroll
-            for (int j = 0; j < GT_NJ; ++j) {
-                const int t = t0 + GT_TW * wn + 16 * j + ec;
-                if (t < T && m < M) {
-                    const float h[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-                    store4(P + static_cast<int64_t>(t) * Mo + col, m, h);
-                }
-            }
-        }
+            for (int j = 0; j < GT_NJ; ++j)
+                P[(i * GT_NJ + j) * 64] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
     } else {
         constexpr int NOUT = GATED ? NH : GT_NI;  // output fragments per wave
 #pragma unroll
@@ -521,6 +517,91 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P
     }
 }
 
+// Sums the tiled kernel's split-K partial blocks in split order and writes the outputs.
+// Thread e handles float4 element e of a split's partials (the same element of every
+// split's block, read 8 splits at a time), i.e. wave w, fragment (i, j), lane l of tile
+// `tile`: four consecutive weight rows of token t0 + 16 j + l % 16.  Gated: fragment i <
+// GT_NI / 2 holds gate sums and fragment i + GT_NI / 2 the up sums of the same outputs;
+// the thread of the gate element does both.  Token t's sums are scaled by tscale[t]
+// (when given) before the epilogue.  The order of the additions does not depend on the
+// launch.
+template <bool GATED, int BN>
+__global__ __launch_bounds__(256) void splitk_reduce_tiles(const float4* __restrict__ P, float* __restrict__ Y,
+                                                           const float* __restrict__ tscale, int M, int T,
+                                                           int nsplit, int ntiles, int vec) {
+    constexpr int B = 8;
+    constexpr int NJ = BN / 16;
+    constexpr int NI = 2;                       // fragments per wave along the weight rows
+    constexpr int RW = GT_BM / GT_WAVES;        // weight rows per wave
+    constexpr int PER_TILE = GT_WAVES * NI * NJ * 64;
+    constexpr int NOUT = GATED ? NI / 2 : NI;   // output fragments per wave
+    const int rows_per_tile = GATED ? GT_BM / 2 : GT_BM;
+    const int nMt = (M + rows_per_tile - 1) / rows_per_tile;
+    const int64_t plane = static_cast<int64_t>(ntiles) * PER_TILE;
+    const int64_t n = static_cast<int64_t>(ntiles) * GT_WAVES * NOUT * NJ * 64;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
+         e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int lane = static_cast<int>(e & 63);
+        int64_t q = e >> 6;
+        const int j = static_cast<int>(q % NJ);
+        q /= NJ;
+        const int i = static_cast<int>(q % NOUT);
+        q /= NOUT;
+        const int wave = static_cast<int>(q % GT_WAVES);
+        const int tile = static_cast<int>(q / GT_WAVES);
+        // The tiled kernel's tile order: weight-row tiles in groups of GT_GROUP_M.
+        const int group = tile / (GT_GROUP_M * ((T + BN - 1) / BN));
+        const int first_m = group * GT_GROUP_M;
+        const int gm = min(GT_GROUP_M, nMt - first_m);
+        const int in_group = tile - group * GT_GROUP_M * ((T + BN - 1) / BN);
+        const int mt = first_m + in_group % gm;
+        const int t = (in_group / gm) * BN + 16 * j + (lane & 15);
+        const int m = mt * rows_per_tile + (GATED ? RW / 2 : RW) * wave + 16 * i + 4 * (lane >> 4);
+        if (t >= T || m >= M) continue;
+        const int64_t idx = static_cast<int64_t>(tile) * PER_TILE + ((wave * NI + i) * NJ + j) * 64 + lane;
+        const int64_t idu = idx + (NI / 2) * NJ * 64;  // gated: the up fragment i + NI / 2
+        float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+        int s = 0;
+        for (; s + B <= nsplit; s += B) {
+            float4 a[B], c[B];
+#pragma unroll
+            for (int k = 0; k < B; ++k) {
+                a[k] = P[(s + k) * plane + idx];
+                if (GATED) c[k] = P[(s + k) * plane + idu];
+            }
+#pragma unroll
+            for (int k = 0; k < B; ++k) {
+                g.x += a[k].x; g.y += a[k].y; g.z += a[k].z; g.w += a[k].w;
+                if (GATED) { u.x += c[k].x; u.y += c[k].y; u.z += c[k].z; u.w += c[k].w; }
+            }
+        }
+        for (; s < nsplit; ++s) {
+            const float4 a = P[s * plane + idx];
+            g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+            if (GATED) {
+                const float4 c = P[s * plane + idu];
+                u.x += c.x; u.y += c.y; u.z += c.z; u.w += c.w;
+            }
+        }
+        const float sc = tscale != nullptr ? tscale[t] : 1.0f;
+        float h[4] = {g.x * sc, g.y * sc, g.z * sc, g.w * sc};
+        if (GATED) {
+            h[0] = silu(h[0]) * (u.x * sc);
+            h[1] = silu(h[1]) * (u.y * sc);
+            h[2] = silu(h[2]) * (u.z * sc);
+            h[3] = silu(h[3]) * (u.w * sc);
+        }
+        float* yp = Y + static_cast<int64_t>(t) * M + m;
+        if (vec) {
+            *reinterpret_cast<float4*>(yp) = make_float4(h[0], h[1], h[2], h[3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (m + k < M) yp[k] = h[k];
+        }
+    }
+}
+
 template <int FMT, bool GATED, bool SPLIT, int BN>
 static void launch_tile_t(const void* W, const void* Wu, const void* X, const float* tscale, float* Y, int64_t M,
                           int64_t K, int64_t T, int nsplit, int ksteps, hipStream_t s) {
@@ -531,6 +612,21 @@ static void launch_tile_t(const void* W, const void* Wu, const void* X, const fl
                        dim3(GT_THREADS), 0, s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu), X,
                        tscale, Y, static_cast<int>(M), static_cast<int>(K), static_cast<int>(T),
                        static_cast<int>(M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0), nsplit, ksteps);
+}
+
+// Adds the partial blocks the split instance of the tiled kernel left in P (nsplit x
+// ntiles x GT_BM x BN fp32) into Y (T x M fp32).
+template <bool GATED, int BN>
+static void launch_reduce_tiles_t(const float* P, float* Y, const float* tscale, int64_t M, int64_t T, int nsplit,
+                                  hipStream_t s) {
+    const int64_t rows_per_tile = GATED ? GT_BM / 2 : GT_BM;
+    const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + BN - 1) / BN);
+    const int64_t n = ntiles * GT_WAVES * (GATED ? 1 : 2) * (BN / 16) * 64;
+    const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 256 * 16));
+    hipLaunchKernelGGL((splitk_reduce_tiles<GATED, BN>), dim3(grid), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(P), Y, tscale, static_cast<int>(M), static_cast<int>(T),
+                       nsplit, static_cast<int>(ntiles),
+                       static_cast<int>(M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0));
 }
 
 void launch_splitk_reduce(const float* P, float* Y, const float* tscale, int64_t T, int64_t M, int nsplit, bool gated,
@@ -546,8 +642,8 @@ void launch_splitk_reduce(const float* P, float* Y, const float* tscale, int64_t
 // aligned rows, K % 256 == 0; F16 K % 64 == 0; 32-bit lane offsets inside a tile need
 // K <= 2^20), the tile width, and the K split.  K is split when the tiles cannot fill
 // the 256 CUs: at most one wave of workgroups, at least 4 K steps (256) per split,
-// split boundaries on multiples of 4 steps.  The partials take nsplit x T x Mo fp32
-// (Mo = 2 M gated) of the caller's workspace.
+// split boundaries on multiples of 4 steps.  The partials take one GT_BM x BN fp32
+// block per tile and split of the caller's workspace.
 TilePlan plan_gemm_tile(int fmt, int64_t M, int64_t K, int64_t T, bool gated) {
     TilePlan p;
     if (fmt != 1 && K % 256 != 0) return p;
@@ -567,7 +663,9 @@ TilePlan plan_gemm_tile(int fmt, int64_t M, int64_t K, int64_t T, bool gated) {
             p.nsplit = static_cast<int>((nsteps + p.ksteps - 1) / p.ksteps);
         }
     }
-    p.ws_bytes = p.nsplit > 1 ? static_cast<size_t>(p.nsplit) * T * (gated ? 2 * M : M) * sizeof(float) : 0;
+    // Partial blocks: GT_BM x bn accumulators per tile and split (gated tiles: 128 gate
+    // and 128 up rows).  nsplit * ntiles <= 256, so at most 64 MiB.
+    p.ws_bytes = p.nsplit > 1 ? static_cast<size_t>(p.nsplit) * ntiles * GT_BM * bn * sizeof(float) : 0;
     p.ok = true;
     return p;
 }
@@ -590,7 +688,13 @@ void launch_gemm_tile(const TilePlan& p, int fmt, const void* W, const void* Wu,
         else if (fmt == 6) { QMM_TILE_CASE(6, true) }
         else if (fmt == 7) { QMM_TILE_CASE(7, true) }
         else { QMM_TILE_CASE(1, true) }
-        launch_splitk_reduce(ws, Y, tscale, T, M, p.nsplit, gated, s);
+        if (p.narrow) {
+            if (gated) launch_reduce_tiles_t<true, 128>(ws, Y, tscale, M, T, p.nsplit, s);
+            else launch_reduce_tiles_t<false, 128>(ws, Y, tscale, M, T, p.nsplit, s);
+        } else {
+            if (gated) launch_reduce_tiles_t<true, GT_BN>(ws, Y, tscale, M, T, p.nsplit, s);
+            else launch_reduce_tiles_t<false, GT_BN>(ws, Y, tscale, M, T, p.nsplit, s);
+        }
     } else {
         if (fmt == 8) { QMM_TILE_CASE(8, false) }
         else if (fmt == 2) { QMM_TILE_CASE(2, false) }
