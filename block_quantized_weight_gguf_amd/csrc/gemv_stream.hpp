@@ -351,15 +351,21 @@ static int64_t launch_nt(const void* W, const void* Wu, const float* x, float* y
             if (M <= kSmallRows)
                 return deep ? launch_t<FMT, NT, 1, true, 4, 2, EP>(W, Wu, x, y, M, K, epi, s)
                             : launch_t<FMT, NT, 1, true, 4, 1, EP>(W, Wu, x, y, M, K, epi, s);
-            return deep ? launch_t<FMT, NT, 1, true, 8, 2, EP>(W, Wu, x, y, M, K, epi, s)
-                        : launch_t<FMT, NT, 1, true, 8, 1, EP>(W, Wu, x, y, M, K, epi, s);
+            // Two Q5_1 tasks in flight at 3-4 tokens need more than the 256 VGPRs of a
+            // wave in an 8-wave workgroup: one task.
+            if constexpr (FMT == 7 && NT >= 3) return launch_t<FMT, NT, 1, true, 8, 1, EP>(W, Wu, x, y, M, K, epi, s);
+            else
+                return deep ? launch_t<FMT, NT, 1, true, 8, 2, EP>(W, Wu, x, y, M, K, epi, s)
+                            : launch_t<FMT, NT, 1, true, 8, 1, EP>(W, Wu, x, y, M, K, epi, s);
         }
     }
     if (M <= kSmallRows) return launch_t<FMT, NT, 1, false, 4, 2, EP>(W, Wu, x, y, M, K, epi, s);
     if (M <= 2 * kSmallRows) return launch_t<FMT, NT, 1, false, 8, 1, EP>(W, Wu, x, y, M, K, epi, s);
-    // 16 waves per workgroup cap a wave at 128 VGPRs; 3-4 tokens need more.
+    // 16 waves per workgroup cap a wave at 128 VGPRs; 3-4 tokens need more, and so do
+    // 2 tokens on 2-row tasks (with the exact-code decode they spilled at 16 waves).
     constexpr int PW = NT <= 2 ? 16 : 8;
-    if (M >= 16384) return launch_t<FMT, NT, 2, false, PW, 1, EP>(W, Wu, x, y, M, K, epi, s);
+    constexpr int PW2 = NT == 1 ? 16 : 8;
+    if (M >= 16384) return launch_t<FMT, NT, 2, false, PW2, 1, EP>(W, Wu, x, y, M, K, epi, s);
     return launch_t<FMT, NT, 1, false, PW, 1, EP>(W, Wu, x, y, M, K, epi, s);
 }
 
