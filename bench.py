@@ -70,6 +70,12 @@ def parse():
 
 
 POOL_BYTES = 512 << 20          # rotation pool: 2 x the 256 MB Infinity Cache
+# Outputs of the timed calls (copied to the host after timing), re-checked against the
+# float64 oracle on sampled rows by the CPU-baseline leg: the single GEMV (all 576
+# outputs), the decode step (the first rows of every launch) and every prefill case
+# (the first PREFILL_CHECK_ROWS weight rows, all tokens).
+TIMED_OUT = {}
+PREFILL_CHECK_ROWS = 16
 
 
 def median_trials(torch, body, trials, per):
@@ -271,6 +277,7 @@ def config1(torch, qmm, si, trials, calls=400):
     g.replay()
     graph_ms, _ = median_trials(torch, g.replay, trials, calls)
     del g
+    TIMED_OUT["single_gemv_576"] = y.cpu().numpy()
     return {"workload": "Q8_0 GEMV 576x576, N=1, W seed 0, x seed 1 (cache-resident, latency-bound)",
             "us_per_call_eager": round(eager_ms * 1e3, 3), "us_per_call_graph": round(graph_ms * 1e3, 3),
             "tok_s_graph": round(1e3 / graph_ms, 1), "GBps_graph": round(nbytes / (graph_ms * 1e-3) / 1e9, 1),
@@ -317,6 +324,7 @@ def prefill(torch, qmm, si, trials, min_calls=200):
                     for i in range(calls):
                         call(i)
                 ms, _ = median_trials(torch, body, trials, calls)
+                TIMED_OUT[("prefill", fmt, M, K, T)] = Yt[:, :PREFILL_CHECK_ROWS].cpu().numpy()
                 fl = 2.0 * T * M * K
                 tot_f += fl
                 tot_ms += ms
@@ -443,10 +451,62 @@ def cpu_baseline(host, si, trials, rows=512):
         pass
     return {"value": round(samp_bytes / samp_t / 1e9, 5), "unit": "GB/s", "cores": min(cores, threads),
             "kind": "oracle", "cpu_model": model, "trials": trials,
+            "parity_of_timed_outputs": timed_parity(oracle, host, si, rows),
             "sample": f"first {rows} rows of each of the 12 weight matrices of the Llama-3-8B decode step "
                       f"(Q8_0 and Q4_0), float64 numpy unpack + BLAS matmul, median of {trials} runs; "
                       f"per-workload figures in configs",
             "configs": out}
+
+
+def timed_parity(oracle, host, si, rows):
+    """The timed calls' outputs against the float64 oracle, on the same inputs: the
+    single 576 x 576 GEMV whole, the first `rows` rows of every decode launch (down
+    from the GPU's own h, the input it consumed), and the first PREFILL_CHECK_ROWS
+    weight rows of every prefill case over all tokens.  Each output's error is divided
+    by its bound (2e-3 S + 1e-6; the SwiGLU bound for h); every ratio must be <= 1."""
+    L = si.LLAMA3_8B
+    H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
+    worst, n, fails = 0.0, 0, []
+
+    def take(name, got, ref, tol):
+        nonlocal worst, n
+        r = float(np.max(np.abs(np.asarray(got, dtype=np.float64) - ref) / tol))
+        n += int(np.size(ref))
+        worst = max(worst, r)
+        if not r <= 1.0:
+            fails.append(name)
+
+    if "single_gemv_576" in TIMED_OUT:
+        raw = si.weights(si.FMT_Q8_0, 576, 576, 0)
+        y, S = oracle.matmul_ref(si.FMT_Q8_0, raw, si.activations(1, 576, 1), 576, 576)
+        take("single_gemv_576", TIMED_OUT["single_gemv_576"], y[0], oracle.tol_linear(S[0]))
+    sel = np.arange(rows)
+    for fmt, base in ((si.FMT_Q8_0, 5000), (si.FMT_Q4_0, 6000)):
+        out = TIMED_OUT.get(("decode", fmt))
+        if out is None:
+            continue
+        name = si.FMT_NAMES[fmt]
+        x = si.activations(1, H, base + 7)
+        for part, off, M, K, key, xin in (("qkv", 1, Q, H, "y_qkv", x), ("o", 2, H, H, "y_o", x),
+                                          ("down", 5, H, I, "y_d", out["h"]), ("lm_head", 6, V, H, "logits", x)):
+            y, S = oracle.matmul_ref(fmt, host[(fmt, base + off)][0], xin, M, K, rows=sel)
+            take(f"{name} {part}", out[key][sel], y[0], oracle.tol_linear(S[0]))
+        h, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, host[(fmt, base + 3)][0], host[(fmt, base + 4)][0], x, I, H,
+                                                  rows=sel)
+        take(f"{name} gate_up", out["h"][sel], h[0], oracle.tol_swiglu(g[0], u[0], Sg[0], Su[0]))
+    for key, Y in TIMED_OUT.items():
+        if not (isinstance(key, tuple) and key[0] == "prefill"):
+            continue
+        _, fmt, M, K, T = key
+        raw = si.weights(fmt, M, K, 7000 + M % 101 + fmt)
+        X = si.activations(T, K, 7100 + T, dtype=np.float16)
+        y, S = oracle.matmul_ref(fmt, raw, X, M, K, rows=np.arange(PREFILL_CHECK_ROWS))
+        take(f"prefill {si.FMT_NAMES[fmt]} {M}x{K} T={T}", Y, y, oracle.tol_linear(S))
+    if fails:
+        print(f"bench: timed outputs outside the oracle bound: {', '.join(fails)}", file=sys.stderr, flush=True)
+    return {"outputs_checked": n, "max_err_over_bound": round(worst, 4), "ok": not fails,
+            "what": f"single 576x576 GEMV whole; first {rows} rows of each decode launch; first "
+                    f"{PREFILL_CHECK_ROWS} rows x all tokens of each prefill case"}
 
 
 def smollm2_step(torch, qmm, si, steps, trials):
@@ -854,6 +914,8 @@ def main():
     for _ in range(args.steps):
         step(timer)
     torch.cuda.synchronize()
+    for fmt, f in fmts.items():
+        TIMED_OUT[("decode", fmt)] = {k: f[k].cpu().numpy() for k in ("y_qkv", "y_o", "h", "y_d", "logits")}
 
     per = {}
     for key, part, b, _ in launches:

@@ -58,3 +58,28 @@ def test_traffic_reported_only_for_the_sources_measured():
 @pytest.mark.parametrize("files", [["gemv_dma.hip"], ["gemv_dma.hip", "dma.hpp"]])
 def test_digest_depends_on_the_file_list(files):
     assert bench.sources_digest(files) != bench.sources_digest()
+
+
+def test_timed_parity_passes_oracle_outputs_and_flags_a_wrong_one():
+    """The re-check of timed outputs in the CPU-baseline leg: outputs equal to the
+    oracle's pass; one output moved by twice its bound fails (no GPU: the "timed"
+    outputs here are the oracle's own, for a single GEMV and a small prefill case)."""
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+    bench.TIMED_OUT.clear()
+    raw = si.weights(si.FMT_Q8_0, 576, 576, 0)
+    y, S = oracle.matmul_ref(si.FMT_Q8_0, raw, si.activations(1, 576, 1), 576, 576)
+    bench.TIMED_OUT["single_gemv_576"] = y[0].astype(np.float32)
+    M, K, T, fmt = 256, 256, 8, si.FMT_Q4_0
+    Y, S2 = oracle.matmul_ref(fmt, si.weights(fmt, M, K, 7000 + M % 101 + fmt),
+                              si.activations(T, K, 7100 + T, dtype=np.float16), M, K,
+                              rows=np.arange(bench.PREFILL_CHECK_ROWS))
+    bench.TIMED_OUT[("prefill", fmt, M, K, T)] = Y
+    r = bench.timed_parity(oracle, {}, si, 512)
+    assert r["ok"] and r["outputs_checked"] == 576 + T * bench.PREFILL_CHECK_ROWS
+    assert r["max_err_over_bound"] < 0.01
+    Y[3, 5] += 2.0 * float(oracle.tol_linear(S2)[3, 5])
+    r = bench.timed_parity(oracle, {}, si, 512)
+    assert not r["ok"] and r["max_err_over_bound"] > 1.5
+    bench.TIMED_OUT.clear()
