@@ -98,7 +98,8 @@ def test_dma_gate_up_silu(fmt, I, K, N):
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
-@pytest.mark.parametrize("M,K,N", [(2305, 768, 1), (4100, 4352, 2), (20000, 2304, 1), (2561, 14336, 1)])
+@pytest.mark.parametrize("M,K,N", [(2305, 768, 1), (4100, 4352, 2), (20000, 2304, 1), (2561, 14336, 1),
+                                   (50000, 512, 1)])  # nibble formats: 12-wave workgroups
 def test_dma_rmsnorm_gemv(fmt, M, K, N):
     seed = 5200 + M + K + N
     raw = si.weights(fmt, M, K, seed)
@@ -112,10 +113,12 @@ def test_dma_rmsnorm_gemv(fmt, M, K, N):
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
-@pytest.mark.parametrize("M,K,N", [(2305, 768, 1), (4100, 4352, 1), (8192, 2304, 2), (20000, 2304, 1)])
+@pytest.mark.parametrize("M,K,N", [(2305, 768, 1), (4100, 4352, 1), (8192, 2304, 2), (20000, 2304, 1),
+                                   (50001, 256, 1)])
 @pytest.mark.parametrize("inplace", [False, True], ids=["out", "inplace"])
 def test_dma_gemv_add(fmt, M, K, N, inplace):
-    """8192 rows: two row groups per wave (read ahead); 20000: five (another kernel)."""
+    """8192 rows: two row groups per wave (read ahead); 20000: five (another kernel);
+    50001 at one token: the nibble formats' 12-wave workgroups, a lone last row."""
     seed = 5300 + M + K + N
     raw = si.weights(fmt, M, K, seed)
     x = si.activations(N, K, seed + 1)
