@@ -99,7 +99,7 @@ def test_dma_gate_up_silu(fmt, I, K, N):
 
 @pytest.mark.parametrize("fmt", ALL_FMTS, ids=FID.get)
 @pytest.mark.parametrize("M,K,N", [(2305, 768, 1), (4100, 4352, 2), (20000, 2304, 1), (2561, 14336, 1),
-                                   (50000, 512, 1)])  # nibble formats: 12-wave workgroups
+                                   (50000, 512, 1)])  # one token: nibble formats on 12-wave workgroups
 def test_dma_rmsnorm_gemv(fmt, M, K, N):
     seed = 5200 + M + K + N
     raw = si.weights(fmt, M, K, seed)
@@ -117,8 +117,9 @@ def test_dma_rmsnorm_gemv(fmt, M, K, N):
                                    (50001, 256, 1)])
 @pytest.mark.parametrize("inplace", [False, True], ids=["out", "inplace"])
 def test_dma_gemv_add(fmt, M, K, N, inplace):
-    """8192 rows: two row groups per wave (read ahead); 20000: five (another kernel);
-    50001 at one token: the nibble formats' 12-wave workgroups, a lone last row."""
+    """8192 rows: two row groups per wave (read ahead); 20000 and 50001: more row
+    groups per wave than the DMA kernel reads residuals for ahead of its loop (the
+    register-staged kernel takes them; 50001: a lone last row)."""
     seed = 5300 + M + K + N
     raw = si.weights(fmt, M, K, seed)
     x = si.activations(N, K, seed + 1)
