@@ -76,6 +76,7 @@ POOL_BYTES = 512 << 20          # rotation pool: 2 x the 256 MB Infinity Cache
 # (the first PREFILL_CHECK_ROWS weight rows, all tokens).
 TIMED_OUT = {}
 PREFILL_CHECK_ROWS = 16
+SB_CHECK_ROWS = 64
 
 
 def median_trials(torch, body, trials, per):
@@ -460,10 +461,12 @@ def cpu_baseline(host, si, trials, rows=512):
 
 def timed_parity(oracle, host, si, rows):
     """The timed calls' outputs against the float64 oracle, on the same inputs: the
-    single 576 x 576 GEMV whole, the first `rows` rows of every decode launch (down
-    from the GPU's own h, the input it consumed), and the first PREFILL_CHECK_ROWS
-    weight rows of every prefill case over all tokens.  Each output's error is divided
-    by its bound (2e-3 S + 1e-6; the SwiGLU bound for h); every ratio must be <= 1."""
+    single 576 x 576 GEMV whole, the first `rows` rows of every 8B decode launch (down
+    from the GPU's own h, the input it consumed), the SmolLM2-135M step's last layer
+    and LM head, the first SB_CHECK_ROWS rows of every small-batch call (its random
+    weights and x copied back from the device), and the first PREFILL_CHECK_ROWS weight
+    rows of every prefill case over all tokens.  Each output's error is divided by its
+    bound (2e-3 S + 1e-6; the SwiGLU bound for h); every ratio must be <= 1."""
     L = si.LLAMA3_8B
     H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
     worst, n, fails = 0.0, 0, []
@@ -494,6 +497,39 @@ def timed_parity(oracle, host, si, rows):
         h, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, host[(fmt, base + 3)][0], host[(fmt, base + 4)][0], x, I, H,
                                                   rows=sel)
         take(f"{name} gate_up", out["h"][sel], h[0], oracle.tol_swiglu(g[0], u[0], Sg[0], Su[0]))
+    Sm = si.SMOLLM2_135M
+    sH, sI, sV, sQ = Sm["hidden"], Sm["intermediate"], Sm["vocab"], si.qkv_rows(Sm)
+    for fmt in (si.FMT_Q8_0, si.FMT_Q4_0):
+        out = TIMED_OUT.get(("smollm2", fmt))
+        if out is None:
+            continue
+        name, base = si.FMT_NAMES[fmt], out["base"]
+        s0 = base + 10 * (Sm["layers"] - 1)
+        x = si.activations(1, sH, base + 998)
+        for part, i, M, K, key, xin in (("qkv", 0, sQ, sH, "y_qkv", x), ("o", 1, sH, sH, "y_o", x),
+                                        ("down", 4, sH, sI, "y_d", out["h"])):
+            y, S = oracle.matmul_ref(fmt, si.weights(fmt, M, K, s0 + i), xin, M, K)
+            take(f"smollm2 {name} {part}", out[key], y[0], oracle.tol_linear(S[0]))
+        h, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, si.weights(fmt, sI, sH, s0 + 2), si.weights(fmt, sI, sH, s0 + 3),
+                                                  x, sI, sH)
+        take(f"smollm2 {name} gate_up", out["h"], h[0], oracle.tol_swiglu(g[0], u[0], Sg[0], Su[0]))
+        y, S = oracle.matmul_ref(fmt, si.weights(fmt, sV, sH, base + 999), x, sV, sH, rows=sel)
+        take(f"smollm2 {name} lm_head", out["logits"][sel], y[0], oracle.tol_linear(S[0]))
+    for key, rec in TIMED_OUT.items():
+        if not (isinstance(key, tuple) and key[0] == "small_batch"):
+            continue
+        _, fmt, sname = key
+        M, K = rec["M"], rec["K"]
+        sub = np.arange(SB_CHECK_ROWS)
+        for (nt, v), got in rec["y"].items():
+            xs = rec["x"][:nt * K].reshape(nt, K)
+            if sname == "gate_up":
+                h, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rec["w"][0], rec["w"][1], xs, SB_CHECK_ROWS, K)
+                take(f"small batch {si.FMT_NAMES[fmt]} {sname} N={nt} {v}", got, h,
+                     oracle.tol_swiglu(g, u, Sg, Su))
+            else:
+                y, S = oracle.matmul_ref(fmt, rec["w"][0], xs, SB_CHECK_ROWS, K, rows=sub)
+                take(f"small batch {si.FMT_NAMES[fmt]} {sname} N={nt} {v}", got, y, oracle.tol_linear(S))
     for key, Y in TIMED_OUT.items():
         if not (isinstance(key, tuple) and key[0] == "prefill"):
             continue
@@ -505,8 +541,10 @@ def timed_parity(oracle, host, si, rows):
     if fails:
         print(f"bench: timed outputs outside the oracle bound: {', '.join(fails)}", file=sys.stderr, flush=True)
     return {"outputs_checked": n, "max_err_over_bound": round(worst, 4), "ok": not fails,
-            "what": f"single 576x576 GEMV whole; first {rows} rows of each decode launch; first "
-                    f"{PREFILL_CHECK_ROWS} rows x all tokens of each prefill case"}
+            "what": f"single 576x576 GEMV whole; first {rows} rows of each 8B decode launch; the SmolLM2-135M "
+                    f"step's last layer whole and its LM head's first {rows} rows; the first {SB_CHECK_ROWS} rows "
+                    f"of every small-batch call (format, shape, N, variant); first {PREFILL_CHECK_ROWS} rows x all "
+                    f"tokens of each prefill case"}
 
 
 def smollm2_step(torch, qmm, si, steps, trials):
@@ -565,6 +603,9 @@ def smollm2_step(torch, qmm, si, steps, trials):
                 graphs[0].replay()
         graph_ms, _ = median_trials(torch, g_rotated, trials, n)
         graph_res_ms, _ = median_trials(torch, g_resident, trials, n)
+        # The last replays ran set 0: its last layer's outputs and the head's logits.
+        TIMED_OUT[("smollm2", fmt)] = {"base": base, "y_qkv": yq.cpu().numpy(), "y_o": yo.cpu().numpy(),
+                                       "h": h.cpu().numpy(), "y_d": yd.cpu().numpy(), "logits": logits.cpu().numpy()}
         del graphs, sets
         torch.cuda.empty_cache()
         out[si.FMT_NAMES[fmt]] = {
@@ -580,8 +621,9 @@ def small_batch(torch, qmm, si, trials, reps=20):
     """Decode GEMV at N in {1,2,4,8,16} on the Llama-3-8B shapes, F16 / Q8_0 / Q4_0.
 
     Each (format, shape) rotates through weight copies totalling >= 512 MB, so every
-    call streams from HBM rather than the 256 MB Infinity Cache (values are random
-    bytes: timing only; parity is covered by the tests).  `reps` rotated calls are
+    call streams from HBM rather than the 256 MB Infinity Cache (the weights are random
+    bytes with finite scales; the first rows of the last call's weights, x and the
+    outputs are copied back for the oracle leg's re-check).  `reps` rotated calls are
     captured as one HIP graph with a preallocated workspace and replayed (the median
     of the trials), so host launch overhead stays out.  Reports weight GB/s of the
     VALU streaming path, of the MFMA path, and of qmm_gemv's own choice, per N, and
@@ -612,6 +654,11 @@ def small_batch(torch, qmm, si, trials, reps=20):
                         m.view(-1, bb)[:, 1] &= 0x3B
                     else:
                         m.view(-1, 2)[:, 1] &= 0x3B
+            last = pool[(reps - 1) % copies]  # the weights of the last call of every replay
+            sb_key = ("small_batch", fmt, sname)
+            TIMED_OUT[sb_key] = {"M": M, "K": K, "x": x[:16 * K].cpu().numpy(),
+                                 "w": [m[:SB_CHECK_ROWS * qmm.qmm_row_bytes(fmt, K)].cpu().numpy() for m in last],
+                                 "y": {}}
             wsb = max(qmm.qmm_workspace_size(op, fmt, M, K, n, v) for n in Ns for v in (0, 1, 2))
             ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
             for n in Ns:
@@ -632,6 +679,7 @@ def small_batch(torch, qmm, si, trials, reps=20):
                     g.replay()
                     ms, _ = median_trials(torch, g.replay, trials, reps)
                     del g
+                    TIMED_OUT[sb_key]["y"][(n, v)] = y[:n * M].view(n, M)[:, :SB_CHECK_ROWS].cpu().numpy()
                     res[v][n][0] += nbytes
                     res[v][n][1] += ms
             del pool, ws

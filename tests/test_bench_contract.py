@@ -83,3 +83,44 @@ def test_timed_parity_passes_oracle_outputs_and_flags_a_wrong_one():
     r = bench.timed_parity(oracle, {}, si, 512)
     assert not r["ok"] and r["max_err_over_bound"] > 1.5
     bench.TIMED_OUT.clear()
+
+
+def test_timed_parity_covers_smollm2_and_small_batch_records():
+    """The SmolLM2-135M and small-batch records of the re-check, filled here with the
+    oracle's own outputs for the same inputs (no GPU), pass; a wrong small-batch output
+    fails."""
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+    bench.TIMED_OUT.clear()
+    S = si.SMOLLM2_135M
+    H, I, V, Q = S["hidden"], S["intermediate"], S["vocab"], si.qkv_rows(S)
+    fmt, base = si.FMT_Q4_0, 8500
+    s0 = base + 10 * (S["layers"] - 1)
+    x = si.activations(1, H, base + 998)
+    rec = {"base": base}
+    for key, i, M, K in (("y_qkv", 0, Q, H), ("y_o", 1, H, H)):
+        rec[key] = oracle.matmul_ref(fmt, si.weights(fmt, M, K, s0 + i), x, M, K)[0][0].astype(np.float32)
+    rec["h"] = oracle.gate_up_silu_ref(fmt, si.weights(fmt, I, H, s0 + 2), si.weights(fmt, I, H, s0 + 3), x, I,
+                                       H)[0][0].astype(np.float32)
+    rec["y_d"] = oracle.matmul_ref(fmt, si.weights(fmt, H, I, s0 + 4), rec["h"], H, I)[0][0].astype(np.float32)
+    logits = np.zeros(V, dtype=np.float32)
+    logits[:64] = oracle.matmul_ref(fmt, si.weights(fmt, V, H, base + 999), x, V, H, rows=np.arange(64))[0][0]
+    rec["logits"] = logits
+    bench.TIMED_OUT[("smollm2", fmt)] = rec
+    rng = np.random.default_rng(5)
+    K, nt, R = 256, 2, bench.SB_CHECK_ROWS
+    xs = rng.standard_normal(16 * K).astype(np.float32)
+    w = [si.weights(si.FMT_Q8_0, R, K, 11), si.weights(si.FMT_Q8_0, R, K, 12)]
+    y = oracle.matmul_ref(si.FMT_Q8_0, w[0], xs[:nt * K].reshape(nt, K), R, K)[0].astype(np.float32)
+    h = oracle.gate_up_silu_ref(si.FMT_Q8_0, w[0], w[1], xs[:nt * K].reshape(nt, K), R, K)[0].astype(np.float32)
+    bench.TIMED_OUT[("small_batch", si.FMT_Q8_0, "o")] = {"M": 4096, "K": K, "x": xs, "w": w[:1],
+                                                           "y": {(nt, "valu"): y}}
+    bench.TIMED_OUT[("small_batch", si.FMT_Q8_0, "gate_up")] = {"M": 14336, "K": K, "x": xs, "w": w,
+                                                                 "y": {(nt, "mfma"): h}}
+    r = bench.timed_parity(oracle, {}, si, 64)
+    assert r["ok"], r
+    assert r["outputs_checked"] == Q + H + I + H + 64 + 2 * nt * R
+    y[1, 7] += 1.0
+    assert not bench.timed_parity(oracle, {}, si, 64)["ok"]
+    bench.TIMED_OUT.clear()
