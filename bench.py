@@ -77,6 +77,8 @@ POOL_BYTES = 512 << 20          # rotation pool: 2 x the 256 MB Infinity Cache
 TIMED_OUT = {}
 PREFILL_CHECK_ROWS = 16
 SB_CHECK_ROWS = 64
+DECODE_CHECK_ROWS = 512
+TOKEN_CHECK = 64  # tokens of the expansion sections' GEMM outputs re-checked
 
 
 def median_trials(torch, body, trials, per):
@@ -157,6 +159,18 @@ def decode_tensors(torch, si, fmt, base, W, X):
         logits=torch.empty(V, device=dev))
 
 
+def capture_decode(qmm, si, fmt, f, rows=DECODE_CHECK_ROWS):
+    """Host copies for the oracle leg's re-check of a decode step: the outputs, x, and
+    the first `rows` rows of every weight matrix (raw blocks, copied back from HBM)."""
+    L = si.LLAMA3_8B
+    H, I = L["hidden"], L["intermediate"]
+    rec = {k: f[k].cpu().numpy() for k in ("y_qkv", "y_o", "h", "y_d", "logits")}
+    rec["x"] = f["x"].cpu().numpy()
+    rec["w"] = {k: f[k][:rows * qmm.qmm_row_bytes(fmt, I if k == "d" else H)].cpu().numpy()
+                for k in ("qkv", "o", "g", "u", "d", "lm")}
+    return rec
+
+
 def decode_launches(qmm, si, fmt, f):
     """(kernel key, part, algorithmic bytes, callable) for each launch of the step."""
     L = si.LLAMA3_8B
@@ -219,6 +233,7 @@ def more_formats(torch, qmm, si, steps, reps=10):
         for _, part, b, _ in launches:
             us = 1e3 * float(np.mean(timer.ms(part)))
             per[part] = {"us": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1), "bytes": int(b)}
+        TIMED_OUT[("decode", fmt)] = capture_decode(qmm, si, fmt, f)
         res = {"step_us": round(ms * 1e3, 2), "step_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
                "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                "step_bytes": int(nbytes), "launches": per}
@@ -248,6 +263,7 @@ def more_formats(torch, qmm, si, steps, reps=10):
             ms_x = timed(lambda: (qmm.qmm_expand_f16(fmt, f["g"], W16, M, K), qmm.qmm_gemm(1, W16, Xh, Y, M, K, T)))
             pf["T"].append({"T": T, "fused_TFLOPs": round(fl / (ms_f * 1e-3) / 1e12, 1),
                             "expand_then_gemm_TFLOPs": round(fl / (ms_x * 1e-3) / 1e12, 1)})
+            capture_expand(("expand", fmt, M, K, T), fmt, f["g"], W16, Xh, Y, rb)
             del Xh, Y
         res["prefill"] = pf
         out[si.FMT_NAMES[fmt]] = res
@@ -452,21 +468,26 @@ def cpu_baseline(host, si, trials, rows=512):
         pass
     return {"value": round(samp_bytes / samp_t / 1e9, 5), "unit": "GB/s", "cores": min(cores, threads),
             "kind": "oracle", "cpu_model": model, "trials": trials,
-            "parity_of_timed_outputs": timed_parity(oracle, host, si, rows),
+            "parity_of_timed_outputs": timed_parity(oracle, si),
             "sample": f"first {rows} rows of each of the 12 weight matrices of the Llama-3-8B decode step "
                       f"(Q8_0 and Q4_0), float64 numpy unpack + BLAS matmul, median of {trials} runs; "
                       f"per-workload figures in configs",
             "configs": out}
 
 
-def timed_parity(oracle, host, si, rows):
-    """The timed calls' outputs against the float64 oracle, on the same inputs: the
-    single 576 x 576 GEMV whole, the first `rows` rows of every 8B decode launch (down
-    from the GPU's own h, the input it consumed), the SmolLM2-135M step's last layer
-    and LM head, the first SB_CHECK_ROWS rows of every small-batch call (its random
-    weights and x copied back from the device), and the first PREFILL_CHECK_ROWS weight
-    rows of every prefill case over all tokens.  Each output's error is divided by its
-    bound (2e-3 S + 1e-6; the SwiGLU bound for h); every ratio must be <= 1."""
+def timed_parity(oracle, si):
+    """The timed calls' outputs against the float64 oracle, on the same inputs (the
+    weights' first rows and x copied back from the device where the section drew them
+    at random): the single 576 x 576 GEMV whole; the first DECODE_CHECK_ROWS rows of
+    every 8B decode launch in every block format (down from the GPU's own h, the input
+    it consumed), and of the fused step (norm prologues; the two residual adds of one
+    call, from the residual before it); the SmolLM2-135M step's last layer and LM head;
+    the first SB_CHECK_ROWS rows of every small-batch call; the first PREFILL_CHECK_ROWS
+    weight rows of every prefill case over all tokens and, for the expand-then-GEMM
+    cases, over the first TOKEN_CHECK tokens, with the fp16 expansion compared bit for
+    bit; and the first 16 gathered rows of every row gather, bit for bit (NaN where the
+    random scale bytes make one).  Each output's error is divided by its bound (2e-3 S
+    + 1e-6; the SwiGLU and residual bounds where they apply): every ratio must be <= 1."""
     L = si.LLAMA3_8B
     H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
     worst, n, fails = 0.0, 0, []
@@ -479,26 +500,45 @@ def timed_parity(oracle, host, si, rows):
         if not r <= 1.0:
             fails.append(name)
 
+    def exact(name, got, ref):
+        nonlocal n
+        n += int(np.size(ref))
+        if not np.array_equal(np.asarray(got), np.asarray(ref), equal_nan=True):
+            fails.append(name)
+
     if "single_gemv_576" in TIMED_OUT:
         raw = si.weights(si.FMT_Q8_0, 576, 576, 0)
         y, S = oracle.matmul_ref(si.FMT_Q8_0, raw, si.activations(1, 576, 1), 576, 576)
         take("single_gemv_576", TIMED_OUT["single_gemv_576"], y[0], oracle.tol_linear(S[0]))
-    sel = np.arange(rows)
-    for fmt, base in ((si.FMT_Q8_0, 5000), (si.FMT_Q4_0, 6000)):
-        out = TIMED_OUT.get(("decode", fmt))
-        if out is None:
+    R = DECODE_CHECK_ROWS
+    for key, rec in TIMED_OUT.items():
+        if not (isinstance(key, tuple) and key[0] in ("decode", "fused")):
             continue
-        name = si.FMT_NAMES[fmt]
-        x = si.activations(1, H, base + 7)
-        for part, off, M, K, key, xin in (("qkv", 1, Q, H, "y_qkv", x), ("o", 2, H, H, "y_o", x),
-                                          ("down", 5, H, I, "y_d", out["h"]), ("lm_head", 6, V, H, "logits", x)):
-            y, S = oracle.matmul_ref(fmt, host[(fmt, base + off)][0], xin, M, K, rows=sel)
-            take(f"{name} {part}", out[key][sel], y[0], oracle.tol_linear(S[0]))
-        h, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, host[(fmt, base + 3)][0], host[(fmt, base + 4)][0], x, I, H,
-                                                  rows=sel)
-        take(f"{name} gate_up", out["h"][sel], h[0], oracle.tol_swiglu(g[0], u[0], Sg[0], Su[0]))
+        kind, fmt = key
+        name = f"{kind} {si.FMT_NAMES[fmt]}"
+        w, x = rec["w"], rec["x"]
+        if kind == "decode":
+            for part, M, K, wk, yk, xin in (("qkv", Q, H, "qkv", "y_qkv", x), ("o", H, H, "o", "y_o", x),
+                                            ("down", H, I, "d", "y_d", rec["h"]), ("lm_head", V, H, "lm", "logits", x)):
+                y, S = oracle.matmul_ref(fmt, w[wk], xin, R, K)
+                take(f"{name} {part}", rec[yk][:R], y[0], oracle.tol_linear(S[0]))
+            h, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, w["g"], w["u"], x, R, H)
+            take(f"{name} gate_up", rec["h"][:R], h[0], oracle.tol_swiglu(g[0], u[0], Sg[0], Su[0]))
+        else:
+            gm, eps = rec["gamma"], rec["eps"]
+            for part, M, wk, yk in (("norm qkv", Q, "qkv", "y_qkv"), ("norm lm_head", V, "lm", "logits")):
+                y, S = oracle.rmsnorm_matmul_ref(fmt, w[wk], x, gm, eps, R, H)
+                take(f"{name} {part}", rec[yk][:R], y[0], oracle.tol_linear(S[0]))
+            h, g, u, Sg, Su = oracle.rmsnorm_gate_up_silu_ref(fmt, w["g"], w["u"], x, gm, eps, R, H)
+            take(f"{name} norm gate_up", rec["h"][:R], h[0], oracle.tol_swiglu(g[0], u[0], Sg[0], Su[0]))
+            # r2 = (r0 + O x) + D h: both adds, each within its residual bound.
+            r1, S1 = oracle.matmul_add_ref(fmt, w["o"], x, np.reshape(rec["r0"], -1)[:R], R, H)
+            r2, S2 = oracle.matmul_add_ref(fmt, w["d"], rec["h"], r1[0], R, I)
+            take(f"{name} O + down residual", np.reshape(rec["r2"], -1)[:R], r2[0],
+                 oracle.tol_residual(S1[0], r1[0]) + oracle.tol_residual(S2[0], r2[0]))
     Sm = si.SMOLLM2_135M
     sH, sI, sV, sQ = Sm["hidden"], Sm["intermediate"], Sm["vocab"], si.qkv_rows(Sm)
+    sel = np.arange(R)
     for fmt in (si.FMT_Q8_0, si.FMT_Q4_0):
         out = TIMED_OUT.get(("smollm2", fmt))
         if out is None:
@@ -516,35 +556,46 @@ def timed_parity(oracle, host, si, rows):
         y, S = oracle.matmul_ref(fmt, si.weights(fmt, sV, sH, base + 999), x, sV, sH, rows=sel)
         take(f"smollm2 {name} lm_head", out["logits"][sel], y[0], oracle.tol_linear(S[0]))
     for key, rec in TIMED_OUT.items():
-        if not (isinstance(key, tuple) and key[0] == "small_batch"):
+        if not isinstance(key, tuple):
             continue
-        _, fmt, sname = key
-        M, K = rec["M"], rec["K"]
-        sub = np.arange(SB_CHECK_ROWS)
-        for (nt, v), got in rec["y"].items():
-            xs = rec["x"][:nt * K].reshape(nt, K)
-            if sname == "gate_up":
-                h, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rec["w"][0], rec["w"][1], xs, SB_CHECK_ROWS, K)
-                take(f"small batch {si.FMT_NAMES[fmt]} {sname} N={nt} {v}", got, h,
-                     oracle.tol_swiglu(g, u, Sg, Su))
-            else:
-                y, S = oracle.matmul_ref(fmt, rec["w"][0], xs, SB_CHECK_ROWS, K, rows=sub)
-                take(f"small batch {si.FMT_NAMES[fmt]} {sname} N={nt} {v}", got, y, oracle.tol_linear(S))
-    for key, Y in TIMED_OUT.items():
-        if not (isinstance(key, tuple) and key[0] == "prefill"):
-            continue
-        _, fmt, M, K, T = key
-        raw = si.weights(fmt, M, K, 7000 + M % 101 + fmt)
-        X = si.activations(T, K, 7100 + T, dtype=np.float16)
-        y, S = oracle.matmul_ref(fmt, raw, X, M, K, rows=np.arange(PREFILL_CHECK_ROWS))
-        take(f"prefill {si.FMT_NAMES[fmt]} {M}x{K} T={T}", Y, y, oracle.tol_linear(S))
+        if key[0] == "small_batch":
+            _, fmt, sname = key
+            K = rec["K"]
+            for (nt, v), got in rec["y"].items():
+                xs = rec["x"][:nt * K].reshape(nt, K)
+                label = f"small batch {si.FMT_NAMES[fmt]} {sname} N={nt} {v}"
+                if sname == "gate_up":
+                    h, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rec["w"][0], rec["w"][1], xs, SB_CHECK_ROWS, K)
+                    take(label, got, h, oracle.tol_swiglu(g, u, Sg, Su))
+                else:
+                    y, S = oracle.matmul_ref(fmt, rec["w"][0], xs, SB_CHECK_ROWS, K)
+                    take(label, got, y, oracle.tol_linear(S))
+        elif key[0] == "prefill":
+            _, fmt, M, K, T = key
+            raw = si.weights(fmt, M, K, 7000 + M % 101 + fmt)
+            X = si.activations(T, K, 7100 + T, dtype=np.float16)
+            y, S = oracle.matmul_ref(fmt, raw, X, M, K, rows=np.arange(PREFILL_CHECK_ROWS))
+            take(f"prefill {si.FMT_NAMES[fmt]} {M}x{K} T={T}", rec, y, oracle.tol_linear(S))
+        elif key[0] == "expand":
+            _, fmt, M, K, T = key
+            label = f"expand {si.FMT_NAMES[fmt]} {M}x{K} T={T}"
+            exact(label + " fp16 weights",
+                  rec["w16"].view(np.uint16), oracle.expand_f16_ref(fmt, rec["w"], PREFILL_CHECK_ROWS, K).view(np.uint16))
+            y, S = oracle.matmul_ref(fmt, rec["w"], rec["x"], PREFILL_CHECK_ROWS, K)
+            take(label + " GEMM", rec["y"], y, oracle.tol_linear(S))
+        elif key[0] == "get_rows":
+            _, fmt, nr = key
+            m = rec["out"].shape[0]  # 16 gathered rows, or every row of a smaller gather
+            with np.errstate(invalid="ignore"):  # NaN rows (random scale bytes) stay NaN in float32
+                ref = oracle.get_rows_ref(fmt, rec["w"], m, rec["K"], np.arange(m)).astype(np.float32)
+            exact(f"get_rows {si.FMT_NAMES[fmt]} n={nr}", rec["out"], ref)
     if fails:
         print(f"bench: timed outputs outside the oracle bound: {', '.join(fails)}", file=sys.stderr, flush=True)
     return {"outputs_checked": n, "max_err_over_bound": round(worst, 4), "ok": not fails,
-            "what": f"single 576x576 GEMV whole; first {rows} rows of each 8B decode launch; the SmolLM2-135M "
-                    f"step's last layer whole and its LM head's first {rows} rows; the first {SB_CHECK_ROWS} rows "
-                    f"of every small-batch call (format, shape, N, variant); first {PREFILL_CHECK_ROWS} rows x all "
-                    f"tokens of each prefill case"}
+            "what": "single 576x576 GEMV whole; the first rows of every 8B decode launch (Q8_0, Q4_0, Q4_1, Q5_0, "
+                    "Q5_1) and of the fused step; the SmolLM2-135M step's last layer and LM-head rows; the first "
+                    "rows of every small-batch call; the first rows of every prefill and expand-then-GEMM case "
+                    "(the expansion bit for bit); the first 16 rows of every row gather, bit for bit"}
 
 
 def smollm2_step(torch, qmm, si, steps, trials):
@@ -737,6 +788,11 @@ def fused_decode(torch, qmm, si, fmts, steps):
             res[name] = {"us": round(ms * 1e3, 2), "GBps": round(nb / (ms * 1e-3) / 1e9, 1), "bytes": int(nb)}
         res["fused_over_plain_time"] = round(res["fused"]["us"] / res["plain"]["us"], 4)
         out[si.FMT_NAMES[fmt]] = res
+        r0 = resid.cpu().numpy()
+        fused()
+        rec = capture_decode(qmm, si, fmt, f)
+        rec.update(r0=r0, r2=resid.cpu().numpy(), gamma=gamma.cpu().numpy(), eps=eps)
+        TIMED_OUT[("fused", fmt)] = rec
     return out
 
 
@@ -778,9 +834,19 @@ def expand_gemm(torch, qmm, si, reps=10):
                 ms_x = timed(lambda: (qmm.qmm_expand_f16(fmt, W, W16, M, K), qmm.qmm_gemm(1, W16, X, Y, M, K, T)))
                 row["T"].append({"T": T, "fused_TFLOPs": round(fl / (ms_f * 1e-3) / 1e12, 1),
                                  "expand_then_gemm_TFLOPs": round(fl / (ms_x * 1e-3) / 1e12, 1)})
+                capture_expand(("expand", fmt, M, K, T), fmt, W, W16, X, Y, rb)
             out.append(row)
             del W, W16
     return out
+
+
+def capture_expand(key, fmt, W, W16, X, Y, rb):
+    """Host copies for the re-check of an expand-then-GEMM case: the first
+    PREFILL_CHECK_ROWS rows of the raw weights and of their fp16 expansion, and the
+    first TOKEN_CHECK tokens of X and of the GEMM output on those rows."""
+    R, n = PREFILL_CHECK_ROWS, TOKEN_CHECK
+    TIMED_OUT[key] = {"w": W[:R * rb].cpu().numpy(), "w16": W16[:R].cpu().numpy(),
+                      "x": X[:n].cpu().numpy(), "y": Y[:n, :R].cpu().numpy()}
 
 
 def get_rows_bench(torch, qmm, si, reps=20):
@@ -808,6 +874,9 @@ def get_rows_bench(torch, qmm, si, reps=20):
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
             res[f"n{n}"] = {"us": round(ms * 1e3, 2), "GBps": round(n * (rb + 4 * H) / (ms * 1e-3) / 1e9, 1)}
+            sel = ids[:16].long()
+            TIMED_OUT[("get_rows", fmt, n)] = {"w": W.view(V, rb)[sel].cpu().numpy().reshape(-1),
+                                               "out": o[:16].cpu().numpy(), "K": H}
         out[si.FMT_NAMES[fmt]] = res
         del W
     return out
@@ -963,7 +1032,7 @@ def main():
         step(timer)
     torch.cuda.synchronize()
     for fmt, f in fmts.items():
-        TIMED_OUT[("decode", fmt)] = {k: f[k].cpu().numpy() for k in ("y_qkv", "y_o", "h", "y_d", "logits")}
+        TIMED_OUT[("decode", fmt)] = capture_decode(qmm, si, fmt, f)
 
     per = {}
     for key, part, b, _ in launches:

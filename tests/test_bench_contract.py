@@ -76,11 +76,11 @@ def test_timed_parity_passes_oracle_outputs_and_flags_a_wrong_one():
                               si.activations(T, K, 7100 + T, dtype=np.float16), M, K,
                               rows=np.arange(bench.PREFILL_CHECK_ROWS))
     bench.TIMED_OUT[("prefill", fmt, M, K, T)] = Y
-    r = bench.timed_parity(oracle, {}, si, 512)
+    r = bench.timed_parity(oracle, si)
     assert r["ok"] and r["outputs_checked"] == 576 + T * bench.PREFILL_CHECK_ROWS
     assert r["max_err_over_bound"] < 0.01
     Y[3, 5] += 2.0 * float(oracle.tol_linear(S2)[3, 5])
-    r = bench.timed_parity(oracle, {}, si, 512)
+    r = bench.timed_parity(oracle, si)
     assert not r["ok"] and r["max_err_over_bound"] > 1.5
     bench.TIMED_OUT.clear()
 
@@ -105,7 +105,8 @@ def test_timed_parity_covers_smollm2_and_small_batch_records():
                                        H)[0][0].astype(np.float32)
     rec["y_d"] = oracle.matmul_ref(fmt, si.weights(fmt, H, I, s0 + 4), rec["h"], H, I)[0][0].astype(np.float32)
     logits = np.zeros(V, dtype=np.float32)
-    logits[:64] = oracle.matmul_ref(fmt, si.weights(fmt, V, H, base + 999), x, V, H, rows=np.arange(64))[0][0]
+    R = bench.DECODE_CHECK_ROWS
+    logits[:R] = oracle.matmul_ref(fmt, si.weights(fmt, V, H, base + 999), x, V, H, rows=np.arange(R))[0][0]
     rec["logits"] = logits
     bench.TIMED_OUT[("smollm2", fmt)] = rec
     rng = np.random.default_rng(5)
@@ -118,9 +119,66 @@ def test_timed_parity_covers_smollm2_and_small_batch_records():
                                                            "y": {(nt, "valu"): y}}
     bench.TIMED_OUT[("small_batch", si.FMT_Q8_0, "gate_up")] = {"M": 14336, "K": K, "x": xs, "w": w,
                                                                  "y": {(nt, "mfma"): h}}
-    r = bench.timed_parity(oracle, {}, si, 64)
+    r = bench.timed_parity(oracle, si)
     assert r["ok"], r
-    assert r["outputs_checked"] == Q + H + I + H + 64 + 2 * nt * R
+    assert r["outputs_checked"] == Q + H + I + H + bench.DECODE_CHECK_ROWS + 2 * nt * R
     y[1, 7] += 1.0
-    assert not bench.timed_parity(oracle, {}, si, 64)["ok"]
+    assert not bench.timed_parity(oracle, si)["ok"]
+    bench.TIMED_OUT.clear()
+
+
+def test_timed_parity_decode_fused_expand_and_gather_records():
+    """Decode, fused-step, expand-then-GEMM and row-gather records built from the
+    oracle (no GPU) pass; a one-ulp change in an expanded weight or a gathered row,
+    or a residual off by twice its bound, fails."""
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+    bench.TIMED_OUT.clear()
+    L = si.LLAMA3_8B
+    H, I = L["hidden"], L["intermediate"]
+    R, fmt = bench.DECODE_CHECK_ROWS, si.FMT_Q4_1
+    w = {k: si.weights(fmt, R, I if k == "d" else H, 40 + i) for i, k in enumerate(("qkv", "o", "g", "u", "d", "lm"))}
+    x = si.activations(1, H, 47)[0]
+    lin = lambda k, xin, K: oracle.matmul_ref(fmt, w[k], xin, R, K)[0][0].astype(np.float32)
+    h = oracle.gate_up_silu_ref(fmt, w["g"], w["u"], x, R, H)[0][0].astype(np.float32)
+    h_full = np.concatenate([h, np.zeros(I - R, np.float32)])
+    rec = {"w": w, "x": x, "y_qkv": lin("qkv", x, H), "y_o": lin("o", x, H), "h": h_full,
+           "y_d": lin("d", h_full, I), "logits": lin("lm", x, H)}
+    bench.TIMED_OUT[("decode", fmt)] = rec
+    gm = (1.0 + 0.1 * si.activations(1, H, 48)[0]).astype(np.float32)
+    xn = oracle.rmsnorm_ref(x, gm, 1e-5)[0]
+    hf = oracle.gate_up_silu_ref(fmt, w["g"], w["u"], xn, R, H)[0][0].astype(np.float32)
+    hf_full = np.concatenate([hf, np.zeros(I - R, np.float32)])
+    r0 = si.activations(1, H, 49)[0]
+    r1 = oracle.matmul_add_ref(fmt, w["o"], x, r0[:R], R, H)[0][0]
+    r2 = oracle.matmul_add_ref(fmt, w["d"], hf_full, r1, R, I)[0][0].astype(np.float32)
+    fused = dict(rec, y_qkv=oracle.matmul_ref(fmt, w["qkv"], xn, R, H)[0][0].astype(np.float32), h=hf_full,
+                 logits=oracle.matmul_ref(fmt, w["lm"], xn, R, H)[0][0].astype(np.float32), gamma=gm, eps=1e-5,
+                 r0=np.concatenate([r0[:R], np.zeros(H - R, np.float32)]),
+                 r2=np.concatenate([r2, np.zeros(H - R, np.float32)]))
+    bench.TIMED_OUT[("fused", fmt)] = fused
+    K, P, n = 256, bench.PREFILL_CHECK_ROWS, bench.TOKEN_CHECK
+    we = si.weights(si.FMT_Q8_0, P, K, 50)
+    xe = si.activations(n, K, 51, dtype=np.float16)
+    bench.TIMED_OUT[("expand", si.FMT_Q8_0, 4096, K, 128)] = {
+        "w": we, "w16": oracle.expand_f16_ref(si.FMT_Q8_0, we, P, K),
+        "x": xe, "y": oracle.matmul_ref(si.FMT_Q8_0, we, xe, P, K)[0].astype(np.float32)}
+    wg = si.weights(si.FMT_Q4_0, 16, K, 52)
+    bench.TIMED_OUT[("get_rows", si.FMT_Q4_0, 1)] = {
+        "w": wg, "out": oracle.get_rows_ref(si.FMT_Q4_0, wg, 16, K, np.arange(16)).astype(np.float32), "K": K}
+    r = bench.timed_parity(oracle, si)
+    assert r["ok"], r
+    bench.TIMED_OUT[("expand", si.FMT_Q8_0, 4096, K, 128)]["w16"].view(np.uint16)[3, 4] ^= 1
+    assert not bench.timed_parity(oracle, si)["ok"]
+    bench.TIMED_OUT[("expand", si.FMT_Q8_0, 4096, K, 128)]["w16"].view(np.uint16)[3, 4] ^= 1
+    bench.TIMED_OUT[("get_rows", si.FMT_Q4_0, 1)]["out"][2, 9] = np.nextafter(
+        bench.TIMED_OUT[("get_rows", si.FMT_Q4_0, 1)]["out"][2, 9], np.float32(np.inf))
+    assert not bench.timed_parity(oracle, si)["ok"]
+    bench.TIMED_OUT.pop(("get_rows", si.FMT_Q4_0, 1))
+    assert bench.timed_parity(oracle, si)["ok"]
+    S1 = oracle.matmul_add_ref(fmt, w["o"], x, r0[:R], R, H)[1][0]
+    S2 = oracle.matmul_add_ref(fmt, w["d"], hf_full, r1, R, I)[1][0]
+    fused["r2"][5] += 2.0 * float(oracle.tol_residual(S1, r1)[5] + oracle.tol_residual(S2, r2)[5])
+    assert not bench.timed_parity(oracle, si)["ok"]
     bench.TIMED_OUT.clear()
