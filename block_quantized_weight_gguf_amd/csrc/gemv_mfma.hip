@@ -1,7 +1,5 @@
 // Small-batch decode GEMV on the matrix cores: y[n][m] = sum_k W[m][k] x[n][k] for a
-// few tokens (2..32), block-format weights, fp32 accumulate.  x enters as fp16 scaled
-// per token (scale_tokens_f16: x16 = fp16(2^s_n x_n)); the epilogue multiplies token
-// n's outputs by tscale[n] = 2^-s_n.
+// few tokens (2..32), block-format weights, fp32 x and y, fp32 accumulate.
 //
 // ("llama.cpp Metal ...", section 3.2 and P9: a batched mat-vec for a handful of
 // tokens, each weight read once and reused for every token; "EdgeRunner Core
@@ -12,19 +10,32 @@
 //   * A workgroup (8 waves, one per CU: LDS-limited) owns 256 weight rows and a
 //     range of K.  Each wave owns 32 rows: 2 MFMA row fragments; the tokens (padded
 //     to 16 or 32) are 1 or 2 column fragments.
-//   * Weights and x stream through a ring of 3 LDS stages by buffer->LDS DMA.  A
-//     stage holds the raw GGUF bytes of 4 blocks of all 256 rows (16-byte chunks of
-//     the row windows, whole 128-byte lines per load instruction) and the fp16 x of
-//     the same 128-wide K range for every token (16-byte chunks XOR-swizzled by
-//     token, so that the 16 token rows of a fragment read hit distinct banks).  Two
-//     stages are always in flight, ~80 KB per CU, which covers HBM latency at the
-//     per-CU share of the bandwidth.
+//   * Weights stream through a ring of 3 LDS stages by buffer->LDS DMA.  A stage
+//     holds the raw GGUF bytes of 4 blocks of all 256 rows (16-byte chunks of the row
+//     windows, whole 128-byte lines per load instruction) and the fp16 x of the same
+//     128-wide K range for every token (16-byte chunks XOR-swizzled by token, so that
+//     the 16 token rows of a fragment read hit distinct banks).  Two stages are always
+//     in flight, ~80 KB per CU, which covers HBM latency at the per-CU share of the
+//     bandwidth.
+//   * x arrives as fp32 and is turned into the fp16 MFMA operand here, one stage
+//     ahead of its use: the stage's 128 values of every token are loaded into
+//     registers while the weight DMA runs, and after the current stage's MFMAs they
+//     are scaled by a power of two 2^S and rounded once to fp16 into the ring slot.
+//     S is a running per-token exponent: the smallest min(126, 14 - floor(log2 max))
+//     over the stages converted so far, so no scaled value reaches 2^15 (fp16 holds
+//     it) and each keeps fp16's relative precision unless it lies about 2^28 below
+//     the largest |x| seen so far.  When S drops, the accumulators of that token are
+//     multiplied by the exact power of two that moves them to the new scale; the
+//     epilogue multiplies by 2^-S.  fp32 tokens thus need no conversion pass of their
+//     own ("alpaca.swift", Design: half-precision activations on the matrix
+//     hardware; Limitations: the activations stay unquantised).
 //   * Each wave decodes its A fragments straight from the raw bytes in the fp16
 //     domain (shared with the prefill GEMM) and issues 2 x (tokens / 16) MFMAs per
 //     block: the matrix cores do the multiply-adds, the VALU only decodes.
 //   * When the rows alone cannot fill the machine (or K is long), K is split over
-//     several workgroups; their partial sums go to the caller's workspace and a
-//     second kernel adds them in a fixed order and applies the gated epilogue.
+//     several workgroups; their partial sums (already at the tokens' true scale) go
+//     to the caller's workspace and a second kernel adds them in a fixed order and
+//     applies the gated epilogue.
 //   * Gated instance: stage rows 0..127 are 128 gate rows and 128..255 the up rows
 //     of the same outputs; each wave takes 16 gate and the matching 16 up rows.
 #include <algorithm>
@@ -50,8 +61,7 @@ constexpr int gm_stage_blocks() { return 4; }
 template <int FMT, bool GATED, int NJ, bool SPLIT>
 __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __restrict__ Wg,
                                                                 const uint8_t* __restrict__ Wu,
-                                                                const _Float16* __restrict__ x,
-                                                                const float* __restrict__ tscale, float* __restrict__ Y,
+                                                                const float* __restrict__ x, float* __restrict__ Y,
                                                                 int M, int K, int N, int nsplit, int kst, int vec) {
     constexpr int BB = Fmt<FMT>::BB;
     constexpr int SB = gm_stage_blocks<FMT, NJ>();
@@ -72,11 +82,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
     constexpr int XC = XROW / 16;                    // 16-byte chunks per token row
     static_assert(XC == 16, "the swizzle key (token & 15) stays inside a row");
     constexpr int XBYTES = NTOK * XROW;              // x bytes per stage
-    constexpr int XINST = XBYTES / 1024;             // wave-wide DMA instructions per stage (x)
-    // As for the weights, surplus instructions repeat the stage's last x instruction.
-    constexpr int XPER = (XINST + GM_WAVES - 1) / GM_WAVES;
-    constexpr int SLOT = WBYTES + XBYTES;            // one ring slot: weights, then x
-    constexpr int NDMA = WPER + XPER;                // DMA instructions per wave and stage
+    constexpr int SLOT = WBYTES + XBYTES + 4 * NTOK;  // one ring slot: weights, x, the tokens' S
 
     __shared__ __align__(16) uint8_t R0[SLOT];
     __shared__ __align__(16) uint8_t R1[SLOT];
@@ -116,19 +122,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
         const int r = GATED ? (R & 127) : R;
         woffs[i] = static_cast<uint32_t>(min(r, wrows - 1) * rb) + 16 * (q % WCH);
     }
-    // x: item q = slot q % XC of token row q / XC, holding chunk slot ^ (token & 15)
-    // of that token's STAGE_K halfs.  Tokens past N re-read token N - 1 (never stored).
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, static_cast<int64_t>(N) * K * 2);
-    uint32_t xoffs[XPER];
-#pragma unroll
-    for (int i = 0; i < XPER; ++i) {
-        const int q = 64 * min(wave + GM_WAVES * i, XINST - 1) + lane;
-        const int n = q / XC, sl = q % XC;
-        xoffs[i] = static_cast<uint32_t>(min(n, N - 1) * K * 2) + 16 * (sl ^ (n & 15));
-    }
     // Stage st: the 16-byte aligned windows around the row segment [SEG st, SEG st +
-    // SEG) of every row (with SHIFT the segment starts 0 or 8 bytes into the window),
-    // then x[., STAGE_K st .. STAGE_K st + STAGE_K - 1].
+    // SEG) of every row (with SHIFT the segment starts 0 or 8 bytes into the window).
     auto issue = [&](QMM_L3 uint8_t* S, int st) {
         const uint32_t a = (static_cast<uint32_t>(st) * SEG) & ~15u;
 #pragma unroll
@@ -136,22 +131,67 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
             const int n = min(wave + GM_WAVES * i, WINST - 1);
             dma16((GATED && n >= WINST / 2) ? wur : wgr, woffs[i], a, S + 1024 * n);
         }
+    };
+
+    // x: thread tid converts floats 4 (tid % 32) .. 4 (tid % 32) + 3 of the stage's
+    // STAGE_K for tokens tid / 32 + 16 j.  Tokens past N read token N - 1 and use
+    // zeros.
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, static_cast<int64_t>(N) * K * 4);
+    const int ct = tid >> 5, ck = tid & 31;
+    // Destination: token row t, 16-byte chunk ck / 2 (8 halfs) at slot chunk ^ (t & 15),
+    // half ck % 2 of it; t & 15 == ct for every j.
+    const int xdst = WBYTES + ct * XROW + 16 * ((ck >> 1) ^ ct) + 8 * (ck & 1);
+    int xs[NJ];  // running exponent S of tokens ct + 16 j (127: nothing seen yet)
 #pragma unroll
-        for (int i = 0; i < XPER; ++i)
-            dma16(xr, xoffs[i], static_cast<uint32_t>(st) * XROW, S + WBYTES + 1024 * min(wave + GM_WAVES * i, XINST - 1));
+    for (int j = 0; j < NJ; ++j) xs[j] = 127;
+    auto load_x = [&](int st, float4_t (&v)[NJ]) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            v[j] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    xr, (min(ct + 16 * j, N - 1) * K + 4 * ck) * 4, st * (STAGE_K * 4), 0));
+    };
+    // Scale by 2^S and round to fp16 into ring slot S_; S of every token to the slot's
+    // tail (one lane per token writes it).
+    auto store_x = [&](QMM_L3 uint8_t* S_, float4_t (&v)[NJ]) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (ct + 16 * j >= N) v[j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            float m = fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3])));
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            const int e = static_cast<int>((__float_as_uint(m) >> 23) & 0xFFu) - 127;  // floor(log2 m); -127 for 0
+            xs[j] = min(xs[j], min(126, 14 - e));                                     // in [-114, 126]
+            const float sc = __uint_as_float(static_cast<uint32_t>(xs[j] + 127) << 23);
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t h = {pack_h2(v[j][0] * sc, v[j][1] * sc), pack_h2(v[j][2] * sc, v[j][3] * sc)};
+            *reinterpret_cast<QMM_L3 u32x2_t*>(S_ + xdst + 16 * j * XROW) = h;
+            if (ck == 0) reinterpret_cast<QMM_L3 int*>(S_ + WBYTES + XBYTES)[ct + 16 * j] = xs[j];
+        }
     };
 
     QMM_L3 uint8_t* W0 = (QMM_L3 uint8_t*)R0;
     QMM_L3 uint8_t* W1 = (QMM_L3 uint8_t*)R1;
     QMM_L3 uint8_t* W2 = (QMM_L3 uint8_t*)R2;
-    issue(W0, st0);
-    issue(W1, min(st0 + 1, st1 - 1));
+    {
+        // x loads first: waiting for them leaves the weight DMA in flight.
+        float4_t v0[NJ], v1[NJ];
+        load_x(st0, v0);
+        load_x(min(st0 + 1, st1 - 1), v1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(W0, st0);
+        issue(W1, min(st0 + 1, st1 - 1));
+        store_x(W0, v0);
+        store_x(W1, v1);
+    }
 
     float4_t acc[2][NJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    int as[NJ];  // exponent S of the accumulators' token 16 j + lane % 16
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) as[j] = 127;
 
     const int q4 = lane >> 4;
     // A fragment i: stage row 32 w + 16 i + l % 16; gated: fragment 0 is gate row
@@ -170,18 +210,34 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
         return *reinterpret_cast<const QMM_L3 half8_t*>(S + xrow + j * 16 * XROW + 16 * (c ^ xsw));
     };
 
-    // Stage st from ring slot Wc: wait for its DMA (the next stage's may stay in
-    // flight), barrier, refill the slot read on the previous stage with stage st + 2
-    // (past the end: the last stage again, into a slot nobody reads), compute.
-    // PAR_ is the stage's parity (st0 is even), which fixes the segment offset at
-    // compile time; with a run-time offset the compiler cannot tell the ring slots'
-    // reads from the DMA in flight and waits for all of it.
+    // Stage st from ring slot Wc: wait for its weight DMA (the next stage's may stay
+    // in flight), barrier, load stage st + 2's x and refill the slot read on the
+    // previous stage with its weights (past the end: the last stage again, into a slot
+    // nobody reads), move the accumulators to the stage's S, compute, then convert
+    // stage st + 2's x into that slot (the wait for the x loads leaves the new weight
+    // DMA in flight).  PAR_ is the stage's parity (st0 is even), which fixes the
+    // segment offset at compile time; with a run-time offset the compiler cannot tell
+    // the ring slots' reads from the DMA in flight and waits for all of it.
     auto stage = [&](auto PAR_, QMM_L3 uint8_t* Wc, QMM_L3 uint8_t* Wn2, int st) {
         constexpr int sh = SHIFT ? 8 * decltype(PAR_)::value : 0;
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<NDMA>();
+        wait_vm<WPER>();
         lds_barrier();
+        float4_t v[NJ];
+        load_x(min(st + 2, st1 - 1), v);
+        __builtin_amdgcn_sched_barrier(0);  // the x loads stay ahead of the weight DMA
         issue(Wn2, min(st + 2, st1 - 1));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int sv = reinterpret_cast<const QMM_L3 int*>(Wc + WBYTES + XBYTES)[16 * j + (lane & 15)];
+            if (__builtin_amdgcn_ballot_w64(sv != as[j])) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_amdgcn_ldexpf(acc[i][j][e], sv - as[j]);
+                as[j] = sv;
+            }
+        }
 #pragma unroll
         for (int b = 0; b < SB; ++b) {
             const half8_t a0 = frag_raw<FMT>(Wc + arow0, sh + BB * b, q4);
@@ -193,6 +249,8 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
                 acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bf, acc[1][j], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        store_x(Wn2, v);
     };
     // Two turns of the ring per iteration (static slots and parities, no branches
     // inside, which keeps the compiler's own wait tracking exact); the remaining
@@ -216,13 +274,17 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
     // Drain the trailing re-load DMAs before the workgroup can exit.
     wait_vm<0>();
 
-    // ---- epilogue.  D fragment: lane l holds rows 4 (l / 16) + e of token l % 16.
+    // ---- epilogue.  D fragment: lane l holds rows 4 (l / 16) + e of token l % 16,
+    // at scale 2^S: the sums are multiplied by 2^-S.
     const int er = 4 * (lane >> 4);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int t = 16 * j + (lane & 15);
         if (t >= N) continue;
-        const float sc = tscale[t];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_amdgcn_ldexpf(acc[i][j][e], -as[j]);
         auto store4 = [&](float* yp, int m, const float (&h)[4]) {
             if (vec) {
                 *reinterpret_cast<float4*>(yp) = make_float4(h[0], h[1], h[2], h[3]);
@@ -249,7 +311,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
             if (m < M) {
                 float h[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = silu(acc[0][j][e] * sc) * (acc[1][j][e] * sc);
+                for (int e = 0; e < 4; ++e) h[e] = silu(acc[0][j][e]) * acc[1][j][e];
                 store4(Y + static_cast<int64_t>(t) * M + m, m, h);
             }
         } else {
@@ -257,7 +319,7 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
             for (int i = 0; i < 2; ++i) {
                 const int m = m0 + 32 * wave + 16 * i + er;
                 if (m < M) {
-                    const float h[4] = {acc[i][j][0] * sc, acc[i][j][1] * sc, acc[i][j][2] * sc, acc[i][j][3] * sc};
+                    const float h[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
                     store4(Y + static_cast<int64_t>(t) * M + m, m, h);
                 }
             }
@@ -266,14 +328,14 @@ __global__ __launch_bounds__(GM_THREADS) void gemv_mfma_kernel(const uint8_t* __
 }
 
 template <int FMT, bool GATED, int NJ, bool SPLIT>
-static void launch_gm_t(const void* W, const void* Wu, const void* x16, const float* tscale, float* Y, int64_t M,
-                        int64_t K, int64_t N, int nsplit, int kst, hipStream_t s) {
+static void launch_gm_t(const void* W, const void* Wu, const float* x, float* Y, int64_t M, int64_t K, int64_t N,
+                        int nsplit, int kst, hipStream_t s) {
     const int64_t rows_per_tile = GATED ? GM_BM / 2 : GM_BM;
     const int64_t ntiles = (M + rows_per_tile - 1) / rows_per_tile;
     const int vec = M % 4 == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
     hipLaunchKernelGGL((gemv_mfma_kernel<FMT, GATED, NJ, SPLIT>), dim3(static_cast<unsigned>(ntiles * nsplit)),
                        dim3(GM_THREADS), 0, s, static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(Wu),
-                       static_cast<const _Float16*>(x16), tscale, Y, static_cast<int>(M), static_cast<int>(K),
+                       x, Y, static_cast<int>(M), static_cast<int>(K),
                        static_cast<int>(N), nsplit, kst, vec);
 }
 
@@ -303,25 +365,25 @@ GemvMfmaPlan plan_gemv_mfma(int fmt, int64_t M, int64_t K, int64_t N, bool gated
 }
 
 template <int FMT, int NJ>
-static void launch_gm_nj(const GemvMfmaPlan& p, const void* W, const void* Wu, const void* x16, const float* tscale,
-                         float* y, int64_t M, int64_t K, int64_t N, float* ws, hipStream_t s) {
+static void launch_gm_nj(const GemvMfmaPlan& p, const void* W, const void* Wu, const float* x, float* y, int64_t M,
+                         int64_t K, int64_t N, float* ws, hipStream_t s) {
     const bool gated = Wu != nullptr;
     if (p.nsplit == 1) {
-        if (gated) launch_gm_t<FMT, true, NJ, false>(W, Wu, x16, tscale, y, M, K, N, 1, p.kst, s);
-        else launch_gm_t<FMT, false, NJ, false>(W, Wu, x16, tscale, y, M, K, N, 1, p.kst, s);
+        if (gated) launch_gm_t<FMT, true, NJ, false>(W, Wu, x, y, M, K, N, 1, p.kst, s);
+        else launch_gm_t<FMT, false, NJ, false>(W, Wu, x, y, M, K, N, 1, p.kst, s);
         return;
     }
-    if (gated) launch_gm_t<FMT, true, NJ, true>(W, Wu, x16, tscale, ws, M, K, N, p.nsplit, p.kst, s);
-    else launch_gm_t<FMT, false, NJ, true>(W, Wu, x16, tscale, ws, M, K, N, p.nsplit, p.kst, s);
-    launch_splitk_reduce(ws, y, tscale, N, M, p.nsplit, gated, s);
+    if (gated) launch_gm_t<FMT, true, NJ, true>(W, Wu, x, ws, M, K, N, p.nsplit, p.kst, s);
+    else launch_gm_t<FMT, false, NJ, true>(W, Wu, x, ws, M, K, N, p.nsplit, p.kst, s);
+    launch_splitk_reduce(ws, y, nullptr, N, M, p.nsplit, gated, s);
 }
 
-void launch_gemv_mfma(const GemvMfmaPlan& p, int fmt, const void* W, const void* Wu, const void* x16,
-                      const float* tscale, float* y, int64_t M, int64_t K, int64_t N, float* ws, hipStream_t s) {
+void launch_gemv_mfma(const GemvMfmaPlan& p, int fmt, const void* W, const void* Wu, const float* x, float* y,
+                      int64_t M, int64_t K, int64_t N, float* ws, hipStream_t s) {
     const bool two = p.nj == 2;
-#define QMM_GM(F)                                                              \
-    if (two) launch_gm_nj<F, 2>(p, W, Wu, x16, tscale, y, M, K, N, ws, s);   \
-    else launch_gm_nj<F, 1>(p, W, Wu, x16, tscale, y, M, K, N, ws, s);
+#define QMM_GM(F)                                                   \
+    if (two) launch_gm_nj<F, 2>(p, W, Wu, x, y, M, K, N, ws, s);   \
+    else launch_gm_nj<F, 1>(p, W, Wu, x, y, M, K, N, ws, s);
     switch (fmt) {
         case 8: QMM_GM(8) break;
         case 2: QMM_GM(2) break;

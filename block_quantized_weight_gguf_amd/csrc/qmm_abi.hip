@@ -64,10 +64,11 @@ bool weight_bytes(int fmt, int64_t M, int64_t K, bool gated, int64_t* out) {
 }
 
 // Workspace of an fp32-token MFMA product (qmm_gemv / qmm_gate_up_silu on the MFMA
-// variant): the tokens as scaled fp16 (N x K halfs), their scales (N floats), then
-// the product's split-K partials; each part starts on a QMM_WORKSPACE_ALIGN boundary.
-// The weight-streaming MFMA GEMV serves 2..32 tokens (block formats, K % 256 == 0);
-// the GEMM every other case.
+// variant).  The weight-streaming MFMA GEMV serves 2..32 tokens (block formats, K %
+// 256 == 0) and scales the tokens to fp16 itself: its workspace is the split-K
+// partials alone.  The GEMM serves every other case: the tokens as scaled fp16 (N x K
+// halfs), their scales (N floats), then the GEMM's split-K partials.  Each part starts
+// on a QMM_WORKSPACE_ALIGN boundary.
 struct MfmaWs {
     qmm::GemvMfmaPlan gp;
     int64_t x16 = 0, inv = 0, part = 0, total = 0;  // byte offsets of the parts, total size
@@ -76,8 +77,12 @@ struct MfmaWs {
 MfmaWs mfma_ws(int fmt, int64_t M, int64_t K, int64_t N, bool gated) {
     MfmaWs w;
     w.gp = qmm::plan_gemv_mfma(fmt, M, K, N, gated);
-    const int64_t part = w.gp.ok ? static_cast<int64_t>(w.gp.ws_bytes)
-                                 : static_cast<int64_t>(qmm::gemm_workspace_bytes(fmt, M, K, N, gated));
+    if (w.gp.ok) {
+        w.total = round_ws(static_cast<int64_t>(w.gp.ws_bytes));
+        w.ok = true;
+        return w;
+    }
+    const int64_t part = static_cast<int64_t>(qmm::gemm_workspace_bytes(fmt, M, K, N, gated));
     int64_t xb, ib;
     if (!mul_ok(N, K, &xb) || !mul_ok(xb, 2, &xb) || !mul_ok(N, 4, &ib)) return w;
     w.x16 = 0;
@@ -120,7 +125,8 @@ int choose_variant(int fmt, int64_t wbytes, int64_t N, bool gated) {
     return QMM_VARIANT_VALU;
 }
 
-// The fp32-token MFMA product: tokens to scaled fp16, then the MFMA GEMV or GEMM.
+// The fp32-token MFMA product: the MFMA GEMV straight from fp32 tokens, or tokens to
+// scaled fp16 and then the GEMM.
 int run_mfma_tokens(int fmt, const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
                     int64_t N, void* ws, int64_t ws_bytes, hipStream_t s) {
     const MfmaWs w = mfma_ws(fmt, M, K, N, Wu != nullptr);
@@ -128,15 +134,15 @@ int run_mfma_tokens(int fmt, const void* W, const void* Wu, const float* x, floa
     const int st = check_ws(ws, ws_bytes, w.total);
     if (st) return st;
     char* base = static_cast<char*>(ws);
-    void* x16 = base + w.x16;
-    float* inv = reinterpret_cast<float*>(base + w.inv);
     float* part = reinterpret_cast<float*>(base + w.part);
-    hipError_t e = qmm::launch_scale_tokens(x, x16, inv, N, K, s);
-    if (e != hipSuccess) return QMM_ERR_HIP;
     if (w.gp.ok) {
-        qmm::launch_gemv_mfma(w.gp, fmt, W, Wu, x16, inv, y, M, K, N, part, s);
+        qmm::launch_gemv_mfma(w.gp, fmt, W, Wu, x, y, M, K, N, part, s);
         return from_hip(hipGetLastError());
     }
+    void* x16 = base + w.x16;
+    float* inv = reinterpret_cast<float*>(base + w.inv);
+    hipError_t e = qmm::launch_scale_tokens(x, x16, inv, N, K, s);
+    if (e != hipSuccess) return QMM_ERR_HIP;
     return from_hip(qmm::launch_gemm_mfma(fmt, W, Wu, x16, inv, y, M, K, N, part, s));
 }
 

@@ -102,11 +102,11 @@ struct GemvMfmaPlan {
     size_t ws_bytes = 0;    // split-K partials
 };
 GemvMfmaPlan plan_gemv_mfma(int fmt, int64_t M, int64_t K, int64_t N, bool gated);
-// y[n][m] = tscale[n] * sum_k W[m][k] x16[n][k] (x16 fp16, tscale never nullptr here).
-void launch_gemv_mfma(const GemvMfmaPlan& p, int fmt, const void* W, const void* Wu, const void* x16,
-                      const float* tscale, float* y, int64_t M, int64_t K, int64_t N, float* ws, hipStream_t s);
+// y[n][m] = sum_k W[m][k] x[n][k] (x fp32, turned into scaled fp16 inside the kernel).
+void launch_gemv_mfma(const GemvMfmaPlan& p, int fmt, const void* W, const void* Wu, const float* x, float* y,
+                      int64_t M, int64_t K, int64_t N, float* ws, hipStream_t s);
 
-// Y[t][m] = tscale[t] * sum over s < nsplit of P[s][t][m] (gated: P holds gate sums in
+// Y[t][m] = tscale[t] (1 when nullptr) * sum over s < nsplit of P[s][t][m] (gated: P holds gate sums in
 // columns 0..M-1 and up sums in M..2M-1 of each 2M-wide row, and Y = silu(gate) * up).
 void launch_splitk_reduce(const float* P, float* Y, const float* tscale, int64_t T, int64_t M, int nsplit, bool gated,
                           hipStream_t s);

@@ -133,8 +133,9 @@ const char* qmm_strerror(int status);
  * qmm_gate_up_silu and the GEMMs, where it is ignored).  Host-only; makes no HIP
  * call.  The workspace holds a call's split-K partial sums (when the output tiles
  * cannot fill the GPU, K is split over several workgroups and a second kernel adds
- * their sums in a fixed order) and, for the fp32-token MFMA variant, the tokens
- * converted to scaled fp16 and their scales.  Its contents need no initialisation
+ * their sums in a fixed order) and, for the fp32-token MFMA variant when it runs on
+ * the GEMM (F16 weights, more than 32 tokens, or K not a multiple of 256), the
+ * tokens converted to scaled fp16 and their scales.  Its contents need no initialisation
  * and are dead after the call's kernels finish.  ("EdgeRunner Core Architecture",
  * section 10 Scratch Buffers: scratch memory is allocated once and reused by every
  * pass.)
@@ -207,12 +208,15 @@ int qmm_expand_f16(int fmt, const void* W, void* out, int64_t M, int64_t K, void
  *   for every finite x (blocks whose dynamic range fp16 cannot hold take an exact
  *   fp32 path); x = e_k returns W[:, k] exactly (biased formats: d u + m rounded
  *   once).  F16 weights and rows left to its fallback use fp32 x and fp32 FMAs.
- *   MFMA variant: each token is scaled by a power of two (its largest |x| into
- *   [2^14, 2^15)) and rounded to fp16; weights enter as fp16(w), one rounding;
- *   |y - y_exact| <= about 2^-10 sum_k |W[m][k] x[n][k]| while every decoded |w|
- *   is below 65520 (larger ones overflow fp16) and no nonzero x lies more than
- *   2^28 below its token's largest (such elements keep an absolute error of at
- *   most 2^-39 times that largest).
+ *   MFMA variant: each token is scaled by a power of two and rounded to fp16 --
+ *   on the GEMM one scale per token, which brings its largest |x| into [2^14,
+ *   2^15); in the weight-streaming kernel (block formats, 2..32 tokens) a running
+ *   scale per token and workgroup, which keeps the largest |x| read so far below
+ *   2^15 -- and weights enter as fp16(w), one rounding; |y - y_exact| <= about
+ *   2^-10 sum_k |W[m][k] x[n][k]| while every decoded |w| is below 65520 (larger
+ *   ones overflow fp16) and no nonzero x lies more than 2^28 below its token's
+ *   largest (such elements keep an absolute error of at most 2^-39 times that
+ *   largest).
  * Fused QKV is this call on the row-concatenation [Wq; Wk; Wv] (M = q + 2 kv).
  */
 int qmm_gemv(int fmt, const void* W, const float* x, float* y,

@@ -223,8 +223,9 @@ AUTO, VALU, MFMA = 0, 1, 2
 
 def test_workspace_size():
     """The size query: nothing for the register-decode products and for GEMMs whose
-    tiles fill the GPU; split-K partials otherwise; the fp32-token MFMA products add
-    the scaled fp16 tokens and their scales.  Sizes are whole multiples of 256."""
+    tiles fill the GPU; split-K partials otherwise; the fp32-token MFMA products that
+    run the GEMM add the scaled fp16 tokens and their scales (the MFMA GEMV converts
+    its tokens itself).  Sizes are whole multiples of 256."""
     W = qmm._lib.qmm_workspace_size
     assert W(OP_GEMV, 8, 4096, 4096, 1, AUTO) == 0
     assert W(OP_GEMV, 8, 4096, 4096, 4, VALU) == 0
@@ -234,11 +235,13 @@ def test_workspace_size():
     assert part > 0 and part % 256 == 0
     assert part % (128 * 14336 * 4) == 0
     assert W(OP_GEMM_GATE, 8, 14336, 4096, 128, AUTO) >= 2 * part // 2
-    # MFMA GEMV at 8 tokens: fp16 tokens (8 x 4096 x 2), scales, partials (16 row tiles: split).
+    # MFMA GEMV at 8 tokens: the partials alone (16 row tiles: K split 16 ways).
     v = W(OP_GEMV, 8, 4096, 4096, 8, AUTO)
-    assert v >= 8 * 4096 * 2 + 256 + 8 * 4096 * 4 and v % 256 == 0
+    assert v == 16 * 8 * 4096 * 4
     assert W(OP_GEMV, 8, 4096, 4096, 8, MFMA) == v
+    assert W(OP_GEMV, 8, 65536, 4096, 8, MFMA) == 0                # 256 row tiles: no split
     assert W(OP_GEMV, 1, 4096, 4096, 64, AUTO) >= 64 * 4096 * 2    # F16 through the GEMM
+    assert W(OP_GEMV, 8, 4096, 4096, 33, MFMA) >= 33 * 4096 * 2    # 33 tokens: the GEMM
     # Errors: op, variant, shape.
     assert W(9, 8, 64, 64, 1, AUTO) == E_ARG
     assert W(OP_GEMV, 8, 64, 64, 1, 7) == E_VAR
