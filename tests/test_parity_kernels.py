@@ -365,3 +365,77 @@ def test_mfma_x_beyond_fp16_range(fmt, scale, M, K, N):
     torch.cuda.synchronize()
     h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, xs, M, K)
     check_swiglu(h.cpu().numpy(), h_ref, g, u, Sg, Su, f"mfma gate_up x range fmt={fmt} scale={scale}")
+
+
+def _stage_profiles(N, K, seed, big=1e7, high=1e20):
+    """fp32 tokens whose magnitude changes along K, so that the weight-streaming MFMA
+    GEMV's running per-token scale (one power of two per 128-wide stage and
+    workgroup) moves from stage to stage: growing and shrinking ramps over 2^-20 ..
+    2^20, a zero prefix, a single element `big` in the last stage, a step from 1e-30
+    to `high` half way, an all-zero token, and plain Gaussian tokens.
+
+    The spike stays within about 2^24 of its token's other values: an element more
+    than 2^28 below the largest |x| read before it keeps only an absolute error of
+    2^-39 times that largest, and where the spike meets a zero weight (a Q4_0 code
+    of 8) the bound's sum |w x| does not contain the spike."""
+    g = si.activations(N, K, seed).astype(np.float64)
+    ramp = np.linspace(-20.0, 20.0, K)
+    x = np.empty((N, K), np.float64)
+    for n in range(N):
+        kind = n % 7
+        if kind == 0:
+            x[n] = g[n] * np.exp2(ramp)
+        elif kind == 1:
+            x[n] = g[n] * np.exp2(-ramp)
+        elif kind == 2:
+            x[n] = np.where(np.arange(K) < K // 2, 0.0, g[n])
+        elif kind == 3:
+            x[n] = g[n]
+            x[n, K - 1 - (n % 128)] = big
+        elif kind == 4:
+            x[n] = np.where(np.arange(K) < K // 2, 1e-30, high) * g[n]
+        elif kind == 5:
+            x[n] = 0.0
+        else:
+            x[n] = g[n]
+    return x.astype(np.float32)
+
+
+# The shapes: split K (2 or 4 stages per workgroup, partials at the tokens' true scale
+# summed by the reduce kernel) and unsplit K (129 row tiles or more: 8 stages in one
+# workgroup, the epilogue descales); one and two token fragments.  Large matrices are
+# checked on their first and last rows.
+@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_0, si.FMT_Q5_1], ids=str)
+@pytest.mark.parametrize("M,K,N", [(300, 2048, 8), (8192, 4096, 7), (33024, 1024, 20), (33024, 1024, 3)])
+def test_mfma_running_token_scale(fmt, M, K, N):
+    seed = 3600 + M + K + N + fmt
+    raw = si.weights(fmt, M, K, seed, scale_mode="gemm_wide", q8_low=-128)
+    x = _stage_profiles(N, K, seed + 1)
+    announce(f"mfma running scale fmt={fmt} M={M} K={K} N={N} seed={seed}")
+    y = qmm.gemv(fmt, dev(raw), dev(x), M, K, variant=MFMA)
+    torch.cuda.synchronize()
+    rows = np.arange(M) if M <= 512 else np.r_[0:256, M - 256:M]
+    y_ref, S = oracle.matmul_ref(fmt, raw, x, M, K, rows=rows)
+    got = y.cpu().numpy().reshape(N, M)[:, rows]
+    check_linear(got, y_ref, S, f"mfma running scale fmt={fmt} M={M} K={K} N={N}")
+    if N > 5:
+        assert np.all(got[5::7] == 0.0)  # the all-zero tokens
+
+
+@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_1], ids=str)
+@pytest.mark.parametrize("I,K,N", [(200, 2048, 8), (16512, 1024, 20)])
+def test_mfma_running_token_scale_gate_up(fmt, I, K, N):
+    """The gated instance of the same: 200 outputs split K; 16512 outputs (129 tiles
+    of 128) keep K whole.  The spike and the step's high side are 1e6, so that
+    silu(gate) * up stays inside fp32's range."""
+    seed = 3700 + I + K + N + fmt
+    rg = si.weights(fmt, I, K, seed, scale_mode="gemm_wide", q8_low=-128)
+    ru = si.weights(fmt, I, K, seed + 2, scale_mode="gemm_wide", q8_low=-128)
+    x = _stage_profiles(N, K, seed + 1, big=1e6, high=1e6)
+    announce(f"mfma running scale gate_up fmt={fmt} I={I} K={K} N={N} seed={seed}")
+    h = qmm.gate_up_silu(fmt, dev(rg), dev(ru), dev(x), I, K, variant=MFMA)
+    torch.cuda.synchronize()
+    rows = np.arange(I) if I <= 512 else np.r_[0:256, I - 256:I]
+    h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, x, I, K, rows=rows)
+    check_swiglu(h.cpu().numpy().reshape(N, I)[:, rows], h_ref, g, u, Sg, Su,
+                 f"mfma running scale gate_up fmt={fmt} I={I} K={K} N={N}")
