@@ -102,26 +102,36 @@ int check_ws(const void* ws, int64_t ws_bytes, int64_t need) {
     return QMM_OK;
 }
 
-// VALU or MFMA variant for N tokens over `wbytes` of weights (`gated`: the gate+up
-// product), measured on MI355X at the Llama-3-8B projection shapes with the weights
-// streamed from HBM.  The block formats' VALU kernels take up to 4 tokens per weight
-// pass, so from 5 tokens they read the weights twice and the single-pass MFMA kernel
-// wins on every shape (by 1.3-1.9x).  At 4 tokens the MFMA kernel wins or ties from
-// about 32 MB of weights (e.g. the Q4_0 LM head 82 vs 87 us, the Q5_1 down projection
-// 20 vs 30 us) and loses on smaller matrices, whose two launches and split-K cost
-// more than the pass -- except the gate+up product of Q4_1 / Q5_0 / Q5_1, whose VALU
-// kernel stays ahead (26-29 vs 28-31 us at 2 x 14336 x 4096).  At 2-3 tokens the VALU
-// kernel wins, but for the Q8_0 LM head at 3 tokens (MFMA 113 vs 120 us; from 256 MB).
-// F16 (sliced VALU kernel against the tiled GEMM): MFMA from 4 tokens.
-int choose_variant(int fmt, int64_t wbytes, int64_t N, bool gated) {
-    if (fmt == QMM_F16) return N >= 4 ? QMM_VARIANT_MFMA : QMM_VARIANT_VALU;
+// VALU or MFMA variant for N tokens over `wbytes` of weights with rows of K (`gated`:
+// the gate+up product), measured on MI355X at the Llama-3-8B projection shapes (QKV
+// 6144 x 4096, O 4096 x 4096, gate+up 2 x 14336 x 4096, down 4096 x 14336, LM head
+// 128256 x 4096) with the weights streamed from HBM; the ratios below are MFMA time /
+// VALU time.
+//   Block formats.  The VALU kernels take up to 4 tokens per weight pass, so from 5
+//   tokens they read the weights twice and the single-pass MFMA kernel wins on every
+//   shape (by 1.3-2x).  At 4 tokens: long rows (K >= 8192, the down projection) go to
+//   MFMA (0.67-0.97: x of 4 such tokens does not fit the DMA-fed kernel's LDS, and the
+//   register-staged kernel is slower); gate+up stays VALU (0.96-1.11), and so does
+//   Q5_0, whose MFMA decode costs the most (LM head 1.12); the rest is MFMA from 256
+//   MiB (LM heads 0.91-1.01) and VALU below (QKV, O 1.21-1.32).  At 2-3 tokens VALU
+//   (1.04-1.71; one tie, Q5_1 gate+up at 3 tokens 0.96).
+//   F16 (its MFMA variant is the tiled GEMM): MFMA from 5 tokens; from 2 tokens on
+//   long rows over 32 MiB (down 0.72-0.85); at 4 tokens from 64 MiB (gate+up 0.94, LM
+//   head 0.65), at 3 from 256 MiB (LM head 0.94); VALU otherwise (QKV, O 1.23-1.37).
+int choose_variant(int fmt, int64_t wbytes, int64_t K, int64_t N, bool gated) {
+    constexpr int64_t MiB = int64_t{1} << 20;
     if (N >= 5) return QMM_VARIANT_MFMA;
-    if (N == 4) {
-        const bool extra = fmt == QMM_Q4_1 || fmt == QMM_Q5_0 || fmt == QMM_Q5_1;
-        if (gated && extra) return QMM_VARIANT_VALU;
-        return wbytes >= (int64_t{32} << 20) ? QMM_VARIANT_MFMA : QMM_VARIANT_VALU;
+    if (fmt == QMM_F16) {
+        if (N >= 2 && K >= 8192 && wbytes >= 32 * MiB) return QMM_VARIANT_MFMA;
+        if (N == 4 && wbytes >= 64 * MiB) return QMM_VARIANT_MFMA;
+        if (N == 3 && wbytes >= 256 * MiB) return QMM_VARIANT_MFMA;
+        return QMM_VARIANT_VALU;
     }
-    if (N == 3 && fmt == QMM_Q8_0 && wbytes >= (int64_t{256} << 20)) return QMM_VARIANT_MFMA;
+    if (N == 4) {
+        if (K >= 8192 && wbytes >= 16 * MiB) return QMM_VARIANT_MFMA;
+        if (gated || fmt == QMM_Q5_0) return QMM_VARIANT_VALU;
+        return wbytes >= 256 * MiB ? QMM_VARIANT_MFMA : QMM_VARIANT_VALU;
+    }
     return QMM_VARIANT_VALU;
 }
 
@@ -211,7 +221,7 @@ int qmm_gemv_choose(int fmt, int64_t M, int64_t K, int64_t N) {
     if (st) return st;
     int64_t wb;
     if (!weight_bytes(fmt, M, K, false, &wb)) return QMM_ERR_OVERFLOW;
-    return choose_variant(fmt, wb, N, false);
+    return choose_variant(fmt, wb, K, N, false);
 }
 
 int64_t qmm_workspace_size(int op, int fmt, int64_t M, int64_t K, int64_t N, int variant) {
@@ -224,7 +234,7 @@ int64_t qmm_workspace_size(int op, int fmt, int64_t M, int64_t K, int64_t N, int
             if (variant == QMM_VARIANT_AUTO) {
                 int64_t wb;
                 if (!weight_bytes(fmt, M, K, gated, &wb)) return QMM_ERR_OVERFLOW;
-                variant = choose_variant(fmt, wb, N, gated);
+                variant = choose_variant(fmt, wb, K, N, gated);
             }
             if (variant == QMM_VARIANT_VALU) return 0;
             if (variant != QMM_VARIANT_MFMA) return QMM_ERR_VARIANT;
@@ -270,7 +280,7 @@ int qmm_gate_up_silu_variant(int fmt, const void* Wg, const void* Wu, const floa
     if (variant == QMM_VARIANT_AUTO) {
         int64_t wb;
         if (!weight_bytes(fmt, I, K, true, &wb)) return QMM_ERR_OVERFLOW;
-        variant = choose_variant(fmt, wb, N, true);
+        variant = choose_variant(fmt, wb, K, N, true);
     }
     auto s = static_cast<hipStream_t>(stream);
     if (variant == QMM_VARIANT_VALU) return from_hip(qmm::launch_gemv_valu(fmt, Wg, Wu, x, h, I, K, N, s));

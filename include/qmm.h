@@ -232,11 +232,13 @@ int qmm_gemv_variant(int fmt, const void* W, const float* x, float* y,
  * or a negative qmm_status for invalid sizes.  Host-only.  The GEMV/GEMM split
  * by token count follows "llama.cpp Metal ...", section 3.2 (mat-vec for few
  * tokens, the tiled matrix-matrix kernel above a threshold); the thresholds here
- * are measured on MI355X: the block formats switch to MFMA from 5 tokens, at 4
- * tokens when the weights reach 32 MB, and Q8_0 at 3 tokens from 256 MB; F16 from
- * 4 tokens.  (qmm_gate_up_silu applies the same rule to the combined gate and up
- * weights, except that Q4_1 / Q5_0 / Q5_1 stay on the register-decode variant at
- * 4 tokens.)
+ * are measured on MI355X at the Llama-3-8B projection shapes: the block formats
+ * switch to MFMA from 5 tokens, and at 4 tokens for rows of K >= 8192 over at least
+ * 16 MiB of weights and, Q5_0 excepted, for matrices of 256 MiB or more; F16 (whose
+ * MFMA variant is the tiled GEMM) from 5 tokens, from 2 for rows of K >= 8192 over
+ * at least 32 MiB, at 4 from 64 MiB and at 3 from 256 MiB.  (qmm_gate_up_silu
+ * applies the same rule to the combined gate and up weights, except that the block
+ * formats' short rows stay on the register-decode variant at 4 tokens.)
  */
 int qmm_gemv_choose(int fmt, int64_t M, int64_t K, int64_t N);
 

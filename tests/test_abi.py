@@ -180,25 +180,32 @@ def test_variant_choice():
         assert L.qmm_gemv_choose(fmt, 4096, 4096, 4096) == 2
         v = [L.qmm_gemv_choose(fmt, 4096, 4096, n) for n in range(1, 65)]
         assert v == sorted(v), "the choice must switch once, from VALU to MFMA"
-    # Measured thresholds: Q8_0 / Q4_0 from 5 tokens, or 4 tokens over >= 32 MB of weights.
+    # Measured thresholds (MI355X, Llama-3-8B shapes).  Block formats: MFMA from 5
+    # tokens; at 4 tokens on long rows (the down projection) and on the LM head
+    # (>= 256 MiB) except Q5_0; VALU at 2-3 tokens.
     for fmt in (2, 8):
         assert L.qmm_gemv_choose(fmt, 4096, 4096, 4) == 1       # 17.8 / 9.4 MB
         assert L.qmm_gemv_choose(fmt, 4096, 4096, 5) == 2
         assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == 2     # LM head
+        assert L.qmm_gemv_choose(fmt, 128256, 4096, 3) == 1
         assert L.qmm_gemv_choose(fmt, 128256, 4096, 2) == 1
-    assert L.qmm_gemv_choose(1, 4096, 4096, 4) == 2
-    assert L.qmm_gemv_choose(1, 4096, 4096, 3) == 1
-    assert L.qmm_gemv_choose(5, 4096, 4096, 1) == E_FMT
-    # Q4_1 / Q5_0 / Q5_1 follow the same rule for the plain product.
+        assert L.qmm_gemv_choose(fmt, 4096, 14336, 4) == 2      # down projection
+        assert L.qmm_gemv_choose(fmt, 4096, 14336, 3) == 1
+        assert L.qmm_gemv_choose(fmt, 14336, 4096, 3) == 1
     for fmt in (3, 6, 7):
         assert [L.qmm_gemv_choose(fmt, 4096, 4096, n) for n in (1, 3, 4, 5, 64)] == [1, 1, 1, 2, 2]
-        assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == 2
         assert L.qmm_gemv_choose(fmt, 4096, 14336, 4) == 2
         assert L.qmm_gemv_choose(fmt, 128256, 4096, 3) == 1
-    # Q8_0 at 3 tokens from 256 MB (the LM head), not below.
-    assert L.qmm_gemv_choose(8, 128256, 4096, 3) == 2
-    assert L.qmm_gemv_choose(8, 14336, 4096, 3) == 1
-    assert L.qmm_gemv_choose(2, 128256, 4096, 3) == 1
+        assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == (1 if fmt == 6 else 2)
+    # Long rows of few rows: not the MFMA kernel (under 16 MiB of weights).
+    assert L.qmm_gemv_choose(8, 512, 14336, 4) == 1
+    # F16 (MFMA = the tiled GEMM): from 5 tokens; from 2 on long rows over 32 MiB; at 4
+    # from 64 MiB; at 3 from 256 MiB.
+    assert [L.qmm_gemv_choose(1, 4096, 4096, n) for n in (2, 3, 4, 5)] == [1, 1, 1, 2]
+    assert [L.qmm_gemv_choose(1, 4096, 14336, n) for n in (1, 2, 3)] == [1, 2, 2]
+    assert [L.qmm_gemv_choose(1, 14336, 4096, n) for n in (3, 4)] == [1, 2]
+    assert [L.qmm_gemv_choose(1, 128256, 4096, n) for n in (2, 3)] == [1, 2]
+    assert L.qmm_gemv_choose(5, 4096, 4096, 1) == E_FMT
     assert L.qmm_gemv_choose(8, 4096, 100, 1) == E_SHAPE
     assert L.qmm_gemv_variant(8, A16, A16, A16 + 1, 4, 64, 1, 9, None, 0, None) == E_ALIGN
     assert L.qmm_gemv_variant(8, A16, A16, A16, 4, 64, 1, 9, None, 0, None) == E_VAR
