@@ -485,8 +485,9 @@ def timed_parity(oracle, si):
     the first SB_CHECK_ROWS rows of every small-batch call; the first PREFILL_CHECK_ROWS
     weight rows of every prefill case over all tokens and, for the expand-then-GEMM
     cases, over the first TOKEN_CHECK tokens, with the fp16 expansion compared bit for
-    bit; and the first 16 gathered rows of every row gather, bit for bit (NaN where the
-    random scale bytes make one).  Each output's error is divided by its bound (2e-3 S
+    bit; the first 16 gathered rows of every row gather, bit for bit (NaN where the
+    random scale bytes make one); and the first DECODE_CHECK_ROWS rows of every launch
+    of the 8-way tensor-parallel shard step (down and gate+up from the GPU's own h).  Each output's error is divided by its bound (2e-3 S
     + 1e-6; the SwiGLU and residual bounds where they apply): every ratio must be <= 1."""
     L = si.LLAMA3_8B
     H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
@@ -583,6 +584,20 @@ def timed_parity(oracle, si):
                   rec["w16"].view(np.uint16), oracle.expand_f16_ref(fmt, rec["w"], PREFILL_CHECK_ROWS, K).view(np.uint16))
             y, S = oracle.matmul_ref(fmt, rec["w"], rec["x"], PREFILL_CHECK_ROWS, K)
             take(label + " GEMM", rec["y"], y, oracle.tol_linear(S))
+        elif key[0] == "tp8":
+            _, fmt = key
+            name = f"tp8 shard {si.FMT_NAMES[fmt]}"
+            dims, w = rec["dims"], rec["w"]
+            for part, wk, xin in (("qkv", "qkv", rec["x"]), ("o", "o", rec["xo"]), ("down", "d", rec["h"]),
+                                  ("lm_head", "lm", rec["x"])):
+                M, K = dims[part]
+                R = min(M, DECODE_CHECK_ROWS)
+                y, S = oracle.matmul_ref(fmt, w[wk], xin, R, K)
+                take(f"{name} {part}", np.reshape(rec["y"][part], -1)[:R], y[0], oracle.tol_linear(S[0]))
+            I8, H8 = dims["gate_up"]
+            R = min(I8, DECODE_CHECK_ROWS)
+            hr, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, w["g"], w["u"], rec["x"], R, H8)
+            take(f"{name} gate_up", np.reshape(rec["h"], -1)[:R], hr[0], oracle.tol_swiglu(g[0], u[0], Sg[0], Su[0]))
         elif key[0] == "get_rows":
             _, fmt, nr = key
             m = rec["out"].shape[0]  # 16 gathered rows, or every row of a smaller gather
@@ -595,7 +610,8 @@ def timed_parity(oracle, si):
             "what": "single 576x576 GEMV whole; the first rows of every 8B decode launch (Q8_0, Q4_0, Q4_1, Q5_0, "
                     "Q5_1) and of the fused step; the SmolLM2-135M step's last layer and LM-head rows; the first "
                     "rows of every small-batch call; the first rows of every prefill and expand-then-GEMM case "
-                    "(the expansion bit for bit); the first 16 rows of every row gather, bit for bit"}
+                    "(the expansion bit for bit); the first 16 rows of every row gather, bit for bit; the first rows of "
+                    "every launch of the 8-way tensor-parallel shard step"}
 
 
 def smollm2_step(torch, qmm, si, steps, trials):
@@ -793,6 +809,89 @@ def fused_decode(torch, qmm, si, fmts, steps):
         rec = capture_decode(qmm, si, fmt, f)
         rec.update(r0=r0, r2=resid.cpu().numpy(), gamma=gamma.cpu().numpy(), eps=eps)
         TIMED_OUT[("fused", fmt)] = rec
+    return out
+
+
+def tp8_shard_decode(torch, qmm, si, trials, reps=20):
+    """One GPU's share of the 8B decode step under 8-way tensor parallelism, Q8_0 and
+    Q4_0, N = 1: QKV (768 of 6144 rows), gate+up+SwiGLU (1792 of 14336) and the LM head
+    (16032 of 128256) split by output rows; O (K = 512 of 4096) and down (K = 1792 of
+    14336, fed by this GPU's h) split by K.  The collectives between them are not built
+    here.  Weight sets (random bytes with finite scales) rotate through >= 512 MB, one set
+    per step.  Reported: the whole step, launched eagerly and replayed as a HIP graph
+    (median of `trials`, each over one pass through the sets), and each launch alone
+    (a graph of `reps` rotated calls, median of `trials`)."""
+    L = si.LLAMA3_8B
+    H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
+    q8, o8, i8, v8 = Q // 8, H // 8, I // 8, V // 8
+    dev = torch.device("cuda")
+    out = {}
+    for fmt in (si.FMT_Q8_0, si.FMT_Q4_0):
+        rb = lambda K: qmm.qmm_row_bytes(fmt, K)
+        shapes = {"qkv": (q8, H), "o": (H, o8), "g": (i8, H), "u": (i8, H), "d": (H, i8), "lm": (v8, H)}
+        set_bytes = sum(M * rb(K) for M, K in shapes.values())
+        copies = max(1, -(-POOL_BYTES // set_bytes))
+        bb = rb(32)
+
+        def rand_w(M, K):
+            w = torch.randint(0, 256, (M * rb(K),), dtype=torch.uint8, device=dev)
+            w.view(-1, bb)[:, 1] &= 0x3B  # finite block scales
+            return w
+        sets = [{k: rand_w(M, K) for k, (M, K) in shapes.items()} for _ in range(copies)]
+        x = torch.from_numpy(si.activations(1, H, 4600 + fmt)).to(dev)
+        xo = torch.from_numpy(si.activations(1, o8, 4601 + fmt)).to(dev)
+        y_qkv, y_o = torch.empty(q8, device=dev), torch.empty(H, device=dev)
+        h, y_d, logits = torch.empty(i8, device=dev), torch.empty(H, device=dev), torch.empty(v8, device=dev)
+        parts = [
+            ("qkv", q8 * rb(H) + 4 * H + 4 * q8, lambda w: qmm.qmm_gemv(fmt, w["qkv"], x, y_qkv, q8, H, 1)),
+            ("o", H * rb(o8) + 4 * o8 + 4 * H, lambda w: qmm.qmm_gemv(fmt, w["o"], xo, y_o, H, o8, 1)),
+            ("gate_up", 2 * i8 * rb(H) + 4 * H + 4 * i8,
+             lambda w: qmm.qmm_gate_up_silu(fmt, w["g"], w["u"], x, h, i8, H, 1)),
+            ("down", H * rb(i8) + 4 * i8 + 4 * H, lambda w: qmm.qmm_gemv(fmt, w["d"], h, y_d, H, i8, 1)),
+            ("lm_head", v8 * rb(H) + 4 * H + 4 * v8, lambda w: qmm.qmm_gemv(fmt, w["lm"], x, logits, v8, H, 1)),
+        ]
+        step_bytes = float(sum(b for _, b, _ in parts))
+
+        def step(i):
+            for _, _, fn in parts:
+                fn(sets[i % copies])
+
+        def one_pass():
+            for i in range(copies):
+                step(i)
+        for i in range(copies):
+            step(i)
+        ms_eager, _ = median_trials(torch, one_pass, trials, copies)
+        g = graph_of(torch, one_pass)
+        g.replay()
+        ms_graph, _ = median_trials(torch, g.replay, trials, copies)
+        del g
+        per = {}
+        for name, b, fn in parts:
+            def body(fn=fn):
+                for i in range(reps):
+                    fn(sets[i % copies])
+            gp = graph_of(torch, body)
+            gp.replay()
+            ms, _ = median_trials(torch, gp.replay, trials, reps)
+            per[name] = {"us": round(ms * 1e3, 2), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": int(b)}
+            del gp
+        # The oracle leg's re-check: one more step on set 0, its outputs and inputs.
+        step(0)
+        w0 = sets[0]
+        TIMED_OUT[("tp8", fmt)] = {
+            "x": x.cpu().numpy(), "xo": xo.cpu().numpy(), "h": h.cpu().numpy(),
+            "y": {"qkv": y_qkv.cpu().numpy(), "o": y_o.cpu().numpy(), "down": y_d.cpu().numpy(),
+                  "lm_head": logits[:DECODE_CHECK_ROWS].cpu().numpy()},
+            "w": {k: w0[k][:min(shapes[k][0], DECODE_CHECK_ROWS) * rb(shapes[k][1])].cpu().numpy() for k in shapes},
+            "dims": {"qkv": (q8, H), "o": (H, o8), "gate_up": (i8, H), "down": (H, i8), "lm_head": (v8, H)}}
+        out[si.FMT_NAMES[fmt]] = {
+            "step_us": round(ms_eager * 1e3, 2), "step_GBps": round(step_bytes / (ms_eager * 1e-3) / 1e9, 1),
+            "graph_step_us": round(ms_graph * 1e3, 2),
+            "graph_step_GBps": round(step_bytes / (ms_graph * 1e-3) / 1e9, 1),
+            "step_bytes": int(step_bytes), "weight_sets": copies, "launches": per}
+        del sets
+        torch.cuda.empty_cache()
     return out
 
 
@@ -1099,6 +1198,7 @@ def main():
         line["expand_then_gemm"] = expand_gemm(torch, qmm, si)
         line["get_rows"] = get_rows_bench(torch, qmm, si)
         line["more_formats"] = more_formats(torch, qmm, si, max(10, args.steps))
+        line["tp8_shard_decode"] = tp8_shard_decode(torch, qmm, si, args.trials)
     if not (args.no_prefill or args.no_small_batch):
         line["ceilings"] = ceilings(torch)
     if not args.no_cpu:

@@ -182,3 +182,38 @@ def test_timed_parity_decode_fused_expand_and_gather_records():
     fused["r2"][5] += 2.0 * float(oracle.tol_residual(S1, r1)[5] + oracle.tol_residual(S2, r2)[5])
     assert not bench.timed_parity(oracle, si)["ok"]
     bench.TIMED_OUT.clear()
+
+
+def test_timed_parity_tp8_shard_records():
+    """Records of the 8-way tensor-parallel shard step built from the oracle (no GPU)
+    pass; a down output moved by twice its bound fails, and so does a gate+up output
+    computed from the wrong operand order (silu of the up sums)."""
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+    bench.TIMED_OUT.clear()
+    L = si.LLAMA3_8B
+    H, I, V, Q = L["hidden"], L["intermediate"], L["vocab"], si.qkv_rows(L)
+    q8, o8, i8, v8 = Q // 8, H // 8, I // 8, V // 8
+    fmt, R = si.FMT_Q8_0, bench.DECODE_CHECK_ROWS
+    dims = {"qkv": (q8, H), "o": (H, o8), "gate_up": (i8, H), "down": (H, i8), "lm_head": (v8, H)}
+    kdim = {"qkv": H, "o": o8, "g": H, "u": H, "d": i8, "lm": H}
+    w = {k: si.weights(fmt, R, K, 60 + i) for i, (k, K) in enumerate(kdim.items())}
+    x, xo = si.activations(1, H, 70)[0], si.activations(1, o8, 71)[0]
+    hR, g, u, _, _ = oracle.gate_up_silu_ref(fmt, w["g"], w["u"], x, R, H)
+    h = np.concatenate([hR[0], np.zeros(i8 - R)]).astype(np.float32)
+    lin = lambda k, xin, K: oracle.matmul_ref(fmt, w[k], xin, R, K)[0][0].astype(np.float32)
+    rec = {"x": x, "xo": xo, "h": h, "w": w, "dims": dims,
+           "y": {"qkv": lin("qkv", x, H), "o": lin("o", xo, o8), "down": lin("d", h, i8), "lm_head": lin("lm", x, H)}}
+    bench.TIMED_OUT[("tp8", fmt)] = rec
+    r = bench.timed_parity(oracle, si)
+    assert r["ok"] and r["outputs_checked"] == 5 * R, r
+    S = oracle.matmul_ref(fmt, w["d"], h, R, i8)[1][0]
+    rec["y"]["down"][7] += 2.0 * float(oracle.tol_linear(S)[7])
+    assert not bench.timed_parity(oracle, si)["ok"]
+    rec["y"]["down"] = lin("d", h, i8)
+    assert bench.timed_parity(oracle, si)["ok"]
+    rec["h"] = np.concatenate([(oracle.silu(u[0]) * g[0]), np.zeros(i8 - R)]).astype(np.float32)
+    rec["y"]["down"] = lin("d", rec["h"], i8)  # down stays consistent with the (wrong) h it consumed
+    assert not bench.timed_parity(oracle, si)["ok"]
+    bench.TIMED_OUT.clear()

@@ -7,6 +7,9 @@
 * Batched decode N in {1, 2, 4, 8, 16}, F16 / Q8_0 / Q4_0, both GEMV variants (sampled rows).
 * Prefill GEMM 4096->14336 and 14336->4096, T in {128, 2048, 4096}, Q8_0 / Q4_0 (sampled rows,
   all tokens), and the fused gate+up GEMM at 4096 -> 2 x 14336.
+* One GPU's share of the Llama-3-8B decode projections under 8-way tensor parallelism (QKV,
+  gate+up and LM head split by output rows, O and down by K), every block format, one token
+  and (Q8_0, Q4_0) eight (every output; LM-head shard on sampled rows).
 """
 import numpy as np
 import pytest
@@ -144,3 +147,46 @@ def test_prefill_gate_up_gemm_sampled(fmt):
     rows = sample_rows(I, 40, 6)
     h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, X, I, K, rows=rows)
     check_swiglu(H[:, rows], h_ref, g, u, Sg, Su, "gemm gate_up")
+
+
+# One GPU's share at 8-way tensor parallelism: column-parallel QKV (768 of 6144 rows),
+# gate+up (1792 of 14336) and LM head (16032 of 128256 rows); row-parallel O (K = 512 of
+# 4096) and down (K = 1792 of 14336).
+TP8 = [("qkv", si.qkv_rows(L8) // 8, L8["hidden"]), ("o", L8["hidden"], L8["hidden"] // 8),
+       ("down", L8["hidden"], L8["intermediate"] // 8), ("lm_head", L8["vocab"] // 8, L8["hidden"])]
+BLOCK_FMTS = [si.FMT_Q8_0, si.FMT_Q4_0, si.FMT_Q4_1, si.FMT_Q5_0, si.FMT_Q5_1]
+
+
+@pytest.mark.parametrize("fmt", BLOCK_FMTS, ids=str)
+def test_tp8_shard_decode(fmt):
+    I8, H = L8["intermediate"] // 8, L8["hidden"]
+    for k, (name, M, K) in enumerate(TP8):
+        seed = 3900 + 10 * fmt + k
+        raw = si.weights(fmt, M, K, seed)
+        x = si.activations(1, K, seed + 1)
+        announce(f"tp8 shard {name} fmt={fmt} M={M} K={K}")
+        y = qmm.gemv(fmt, dev(raw), dev(x), M, K)
+        torch.cuda.synchronize()
+        rows = sample_rows(M, 300, seed) if M > 8192 else np.arange(M)
+        r, S = oracle.matmul_ref(fmt, raw, x, M, K, rows=rows)
+        check_linear(y.cpu().numpy()[:, rows], r, S, f"tp8 {name} fmt={fmt}")
+    rg, ru = si.weights(fmt, I8, H, 3950 + fmt), si.weights(fmt, I8, H, 3951 + fmt)
+    x = si.activations(1, H, 3952)
+    announce(f"tp8 shard gate_up fmt={fmt} I={I8}")
+    h = qmm.gate_up_silu(fmt, dev(rg), dev(ru), dev(x), I8, H)
+    torch.cuda.synchronize()
+    h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, x, I8, H)
+    check_swiglu(h.cpu().numpy(), h_ref, g, u, Sg, Su, f"tp8 gate_up fmt={fmt}")
+
+
+@pytest.mark.parametrize("fmt", [si.FMT_Q8_0, si.FMT_Q4_0], ids=FID.get)
+@pytest.mark.parametrize("name,M,K", TP8[:3], ids=[n for n, _, _ in TP8[:3]])
+def test_tp8_shard_eight_tokens(fmt, name, M, K):
+    seed = 3960 + 10 * fmt + M % 7
+    raw = si.weights(fmt, M, K, seed)
+    x = si.activations(8, K, seed + 1)
+    announce(f"tp8 shard {name} N=8 fmt={fmt} M={M} K={K}")
+    y = qmm.gemv(fmt, dev(raw), dev(x), M, K)
+    torch.cuda.synchronize()
+    r, S = oracle.matmul_ref(fmt, raw, x, M, K)
+    check_linear(y.cpu().numpy(), r, S, f"tp8 {name} N=8 fmt={fmt}")
