@@ -983,8 +983,9 @@ def get_rows_bench(torch, qmm, si, reps=20):
 
 def ceilings(torch):
     """Achievable ceilings measured with vendor code (never linked into qmm): a 2 GiB
-    device-to-device copy (bytes read + bytes written per second) and fp16
-    torch.matmul at the prefill shapes."""
+    device-to-device copy (bytes read + bytes written per second), a 2 GiB streaming
+    read (torch's sum and max reductions, bytes read per second, the faster of the
+    two) and fp16 torch.matmul at the prefill shapes."""
     dev = torch.device("cuda")
     a = torch.ones(1 << 29, device=dev)  # 2 GiB fp32
     b = torch.empty_like(a)
@@ -998,7 +999,19 @@ def ceilings(torch):
     e1.record()
     torch.cuda.synchronize()
     copy_gbs = 2 * (1 << 31) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
-    del a, b
+    del b
+    read_gbs = 0.0
+    for red in (torch.sum, torch.amax):
+        for _ in range(3):
+            red(a)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            red(a)
+        e1.record()
+        torch.cuda.synchronize()
+        read_gbs = max(read_gbs, (1 << 31) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9)
+    del a
     mm = []
     for (M, K) in ((14336, 4096), (4096, 14336)):
         B = torch.randn(M, K, device=dev).half()
@@ -1014,7 +1027,8 @@ def ceilings(torch):
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / 10
             mm.append({"M": M, "K": K, "T": T, "TFLOPs": round(2.0 * T * M * K / (ms * 1e-3) / 1e12, 1)})
-    return {"copy_read_plus_write_GBps": round(copy_gbs, 1), "torch_fp16_matmul": mm}
+    return {"copy_read_plus_write_GBps": round(copy_gbs, 1), "read_only_GBps": round(read_gbs, 1),
+            "torch_fp16_matmul": mm}
 
 
 # Sources the dominant decode kernel is built from; its counter-derived traffic is
