@@ -26,7 +26,7 @@ __all__ = [
     "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16", "qmm_rmsnorm_gemv", "qmm_rmsnorm_gate_up_silu",
     "qmm_gemv_add", "QMM_ERR_ARG", "QMM_ERR_WORKSPACE", "QMM_WORKSPACE_ALIGN", "qmm_workspace_size",
     "QMM_OP_GEMV", "QMM_OP_GATE_UP_SILU", "QMM_OP_GEMM", "QMM_OP_GEMM_GATE_UP_SILU", "qmm_gemm_noalloc",
-    "QMM_ERR_SCRATCH", "QMM_NOALLOC_SCRATCH_BYTES",
+    "QMM_ERR_SCRATCH", "QMM_NOALLOC_SCRATCH_BYTES", "qmm_stream_read", "QMM_STREAM_READ_BLOCKS",
     "gemv", "get_rows", "expand_f16", "rmsnorm_gemv", "rmsnorm_gate_up_silu", "gemv_add", "gate_up_silu", "gemm", "gemm_gate_up_silu", "dequant",
 ]
 
@@ -36,6 +36,7 @@ QMM_ERR_ARG = -8
 QMM_ERR_WORKSPACE = -9
 QMM_ERR_SCRATCH = -10
 QMM_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+QMM_STREAM_READ_BLOCKS = 8192
 QMM_WORKSPACE_ALIGN = 256
 QMM_OP_GEMV, QMM_OP_GATE_UP_SILU, QMM_OP_GEMM, QMM_OP_GEMM_GATE_UP_SILU = 1, 2, 3, 4
 
@@ -69,6 +70,7 @@ _SIGS = {
     "qmm_gemm": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]),
     "qmm_gemm_gate_up_silu": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp]),
     "qmm_gemm_noalloc": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "qmm_stream_read": (_i32, [_vp, _i64, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -217,6 +219,10 @@ def qmm_gemm(fmt, W, X, Y, M, K, T, workspace=None, workspace_bytes=None, stream
 
 def qmm_gemm_noalloc(fmt, W, X, Y, M, K, T, stream=None) -> None:
     _check(_lib.qmm_gemm_noalloc(fmt, _ptr(W), _ptr(X), _ptr(Y), M, K, T, _stream(stream)), "qmm_gemm_noalloc")
+
+
+def qmm_stream_read(buf, nbytes, sink, stream=None) -> None:
+    _check(_lib.qmm_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "qmm_stream_read")
 
 
 def qmm_gemm_gate_up_silu(fmt, Wg, Wu, X, H, I, K, T, workspace=None, workspace_bytes=None, stream=None) -> None:

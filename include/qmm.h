@@ -337,6 +337,24 @@ int qmm_gemm_gate_up_silu(int fmt, const void* Wg, const void* Wu, const void* X
                           int64_t I, int64_t K, int64_t T, void* workspace, int64_t workspace_bytes,
                           void* stream);
 
+/* Workgroups of qmm_stream_read: the length of its sink array. */
+#define QMM_STREAM_READ_BLOCKS 8192
+
+/*
+ * Streaming-read reference, a measurement aid rather than a step of the method: reads
+ * `bytes` of device memory at buf with the 16-byte non-temporal loads of the
+ * single-token decode stream and stores one word per workgroup, sink[b] = the XOR of
+ * the 32-bit words of the b-th of QMM_STREAM_READ_BLOCKS ranges of 16-byte units, each
+ * ceil(units / QMM_STREAM_READ_BLOCKS) long (the last ones shorter or empty: 0).
+ * bytes / elapsed time is the read rate a plain kernel reaches on the GPU, the
+ * achievable ceiling against which the decode GEMVs' weight streams are read beside
+ * the nominal HBM peak.  buf 16-byte aligned, bytes a positive multiple of 16, sink
+ * QMM_STREAM_READ_BLOCKS uint32 of device memory, 4-byte aligned; otherwise
+ * QMM_ERR_NULL, QMM_ERR_SHAPE or QMM_ERR_ALIGN before any launch.  Asynchronous on
+ * stream like every other call.
+ */
+int qmm_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

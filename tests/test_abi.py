@@ -31,7 +31,8 @@ def test_header_declares_expected_api():
         "qmm_version", "qmm_strerror", "qmm_row_bytes", "qmm_dequant", "qmm_gemv", "qmm_gemv_variant",
         "qmm_gemv_choose", "qmm_gate_up_silu", "qmm_gate_up_silu_variant", "qmm_gemm",
         "qmm_gemm_gate_up_silu", "qmm_get_rows", "qmm_expand_f16", "qmm_rmsnorm_gemv",
-        "qmm_rmsnorm_gate_up_silu", "qmm_gemv_add", "qmm_workspace_size", "qmm_gemm_noalloc"])
+        "qmm_rmsnorm_gate_up_silu", "qmm_gemv_add", "qmm_workspace_size", "qmm_gemm_noalloc",
+        "qmm_stream_read"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -299,3 +300,18 @@ def test_gemm_workspace_fits_the_noalloc_scratch():
                 for K in (4096, 14336):
                     worst = max(worst, W(OP_GEMM, fmt, M, K, T, AUTO))
     assert 0 < worst <= qmm.QMM_NOALLOC_SCRATCH_BYTES
+
+
+def test_stream_read_validation():
+    """The streaming-read reference checks its arguments before any HIP call (the fake
+    addresses are never touched)."""
+    L = qmm._lib
+    assert L.qmm_stream_read(None, 16, A16, None) == E_NULL
+    assert L.qmm_stream_read(A16, 16, None, None) == E_NULL
+    assert L.qmm_stream_read(A16, 0, A16, None) == E_SHAPE
+    assert L.qmm_stream_read(A16, -16, A16, None) == E_SHAPE
+    assert L.qmm_stream_read(A16, 24, A16, None) == E_SHAPE
+    assert L.qmm_stream_read(A16 + 8, 16, A16, None) == E_ALIGN
+    assert L.qmm_stream_read(A16, 16, A16 + 2, None) == E_ALIGN
+    assert qmm.QMM_STREAM_READ_BLOCKS == int(re.search(r"#define QMM_STREAM_READ_BLOCKS (\d+)",
+                                                       open(HEADER).read()).group(1))

@@ -439,3 +439,27 @@ def test_mfma_running_token_scale_gate_up(fmt, I, K, N):
     h_ref, g, u, Sg, Su = oracle.gate_up_silu_ref(fmt, rg, ru, x, I, K, rows=rows)
     check_swiglu(h.cpu().numpy().reshape(N, I)[:, rows], h_ref, g, u, Sg, Su,
                  f"mfma running scale gate_up fmt={fmt} I={I} K={K} N={N}")
+
+
+# ------------------------------------------------------------- streaming-read reference
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 8191, 16 * 8193, (1 << 20) + 48, (64 << 20) + 16 * 12345])
+def test_stream_read_fold(nbytes):
+    """qmm_stream_read's per-workgroup XOR folds, bit for bit: the ranges of 16-byte
+    units, ceil(units / blocks) long, including sizes that leave trailing workgroups
+    with empty ranges (their word is 0) and ragged last ranges."""
+    g = np.random.default_rng(nbytes % 1000)
+    buf = g.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    B = qmm.QMM_STREAM_READ_BLOCKS
+    sink = torch.full((B,), 0xDEADBEEF & 0x7FFFFFFF, dtype=torch.int32, device="cuda")
+    announce(f"stream_read fold bytes={nbytes}")
+    qmm.qmm_stream_read(torch.from_numpy(buf.view(np.int32)).cuda(), nbytes, sink)
+    torch.cuda.synchronize()
+    n = nbytes // 16
+    per = -(-n // B)
+    words = buf.reshape(n, 4)
+    want = np.zeros(B, dtype=np.uint32)
+    for b in range(B):
+        lo, hi = min(b * per, n), min((b + 1) * per, n)
+        if hi > lo:
+            want[b] = np.bitwise_xor.reduce(words[lo:hi].reshape(-1))
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
