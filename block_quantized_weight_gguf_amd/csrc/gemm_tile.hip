@@ -531,7 +531,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_tiles(const float4* __restr
                                                            int nsplit, int ntiles, int vec) {
     constexpr int B = 8;
     constexpr int NJ = BN / 16;
-    constexpr int NI = 2;                       // fragments per wave along the weight rows
+    constexpr int NI = GT_BM / GT_WAVES / 16;   // fragments per wave along the weight rows
     constexpr int RW = GT_BM / GT_WAVES;        // weight rows per wave
     constexpr int PER_TILE = GT_WAVES * NI * NJ * 64;
     constexpr int NOUT = GATED ? NI / 2 : NI;   // output fragments per wave
@@ -621,7 +621,7 @@ static void launch_reduce_tiles_t(const float* P, float* Y, const float* tscale,
                                   hipStream_t s) {
     const int64_t rows_per_tile = GATED ? GT_BM / 2 : GT_BM;
     const int64_t ntiles = ((M + rows_per_tile - 1) / rows_per_tile) * ((T + BN - 1) / BN);
-    const int64_t n = ntiles * GT_WAVES * (GATED ? 1 : 2) * (BN / 16) * 64;
+    const int64_t n = ntiles * GT_WAVES * (GT_BM / GT_WAVES / 16 / (GATED ? 2 : 1)) * (BN / 16) * 64;
     const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 256 * 16));
     hipLaunchKernelGGL((splitk_reduce_tiles<GATED, BN>), dim3(grid), dim3(256), 0, s,
                        reinterpret_cast<const float4*>(P), Y, tscale, static_cast<int>(M), static_cast<int>(T),
