@@ -406,17 +406,21 @@ static int64_t dma_launch(const void* W, const void* Wu, const float* x, float* 
 // Q4_0 / Q4_1 / Q5_0 / Q5_1 58.6 / 63.0 / 75.4 / 82.4 us against 62.7 / 65.9 / 79.2 /
 // 86.4 us with 8 (same process), while at 4096 rows (fewer groups than waves) they
 // lose 10-20%; so 12 waves from 49152 rows.
-// The gated product (gate and up rows in every task), one token at 2 x 14336 x 4096
-// (HIP-graph replays, weights rotated through 512 MB, two passes): Q8_0 runs here with
-// 1-row tasks, 8 waves and a 3-slot ring in 23.8 us against 25.0-25.3 us on the
-// register-staged kernel; the nibble formats stay there (Q4_0 16.8 against 18.3 us
-// here, Q4_1 18.8-18.9 against 20.1-20.2; 12- or 16-wave and 2-row gated variants were
-// slower still).
+// The gated product (gate and up rows in every task) at 2 x 14336 x 4096 (HIP-graph
+// replays, weights rotated through 512 MB, two passes each): Q8_0 runs here with
+// 1-row tasks, 8 waves and a 3-slot ring for 1-4 tokens (23.8 / 25.0-25.4 / 27.3-27.9 /
+// 30.0-30.4 us against 25.0-25.3 / 26.0 / 33.0 / 34.2-34.5 us on the register-staged
+// kernel), and Q4_0 from 2 tokens (21.8 / 24.7-25.0 / 26.7-27.2 against 24.6-25.6 /
+// 25.2-26.0 / 29.9-30.3 us); the single-token Q4_0 product stays there (16.8 against
+// 18.3 us here; 12- or 16-wave and 2-row gated instances were slower still), as do
+// the 20- to 24-byte formats, whose gated rings leave no room for x (Q4_1 at one token
+// 18.8-18.9 against 20.1-20.2 us here).
 template <int FMT, int NT, int EP>
 static int64_t dma_nt(const void* W, const void* Wu, const float* x, float* y, int64_t M, int64_t K,
                       const DecodeEpi& epi, hipStream_t s) {
     if (Wu) {
-        if constexpr (FMT == 8 && NT == 1) return dma_launch<FMT, NT, 1, true, 8, 3, EP>(W, Wu, x, y, M, K, epi, s);
+        if constexpr (FMT == 8 || (FMT == 2 && NT >= 2))
+            return dma_launch<FMT, NT, 1, true, 8, 3, EP>(W, Wu, x, y, M, K, epi, s);
         return 0;
     }
     int64_t r = 0;
