@@ -405,7 +405,14 @@ static int64_t dma_launch(const void* W, const void* Wu, const float* x, float* 
 // 21 two-row groups per wave) gain from a third wave per SIMD: 12-wave workgroups take
 // Q4_0 / Q4_1 / Q5_0 / Q5_1 58.6 / 63.0 / 75.4 / 82.4 us against 62.7 / 65.9 / 79.2 /
 // 86.4 us with 8 (same process), while at 4096 rows (fewer groups than waves) they
-// lose 10-20%; so 12 waves from 49152 rows.
+// lose 10-20%; so 12 waves from 49152 rows.  With 2-4 tokens the third wave still pays
+// for Q4_0 (LM head, two passes each: 72.6-76.0 / 82.3 / 88.8-91.1 us against 80.0-84.0
+// / 84.1-86.9 / 92.4-93.5 us with 8 waves at 2 / 3 / 4 tokens) and is within noise for
+// the 20- to 24-byte formats (Q4_1 at 3 tokens 92-93 against 89-90 us), which keep 8.
+// Q8_0 with 2-4 tokens is no longer bound by the stream alone, and on the LM head
+// 2-row tasks on 12 waves win too: 93.7-97.4 / 99.5-101.7 / 107 us against 107-112 /
+// 108.6-111.8 / 120-121.6 us for 1-row tasks on 8 waves (1-row tasks on 12 waves:
+// 103.6-104.3 / 109.4-110.6 / 117.7-118.8).
 // The gated product (gate and up rows in every task) at 2 x 14336 x 4096 (HIP-graph
 // replays, weights rotated through 512 MB, two passes each): Q8_0 runs here with
 // 1-row tasks, 8 waves and a 3-slot ring for 1-4 tokens (23.8 / 25.0-25.4 / 27.3-27.9 /
@@ -429,11 +436,13 @@ static int64_t dma_nt(const void* W, const void* Wu, const float* x, float* y, i
         const int64_t rows1 = (M + kWaves - 1) / kWaves;              // rows per wave, 1-row tasks
         const int64_t rows2 = 2 * ((M + 2 * kWaves - 1) / (2 * kWaves));  // and 2-row tasks
         if (20 * rows2 <= 21 * rows1) {
-            if constexpr (NT == 1)
+            if constexpr (NT == 1 || FMT == 2)
                 if (M >= 49152) r = dma_launch<FMT, NT, 2, false, 12, 2, EP>(W, Wu, x, y, M, K, epi, s);
             if (!r) r = dma_launch<FMT, NT, 2, false, 8, 2, EP>(W, Wu, x, y, M, K, epi, s);
         }
     }
+    if constexpr (FMT == 8 && NT >= 2)
+        if (M >= 49152) r = dma_launch<FMT, NT, 2, false, 12, 2, EP>(W, Wu, x, y, M, K, epi, s);
     if (!r) r = dma_launch<FMT, NT, 1, false, 8, 3, EP>(W, Wu, x, y, M, K, epi, s);
     return r;
 }
