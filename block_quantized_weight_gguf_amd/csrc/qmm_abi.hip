@@ -110,11 +110,12 @@ int check_ws(const void* ws, int64_t ws_bytes, int64_t need) {
 //   Block formats.  The VALU kernels take up to 4 tokens per weight pass, so from 5
 //   tokens they read the weights twice and the single-pass MFMA kernel wins on every
 //   shape (by 1.3-2x).  At 4 tokens: long rows (K >= 8192, the down projection) go to
-//   MFMA (0.67-0.97: x of 4 such tokens does not fit the DMA-fed kernel's LDS, and the
-//   register-staged kernel is slower); gate+up stays VALU (0.96-1.11), and so does
-//   Q5_0, whose MFMA decode costs the most (LM head 1.12); the rest is MFMA from 256
-//   MiB (LM heads 0.91-1.01) and VALU below (QKV, O 1.21-1.32).  At 2-3 tokens VALU
-//   (1.04-1.71; one tie, Q5_1 gate+up at 3 tokens 0.96).
+//   MFMA (0.68-0.96: x of 4 such tokens does not fit the DMA-fed kernel's LDS, and the
+//   register-staged kernel is slower); gate+up stays VALU (0.96-1.16); the LM heads
+//   of Q4_0 and Q4_1 go to MFMA (1.00, 0.92), those of Q8_0, Q5_0 and Q5_1 stay VALU
+//   (1.17, 1.12, 1.02: their 4-token VALU passes run on 12-wave workgroups, and the
+//   5-bit MFMA decode costs the most); QKV and O stay VALU (1.21-1.30).  At 2-3 tokens
+//   VALU (1.01-1.71; one tie, Q5_1 gate+up at 3 tokens 0.96).
 //   F16 (its MFMA variant is the tiled GEMM): MFMA from 5 tokens; from 2 tokens on
 //   long rows over 32 MiB (down 0.72-0.85); at 4 tokens from 64 MiB (gate+up 0.94, LM
 //   head 0.65), at 3 from 256 MiB (LM head 0.94); VALU otherwise (QKV, O 1.23-1.37).
@@ -129,7 +130,7 @@ int choose_variant(int fmt, int64_t wbytes, int64_t K, int64_t N, bool gated) {
     }
     if (N == 4) {
         if (K >= 8192 && wbytes >= 16 * MiB) return QMM_VARIANT_MFMA;
-        if (gated || fmt == QMM_Q5_0) return QMM_VARIANT_VALU;
+        if (gated || !(fmt == QMM_Q4_0 || fmt == QMM_Q4_1)) return QMM_VARIANT_VALU;
         return wbytes >= 256 * MiB ? QMM_VARIANT_MFMA : QMM_VARIANT_VALU;
     }
     return QMM_VARIANT_VALU;

@@ -234,7 +234,7 @@ int qmm_gemv_variant(int fmt, const void* W, const float* x, float* y,
  * tokens, the tiled matrix-matrix kernel above a threshold); the thresholds here
  * are measured on MI355X at the Llama-3-8B projection shapes: the block formats
  * switch to MFMA from 5 tokens, and at 4 tokens for rows of K >= 8192 over at least
- * 16 MiB of weights and, Q5_0 excepted, for matrices of 256 MiB or more; F16 (whose
+ * 16 MiB of weights and for Q4_0 / Q4_1 matrices of 256 MiB or more; F16 (whose
  * MFMA variant is the tiled GEMM) from 5 tokens, from 2 for rows of K >= 8192 over
  * at least 32 MiB, at 4 from 64 MiB and at 3 from 256 MiB.  (qmm_gate_up_silu
  * applies the same rule to the combined gate and up weights, except that the block

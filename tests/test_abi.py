@@ -182,12 +182,12 @@ def test_variant_choice():
         v = [L.qmm_gemv_choose(fmt, 4096, 4096, n) for n in range(1, 65)]
         assert v == sorted(v), "the choice must switch once, from VALU to MFMA"
     # Measured thresholds (MI355X, Llama-3-8B shapes).  Block formats: MFMA from 5
-    # tokens; at 4 tokens on long rows (the down projection) and on the LM head
-    # (>= 256 MiB) except Q5_0; VALU at 2-3 tokens.
+    # tokens; at 4 tokens on long rows (the down projection) and on the Q4_0 / Q4_1 LM
+    # heads (>= 256 MiB); VALU at 2-3 tokens.
     for fmt in (2, 8):
         assert L.qmm_gemv_choose(fmt, 4096, 4096, 4) == 1       # 17.8 / 9.4 MB
         assert L.qmm_gemv_choose(fmt, 4096, 4096, 5) == 2
-        assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == 2     # LM head
+        assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == (2 if fmt == 2 else 1)     # LM head
         assert L.qmm_gemv_choose(fmt, 128256, 4096, 3) == 1
         assert L.qmm_gemv_choose(fmt, 128256, 4096, 2) == 1
         assert L.qmm_gemv_choose(fmt, 4096, 14336, 4) == 2      # down projection
@@ -197,7 +197,7 @@ def test_variant_choice():
         assert [L.qmm_gemv_choose(fmt, 4096, 4096, n) for n in (1, 3, 4, 5, 64)] == [1, 1, 1, 2, 2]
         assert L.qmm_gemv_choose(fmt, 4096, 14336, 4) == 2
         assert L.qmm_gemv_choose(fmt, 128256, 4096, 3) == 1
-        assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == (1 if fmt == 6 else 2)
+        assert L.qmm_gemv_choose(fmt, 128256, 4096, 4) == (2 if fmt == 3 else 1)
     # Long rows of few rows: not the MFMA kernel (under 16 MiB of weights).
     assert L.qmm_gemv_choose(8, 512, 14336, 4) == 1
     # F16 (MFMA = the tiled GEMM): from 5 tokens; from 2 on long rows over 32 MiB; at 4
