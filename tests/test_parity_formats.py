@@ -321,7 +321,7 @@ def test_gemv_mfma(fmt, M, K, N):
     qmm.qmm_gemv_variant(fmt, dev(raw), dev(x), buf, M, K, N, MFMA)
     torch.cuda.synchronize()
     assert guard_intact(buf, N * M)
-    # x is rounded to fp16 inside the MFMA kernels: the oracle takes the same inputs.
+    # The oracle takes the caller's fp32 x; the kernels scale and round it to fp16 themselves.
     y_ref, S = oracle.matmul_ref(fmt, raw, x, M, K)
     check_linear(buf[:N * M].cpu().numpy().reshape(N, M), y_ref, S, f"gemv mfma fmt={fmt} M={M} K={K} N={N}")
 
