@@ -16,7 +16,7 @@
 //     per MFMA.
 //   * The activation tile (256 tokens x 64 halfs) is copied with coalesced 16-byte
 //     loads.  Tokens are fp16; fp32 ones (the batched-GEMV hand-off) arrive scaled
-//     per token (scale_tokens_f16) and the epilogue multiplies by tscale[t].
+//     per token (scale_tokens_kernel) and the epilogue multiplies by tscale[t].
 //   * Global loads for step k+1 are issued before the MFMAs of step k, so HBM
 //     latency hides behind the matrix work; LDS holds one stage.
 //   * LDS rows are padded from 128 to 144 bytes so the 16-lane groups of each

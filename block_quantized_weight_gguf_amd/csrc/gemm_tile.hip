@@ -48,7 +48,7 @@
 //     takes 32 gate and the matching 32 up rows, so every lane ends holding g and u
 //     for the same outputs and applies h = silu(g) * u before the store.
 //   * Tokens are always fp16.  fp32 tokens (batched decode through the MFMA path)
-//     arrive pre-scaled: scale_tokens_f16 wrote fp16(2^s_t x_t) per token t, and the
+//     arrive pre-scaled: scale_tokens_kernel wrote fp16(2^s_t x_t) per token t, and the
 //     epilogue (or the split-K reduce) multiplies token t's outputs by tscale[t] =
 //     2^-s_t.
 #include <algorithm>

@@ -1,4 +1,6 @@
-// fp32 tokens -> per-token scaled fp16, the operand form of the MFMA products.
+// fp32 tokens -> per-token scaled fp16, the operand form of the tiled GEMM when it
+// serves fp32-token products (more than 32 tokens, F16 weights, K % 256 != 0; the
+// weight-streaming MFMA GEMV converts its tokens itself, stage by stage).
 //
 // The MFMA products multiply fp16 operands ("alpaca.swift", Design: half-precision
 // activations on the matrix hardware).  Decode activations arrive as fp32, whose
@@ -6,7 +8,7 @@
 // quantised), so each token row t is scaled by the power of two 2^s_t that brings its
 // largest magnitude into [2^14, 2^15) before the one rounding to fp16: nothing
 // overflows, and every element keeps a relative error <= 2^-11 unless it lies more
-// than about 2^28 below its token's largest.  The products multiply token t's sums by
+// than about 2^28 below its token's largest.  The GEMM multiplies token t's sums by
 // inv[t] = 2^-s_t, an exact power of two.
 //
 // One workgroup per token row: a pass over the row for its largest |x| (waves reduce
