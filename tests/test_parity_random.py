@@ -52,7 +52,7 @@ ROUTES = [(si.FMT_Q4_0, "gate_up", 3000, 1024, n) for n in (2, 3, 4)] + \
          [(si.FMT_Q8_0, "gemv", 50001, 512, n) for n in (2, 3, 4)] + \
          [(si.FMT_Q4_0, "gemv", 49153, 1024, 3), (si.FMT_Q8_0, "rmsnorm_gemv", 49160, 768, 2),
           (si.FMT_Q4_0, "rmsnorm_gemv", 2600, 512, 3)]
-CASES = [_draw(i) for i in range(48)] + ROUTES
+CASES = [_draw(i) for i in range(120)] + ROUTES
 
 
 @pytest.mark.parametrize("fmt,op,M,K,N", CASES, ids=[f"{c[1]}-f{c[0]}-{c[2]}x{c[3]}-n{c[4]}" for c in CASES])
