@@ -289,15 +289,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
             return;
         }
         float* xf = reinterpret_cast<float*>(xs);
-        for (int j = threadIdx.x; j < NT * nb * 8; j += XT) {
-            const int n = j / (nb * 8), r = j - n * (nb * 8);
-            const int64_t k = 4 * static_cast<int64_t>(r);
-            float4 v = *reinterpret_cast<const float4*>(x + n * ldx + k);
-            if constexpr (EP == EP_NORM) {
-                const float4 gm = *reinterpret_cast<const float4*>(epi.gamma + k);
-                v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
+        if (nxb <= XT) {
+            // One staging round: each lane still holds its block in xv (times gamma
+            // under EP_NORM), so x is not read again.
+            if (static_cast<int>(threadIdx.x) < nxb) {
+                const int j = threadIdx.x;
+                const int n = j / nb, b = j - (j / nb) * nb;
+                float* dst = xf + (n * nb + b) * XS_STRIDE;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) *reinterpret_cast<float4*>(dst + 4 * c) = xv[c];
             }
-            *reinterpret_cast<float4*>(xf + n * nb * XS_STRIDE + (r >> 3) * XS_STRIDE + 4 * (r & 7)) = v;
+        } else {
+            for (int j = threadIdx.x; j < NT * nb * 8; j += XT) {
+                const int n = j / (nb * 8), r = j - n * (nb * 8);
+                const int64_t k = 4 * static_cast<int64_t>(r);
+                float4 v = *reinterpret_cast<const float4*>(x + n * ldx + k);
+                if constexpr (EP == EP_NORM) {
+                    const float4 gm = *reinterpret_cast<const float4*>(epi.gamma + k);
+                    v.x *= gm.x, v.y *= gm.y, v.z *= gm.z, v.w *= gm.w;
+                }
+                *reinterpret_cast<float4*>(xf + n * nb * XS_STRIDE + (r >> 3) * XS_STRIDE + 4 * (r & 7)) = v;
+            }
         }
         lds_barrier();
     }
