@@ -367,13 +367,35 @@ __device__ __forceinline__ bool stage_x16(float4 v, int c, uint32_t* blk) {
     return k < s.wide_key;
 }
 
+// Rotated code order (Q8_0 and Q4_0, whose 34- and 18-byte blocks put the codes of
+// every other block at an offset of 2 mod 4 in a 16-byte aligned slice): such a
+// block's code dwords come from lds_read_rotated, so code dword i holds code bytes
+// rot_byte(i, p), p = 0..3 (ND code dwords in all).  Aligned blocks keep 4i + p.
+__host__ __device__ constexpr int rot_byte(int nd, int i, int p, bool rot) {
+    return !rot ? 4 * i + p : i > 0 ? 4 * i - 2 + p : p < 2 ? p : 4 * nd - 4 + p;
+}
+// The value index of half h (0 = low) of staged dword j for Q8_0 / Q4_0 in either
+// code order: Q8_0 pairs bytes (0, 2) and (1, 3) of code dword j / 2 (sel02, sel13);
+// Q4_0 dword 4i + k pairs the low (k < 2) or high nibbles of bytes (k & 1) and
+// (k & 1) + 2 of code dword i, the high nibble of byte c being value 16 + c.
+template <int FMT>
+__host__ __device__ constexpr int staged_value(int j, int h, bool rot) {
+    return FMT == 8 ? rot_byte(8, j >> 1, (j & 1) + 2 * h, rot)
+                    : ((j & 3) >= 2 ? 16 : 0) + rot_byte(4, j >> 2, (j & 1) + 2 * h, rot);
+}
+__device__ __forceinline__ float value_at(const float4 (&v)[8], int k) {
+    const float4 t = v[k >> 2];
+    return (k & 3) == 0 ? t.x : (k & 3) == 1 ? t.y : (k & 3) == 2 ? t.z : t.w;
+}
+
 // One whole block of one token staged by one lane: v holds its 32 values (chunk c =
 // values 4c..4c+3).  The same block floating point and pair order as stage_x16, and
 // X (biased formats: stage_chain's dot2 steps, so it is bit-identical) formed from
 // the lane's own registers; the block's 20 dwords go out as five 16-byte LDS writes.
+// ROT (Q8_0 / Q4_0 only) stages the pairs in the rotated code order instead.
 // Returns true when the block is wide.
 template <int FMT>
-__device__ __forceinline__ bool stage_block(const float4 (&v)[8], uint32_t* blk) {
+__device__ __forceinline__ bool stage_block(const float4 (&v)[8], uint32_t* blk, bool rot = false) {
     float m = 0.0f;
     uint32_t k = 0xFFFFFFFFu;
 #pragma unroll
@@ -383,11 +405,25 @@ __device__ __forceinline__ bool stage_block(const float4 (&v)[8], uint32_t* blk)
     }
     const BlockScale s = block_scale(m);
     uint32_t w[16];
+    if constexpr (FMT == 8 || FMT == 2) {
+        if (rot) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const int slot = (FMT == 8) ? 2 * c : 4 * (c & 3) + ((c >> 2) << 1);
-        w[slot] = pack_h2(v[c].x * s.sc, v[c].z * s.sc);
-        w[slot + 1] = pack_h2(v[c].y * s.sc, v[c].w * s.sc);
+            for (int j = 0; j < 16; ++j)
+                w[j] = pack_h2(value_at(v, staged_value<FMT>(j, 0, true)) * s.sc,
+                               value_at(v, staged_value<FMT>(j, 1, true)) * s.sc);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                w[j] = pack_h2(value_at(v, staged_value<FMT>(j, 0, false)) * s.sc,
+                               value_at(v, staged_value<FMT>(j, 1, false)) * s.sc);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int slot = 4 * (c & 3) + ((c >> 2) << 1);
+            w[slot] = pack_h2(v[c].x * s.sc, v[c].z * s.sc);
+            w[slot + 1] = pack_h2(v[c].y * s.sc, v[c].w * s.sc);
+        }
     }
     float chain = 0.0f;
     if constexpr (DotCode<FMT>::BIAS) {
@@ -418,8 +454,11 @@ __device__ __forceinline__ void stage_chain(uint32_t* blk) {
 }
 
 // One lane's block for RU row units and NT tokens with packed fp16 dot products
-// (xb[n]: the token's staged block, XS16 dwords).
-template <int FMT, int RU, int NT>
+// (xb[n]: the token's staged block, XS16 dwords).  ROT (Q8_0 / Q4_0): the codes are
+// read in the rotated order (lds_read_rotated), one v_perm per block in place of a
+// realignment per dword, against x staged in the matching order (stage_block's rot
+// for blocks whose codes start at 2 mod 4).
+template <int FMT, int RU, int NT, bool ROT = false>
 __device__ __forceinline__ void block_dot(const uint8_t* const (&buf)[RU], const int (&off)[RU],
                                           const uint32_t* const (&xb)[NT], float (&acc)[RU][NT]) {
     using DC = DotCode<FMT>;
@@ -441,7 +480,8 @@ __device__ __forceinline__ void block_dot(const uint8_t* const (&buf)[RU], const
         r[u] = 0.0f;
         if constexpr (FMT == 8 || FMT == 2) {
             d[u] = half_bits_to_float(lds_read_u16(buf[u], off[u]));
-            lds_read_dwords<NDW>(buf[u], off[u] + 2, cw[u]);
+            if constexpr (ROT) lds_read_rotated<NDW>(buf[u], off[u] + 2, cw[u]);
+            else lds_read_dwords<NDW>(buf[u], off[u] + 2, cw[u]);
             qh[u] = 0;
         } else {
             float m;

@@ -126,6 +126,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
     constexpr int RU = GATED ? 2 * R : R;
     constexpr int NI = RU * DG_NI;         // DMA instructions per task
     constexpr int WS = WAVES * RU * SLOT;  // bytes of one ring stage (all waves)
+    // Q8_0 / Q4_0 blocks (34 / 18 bytes) sit at 2 mod 4 in a slot for even block
+    // indices (slices start at even blocks, slots on 16 bytes): their codes are read
+    // in the rotated order and x is staged to match (block_dot, stage_block).
+    constexpr bool ROT = FMT == 8 || FMT == 2;
     __shared__ __align__(16) uint8_t RS0[WS + DG_PAD];
     __shared__ __align__(16) uint8_t RS1[WS + DG_PAD];
     __shared__ __align__(16) uint8_t RS2[S > 2 ? WS + DG_PAD : 16];
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
 #pragma unroll
                 for (int k = 0; k < NT; ++k) ss[k] += (k == n) ? q : 0.0f;
             }
-            wide |= stage_block<FMT>(xv, xs + n * xstride + b * XS16);
+            wide |= stage_block<FMT>(xv, xs + n * xstride + b * XS16, ROT && (b & 1) == 0);
         }
     };
     load_round(threadIdx.x);
@@ -345,7 +349,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_dma_kernel(const uint8_t* __r
                         const uint32_t* xb[NT];
 #pragma unroll
                         for (int n = 0; n < NT; ++n) xb[n] = xs + n * xstride + (s0 + blk) * XS16;
-                        block_dot<FMT, RU, NT>(buf, off, xb, acc);
+                        block_dot<FMT, RU, NT, ROT>(buf, off, xb, acc);
                     }
                 }
             }

@@ -140,6 +140,24 @@ __device__ __forceinline__ void lds_read_dwords(const uint8_t* buf, int off, uin
     for (int i = 0; i < ND; ++i) out[i] = align_bytes(d[i + 1], d[i], sh);
 }
 
+// The same ND + 1 dwords read without realignment: with off = 4a + 2 (2-byte aligned
+// codes), d[0] holds bytes off-2 .. off+1 and d[ND] bytes off+4ND-2 .. off+4ND+1, so
+// out[0] = bytes off, off+1, off+4ND-2, off+4ND-1 (one v_perm) and out[i] = d[i]
+// holds bytes off+4i-2 .. off+4i+1 for i >= 1; with off = 4a, out[i] = d[i] are the
+// aligned dwords.  Every code byte appears once, in an order that depends only on
+// off % 4, which the staged operand it meets is laid out for.
+template <int ND>
+__device__ __forceinline__ void lds_read_rotated(const uint8_t* buf, int off, uint32_t (&out)[ND]) {
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(buf + (off & ~3));
+    const uint32_t sel = (off & 2) ? 0x05040302u : 0x03020100u;
+    uint32_t d[ND + 1];
+#pragma unroll
+    for (int i = 0; i <= ND; ++i) d[i] = base[i];
+    out[0] = __builtin_amdgcn_perm(d[ND], d[0], sel);
+#pragma unroll
+    for (int i = 1; i < ND; ++i) out[i] = d[i];
+}
+
 __device__ __forceinline__ uint32_t lds_read_u16(const uint8_t* buf, int off) {
     return *reinterpret_cast<const uint16_t*>(buf + off);
 }
