@@ -24,13 +24,26 @@ namespace qmm {
 constexpr int XS_STRIDE = 36;  // floats per block in the LDS copy of x (32 + 4 padding)
 
 // The fields of a Q4_1 / Q5_0 / Q5_1 block from LDS: scale, bias (biased formats),
-// the fifth-bit word (5-bit formats) and the four dwords of nibbles.
+// the fifth-bit word (5-bit formats) and the four dwords of nibbles.  Q4_1 and Q5_1
+// blocks (20 and 24 bytes, every field on 4 bytes) lie on 4 bytes wherever they are
+// staged, since W is 16-byte aligned and rows and blocks are multiples of 4 bytes
+// long, so their dwords are read as they lie; Q5_0 blocks (22 bytes) are realigned.
 template <int FMT>
 __device__ __forceinline__ void read_nib_block(const uint8_t* buf, int off, float& d, float& m, uint32_t& qh,
                                                uint32_t (&cw)[4]) {
     using T = Nib<FMT>;
+    if constexpr (T::BIAS) {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(buf + off);
+        const uint32_t dm = w[0];
+        d = half_bits_to_float(static_cast<uint16_t>(dm));
+        m = half_bits_to_float(static_cast<uint16_t>(dm >> 16));
+        qh = T::FIVE ? w[1] : 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cw[i] = w[(T::FIVE ? 2 : 1) + i];
+        return;
+    }
     d = half_bits_to_float(lds_read_u16(buf, off));
-    m = T::BIAS ? half_bits_to_float(lds_read_u16(buf, off + 2)) : 0.0f;
+    m = 0.0f;
     if constexpr (T::FIVE) {
         uint32_t w[5];  // qh is followed directly by the nibbles
         lds_read_dwords<5>(buf, off + T::QH, w);
