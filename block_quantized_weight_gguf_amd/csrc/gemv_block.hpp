@@ -1,8 +1,9 @@
 // Per-block decode + FMA used by the GEMV kernels.
 //
 // One lane handles one 32-weight block of up to RU row units at once, reading the
-// raw block bytes from LDS at any 2-byte aligned address and the matching 32
-// activations per token from LDS (block stride XS_STRIDE floats).  The activations
+// raw block bytes from LDS at any 2-byte aligned address (Q4_1 and Q5_1 blocks, whose
+// fields all lie on 4 bytes, at 4-byte aligned ones) and the matching 32 activations
+// per token from LDS (block stride XS_STRIDE floats).  The activations
 // are read once and reused for all row units.
 //   Q8_0: 32 codes -> one signed-byte-to-float op each (SDWA sext) -> one FMA each;
 //         the block partial is scaled by d once.
